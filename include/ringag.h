@@ -1,0 +1,194 @@
+/*
+ * ringag.h — C ABI of libringag.so: one tensor-parallel rank's share of the ring-decomposed
+ * all-gather + GEMM (AG+GEMM) and of its mirror, GEMM + reduce-scatter (GEMM+RS), on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Pages the operations come from (cited by title and section):
+ *   - TransformerEngine issue #1583 "curious about atomic_gemm_overlap_ag", C++ listing:
+ *     a ring of tp-1 send/receive steps fills a gathered buffer chunk by chunk; one GEMM launch
+ *     split into tp pieces along n waits on a per-chunk counter bumped after each receive; the
+ *     output goes through a buffer of tp+1 chunks; the GEMM is "TN" (m = weight rows, n = gathered
+ *     rows); communication runs on its own streams joined by events.
+ *   - nvFuser PR #3392 "Ring-based decomposition for Allgather+GEMM overlap ATen implementation",
+ *     experiment: posting communication before compute gave near-complete overlap.
+ *   - TransformerEngine PR #2443 "Comm+GEMM overlap API updated to support cuBlasMp backend",
+ *     sequence diagram: AG+GEMM and GEMM+RS as the two phases of one context object with
+ *     create/destroy; review comments: global k = local k * tp for the RS GEMM, argument-order
+ *     mistakes between tp_rank and tp_size.
+ *   - nvFuser PR #5742 "Reference implementation for Linear+Allreduce with overlapping",
+ *     walkthrough: the chunked row-parallel linear equals the unchunked one; each output chunk is a
+ *     sum over ranks.
+ *
+ * Simulated ring: the library runs one rank (self_rank) of a tp-rank ring on a single GPU.  The
+ * other ranks' chunks are caller-provided device buffers; their "arrival" is a device-to-device
+ * copy into the gathered buffer on a library-owned side stream, in ring order, each followed by a
+ * bump of that chunk's ready counter.  A rank sends to rank+1 and receives from rank-1, so chunks
+ * reach self_rank in the order s, s-1, s-2, ... (mod tp).
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers (memory from hipMalloc / torch on the context's device),
+ *     owned by the caller, row-major, 16-byte aligned, and must stay valid until `stream` has
+ *     passed the operation.  Host arrays of pointers (B_chunks, partials) are read during the call
+ *     only.
+ *   - Every call is stream-ordered on `stream` (0 = the null stream): it enqueues work and returns.
+ *     Outputs are valid in `stream` order.  Library-internal side work is joined back into `stream`
+ *     before the call returns, so nothing of a call is left running outside `stream`.
+ *   - One operation in flight per context; a context is not thread-safe.  Calls on different
+ *     contexts are independent.
+ *   - Every entry point returns RAG_OK (0) or a negative RAG_E* code and never throws.  Arguments
+ *     are validated before any device work is enqueued; on failure nothing is enqueued and
+ *     rag_last_error() describes the problem.
+ *   - Integer order is always (tp, self_rank).
+ */
+#ifndef RINGAG_H
+#define RINGAG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+enum {
+    RAG_OK = 0,
+    RAG_EINVAL = -1,    /* bad argument; nothing was enqueued */
+    RAG_EHIP = -2,      /* a HIP runtime call failed (message names it) */
+    RAG_ETIMEOUT = -3,  /* a chunk's ready counter did not reach the call's epoch within the spin
+                           limit; the tiles that waited were skipped (reported by rag_check) */
+    RAG_ENOMEM = -4     /* a library-owned buffer could not be allocated */
+};
+
+/* Element types of the GEMM inputs.  The output D is always bf16. */
+typedef enum {
+    RAG_BF16 = 0,       /* bfloat16 */
+    RAG_FP8_E4M3 = 1    /* OCP FP8 E4M3 (no infinities, max 448) with one fp32 scale per tensor */
+} rag_dtype;
+
+/* Flags for ag_gemm / gemm_rs (bitwise or). */
+enum {
+    RAG_STAGED_OUT = 1, /* AG+GEMM: write the output through a library-owned buffer of tp+1 chunks
+                           in consumption order and copy it to D afterwards (the listing's output
+                           staging); the default writes each chunk at its rank offset directly */
+    RAG_NO_COPY = 2,    /* AG+GEMM: no arrivals; every chunk counts as ready and is read from its
+                           slot of G as it is (GEMM-only timing; G must already hold the chunks) */
+    RAG_COPY_ONLY = 4   /* AG+GEMM: arrivals (copies + counter bumps) only, no GEMM */
+};
+
+/* Option keys for rag_set_option. */
+enum {
+    RAG_OPT_COPY_ENGINE = 1,    /* 0 = copy kernel on compute units (default), 1 = SDMA engines
+                                   (hipMemcpyDeviceToDeviceNoCU + hipStreamWriteValue32) */
+    RAG_OPT_COMM_WGS = 2,       /* workgroups of the copy kernel (default 32, 1..1024): the share of
+                                   compute units that communication takes */
+    RAG_OPT_SPIN_LIMIT_US = 3,  /* how long a tile waits for its chunk before giving up
+                                   (microseconds, default 2,000,000) */
+    RAG_OPT_ARRIVAL_DELAY_US = 4, /* test hook: the copy kernel holds each counter bump back by this
+                                   many microseconds after the chunk's copy (default 0, max 10^6) */
+    RAG_OPT_WITHHOLD_MASK = 5,  /* test hook: bit j set = never bump the counter of the chunk at
+                                   ring position j (1..tp-1); the waiting tiles then time out */
+    RAG_OPT_TIMING = 6,         /* 1 = record HIP events around every GEMM launch (rag_kernel_times) */
+    RAG_OPT_TILE = 7            /* GEMM tile configuration: 0 = automatic, else a RAG_TILE_* value */
+};
+
+/* Tile configurations (rows of D x columns of D per workgroup). */
+enum { RAG_TILE_AUTO = 0, RAG_TILE_128x128 = 1, RAG_TILE_256x128 = 2, RAG_TILE_256x256 = 3 };
+
+typedef struct rag_ctx rag_ctx;     /* opaque; owned by the library */
+
+#define RAG_MAX_TP 16
+
+/* Create a context on `device` for rings of up to max_tp ranks (1..RAG_MAX_TP).  Allocates the
+ * side stream, events, per-chunk ready counters, an error word and the epoch (all cached for the
+ * context's life; no per-call allocation).  flags: reserved, pass 0.  On success *out receives the
+ * context.  TransformerEngine PR #2443, sequence diagram: context creation at initialisation. */
+int rag_create(rag_ctx** out, int device, int max_tp, int flags);
+
+/* Destroy a context (waits for its side stream first).  Safe on NULL. */
+int rag_destroy(rag_ctx* ctx);
+
+/* Set an option (RAG_OPT_*).  Takes effect from the next call. */
+int rag_set_option(rag_ctx* ctx, int key, long long value);
+
+/*
+ * AG+GEMM for rank self_rank of a tp-rank ring:
+ *     G = [B_0; B_1; ...; B_{tp-1}]          (rank-ordered all-gather, chunk r at row r*nc)
+ *     D = G * A^T                            (bf16 out, fp32 accumulation)
+ * TransformerEngine issue #1583, C++ listing (ring steps, per-chunk counters, split GEMM, TN
+ * layout, N+1-chunk output staging); nvFuser PR #3392 (ring decomposition; communication posted
+ * before compute).
+ *
+ *   A         weight shard [M, K], dt
+ *   M, K      M >= 1; K >= 1 and a multiple of 64 (bf16) or 128 (fp8)
+ *   B_chunks  HOST array of tp device pointers, B_chunks[r] = rank r's chunk [nc, K], dt.  Entry
+ *             self_rank is this rank's own chunk (read directly, never waited for); the others
+ *             stand for the peers' chunks and are copied into G as they "arrive".
+ *   nc        rows per chunk (>= 1); N = tp * nc
+ *   tp, self_rank  1 <= tp <= max_tp of the context, 0 <= self_rank < tp
+ *   G         [N, K] dt, receives the gathered input (chunk r at rows [r*nc, (r+1)*nc)); NULL = use
+ *             a library-owned gather buffer (then the gathered input is not returned)
+ *   D         [N, M] bf16 output; chunk r's rows are B_r * A^T whatever self_rank is
+ *   dt        RAG_BF16 or RAG_FP8_E4M3
+ *   scale_A, scale_B  device fp32 scalars (dequantisation factors: value = code * scale); required
+ *             for fp8, must be NULL for bf16
+ *   flags     RAG_STAGED_OUT | RAG_NO_COPY | RAG_COPY_ONLY (NO_COPY and COPY_ONLY are exclusive)
+ *   stream    caller's stream
+ * Errors: RAG_EINVAL (bad sizes/pointers/flags, any operand of 2 GiB or more, G or D overlapping
+ * an input), RAG_EHIP, RAG_ENOMEM.  A chunk that never arrives is reported by rag_check.
+ */
+int ag_gemm(rag_ctx* ctx,
+            const void* A, int M, int K,
+            const void* const* B_chunks, int nc,
+            int tp, int self_rank,
+            void* G, void* D,
+            rag_dtype dt, const float* scale_A, const float* scale_B,
+            int flags, void* stream);
+
+/*
+ * GEMM + reduce-scatter (row-parallel linear) for rank self_rank of a tp-rank ring:
+ *     P     = X * W^T over all T rows            (this rank's partial of the full output, fp32)
+ *     D     = sum over ranks p of P_p[rows of chunk self_rank]   (bf16 out)
+ *     send[c] = P[rows of chunk c]  for c != self_rank            (fp32, the outgoing chunks)
+ * where P_p for p != self_rank are the peers' partials given in `partials`.
+ * TransformerEngine PR #2443 (sequence diagram: split GEMM then reduce-scatter; review: the RS
+ * GEMM's contraction dimension is the local shard of a global k); nvFuser PR #5742 (walkthrough:
+ * each output chunk is summed over ranks).
+ *
+ *   X         [T, Kl] bf16 activation shard; T = tp * nc
+ *   W         [Mo, Kl] bf16 weight shard
+ *   Kl        >= 1, multiple of 64;  Mo >= 1
+ *   partials  HOST array of tp device pointers to fp32 [T, Mo] partials with row stride ldp
+ *             (elements, >= Mo); only rows of chunk self_rank are read; entry self_rank ignored
+ *   send      [tp, nc, Mo] fp32 outgoing chunks (slot self_rank untouched); NULL = not stored
+ *   D         [nc, Mo] bf16, this rank's reduced chunk
+ * Errors: RAG_EINVAL, RAG_EHIP.
+ */
+int gemm_rs(rag_ctx* ctx,
+            const void* X, int T, int Kl,
+            const void* W, int Mo,
+            const float* const* partials, long long ldp,
+            int tp, int self_rank,
+            float* send, void* D,
+            int flags, void* stream);
+
+/* Synchronise the context's device work and report whether any wait timed out since the last
+ * check (RAG_ETIMEOUT; the error word is then cleared), or RAG_OK. */
+int rag_check(rag_ctx* ctx);
+
+/* GEMM kernel durations (milliseconds) recorded since the last call to this function while
+ * RAG_OPT_TIMING was on; synchronises those events.  Writes up to max_n values to out and returns
+ * how many were recorded (>= 0), or a negative RAG_E* code. */
+int rag_kernel_times(rag_ctx* ctx, float* out, int max_n);
+
+/* Text for the last non-zero return on the calling thread ("" if none). */
+const char* rag_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int rag_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RINGAG_H */

@@ -1,0 +1,203 @@
+"""Thin ctypes binding of libringag.so (include/ringag.h).
+
+Argument marshalling only: tensors are turned into device pointers and sizes, the caller's current
+torch stream is passed as the stream, and a non-zero return becomes a RuntimeError carrying
+rag_last_error().  Every step of the operations runs in the library's HIP kernels; there is no
+other code path.  If the library has not been built, the first call raises.
+
+Environment overrides applied when a Context is created (all optional):
+  RAG_COPY_ENGINE=kernel|sdma   RAG_COMM_WGS=n   RAG_SPIN_LIMIT_US=n   RAG_TILE=auto|128x128|256x128|256x256
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Sequence
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libringag.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "ringag.h")
+
+# constants of include/ringag.h
+RAG_OK, RAG_EINVAL, RAG_EHIP, RAG_ETIMEOUT, RAG_ENOMEM = 0, -1, -2, -3, -4
+RAG_BF16, RAG_FP8_E4M3 = 0, 1
+RAG_STAGED_OUT, RAG_NO_COPY, RAG_COPY_ONLY = 1, 2, 4
+RAG_OPT_COPY_ENGINE, RAG_OPT_COMM_WGS, RAG_OPT_SPIN_LIMIT_US = 1, 2, 3
+RAG_OPT_ARRIVAL_DELAY_US, RAG_OPT_WITHHOLD_MASK, RAG_OPT_TIMING, RAG_OPT_TILE = 4, 5, 6, 7
+TILES = {"auto": 0, "128x128": 1, "256x128": 2, "256x256": 3}
+RAG_MAX_TP = 16
+
+_lib = None
+
+
+class RagError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"ringag error {code}: {msg}")
+        self.code = code
+
+
+def lib():
+    """Load libringag.so (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it first (python -m "
+                           "ring_all_gather_amd.build or __graft_entry__.build())")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, ll = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong
+    L.rag_create.argtypes = [ctypes.POINTER(vp), i, i, i]
+    L.rag_destroy.argtypes = [vp]
+    L.rag_set_option.argtypes = [vp, i, ll]
+    L.ag_gemm.argtypes = [vp, vp, i, i, ctypes.POINTER(vp), i, i, i, vp, vp, i, vp, vp, i, vp]
+    L.gemm_rs.argtypes = [vp, vp, i, i, vp, i, ctypes.POINTER(vp), ll, i, i, vp, vp, i, vp]
+    L.rag_check.argtypes = [vp]
+    L.rag_kernel_times.argtypes = [vp, ctypes.POINTER(ctypes.c_float), i]
+    L.rag_last_error.restype = ctypes.c_char_p
+    L.rag_version.restype = i
+    for f in ("rag_create", "rag_destroy", "rag_set_option", "ag_gemm", "gemm_rs", "rag_check",
+              "rag_kernel_times"):
+        getattr(L, f).restype = i
+    _lib = L
+    return L
+
+
+def declared_functions():
+    """Names of the functions include/ringag.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def last_error() -> str:
+    return lib().rag_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != RAG_OK:
+        raise RagError(rc, last_error())
+    return rc
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors passed to libringag must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libringag must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Context:
+    """Owns a rag_ctx (side stream, events, counters, epoch, cached buffers)."""
+
+    def __init__(self, device: int = 0, max_tp: int = 8):
+        h = ctypes.c_void_p()
+        _check(lib().rag_create(ctypes.byref(h), device, max_tp, 0))
+        self.h = h
+        self.device = device
+        self.max_tp = max_tp
+        env = os.environ
+        if "RAG_COPY_ENGINE" in env:
+            self.set_option(RAG_OPT_COPY_ENGINE, {"kernel": 0, "sdma": 1}[env["RAG_COPY_ENGINE"]])
+        if "RAG_COMM_WGS" in env:
+            self.set_option(RAG_OPT_COMM_WGS, int(env["RAG_COMM_WGS"]))
+        if "RAG_SPIN_LIMIT_US" in env:
+            self.set_option(RAG_OPT_SPIN_LIMIT_US, int(env["RAG_SPIN_LIMIT_US"]))
+        if "RAG_TILE" in env:
+            self.set_option(RAG_OPT_TILE, TILES[env["RAG_TILE"]])
+
+    def set_option(self, key: int, value: int):
+        _check(lib().rag_set_option(self.h, key, int(value)))
+
+    def check(self):
+        """Synchronise and raise RagError(RAG_ETIMEOUT) if a chunk never arrived."""
+        _check(lib().rag_check(self.h))
+
+    def kernel_times(self, max_n: int = 4096):
+        buf = (ctypes.c_float * max_n)()
+        n = lib().rag_kernel_times(self.h, buf, max_n)
+        if n < 0:
+            _check(n)
+        return [buf[i] for i in range(min(n, max_n))]
+
+    def close(self):
+        if getattr(self, "h", None):
+            lib().rag_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def ag_gemm(ctx: Context, A: torch.Tensor, B_chunks: Sequence[torch.Tensor], tp: int,
+            self_rank: int, D: torch.Tensor, G: Optional[torch.Tensor] = None,
+            scale_A: Optional[torch.Tensor] = None, scale_B: Optional[torch.Tensor] = None,
+            flags: int = 0, stream=None) -> int:
+    """D = [B_0; ...; B_{tp-1}] A^T for rank self_rank of a tp-rank ring (see ringag.h)."""
+    if len(B_chunks) != tp:
+        raise ValueError(f"need tp={tp} chunks, got {len(B_chunks)}")
+    fp8 = A.dtype == torch.float8_e4m3fn
+    if not fp8 and A.dtype != torch.bfloat16:
+        raise ValueError("A must be bfloat16 or float8_e4m3fn")
+    M, K = A.shape
+    nc = B_chunks[0].shape[0]
+    for b in B_chunks:
+        if b.dtype != A.dtype or tuple(b.shape) != (nc, K):
+            raise ValueError("every chunk must be [nc, K] with A's dtype")
+    if D.dtype != torch.bfloat16 or tuple(D.shape) != (tp * nc, M):
+        raise ValueError(f"D must be bfloat16 [{tp * nc}, {M}]")
+    if G is not None and (G.dtype != A.dtype or tuple(G.shape) != (tp * nc, K)):
+        raise ValueError(f"G must be [{tp * nc}, {K}] with A's dtype")
+    ptrs = (ctypes.c_void_p * tp)(*[_ptr(b) for b in B_chunks])
+    return _check(lib().ag_gemm(ctx.h, _ptr(A), M, K, ptrs, nc, tp, self_rank, _ptr(G), _ptr(D),
+                                RAG_FP8_E4M3 if fp8 else RAG_BF16, _ptr(scale_A), _ptr(scale_B),
+                                flags, _stream(stream)))
+
+
+def gemm_rs(ctx: Context, X: torch.Tensor, W: torch.Tensor,
+            partials: Sequence[Optional[torch.Tensor]], tp: int, self_rank: int,
+            D: torch.Tensor, send: Optional[torch.Tensor] = None, stream=None) -> int:
+    """D = sum over ranks of the rows of chunk self_rank of X W^T (peers' partials given)."""
+    T, Kl = X.shape
+    Mo = W.shape[0]
+    if X.dtype != torch.bfloat16 or W.dtype != torch.bfloat16 or W.shape[1] != Kl:
+        raise ValueError("X [T, Kl] and W [Mo, Kl] must be bfloat16")
+    if len(partials) != tp:
+        raise ValueError(f"need tp={tp} partial entries (entry self_rank may be None)")
+    nc = T // tp
+    if D.dtype != torch.bfloat16 or tuple(D.shape) != (nc, Mo):
+        raise ValueError(f"D must be bfloat16 [{nc}, {Mo}]")
+    if send is not None and (send.dtype != torch.float32 or tuple(send.shape) != (tp, nc, Mo)):
+        raise ValueError(f"send must be float32 [{tp}, {nc}, {Mo}]")
+    ldp = Mo
+    arr = []
+    for p, t in enumerate(partials):
+        if p == self_rank or t is None:
+            arr.append(None)
+            continue
+        if t.dtype != torch.float32 or t.dim() != 2 or t.shape[0] != T or t.shape[1] < Mo \
+                or t.stride(1) != 1 or not t.is_cuda:
+            raise ValueError("each peer partial must be a float32 GPU tensor [T, >=Mo], unit "
+                             "column stride")
+        ldp = t.stride(0)
+        arr.append(ctypes.c_void_p(t.data_ptr()))
+    for p, t in enumerate(partials):
+        if p != self_rank and t is not None and t.stride(0) != ldp:
+            raise ValueError("all peer partials must share one row stride")
+    ptrs = (ctypes.c_void_p * tp)(*arr)
+    return _check(lib().gemm_rs(ctx.h, _ptr(X), T, Kl, _ptr(W), Mo, ptrs, ldp, tp, self_rank,
+                                _ptr(send), _ptr(D), 0, _stream(stream)))

@@ -1,0 +1,77 @@
+// Arrival (producer) kernel: stands in for the receive side of the ring on one GPU.
+//
+// TransformerEngine issue #1583, C++ listing: on the receive stream, each ring step copies one
+// chunk into the gathered buffer and then marks it ready with a per-chunk counter ("producer");
+// the listing's multi-atomic variant does all steps in one launch.  This kernel is that one-launch
+// form: its workgroups copy the chunks one after another in ring order, each workgroup taking a
+// contiguous slice of every chunk; the last workgroup to finish a chunk (a self-resetting ticket)
+// releases the chunk's counter with the call's epoch, so tiles of that chunk can start while the
+// next chunk is still being copied.  It needs no LDS and few registers, so its waves fit beside
+// the GEMM's on every compute unit.
+#include <hip/hip_runtime.h>
+
+#include "kernels.hpp"
+
+namespace ringag {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kArrThreads = 256;
+constexpr int kArrUnroll = 8;
+
+__global__ void __launch_bounds__(kArrThreads) arrival_kernel(ArrivalArgs a) {
+  const unsigned long long nvec = a.bytes / 16;
+  const unsigned long long per = (nvec + gridDim.x - 1) / gridDim.x;
+  const unsigned long long beg = min(nvec, (unsigned long long)blockIdx.x * per);
+  const unsigned long long end = min(nvec, beg + per);
+  for (int j = 0; j < a.n; ++j) {
+    const v4i* src = (const v4i*)a.src[j];
+    v4i* dst = (v4i*)a.dst[j];
+    unsigned long long i = beg + threadIdx.x;
+    for (; i + (kArrUnroll - 1) * kArrThreads < end; i += kArrUnroll * kArrThreads) {
+      v4i v[kArrUnroll];
+#pragma unroll
+      for (int u = 0; u < kArrUnroll; ++u) v[u] = src[i + u * kArrThreads];
+#pragma unroll
+      for (int u = 0; u < kArrUnroll; ++u) dst[i + u * kArrThreads] = v[u];
+    }
+    for (; i < end; i += kArrThreads) dst[i] = src[i];
+
+    if (a.ctr_index[j] >= 0) {
+      __threadfence();          // this thread's stores are visible device-wide
+      __syncthreads();          // ... for every thread of the workgroup
+      if (threadIdx.x == 0) {
+        const int old = __hip_atomic_fetch_add(a.ticket + j, 1, __ATOMIC_ACQ_REL,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        if (old == (int)gridDim.x - 1) {
+          __hip_atomic_store(a.ticket + j, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (a.delay_ticks > 0) {
+            const unsigned long long t0 = wall_clock64();
+            while ((long long)(wall_clock64() - t0) < a.delay_ticks) __builtin_amdgcn_s_sleep(8);
+          }
+          if (!((a.withhold_mask >> a.pos[j]) & 1u))
+            __hip_atomic_store(a.ctr + a.ctr_index[j], a.epoch, __ATOMIC_RELEASE,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_arrival(const ArrivalArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(arrival_kernel, dim3(grid), dim3(kArrThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t arrival_kernel_info(KernelInfo* info) {
+  hipFuncAttributes at;
+  hipError_t e = hipFuncGetAttributes(&at, (const void*)arrival_kernel);
+  if (e != hipSuccess) return e;
+  info->threads = kArrThreads;
+  info->lds_bytes = (int)at.sharedSizeBytes;
+  info->vgprs_per_wave = at.numRegs;
+  info->max_blocks_per_cu = 0;
+  return hipSuccess;
+}
+
+}  // namespace ringag

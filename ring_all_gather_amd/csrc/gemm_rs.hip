@@ -1,0 +1,137 @@
+// GEMM + reduce-scatter kernel (row-parallel linear, one rank's share).
+//
+// TransformerEngine PR #2443, sequence diagram: the RS path splits the GEMM and reduce-scatters
+// its output; review comments: the contraction dimension of that GEMM is the local shard of a
+// global k.  nvFuser PR #5742, walkthrough: each chunk of the output is summed over ranks.
+//
+// The rank computes its whole partial P = X W^T, chunk by chunk in ring order (the rank's own
+// chunk last, as in a ring reduce-scatter where the own chunk's sum completes last).  Tiles of
+// another rank's chunk store their fp32 accumulators to `send` (the outgoing contribution).
+// Tiles of the own chunk add the peers' fp32 partials to the accumulators while they are still in
+// registers and store the bf16 result: the reduction costs no extra pass over D.
+#include "gemm_core.hpp"
+#include "kernels.hpp"
+
+namespace ringag {
+
+__device__ inline void map_tile_rs(int u, int U, int R, int* rb, int* cb) {
+  int v = u;
+  if ((U & 7) == 0) v = (u & 7) * (U >> 3) + (u >> 3);
+  *rb = v % R;
+  *cb = v / R;
+}
+
+template <int BI, int BJ>
+__global__ void __launch_bounds__(kThreads) gemm_rs_kernel(RsArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds[2 * (BI + BJ) * kRowBytes];
+  constexpr int FI = BI / 64, FJ = BJ / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wi = wave >> 1, wj = wave & 1;
+  const uint32_t ldb = (uint32_t)a.Kl * 2u;
+  const int ksteps = (int)(ldb / kRowBytes);
+  const int U = a.tiles_i * a.tiles_j;
+  const int total = U * a.tp;
+  const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.W, (uint32_t)a.Mo * ldb);
+
+  for (int t = blockIdx.x; t < total; t += gridDim.x) {
+    const int j = t / U;
+    const int u = t - j * U;
+    const int c = a.chunk_of[j];
+    const bool own = (c == a.self_rank);
+    if (!own && a.send == nullptr) continue;
+    int rb, cb;
+    map_tile_rs(u, U, a.tiles_i, &rb, &cb);
+    const char* xbase = (const char*)a.X + (size_t)c * a.nc * ldb;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(xbase, (uint32_t)a.nc * ldb);
+    uint32_t xo[BI / 32], yo[BJ / 32];
+    tile_offsets<BI>(xo, rb * BI, a.nc, ldb, wave, lane);
+    tile_offsets<BJ>(yo, cb * BJ, a.Mo, ldb, wave, lane);
+    f32x16 acc[FI][FJ];
+    tile_kloop<BI, BJ, false>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);
+
+    const int row0 = rb * BI + wi * (BI / 2);
+    const int col0 = cb * BJ + wj * (BJ / 2);
+    if (!own) {
+      float* out = a.send + (size_t)c * a.nc * a.Mo;
+#pragma unroll
+      for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int jj = 0; jj < FJ; ++jj) {
+          const int col = col0 + acc_col(jj, lane);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int row = row0 + acc_row(i, e, lane);
+            if (row < a.nc && col < a.Mo) out[(size_t)row * a.Mo + col] = acc[i][jj][e];
+          }
+        }
+    } else {
+      // Own chunk: add every peer's partial to the accumulators (one fragment at a time, so only
+      // 16 extra registers are live), then round to bf16 and store.
+      __bf16* out = (__bf16*)a.D;
+      const size_t prow0 = (size_t)a.self_rank * a.nc;
+#pragma unroll
+      for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int jj = 0; jj < FJ; ++jj) {
+          const int col = col0 + acc_col(jj, lane);
+          float v[16];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) v[e] = acc[i][jj][e];
+          for (int p = 0; p < a.tp; ++p) {
+            if (p == a.self_rank) continue;
+            const float* part = a.partial[p] + prow0 * (size_t)a.ldp;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int row = row0 + acc_row(i, e, lane);
+              if (row < a.nc && col < a.Mo) v[e] += part[(size_t)row * a.ldp + col];
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int row = row0 + acc_row(i, e, lane);
+            if (row < a.nc && col < a.Mo) out[(size_t)row * a.Mo + col] = (__bf16)v[e];
+          }
+        }
+    }
+  }
+}
+
+template <int BI, int BJ>
+static hipError_t launch_t(const RsArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_rs_kernel<BI, BJ>), dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int BI, int BJ>
+static hipError_t info_t(KernelInfo* info) {
+  hipFuncAttributes at;
+  hipError_t e = hipFuncGetAttributes(&at, (const void*)gemm_rs_kernel<BI, BJ>);
+  if (e != hipSuccess) return e;
+  int nb = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, gemm_rs_kernel<BI, BJ>, kThreads, 0);
+  if (e != hipSuccess) return e;
+  info->threads = kThreads;
+  info->lds_bytes = (int)at.sharedSizeBytes;
+  info->vgprs_per_wave = at.numRegs;
+  info->max_blocks_per_cu = nb;
+  return hipSuccess;
+}
+
+hipError_t launch_gemm_rs(const RsArgs& a, int tile, int grid, hipStream_t s) {
+  switch (tile) {
+    case kTile256x256: return launch_t<256, 256>(a, grid, s);
+    case kTile256x128: return launch_t<256, 128>(a, grid, s);
+    default: return launch_t<128, 128>(a, grid, s);
+  }
+}
+
+hipError_t rs_kernel_info(int tile, KernelInfo* info) {
+  switch (tile) {
+    case kTile256x256: return info_t<256, 256>(info);
+    case kTile256x128: return info_t<256, 128>(info);
+    default: return info_t<128, 128>(info);
+  }
+}
+
+}  // namespace ringag

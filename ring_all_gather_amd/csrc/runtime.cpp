@@ -1,0 +1,615 @@
+// Host runtime of libringag.so: the C ABI declared in include/ringag.h.
+//
+// It owns the per-context resources (side stream, fork/join events, ready counters, tickets, error
+// word, epoch, cached gather and staging buffers), validates every argument before enqueueing
+// anything, and orders the work of one call:
+//
+//   caller stream:  [record fork] ...................... GEMM (tiles wait on counters) [wait join]
+//   side stream:        [wait fork] arrivals: copy chunk r_1, bump ctr[r_1]; copy r_2, bump ... [record join]
+//
+// The arrivals are enqueued before the GEMM (nvFuser PR #3392, experiment: posting communication
+// before compute gave near-complete overlap), and the side stream is joined back into the caller's
+// stream before the call returns (TransformerEngine issue #1583, C++ listing: communication
+// streams fork from and join the main stream through events).  Counters are compared with a
+// per-call epoch instead of being reset by a kernel, so a late producer of one call can never be
+// mistaken for the next call's.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "ringag.h"
+#include "kernels.hpp"
+
+using namespace ringag;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[1024];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+#define HIPCHK(call)                                                                   \
+  do {                                                                                 \
+    hipError_t e_ = (call);                                                            \
+    if (e_ != hipSuccess)                                                              \
+      return fail(RAG_EHIP, "%s failed: %s (%s:%d)", #call, hipGetErrorString(e_),     \
+                  __FILE__, __LINE__);                                                 \
+  } while (0)
+
+constexpr long long kMaxOperandBytes = 0x7fffffffLL;   // buffer descriptors address < 2 GiB
+constexpr int kTimingSlots = 4096;
+
+bool debug_enabled() {
+  const char* v = getenv("RAG_DEBUG");
+  return v && v[0] && v[0] != '0';
+}
+
+}  // namespace
+
+struct rag_ctx {
+  int device = 0;
+  int max_tp = 0;
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  int* words = nullptr;   // ctr[max_tp] | ticket[max_tp + 2] | err
+  int* ctr = nullptr;
+  int* ticket = nullptr;
+  int* err = nullptr;
+  int epoch = 0;
+  void* gbuf = nullptr;
+  size_t gbuf_bytes = 0;
+  void* stage = nullptr;
+  size_t stage_bytes = 0;
+  int num_cus = 0;
+  long long wall_khz = 100000;
+  // options
+  int copy_engine = 0;
+  int comm_wgs = 32;
+  long long spin_us = 2000000;
+  long long delay_us = 0;
+  unsigned withhold = 0;
+  int tile = RAG_TILE_AUTO;
+  bool timing = false;
+  std::vector<hipEvent_t> t_start, t_stop;
+  int n_timed = 0;
+  // occupancy cache: [tile][fp8]
+  KernelInfo ag_info[4][2] = {};
+  bool ag_info_ok[4][2] = {};
+  KernelInfo rs_info[4] = {};
+  bool rs_info_ok[4] = {};
+};
+
+namespace {
+
+int ensure_buffer(void** p, size_t* have, size_t need, const char* what) {
+  if (*have >= need) return RAG_OK;
+  if (*p) {
+    hipError_t e = hipFree(*p);
+    if (e != hipSuccess) return fail(RAG_EHIP, "hipFree(%s) failed: %s", what, hipGetErrorString(e));
+    *p = nullptr;
+    *have = 0;
+  }
+  hipError_t e = hipMalloc(p, need);
+  if (e != hipSuccess) {
+    *p = nullptr;
+    (void)hipGetLastError();
+    return fail(RAG_ENOMEM, "cannot allocate the %s (%zu bytes): %s", what, need,
+                hipGetErrorString(e));
+  }
+  *have = need;
+  return RAG_OK;
+}
+
+// True when p is device memory of `device` (hipMalloc'd, or managed).  Host pointers, pointers
+// of another device and unknown addresses are rejected before anything reaches a kernel.
+bool on_device(const void* p, int device) {
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged) && at.device == device;
+}
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || !na || !nb) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+int next_epoch(rag_ctx* c) {
+  c->epoch = (c->epoch == 0x7fffffff) ? 1 : c->epoch + 1;
+  return c->epoch;
+}
+
+int choose_ag_tile(const rag_ctx* c, int nc, int M) {
+  if (c->tile != RAG_TILE_AUTO) return c->tile;
+  if (nc >= 256 && M >= 128) return kTile256x128;
+  return kTile128x128;
+}
+
+// Compute units kept free of GEMM workgroups while arrivals run.  The 256x256 tile uses every
+// vector register of its SIMDs (512 per lane), so no wave of the copy kernel could share a CU
+// with it; with one such workgroup per CU (its LDS allows no second), leaving 8 CUs without one
+// guarantees the copy kernel a place to run while GEMM tiles wait for its chunks.
+int reserved_cus(int tile, bool arrivals) {
+  return (arrivals && tile == kTile256x256) ? 8 : 0;
+}
+
+int choose_rs_tile(const rag_ctx* c, int nc, int Mo) {
+  if (c->tile != RAG_TILE_AUTO) return c->tile;
+  if (nc >= 256 && Mo >= 256) return kTile256x256;
+  return kTile128x128;
+}
+
+// Persistent grid: every workgroup resident at once (so none waits for a slot while others spin
+// on counters), a multiple of 8 so that tile t always runs on XCD t % 8.
+int persistent_grid(int total_tiles, int num_cus, int blocks_per_cu) {
+  int cap = num_cus * std::max(1, blocks_per_cu);
+  int g = std::min(total_tiles, cap);
+  if (g >= 8) g -= g % 8;
+  return std::max(1, g);
+}
+
+int record_timing_start(rag_ctx* c, hipStream_t s, bool* recorded) {
+  *recorded = false;
+  if (!c->timing || c->n_timed >= (int)c->t_start.size()) return RAG_OK;
+  HIPCHK(hipEventRecord(c->t_start[c->n_timed], s));
+  *recorded = true;
+  return RAG_OK;
+}
+
+int record_timing_stop(rag_ctx* c, hipStream_t s, bool recorded) {
+  if (!recorded) return RAG_OK;
+  HIPCHK(hipEventRecord(c->t_stop[c->n_timed], s));
+  c->n_timed++;
+  return RAG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rag_version(void) { return 100; }
+
+const char* rag_last_error(void) { return g_last_error.c_str(); }
+
+int rag_create(rag_ctx** out, int device, int max_tp, int flags) {
+  if (!out) return fail(RAG_EINVAL, "rag_create: out is NULL");
+  *out = nullptr;
+  if (max_tp < 1 || max_tp > RAG_MAX_TP)
+    return fail(RAG_EINVAL, "rag_create: max_tp=%d outside [1, %d]", max_tp, RAG_MAX_TP);
+  if (flags != 0) return fail(RAG_EINVAL, "rag_create: flags must be 0 (got %d)", flags);
+  int ndev = 0;
+  HIPCHK(hipGetDeviceCount(&ndev));
+  if (device < 0 || device >= ndev)
+    return fail(RAG_EINVAL, "rag_create: device %d outside [0, %d)", device, ndev);
+  HIPCHK(hipSetDevice(device));
+  hipDeviceProp_t prop;
+  HIPCHK(hipGetDeviceProperties(&prop, device));
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(RAG_EINVAL, "rag_create: device %d is %s; this library is built for gfx950",
+                device, prop.gcnArchName);
+  rag_ctx* c = new rag_ctx();
+  c->device = device;
+  c->max_tp = max_tp;
+  c->num_cus = prop.multiProcessorCount;
+  int khz = 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, device) == hipSuccess && khz > 0)
+    c->wall_khz = khz;
+  const size_t nwords = (size_t)max_tp + (size_t)max_tp + 2 + 1;
+  hipError_t e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipMalloc((void**)&c->words, nwords * sizeof(int));
+  if (e == hipSuccess) e = hipMemset(c->words, 0, nwords * sizeof(int));
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    std::string msg = std::string("rag_create: ") + hipGetErrorString(e);
+    rag_destroy(c);
+    return fail(RAG_EHIP, "%s", msg.c_str());
+  }
+  c->ctr = c->words;
+  c->ticket = c->words + max_tp;
+  c->err = c->words + 2 * max_tp + 2;
+  *out = c;
+  if (debug_enabled())
+    fprintf(stderr, "[ringag] context on device %d (%s, %d CUs, wall clock %lld kHz), max_tp %d\n",
+            device, prop.gcnArchName, c->num_cus, c->wall_khz, max_tp);
+  return RAG_OK;
+}
+
+int rag_destroy(rag_ctx* c) {
+  if (!c) return RAG_OK;
+  (void)hipSetDevice(c->device);
+  if (c->side) (void)hipStreamSynchronize(c->side);
+  for (auto ev : c->t_start) (void)hipEventDestroy(ev);
+  for (auto ev : c->t_stop) (void)hipEventDestroy(ev);
+  if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
+  if (c->ev_join) (void)hipEventDestroy(c->ev_join);
+  if (c->side) (void)hipStreamDestroy(c->side);
+  if (c->words) (void)hipFree(c->words);
+  if (c->gbuf) (void)hipFree(c->gbuf);
+  if (c->stage) (void)hipFree(c->stage);
+  delete c;
+  return RAG_OK;
+}
+
+int rag_set_option(rag_ctx* c, int key, long long v) {
+  if (!c) return fail(RAG_EINVAL, "rag_set_option: ctx is NULL");
+  switch (key) {
+    case RAG_OPT_COPY_ENGINE:
+      if (v != 0 && v != 1) return fail(RAG_EINVAL, "copy engine must be 0 (kernel) or 1 (sdma)");
+      c->copy_engine = (int)v;
+      return RAG_OK;
+    case RAG_OPT_COMM_WGS:
+      if (v < 1 || v > 1024) return fail(RAG_EINVAL, "comm workgroups must be in [1, 1024]");
+      c->comm_wgs = (int)v;
+      return RAG_OK;
+    case RAG_OPT_SPIN_LIMIT_US:
+      if (v < 1 || v > 60000000LL) return fail(RAG_EINVAL, "spin limit must be in [1, 6e7] us");
+      c->spin_us = v;
+      return RAG_OK;
+    case RAG_OPT_ARRIVAL_DELAY_US:
+      if (v < 0 || v > 1000000LL) return fail(RAG_EINVAL, "arrival delay must be in [0, 1e6] us");
+      c->delay_us = v;
+      return RAG_OK;
+    case RAG_OPT_WITHHOLD_MASK:
+      if (v < 0 || v > 0xffffLL) return fail(RAG_EINVAL, "withhold mask must fit in 16 bits");
+      c->withhold = (unsigned)v;
+      return RAG_OK;
+    case RAG_OPT_TIMING:
+      if (v != 0 && v != 1) return fail(RAG_EINVAL, "timing must be 0 or 1");
+      if (v && c->t_start.empty()) {
+        HIPCHK(hipSetDevice(c->device));
+        c->t_start.resize(kTimingSlots);
+        c->t_stop.resize(kTimingSlots);
+        for (int i = 0; i < kTimingSlots; ++i) {
+          HIPCHK(hipEventCreate(&c->t_start[i]));
+          HIPCHK(hipEventCreate(&c->t_stop[i]));
+        }
+      }
+      c->timing = v != 0;
+      return RAG_OK;
+    case RAG_OPT_TILE:
+      if (v < RAG_TILE_AUTO || v > RAG_TILE_256x256) return fail(RAG_EINVAL, "unknown tile %lld", v);
+      c->tile = (int)v;
+      return RAG_OK;
+    default:
+      return fail(RAG_EINVAL, "rag_set_option: unknown key %d", key);
+  }
+}
+
+int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int nc, int tp,
+            int self_rank, void* G, void* D, rag_dtype dt, const float* scale_A,
+            const float* scale_B, int flags, void* stream_v) {
+  if (!c) return fail(RAG_EINVAL, "ag_gemm: ctx is NULL");
+  if (tp < 1 || tp > c->max_tp)
+    return fail(RAG_EINVAL, "ag_gemm: tp=%d outside [1, %d] (max_tp of the context)", tp, c->max_tp);
+  if (self_rank < 0 || self_rank >= tp)
+    return fail(RAG_EINVAL, "ag_gemm: self_rank=%d outside [0, tp=%d)", self_rank, tp);
+  if (dt != RAG_BF16 && dt != RAG_FP8_E4M3) return fail(RAG_EINVAL, "ag_gemm: unknown dtype %d", dt);
+  const bool fp8 = dt == RAG_FP8_E4M3;
+  const int esz = fp8 ? 1 : 2;
+  const int kmul = fp8 ? 128 : 64;
+  if (M < 1 || nc < 1 || K < 1)
+    return fail(RAG_EINVAL, "ag_gemm: M=%d, K=%d, nc=%d must all be >= 1", M, K, nc);
+  if (K % kmul)
+    return fail(RAG_EINVAL, "ag_gemm: K=%d must be a multiple of %d for %s", K, kmul,
+                fp8 ? "fp8" : "bf16");
+  if (flags & ~(RAG_STAGED_OUT | RAG_NO_COPY | RAG_COPY_ONLY))
+    return fail(RAG_EINVAL, "ag_gemm: unknown flag bits 0x%x", flags);
+  if ((flags & RAG_NO_COPY) && (flags & RAG_COPY_ONLY))
+    return fail(RAG_EINVAL, "ag_gemm: RAG_NO_COPY and RAG_COPY_ONLY exclude each other");
+  if (!A || !B || !D) return fail(RAG_EINVAL, "ag_gemm: A, B_chunks and D must not be NULL");
+  for (int r = 0; r < tp; ++r) {
+    if (!B[r]) return fail(RAG_EINVAL, "ag_gemm: B_chunks[%d] is NULL", r);
+    if (misaligned(B[r])) return fail(RAG_EINVAL, "ag_gemm: B_chunks[%d] is not 16-byte aligned", r);
+  }
+  if (misaligned(A) || misaligned(D) || (G && misaligned(G)))
+    return fail(RAG_EINVAL, "ag_gemm: A, G and D must be 16-byte aligned");
+  if (fp8 && (!scale_A || !scale_B))
+    return fail(RAG_EINVAL, "ag_gemm: fp8 needs scale_A and scale_B");
+  if (!fp8 && (scale_A || scale_B))
+    return fail(RAG_EINVAL, "ag_gemm: scales are only meaningful for fp8; pass NULL for bf16");
+  {
+    HIPCHK(hipSetDevice(c->device));
+    const void* named[] = {A, D, G, scale_A, scale_B};
+    const char* names[] = {"A", "D", "G", "scale_A", "scale_B"};
+    for (int i = 0; i < 5; ++i)
+      if (named[i] && !on_device(named[i], c->device))
+        return fail(RAG_EINVAL, "ag_gemm: %s is not device memory of device %d", names[i],
+                    c->device);
+    for (int r = 0; r < tp; ++r)
+      if (!on_device(B[r], c->device))
+        return fail(RAG_EINVAL, "ag_gemm: B_chunks[%d] is not device memory of device %d", r,
+                    c->device);
+  }
+  const long long a_bytes = (long long)M * K * esz;
+  const long long chunk_bytes = (long long)nc * K * esz;
+  const long long g_bytes = chunk_bytes * tp;
+  const long long d_bytes = (long long)tp * nc * M * 2;
+  if (a_bytes > kMaxOperandBytes || chunk_bytes > kMaxOperandBytes)
+    return fail(RAG_EINVAL, "ag_gemm: the weight (%lld B) and each chunk (%lld B) must be < 2 GiB",
+                a_bytes, chunk_bytes);
+  if (overlaps(D, d_bytes, A, a_bytes) || (G && overlaps(G, g_bytes, A, a_bytes)) ||
+      (G && overlaps(G, g_bytes, D, d_bytes)))
+    return fail(RAG_EINVAL, "ag_gemm: G and D must not overlap A or each other");
+  for (int r = 0; r < tp; ++r)
+    if (overlaps(D, d_bytes, B[r], chunk_bytes) ||
+        (G && r != self_rank && overlaps(G, g_bytes, B[r], chunk_bytes)))
+      return fail(RAG_EINVAL, "ag_gemm: G and D must not overlap B_chunks[%d]", r);
+  if (G && overlaps(G, g_bytes, B[self_rank], chunk_bytes) &&
+      (const char*)B[self_rank] != (const char*)G + (size_t)self_rank * chunk_bytes)
+    return fail(RAG_EINVAL, "ag_gemm: the own chunk may only sit in G at its own slot");
+  if ((flags & RAG_NO_COPY) && !G && !c->gbuf)
+    return fail(RAG_EINVAL, "ag_gemm: RAG_NO_COPY reads the chunks from G; pass G");
+  if (c->copy_engine == 1 && c->delay_us > 0 && !(flags & RAG_NO_COPY))
+    return fail(RAG_EINVAL, "ag_gemm: the arrival delay hook needs the kernel copy engine");
+
+  HIPCHK(hipSetDevice(c->device));
+  hipStream_t stream = (hipStream_t)stream_v;
+  const bool staged = (flags & RAG_STAGED_OUT) != 0;
+  const bool no_copy = (flags & RAG_NO_COPY) != 0;
+  const bool copy_only = (flags & RAG_COPY_ONLY) != 0;
+
+  char* Gp = (char*)G;
+  if (!Gp) {
+    int rc = ensure_buffer(&c->gbuf, &c->gbuf_bytes, (size_t)g_bytes, "gather buffer");
+    if (rc) return rc;
+    Gp = (char*)c->gbuf;
+  }
+  if (staged && !copy_only) {
+    int rc = ensure_buffer(&c->stage, &c->stage_bytes, (size_t)(tp + 1) * nc * M * 2,
+                           "staging buffer");
+    if (rc) return rc;
+  }
+  const int epoch = next_epoch(c);
+  int order[kMaxTp];
+  for (int j = 0; j < tp; ++j) order[j] = ((self_rank - j) % tp + tp) % tp;
+
+  if (!no_copy) {
+    HIPCHK(hipEventRecord(c->ev_fork, stream));
+    HIPCHK(hipStreamWaitEvent(c->side, c->ev_fork, 0));
+    if (c->copy_engine == 0) {
+      ArrivalArgs aa = {};
+      int n = 0;
+      for (int j = 1; j < tp; ++j, ++n) {
+        const int r = order[j];
+        aa.src[n] = B[r];
+        aa.dst[n] = Gp + (size_t)r * chunk_bytes;
+        aa.ctr_index[n] = r;
+        aa.pos[n] = j;
+      }
+      if (G && (const char*)B[self_rank] != Gp + (size_t)self_rank * chunk_bytes) {
+        aa.src[n] = B[self_rank];
+        aa.dst[n] = Gp + (size_t)self_rank * chunk_bytes;
+        aa.ctr_index[n] = -1;
+        aa.pos[n] = 0;
+        ++n;
+      }
+      aa.n = n;
+      aa.bytes = (unsigned long long)chunk_bytes;
+      aa.ctr = c->ctr;
+      aa.ticket = c->ticket;
+      aa.epoch = epoch;
+      aa.delay_ticks = c->delay_us * c->wall_khz / 1000;
+      aa.withhold_mask = c->withhold;
+      if (n > 0) HIPCHK(launch_arrival(aa, c->comm_wgs, c->side));
+    } else {
+      for (int j = 1; j < tp; ++j) {
+        const int r = order[j];
+        HIPCHK(hipMemcpyAsync(Gp + (size_t)r * chunk_bytes, B[r], (size_t)chunk_bytes,
+                              hipMemcpyDeviceToDeviceNoCU, c->side));
+        if (!((c->withhold >> j) & 1u))
+          HIPCHK(hipStreamWriteValue32(c->side, c->ctr + r, (uint32_t)epoch, 0));
+      }
+      if (G && (const char*)B[self_rank] != Gp + (size_t)self_rank * chunk_bytes)
+        HIPCHK(hipMemcpyAsync(Gp + (size_t)self_rank * chunk_bytes, B[self_rank],
+                              (size_t)chunk_bytes, hipMemcpyDeviceToDeviceNoCU, c->side));
+    }
+    HIPCHK(hipEventRecord(c->ev_join, c->side));
+  }
+
+  if (!copy_only) {
+    AgArgs a = {};
+    for (int j = 0; j < tp; ++j) {
+      const int r = order[j];
+      a.chunk[j] = (j == 0) ? B[self_rank] : (const void*)(Gp + (size_t)r * chunk_bytes);
+      a.ctr_index[j] = (j == 0 || no_copy) ? -1 : r;
+      a.out[j] = staged ? (void*)((char*)c->stage + (size_t)j * nc * M * 2)
+                        : (void*)((char*)D + (size_t)r * nc * M * 2);
+    }
+    a.A = A;
+    a.M = M;
+    a.K = K;
+    a.nc = nc;
+    a.tp = tp;
+    a.ctr = c->ctr;
+    a.epoch = epoch;
+    a.err = c->err;
+    a.spin_limit = c->spin_us * c->wall_khz / 1000;
+    a.scale_A = scale_A;
+    a.scale_B = scale_B;
+    const int tile = choose_ag_tile(c, nc, M);
+    int bi, bj;
+    tile_dims(tile, &bi, &bj);
+    a.tiles_i = (nc + bi - 1) / bi;
+    a.tiles_j = (M + bj - 1) / bj;
+    if (!c->ag_info_ok[tile][fp8]) {
+      HIPCHK(ag_kernel_info(tile, fp8, &c->ag_info[tile][fp8]));
+      c->ag_info_ok[tile][fp8] = true;
+    }
+    const int total = a.tiles_i * a.tiles_j * tp;
+    const int grid = persistent_grid(total, c->num_cus - reserved_cus(tile, !no_copy),
+                                     c->ag_info[tile][fp8].max_blocks_per_cu);
+    if (debug_enabled())
+      fprintf(stderr, "[ringag] ag_gemm tp=%d s=%d nc=%d K=%d M=%d %s tile=%dx%d tiles=%d grid=%d "
+              "(blocks/CU %d, VGPRs %d, LDS %d) engine=%s comm_wgs=%d flags=0x%x epoch=%d\n",
+              tp, self_rank, nc, K, M, fp8 ? "fp8" : "bf16", bi, bj, total, grid,
+              c->ag_info[tile][fp8].max_blocks_per_cu, c->ag_info[tile][fp8].vgprs_per_wave,
+              c->ag_info[tile][fp8].lds_bytes, c->copy_engine ? "sdma" : "kernel", c->comm_wgs,
+              flags, epoch);
+    bool rec = false;
+    int rc = record_timing_start(c, stream, &rec);
+    if (rc) return rc;
+    HIPCHK(launch_ag_gemm(a, tile, fp8, grid, stream));
+    rc = record_timing_stop(c, stream, rec);
+    if (rc) return rc;
+  }
+  if (!no_copy) HIPCHK(hipStreamWaitEvent(stream, c->ev_join, 0));
+
+  if (staged && !copy_only) {
+    const size_t dchunk = (size_t)nc * M * 2;
+    char* st = (char*)c->stage;
+    bool rotation = true;   // slot j holds chunk j-1 and slot 0 chunk tp-1
+    for (int j = 0; j < tp; ++j)
+      if (order[j] != (j + tp - 1) % tp) rotation = false;
+    if (rotation) {
+      // the listing's two copies: first chunk to the spare slot, then slots 1..tp are D
+      HIPCHK(hipMemcpyAsync(st + (size_t)tp * dchunk, st, dchunk, hipMemcpyDeviceToDevice, stream));
+      HIPCHK(hipMemcpyAsync(D, st + dchunk, (size_t)tp * dchunk, hipMemcpyDeviceToDevice, stream));
+    } else {
+      for (int j = 0; j < tp; ++j)
+        HIPCHK(hipMemcpyAsync((char*)D + (size_t)order[j] * dchunk, st + (size_t)j * dchunk,
+                              dchunk, hipMemcpyDeviceToDevice, stream));
+    }
+  }
+  return RAG_OK;
+}
+
+int gemm_rs(rag_ctx* c, const void* X, int T, int Kl, const void* W, int Mo,
+            const float* const* partials, long long ldp, int tp, int self_rank, float* send,
+            void* D, int flags, void* stream_v) {
+  if (!c) return fail(RAG_EINVAL, "gemm_rs: ctx is NULL");
+  if (tp < 1 || tp > c->max_tp)
+    return fail(RAG_EINVAL, "gemm_rs: tp=%d outside [1, %d] (max_tp of the context)", tp, c->max_tp);
+  if (self_rank < 0 || self_rank >= tp)
+    return fail(RAG_EINVAL, "gemm_rs: self_rank=%d outside [0, tp=%d)", self_rank, tp);
+  if (T < 1 || Kl < 1 || Mo < 1)
+    return fail(RAG_EINVAL, "gemm_rs: T=%d, Kl=%d, Mo=%d must all be >= 1", T, Kl, Mo);
+  if (T % tp) return fail(RAG_EINVAL, "gemm_rs: T=%d is not a multiple of tp=%d", T, tp);
+  if (Kl % 64) return fail(RAG_EINVAL, "gemm_rs: Kl=%d must be a multiple of 64", Kl);
+  if (flags != 0) return fail(RAG_EINVAL, "gemm_rs: flags must be 0 (got 0x%x)", flags);
+  if (!X || !W || !D) return fail(RAG_EINVAL, "gemm_rs: X, W and D must not be NULL");
+  if (tp > 1 && !partials) return fail(RAG_EINVAL, "gemm_rs: partials must not be NULL for tp > 1");
+  if (ldp < Mo) return fail(RAG_EINVAL, "gemm_rs: ldp=%lld must be >= Mo=%d", ldp, Mo);
+  if (misaligned(X) || misaligned(W) || misaligned(D) || (send && misaligned(send)))
+    return fail(RAG_EINVAL, "gemm_rs: X, W, send and D must be 16-byte aligned");
+  {
+    HIPCHK(hipSetDevice(c->device));
+    const void* named[] = {X, W, D, send};
+    const char* names[] = {"X", "W", "D", "send"};
+    for (int i = 0; i < 4; ++i)
+      if (named[i] && !on_device(named[i], c->device))
+        return fail(RAG_EINVAL, "gemm_rs: %s is not device memory of device %d", names[i],
+                    c->device);
+    for (int p = 0; p < tp; ++p)
+      if (p != self_rank && partials && partials[p] && !on_device(partials[p], c->device))
+        return fail(RAG_EINVAL, "gemm_rs: partials[%d] is not device memory of device %d", p,
+                    c->device);
+  }
+  const int nc = T / tp;
+  const long long x_bytes = (long long)T * Kl * 2, w_bytes = (long long)Mo * Kl * 2;
+  if (x_bytes > kMaxOperandBytes || w_bytes > kMaxOperandBytes)
+    return fail(RAG_EINVAL, "gemm_rs: X (%lld B) and W (%lld B) must be < 2 GiB", x_bytes, w_bytes);
+  const long long d_bytes = (long long)nc * Mo * 2;
+  const long long send_bytes = (long long)tp * nc * Mo * 4;
+  for (int p = 0; p < tp; ++p) {
+    if (p == self_rank) continue;
+    if (!partials[p]) return fail(RAG_EINVAL, "gemm_rs: partials[%d] is NULL", p);
+    if ((reinterpret_cast<uintptr_t>(partials[p]) & 3u) != 0)
+      return fail(RAG_EINVAL, "gemm_rs: partials[%d] is not 4-byte aligned", p);
+    const long long pb = ((long long)(T - 1) * ldp + Mo) * 4;
+    if (overlaps(D, d_bytes, partials[p], pb) || (send && overlaps(send, send_bytes, partials[p], pb)))
+      return fail(RAG_EINVAL, "gemm_rs: D and send must not overlap partials[%d]", p);
+  }
+  if (overlaps(D, d_bytes, X, x_bytes) || overlaps(D, d_bytes, W, w_bytes) ||
+      (send && (overlaps(send, send_bytes, X, x_bytes) || overlaps(send, send_bytes, W, w_bytes) ||
+                overlaps(send, send_bytes, D, d_bytes))))
+    return fail(RAG_EINVAL, "gemm_rs: D and send must not overlap X, W or each other");
+
+  HIPCHK(hipSetDevice(c->device));
+  hipStream_t stream = (hipStream_t)stream_v;
+  RsArgs a = {};
+  a.X = X;
+  a.W = W;
+  for (int j = 0; j < tp; ++j) a.chunk_of[j] = (self_rank + 1 + j) % tp;
+  for (int p = 0; p < tp; ++p) a.partial[p] = (p == self_rank || !partials) ? nullptr : partials[p];
+  a.ldp = ldp;
+  a.send = send;
+  a.D = D;
+  a.T = T;
+  a.Kl = Kl;
+  a.Mo = Mo;
+  a.nc = nc;
+  a.tp = tp;
+  a.self_rank = self_rank;
+  const int tile = choose_rs_tile(c, nc, Mo);
+  int bi, bj;
+  tile_dims(tile, &bi, &bj);
+  a.tiles_i = (nc + bi - 1) / bi;
+  a.tiles_j = (Mo + bj - 1) / bj;
+  if (!c->rs_info_ok[tile]) {
+    HIPCHK(rs_kernel_info(tile, &c->rs_info[tile]));
+    c->rs_info_ok[tile] = true;
+  }
+  const int total = a.tiles_i * a.tiles_j * tp;
+  const int grid = persistent_grid(total, c->num_cus, c->rs_info[tile].max_blocks_per_cu);
+  if (debug_enabled())
+    fprintf(stderr, "[ringag] gemm_rs tp=%d s=%d T=%d Kl=%d Mo=%d tile=%dx%d tiles=%d grid=%d\n",
+            tp, self_rank, T, Kl, Mo, bi, bj, total, grid);
+  bool rec = false;
+  int rc = record_timing_start(c, stream, &rec);
+  if (rc) return rc;
+  HIPCHK(launch_gemm_rs(a, tile, grid, stream));
+  return record_timing_stop(c, stream, rec);
+}
+
+int rag_check(rag_ctx* c) {
+  if (!c) return fail(RAG_EINVAL, "rag_check: ctx is NULL");
+  HIPCHK(hipSetDevice(c->device));
+  HIPCHK(hipDeviceSynchronize());
+  int err = 0;
+  HIPCHK(hipMemcpy(&err, c->err, sizeof(int), hipMemcpyDeviceToHost));
+  if (err != 0) {
+    HIPCHK(hipMemset(c->err, 0, sizeof(int)));
+    HIPCHK(hipDeviceSynchronize());
+    return fail(RAG_ETIMEOUT, "a chunk did not arrive within the spin limit (%lld us) in the call "
+                "with epoch %d; its tiles were skipped", c->spin_us, err);
+  }
+  return RAG_OK;
+}
+
+int rag_kernel_times(rag_ctx* c, float* out, int max_n) {
+  if (!c) return fail(RAG_EINVAL, "rag_kernel_times: ctx is NULL");
+  if (max_n < 0 || (max_n > 0 && !out)) return fail(RAG_EINVAL, "rag_kernel_times: bad output");
+  HIPCHK(hipSetDevice(c->device));
+  const int n = c->n_timed;
+  for (int i = 0; i < n; ++i) {
+    HIPCHK(hipEventSynchronize(c->t_stop[i]));
+    float ms = 0.f;
+    HIPCHK(hipEventElapsedTime(&ms, c->t_start[i], c->t_stop[i]));
+    if (i < max_n) out[i] = ms;
+  }
+  c->n_timed = 0;
+  return n;
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+"""Argument validation of the C ABI with a real context (GPU): every bad argument is refused
+with RAG_EINVAL and a message, and nothing is enqueued."""
+import ctypes
+
+import pytest
+import torch
+
+from ring_all_gather_amd import binding as B
+
+from gpu_common import DEV, ctx, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _ag(c, A, M, K, chunks, nc, tp, s, G, D, dt=0, sa=None, sb=None, flags=0):
+    ptrs = (ctypes.c_void_p * max(len(chunks), 1))(*[ctypes.c_void_p(x) for x in chunks])
+    return B.lib().ag_gemm(c.h, A, M, K, ptrs, nc, tp, s, G, D, dt, sa, sb, flags, None)
+
+
+def test_ag_gemm_rejects_bad_arguments():
+    c = ctx()
+    say("case abi validation")
+    A = torch.zeros((64, 128), dtype=torch.bfloat16, device=DEV)
+    b = [torch.zeros((32, 128), dtype=torch.bfloat16, device=DEV) for _ in range(2)]
+    D = torch.zeros((64, 64), dtype=torch.bfloat16, device=DEV)
+    Ap, Dp = A.data_ptr(), D.data_ptr()
+    bp = [x.data_ptr() for x in b]
+    good = dict(A=Ap, M=64, K=128, chunks=bp, nc=32, tp=2, s=0, G=None, D=Dp)
+    assert _ag(c, **good) == B.RAG_OK
+    torch.cuda.synchronize()
+    bad = [
+        (dict(tp=0), "tp="), (dict(tp=17), "tp="), (dict(s=2), "self_rank"), (dict(s=-1), "self_rank"),
+        (dict(K=100), "multiple of 64"), (dict(M=0), ">= 1"), (dict(nc=0), ">= 1"),
+        (dict(A=None), "NULL"), (dict(D=None), "NULL"), (dict(A=Ap + 2), "aligned"),
+        (dict(D=Dp + 8), "aligned"), (dict(chunks=[bp[0], 0]), "B_chunks[1]"),
+        (dict(flags=8), "flag"), (dict(flags=B.RAG_NO_COPY | B.RAG_COPY_ONLY), "exclude"),
+        (dict(D=Ap), "overlap"), (dict(dt=5), "dtype"),
+    ]
+    for change, needle in bad:
+        args = dict(good)
+        args.update(change)
+        rc = _ag(c, **args)
+        assert rc == B.RAG_EINVAL, (change, rc)
+        assert needle in B.last_error(), (change, B.last_error())
+    # a host pointer must never reach a kernel
+    host = (ctypes.c_char * (64 * 128 * 2))()
+    args = dict(good, A=ctypes.addressof(host))
+    assert _ag(c, **args) == B.RAG_EINVAL
+    assert "device memory" in B.last_error()
+    # fp8 needs both scales, bf16 takes none
+    s = torch.ones(1, device=DEV)
+    assert _ag(c, **good, dt=1) == B.RAG_EINVAL
+    assert _ag(c, **good, sa=s.data_ptr(), sb=s.data_ptr()) == B.RAG_EINVAL
+    # tp above the context's max_tp
+    small = B.Context(0, max_tp=2)
+    assert _ag(small, **dict(good, tp=3, chunks=bp + [bp[0]])) == B.RAG_EINVAL
+    small.close()
+    torch.cuda.synchronize()
+
+
+def test_gemm_rs_rejects_bad_arguments():
+    c = ctx()
+    X = torch.zeros((64, 128), dtype=torch.bfloat16, device=DEV)
+    Wt = torch.zeros((48, 128), dtype=torch.bfloat16, device=DEV)
+    P = torch.zeros((64, 48), dtype=torch.float32, device=DEV)
+    D = torch.zeros((32, 48), dtype=torch.bfloat16, device=DEV)
+    parts = (ctypes.c_void_p * 2)(None, ctypes.c_void_p(P.data_ptr()))
+    L = B.lib()
+
+    def rs(T=64, Kl=128, Mo=48, ldp=48, tp=2, s=0, Dp=D.data_ptr(), flags=0, Xp=X.data_ptr()):
+        return L.gemm_rs(c.h, Xp, T, Kl, Wt.data_ptr(), Mo, parts, ldp, tp, s, None, Dp, flags,
+                         None)
+
+    assert rs() == B.RAG_OK
+    torch.cuda.synchronize()
+    for kw, needle in [(dict(T=63), "multiple of tp"), (dict(Kl=100), "multiple of 64"),
+                       (dict(ldp=40), "ldp"), (dict(s=2), "self_rank"), (dict(flags=1), "flags"),
+                       (dict(Dp=0), "NULL"), (dict(Dp=P.data_ptr()), "overlap"),
+                       (dict(Xp=X.data_ptr() + 4), "aligned")]:
+        assert rs(**kw) == B.RAG_EINVAL, kw
+        assert needle in B.last_error(), (kw, B.last_error())

@@ -1,0 +1,228 @@
+"""GPU parity of the AG+GEMM path (libringag.so through the C ABI) against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import ringag_oracle as O
+from ring_all_gather_amd import binding as B
+from ring_all_gather_amd import workloads as W
+
+from gpu_common import (AGRun, TOL_BF16, TOL_FP8, ctx, oracle_ag, oracle_ag_rows, rel_err,
+                        reset_options, sampled_rows, say)
+
+pytestmark = pytest.mark.gpu
+
+TILE_NAMES = ["128x128", "256x128", "256x256"]
+
+
+@pytest.fixture(autouse=True)
+def _fresh_options():
+    reset_options(ctx())
+    yield
+    reset_options(ctx())
+
+
+def test_ag_tiny_workload_full_parity():
+    shape = W.WORKLOADS["ag_tiny"]
+    say(f"case {shape}")
+    inp = W.make_ag(shape)
+    run = AGRun(inp).run(ctx())
+    G_ref, ref = oracle_ag(inp)
+    assert np.array_equal(W.bits_u16(run.G.cpu()), G_ref)
+    assert rel_err(run.D_bits(), ref) <= TOL_BF16
+
+
+def _int_case(tp, s, nc, K, M, seed, dtype="bf16"):
+    return W.make_ag(W.ag_shape(tp, s, nc, K, M, dtype=dtype, dist="int3", seed=seed))
+
+
+CASES = [(tp, s, nc) for tp in (1, 2, 3, 4, 8) for s in range(tp) for nc in (16, 48, 256)]
+
+
+@pytest.mark.parametrize("tp,s,nc", CASES)
+def test_ag_exact_integers_every_rank(tp, s, nc):
+    """Small integers are exact in bf16 and their fp32 sums are exact in any order, so D must be
+    the oracle's sum rounded to bf16, bit for bit; G must be the rank-ordered concatenation."""
+    c = ctx()
+    tile = TILE_NAMES[(tp + s + nc) % 3]
+    c.set_option(B.RAG_OPT_TILE, B.TILES[tile])
+    inp = _int_case(tp, s, nc, K=128, M=80, seed=tp * 100 + s * 10 + nc)
+    say(f"case tp={tp} s={s} nc={nc} K=128 M=80 tile={tile}")
+    run = AGRun(inp).run(c)
+    G_ref, ref = oracle_ag(inp)
+    assert np.array_equal(W.bits_u16(run.G.cpu()), G_ref)
+    assert np.array_equal(run.D_bits(), O.f32_to_bf16(ref))
+
+
+@pytest.mark.parametrize("tile", TILE_NAMES)
+def test_ag_ragged_tiles_random(tile):
+    """Chunk rows and output columns that are not multiples of any tile (several tiles plus a
+    ragged tail in both directions), normal data, every tile configuration."""
+    c = ctx()
+    c.set_option(B.RAG_OPT_TILE, B.TILES[tile])
+    shape = W.ag_shape(3, 2, 300, 320, 333, dist="normal_sqrtk", seed=5)
+    say(f"case {shape.name} tile={tile}")
+    inp = W.make_ag(shape)
+    run = AGRun(inp).run(c)
+    G_ref, ref = oracle_ag(inp)
+    assert np.array_equal(W.bits_u16(run.G.cpu()), G_ref)
+    assert rel_err(run.D_bits(), ref) <= TOL_BF16
+
+
+def test_ag_bitwise_invariant_across_ranks_and_modes():
+    """Chunking splits the gathered rows, not K: the result must not depend on the self rank,
+    on whether chunks arrive (counters) or are already there, or on the split at all (tp=1)."""
+    c = ctx()
+    shape = W.ag_shape(4, 0, 200, 256, 200, dist="normal_sqrtk", seed=9)
+    inp = W.make_ag(shape)
+    run = AGRun(inp)
+    outs = []
+    for s in range(4):
+        say(f"case invariance s={s}")
+        run.run(c, self_rank=s)
+        outs.append(run.D_bits())
+        assert np.array_equal(W.bits_u16(run.G.cpu()), O.gather([W.bits_u16(x) for x in inp.chunks]))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    run.D.zero_()
+    run.run(c, flags=B.RAG_NO_COPY, self_rank=2)
+    assert np.array_equal(run.D_bits(), outs[0])
+    # tp = 1 on the gathered input
+    G = run.G.clone()
+    D1 = torch.empty_like(run.D)
+    B.ag_gemm(c, run.A, [G], 1, 0, D1)
+    torch.cuda.synchronize()
+    assert np.array_equal(W.bits_u16(D1.cpu()), outs[0])
+    _, ref = oracle_ag(inp)
+    assert rel_err(outs[0], ref) <= TOL_BF16
+
+
+def test_ag_flags_staged_copy_only_sdma():
+    c = ctx()
+    for tp, s in ((4, 1), (2, 1), (3, 0)):
+        inp = W.make_ag(W.ag_shape(tp, s, 96, 192, 160, dist="int3", seed=tp + s))
+        _, ref = oracle_ag(inp)
+        want = O.f32_to_bf16(ref)
+        G_ref = O.gather([W.bits_u16(x) for x in inp.chunks])
+        run = AGRun(inp)
+        say(f"case staged tp={tp} s={s}")
+        run.run(c, flags=B.RAG_STAGED_OUT)
+        assert np.array_equal(run.D_bits(), want)
+        say(f"case copy-only tp={tp} s={s}")
+        run.D.fill_(7.0)
+        run.G.zero_()
+        run.run(c, flags=B.RAG_COPY_ONLY)
+        assert np.array_equal(W.bits_u16(run.G.cpu()), G_ref)
+        assert bool((run.D.float() == 7.0).all())
+        say(f"case sdma tp={tp} s={s}")
+        c.set_option(B.RAG_OPT_COPY_ENGINE, 1)
+        run.G.zero_()
+        run.run(c)
+        assert np.array_equal(run.D_bits(), want)
+        assert np.array_equal(W.bits_u16(run.G.cpu()), G_ref)
+        c.set_option(B.RAG_OPT_COPY_ENGINE, 0)
+
+
+def test_ag_internal_gather_buffer():
+    c = ctx()
+    inp = W.make_ag(W.ag_shape(4, 3, 64, 128, 96, dist="int3", seed=3))
+    run = AGRun(inp, with_G=False)
+    say("case G=NULL")
+    run.run(c)
+    _, ref = oracle_ag(inp)
+    assert np.array_equal(run.D_bits(), O.f32_to_bf16(ref))
+
+
+def test_ag_gating_delayed_arrivals_on_poisoned_slots():
+    """Every slot of G is NaN before the call and each arrival is held back 2 ms after its copy:
+    a tile that read its chunk before the counter said so would produce NaN or a wrong value."""
+    c = ctx()
+    c.set_option(B.RAG_OPT_ARRIVAL_DELAY_US, 2000)
+    inp = W.make_ag(W.ag_shape(4, 1, 256, 256, 256, dist="int3", seed=17))
+    _, ref = oracle_ag(inp)
+    want = O.f32_to_bf16(ref)
+    run = AGRun(inp)
+    for it in range(3):
+        say(f"case gating it={it}")
+        run.G.fill_(float("nan"))
+        run.D.fill_(float("nan"))
+        run.run(c)
+        assert np.array_equal(run.D_bits(), want)
+
+
+def test_ag_withheld_chunk_times_out_and_context_recovers():
+    c = ctx()
+    c.set_option(B.RAG_OPT_SPIN_LIMIT_US, 20000)
+    c.set_option(B.RAG_OPT_WITHHOLD_MASK, 1 << 2)
+    inp = W.make_ag(W.ag_shape(4, 0, 128, 128, 128, dist="int3", seed=23))
+    run = AGRun(inp)
+    say("case withheld chunk")
+    run.run(c)
+    with pytest.raises(B.RagError) as ei:
+        c.check()
+    assert ei.value.code == B.RAG_ETIMEOUT
+    c.set_option(B.RAG_OPT_WITHHOLD_MASK, 0)
+    c.set_option(B.RAG_OPT_SPIN_LIMIT_US, 2_000_000)
+    run.run(c)
+    c.check()
+    _, ref = oracle_ag(inp)
+    assert np.array_equal(run.D_bits(), O.f32_to_bf16(ref))
+
+
+def test_ag_epoch_stress_fresh_data_same_buffers():
+    """Back-to-back calls in the same buffers with new data each time: stale cache lines or a
+    counter left over from the previous call would show up as a mismatch."""
+    c = ctx()
+    shape = W.ag_shape(4, 2, 256, 256, 256, dist="int3", seed=0)
+    run = AGRun(W.make_ag(shape))
+    for it in range(30):
+        inp = W.make_ag(W.ag_shape(4, 2, 256, 256, 256, dist="int3", seed=1000 + it))
+        run.A.copy_(inp.A)
+        for d, h in zip(run.chunks, inp.chunks):
+            d.copy_(h)
+        run.run(c)
+        _, ref = oracle_ag(inp)
+        if not np.array_equal(run.D_bits(), O.f32_to_bf16(ref)):
+            pytest.fail(f"iteration {it} differs from its oracle")
+    say("case epoch stress done")
+
+
+def test_ag_fp8_small_parity_and_exact():
+    c = ctx()
+    shape = W.ag_shape(4, 3, 160, 256, 224, dtype="fp8", dist="normal", seed=31)
+    say(f"case {shape.name}")
+    inp = W.make_ag(shape)
+    run = AGRun(inp).run(c)
+    G_ref, ref = oracle_ag(inp)
+    assert np.array_equal(W.bits_u8(run.G.cpu()), G_ref)
+    assert rel_err(run.D_bits(), ref) <= TOL_FP8
+    for tile in TILE_NAMES:
+        c.set_option(B.RAG_OPT_TILE, B.TILES[tile])
+        inp = W.make_ag(W.ag_shape(2, 1, 100, 256, 90, dtype="fp8", dist="int3", seed=37))
+        say(f"case fp8 exact tile={tile}")
+        run = AGRun(inp).run(c)
+        _, ref = oracle_ag(inp)
+        assert np.array_equal(run.D_bits(), O.f32_to_bf16(ref))
+
+
+@pytest.mark.parametrize("name", ["ag_4k", "ag_qkv", "ag_fc1_f8"])
+def test_ag_full_size_sampled_rows(name):
+    """The measured workloads at full size: first, last and 62 seeded rows of every chunk are
+    compared with the oracle's rows (the full product would take the host minutes)."""
+    shape = W.WORKLOADS[name]
+    say(f"case {shape}")
+    inp = W.make_ag(shape)
+    run = AGRun(inp).run(ctx())
+    ctx().check()
+    rows = sampled_rows(shape.tp, shape.nc, seed=shape.seed)
+    ref = oracle_ag_rows(inp, rows)
+    got = run.D_bits()[rows]
+    tol = TOL_FP8 if shape.dtype == "fp8" else TOL_BF16
+    err = rel_err(got, ref)
+    say(f"{name}: sampled {len(rows)} rows, max rel err {err:.3e}")
+    assert err <= tol
+    G = run.G.cpu()
+    Gb = W.bits_u8(G) if shape.dtype == "fp8" else W.bits_u16(G)
+    for r in range(shape.tp):
+        src = W.bits_u8(inp.chunks[r]) if shape.dtype == "fp8" else W.bits_u16(inp.chunks[r])
+        assert np.array_equal(Gb[r * shape.nc:(r + 1) * shape.nc], src)
