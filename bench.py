@@ -1,0 +1,253 @@
+"""Benchmark of the ring-decomposed AG+GEMM (and GEMM+RS) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ag_4k|ag_qkv|ag_fc1_f8|rs_8k]
+
+A step is one ag_gemm call (or one gemm_rs call for rs_8k) through the C ABI on inputs already
+resident in HBM: the arrival copies on the side stream, the counter-gated GEMM on the caller's
+stream and the join.  The default workload is AG+GEMM at M=K=N=4096, tp=4, self_rank=1, bf16.
+
+Prints one JSON line: throughput (TFLOP/s) of the whole step, the overlap figures (GEMM-only and
+copy-only times of the same kernels, overlap ratio T_chunked / (T_copy_only + T_gemm_only) and the
+hidden fraction of the copy time), the roofline of the GEMM kernel (algorithmic flops per launch
+over its average launch duration, from HIP events around each launch on the stream it runs on) and
+the CPU oracle's throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}   # 256 CU x 2.4 GHz x (4096 | 8192) flop/clk
+PEAK_HBM_GBS = 8000.0
+METRICS = {
+    "ag": "AG+GEMM TFLOP/s (+% MFMA peak) and overlap efficiency, M=K=N=4096 tp=4",
+    "rs": "GEMM+RS TFLOP/s (+% MFMA peak) and epilogue HBM GB/s",
+}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="ag_4k")
+    p.add_argument("--copy-engine", default=os.environ.get("RAG_COPY_ENGINE", "kernel"),
+                   choices=["kernel", "sdma"])
+    p.add_argument("--comm-wgs", type=int, default=int(os.environ.get("RAG_COMM_WGS", "32")))
+    p.add_argument("--tile", default=os.environ.get("RAG_TILE", "auto"))
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="target wall time of the CPU oracle sample")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    return p.parse_args()
+
+
+def time_steps(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    stops = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        starts[i].record(stream)
+        fn()
+        stops[i].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in zip(starts, stops)]
+    return t0.elapsed_time(t1) / steps, per
+
+
+def pctl(xs, q):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))]
+
+
+def cpu_baseline_ag(inp, target_s):
+    """The oracle (as it stands) on whole output rows of the same workload; sample sized so the
+    timed part takes about target_s seconds of wall time."""
+    import numpy as np
+    from oracle import ringag_oracle as O
+    from ring_all_gather_amd import workloads as W
+    s = inp.shape
+    fp8 = s.dtype == "fp8"
+    conv = (lambda t: O.dequantize_e4m3(W.bits_u8(t), inp.scale_B)) if fp8 else \
+        (lambda t: O.bf16_to_f32(W.bits_u16(t)))
+    A = O.dequantize_e4m3(W.bits_u8(inp.A), inp.scale_A) if fp8 else O.bf16_to_f32(
+        W.bits_u16(inp.A))
+    G = O.gather([conv(c) for c in inp.chunks])
+    flops_row = 2.0 * s.M * s.K
+    probe = np.arange(0, min(s.N, 16))
+    t = time.perf_counter()
+    O.gemm_tn_rows(G, A, probe)
+    dt = max(time.perf_counter() - t, 1e-4)
+    nrows = int(min(s.N, max(16, len(probe) * target_s / dt)))
+    rows = np.linspace(0, s.N - 1, nrows).astype(np.int64)
+    t = time.perf_counter()
+    O.gemm_tn_rows(G, A, rows)
+    dt = time.perf_counter() - t
+    return {"value": round(flops_row * nrows / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"{nrows} of the {s.N} output rows (each {s.M}x{s.K} MACs, fp32 triple loop "
+                      f"over the gathered input), {dt:.1f} s wall"}
+
+
+def cpu_baseline_rs(inp, target_s):
+    import numpy as np
+    from oracle import ringag_oracle as O
+    from ring_all_gather_amd import workloads as W
+    s = inp.shape
+    Xb, Wb = W.bits_u16(inp.X), W.bits_u16(inp.W)
+    Xf, Wf = O.bf16_to_f32(Xb), O.bf16_to_f32(Wb)
+    flops_row = 2.0 * s.Mo * s.Kl
+    probe = np.arange(0, 16)
+    t = time.perf_counter()
+    O.gemm_tn_rows(Xf, Wf, probe)
+    dt = max(time.perf_counter() - t, 1e-4)
+    nrows = int(min(s.T, max(16, len(probe) * target_s / dt)))
+    rows = np.linspace(0, s.T - 1, nrows).astype(np.int64)
+    t = time.perf_counter()
+    O.gemm_tn_rows(Xf, Wf, rows)
+    dt = time.perf_counter() - t
+    return {"value": round(flops_row * nrows / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"{nrows} of the {s.T} rows of the local partial X W^T (each {s.Mo}x{s.Kl} "
+                      f"MACs, fp32 triple loop), {dt:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs one rank's share on one GPU; --gpus {args.gpus} is not supported "
+              "(the ring's peers are simulated on the same device)", file=sys.stderr)
+        return 2
+    import torch
+    from ring_all_gather_amd import binding as B
+    from ring_all_gather_amd import workloads as W
+
+    dev = "cuda:0"
+    ctx = B.Context(0, max_tp=16)
+    ctx.set_option(B.RAG_OPT_COPY_ENGINE, {"kernel": 0, "sdma": 1}[args.copy_engine])
+    ctx.set_option(B.RAG_OPT_COMM_WGS, args.comm_wgs)
+    ctx.set_option(B.RAG_OPT_TILE, B.TILES[args.tile])
+    shape = W.WORKLOADS[args.workload]
+    stream = torch.cuda.current_stream()
+    out = {}
+
+    if isinstance(shape, W.AGShape):
+        inp = W.make_ag(shape)
+        A = inp.A.to(dev)
+        chunks = [c.to(dev) for c in inp.chunks]
+        G = torch.empty((shape.N, shape.K), dtype=inp.A.dtype, device=dev)
+        D = torch.empty((shape.N, shape.M), dtype=torch.bfloat16, device=dev)
+        sA = sB = None
+        if shape.dtype == "fp8":
+            sA = torch.tensor([inp.scale_A], dtype=torch.float32, device=dev)
+            sB = torch.tensor([inp.scale_B], dtype=torch.float32, device=dev)
+
+        def step(flags=0):
+            B.ag_gemm(ctx, A, chunks, shape.tp, shape.self_rank, D, G=G, scale_A=sA, scale_B=sB,
+                      flags=flags)
+
+        torch.cuda.synchronize()
+        ctx.kernel_times()
+        ctx.set_option(B.RAG_OPT_TIMING, 1)
+        ms, per = time_steps(step, args.steps, args.warmup, stream)
+        kt = ctx.kernel_times()[args.warmup:]
+        ctx.set_option(B.RAG_OPT_TIMING, 0)
+        ctx.check()
+        ms_gemm, _ = time_steps(lambda: step(B.RAG_NO_COPY), args.steps, args.warmup, stream)
+        ms_copy, _ = time_steps(lambda: step(B.RAG_COPY_ONLY), args.steps, args.warmup, stream)
+        ms_staged, _ = time_steps(lambda: step(B.RAG_STAGED_OUT), args.steps, args.warmup, stream)
+        ctx.check()
+        flops = shape.flops
+        kernel_ms = statistics.fmean(kt)
+        achieved = flops / (kernel_ms * 1e-3) / 1e12
+        peak = PEAK_TFLOPS[shape.dtype]
+        value = flops / (ms * 1e-3) / 1e12
+        out = {
+            "metric": METRICS["ag"] if args.workload == "ag_4k" else
+            f"AG+GEMM TFLOP/s (+% MFMA peak) and overlap efficiency, {args.workload}",
+            "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": shape.dtype, "data": "synthetic",
+            "config": {"workload": f"ag_gemm tp={shape.tp} self_rank={shape.self_rank} "
+                                   f"N={shape.N} (chunks of {shape.nc}) M={shape.M} K={shape.K} "
+                                   f"{shape.dtype}",
+                       "tp": shape.tp, "self_rank": shape.self_rank, "N": shape.N, "M": shape.M,
+                       "K": shape.K, "copy_engine": args.copy_engine, "comm_wgs": args.comm_wgs,
+                       "tile": args.tile},
+            "pct_mfma_peak": round(100.0 * value / peak, 2),
+            "step_ms": {"p10": round(pctl(per, 0.1), 5), "p50": round(pctl(per, 0.5), 5),
+                        "p90": round(pctl(per, 0.9), 5)},
+            "overlap": {"t_chunked_ms": round(ms, 5), "t_gemm_only_ms": round(ms_gemm, 5),
+                        "t_copy_only_ms": round(ms_copy, 5),
+                        "overlap_ratio": round(ms / (ms_copy + ms_gemm), 4),
+                        "hidden_fraction": round((ms_copy + ms_gemm - ms) / ms_copy, 4),
+                        "t_staged_out_ms": round(ms_staged, 5)},
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                         "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                         "kernel": "ag_gemm_kernel", "kernel_ms": round(kernel_ms, 5)},
+        }
+        if not args.no_cpu:
+            out["cpu_baseline"] = cpu_baseline_ag(inp, args.cpu_seconds)
+    else:
+        inp = W.make_rs(shape)
+        X, Wt = inp.X.to(dev), inp.W.to(dev)
+        parts = [None if p is None else p.to(dev) for p in inp.partials]
+        D = torch.empty((shape.nc, shape.Mo), dtype=torch.bfloat16, device=dev)
+        send = torch.empty((shape.tp, shape.nc, shape.Mo), dtype=torch.float32, device=dev)
+
+        def step():
+            B.gemm_rs(ctx, X, Wt, parts, shape.tp, shape.self_rank, D, send=send)
+
+        torch.cuda.synchronize()
+        ctx.kernel_times()
+        ctx.set_option(B.RAG_OPT_TIMING, 1)
+        ms, per = time_steps(step, args.steps, args.warmup, stream)
+        kt = ctx.kernel_times()[args.warmup:]
+        ctx.set_option(B.RAG_OPT_TIMING, 0)
+        kernel_ms = statistics.fmean(kt)
+        flops = shape.flops
+        nc, Mo, tp = shape.nc, shape.Mo, shape.tp
+        alg_bytes = (shape.T * shape.Kl * 2 + Mo * shape.Kl * 2 + (tp - 1) * nc * Mo * 4 * 2
+                     + nc * Mo * 2)
+        value = flops / (ms * 1e-3) / 1e12
+        gbs = alg_bytes / (kernel_ms * 1e-3) / 1e9
+        out = {
+            "metric": METRICS["rs"], "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": f"gemm_rs tp={tp} self_rank={shape.self_rank} T={shape.T} "
+                                   f"Kl={shape.Kl} Mo={Mo} bf16, fp32 partials and send",
+                       "tile": args.tile},
+            "pct_mfma_peak": round(100.0 * value / PEAK_TFLOPS["bf16"], 2),
+            "step_ms": {"p10": round(pctl(per, 0.1), 5), "p50": round(pctl(per, 0.5), 5),
+                        "p90": round(pctl(per, 0.9), 5)},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "kernel": "gemm_rs_kernel", "kernel_ms": round(kernel_ms, 5),
+                         "algorithmic_bytes": alg_bytes},
+        }
+        if not args.no_cpu:
+            out["cpu_baseline"] = cpu_baseline_rs(inp, args.cpu_seconds)
+    ctx.close()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

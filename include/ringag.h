@@ -92,8 +92,9 @@ enum {
     RAG_OPT_TILE = 7            /* GEMM tile configuration: 0 = automatic, else a RAG_TILE_* value */
 };
 
-/* Tile configurations (rows of D x columns of D per workgroup). */
-enum { RAG_TILE_AUTO = 0, RAG_TILE_128x128 = 1, RAG_TILE_256x128 = 2, RAG_TILE_256x256 = 3 };
+/* Tile configurations (rows of D x columns of D per workgroup; 4 waves unless stated). */
+enum { RAG_TILE_AUTO = 0, RAG_TILE_128x128 = 1, RAG_TILE_256x128 = 2, RAG_TILE_256x256 = 3,
+       RAG_TILE_256x256_8W = 4 /* 8 waves of 128x64 */ };
 
 typedef struct rag_ctx rag_ctx;     /* opaque; owned by the library */
 

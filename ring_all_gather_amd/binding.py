@@ -10,9 +10,12 @@ Environment overrides applied when a Context is created (all optional):
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
 import re
+import sys
+import weakref
 from typing import Optional, Sequence
 
 import torch
@@ -27,10 +30,20 @@ RAG_BF16, RAG_FP8_E4M3 = 0, 1
 RAG_STAGED_OUT, RAG_NO_COPY, RAG_COPY_ONLY = 1, 2, 4
 RAG_OPT_COPY_ENGINE, RAG_OPT_COMM_WGS, RAG_OPT_SPIN_LIMIT_US = 1, 2, 3
 RAG_OPT_ARRIVAL_DELAY_US, RAG_OPT_WITHHOLD_MASK, RAG_OPT_TIMING, RAG_OPT_TILE = 4, 5, 6, 7
-TILES = {"auto": 0, "128x128": 1, "256x128": 2, "256x256": 3}
+TILES = {"auto": 0, "128x128": 1, "256x128": 2, "256x256": 3, "256x256w8": 4}
 RAG_MAX_TP = 16
 
 _lib = None
+_live = weakref.WeakSet()     # open contexts, closed at exit before the runtime shuts down
+
+
+@atexit.register
+def _close_all():
+    for c in list(_live):
+        try:
+            c.close()
+        except Exception:
+            pass
 
 
 class RagError(RuntimeError):
@@ -107,6 +120,7 @@ class Context:
         self.h = h
         self.device = device
         self.max_tp = max_tp
+        _live.add(self)
         env = os.environ
         if "RAG_COPY_ENGINE" in env:
             self.set_option(RAG_OPT_COPY_ENGINE, {"kernel": 0, "sdma": 1}[env["RAG_COPY_ENGINE"]])
@@ -137,6 +151,10 @@ class Context:
             self.h = None
 
     def __del__(self):
+        # During interpreter shutdown the HIP runtime may already be going away: leave the
+        # context to the process exit (atexit above closes it earlier in a normal exit).
+        if sys.is_finalizing():
+            return
         try:
             self.close()
         except Exception:

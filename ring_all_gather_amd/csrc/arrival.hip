@@ -38,8 +38,10 @@ __global__ void __launch_bounds__(kArrThreads) arrival_kernel(ArrivalArgs a) {
     for (; i < end; i += kArrThreads) dst[i] = src[i];
 
     if (a.ctr_index[j] >= 0) {
-      __threadfence();          // this thread's stores are visible device-wide
-      __syncthreads();          // ... for every thread of the workgroup
+      // Each wave waits for its own stores to be acknowledged; after the barrier, one release
+      // (agent scope: writes the XCD's L2 back) by thread 0 covers the whole workgroup's slice.
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
       if (threadIdx.x == 0) {
         const int old = __hip_atomic_fetch_add(a.ticket + j, 1, __ATOMIC_ACQ_REL,
                                                __HIP_MEMORY_SCOPE_AGENT);

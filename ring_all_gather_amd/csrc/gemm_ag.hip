@@ -40,21 +40,19 @@ __device__ inline bool wait_ready(int* ctr, int epoch, int* err, long long limit
   }
 }
 
-template <int BI, int BJ, bool FP8>
-__global__ void __launch_bounds__(kThreads) ag_gemm_kernel(AgArgs a) {
-  __shared__ __attribute__((aligned(1024))) char lds[2 * (BI + BJ) * kRowBytes];
+template <class S, bool FP8>
+__global__ void __launch_bounds__(S::NT) ag_gemm_kernel(AgArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds[S::LDS];
   __shared__ int s_ok;
-  constexpr int FI = BI / 64, FJ = BJ / 64;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wi = wave >> 1, wj = wave & 1;
   const uint32_t ldb = (uint32_t)a.K * (FP8 ? 1u : 2u);
   const int ksteps = (int)(ldb / kRowBytes);
   const int U = a.tiles_i * a.tiles_j;
   const int total = U * a.tp;
   float scale = 1.0f;
   if constexpr (FP8) scale = a.scale_A[0] * a.scale_B[0];
-  const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.A, (uint32_t)a.M * ldb);
+  const i32x4 ry = make_rsrc(a.A, (uint32_t)a.M * ldb);
 
   for (int t = blockIdx.x; t < total; t += gridDim.x) {
     const int j = t / U;
@@ -68,68 +66,63 @@ __global__ void __launch_bounds__(kThreads) ag_gemm_kernel(AgArgs a) {
       __syncthreads();
       if (!ok) continue;
     }
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.chunk[j], (uint32_t)a.nc * ldb);
-    uint32_t xo[BI / 32], yo[BJ / 32];
-    tile_offsets<BI>(xo, rb * BI, a.nc, ldb, wave, lane);
-    tile_offsets<BJ>(yo, cb * BJ, a.M, ldb, wave, lane);
-    f32x16 acc[FI][FJ];
-    tile_kloop<BI, BJ, FP8>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);
-
-    __bf16* out = (__bf16*)a.out[j];
-    const int row0 = rb * BI + wi * (BI / 2);
-    const int col0 = cb * BJ + wj * (BJ / 2);
-#pragma unroll
-    for (int i = 0; i < FI; ++i)
-#pragma unroll
-      for (int jj = 0; jj < FJ; ++jj) {
-        const int col = col0 + acc_col(jj, lane);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = row0 + acc_row(i, e, lane);
-          if (row < a.nc && col < a.M)
-            out[(size_t)row * a.M + col] = (__bf16)(acc[i][jj][e] * scale);
-        }
-      }
+    const i32x4 rx = make_rsrc(a.chunk[j], (uint32_t)a.nc * ldb);
+    uint32_t xo[S::XQ], yo[S::YQ];
+    tile_offsets<S::XQ, S::NW>(xo, rb * S::BI, a.nc, ldb, wave, lane);
+    tile_offsets<S::YQ, S::NW>(yo, cb * S::BJ, a.M, ldb, wave, lane);
+    f32x16 acc[S::FI][S::FJ];
+    tile_kloop<S, FP8>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);
+    __bf16* out = (__bf16*)a.out[j] + (size_t)rb * S::BI * a.M + (size_t)cb * S::BJ;
+    store_tile_bf16<S>(acc, scale, lds, out, a.M, a.nc - rb * S::BI, a.M - cb * S::BJ, wave, lane);
   }
 }
 
-template <int BI, int BJ, bool FP8>
+template <class S, bool FP8>
 static hipError_t launch_t(const AgArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((ag_gemm_kernel<BI, BJ, FP8>), dim3(grid), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((ag_gemm_kernel<S, FP8>), dim3(grid), dim3(S::NT), 0, s, a);
   return hipGetLastError();
 }
 
-template <int BI, int BJ, bool FP8>
+template <class S, bool FP8>
 static hipError_t info_t(KernelInfo* info) {
   hipFuncAttributes at;
-  hipError_t e = hipFuncGetAttributes(&at, (const void*)ag_gemm_kernel<BI, BJ, FP8>);
+  hipError_t e = hipFuncGetAttributes(&at, (const void*)ag_gemm_kernel<S, FP8>);
   if (e != hipSuccess) return e;
   int nb = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ag_gemm_kernel<BI, BJ, FP8>, kThreads, 0);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ag_gemm_kernel<S, FP8>, S::NT, 0);
   if (e != hipSuccess) return e;
-  info->threads = kThreads;
+  info->threads = S::NT;
   info->lds_bytes = (int)at.sharedSizeBytes;
   info->vgprs_per_wave = at.numRegs;
   info->max_blocks_per_cu = nb;
   return hipSuccess;
 }
 
+template <class S>
+static hipError_t launch_dt(const AgArgs& a, bool fp8, int grid, hipStream_t s) {
+  return fp8 ? launch_t<S, true>(a, grid, s) : launch_t<S, false>(a, grid, s);
+}
+
+template <class S>
+static hipError_t info_dt(bool fp8, KernelInfo* info) {
+  return fp8 ? info_t<S, true>(info) : info_t<S, false>(info);
+}
+
 hipError_t launch_ag_gemm(const AgArgs& a, int tile, bool fp8, int grid, hipStream_t s) {
   switch (tile) {
-    case kTile256x256: return fp8 ? launch_t<256, 256, true>(a, grid, s)
-                                  : launch_t<256, 256, false>(a, grid, s);
-    case kTile256x128: return fp8 ? launch_t<256, 128, true>(a, grid, s)
-                                  : launch_t<256, 128, false>(a, grid, s);
-    default: return fp8 ? launch_t<128, 128, true>(a, grid, s)
-                        : launch_t<128, 128, false>(a, grid, s);
+    case kTile256x256: return launch_dt<Tile256x256>(a, fp8, grid, s);
+    case kTile256x256w8: return launch_dt<Tile256x256w8>(a, fp8, grid, s);
+    case kTile256x128: return launch_dt<Tile256x128>(a, fp8, grid, s);
+    default: return launch_dt<Tile128x128>(a, fp8, grid, s);
   }
 }
 
 hipError_t ag_kernel_info(int tile, bool fp8, KernelInfo* info) {
   switch (tile) {
-    case kTile256x256: return fp8 ? info_t<256, 256, true>(info) : info_t<256, 256, false>(info);
-    case kTile256x128: return fp8 ? info_t<256, 128, true>(info) : info_t<256, 128, false>(info);
-    default: return fp8 ? info_t<128, 128, true>(info) : info_t<128, 128, false>(info);
+    case kTile256x256: return info_dt<Tile256x256>(fp8, info);
+    case kTile256x256w8: return info_dt<Tile256x256w8>(fp8, info);
+    case kTile256x128: return info_dt<Tile256x128>(fp8, info);
+    default: return info_dt<Tile128x128>(fp8, info);
   }
 }
 

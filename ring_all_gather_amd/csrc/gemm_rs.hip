@@ -21,18 +21,17 @@ __device__ inline void map_tile_rs(int u, int U, int R, int* rb, int* cb) {
   *cb = v / R;
 }
 
-template <int BI, int BJ>
-__global__ void __launch_bounds__(kThreads) gemm_rs_kernel(RsArgs a) {
-  __shared__ __attribute__((aligned(1024))) char lds[2 * (BI + BJ) * kRowBytes];
-  constexpr int FI = BI / 64, FJ = BJ / 64;
+template <class S>
+__global__ void __launch_bounds__(S::NT) gemm_rs_kernel(RsArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds[S::LDS];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wi = wave >> 1, wj = wave & 1;
+  const int wi = wave / S::WJ, wj = wave % S::WJ;
   const uint32_t ldb = (uint32_t)a.Kl * 2u;
   const int ksteps = (int)(ldb / kRowBytes);
   const int U = a.tiles_i * a.tiles_j;
   const int total = U * a.tp;
-  const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.W, (uint32_t)a.Mo * ldb);
+  const i32x4 ry = make_rsrc(a.W, (uint32_t)a.Mo * ldb);
 
   for (int t = blockIdx.x; t < total; t += gridDim.x) {
     const int j = t / U;
@@ -43,21 +42,21 @@ __global__ void __launch_bounds__(kThreads) gemm_rs_kernel(RsArgs a) {
     int rb, cb;
     map_tile_rs(u, U, a.tiles_i, &rb, &cb);
     const char* xbase = (const char*)a.X + (size_t)c * a.nc * ldb;
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(xbase, (uint32_t)a.nc * ldb);
-    uint32_t xo[BI / 32], yo[BJ / 32];
-    tile_offsets<BI>(xo, rb * BI, a.nc, ldb, wave, lane);
-    tile_offsets<BJ>(yo, cb * BJ, a.Mo, ldb, wave, lane);
-    f32x16 acc[FI][FJ];
-    tile_kloop<BI, BJ, false>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);
+    const i32x4 rx = make_rsrc(xbase, (uint32_t)a.nc * ldb);
+    uint32_t xo[S::XQ], yo[S::YQ];
+    tile_offsets<S::XQ, S::NW>(xo, rb * S::BI, a.nc, ldb, wave, lane);
+    tile_offsets<S::YQ, S::NW>(yo, cb * S::BJ, a.Mo, ldb, wave, lane);
+    f32x16 acc[S::FI][S::FJ];
+    tile_kloop<S, false>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);
 
-    const int row0 = rb * BI + wi * (BI / 2);
-    const int col0 = cb * BJ + wj * (BJ / 2);
+    const int row0 = rb * S::BI + wi * S::TM;
+    const int col0 = cb * S::BJ + wj * S::TN;
     if (!own) {
       float* out = a.send + (size_t)c * a.nc * a.Mo;
 #pragma unroll
-      for (int i = 0; i < FI; ++i)
+      for (int i = 0; i < S::FI; ++i)
 #pragma unroll
-        for (int jj = 0; jj < FJ; ++jj) {
+        for (int jj = 0; jj < S::FJ; ++jj) {
           const int col = col0 + acc_col(jj, lane);
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
@@ -66,14 +65,14 @@ __global__ void __launch_bounds__(kThreads) gemm_rs_kernel(RsArgs a) {
           }
         }
     } else {
-      // Own chunk: add every peer's partial to the accumulators (one fragment at a time, so only
-      // 16 extra registers are live), then round to bf16 and store.
+      // Own chunk: add every peer's partial to the accumulators one block at a time (16 extra
+      // registers live), then round to bf16 and store.
       __bf16* out = (__bf16*)a.D;
       const size_t prow0 = (size_t)a.self_rank * a.nc;
 #pragma unroll
-      for (int i = 0; i < FI; ++i)
+      for (int i = 0; i < S::FI; ++i)
 #pragma unroll
-        for (int jj = 0; jj < FJ; ++jj) {
+        for (int jj = 0; jj < S::FJ; ++jj) {
           const int col = col0 + acc_col(jj, lane);
           float v[16];
 #pragma unroll
@@ -97,21 +96,21 @@ __global__ void __launch_bounds__(kThreads) gemm_rs_kernel(RsArgs a) {
   }
 }
 
-template <int BI, int BJ>
+template <class S>
 static hipError_t launch_t(const RsArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_rs_kernel<BI, BJ>), dim3(grid), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((gemm_rs_kernel<S>), dim3(grid), dim3(S::NT), 0, s, a);
   return hipGetLastError();
 }
 
-template <int BI, int BJ>
+template <class S>
 static hipError_t info_t(KernelInfo* info) {
   hipFuncAttributes at;
-  hipError_t e = hipFuncGetAttributes(&at, (const void*)gemm_rs_kernel<BI, BJ>);
+  hipError_t e = hipFuncGetAttributes(&at, (const void*)gemm_rs_kernel<S>);
   if (e != hipSuccess) return e;
   int nb = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, gemm_rs_kernel<BI, BJ>, kThreads, 0);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, gemm_rs_kernel<S>, S::NT, 0);
   if (e != hipSuccess) return e;
-  info->threads = kThreads;
+  info->threads = S::NT;
   info->lds_bytes = (int)at.sharedSizeBytes;
   info->vgprs_per_wave = at.numRegs;
   info->max_blocks_per_cu = nb;
@@ -120,17 +119,19 @@ static hipError_t info_t(KernelInfo* info) {
 
 hipError_t launch_gemm_rs(const RsArgs& a, int tile, int grid, hipStream_t s) {
   switch (tile) {
-    case kTile256x256: return launch_t<256, 256>(a, grid, s);
-    case kTile256x128: return launch_t<256, 128>(a, grid, s);
-    default: return launch_t<128, 128>(a, grid, s);
+    case kTile256x256: return launch_t<Tile256x256>(a, grid, s);
+    case kTile256x256w8: return launch_t<Tile256x256w8>(a, grid, s);
+    case kTile256x128: return launch_t<Tile256x128>(a, grid, s);
+    default: return launch_t<Tile128x128>(a, grid, s);
   }
 }
 
 hipError_t rs_kernel_info(int tile, KernelInfo* info) {
   switch (tile) {
-    case kTile256x256: return info_t<256, 256>(info);
-    case kTile256x128: return info_t<256, 128>(info);
-    default: return info_t<128, 128>(info);
+    case kTile256x256: return info_t<Tile256x256>(info);
+    case kTile256x256w8: return info_t<Tile256x256w8>(info);
+    case kTile256x128: return info_t<Tile256x128>(info);
+    default: return info_t<Tile128x128>(info);
   }
 }
 

@@ -56,7 +56,7 @@ struct ArrivalArgs {
   unsigned withhold_mask;        // test hook: bit pos set = never release that chunk
 };
 
-enum TileCfg { kTile128x128 = 1, kTile256x128 = 2, kTile256x256 = 3 };
+enum TileCfg { kTile128x128 = 1, kTile256x128 = 2, kTile256x256 = 3, kTile256x256w8 = 4 };
 
 struct KernelInfo {
   int threads;
@@ -78,7 +78,8 @@ hipError_t arrival_kernel_info(KernelInfo* info);
 // Tile sizes of a configuration.
 inline void tile_dims(int tile, int* bi, int* bj) {
   switch (tile) {
-    case kTile256x256: *bi = 256; *bj = 256; break;
+    case kTile256x256:
+    case kTile256x256w8: *bi = 256; *bj = 256; break;
     case kTile256x128: *bi = 256; *bj = 128; break;
     default: *bi = 128; *bj = 128; break;
   }

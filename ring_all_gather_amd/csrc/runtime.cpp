@@ -30,15 +30,14 @@ using namespace ringag;
 
 namespace {
 
-thread_local std::string g_last_error;
+// Trivially destructible, so nothing of it runs at thread or process exit.
+thread_local char g_last_error[1024];
 
 int fail(int code, const char* fmt, ...) {
-  char buf[1024];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
   va_end(ap);
-  g_last_error = buf;
   return code;
 }
 
@@ -144,10 +143,11 @@ int choose_ag_tile(const rag_ctx* c, int nc, int M) {
   return kTile128x128;
 }
 
-// Compute units kept free of GEMM workgroups while arrivals run.  The 256x256 tile uses every
-// vector register of its SIMDs (512 per lane), so no wave of the copy kernel could share a CU
-// with it; with one such workgroup per CU (its LDS allows no second), leaving 8 CUs without one
-// guarantees the copy kernel a place to run while GEMM tiles wait for its chunks.
+// Compute units kept free of GEMM workgroups while arrivals run.  The 4-wave 256x256 tile uses
+// every vector register of its SIMDs (512 per lane), so no wave of the copy kernel could share a
+// CU with it; with one such workgroup per CU (its LDS allows no second), leaving 8 CUs without one
+// guarantees the copy kernel a place to run while GEMM tiles wait for its chunks.  Every other
+// tile leaves at least 64 registers per SIMD lane free, enough for the copy kernel's waves.
 int reserved_cus(int tile, bool arrivals) {
   return (arrivals && tile == kTile256x256) ? 8 : 0;
 }
@@ -188,7 +188,7 @@ extern "C" {
 
 int rag_version(void) { return 100; }
 
-const char* rag_last_error(void) { return g_last_error.c_str(); }
+const char* rag_last_error(void) { return g_last_error; }
 
 int rag_create(rag_ctx** out, int device, int max_tp, int flags) {
   if (!out) return fail(RAG_EINVAL, "rag_create: out is NULL");
@@ -288,7 +288,7 @@ int rag_set_option(rag_ctx* c, int key, long long v) {
       c->timing = v != 0;
       return RAG_OK;
     case RAG_OPT_TILE:
-      if (v < RAG_TILE_AUTO || v > RAG_TILE_256x256) return fail(RAG_EINVAL, "unknown tile %lld", v);
+      if (v < RAG_TILE_AUTO || v > RAG_TILE_256x256_8W) return fail(RAG_EINVAL, "unknown tile %lld", v);
       c->tile = (int)v;
       return RAG_OK;
     default:

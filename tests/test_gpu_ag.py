@@ -12,7 +12,7 @@ from gpu_common import (AGRun, TOL_BF16, TOL_FP8, ctx, oracle_ag, oracle_ag_rows
 
 pytestmark = pytest.mark.gpu
 
-TILE_NAMES = ["128x128", "256x128", "256x256"]
+TILE_NAMES = ["128x128", "256x128", "256x256", "256x256w8"]
 
 
 @pytest.fixture(autouse=True)
@@ -44,7 +44,7 @@ def test_ag_exact_integers_every_rank(tp, s, nc):
     """Small integers are exact in bf16 and their fp32 sums are exact in any order, so D must be
     the oracle's sum rounded to bf16, bit for bit; G must be the rank-ordered concatenation."""
     c = ctx()
-    tile = TILE_NAMES[(tp + s + nc) % 3]
+    tile = TILE_NAMES[(tp + s + nc) % len(TILE_NAMES)]
     c.set_option(B.RAG_OPT_TILE, B.TILES[tile])
     inp = _int_case(tp, s, nc, K=128, M=80, seed=tp * 100 + s * 10 + nc)
     say(f"case tp={tp} s={s} nc={nc} K=128 M=80 tile={tile}")
