@@ -46,6 +46,12 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#if defined(__GNUC__) || defined(__clang__)
+#define RAG_API __attribute__((visibility("default")))
+#else
+#define RAG_API
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -94,7 +100,8 @@ enum {
 
 /* Tile configurations (rows of D x columns of D per workgroup; 4 waves unless stated). */
 enum { RAG_TILE_AUTO = 0, RAG_TILE_128x128 = 1, RAG_TILE_256x128 = 2, RAG_TILE_256x256 = 3,
-       RAG_TILE_256x256_8W = 4 /* 8 waves of 128x64 */ };
+       RAG_TILE_256x256_8W = 4 /* 8 waves of 128x64, 2 LDS stages of 128-byte rows */,
+       RAG_TILE_256x256_8W_S4 = 5 /* 8 waves of 128x64, 4 LDS stages of 64-byte rows */ };
 
 typedef struct rag_ctx rag_ctx;     /* opaque; owned by the library */
 
@@ -104,13 +111,13 @@ typedef struct rag_ctx rag_ctx;     /* opaque; owned by the library */
  * side stream, events, per-chunk ready counters, an error word and the epoch (all cached for the
  * context's life; no per-call allocation).  flags: reserved, pass 0.  On success *out receives the
  * context.  TransformerEngine PR #2443, sequence diagram: context creation at initialisation. */
-int rag_create(rag_ctx** out, int device, int max_tp, int flags);
+RAG_API int rag_create(rag_ctx** out, int device, int max_tp, int flags);
 
 /* Destroy a context (waits for its side stream first).  Safe on NULL. */
-int rag_destroy(rag_ctx* ctx);
+RAG_API int rag_destroy(rag_ctx* ctx);
 
 /* Set an option (RAG_OPT_*).  Takes effect from the next call. */
-int rag_set_option(rag_ctx* ctx, int key, long long value);
+RAG_API int rag_set_option(rag_ctx* ctx, int key, long long value);
 
 /*
  * AG+GEMM for rank self_rank of a tp-rank ring:
@@ -138,7 +145,7 @@ int rag_set_option(rag_ctx* ctx, int key, long long value);
  * Errors: RAG_EINVAL (bad sizes/pointers/flags, any operand of 2 GiB or more, G or D overlapping
  * an input), RAG_EHIP, RAG_ENOMEM.  A chunk that never arrives is reported by rag_check.
  */
-int ag_gemm(rag_ctx* ctx,
+RAG_API int ag_gemm(rag_ctx* ctx,
             const void* A, int M, int K,
             const void* const* B_chunks, int nc,
             int tp, int self_rank,
@@ -165,7 +172,7 @@ int ag_gemm(rag_ctx* ctx,
  *   D         [nc, Mo] bf16, this rank's reduced chunk
  * Errors: RAG_EINVAL, RAG_EHIP.
  */
-int gemm_rs(rag_ctx* ctx,
+RAG_API int gemm_rs(rag_ctx* ctx,
             const void* X, int T, int Kl,
             const void* W, int Mo,
             const float* const* partials, long long ldp,
@@ -175,18 +182,18 @@ int gemm_rs(rag_ctx* ctx,
 
 /* Synchronise the context's device work and report whether any wait timed out since the last
  * check (RAG_ETIMEOUT; the error word is then cleared), or RAG_OK. */
-int rag_check(rag_ctx* ctx);
+RAG_API int rag_check(rag_ctx* ctx);
 
 /* GEMM kernel durations (milliseconds) recorded since the last call to this function while
  * RAG_OPT_TIMING was on; synchronises those events.  Writes up to max_n values to out and returns
  * how many were recorded (>= 0), or a negative RAG_E* code. */
-int rag_kernel_times(rag_ctx* ctx, float* out, int max_n);
+RAG_API int rag_kernel_times(rag_ctx* ctx, float* out, int max_n);
 
 /* Text for the last non-zero return on the calling thread ("" if none). */
-const char* rag_last_error(void);
+RAG_API const char* rag_last_error(void);
 
 /* Library version, major * 10000 + minor * 100 + patch. */
-int rag_version(void);
+RAG_API int rag_version(void);
 
 #ifdef __cplusplus
 }

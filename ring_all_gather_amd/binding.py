@@ -30,10 +30,11 @@ RAG_BF16, RAG_FP8_E4M3 = 0, 1
 RAG_STAGED_OUT, RAG_NO_COPY, RAG_COPY_ONLY = 1, 2, 4
 RAG_OPT_COPY_ENGINE, RAG_OPT_COMM_WGS, RAG_OPT_SPIN_LIMIT_US = 1, 2, 3
 RAG_OPT_ARRIVAL_DELAY_US, RAG_OPT_WITHHOLD_MASK, RAG_OPT_TIMING, RAG_OPT_TILE = 4, 5, 6, 7
-TILES = {"auto": 0, "128x128": 1, "256x128": 2, "256x256": 3, "256x256w8": 4}
+TILES = {"auto": 0, "128x128": 1, "256x128": 2, "256x256": 3, "256x256w8": 4, "256x256w8s4": 5}
 RAG_MAX_TP = 16
 
 _lib = None
+_is_finalizing = sys.is_finalizing
 _live = weakref.WeakSet()     # open contexts, closed at exit before the runtime shuts down
 
 
@@ -83,7 +84,8 @@ def declared_functions():
     with open(HEADER) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*RAG_API\s+(?:const\s+)?\w+\s*\**\s*(\w+)\s*\(", text,
+                                 flags=re.M)))
 
 
 def last_error() -> str:
@@ -153,7 +155,7 @@ class Context:
     def __del__(self):
         # During interpreter shutdown the HIP runtime may already be going away: leave the
         # context to the process exit (atexit above closes it earlier in a normal exit).
-        if sys.is_finalizing():
+        if _is_finalizing():
             return
         try:
             self.close()

@@ -8,6 +8,8 @@
 // releases the chunk's counter with the call's epoch, so tiles of that chunk can start while the
 // next chunk is still being copied.  It needs no LDS and few registers, so its waves fit beside
 // the GEMM's on every compute unit.
+#pragma once
+
 #include <hip/hip_runtime.h>
 
 #include "kernels.hpp"
@@ -16,10 +18,10 @@ namespace ringag {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int kArrThreads = 256;
+constexpr int kArrThreads = kArrivalThreads;
 constexpr int kArrUnroll = 8;
 
-__global__ void __launch_bounds__(kArrThreads) arrival_kernel(ArrivalArgs a) {
+__device__ __forceinline__ void arrival_body(const ArrivalArgs& a) {
   const unsigned long long nvec = a.bytes / 16;
   const unsigned long long per = (nvec + gridDim.x - 1) / gridDim.x;
   const unsigned long long beg = min(nvec, (unsigned long long)blockIdx.x * per);
@@ -58,22 +60,6 @@ __global__ void __launch_bounds__(kArrThreads) arrival_kernel(ArrivalArgs a) {
       }
     }
   }
-}
-
-hipError_t launch_arrival(const ArrivalArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(arrival_kernel, dim3(grid), dim3(kArrThreads), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t arrival_kernel_info(KernelInfo* info) {
-  hipFuncAttributes at;
-  hipError_t e = hipFuncGetAttributes(&at, (const void*)arrival_kernel);
-  if (e != hipSuccess) return e;
-  info->threads = kArrThreads;
-  info->lds_bytes = (int)at.sharedSizeBytes;
-  info->vgprs_per_wave = at.numRegs;
-  info->max_blocks_per_cu = 0;
-  return hipSuccess;
 }
 
 }  // namespace ringag

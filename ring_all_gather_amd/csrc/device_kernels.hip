@@ -1,0 +1,33 @@
+// The library's GPU code: every kernel entry point, compiled on its own into one gfx950 code
+// object (hipcc --genco).  The host side embeds that object and loads it explicitly per device
+// (launch.cpp), so the shared library holds no compiler-generated registration code.
+//
+// Entry points: rag_ag_<bf16|fp8>_<tile>, rag_rs_<tile>, rag_arrival.  Tile names:
+//   t128x128, t256x128, t256x256 (4 waves), t256x256w8 (8 waves, 2 stages), t256x256w8s4 (8 waves,
+//   4 stages); see gemm_core.hpp.
+#include "arrival_kernel.hpp"
+#include "gemm_ag_kernel.hpp"
+#include "gemm_rs_kernel.hpp"
+
+using namespace ringag;
+
+#define RAG_AG_ENTRY(TILE, SHAPE)                                                            \
+  extern "C" __global__ void __launch_bounds__(SHAPE::NT) rag_ag_bf16_##TILE(AgArgs a) {    \
+    ag_gemm_body<SHAPE, false>(a);                                                           \
+  }                                                                                          \
+  extern "C" __global__ void __launch_bounds__(SHAPE::NT) rag_ag_fp8_##TILE(AgArgs a) {     \
+    ag_gemm_body<SHAPE, true>(a);                                                            \
+  }                                                                                          \
+  extern "C" __global__ void __launch_bounds__(SHAPE::NT) rag_rs_##TILE(RsArgs a) {         \
+    gemm_rs_body<SHAPE>(a);                                                                  \
+  }
+
+RAG_AG_ENTRY(t128x128, Tile128x128)
+RAG_AG_ENTRY(t256x128, Tile256x128)
+RAG_AG_ENTRY(t256x256, Tile256x256)
+RAG_AG_ENTRY(t256x256w8, Tile256x256w8)
+RAG_AG_ENTRY(t256x256w8s4, Tile256x256w8s4)
+
+extern "C" __global__ void __launch_bounds__(kArrThreads) rag_arrival(ArrivalArgs a) {
+  arrival_body(a);
+}

@@ -4,17 +4,20 @@
 // (wi, wj) owns the (BI/WI) x (BJ/WJ) sub-tile at (wi * BI/WI, wj * BJ/WJ), made of 32 x 32 MFMA
 // blocks with fp32 accumulators.
 //
-// Data path per K step (128 bytes of K per row: 64 bf16 or 128 fp8 elements):
+// Data path per K step (BKB bytes of K per row: 64 or 128 bytes, i.e. 32/64 bf16 or 64/128 fp8):
 //   HBM/L2 --buffer_load_dwordx4 ... lds (16 B per lane, range-checked by the descriptor)--> LDS
 //   LDS --ds_read_b128--> VGPR fragments --v_mfma--> accumulators
-// LDS holds two stages: while the waves multiply stage s, the loads of stage s^1 are in flight.
-// The loads are issued with inline assembly so that the compiler, which cannot tell that they
-// write the other stage, does not wait for them before every read of the current one; the code
-// waits for them explicitly (vmcnt(0)) at the end of each step, before the barrier that hands the
-// stage to the readers.  Rows of 128 bytes are stored with their eight 16-byte segments permuted by
-// XOR with ((row >> 1) & 7): gfx950's LDS serves 256 bytes (64 banks) per cycle, i.e. 16 lanes of
-// a ds_read_b128, which read 16 consecutive rows at the same logical segment; even and odd rows
-// fall in different bank halves and the key gives the 8 rows of each parity 8 distinct segments.
+// LDS holds NS stages in a ring: while the waves multiply stage s, the loads of the next NS-1
+// stages are in flight, so a load has NS-1 steps of MFMA work to arrive.  The loads are issued with
+// inline assembly: the compiler cannot tell which stage they write, and would otherwise wait for
+// all of them before every LDS read.  Their completion is awaited explicitly with s_waitcnt
+// vmcnt(N), N = the loads issued after the stage about to be read, followed by the one barrier of
+// the step, which also tells the loads of the step that the stage they overwrite has been read.
+//
+// LDS layout: rows of BKB bytes, split into 16-byte segments whose order is permuted by an XOR
+// key of the row (swz).  gfx950's LDS serves 256 bytes (64 banks) per cycle, i.e. 16 lanes of a
+// ds_read_b128; an MFMA operand read has those 16 lanes on 16 consecutive rows at the same logical
+// segment, and the key spreads them over all 64 banks.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -25,39 +28,56 @@
 namespace ringag {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kRowBytes = 128;                 // bytes of K per row per stage
 constexpr uint32_t kOOB = 0x80000000u;         // voffset that is always past num_records
 
-template <int BI_, int BJ_, int WI_, int WJ_>
+template <int BI_, int BJ_, int WI_, int WJ_, int BKB_, int NS_>
 struct TileShape {
   static constexpr int BI = BI_, BJ = BJ_, WI = WI_, WJ = WJ_;
+  static constexpr int BKB = BKB_;               // bytes of K per row per stage
+  static constexpr int NS = NS_;                 // LDS stages
   static constexpr int NW = WI * WJ;             // waves
   static constexpr int NT = NW * 64;             // threads
   static constexpr int TM = BI / WI, TN = BJ / WJ;   // wave sub-tile
   static constexpr int FI = TM / 32, FJ = TN / 32;   // MFMA blocks per wave
-  static constexpr int STAGE = (BI + BJ) * kRowBytes;
-  static constexpr int XQ = BI / (8 * NW);       // 8-row load groups of X per wave
-  static constexpr int YQ = BJ / (8 * NW);
+  static constexpr int SEGS = BKB / 16;          // 16-byte segments per row
+  static constexpr int RPI = 1024 / BKB;         // rows written by one 64-lane DMA instruction
+  static constexpr int STAGE = (BI + BJ) * BKB;
+  static constexpr int XQ = BI / (RPI * NW);     // DMA instructions per wave per stage (X)
+  static constexpr int YQ = BJ / (RPI * NW);
+  static constexpr int LOADS = XQ + YQ;          // vmcnt increments per wave per stage
   // bf16 output staging: rows padded by 16 bytes so the two row halves a wave writes do not
   // share banks
   static constexpr int OUT_LD = BJ * 2 + 16;
-  static constexpr int LDS_MAIN = 2 * STAGE;
+  static constexpr int LDS_MAIN = NS * STAGE;
   static constexpr int LDS_OUT = BI * OUT_LD;
   static constexpr int LDS = LDS_MAIN > LDS_OUT ? LDS_MAIN : LDS_OUT;
-  static_assert(BI % (8 * NW) == 0 && BJ % (8 * NW) == 0, "load groups must divide evenly");
+  static_assert(BKB == 64 || BKB == 128, "rows of 64 or 128 bytes");
+  static_assert(NS >= 2 && NS <= 4, "2 to 4 stages");
+  static_assert(BI % (RPI * NW) == 0 && BJ % (RPI * NW) == 0, "load groups must divide evenly");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tiles are made of 32x32 blocks");
+  static_assert((NS - 2) * LOADS <= 63, "vmcnt field holds at most 63");
+  static_assert(LDS <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
 };
 
-using Tile128x128 = TileShape<128, 128, 2, 2>;
-using Tile256x128 = TileShape<256, 128, 2, 2>;
-using Tile256x256 = TileShape<256, 256, 2, 2>;     // 4 waves of 128x128
-using Tile256x256w8 = TileShape<256, 256, 2, 4>;   // 8 waves of 128x64
+// The configurations the kernels are built for.
+using Tile128x128 = TileShape<128, 128, 2, 2, 128, 2>;
+using Tile256x128 = TileShape<256, 128, 2, 2, 128, 2>;
+using Tile256x256 = TileShape<256, 256, 2, 2, 64, 4>;       // 4 waves of 128x128, 4 stages
+using Tile256x256w8 = TileShape<256, 256, 2, 4, 128, 2>;    // 8 waves of 128x64, 2 stages
+using Tile256x256w8s4 = TileShape<256, 256, 2, 4, 64, 4>;   // 8 waves of 128x64, 4 stages
+
+// Swizzle key of a tile row.  128-byte rows: 2 rows per 256-byte bank line, key (row >> 1) & 7
+// gives the 8 rows of each parity in a 16-row group 8 distinct segments.  64-byte rows: 4 rows per
+// line, key (row >> 2) & 3 gives the 4 rows of each residue 4 distinct segments.
+template <int BKB>
+__device__ inline int swz(int row) {
+  if constexpr (BKB == 128) return (row >> 1) & 7;
+  else return (row >> 2) & 3;
+}
 
 // Raw buffer descriptor (gfx9 family: base, stride 0, num_records = size in bytes, word 3 =
 // 0x00020000).  Loads at offsets >= num_records return zero instead of faulting, which is how
@@ -80,72 +100,74 @@ __device__ inline void dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
                : "memory", "m0");
 }
 
-__device__ inline void wait_vmem_all() {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+template <int N>
+__device__ inline void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 __device__ inline uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)p;
 }
 
-// Swizzle key of a tile row (see the header comment).
-__device__ inline int swz(int row) { return (row >> 1) & 7; }
-
-// Per-lane byte offsets (relative to the operand's first row) of the segments this lane loads in
-// each of its Q row groups.  Lane l of an 8-row group writes tile row 8 g + l/8 at physical segment
-// l%8, so it fetches logical segment (l%8) ^ swz(row).  Rows at or past rows_valid get kOOB
-// (zeros).  row0 is a multiple of 16, so tile-local and global rows share their swizzle key.
-template <int Q, int NW>
+// Per-lane byte offsets (relative to the operand's first row) of the segment this lane loads in
+// each of its Q row groups.  Lane l of a group writes tile row RPI g + l / SEGS at physical segment
+// l % SEGS, so it fetches logical segment (l % SEGS) ^ swz(row).  Rows at or past rows_valid get
+// kOOB (zeros).  row0 is a multiple of 16, so tile-local and global rows share their key.
+template <class S, int Q>
 __device__ inline void tile_offsets(uint32_t* voff, int row0, int rows_valid, uint32_t ld_bytes,
                                     int wave, int lane) {
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
-    const int lr = (q * NW + wave) * 8 + (lane >> 3);
-    const int logical = (lane & 7) ^ swz(lr);
+    const int lr = (q * S::NW + wave) * S::RPI + lane / S::SEGS;
+    const int logical = (lane % S::SEGS) ^ swz<S::BKB>(lr);
     const int r = row0 + lr;
     voff[q] = (r < rows_valid) ? (uint32_t)r * ld_bytes + (uint32_t)logical * 16u : kOOB;
   }
 }
 
-template <int Q, int NW>
+template <class S, int Q>
 __device__ inline void issue_loads(i32x4 rsrc, const uint32_t* voff, uint32_t kbytes,
                                    uint32_t lds_tile, int wave) {
 #pragma unroll
   for (int q = 0; q < Q; ++q)
-    dma16(rsrc, lds_tile + (uint32_t)((q * NW + wave) * 8 * kRowBytes), voff[q] + kbytes);
+    dma16(rsrc, lds_tile + (uint32_t)((q * S::NW + wave) * S::RPI * S::BKB), voff[q] + kbytes);
 }
 
-// Load one MFMA operand fragment (32 rows x 16 bytes of K per lane half) from a swizzled tile.
-// tile_rows is at a multiple of 32 rows, so the lane's row key is swz(lane & 31).
-__device__ inline bf16x8 frag_bf16(const char* tile_rows, int seg_logical, int lane) {
+// One MFMA operand fragment: rows (lane & 31) of a 32-row block starting at tile_rows (a multiple
+// of 32 rows into the tile), 16 bytes (bf16) or 32 bytes (fp8) at logical segment `seg`.
+template <int BKB>
+__device__ inline bf16x8 frag_bf16(const char* tile_rows, int seg, int lane) {
   const int r = lane & 31;
-  return *(const bf16x8*)(tile_rows + r * kRowBytes + ((seg_logical ^ swz(r)) << 4));
+  return *(const bf16x8*)(tile_rows + r * BKB + ((seg ^ swz<BKB>(r)) << 4));
 }
 
-__device__ inline i32x8 frag_fp8(const char* tile_rows, int seg_logical, int lane) {
+template <int BKB>
+__device__ inline i32x8 frag_fp8(const char* tile_rows, int seg, int lane) {
   const int r = lane & 31;
-  const char* row = tile_rows + r * kRowBytes;
-  const i32x4 lo = *(const i32x4*)(row + ((seg_logical ^ swz(r)) << 4));
-  const i32x4 hi = *(const i32x4*)(row + (((seg_logical + 1) ^ swz(r)) << 4));
+  const char* row = tile_rows + r * BKB;
+  const i32x4 lo = *(const i32x4*)(row + ((seg ^ swz<BKB>(r)) << 4));
+  const i32x4 hi = *(const i32x4*)(row + (((seg + 1) ^ swz<BKB>(r)) << 4));
   return (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// Multiply one stage held in LDS.  bf16: 4 MFMA k-steps of 16 (v_mfma_f32_32x32x16_bf16); fp8
-// E4M3: 2 k-steps of 64 (v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales).  Lane l of a 32x32
-// operand fragment holds row (l & 31) and the (l >> 5)-th half of the k-step; X (MFMA A operand,
-// output rows) and Y (B operand, output columns) use the same k assignment.
+// Multiply one stage held in LDS.  bf16: k-steps of 16 (v_mfma_f32_32x32x16_bf16); fp8 E4M3:
+// k-steps of 64 (v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales).  Lane l of a 32x32 operand
+// fragment holds row (l & 31) and the (l >> 5)-th half of the k-step; X (MFMA A operand, output
+// rows) and Y (B operand, output columns) use the same k assignment.
 template <class S, bool FP8>
 __device__ inline void stage_mma(const char* xs, const char* ys, int lane,
                                  f32x16 (&acc)[S::FI][S::FJ]) {
   const int h = lane >> 5;
   if constexpr (!FP8) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < S::SEGS / 2; ++kk) {
       bf16x8 a[S::FI], b[S::FJ];
 #pragma unroll
-      for (int f = 0; f < S::FI; ++f) a[f] = frag_bf16(xs + f * 32 * kRowBytes, kk * 2 + h, lane);
+      for (int f = 0; f < S::FI; ++f)
+        a[f] = frag_bf16<S::BKB>(xs + f * 32 * S::BKB, kk * 2 + h, lane);
 #pragma unroll
-      for (int f = 0; f < S::FJ; ++f) b[f] = frag_bf16(ys + f * 32 * kRowBytes, kk * 2 + h, lane);
+      for (int f = 0; f < S::FJ; ++f)
+        b[f] = frag_bf16<S::BKB>(ys + f * 32 * S::BKB, kk * 2 + h, lane);
 #pragma unroll
       for (int i = 0; i < S::FI; ++i)
 #pragma unroll
@@ -154,12 +176,14 @@ __device__ inline void stage_mma(const char* xs, const char* ys, int lane,
     }
   } else {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < S::SEGS / 4; ++kk) {
       i32x8 a[S::FI], b[S::FJ];
 #pragma unroll
-      for (int f = 0; f < S::FI; ++f) a[f] = frag_fp8(xs + f * 32 * kRowBytes, kk * 4 + h * 2, lane);
+      for (int f = 0; f < S::FI; ++f)
+        a[f] = frag_fp8<S::BKB>(xs + f * 32 * S::BKB, kk * 4 + h * 2, lane);
 #pragma unroll
-      for (int f = 0; f < S::FJ; ++f) b[f] = frag_fp8(ys + f * 32 * kRowBytes, kk * 4 + h * 2, lane);
+      for (int f = 0; f < S::FJ; ++f)
+        b[f] = frag_fp8<S::BKB>(ys + f * 32 * S::BKB, kk * 4 + h * 2, lane);
 #pragma unroll
       for (int i = 0; i < S::FI; ++i)
 #pragma unroll
@@ -172,7 +196,7 @@ __device__ inline void stage_mma(const char* xs, const char* ys, int lane,
 }
 
 // Full K loop of one tile.  rx/ry: descriptors of X and Y; xo/yo from tile_offsets; ksteps = K
-// bytes / 128.  Returns with acc = the wave's fp32 sub-tile and all waves past a final barrier
+// bytes / BKB.  Returns with acc = the wave's fp32 sub-tile and all waves past a final barrier
 // (LDS free for the epilogue).  The caller must have passed a barrier since the last LDS reads.
 template <class S, bool FP8>
 __device__ inline void tile_kloop(i32x4 rx, const uint32_t* xo, i32x4 ry, const uint32_t* yo,
@@ -187,24 +211,30 @@ __device__ inline void tile_kloop(i32x4 rx, const uint32_t* xo, i32x4 ry, const 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  issue_loads<S::XQ, S::NW>(rx, xo, 0, base, wave);
-  issue_loads<S::YQ, S::NW>(ry, yo, 0, base + S::BI * kRowBytes, wave);
-  wait_vmem_all();
-  __syncthreads();
-  for (int kt = 0; kt < ksteps; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < ksteps) {
-      const uint32_t kb = (uint32_t)(kt + 1) * kRowBytes;
-      const uint32_t nxt = base + (uint32_t)((cur ^ 1) * S::STAGE);
-      issue_loads<S::XQ, S::NW>(rx, xo, kb, nxt, wave);
-      issue_loads<S::YQ, S::NW>(ry, yo, kb, nxt + S::BI * kRowBytes, wave);
+  // prologue: stages 0 .. NS-2
+#pragma unroll
+  for (int s = 0; s < S::NS - 1; ++s) {
+    if (s < ksteps) {
+      const uint32_t st = base + (uint32_t)(s * S::STAGE);
+      issue_loads<S, S::XQ>(rx, xo, (uint32_t)(s * S::BKB), st, wave);
+      issue_loads<S, S::YQ>(ry, yo, (uint32_t)(s * S::BKB), st + S::BI * S::BKB, wave);
     }
-    const char* st = lds + cur * S::STAGE;
-    stage_mma<S, FP8>(st + wi * S::TM * kRowBytes, st + (S::BI + wj * S::TN) * kRowBytes, lane,
-                      acc);
-    wait_vmem_all();
-    __syncthreads();
   }
+  for (int kt = 0; kt < ksteps; ++kt) {
+    // stage kt is complete once at most the loads of the stages after it are outstanding
+    if (kt + S::NS - 2 < ksteps) wait_vmem<(S::NS - 2) * S::LOADS>();
+    else wait_vmem<0>();
+    __syncthreads();
+    const int nx = kt + S::NS - 1;
+    if (nx < ksteps) {
+      const uint32_t st = base + (uint32_t)((nx % S::NS) * S::STAGE);
+      issue_loads<S, S::XQ>(rx, xo, (uint32_t)nx * S::BKB, st, wave);
+      issue_loads<S, S::YQ>(ry, yo, (uint32_t)nx * S::BKB, st + S::BI * S::BKB, wave);
+    }
+    const char* st = lds + (kt % S::NS) * S::STAGE;
+    stage_mma<S, FP8>(st + wi * S::TM * S::BKB, st + (S::BI + wj * S::TN) * S::BKB, lane, acc);
+  }
+  __syncthreads();
 }
 
 // Output coordinates of accumulator element e of block (i, j) for this lane, relative to the
@@ -215,9 +245,9 @@ __device__ inline int acc_row(int i, int e, int lane) {
 __device__ inline int acc_col(int j, int lane) { return j * 32 + (lane & 31); }
 
 // Epilogue for bf16 output: the accumulators (times `scale`) are rounded to bf16 into an LDS
-// tile, then written out row by row with 16-byte stores (whole 64-byte+ row segments per group of
-// lanes).  out points at row 0 of the tile's rows; ld = row stride in elements; rows/cols valid =
-// how much of the tile lies inside the output.  Ends with a barrier (LDS free again).
+// tile, then written out row by row with 16-byte stores.  out points at row 0 / column 0 of the
+// tile; ld = row stride in elements; rows/cols valid = how much of the tile lies inside the
+// output.  Ends with a barrier (LDS free again).
 template <class S>
 __device__ inline void store_tile_bf16(const f32x16 (&acc)[S::FI][S::FJ], float scale, char* lds,
                                        __bf16* out, int ld, int rows_valid, int cols_valid,
@@ -235,10 +265,10 @@ __device__ inline void store_tile_bf16(const f32x16 (&acc)[S::FI][S::FJ], float 
       }
     }
   __syncthreads();
-  constexpr int SEGS = S::BJ / 8;   // 16-byte segments per tile row
+  constexpr int OSEGS = S::BJ / 8;   // 16-byte segments per tile row
   const bool vec = (ld % 8) == 0 && (((uintptr_t)out) & 15u) == 0;
-  for (int idx = threadIdx.x; idx < S::BI * SEGS; idx += S::NT) {
-    const int r = idx / SEGS, sg = idx % SEGS;
+  for (int idx = threadIdx.x; idx < S::BI * OSEGS; idx += S::NT) {
+    const int r = idx / OSEGS, sg = idx % OSEGS;
     const int c = sg * 8;
     if (r >= rows_valid || c >= cols_valid) continue;
     const char* src = lds + r * S::OUT_LD + c * 2;

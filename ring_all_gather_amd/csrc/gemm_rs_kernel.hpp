@@ -9,26 +9,21 @@
 // another rank's chunk store their fp32 accumulators to `send` (the outgoing contribution).
 // Tiles of the own chunk add the peers' fp32 partials to the accumulators while they are still in
 // registers and store the bf16 result: the reduction costs no extra pass over D.
+#pragma once
+
 #include "gemm_core.hpp"
 #include "kernels.hpp"
 
 namespace ringag {
 
-__device__ inline void map_tile_rs(int u, int U, int R, int* rb, int* cb) {
-  int v = u;
-  if ((U & 7) == 0) v = (u & 7) * (U >> 3) + (u >> 3);
-  *rb = v % R;
-  *cb = v / R;
-}
-
 template <class S>
-__global__ void __launch_bounds__(S::NT) gemm_rs_kernel(RsArgs a) {
+__device__ __forceinline__ void gemm_rs_body(const RsArgs& a) {
   __shared__ __attribute__((aligned(1024))) char lds[S::LDS];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wi = wave / S::WJ, wj = wave % S::WJ;
   const uint32_t ldb = (uint32_t)a.Kl * 2u;
-  const int ksteps = (int)(ldb / kRowBytes);
+  const int ksteps = (int)(ldb / S::BKB);
   const int U = a.tiles_i * a.tiles_j;
   const int total = U * a.tp;
   const i32x4 ry = make_rsrc(a.W, (uint32_t)a.Mo * ldb);
@@ -40,12 +35,12 @@ __global__ void __launch_bounds__(S::NT) gemm_rs_kernel(RsArgs a) {
     const bool own = (c == a.self_rank);
     if (!own && a.send == nullptr) continue;
     int rb, cb;
-    map_tile_rs(u, U, a.tiles_i, &rb, &cb);
+    map_tile_xcd(u, U, a.tiles_i, a.tiles_j, a.xcd_rows, &rb, &cb);
     const char* xbase = (const char*)a.X + (size_t)c * a.nc * ldb;
     const i32x4 rx = make_rsrc(xbase, (uint32_t)a.nc * ldb);
     uint32_t xo[S::XQ], yo[S::YQ];
-    tile_offsets<S::XQ, S::NW>(xo, rb * S::BI, a.nc, ldb, wave, lane);
-    tile_offsets<S::YQ, S::NW>(yo, cb * S::BJ, a.Mo, ldb, wave, lane);
+    tile_offsets<S, S::XQ>(xo, rb * S::BI, a.nc, ldb, wave, lane);
+    tile_offsets<S, S::YQ>(yo, cb * S::BJ, a.Mo, ldb, wave, lane);
     f32x16 acc[S::FI][S::FJ];
     tile_kloop<S, false>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);
 
@@ -93,45 +88,6 @@ __global__ void __launch_bounds__(S::NT) gemm_rs_kernel(RsArgs a) {
           }
         }
     }
-  }
-}
-
-template <class S>
-static hipError_t launch_t(const RsArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_rs_kernel<S>), dim3(grid), dim3(S::NT), 0, s, a);
-  return hipGetLastError();
-}
-
-template <class S>
-static hipError_t info_t(KernelInfo* info) {
-  hipFuncAttributes at;
-  hipError_t e = hipFuncGetAttributes(&at, (const void*)gemm_rs_kernel<S>);
-  if (e != hipSuccess) return e;
-  int nb = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, gemm_rs_kernel<S>, S::NT, 0);
-  if (e != hipSuccess) return e;
-  info->threads = S::NT;
-  info->lds_bytes = (int)at.sharedSizeBytes;
-  info->vgprs_per_wave = at.numRegs;
-  info->max_blocks_per_cu = nb;
-  return hipSuccess;
-}
-
-hipError_t launch_gemm_rs(const RsArgs& a, int tile, int grid, hipStream_t s) {
-  switch (tile) {
-    case kTile256x256: return launch_t<Tile256x256>(a, grid, s);
-    case kTile256x256w8: return launch_t<Tile256x256w8>(a, grid, s);
-    case kTile256x128: return launch_t<Tile256x128>(a, grid, s);
-    default: return launch_t<Tile128x128>(a, grid, s);
-  }
-}
-
-hipError_t rs_kernel_info(int tile, KernelInfo* info) {
-  switch (tile) {
-    case kTile256x256: return info_t<Tile256x256>(info);
-    case kTile256x256w8: return info_t<Tile256x256w8>(info);
-    case kTile256x128: return info_t<Tile256x128>(info);
-    default: return info_t<Tile128x128>(info);
   }
 }
 

@@ -1,9 +1,16 @@
-// Internal interface between the host runtime (runtime.cpp) and the kernel translation units.
+// Internal interface shared by the host runtime (runtime.cpp, launch.cpp) and the device code
+// (device_kernels.hip): kernel argument structs, tile geometry and the tile-to-XCD mapping.
 // Nothing here is part of the public ABI.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
+
+#ifndef __HIPCC__
+#define RAG_HD
+#else
+#define RAG_HD __host__ __device__
+#endif
 
 namespace ringag {
 
@@ -24,6 +31,7 @@ struct AgArgs {
   const float* scale_A;          // fp8: dequantisation factors (device scalars)
   const float* scale_B;
   int tiles_i, tiles_j;          // tile grid of one chunk
+  int xcd_rows;                  // XCD rectangle split (see map_tile_xcd); 0 = linear order
 };
 
 // Arguments of the GEMM+RS kernel.  Row-chunk positions j = 0..tp-1 in visiting order; the last
@@ -38,6 +46,7 @@ struct RsArgs {
   void* D;                       // [nc, Mo] bf16
   int T, Kl, Mo, nc, tp, self_rank;
   int tiles_i, tiles_j;
+  int xcd_rows;
 };
 
 // Arguments of the arrival (producer) kernel: copies j = 0..n-1 in order, each followed (when
@@ -56,7 +65,9 @@ struct ArrivalArgs {
   unsigned withhold_mask;        // test hook: bit pos set = never release that chunk
 };
 
-enum TileCfg { kTile128x128 = 1, kTile256x128 = 2, kTile256x256 = 3, kTile256x256w8 = 4 };
+enum TileCfg {
+  kTile128x128 = 1, kTile256x128 = 2, kTile256x256 = 3, kTile256x256w8 = 4, kTile256x256w8s4 = 5
+};
 
 struct KernelInfo {
   int threads;
@@ -65,21 +76,69 @@ struct KernelInfo {
   int max_blocks_per_cu;
 };
 
-// Launchers: enqueue on `stream`, return hipError_t of the launch.
-hipError_t launch_ag_gemm(const AgArgs& a, int tile, bool fp8, int grid, hipStream_t stream);
-hipError_t launch_gemm_rs(const RsArgs& a, int tile, int grid, hipStream_t stream);
-hipError_t launch_arrival(const ArrivalArgs& a, int grid, hipStream_t stream);
+// Kernel loading and launching (launch.cpp).  load_kernels loads the embedded code object on
+// `device` once per process (kept until the process ends, so nothing of the library runs at exit);
+// the launchers enqueue on `stream` (the current device must be `device`) and return the
+// hipError_t of the launch.
+hipError_t load_kernels(int device);
+hipError_t launch_ag_gemm(int device, const AgArgs& a, int tile, bool fp8, int grid,
+                          hipStream_t stream);
+hipError_t launch_gemm_rs(int device, const RsArgs& a, int tile, int grid, hipStream_t stream);
+hipError_t launch_arrival(int device, const ArrivalArgs& a, int grid, hipStream_t stream);
 
 // Occupancy / resource facts for a kernel variant (cached by the caller).
-hipError_t ag_kernel_info(int tile, bool fp8, KernelInfo* info);
-hipError_t rs_kernel_info(int tile, KernelInfo* info);
-hipError_t arrival_kernel_info(KernelInfo* info);
+hipError_t ag_kernel_info(int device, int tile, bool fp8, KernelInfo* info);
+hipError_t rs_kernel_info(int device, int tile, KernelInfo* info);
+
+constexpr int kArrivalThreads = 256;   // block size of the arrival kernel
+
+// Threads per workgroup of a tile configuration (4 waves, or 8 for the 8-wave tiles).
+inline int tile_threads(int tile) {
+  return (tile == kTile256x256w8 || tile == kTile256x256w8s4) ? 512 : 256;
+}
+
+// Chunk-local tile u -> (row block rb, column block cb) of a chunk's R x C tile grid.
+// Workgroups are dealt round-robin to the 8 XCDs, each with its own L2; with the persistent grid
+// and the chunk's tile count both multiples of 8, tile u runs on XCD u % 8.  With xcd_rows = a
+// (a divides 8, R % a == 0, C % (8 / a) == 0) the grid is cut into an a x (8/a) array of equal
+// rectangles and XCD x gets rectangle (x % a, x / a) in every chunk: its L2 then serves R/a row
+// blocks of the chunk and C/(8/a) column blocks of the weight, the same columns in every chunk.
+// xcd_rows = 0 (or shapes that do not divide) keeps row-block-fastest linear order.
+RAG_HD inline void map_tile_xcd(int u, int U, int R, int C, int a, int* rb, int* cb) {
+  if (a > 0 && (U & 7) == 0 && R % a == 0 && C % (8 / a) == 0) {
+    const int x = u & 7, q = u >> 3;
+    const int rr = R / a, cc = C / (8 / a);
+    *rb = (x % a) * rr + q % rr;
+    *cb = (x / a) * cc + q / rr;
+    return;
+  }
+  *rb = u % R;
+  *cb = u / R;
+}
+
+// The split a in {1, 2, 4, 8} that minimises the rows an XCD's L2 must hold when `chunks`
+// chunks' tiles run at once: chunks * (R / a) * bi + (C / (8 / a)) * bj; 0 if none divides.
+inline int choose_xcd_rows(int R, int C, int chunks, int bi, int bj) {
+  if ((R * C) % 8 != 0) return 0;
+  int best = 0;
+  long long best_rows = -1;
+  for (int a = 1; a <= 8; a *= 2) {
+    if (R % a || C % (8 / a)) continue;
+    const long long rows = (long long)chunks * (R / a) * bi + (long long)(C / (8 / a)) * bj;
+    if (best_rows < 0 || rows < best_rows) {
+      best_rows = rows;
+      best = a;
+    }
+  }
+  return best;
+}
 
 // Tile sizes of a configuration.
 inline void tile_dims(int tile, int* bi, int* bj) {
   switch (tile) {
     case kTile256x256:
-    case kTile256x256w8: *bi = 256; *bj = 256; break;
+    case kTile256x256w8:
+    case kTile256x256w8s4: *bi = 256; *bj = 256; break;
     case kTile256x128: *bi = 256; *bj = 128; break;
     default: *bi = 128; *bj = 128; break;
   }

@@ -1,0 +1,121 @@
+// Loading and launching the library's kernels.
+//
+// The kernels live in one gfx950 code object (device_kernels.hip, built with hipcc --genco) that
+// the build embeds into the shared library as a byte array.  load_kernels() loads it with
+// hipModuleLoadData on a device the first time a context is created there and keeps the module
+// (and the function handles) until the process ends.  The shared library therefore contains no
+// compiler-generated registration constructors or destructors: nothing of it runs at process exit,
+// when the HIP runtime itself may already be shutting down.
+#include <hip/hip_runtime_api.h>
+
+#include <mutex>
+
+#include "kernels.hpp"
+
+extern "C" const unsigned char ringag_kernels_co[];
+
+namespace ringag {
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int kTiles = 6;   // tile ids 1..5
+
+const char* const kAgName[2][kTiles] = {
+    {nullptr, "rag_ag_bf16_t128x128", "rag_ag_bf16_t256x128", "rag_ag_bf16_t256x256",
+     "rag_ag_bf16_t256x256w8", "rag_ag_bf16_t256x256w8s4"},
+    {nullptr, "rag_ag_fp8_t128x128", "rag_ag_fp8_t256x128", "rag_ag_fp8_t256x256",
+     "rag_ag_fp8_t256x256w8", "rag_ag_fp8_t256x256w8s4"}};
+const char* const kRsName[kTiles] = {nullptr, "rag_rs_t128x128", "rag_rs_t256x128",
+                                     "rag_rs_t256x256", "rag_rs_t256x256w8",
+                                     "rag_rs_t256x256w8s4"};
+
+struct DeviceKernels {
+  bool loaded = false;
+  hipModule_t module = nullptr;
+  hipFunction_t ag[2][kTiles] = {};
+  hipFunction_t rs[kTiles] = {};
+  hipFunction_t arrival = nullptr;
+};
+
+DeviceKernels g_dev[kMaxDevices];
+std::mutex g_mu;
+
+bool valid_tile(int tile) { return tile >= 1 && tile < kTiles; }
+
+hipError_t launch(hipFunction_t f, int grid, int threads, hipStream_t s, void* args) {
+  if (!f) return hipErrorInvalidDeviceFunction;
+  void* params[] = {args};
+  return hipModuleLaunchKernel(f, grid, 1, 1, threads, 1, 1, 0, s, params, nullptr);
+}
+
+hipError_t info(hipFunction_t f, int threads, KernelInfo* out) {
+  if (!f) return hipErrorInvalidDeviceFunction;
+  int regs = 0, lds = 0, nb = 0;
+  hipError_t e = hipFuncGetAttribute(&regs, HIP_FUNC_ATTRIBUTE_NUM_REGS, f);
+  if (e == hipSuccess) e = hipFuncGetAttribute(&lds, HIP_FUNC_ATTRIBUTE_SHARED_SIZE_BYTES, f);
+  if (e == hipSuccess) e = hipModuleOccupancyMaxActiveBlocksPerMultiprocessor(&nb, f, threads, 0);
+  if (e != hipSuccess) return e;
+  out->threads = threads;
+  out->lds_bytes = lds;
+  out->vgprs_per_wave = regs;
+  out->max_blocks_per_cu = nb;
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t load_kernels(int device) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceKernels& d = g_dev[device];
+  if (d.loaded) return hipSuccess;
+  hipError_t e = hipSetDevice(device);
+  if (e != hipSuccess) return e;
+  hipModule_t m = nullptr;
+  e = hipModuleLoadData(&m, ringag_kernels_co);
+  if (e != hipSuccess) return e;
+  for (int fp8 = 0; fp8 < 2; ++fp8)
+    for (int t = 1; t < kTiles; ++t)
+      if ((e = hipModuleGetFunction(&d.ag[fp8][t], m, kAgName[fp8][t])) != hipSuccess) return e;
+  for (int t = 1; t < kTiles; ++t)
+    if ((e = hipModuleGetFunction(&d.rs[t], m, kRsName[t])) != hipSuccess) return e;
+  if ((e = hipModuleGetFunction(&d.arrival, m, "rag_arrival")) != hipSuccess) return e;
+  d.module = m;
+  d.loaded = true;
+  return hipSuccess;
+}
+
+hipError_t launch_ag_gemm(int device, const AgArgs& a, int tile, bool fp8, int grid,
+                          hipStream_t s) {
+  if (device < 0 || device >= kMaxDevices || !g_dev[device].loaded || !valid_tile(tile))
+    return hipErrorInvalidValue;
+  AgArgs copy = a;
+  return launch(g_dev[device].ag[fp8 ? 1 : 0][tile], grid, tile_threads(tile), s, &copy);
+}
+
+hipError_t launch_gemm_rs(int device, const RsArgs& a, int tile, int grid, hipStream_t s) {
+  if (device < 0 || device >= kMaxDevices || !g_dev[device].loaded || !valid_tile(tile))
+    return hipErrorInvalidValue;
+  RsArgs copy = a;
+  return launch(g_dev[device].rs[tile], grid, tile_threads(tile), s, &copy);
+}
+
+hipError_t launch_arrival(int device, const ArrivalArgs& a, int grid, hipStream_t s) {
+  if (device < 0 || device >= kMaxDevices || !g_dev[device].loaded) return hipErrorInvalidValue;
+  ArrivalArgs copy = a;
+  return launch(g_dev[device].arrival, grid, kArrivalThreads, s, &copy);
+}
+
+hipError_t ag_kernel_info(int device, int tile, bool fp8, KernelInfo* out) {
+  if (device < 0 || device >= kMaxDevices || !g_dev[device].loaded || !valid_tile(tile))
+    return hipErrorInvalidValue;
+  return info(g_dev[device].ag[fp8 ? 1 : 0][tile], tile_threads(tile), out);
+}
+
+hipError_t rs_kernel_info(int device, int tile, KernelInfo* out) {
+  if (device < 0 || device >= kMaxDevices || !g_dev[device].loaded || !valid_tile(tile))
+    return hipErrorInvalidValue;
+  return info(g_dev[device].rs[tile], tile_threads(tile), out);
+}
+
+}  // namespace ringag

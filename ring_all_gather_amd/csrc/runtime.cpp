@@ -13,7 +13,7 @@
 // streams fork from and join the main stream through events).  Counters are compared with a
 // per-call epoch instead of being reset by a kernel, so a late producer of one call can never be
 // mistaken for the next call's.
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <algorithm>
 #include <cstdarg>
@@ -86,10 +86,10 @@ struct rag_ctx {
   std::vector<hipEvent_t> t_start, t_stop;
   int n_timed = 0;
   // occupancy cache: [tile][fp8]
-  KernelInfo ag_info[4][2] = {};
-  bool ag_info_ok[4][2] = {};
-  KernelInfo rs_info[4] = {};
-  bool rs_info_ok[4] = {};
+  KernelInfo ag_info[6][2] = {};
+  bool ag_info_ok[6][2] = {};
+  KernelInfo rs_info[6] = {};
+  bool rs_info_ok[6] = {};
 };
 
 namespace {
@@ -214,7 +214,13 @@ int rag_create(rag_ctx** out, int device, int max_tp, int flags) {
   if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, device) == hipSuccess && khz > 0)
     c->wall_khz = khz;
   const size_t nwords = (size_t)max_tp + (size_t)max_tp + 2 + 1;
-  hipError_t e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);
+  hipError_t e = load_kernels(device);
+  if (e != hipSuccess) {
+    delete c;
+    return fail(RAG_EHIP, "rag_create: loading the gfx950 kernels on device %d failed: %s", device,
+                hipGetErrorString(e));
+  }
+  e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming);
   if (e == hipSuccess) e = hipMalloc((void**)&c->words, nwords * sizeof(int));
@@ -288,7 +294,7 @@ int rag_set_option(rag_ctx* c, int key, long long v) {
       c->timing = v != 0;
       return RAG_OK;
     case RAG_OPT_TILE:
-      if (v < RAG_TILE_AUTO || v > RAG_TILE_256x256_8W) return fail(RAG_EINVAL, "unknown tile %lld", v);
+      if (v < RAG_TILE_AUTO || v > RAG_TILE_256x256_8W_S4) return fail(RAG_EINVAL, "unknown tile %lld", v);
       c->tile = (int)v;
       return RAG_OK;
     default:
@@ -411,7 +417,7 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
       aa.epoch = epoch;
       aa.delay_ticks = c->delay_us * c->wall_khz / 1000;
       aa.withhold_mask = c->withhold;
-      if (n > 0) HIPCHK(launch_arrival(aa, c->comm_wgs, c->side));
+      if (n > 0) HIPCHK(launch_arrival(c->device, aa, c->comm_wgs, c->side));
     } else {
       for (int j = 1; j < tp; ++j) {
         const int r = order[j];
@@ -453,23 +459,30 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
     a.tiles_i = (nc + bi - 1) / bi;
     a.tiles_j = (M + bj - 1) / bj;
     if (!c->ag_info_ok[tile][fp8]) {
-      HIPCHK(ag_kernel_info(tile, fp8, &c->ag_info[tile][fp8]));
+      HIPCHK(ag_kernel_info(c->device, tile, fp8, &c->ag_info[tile][fp8]));
       c->ag_info_ok[tile][fp8] = true;
     }
     const int total = a.tiles_i * a.tiles_j * tp;
     const int grid = persistent_grid(total, c->num_cus - reserved_cus(tile, !no_copy),
                                      c->ag_info[tile][fp8].max_blocks_per_cu);
+    {
+      const int U = a.tiles_i * a.tiles_j;
+      const int concurrent = std::min(tp, std::max(1, (grid + U - 1) / U));
+      a.xcd_rows = (grid % 8 == 0) ? choose_xcd_rows(a.tiles_i, a.tiles_j, concurrent, bi, bj) : 0;
+    }
     if (debug_enabled())
       fprintf(stderr, "[ringag] ag_gemm tp=%d s=%d nc=%d K=%d M=%d %s tile=%dx%d tiles=%d grid=%d "
-              "(blocks/CU %d, VGPRs %d, LDS %d) engine=%s comm_wgs=%d flags=0x%x epoch=%d\n",
+              "(blocks/CU %d, VGPRs %d, LDS %d) xcd_rows=%d engine=%s comm_wgs=%d flags=0x%x "
+              "epoch=%d\n",
               tp, self_rank, nc, K, M, fp8 ? "fp8" : "bf16", bi, bj, total, grid,
               c->ag_info[tile][fp8].max_blocks_per_cu, c->ag_info[tile][fp8].vgprs_per_wave,
-              c->ag_info[tile][fp8].lds_bytes, c->copy_engine ? "sdma" : "kernel", c->comm_wgs,
+              c->ag_info[tile][fp8].lds_bytes, a.xcd_rows, c->copy_engine ? "sdma" : "kernel",
+              c->comm_wgs,
               flags, epoch);
     bool rec = false;
     int rc = record_timing_start(c, stream, &rec);
     if (rc) return rc;
-    HIPCHK(launch_ag_gemm(a, tile, fp8, grid, stream));
+    HIPCHK(launch_ag_gemm(c->device, a, tile, fp8, grid, stream));
     rc = record_timing_stop(c, stream, rec);
     if (rc) return rc;
   }
@@ -567,18 +580,23 @@ int gemm_rs(rag_ctx* c, const void* X, int T, int Kl, const void* W, int Mo,
   a.tiles_i = (nc + bi - 1) / bi;
   a.tiles_j = (Mo + bj - 1) / bj;
   if (!c->rs_info_ok[tile]) {
-    HIPCHK(rs_kernel_info(tile, &c->rs_info[tile]));
+    HIPCHK(rs_kernel_info(c->device, tile, &c->rs_info[tile]));
     c->rs_info_ok[tile] = true;
   }
   const int total = a.tiles_i * a.tiles_j * tp;
   const int grid = persistent_grid(total, c->num_cus, c->rs_info[tile].max_blocks_per_cu);
+  {
+    const int U = a.tiles_i * a.tiles_j;
+    const int concurrent = std::min(tp, std::max(1, (grid + U - 1) / U));
+    a.xcd_rows = (grid % 8 == 0) ? choose_xcd_rows(a.tiles_i, a.tiles_j, concurrent, bi, bj) : 0;
+  }
   if (debug_enabled())
     fprintf(stderr, "[ringag] gemm_rs tp=%d s=%d T=%d Kl=%d Mo=%d tile=%dx%d tiles=%d grid=%d\n",
             tp, self_rank, T, Kl, Mo, bi, bj, total, grid);
   bool rec = false;
   int rc = record_timing_start(c, stream, &rec);
   if (rc) return rc;
-  HIPCHK(launch_gemm_rs(a, tile, grid, stream));
+  HIPCHK(launch_gemm_rs(c->device, a, tile, grid, stream));
   return record_timing_stop(c, stream, rec);
 }
 

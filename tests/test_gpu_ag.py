@@ -12,7 +12,7 @@ from gpu_common import (AGRun, TOL_BF16, TOL_FP8, ctx, oracle_ag, oracle_ag_rows
 
 pytestmark = pytest.mark.gpu
 
-TILE_NAMES = ["128x128", "256x128", "256x256", "256x256w8"]
+TILE_NAMES = ["128x128", "256x128", "256x256", "256x256w8", "256x256w8s4"]
 
 
 @pytest.fixture(autouse=True)

@@ -56,7 +56,7 @@ def _check_send(run, send_ref, exact=False):
             assert np.abs(got[c] - send_ref[c]).max() <= TOL_SEND * scale
 
 
-@pytest.mark.parametrize("tile", ["128x128", "256x128", "256x256", "256x256w8"])
+@pytest.mark.parametrize("tile", ["128x128", "256x128", "256x256", "256x256w8", "256x256w8s4"])
 def test_rs_ragged_random(tile):
     c = ctx()
     c.set_option(B.RAG_OPT_TILE, B.TILES[tile])
