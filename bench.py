@@ -26,6 +26,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}   # 256 CU x 2.4 GHz x (4096 | 8192) flop/clk
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "ag_4k_gemm_hbm_traffic.json")
 PEAK_HBM_GBS = 8000.0
 METRICS = {
     "ag": "AG+GEMM TFLOP/s (+% MFMA peak) and overlap efficiency, M=K=N=4096 tp=4",
@@ -127,6 +128,19 @@ def cpu_baseline_rs(inp, target_s):
                       f"MACs, fp32 triple loop), {dt:.1f} s wall"}
 
 
+def measured_traffic(kernel: str, fingerprint: str):
+    """HBM bytes per launch from the committed counter record, if it was taken with this exact
+    build of the kernels and this kernel; otherwise None."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernels_sha256") != fingerprint or rec.get("kernel") != kernel:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -175,6 +189,9 @@ def main():
         flops = shape.flops
         kernel_ms = statistics.fmean(kt)
         achieved = flops / (kernel_ms * 1e-3) / 1e12
+        kname = ctx.ag_kernel_name(shape.nc, shape.M, shape.dtype == "fp8")
+        traffic = measured_traffic(kname, B.kernels_fingerprint()) \
+            if args.workload == "ag_4k" else None
         peak = PEAK_TFLOPS[shape.dtype]
         value = flops / (ms * 1e-3) / 1e12
         out = {
@@ -198,8 +215,8 @@ def main():
                         "hidden_fraction": round((ms_copy + ms_gemm - ms) / ms_copy, 4),
                         "t_staged_out_ms": round(ms_staged, 5)},
             "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                         "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
-                         "kernel": "ag_gemm_kernel", "kernel_ms": round(kernel_ms, 5)},
+                         "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+                         "kernel": kname, "kernel_ms": round(kernel_ms, 5)},
         }
         if not args.no_cpu:
             out["cpu_baseline"] = cpu_baseline_ag(inp, args.cpu_seconds)
@@ -239,7 +256,7 @@ def main():
                         "p90": round(pctl(per, 0.9), 5)},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                         "kernel": "gemm_rs_kernel", "kernel_ms": round(kernel_ms, 5),
+                         "kernel": "rag_rs (tile %s)" % args.tile, "kernel_ms": round(kernel_ms, 5),
                          "algorithmic_bytes": alg_bytes},
         }
         if not args.no_cpu:

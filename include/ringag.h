@@ -95,7 +95,20 @@ enum {
     RAG_OPT_WITHHOLD_MASK = 5,  /* test hook: bit j set = never bump the counter of the chunk at
                                    ring position j (1..tp-1); the waiting tiles then time out */
     RAG_OPT_TIMING = 6,         /* 1 = record HIP events around every GEMM launch (rag_kernel_times) */
-    RAG_OPT_TILE = 7            /* GEMM tile configuration: 0 = automatic, else a RAG_TILE_* value */
+    RAG_OPT_TILE = 7,           /* GEMM tile configuration: 0 = automatic, else a RAG_TILE_* value */
+    RAG_OPT_TRACE_BUF = 8,      /* diagnostics: device address of a buffer of 64-bit words that the
+                                   next ag_gemm calls fill with wall-clock stamps (100 MHz): words
+                                   0..tp-2 = release time of the chunk at ring position 1..tp-1,
+                                   word 32 = start of the copies, then 4 words per GEMM tile in
+                                   ring order from word 64 (start, after its wait, end, location);
+                                   0 = off (default) */
+    RAG_OPT_TRACE_BYTES = 9,    /* diagnostics: size of that buffer; a call whose stamps would not
+                                   fit records none */
+    RAG_OPT_WGS_PER_CU = 10,    /* GEMM workgroups resident per compute unit: 0 = as many as fit
+                                   (default), n = at most n (fewer, longer-lived workgroups take the
+                                   ring's chunks in more rounds) */
+    RAG_OPT_COPY_PRIORITY = 11  /* 1 (default) = copy-kernel waves issue at the highest wave
+                                   priority, 0 = normal */
 };
 
 /* Tile configurations (rows of D x columns of D per workgroup; 4 waves unless stated). */
@@ -188,6 +201,11 @@ RAG_API int rag_check(rag_ctx* ctx);
  * RAG_OPT_TIMING was on; synchronises those events.  Writes up to max_n values to out and returns
  * how many were recorded (>= 0), or a negative RAG_E* code. */
 RAG_API int rag_kernel_times(rag_ctx* ctx, float* out, int max_n);
+
+/* Name of the GPU kernel entry point ag_gemm would launch for these sizes with the context's
+ * current options (e.g. "rag_ag_bf16_t256x128"), written NUL-terminated into buf (len bytes).
+ * Diagnostics: lets a profile be matched to the kernel a measurement ran. */
+RAG_API int rag_ag_kernel_name(rag_ctx* ctx, int nc, int M, rag_dtype dt, char* buf, int len);
 
 /* Text for the last non-zero return on the calling thread ("" if none). */
 RAG_API const char* rag_last_error(void);

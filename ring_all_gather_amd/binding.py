@@ -30,6 +30,8 @@ RAG_BF16, RAG_FP8_E4M3 = 0, 1
 RAG_STAGED_OUT, RAG_NO_COPY, RAG_COPY_ONLY = 1, 2, 4
 RAG_OPT_COPY_ENGINE, RAG_OPT_COMM_WGS, RAG_OPT_SPIN_LIMIT_US = 1, 2, 3
 RAG_OPT_ARRIVAL_DELAY_US, RAG_OPT_WITHHOLD_MASK, RAG_OPT_TIMING, RAG_OPT_TILE = 4, 5, 6, 7
+RAG_OPT_TRACE_BUF, RAG_OPT_TRACE_BYTES, RAG_OPT_WGS_PER_CU, RAG_OPT_COPY_PRIORITY = 8, 9, 10, 11
+TRACE_HEADER, TRACE_START, TRACE_TILE_WORDS = 64, 32, 4
 TILES = {"auto": 0, "128x128": 1, "256x128": 2, "256x256": 3, "256x256w8": 4, "256x256w8s4": 5}
 RAG_MAX_TP = 16
 
@@ -70,10 +72,11 @@ def lib():
     L.gemm_rs.argtypes = [vp, vp, i, i, vp, i, ctypes.POINTER(vp), ll, i, i, vp, vp, i, vp]
     L.rag_check.argtypes = [vp]
     L.rag_kernel_times.argtypes = [vp, ctypes.POINTER(ctypes.c_float), i]
+    L.rag_ag_kernel_name.argtypes = [vp, i, i, i, ctypes.c_char_p, i]
     L.rag_last_error.restype = ctypes.c_char_p
     L.rag_version.restype = i
     for f in ("rag_create", "rag_destroy", "rag_set_option", "ag_gemm", "gemm_rs", "rag_check",
-              "rag_kernel_times"):
+              "rag_kernel_times", "rag_ag_kernel_name"):
         getattr(L, f).restype = i
     _lib = L
     return L
@@ -86,6 +89,11 @@ def declared_functions():
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*RAG_API\s+(?:const\s+)?\w+\s*\**\s*(\w+)\s*\(", text,
                                  flags=re.M)))
+
+
+def kernels_fingerprint() -> str:
+    """SHA-256 of the gfx950 code object embedded in the loaded library."""
+    return (ctypes.c_char * 65).in_dll(lib(), "ringag_kernels_sha256").value.decode()
 
 
 def last_error() -> str:
@@ -135,6 +143,24 @@ class Context:
 
     def set_option(self, key: int, value: int):
         _check(lib().rag_set_option(self.h, key, int(value)))
+
+    def set_trace(self, buf: Optional[torch.Tensor]):
+        """Diagnostics: record wall-clock stamps of the next ag_gemm calls into `buf` (an int64 GPU
+        tensor; layout in ringag.h under RAG_OPT_TRACE_BUF), or stop with None."""
+        if buf is None:
+            self.set_option(RAG_OPT_TRACE_BUF, 0)
+            self.set_option(RAG_OPT_TRACE_BYTES, 0)
+            return
+        if buf.dtype != torch.int64 or not buf.is_cuda or not buf.is_contiguous():
+            raise ValueError("trace buffer must be a contiguous int64 GPU tensor")
+        self.set_option(RAG_OPT_TRACE_BYTES, buf.numel() * 8)
+        self.set_option(RAG_OPT_TRACE_BUF, buf.data_ptr())
+
+    def ag_kernel_name(self, nc: int, M: int, fp8: bool = False) -> str:
+        """Entry point ag_gemm would launch for these sizes (diagnostics)."""
+        buf = ctypes.create_string_buffer(128)
+        _check(lib().rag_ag_kernel_name(self.h, nc, M, RAG_FP8_E4M3 if fp8 else RAG_BF16, buf, 128))
+        return buf.value.decode()
 
     def check(self):
         """Synchronise and raise RagError(RAG_ETIMEOUT) if a chunk never arrived."""

@@ -12,6 +12,7 @@ Steps:
 The host objects contain no device code, so the library has no HIP registration constructors or
 destructors; the kernels are loaded explicitly when a context is created.
 """
+import hashlib
 import os
 import subprocess
 import sys
@@ -51,6 +52,10 @@ def build_code_object(extra=()) -> str:
 
 
 def _blob_object(co: str) -> str:
+    """Embed the code object, and its SHA-256 as the string ringag_kernels_sha256 (so that
+    measurements taken with one build of the kernels can be told apart from another's)."""
+    with open(co, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
     asm = os.path.join(BUILD_DIR, "kernels_blob.S")
     with open(asm, "w") as f:
         f.write('    .section .rodata.ringag_kernels,"a"\n'
@@ -60,6 +65,11 @@ def _blob_object(co: str) -> str:
                 "ringag_kernels_co:\n"
                 f'    .incbin "{co}"\n'
                 "    .size ringag_kernels_co, . - ringag_kernels_co\n"
+                "    .globl ringag_kernels_sha256\n"
+                "    .type ringag_kernels_sha256, @object\n"
+                "ringag_kernels_sha256:\n"
+                f'    .asciz "{digest}"\n'
+                "    .size ringag_kernels_sha256, . - ringag_kernels_sha256\n"
                 '    .section .note.GNU-stack,"",@progbits\n')
     obj = os.path.join(BUILD_DIR, "kernels_blob.o")
     _run([CXX, "-c", asm, "-o", obj], "blob assembly")

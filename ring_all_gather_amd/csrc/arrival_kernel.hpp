@@ -26,6 +26,10 @@ __device__ __forceinline__ void arrival_body(const ArrivalArgs& a) {
   const unsigned long long per = (nvec + gridDim.x - 1) / gridDim.x;
   const unsigned long long beg = min(nvec, (unsigned long long)blockIdx.x * per);
   const unsigned long long end = min(nvec, beg + per);
+  // The copy shares SIMDs with GEMM waves: issue its (few) instructions first so the chunks the
+  // GEMM waits for are not starved by the waves that will consume them.
+  if (a.raise_priority) __builtin_amdgcn_s_setprio(3);
+  if (a.trace && blockIdx.x == 0 && threadIdx.x == 0) a.trace[kTraceStart] = wall_clock64();
   for (int j = 0; j < a.n; ++j) {
     const v4i* src = (const v4i*)a.src[j];
     v4i* dst = (v4i*)a.dst[j];
@@ -56,6 +60,7 @@ __device__ __forceinline__ void arrival_body(const ArrivalArgs& a) {
           if (!((a.withhold_mask >> a.pos[j]) & 1u))
             __hip_atomic_store(a.ctr + a.ctr_index[j], a.epoch, __ATOMIC_RELEASE,
                                __HIP_MEMORY_SCOPE_AGENT);
+          if (a.trace) a.trace[j] = wall_clock64();
         }
       }
     }

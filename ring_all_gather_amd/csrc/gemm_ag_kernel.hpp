@@ -31,6 +31,14 @@ __device__ inline bool wait_ready(int* ctr, int epoch, int* err, long long limit
   }
 }
 
+// (XCC << 16) | (shader engine << 8) | CU of the calling wave (hardware id registers).
+__device__ inline unsigned hw_location() {
+  const unsigned xcc = __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20);   // XCC_ID[3:0]
+  const unsigned se = __builtin_amdgcn_s_getreg((1 << 11) | (13 << 6) | 4);    // HW_ID[14:13]
+  const unsigned cu = __builtin_amdgcn_s_getreg((3 << 11) | (8 << 6) | 4);     // HW_ID[11:8]
+  return (xcc << 16) | (se << 8) | cu;
+}
+
 template <class S, bool FP8>
 __device__ __forceinline__ void ag_gemm_body(const AgArgs& a) {
   __shared__ __attribute__((aligned(1024))) char lds[S::LDS];
@@ -50,6 +58,8 @@ __device__ __forceinline__ void ag_gemm_body(const AgArgs& a) {
     const int u = t - j * U;
     int rb, cb;
     map_tile_xcd(u, U, a.tiles_i, a.tiles_j, a.xcd_rows, &rb, &cb);
+    unsigned long long* tr = a.trace ? a.trace + kTraceTileWords * (size_t)t : nullptr;
+    if (tr && threadIdx.x == 0) tr[0] = wall_clock64();
     if (a.ctr_index[j] >= 0) {
       if (threadIdx.x == 0) s_ok = wait_ready(a.ctr + a.ctr_index[j], a.epoch, a.err, a.spin_limit);
       __syncthreads();
@@ -57,6 +67,7 @@ __device__ __forceinline__ void ag_gemm_body(const AgArgs& a) {
       __syncthreads();
       if (!ok) continue;
     }
+    if (tr && threadIdx.x == 0) tr[1] = wall_clock64();
     const i32x4 rx = make_rsrc(a.chunk[j], (uint32_t)a.nc * ldb);
     uint32_t xo[S::XQ], yo[S::YQ];
     tile_offsets<S, S::XQ>(xo, rb * S::BI, a.nc, ldb, wave, lane);
@@ -65,6 +76,10 @@ __device__ __forceinline__ void ag_gemm_body(const AgArgs& a) {
     tile_kloop<S, FP8>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);
     __bf16* out = (__bf16*)a.out[j] + (size_t)rb * S::BI * a.M + (size_t)cb * S::BJ;
     store_tile_bf16<S>(acc, scale, lds, out, a.M, a.nc - rb * S::BI, a.M - cb * S::BJ, wave, lane);
+    if (tr && threadIdx.x == 0) {
+      tr[2] = wall_clock64();
+      tr[3] = ((unsigned long long)blockIdx.x << 32) | hw_location();
+    }
   }
 }
 

@@ -32,6 +32,7 @@ struct AgArgs {
   const float* scale_B;
   int tiles_i, tiles_j;          // tile grid of one chunk
   int xcd_rows;                  // XCD rectangle split (see map_tile_xcd); 0 = linear order
+  unsigned long long* trace;     // optional per-tile stamps (kTraceTileWords per tile), or null
 };
 
 // Arguments of the GEMM+RS kernel.  Row-chunk positions j = 0..tp-1 in visiting order; the last
@@ -63,7 +64,17 @@ struct ArrivalArgs {
   int epoch;
   long long delay_ticks;         // test hook: hold each release back this long
   unsigned withhold_mask;        // test hook: bit pos set = never release that chunk
+  unsigned long long* trace;     // optional: [j] = release time of copy j, [kTraceStart] = start
+  int raise_priority;            // 1 = run the copy waves at the highest issue priority
 };
+
+// Trace layout (64-bit words, wall clock at 100 MHz): words [0, kTraceHeader) belong to the
+// arrival kernel (release time of copy j at [j], first workgroup's start at [kTraceStart]); tile t
+// of the GEMM (ring-ordered index) owns words kTraceHeader + 4 t .. + 3: start (before its wait),
+// after the wait, end (after its stores), and (workgroup << 32) | (XCC << 16) | (SE << 8) | CU.
+constexpr int kTraceHeader = 64;
+constexpr int kTraceStart = 32;
+constexpr int kTraceTileWords = 4;
 
 enum TileCfg {
   kTile128x128 = 1, kTile256x128 = 2, kTile256x256 = 3, kTile256x256w8 = 4, kTile256x256w8s4 = 5
@@ -85,6 +96,10 @@ hipError_t launch_ag_gemm(int device, const AgArgs& a, int tile, bool fp8, int g
                           hipStream_t stream);
 hipError_t launch_gemm_rs(int device, const RsArgs& a, int tile, int grid, hipStream_t stream);
 hipError_t launch_arrival(int device, const ArrivalArgs& a, int grid, hipStream_t stream);
+
+// Entry-point names (launch.cpp).
+const char* ag_kernel_name(int tile, bool fp8);
+const char* rs_kernel_name(int tile);
 
 // Occupancy / resource facts for a kernel variant (cached by the caller).
 hipError_t ag_kernel_info(int device, int tile, bool fp8, KernelInfo* info);

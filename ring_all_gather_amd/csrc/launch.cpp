@@ -64,6 +64,12 @@ hipError_t info(hipFunction_t f, int threads, KernelInfo* out) {
 
 }  // namespace
 
+const char* ag_kernel_name(int tile, bool fp8) {
+  return valid_tile(tile) ? kAgName[fp8 ? 1 : 0][tile] : "";
+}
+
+const char* rs_kernel_name(int tile) { return valid_tile(tile) ? kRsName[tile] : ""; }
+
 hipError_t load_kernels(int device) {
   if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
   std::lock_guard<std::mutex> lock(g_mu);

@@ -83,6 +83,10 @@ struct rag_ctx {
   unsigned withhold = 0;
   int tile = RAG_TILE_AUTO;
   bool timing = false;
+  int wgs_per_cu = 0;
+  int copy_priority = 1;
+  unsigned long long trace_buf = 0;
+  long long trace_bytes = 0;
   std::vector<hipEvent_t> t_start, t_stop;
   int n_timed = 0;
   // occupancy cache: [tile][fp8]
@@ -293,6 +297,24 @@ int rag_set_option(rag_ctx* c, int key, long long v) {
       }
       c->timing = v != 0;
       return RAG_OK;
+    case RAG_OPT_WGS_PER_CU:
+      if (v < 0 || v > 16) return fail(RAG_EINVAL, "workgroups per CU must be in [0, 16]");
+      c->wgs_per_cu = (int)v;
+      return RAG_OK;
+    case RAG_OPT_COPY_PRIORITY:
+      if (v != 0 && v != 1) return fail(RAG_EINVAL, "copy priority must be 0 or 1");
+      c->copy_priority = (int)v;
+      return RAG_OK;
+    case RAG_OPT_TRACE_BUF:
+      if (v != 0 && (v & 7)) return fail(RAG_EINVAL, "trace buffer must be 8-byte aligned");
+      if (v != 0 && !on_device(reinterpret_cast<const void*>(v), c->device))
+        return fail(RAG_EINVAL, "trace buffer is not device memory of device %d", c->device);
+      c->trace_buf = (unsigned long long)v;
+      return RAG_OK;
+    case RAG_OPT_TRACE_BYTES:
+      if (v < 0) return fail(RAG_EINVAL, "trace size must be >= 0");
+      c->trace_bytes = v;
+      return RAG_OK;
     case RAG_OPT_TILE:
       if (v < RAG_TILE_AUTO || v > RAG_TILE_256x256_8W_S4) return fail(RAG_EINVAL, "unknown tile %lld", v);
       c->tile = (int)v;
@@ -387,6 +409,14 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
     if (rc) return rc;
   }
   const int epoch = next_epoch(c);
+  unsigned long long* trace = nullptr;
+  if (c->trace_buf) {
+    int bi, bj;
+    tile_dims(choose_ag_tile(c, nc, M), &bi, &bj);
+    const long long tiles = (long long)((nc + bi - 1) / bi) * ((M + bj - 1) / bj) * tp;
+    if ((kTraceHeader + kTraceTileWords * tiles) * 8 <= c->trace_bytes)
+      trace = reinterpret_cast<unsigned long long*>(c->trace_buf);
+  }
   int order[kMaxTp];
   for (int j = 0; j < tp; ++j) order[j] = ((self_rank - j) % tp + tp) % tp;
 
@@ -417,6 +447,8 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
       aa.epoch = epoch;
       aa.delay_ticks = c->delay_us * c->wall_khz / 1000;
       aa.withhold_mask = c->withhold;
+      aa.trace = trace;
+      aa.raise_priority = c->copy_priority;
       if (n > 0) HIPCHK(launch_arrival(c->device, aa, c->comm_wgs, c->side));
     } else {
       for (int j = 1; j < tp; ++j) {
@@ -453,6 +485,7 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
     a.spin_limit = c->spin_us * c->wall_khz / 1000;
     a.scale_A = scale_A;
     a.scale_B = scale_B;
+    a.trace = trace ? trace + kTraceHeader : nullptr;
     const int tile = choose_ag_tile(c, nc, M);
     int bi, bj;
     tile_dims(tile, &bi, &bj);
@@ -463,8 +496,9 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
       c->ag_info_ok[tile][fp8] = true;
     }
     const int total = a.tiles_i * a.tiles_j * tp;
-    const int grid = persistent_grid(total, c->num_cus - reserved_cus(tile, !no_copy),
-                                     c->ag_info[tile][fp8].max_blocks_per_cu);
+    int bpc = c->ag_info[tile][fp8].max_blocks_per_cu;
+    if (c->wgs_per_cu > 0) bpc = std::min(bpc, c->wgs_per_cu);
+    const int grid = persistent_grid(total, c->num_cus - reserved_cus(tile, !no_copy), bpc);
     {
       const int U = a.tiles_i * a.tiles_j;
       const int concurrent = std::min(tp, std::max(1, (grid + U - 1) / U));
@@ -598,6 +632,13 @@ int gemm_rs(rag_ctx* c, const void* X, int T, int Kl, const void* W, int Mo,
   if (rc) return rc;
   HIPCHK(launch_gemm_rs(c->device, a, tile, grid, stream));
   return record_timing_stop(c, stream, rec);
+}
+
+int rag_ag_kernel_name(rag_ctx* c, int nc, int M, rag_dtype dt, char* buf, int len) {
+  if (!c || !buf || len < 1) return fail(RAG_EINVAL, "rag_ag_kernel_name: bad arguments");
+  if (dt != RAG_BF16 && dt != RAG_FP8_E4M3) return fail(RAG_EINVAL, "unknown dtype %d", dt);
+  snprintf(buf, (size_t)len, "%s", ag_kernel_name(choose_ag_tile(c, nc, M), dt == RAG_FP8_E4M3));
+  return RAG_OK;
 }
 
 int rag_check(rag_ctx* c) {
