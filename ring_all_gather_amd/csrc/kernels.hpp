@@ -51,16 +51,20 @@ struct RsArgs {
 };
 
 // Arguments of the arrival (producer) kernel: copies j = 0..n-1 in order, each followed (when
-// ctr_index[j] >= 0) by a release of ctr[ctr_index[j]] = epoch once every workgroup finished it.
+// ctr_index[j] >= 0) by a release of ctr[ctr_index[j]] = epoch once every piece of it is copied.
+constexpr int kArrSlots = kMaxTp + 1;   // copies per launch at most (tp - 1 peers + the own chunk)
+
 struct ArrivalArgs {
-  const void* src[kMaxTp + 1];
-  void* dst[kMaxTp + 1];
-  int ctr_index[kMaxTp + 1];
-  int pos[kMaxTp + 1];           // ring position of copy j (for the withhold mask)
+  const void* src[kArrSlots];
+  void* dst[kArrSlots];
+  int ctr_index[kArrSlots];
+  int pos[kArrSlots];            // ring position of copy j (for the withhold mask)
   int n;
   unsigned long long bytes;      // bytes per copy, multiple of 16
   int* ctr;
-  int* ticket;                   // one per copy, self-resetting
+  unsigned* grab;                // [kArrSlots] next piece to take, per copy (this launch's set)
+  unsigned* done;                // [kArrSlots] pieces copied, per copy (this launch's set)
+  unsigned* clear_next;          // 2 * kArrSlots words of the other set, zeroed for the next launch
   int epoch;
   long long delay_ticks;         // test hook: hold each release back this long
   unsigned withhold_mask;        // test hook: bit pos set = never release that chunk

@@ -1,6 +1,6 @@
 // Host runtime of libringag.so: the C ABI declared in include/ringag.h.
 //
-// It owns the per-context resources (side stream, fork/join events, ready counters, tickets, error
+// It owns the per-context resources (side stream, fork/join events, ready counters, piece counts, error
 // word, epoch, cached gather and staging buffers), validates every argument before enqueueing
 // anything, and orders the work of one call:
 //
@@ -64,11 +64,12 @@ struct rag_ctx {
   int max_tp = 0;
   hipStream_t side = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
-  int* words = nullptr;   // ctr[max_tp] | ticket[max_tp + 2] | err
+  int* words = nullptr;   // ctr[max_tp] | arrival counts [2 sets][grab, done][kArrSlots] | err
   int* ctr = nullptr;
-  int* ticket = nullptr;
+  unsigned* arr = nullptr;
   int* err = nullptr;
   int epoch = 0;
+  unsigned arr_seq = 0;   // arrival launches so far (selects the set of grab/done counts)
   void* gbuf = nullptr;
   size_t gbuf_bytes = 0;
   void* stage = nullptr;
@@ -217,7 +218,7 @@ int rag_create(rag_ctx** out, int device, int max_tp, int flags) {
   int khz = 0;
   if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, device) == hipSuccess && khz > 0)
     c->wall_khz = khz;
-  const size_t nwords = (size_t)max_tp + (size_t)max_tp + 2 + 1;
+  const size_t nwords = (size_t)max_tp + 4 * (size_t)kArrSlots + 1;
   hipError_t e = load_kernels(device);
   if (e != hipSuccess) {
     delete c;
@@ -236,8 +237,8 @@ int rag_create(rag_ctx** out, int device, int max_tp, int flags) {
     return fail(RAG_EHIP, "%s", msg.c_str());
   }
   c->ctr = c->words;
-  c->ticket = c->words + max_tp;
-  c->err = c->words + 2 * max_tp + 2;
+  c->arr = reinterpret_cast<unsigned*>(c->words + max_tp);
+  c->err = c->words + max_tp + 4 * kArrSlots;
   *out = c;
   if (debug_enabled())
     fprintf(stderr, "[ringag] context on device %d (%s, %d CUs, wall clock %lld kHz), max_tp %d\n",
@@ -443,13 +444,19 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
       aa.n = n;
       aa.bytes = (unsigned long long)chunk_bytes;
       aa.ctr = c->ctr;
-      aa.ticket = c->ticket;
+      const unsigned set = c->arr_seq & 1u;
+      aa.grab = c->arr + set * 2 * kArrSlots;
+      aa.done = aa.grab + kArrSlots;
+      aa.clear_next = c->arr + (set ^ 1u) * 2 * kArrSlots;
       aa.epoch = epoch;
       aa.delay_ticks = c->delay_us * c->wall_khz / 1000;
       aa.withhold_mask = c->withhold;
       aa.trace = trace;
       aa.raise_priority = c->copy_priority;
-      if (n > 0) HIPCHK(launch_arrival(c->device, aa, c->comm_wgs, c->side));
+      if (n > 0) {
+        HIPCHK(launch_arrival(c->device, aa, c->comm_wgs, c->side));
+        c->arr_seq++;
+      }
     } else {
       for (int j = 1; j < tp; ++j) {
         const int r = order[j];
