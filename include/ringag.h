@@ -8,7 +8,7 @@
  *     a ring of tp-1 send/receive steps fills a gathered buffer chunk by chunk; one GEMM launch
  *     split into tp pieces along n waits on a per-chunk counter bumped after each receive; the
  *     output goes through a buffer of tp+1 chunks; the GEMM is "TN" (m = weight rows, n = gathered
- *     rows); communication runs on its own streams joined by events.
+ *     rows); communication runs on its own streams, forked from and joined to the main one.
  *   - nvFuser PR #3392 "Ring-based decomposition for Allgather+GEMM overlap ATen implementation",
  *     experiment: posting communication before compute gave near-complete overlap.
  *   - TransformerEngine PR #2443 "Comm+GEMM overlap API updated to support cuBlasMp backend",
@@ -31,8 +31,11 @@
  *     passed the operation.  Host arrays of pointers (B_chunks, partials) are read during the call
  *     only.
  *   - Every call is stream-ordered on `stream` (0 = the null stream): it enqueues work and returns.
- *     Outputs are valid in `stream` order.  Library-internal side work is joined back into `stream`
- *     before the call returns, so nothing of a call is left running outside `stream`.
+ *     Outputs are valid in `stream` order.  The side stream that carries the copies starts after
+ *     the work already in `stream` (event fork), and the call's last kernel on `stream` completes
+ *     only after every copy of the call has completed (its workgroups wait for the copy counters;
+ *     with RAG_COPY_ONLY, `stream` waits for an event of the side stream instead).  So in `stream`
+ *     order the inputs may be reused and the outputs are complete.
  *   - One operation in flight per context; a context is not thread-safe.  Calls on different
  *     contexts are independent.
  *   - Every entry point returns RAG_OK (0) or a negative RAG_E* code and never throws.  Arguments

@@ -37,7 +37,8 @@ __device__ __forceinline__ void arrival_body(const ArrivalArgs& a) {
   if (a.raise_priority) __builtin_amdgcn_s_setprio(3);
   if (a.trace && blockIdx.x == 0 && threadIdx.x == 0) a.trace[kTraceStart] = wall_clock64();
   if (blockIdx.x == 0 && threadIdx.x < 2 * kArrSlots)
-    __hip_atomic_store(a.clear_next + threadIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.clear_next + threadIdx.x * kWordStride, 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 
   const unsigned long long pieces = (a.bytes + kArrPiece - 1) / kArrPiece;
   for (int j = 0; j < a.n; ++j) {
@@ -46,7 +47,7 @@ __device__ __forceinline__ void arrival_body(const ArrivalArgs& a) {
     unsigned mine = 0;
     while (true) {
       if (threadIdx.x == 0)
-        s_piece = __hip_atomic_fetch_add(a.grab + j, 1u, __ATOMIC_RELAXED,
+        s_piece = __hip_atomic_fetch_add(a.grab + j * kWordStride, 1u, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT);
       __syncthreads();
       const unsigned long long p = s_piece;
@@ -75,17 +76,19 @@ __device__ __forceinline__ void arrival_body(const ArrivalArgs& a) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (threadIdx.x == 0) {
-        const unsigned old = __hip_atomic_fetch_add(a.done + j, mine, __ATOMIC_ACQ_REL,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned old = __hip_atomic_fetch_add(a.done + j * kWordStride, mine,
+                                                    __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
         if (old + mine == (unsigned)pieces) {
           if (a.delay_ticks > 0) {
             const unsigned long long t0 = wall_clock64();
             while ((long long)(wall_clock64() - t0) < a.delay_ticks) __builtin_amdgcn_s_sleep(8);
           }
-          if (!((a.withhold_mask >> a.pos[j]) & 1u))
-            __hip_atomic_store(a.ctr + a.ctr_index[j], a.epoch, __ATOMIC_RELEASE,
-                               __HIP_MEMORY_SCOPE_AGENT);
+          // (the stamp goes first: once the last counter is out, the consumer may finish and
+          // the caller may read the trace)
           if (a.trace) a.trace[j] = wall_clock64();
+          if (a.pos[j] == 0 || !((a.withhold_mask >> a.pos[j]) & 1u))
+            __hip_atomic_store(a.ctr + a.ctr_index[j] * kWordStride, a.epoch, __ATOMIC_RELEASE,
+                               __HIP_MEMORY_SCOPE_AGENT);
         }
       }
     }

@@ -72,7 +72,8 @@ __device__ __forceinline__ void ag_gemm_body(const AgArgs& a) {
     unsigned long long* tr = a.trace ? a.trace + kTraceTileWords * (size_t)t : nullptr;
     if (tr && threadIdx.x == 0) tr[0] = wall_clock64();
     if (a.ctr_index[j] >= 0) {
-      if (threadIdx.x == 0) s_ok = wait_ready(a.ctr + a.ctr_index[j], a.epoch, a.err, a.spin_limit);
+      if (threadIdx.x == 0)
+        s_ok = wait_ready(a.ctr + a.ctr_index[j] * kWordStride, a.epoch, a.err, a.spin_limit);
       __syncthreads();
       const int ok = s_ok;
       __syncthreads();
@@ -92,6 +93,12 @@ __device__ __forceinline__ void ag_gemm_body(const AgArgs& a) {
       tr[3] = ((unsigned long long)blockIdx.x << 32) | hw_location();
     }
   }
+  // The copies run on another stream, which the caller's stream does not wait for: the kernel
+  // ends only once the last copy (the own chunk into G) is complete, so that everything enqueued
+  // after it sees a complete G.  The peers' chunks are complete already, since some tile waited
+  // for each of them.
+  if (a.join_index >= 0 && threadIdx.x == 0)
+    (void)wait_ready(a.ctr + a.join_index * kWordStride, a.epoch, a.err, a.spin_limit);
 }
 
 }  // namespace ringag

@@ -16,15 +16,22 @@ namespace ringag {
 
 constexpr int kMaxTp = 16;
 
+// Device counters live kWordStride ints apart (256 bytes), one per cache line: the GEMM's tiles
+// poll the ready counters continuously, and an atomic on a line that is being polled queues
+// behind the polls.
+constexpr int kWordStride = 64;
+
 // Arguments of the counter-gated AG+GEMM kernel.  Chunk positions j = 0..tp-1 are the ring order
 // at this rank (position 0 = own chunk).
 struct AgArgs {
   const void* chunk[kMaxTp];     // by position: where the kernel reads that chunk's rows
   void* out[kMaxTp];             // by position: where that chunk's [nc, M] bf16 output rows go
   int ctr_index[kMaxTp];         // by position: counter to wait for, -1 = ready from the start
+  int join_index;                // counter marking the copy into the own slot of G done, or -1:
+                                 // every workgroup waits for it before it exits
   const void* A;                 // weight [M, K]
   int M, K, nc, tp;
-  int* ctr;                      // per-chunk ready counters
+  int* ctr;                      // per-chunk ready counters (kWordStride apart)
   int epoch;                     // value meaning "ready" for this call
   int* err;                      // error word: set to 1 when a wait times out
   long long spin_limit;          // wall-clock ticks a tile waits before giving up
@@ -52,6 +59,7 @@ struct RsArgs {
 
 // Arguments of the arrival (producer) kernel: copies j = 0..n-1 in order, each followed (when
 // ctr_index[j] >= 0) by a release of ctr[ctr_index[j]] = epoch once every piece of it is copied.
+// Counters and per-copy counts are kWordStride ints apart.
 constexpr int kArrSlots = kMaxTp + 1;   // copies per launch at most (tp - 1 peers + the own chunk)
 
 struct ArrivalArgs {
@@ -64,10 +72,10 @@ struct ArrivalArgs {
   int* ctr;
   unsigned* grab;                // [kArrSlots] next piece to take, per copy (this launch's set)
   unsigned* done;                // [kArrSlots] pieces copied, per copy (this launch's set)
-  unsigned* clear_next;          // 2 * kArrSlots words of the other set, zeroed for the next launch
+  unsigned* clear_next;          // 2 * kArrSlots counts of the other set, zeroed for the next launch
   int epoch;
   long long delay_ticks;         // test hook: hold each release back this long
-  unsigned withhold_mask;        // test hook: bit pos set = never release that chunk
+  unsigned withhold_mask;        // test hook: bit pos (>= 1) set = never release that chunk
   unsigned long long* trace;     // optional: [j] = release time of copy j, [kTraceStart] = start
   int raise_priority;            // 1 = run the copy waves at the highest issue priority
 };

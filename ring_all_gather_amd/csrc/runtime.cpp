@@ -64,7 +64,9 @@ struct rag_ctx {
   int max_tp = 0;
   hipStream_t side = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
-  int* words = nullptr;   // ctr[max_tp] | arrival counts [2 sets][grab, done][kArrSlots] | err
+  // device counters, kWordStride ints apart: ctr[max_tp] | copy-complete | arrival counts
+  // [2 sets][grab, done][kArrSlots] | err
+  int* words = nullptr;
   int* ctr = nullptr;
   unsigned* arr = nullptr;
   int* err = nullptr;
@@ -218,7 +220,7 @@ int rag_create(rag_ctx** out, int device, int max_tp, int flags) {
   int khz = 0;
   if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, device) == hipSuccess && khz > 0)
     c->wall_khz = khz;
-  const size_t nwords = (size_t)max_tp + 4 * (size_t)kArrSlots + 1;
+  const size_t nwords = ((size_t)max_tp + 1 + 4 * (size_t)kArrSlots + 1) * kWordStride;
   hipError_t e = load_kernels(device);
   if (e != hipSuccess) {
     delete c;
@@ -237,8 +239,8 @@ int rag_create(rag_ctx** out, int device, int max_tp, int flags) {
     return fail(RAG_EHIP, "%s", msg.c_str());
   }
   c->ctr = c->words;
-  c->arr = reinterpret_cast<unsigned*>(c->words + max_tp);
-  c->err = c->words + max_tp + 4 * kArrSlots;
+  c->arr = reinterpret_cast<unsigned*>(c->words + (size_t)(max_tp + 1) * kWordStride);
+  c->err = c->words + (size_t)(max_tp + 1 + 4 * kArrSlots) * kWordStride;
   *out = c;
   if (debug_enabled())
     fprintf(stderr, "[ringag] context on device %d (%s, %d CUs, wall clock %lld kHz), max_tp %d\n",
@@ -404,6 +406,8 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
     if (rc) return rc;
     Gp = (char*)c->gbuf;
   }
+  // the own chunk also goes into G (after the peers' chunks) unless it is already there
+  const bool own_copy = G && (const char*)B[self_rank] != Gp + (size_t)self_rank * chunk_bytes;
   if (staged && !copy_only) {
     int rc = ensure_buffer(&c->stage, &c->stage_bytes, (size_t)(tp + 1) * nc * M * 2,
                            "staging buffer");
@@ -434,10 +438,10 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
         aa.ctr_index[n] = r;
         aa.pos[n] = j;
       }
-      if (G && (const char*)B[self_rank] != Gp + (size_t)self_rank * chunk_bytes) {
+      if (own_copy) {
         aa.src[n] = B[self_rank];
         aa.dst[n] = Gp + (size_t)self_rank * chunk_bytes;
-        aa.ctr_index[n] = -1;
+        aa.ctr_index[n] = copy_only ? -1 : c->max_tp;
         aa.pos[n] = 0;
         ++n;
       }
@@ -445,9 +449,9 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
       aa.bytes = (unsigned long long)chunk_bytes;
       aa.ctr = c->ctr;
       const unsigned set = c->arr_seq & 1u;
-      aa.grab = c->arr + set * 2 * kArrSlots;
-      aa.done = aa.grab + kArrSlots;
-      aa.clear_next = c->arr + (set ^ 1u) * 2 * kArrSlots;
+      aa.grab = c->arr + (size_t)set * 2 * kArrSlots * kWordStride;
+      aa.done = aa.grab + (size_t)kArrSlots * kWordStride;
+      aa.clear_next = c->arr + (size_t)(set ^ 1u) * 2 * kArrSlots * kWordStride;
       aa.epoch = epoch;
       aa.delay_ticks = c->delay_us * c->wall_khz / 1000;
       aa.withhold_mask = c->withhold;
@@ -463,13 +467,20 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
         HIPCHK(hipMemcpyAsync(Gp + (size_t)r * chunk_bytes, B[r], (size_t)chunk_bytes,
                               hipMemcpyDeviceToDeviceNoCU, c->side));
         if (!((c->withhold >> j) & 1u))
-          HIPCHK(hipStreamWriteValue32(c->side, c->ctr + r, (uint32_t)epoch, 0));
+          HIPCHK(hipStreamWriteValue32(c->side, c->ctr + (size_t)r * kWordStride,
+                                       (uint32_t)epoch, 0));
       }
-      if (G && (const char*)B[self_rank] != Gp + (size_t)self_rank * chunk_bytes)
+      if (own_copy) {
         HIPCHK(hipMemcpyAsync(Gp + (size_t)self_rank * chunk_bytes, B[self_rank],
                               (size_t)chunk_bytes, hipMemcpyDeviceToDeviceNoCU, c->side));
+        if (!copy_only)
+          HIPCHK(hipStreamWriteValue32(c->side, c->ctr + (size_t)c->max_tp * kWordStride,
+                                       (uint32_t)epoch, 0));
+      }
     }
-    HIPCHK(hipEventRecord(c->ev_join, c->side));
+    // With a GEMM the join is on the device (its workgroups wait for the last copy before they
+    // exit); without one the caller's stream waits for the side stream's end.
+    if (copy_only) HIPCHK(hipEventRecord(c->ev_join, c->side));
   }
 
   if (!copy_only) {
@@ -487,6 +498,7 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
     a.nc = nc;
     a.tp = tp;
     a.ctr = c->ctr;
+    a.join_index = (own_copy && !no_copy) ? c->max_tp : -1;
     a.epoch = epoch;
     a.err = c->err;
     a.spin_limit = c->spin_us * c->wall_khz / 1000;
@@ -527,7 +539,7 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
     rc = record_timing_stop(c, stream, rec);
     if (rc) return rc;
   }
-  if (!no_copy) HIPCHK(hipStreamWaitEvent(stream, c->ev_join, 0));
+  if (!no_copy && copy_only) HIPCHK(hipStreamWaitEvent(stream, c->ev_join, 0));
 
   if (staged && !copy_only) {
     const size_t dchunk = (size_t)nc * M * 2;
