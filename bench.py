@@ -40,8 +40,11 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="ag_4k")
-    p.add_argument("--copy-engine", default=os.environ.get("RAG_COPY_ENGINE", "kernel"),
-                   choices=["kernel", "sdma"])
+    p.add_argument("--copy-engine", default=os.environ.get("RAG_COPY_ENGINE", "in-gemm"),
+                   choices=["kernel", "sdma", "in-gemm"])
+    p.add_argument("--own-chunk", default="in-g", choices=["in-g", "separate"],
+                   help="in-g: the own chunk lives in its slot of G, as the local shard does in a "
+                        "ring all-gather; separate: it is its own buffer and is copied into G")
     p.add_argument("--comm-wgs", type=int, default=int(os.environ.get("RAG_COMM_WGS", "32")))
     p.add_argument("--tile", default=os.environ.get("RAG_TILE", "auto"))
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -153,7 +156,7 @@ def main():
 
     dev = "cuda:0"
     ctx = B.Context(0, max_tp=16)
-    ctx.set_option(B.RAG_OPT_COPY_ENGINE, {"kernel": 0, "sdma": 1}[args.copy_engine])
+    ctx.set_option(B.RAG_OPT_COPY_ENGINE, B.ENGINES[args.copy_engine])
     ctx.set_option(B.RAG_OPT_COMM_WGS, args.comm_wgs)
     ctx.set_option(B.RAG_OPT_TILE, B.TILES[args.tile])
     shape = W.WORKLOADS[args.workload]
@@ -163,8 +166,12 @@ def main():
     if isinstance(shape, W.AGShape):
         inp = W.make_ag(shape)
         A = inp.A.to(dev)
-        chunks = [c.to(dev) for c in inp.chunks]
         G = torch.empty((shape.N, shape.K), dtype=inp.A.dtype, device=dev)
+        chunks = [c.to(dev) for c in inp.chunks]
+        if args.own_chunk == "in-g":
+            s0 = shape.self_rank * shape.nc
+            G[s0:s0 + shape.nc].copy_(chunks[shape.self_rank])
+            chunks[shape.self_rank] = G[s0:s0 + shape.nc]
         D = torch.empty((shape.N, shape.M), dtype=torch.bfloat16, device=dev)
         sA = sB = None
         if shape.dtype == "fp8":
@@ -189,7 +196,7 @@ def main():
         flops = shape.flops
         kernel_ms = statistics.fmean(kt)
         achieved = flops / (kernel_ms * 1e-3) / 1e12
-        kname = ctx.ag_kernel_name(shape.nc, shape.M, shape.dtype == "fp8")
+        kname = ctx.ag_kernel_name(shape.nc, shape.M, shape.tp, shape.dtype == "fp8")
         traffic = measured_traffic(kname, B.kernels_fingerprint()) \
             if args.workload == "ag_4k" else None
         peak = PEAK_TFLOPS[shape.dtype]
@@ -204,7 +211,8 @@ def main():
                                    f"N={shape.N} (chunks of {shape.nc}) M={shape.M} K={shape.K} "
                                    f"{shape.dtype}",
                        "tp": shape.tp, "self_rank": shape.self_rank, "N": shape.N, "M": shape.M,
-                       "K": shape.K, "copy_engine": args.copy_engine, "comm_wgs": args.comm_wgs,
+                       "K": shape.K, "copy_engine": args.copy_engine, "own_chunk": args.own_chunk,
+                       "comm_wgs": args.comm_wgs,
                        "tile": args.tile},
             "pct_mfma_peak": round(100.0 * value / peak, 2),
             "step_ms": {"p10": round(pctl(per, 0.1), 5), "p50": round(pctl(per, 0.5), 5),

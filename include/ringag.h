@@ -85,16 +85,26 @@ enum {
     RAG_COPY_ONLY = 4   /* AG+GEMM: arrivals (copies + counter bumps) only, no GEMM */
 };
 
+/* Copy engines of the simulated arrival (RAG_OPT_COPY_ENGINE). */
+enum {
+    RAG_COPY_KERNEL = 0,   /* a copy kernel on the side stream, beside the GEMM */
+    RAG_COPY_SDMA = 1,     /* SDMA engines on the side stream (hipMemcpyDeviceToDeviceNoCU, then
+                              hipStreamWriteValue32 of the counter) */
+    RAG_COPY_IN_GEMM = 2   /* the GEMM launch itself: workgroups whose chunk is not there yet copy
+                              pieces of the peers' chunks (ring order) until it is released, and
+                              help with the rest once out of tiles; no side stream is used */
+};
+
 /* Option keys for rag_set_option. */
 enum {
-    RAG_OPT_COPY_ENGINE = 1,    /* 0 = copy kernel on compute units (default), 1 = SDMA engines
-                                   (hipMemcpyDeviceToDeviceNoCU + hipStreamWriteValue32) */
-    RAG_OPT_COMM_WGS = 2,       /* workgroups of the copy kernel (default 32, 1..1024): the share of
-                                   compute units that communication takes */
+    RAG_OPT_COPY_ENGINE = 1,    /* a RAG_COPY_* value (default RAG_COPY_IN_GEMM) */
+    RAG_OPT_COMM_WGS = 2,       /* workgroups of the side-stream copy kernel (default 32, 1..1024):
+                                   the share of compute units that communication takes */
     RAG_OPT_SPIN_LIMIT_US = 3,  /* how long a tile waits for its chunk before giving up
                                    (microseconds, default 2,000,000) */
-    RAG_OPT_ARRIVAL_DELAY_US = 4, /* test hook: the copy kernel holds each counter bump back by this
-                                   many microseconds after the chunk's copy (default 0, max 10^6) */
+    RAG_OPT_ARRIVAL_DELAY_US = 4, /* test hook: the kernel copy engines hold each counter bump back
+                                   by this many microseconds after the chunk's copy (default 0,
+                                   max 10^6) */
     RAG_OPT_WITHHOLD_MASK = 5,  /* test hook: bit j set = never bump the counter of the chunk at
                                    ring position j (1..tp-1); the waiting tiles then time out */
     RAG_OPT_TIMING = 6,         /* 1 = record HIP events around every GEMM launch (rag_kernel_times) */
@@ -102,16 +112,21 @@ enum {
     RAG_OPT_TRACE_BUF = 8,      /* diagnostics: device address of a buffer of 64-bit words that the
                                    next ag_gemm calls fill with wall-clock stamps (100 MHz): words
                                    0..tp-2 = release time of the chunk at ring position 1..tp-1,
-                                   word 32 = start of the copies, then 4 words per GEMM tile in
-                                   ring order from word 64 (start, after its wait, end, location);
-                                   0 = off (default) */
+                                   word tp-1 = completion of the own chunk's copy into G, word 32
+                                   = start of the copies, then 5 words per GEMM tile in ring order
+                                   from word 64 (start, after its wait, end, location = workgroup
+                                   << 32 | XCC << 16 | SE << 8 | CU, core clock cycles from after
+                                   the wait to the end); 0 = off (default) */
     RAG_OPT_TRACE_BYTES = 9,    /* diagnostics: size of that buffer; a call whose stamps would not
                                    fit records none */
     RAG_OPT_WGS_PER_CU = 10,    /* GEMM workgroups resident per compute unit: 0 = as many as fit
                                    (default), n = at most n (fewer, longer-lived workgroups take the
                                    ring's chunks in more rounds) */
-    RAG_OPT_COPY_PRIORITY = 11  /* 1 (default) = copy-kernel waves issue at the highest wave
+    RAG_OPT_COPY_PRIORITY = 11, /* 1 (default) = copy-kernel waves issue at the highest wave
                                    priority, 0 = normal */
+    RAG_OPT_GEMM_COPY_WGS = 12  /* RAG_COPY_IN_GEMM: how many of the GEMM's workgroups take part in
+                                   the copies, spread evenly over the XCDs (0 = all, the default);
+                                   fewer copy more slowly but draw less power at once */
 };
 
 /* Tile configurations (rows of D x columns of D per workgroup; 4 waves unless stated). */
@@ -205,10 +220,12 @@ RAG_API int rag_check(rag_ctx* ctx);
  * how many were recorded (>= 0), or a negative RAG_E* code. */
 RAG_API int rag_kernel_times(rag_ctx* ctx, float* out, int max_n);
 
-/* Name of the GPU kernel entry point ag_gemm would launch for these sizes with the context's
- * current options (e.g. "rag_ag_bf16_t256x128"), written NUL-terminated into buf (len bytes).
- * Diagnostics: lets a profile be matched to the kernel a measurement ran. */
-RAG_API int rag_ag_kernel_name(rag_ctx* ctx, int nc, int M, rag_dtype dt, char* buf, int len);
+/* Name of the GPU kernel entry point ag_gemm would launch for these sizes (nc rows per chunk, M
+ * output columns, tp chunks) with the context's current options (e.g. "rag_ag_bf16_t256x256w8"),
+ * written NUL-terminated into buf (len bytes).  Diagnostics: lets a profile be matched to the
+ * kernel a measurement ran. */
+RAG_API int rag_ag_kernel_name(rag_ctx* ctx, int nc, int M, int tp, rag_dtype dt, char* buf,
+                               int len);
 
 /* Text for the last non-zero return on the calling thread ("" if none). */
 RAG_API const char* rag_last_error(void);

@@ -31,7 +31,10 @@ RAG_STAGED_OUT, RAG_NO_COPY, RAG_COPY_ONLY = 1, 2, 4
 RAG_OPT_COPY_ENGINE, RAG_OPT_COMM_WGS, RAG_OPT_SPIN_LIMIT_US = 1, 2, 3
 RAG_OPT_ARRIVAL_DELAY_US, RAG_OPT_WITHHOLD_MASK, RAG_OPT_TIMING, RAG_OPT_TILE = 4, 5, 6, 7
 RAG_OPT_TRACE_BUF, RAG_OPT_TRACE_BYTES, RAG_OPT_WGS_PER_CU, RAG_OPT_COPY_PRIORITY = 8, 9, 10, 11
-TRACE_HEADER, TRACE_START, TRACE_TILE_WORDS = 64, 32, 4
+RAG_OPT_GEMM_COPY_WGS = 12
+RAG_COPY_KERNEL, RAG_COPY_SDMA, RAG_COPY_IN_GEMM = 0, 1, 2
+ENGINES = {"kernel": RAG_COPY_KERNEL, "sdma": RAG_COPY_SDMA, "in-gemm": RAG_COPY_IN_GEMM}
+TRACE_HEADER, TRACE_START, TRACE_TILE_WORDS = 64, 32, 5
 TILES = {"auto": 0, "128x128": 1, "256x128": 2, "256x256": 3, "256x256w8": 4, "256x256w8s4": 5}
 RAG_MAX_TP = 16
 
@@ -72,7 +75,7 @@ def lib():
     L.gemm_rs.argtypes = [vp, vp, i, i, vp, i, ctypes.POINTER(vp), ll, i, i, vp, vp, i, vp]
     L.rag_check.argtypes = [vp]
     L.rag_kernel_times.argtypes = [vp, ctypes.POINTER(ctypes.c_float), i]
-    L.rag_ag_kernel_name.argtypes = [vp, i, i, i, ctypes.c_char_p, i]
+    L.rag_ag_kernel_name.argtypes = [vp, i, i, i, i, ctypes.c_char_p, i]
     L.rag_last_error.restype = ctypes.c_char_p
     L.rag_version.restype = i
     for f in ("rag_create", "rag_destroy", "rag_set_option", "ag_gemm", "gemm_rs", "rag_check",
@@ -133,7 +136,7 @@ class Context:
         _live.add(self)
         env = os.environ
         if "RAG_COPY_ENGINE" in env:
-            self.set_option(RAG_OPT_COPY_ENGINE, {"kernel": 0, "sdma": 1}[env["RAG_COPY_ENGINE"]])
+            self.set_option(RAG_OPT_COPY_ENGINE, ENGINES[env["RAG_COPY_ENGINE"]])
         if "RAG_COMM_WGS" in env:
             self.set_option(RAG_OPT_COMM_WGS, int(env["RAG_COMM_WGS"]))
         if "RAG_SPIN_LIMIT_US" in env:
@@ -156,10 +159,11 @@ class Context:
         self.set_option(RAG_OPT_TRACE_BYTES, buf.numel() * 8)
         self.set_option(RAG_OPT_TRACE_BUF, buf.data_ptr())
 
-    def ag_kernel_name(self, nc: int, M: int, fp8: bool = False) -> str:
+    def ag_kernel_name(self, nc: int, M: int, tp: int, fp8: bool = False) -> str:
         """Entry point ag_gemm would launch for these sizes (diagnostics)."""
         buf = ctypes.create_string_buffer(128)
-        _check(lib().rag_ag_kernel_name(self.h, nc, M, RAG_FP8_E4M3 if fp8 else RAG_BF16, buf, 128))
+        _check(lib().rag_ag_kernel_name(self.h, nc, M, tp, RAG_FP8_E4M3 if fp8 else RAG_BF16,
+                                        buf, 128))
         return buf.value.decode()
 
     def check(self):

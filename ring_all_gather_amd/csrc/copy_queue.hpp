@@ -1,0 +1,113 @@
+// The piece queue of a call's copies (the simulated arrival of the peers' chunks), run by whole
+// workgroups: those of the arrival kernel on the side stream, or the GEMM's own workgroups while
+// the chunk of their next tile is not there yet.
+//
+// TransformerEngine issue #1583, C++ listing: each ring step copies one chunk into the gathered
+// buffer and then bumps that chunk's counter.  Here a chunk is cut into pieces; workgroups take
+// pieces in ring order with an atomic, copy them, and add them to the chunk's done count with one
+// agent-scope release each (which writes the copying XCD's L2 back).  The add that completes the
+// count releases the chunk's counter, after an acquire fence that orders every other workgroup's
+// pieces before it.  Whoever takes a piece copies it without waiting on anything, so every
+// chunk's count completes even when not all workgroups are resident.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "kernels.hpp"
+
+namespace ringag {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Copy piece k of copy c with the NT threads of the workgroup (16-byte vectors, 8 in flight per
+// thread).
+template <int NT>
+__device__ __forceinline__ void copy_piece(const CopyPlan& p, unsigned c, unsigned k) {
+  constexpr int U = 8;
+  const unsigned long long beg = (unsigned long long)k * p.piece_bytes;
+  const unsigned long long len = min((unsigned long long)p.piece_bytes, p.bytes - beg);
+  const v4i* s = (const v4i*)((const char*)p.src[c] + beg);
+  v4i* d = (v4i*)((char*)p.dst[c] + beg);
+  const unsigned nvec = (unsigned)(len / 16);
+  unsigned i = threadIdx.x;
+  for (; i + (U - 1) * NT < nvec; i += U * NT) {
+    v4i v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = s[i + u * NT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) d[i + u * NT] = v[u];
+  }
+  for (; i < nvec; i += NT) d[i] = s[i];
+}
+
+// Thread 0, after the workgroup's stores of `count` pieces of copy c are complete: add them to the
+// copy's done count; the add that completes it releases the copy's counter.
+__device__ inline void pieces_done(const CopyPlan& p, int* ctr, int epoch, unsigned c,
+                                   unsigned count) {
+  const unsigned old = __hip_atomic_fetch_add(p.done + c * kWordStride, count, __ATOMIC_RELEASE,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+  if (old + count != p.pieces) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (p.delay_ticks > 0) {
+    const unsigned long long t0 = wall_clock64();
+    while ((long long)(wall_clock64() - t0) < p.delay_ticks) __builtin_amdgcn_s_sleep(8);
+  }
+  // (the stamp goes first: once the last counter is out, the consumer may finish and the caller
+  // may read the trace)
+  if (p.trace) p.trace[c] = wall_clock64();
+  if (p.ctr_index[c] >= 0 && (p.pos[c] == 0 || !((p.withhold_mask >> p.pos[c]) & 1u)))
+    __hip_atomic_store(ctr + p.ctr_index[c] * kWordStride, epoch, __ATOMIC_RELEASE,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Start of a launch that runs copies: zero the other set of counts for the next call and stamp
+// the start.  Called by every thread.
+__device__ inline void copy_queue_begin(const CopyPlan& p) {
+  if (blockIdx.x != 0) return;
+  if (threadIdx.x < 2 * kArrSlots)
+    __hip_atomic_store(p.clear_next + threadIdx.x * kWordStride, 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  if (p.trace && threadIdx.x == 0) p.trace[kTraceStart] = wall_clock64();
+}
+
+// Take pieces of queue q (0 = the peers' chunks, 1 = the own chunk) and copy them until the queue
+// is empty or, with stop >= 0, until ctr[stop] == epoch (checked before each take).  Called by
+// every thread of the workgroup; s_word is a workgroup-shared word.
+//
+// Each iteration has exactly one thread-0 step, between barriers: complete the piece copied in
+// the previous iteration, then take the next one.  (With a thread-0 step at the end of the body
+// and another at the start, the compiler may thread their common condition across the back edge
+// and lower the loop so that thread 0's lane is held back while the wave's other lanes start the
+// next iteration with the stale piece number, a loop that never ends.)  The taken number is read
+// into a scalar register, so the loop's exit is uniform.
+template <int NT>
+__device__ inline void run_copy_queue(const CopyPlan& p, int* ctr, int epoch, int q, int stop,
+                                      unsigned* s_word) {
+  const unsigned first = q == 0 ? 0u : (unsigned)p.n_peer;
+  const unsigned total = (q == 0 ? (unsigned)p.n_peer : (unsigned)(p.n - p.n_peer)) * p.pieces;
+  if (total == 0) return;
+  unsigned prev = ~0u;   // copy of the piece finished in the previous iteration, if any
+  while (true) {
+    if (threadIdx.x == 0) {
+      if (prev != ~0u) pieces_done(p, ctr, epoch, prev, 1);
+      unsigned g = ~0u;
+      if (stop < 0 || __hip_atomic_load(ctr + stop * kWordStride, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) != epoch)
+        g = __hip_atomic_fetch_add(p.grab + q * kWordStride, 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+      *s_word = g;
+    }
+    __syncthreads();
+    const unsigned g = __builtin_amdgcn_readfirstlane(*s_word);
+    __syncthreads();
+    if (g >= total) return;
+    const unsigned c = first + g / p.pieces;
+    copy_piece<NT>(p, c, g % p.pieces);
+    // every wave waits for its own stores; after the barrier thread 0 completes the piece
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    prev = c;
+  }
+}
+
+}  // namespace ringag

@@ -28,6 +28,6 @@ RAG_AG_ENTRY(t256x256, Tile256x256)
 RAG_AG_ENTRY(t256x256w8, Tile256x256w8)
 RAG_AG_ENTRY(t256x256w8s4, Tile256x256w8s4)
 
-extern "C" __global__ void __launch_bounds__(kArrThreads) rag_arrival(ArrivalArgs a) {
+extern "C" __global__ void __launch_bounds__(kArrivalThreads) rag_arrival(ArrivalArgs a) {
   arrival_body(a);
 }

@@ -8,8 +8,16 @@
 // its chunk's counter (agent-scope acquire, bounded by a wall-clock limit), the workgroup meets at
 // a barrier, and the K loop starts.  Each chunk's output rows go straight to that chunk's rank
 // offset of D (or to its staging slot), so D is rank-ordered for every self rank.
+//
+// With in-kernel copies (AgArgs::copies) the launch also carries the call's arrival: a workgroup
+// whose next tile belongs to a chunk that is not there yet takes pieces of the peers' chunks from
+// the copy queue (ring order) until that chunk is released, and once out of tiles it helps with
+// whatever is left, the own chunk's copy into G last.  The waiting workgroups are exactly the ones
+// with nothing to compute, so the copies use compute units that would otherwise idle, and no side
+// stream or stream fork/join is involved.
 #pragma once
 
+#include "copy_queue.hpp"
 #include "gemm_core.hpp"
 #include "kernels.hpp"
 
@@ -50,10 +58,27 @@ __device__ inline unsigned hw_location() {
   return (xcc << 16) | (se << 8) | cu;
 }
 
+// The tile this workgroup runs in the round that covers ring-ordered tiles [r0, r0 + n) of a grid
+// of `grid` workgroups, or -1.  Workgroup w runs on XCD w % 8 (workgroups are dealt to the 8 XCDs
+// in turn), and XCD x takes the x-th eighth of the round as one contiguous block, so the tiles
+// that share an XCD's L2 come from one chunk (or two neighbours in ring order) and are released
+// together; tiles from chunks released at different times would share an L2 out of phase and
+// fetch the weight's slices separately.  Within a chunk u -> (u % tiles_i, u / tiles_i): an
+// XCD's block covers all of a chunk's row blocks and a band of the weight's rows.  Grids that
+// are not a multiple of 8 use plain round-robin.
+__device__ inline int round_tile(int r0, int n, int grid) {
+  const int w = (int)blockIdx.x;
+  if ((grid & 7) != 0) return w < n ? r0 + w : -1;
+  const int x = w & 7, q = w >> 3;
+  const int lo = (x * n) >> 3, hi = ((x + 1) * n) >> 3;
+  return q < hi - lo ? r0 + lo + q : -1;
+}
+
 template <class S, bool FP8>
 __device__ __forceinline__ void ag_gemm_body(const AgArgs& a) {
   __shared__ __attribute__((aligned(1024))) char lds[S::LDS];
   __shared__ int s_ok;
+  __shared__ unsigned s_piece;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t ldb = (uint32_t)a.K * (FP8 ? 1u : 2u);
@@ -63,23 +88,32 @@ __device__ __forceinline__ void ag_gemm_body(const AgArgs& a) {
   float scale = 1.0f;
   if constexpr (FP8) scale = a.scale_A[0] * a.scale_B[0];
   const i32x4 ry = make_rsrc(a.A, (uint32_t)a.M * ldb);
+  if (a.copies) copy_queue_begin(a.cp);
+  const bool copier = a.copies && ((blockIdx.x >> 3) % a.copy_stride) == 0;
 
-  for (int t = blockIdx.x; t < total; t += gridDim.x) {
+  const int grid = (int)gridDim.x;
+  for (int r0 = 0; a.compute && r0 < total; r0 += grid) {
+    const int t = round_tile(r0, min(grid, total - r0), grid);
+    if (t < 0) continue;
     const int j = t / U;
     const int u = t - j * U;
-    int rb, cb;
-    map_tile_xcd(u, U, a.tiles_i, a.tiles_j, a.xcd_rows, &rb, &cb);
+    const int rb = u % a.tiles_i, cb = u / a.tiles_i;
     unsigned long long* tr = a.trace ? a.trace + kTraceTileWords * (size_t)t : nullptr;
     if (tr && threadIdx.x == 0) tr[0] = wall_clock64();
     if (a.ctr_index[j] >= 0) {
+      if (copier) run_copy_queue<S::NT>(a.cp, a.ctr, a.epoch, 0, a.ctr_index[j], &s_piece);
       if (threadIdx.x == 0)
         s_ok = wait_ready(a.ctr + a.ctr_index[j] * kWordStride, a.epoch, a.err, a.spin_limit);
       __syncthreads();
-      const int ok = s_ok;
+      const int ok = __builtin_amdgcn_readfirstlane(s_ok);   // uniform: see run_copy_queue
       __syncthreads();
       if (!ok) continue;
     }
-    if (tr && threadIdx.x == 0) tr[1] = wall_clock64();
+    unsigned long long cyc0 = 0;
+    if (tr && threadIdx.x == 0) {
+      tr[1] = wall_clock64();
+      cyc0 = __builtin_amdgcn_s_memtime();
+    }
     const i32x4 rx = make_rsrc(a.chunk[j], (uint32_t)a.nc * ldb);
     uint32_t xo[S::XQ], yo[S::YQ];
     tile_offsets<S, S::XQ>(xo, rb * S::BI, a.nc, ldb, wave, lane);
@@ -91,9 +125,16 @@ __device__ __forceinline__ void ag_gemm_body(const AgArgs& a) {
     if (tr && threadIdx.x == 0) {
       tr[2] = wall_clock64();
       tr[3] = ((unsigned long long)blockIdx.x << 32) | hw_location();
+      tr[4] = __builtin_amdgcn_s_memtime() - cyc0;
     }
+    // keeps this thread-0 step and the next tile's apart (see run_copy_queue)
+    __syncthreads();
   }
-  // The copies run on another stream, which the caller's stream does not wait for: the kernel
+  if (copier) {
+    run_copy_queue<S::NT>(a.cp, a.ctr, a.epoch, 0, -1, &s_piece);
+    run_copy_queue<S::NT>(a.cp, a.ctr, a.epoch, 1, -1, &s_piece);
+  }
+  // With the copies on another stream, which the caller's stream does not wait for, the kernel
   // ends only once the last copy (the own chunk into G) is complete, so that everything enqueued
   // after it sees a complete G.  The peers' chunks are complete already, since some tile waited
   // for each of them.

@@ -21,6 +21,33 @@ constexpr int kMaxTp = 16;
 // behind the polls.
 constexpr int kWordStride = 64;
 
+// The copies of one call's simulated arrival, as a queue of pieces (copy kernel on the side
+// stream, or the GEMM's own workgroups while their chunk is not there yet).  Copies
+// 0..n_peer-1 are the peers' chunks in ring order; each releases ctr[ctr_index[c]] = epoch once
+// all its pieces are copied.  Copy n_peer, when n > n_peer, is the own chunk into its slot of G
+// (ctr_index -1 unless something waits for it).  Two grab counts hand out the pieces in order:
+// grab[0] over the peers' pieces, grab[kWordStride] over the own chunk's; done[c * kWordStride]
+// counts the copied pieces of copy c.  The counts come in two sets used by alternate calls; a
+// launch zeroes the other set (clear_next, 2 * kArrSlots counts) for the next call.
+constexpr int kArrSlots = kMaxTp + 1;   // copies per call at most (tp - 1 peers + the own chunk)
+
+struct CopyPlan {
+  const void* src[kArrSlots];
+  void* dst[kArrSlots];
+  int ctr_index[kArrSlots];      // counter released when copy c is complete, or -1
+  int pos[kArrSlots];            // ring position of copy c (withhold hook); 0 = the own chunk
+  int n_peer, n;
+  unsigned long long bytes;      // bytes per copy, multiple of 16
+  unsigned pieces;               // pieces per copy: ceil(bytes / piece_bytes)
+  unsigned piece_bytes;          // multiple of 16
+  unsigned* grab;
+  unsigned* done;
+  unsigned* clear_next;
+  long long delay_ticks;         // test hook: hold each release back this long
+  unsigned withhold_mask;        // test hook: bit pos (>= 1) set = never release that chunk
+  unsigned long long* trace;     // optional: [c] = completion time of copy c, [kTraceStart] = start
+};
+
 // Arguments of the counter-gated AG+GEMM kernel.  Chunk positions j = 0..tp-1 are the ring order
 // at this rank (position 0 = own chunk).
 struct AgArgs {
@@ -33,13 +60,17 @@ struct AgArgs {
   int M, K, nc, tp;
   int* ctr;                      // per-chunk ready counters (kWordStride apart)
   int epoch;                     // value meaning "ready" for this call
-  int* err;                      // error word: set to 1 when a wait times out
+  int* err;                      // error word: set to the epoch when a wait times out
   long long spin_limit;          // wall-clock ticks a tile waits before giving up
   const float* scale_A;          // fp8: dequantisation factors (device scalars)
   const float* scale_B;
   int tiles_i, tiles_j;          // tile grid of one chunk
-  int xcd_rows;                  // XCD rectangle split (see map_tile_xcd); 0 = linear order
+  int xcd_rows;                  // unused (the AG kernel's schedule is fixed, see round_tile)
   unsigned long long* trace;     // optional per-tile stamps (kTraceTileWords per tile), or null
+  int copies;                    // 1 = this kernel also runs the copies of `cp`
+  int copy_stride;               // workgroups w with (w / 8) % copy_stride == 0 copy
+  int compute;                   // 0 = copies only, no tiles
+  CopyPlan cp;
 };
 
 // Arguments of the GEMM+RS kernel.  Row-chunk positions j = 0..tp-1 in visiting order; the last
@@ -57,36 +88,23 @@ struct RsArgs {
   int xcd_rows;
 };
 
-// Arguments of the arrival (producer) kernel: copies j = 0..n-1 in order, each followed (when
-// ctr_index[j] >= 0) by a release of ctr[ctr_index[j]] = epoch once every piece of it is copied.
-// Counters and per-copy counts are kWordStride ints apart.
-constexpr int kArrSlots = kMaxTp + 1;   // copies per launch at most (tp - 1 peers + the own chunk)
-
+// Arguments of the arrival (producer) kernel on the side stream: runs the whole piece queue.
 struct ArrivalArgs {
-  const void* src[kArrSlots];
-  void* dst[kArrSlots];
-  int ctr_index[kArrSlots];
-  int pos[kArrSlots];            // ring position of copy j (for the withhold mask)
-  int n;
-  unsigned long long bytes;      // bytes per copy, multiple of 16
+  CopyPlan cp;
   int* ctr;
-  unsigned* grab;                // [kArrSlots] next piece to take, per copy (this launch's set)
-  unsigned* done;                // [kArrSlots] pieces copied, per copy (this launch's set)
-  unsigned* clear_next;          // 2 * kArrSlots counts of the other set, zeroed for the next launch
   int epoch;
-  long long delay_ticks;         // test hook: hold each release back this long
-  unsigned withhold_mask;        // test hook: bit pos (>= 1) set = never release that chunk
-  unsigned long long* trace;     // optional: [j] = release time of copy j, [kTraceStart] = start
   int raise_priority;            // 1 = run the copy waves at the highest issue priority
 };
 
 // Trace layout (64-bit words, wall clock at 100 MHz): words [0, kTraceHeader) belong to the
-// arrival kernel (release time of copy j at [j], first workgroup's start at [kTraceStart]); tile t
-// of the GEMM (ring-ordered index) owns words kTraceHeader + 4 t .. + 3: start (before its wait),
-// after the wait, end (after its stores), and (workgroup << 32) | (XCC << 16) | (SE << 8) | CU.
+// copies (completion time of copy c at [c], start of the first copying launch at [kTraceStart]);
+// tile t of the GEMM (ring-ordered index) owns words kTraceHeader + 5 t .. + 4: start (before its
+// wait), after the wait, end (after its stores), (workgroup << 32) | (XCC << 16) | (SE << 8) | CU,
+// and the core clock cycles (s_memtime) from after the wait to the end, so that cycles / wall
+// time gives the clock the tile ran at.
 constexpr int kTraceHeader = 64;
 constexpr int kTraceStart = 32;
-constexpr int kTraceTileWords = 4;
+constexpr int kTraceTileWords = 5;
 
 enum TileCfg {
   kTile128x128 = 1, kTile256x128 = 2, kTile256x256 = 3, kTile256x256w8 = 4, kTile256x256w8s4 = 5

@@ -79,7 +79,7 @@ struct rag_ctx {
   int num_cus = 0;
   long long wall_khz = 100000;
   // options
-  int copy_engine = 0;
+  int copy_engine = RAG_COPY_IN_GEMM;
   int comm_wgs = 32;
   long long spin_us = 2000000;
   long long delay_us = 0;
@@ -88,6 +88,7 @@ struct rag_ctx {
   bool timing = false;
   int wgs_per_cu = 0;
   int copy_priority = 1;
+  int gemm_copy_wgs = 0;
   unsigned long long trace_buf = 0;
   long long trace_bytes = 0;
   std::vector<hipEvent_t> t_start, t_stop;
@@ -144,10 +145,20 @@ int next_epoch(rag_ctx* c) {
   return c->epoch;
 }
 
-int choose_ag_tile(const rag_ctx* c, int nc, int M) {
+// The largest tile that still gives every compute unit a tile: bigger tiles re-read less from
+// L2 per flop, but a grid with idle compute units loses more than that.
+int choose_ag_tile(const rag_ctx* c, int nc, int M, int tp) {
   if (c->tile != RAG_TILE_AUTO) return c->tile;
-  if (nc >= 256 && M >= 128) return kTile256x128;
+  auto tiles = [&](int bi, int bj) {
+    return (long long)((nc + bi - 1) / bi) * ((M + bj - 1) / bj) * tp;
+  };
+  if (tiles(256, 256) >= c->num_cus) return kTile256x256w8;
+  if (tiles(256, 128) >= c->num_cus) return kTile256x128;
   return kTile128x128;
+}
+
+const char* engine_name(int e) {
+  return e == RAG_COPY_SDMA ? "sdma" : e == RAG_COPY_IN_GEMM ? "in-gemm" : "kernel";
 }
 
 // Compute units kept free of GEMM workgroups while arrivals run.  The 4-wave 256x256 tile uses
@@ -268,7 +279,8 @@ int rag_set_option(rag_ctx* c, int key, long long v) {
   if (!c) return fail(RAG_EINVAL, "rag_set_option: ctx is NULL");
   switch (key) {
     case RAG_OPT_COPY_ENGINE:
-      if (v != 0 && v != 1) return fail(RAG_EINVAL, "copy engine must be 0 (kernel) or 1 (sdma)");
+      if (v != RAG_COPY_KERNEL && v != RAG_COPY_SDMA && v != RAG_COPY_IN_GEMM)
+        return fail(RAG_EINVAL, "copy engine must be 0 (kernel), 1 (sdma) or 2 (in the GEMM)");
       c->copy_engine = (int)v;
       return RAG_OK;
     case RAG_OPT_COMM_WGS:
@@ -303,6 +315,10 @@ int rag_set_option(rag_ctx* c, int key, long long v) {
     case RAG_OPT_WGS_PER_CU:
       if (v < 0 || v > 16) return fail(RAG_EINVAL, "workgroups per CU must be in [0, 16]");
       c->wgs_per_cu = (int)v;
+      return RAG_OK;
+    case RAG_OPT_GEMM_COPY_WGS:
+      if (v < 0 || v > 65536) return fail(RAG_EINVAL, "GEMM copy workgroups must be in [0, 65536]");
+      c->gemm_copy_wgs = (int)v;
       return RAG_OK;
     case RAG_OPT_COPY_PRIORITY:
       if (v != 0 && v != 1) return fail(RAG_EINVAL, "copy priority must be 0 or 1");
@@ -391,7 +407,7 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
     return fail(RAG_EINVAL, "ag_gemm: the own chunk may only sit in G at its own slot");
   if ((flags & RAG_NO_COPY) && !G && !c->gbuf)
     return fail(RAG_EINVAL, "ag_gemm: RAG_NO_COPY reads the chunks from G; pass G");
-  if (c->copy_engine == 1 && c->delay_us > 0 && !(flags & RAG_NO_COPY))
+  if (c->copy_engine == RAG_COPY_SDMA && c->delay_us > 0 && !(flags & RAG_NO_COPY))
     return fail(RAG_EINVAL, "ag_gemm: the arrival delay hook needs the kernel copy engine");
 
   HIPCHK(hipSetDevice(c->device));
@@ -417,7 +433,7 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
   unsigned long long* trace = nullptr;
   if (c->trace_buf) {
     int bi, bj;
-    tile_dims(choose_ag_tile(c, nc, M), &bi, &bj);
+    tile_dims(choose_ag_tile(c, nc, M, tp), &bi, &bj);
     const long long tiles = (long long)((nc + bi - 1) / bi) * ((M + bj - 1) / bj) * tp;
     if ((kTraceHeader + kTraceTileWords * tiles) * 8 <= c->trace_bytes)
       trace = reinterpret_cast<unsigned long long*>(c->trace_buf);
@@ -425,56 +441,63 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
   int order[kMaxTp];
   for (int j = 0; j < tp; ++j) order[j] = ((self_rank - j) % tp + tp) % tp;
 
+  // The copies of the simulated arrival: the peers' chunks in ring order, then the own chunk
+  // into G.  Engines: a copy kernel on the side stream, SDMA on the side stream, or the GEMM's
+  // own workgroups (in-kernel: no side stream, no fork or join).
+  const bool in_kernel = !no_copy && c->copy_engine == RAG_COPY_IN_GEMM;
+  const int tile = choose_ag_tile(c, nc, M, tp);
+  CopyPlan cp = {};
   if (!no_copy) {
+    int n = 0;
+    for (int j = 1; j < tp; ++j, ++n) {
+      const int r = order[j];
+      cp.src[n] = B[r];
+      cp.dst[n] = Gp + (size_t)r * chunk_bytes;
+      cp.ctr_index[n] = r;
+      cp.pos[n] = j;
+    }
+    cp.n_peer = n;
+    if (own_copy) {
+      cp.src[n] = B[self_rank];
+      cp.dst[n] = Gp + (size_t)self_rank * chunk_bytes;
+      // the GEMM waits for it before exiting only when the copies run beside it
+      cp.ctr_index[n] = (copy_only || in_kernel) ? -1 : c->max_tp;
+      cp.pos[n] = 0;
+      ++n;
+    }
+    cp.n = n;
+    cp.bytes = (unsigned long long)chunk_bytes;
+    // a piece is two rounds of 8 16-byte vectors per thread of the copying workgroup
+    cp.piece_bytes = (unsigned)(in_kernel ? tile_threads(tile) : kArrivalThreads) * 256u;
+    cp.pieces = (unsigned)((cp.bytes + cp.piece_bytes - 1) / cp.piece_bytes);
+    const unsigned set = c->arr_seq & 1u;
+    cp.grab = c->arr + (size_t)set * 2 * kArrSlots * kWordStride;
+    cp.done = cp.grab + (size_t)kArrSlots * kWordStride;
+    cp.clear_next = c->arr + (size_t)(set ^ 1u) * 2 * kArrSlots * kWordStride;
+    cp.delay_ticks = c->delay_us * c->wall_khz / 1000;
+    cp.withhold_mask = c->withhold;
+    cp.trace = trace;
+  }
+
+  if (!no_copy && !in_kernel) {
     HIPCHK(hipEventRecord(c->ev_fork, stream));
     HIPCHK(hipStreamWaitEvent(c->side, c->ev_fork, 0));
-    if (c->copy_engine == 0) {
+    if (c->copy_engine == RAG_COPY_KERNEL) {
       ArrivalArgs aa = {};
-      int n = 0;
-      for (int j = 1; j < tp; ++j, ++n) {
-        const int r = order[j];
-        aa.src[n] = B[r];
-        aa.dst[n] = Gp + (size_t)r * chunk_bytes;
-        aa.ctr_index[n] = r;
-        aa.pos[n] = j;
-      }
-      if (own_copy) {
-        aa.src[n] = B[self_rank];
-        aa.dst[n] = Gp + (size_t)self_rank * chunk_bytes;
-        aa.ctr_index[n] = copy_only ? -1 : c->max_tp;
-        aa.pos[n] = 0;
-        ++n;
-      }
-      aa.n = n;
-      aa.bytes = (unsigned long long)chunk_bytes;
+      aa.cp = cp;
       aa.ctr = c->ctr;
-      const unsigned set = c->arr_seq & 1u;
-      aa.grab = c->arr + (size_t)set * 2 * kArrSlots * kWordStride;
-      aa.done = aa.grab + (size_t)kArrSlots * kWordStride;
-      aa.clear_next = c->arr + (size_t)(set ^ 1u) * 2 * kArrSlots * kWordStride;
       aa.epoch = epoch;
-      aa.delay_ticks = c->delay_us * c->wall_khz / 1000;
-      aa.withhold_mask = c->withhold;
-      aa.trace = trace;
       aa.raise_priority = c->copy_priority;
-      if (n > 0) {
+      if (cp.n > 0) {
         HIPCHK(launch_arrival(c->device, aa, c->comm_wgs, c->side));
         c->arr_seq++;
       }
     } else {
-      for (int j = 1; j < tp; ++j) {
-        const int r = order[j];
-        HIPCHK(hipMemcpyAsync(Gp + (size_t)r * chunk_bytes, B[r], (size_t)chunk_bytes,
+      for (int k = 0; k < cp.n; ++k) {
+        HIPCHK(hipMemcpyAsync(cp.dst[k], cp.src[k], (size_t)chunk_bytes,
                               hipMemcpyDeviceToDeviceNoCU, c->side));
-        if (!((c->withhold >> j) & 1u))
-          HIPCHK(hipStreamWriteValue32(c->side, c->ctr + (size_t)r * kWordStride,
-                                       (uint32_t)epoch, 0));
-      }
-      if (own_copy) {
-        HIPCHK(hipMemcpyAsync(Gp + (size_t)self_rank * chunk_bytes, B[self_rank],
-                              (size_t)chunk_bytes, hipMemcpyDeviceToDeviceNoCU, c->side));
-        if (!copy_only)
-          HIPCHK(hipStreamWriteValue32(c->side, c->ctr + (size_t)c->max_tp * kWordStride,
+        if (cp.ctr_index[k] >= 0 && (cp.pos[k] == 0 || !((c->withhold >> cp.pos[k]) & 1u)))
+          HIPCHK(hipStreamWriteValue32(c->side, c->ctr + (size_t)cp.ctr_index[k] * kWordStride,
                                        (uint32_t)epoch, 0));
       }
     }
@@ -483,14 +506,14 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
     if (copy_only) HIPCHK(hipEventRecord(c->ev_join, c->side));
   }
 
-  if (!copy_only) {
+  if (!copy_only || in_kernel) {
     AgArgs a = {};
     for (int j = 0; j < tp; ++j) {
       const int r = order[j];
       a.chunk[j] = (j == 0) ? B[self_rank] : (const void*)(Gp + (size_t)r * chunk_bytes);
       a.ctr_index[j] = (j == 0 || no_copy) ? -1 : r;
-      a.out[j] = staged ? (void*)((char*)c->stage + (size_t)j * nc * M * 2)
-                        : (void*)((char*)D + (size_t)r * nc * M * 2);
+      a.out[j] = (staged && !copy_only) ? (void*)((char*)c->stage + (size_t)j * nc * M * 2)
+                                        : (void*)((char*)D + (size_t)r * nc * M * 2);
     }
     a.A = A;
     a.M = M;
@@ -498,14 +521,16 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
     a.nc = nc;
     a.tp = tp;
     a.ctr = c->ctr;
-    a.join_index = (own_copy && !no_copy) ? c->max_tp : -1;
+    a.join_index = (own_copy && !no_copy && !in_kernel) ? c->max_tp : -1;
     a.epoch = epoch;
     a.err = c->err;
     a.spin_limit = c->spin_us * c->wall_khz / 1000;
     a.scale_A = scale_A;
     a.scale_B = scale_B;
     a.trace = trace ? trace + kTraceHeader : nullptr;
-    const int tile = choose_ag_tile(c, nc, M);
+    a.copies = in_kernel && cp.n > 0;
+    a.compute = copy_only ? 0 : 1;
+    a.cp = cp;
     int bi, bj;
     tile_dims(tile, &bi, &bj);
     a.tiles_i = (nc + bi - 1) / bi;
@@ -517,29 +542,30 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
     const int total = a.tiles_i * a.tiles_j * tp;
     int bpc = c->ag_info[tile][fp8].max_blocks_per_cu;
     if (c->wgs_per_cu > 0) bpc = std::min(bpc, c->wgs_per_cu);
-    const int grid = persistent_grid(total, c->num_cus - reserved_cus(tile, !no_copy), bpc);
-    {
-      const int U = a.tiles_i * a.tiles_j;
-      const int concurrent = std::min(tp, std::max(1, (grid + U - 1) / U));
-      a.xcd_rows = (grid % 8 == 0) ? choose_xcd_rows(a.tiles_i, a.tiles_j, concurrent, bi, bj) : 0;
-    }
+    const bool beside = !no_copy && c->copy_engine == RAG_COPY_KERNEL;
+    const int grid = persistent_grid(total, c->num_cus - reserved_cus(tile, beside), bpc);
+    a.xcd_rows = 0;   // the AG kernel deals each round's tiles to XCDs in contiguous blocks
+    // in-kernel copies: workgroups w with (w / 8) % copy_stride == 0 take part (workgroup 0 always)
+    a.copy_stride = 1;
+    if (a.copies && c->gemm_copy_wgs > 0 && grid >= 8)
+      a.copy_stride = std::max(1, (grid / 8) / std::max(1, c->gemm_copy_wgs / 8));
     if (debug_enabled())
       fprintf(stderr, "[ringag] ag_gemm tp=%d s=%d nc=%d K=%d M=%d %s tile=%dx%d tiles=%d grid=%d "
-              "(blocks/CU %d, VGPRs %d, LDS %d) xcd_rows=%d engine=%s comm_wgs=%d flags=0x%x "
-              "epoch=%d\n",
+              "(blocks/CU %d, VGPRs %d, LDS %d) engine=%s comm_wgs=%d pieces=%ux%u B "
+              "flags=0x%x epoch=%d\n",
               tp, self_rank, nc, K, M, fp8 ? "fp8" : "bf16", bi, bj, total, grid,
               c->ag_info[tile][fp8].max_blocks_per_cu, c->ag_info[tile][fp8].vgprs_per_wave,
-              c->ag_info[tile][fp8].lds_bytes, a.xcd_rows, c->copy_engine ? "sdma" : "kernel",
-              c->comm_wgs,
-              flags, epoch);
+              c->ag_info[tile][fp8].lds_bytes, engine_name(c->copy_engine),
+              c->comm_wgs, cp.pieces, cp.piece_bytes, flags, epoch);
     bool rec = false;
     int rc = record_timing_start(c, stream, &rec);
     if (rc) return rc;
     HIPCHK(launch_ag_gemm(c->device, a, tile, fp8, grid, stream));
+    if (a.copies) c->arr_seq++;
     rc = record_timing_stop(c, stream, rec);
     if (rc) return rc;
   }
-  if (!no_copy && copy_only) HIPCHK(hipStreamWaitEvent(stream, c->ev_join, 0));
+  if (!no_copy && !in_kernel && copy_only) HIPCHK(hipStreamWaitEvent(stream, c->ev_join, 0));
 
   if (staged && !copy_only) {
     const size_t dchunk = (size_t)nc * M * 2;
@@ -653,10 +679,11 @@ int gemm_rs(rag_ctx* c, const void* X, int T, int Kl, const void* W, int Mo,
   return record_timing_stop(c, stream, rec);
 }
 
-int rag_ag_kernel_name(rag_ctx* c, int nc, int M, rag_dtype dt, char* buf, int len) {
-  if (!c || !buf || len < 1) return fail(RAG_EINVAL, "rag_ag_kernel_name: bad arguments");
+int rag_ag_kernel_name(rag_ctx* c, int nc, int M, int tp, rag_dtype dt, char* buf, int len) {
+  if (!c || !buf || len < 1 || nc < 1 || M < 1 || tp < 1)
+    return fail(RAG_EINVAL, "rag_ag_kernel_name: bad arguments");
   if (dt != RAG_BF16 && dt != RAG_FP8_E4M3) return fail(RAG_EINVAL, "unknown dtype %d", dt);
-  snprintf(buf, (size_t)len, "%s", ag_kernel_name(choose_ag_tile(c, nc, M), dt == RAG_FP8_E4M3));
+  snprintf(buf, (size_t)len, "%s", ag_kernel_name(choose_ag_tile(c, nc, M, tp), dt == RAG_FP8_E4M3));
   return RAG_OK;
 }
 

@@ -13,6 +13,13 @@ from gpu_common import (AGRun, TOL_BF16, TOL_FP8, ctx, oracle_ag, oracle_ag_rows
 pytestmark = pytest.mark.gpu
 
 TILE_NAMES = ["128x128", "256x128", "256x256", "256x256w8", "256x256w8s4"]
+# copy engines of the simulated arrival that run on compute units: the side-stream copy kernel and
+# the GEMM's own waiting workgroups (SDMA is covered in the flags test)
+ENGINES = ["kernel", "in-gemm"]
+
+
+def set_engine(c, engine):
+    c.set_option(B.RAG_OPT_COPY_ENGINE, B.ENGINES[engine])
 
 
 @pytest.fixture(autouse=True)
@@ -39,29 +46,33 @@ def _int_case(tp, s, nc, K, M, seed, dtype="bf16"):
 CASES = [(tp, s, nc) for tp in (1, 2, 3, 4, 8) for s in range(tp) for nc in (16, 48, 256)]
 
 
+@pytest.mark.parametrize("engine", ENGINES)
 @pytest.mark.parametrize("tp,s,nc", CASES)
-def test_ag_exact_integers_every_rank(tp, s, nc):
+def test_ag_exact_integers_every_rank(tp, s, nc, engine):
     """Small integers are exact in bf16 and their fp32 sums are exact in any order, so D must be
     the oracle's sum rounded to bf16, bit for bit; G must be the rank-ordered concatenation."""
     c = ctx()
+    set_engine(c, engine)
     tile = TILE_NAMES[(tp + s + nc) % len(TILE_NAMES)]
     c.set_option(B.RAG_OPT_TILE, B.TILES[tile])
     inp = _int_case(tp, s, nc, K=128, M=80, seed=tp * 100 + s * 10 + nc)
-    say(f"case tp={tp} s={s} nc={nc} K=128 M=80 tile={tile}")
+    say(f"case tp={tp} s={s} nc={nc} K=128 M=80 tile={tile} engine={engine}")
     run = AGRun(inp).run(c)
     G_ref, ref = oracle_ag(inp)
     assert np.array_equal(W.bits_u16(run.G.cpu()), G_ref)
     assert np.array_equal(run.D_bits(), O.f32_to_bf16(ref))
 
 
+@pytest.mark.parametrize("engine", ENGINES)
 @pytest.mark.parametrize("tile", TILE_NAMES)
-def test_ag_ragged_tiles_random(tile):
+def test_ag_ragged_tiles_random(tile, engine):
     """Chunk rows and output columns that are not multiples of any tile (several tiles plus a
     ragged tail in both directions), normal data, every tile configuration."""
     c = ctx()
+    set_engine(c, engine)
     c.set_option(B.RAG_OPT_TILE, B.TILES[tile])
     shape = W.ag_shape(3, 2, 300, 320, 333, dist="normal_sqrtk", seed=5)
-    say(f"case {shape.name} tile={tile}")
+    say(f"case {shape.name} tile={tile} engine={engine}")
     inp = W.make_ag(shape)
     run = AGRun(inp).run(c)
     G_ref, ref = oracle_ag(inp)
@@ -97,9 +108,11 @@ def test_ag_bitwise_invariant_across_ranks_and_modes():
     assert rel_err(outs[0], ref) <= TOL_BF16
 
 
-def test_ag_flags_staged_copy_only_sdma():
+@pytest.mark.parametrize("engine", ENGINES)
+def test_ag_flags_staged_copy_only_sdma(engine):
     c = ctx()
-    for tp, s in ((4, 1), (2, 1), (3, 0)):
+    set_engine(c, engine)
+    for tp, s in ((4, 1), (2, 1), (3, 0), (1, 0)):
         inp = W.make_ag(W.ag_shape(tp, s, 96, 192, 160, dist="int3", seed=tp + s))
         _, ref = oracle_ag(inp)
         want = O.f32_to_bf16(ref)
@@ -115,16 +128,18 @@ def test_ag_flags_staged_copy_only_sdma():
         assert np.array_equal(W.bits_u16(run.G.cpu()), G_ref)
         assert bool((run.D.float() == 7.0).all())
         say(f"case sdma tp={tp} s={s}")
-        c.set_option(B.RAG_OPT_COPY_ENGINE, 1)
+        set_engine(c, "sdma")
         run.G.zero_()
         run.run(c)
         assert np.array_equal(run.D_bits(), want)
         assert np.array_equal(W.bits_u16(run.G.cpu()), G_ref)
-        c.set_option(B.RAG_OPT_COPY_ENGINE, 0)
+        set_engine(c, engine)
 
 
-def test_ag_internal_gather_buffer():
+@pytest.mark.parametrize("engine", ENGINES)
+def test_ag_internal_gather_buffer(engine):
     c = ctx()
+    set_engine(c, engine)
     inp = W.make_ag(W.ag_shape(4, 3, 64, 128, 96, dist="int3", seed=3))
     run = AGRun(inp, with_G=False)
     say("case G=NULL")
@@ -133,30 +148,34 @@ def test_ag_internal_gather_buffer():
     assert np.array_equal(run.D_bits(), O.f32_to_bf16(ref))
 
 
-def test_ag_gating_delayed_arrivals_on_poisoned_slots():
+@pytest.mark.parametrize("engine", ENGINES)
+def test_ag_gating_delayed_arrivals_on_poisoned_slots(engine):
     """Every slot of G is NaN before the call and each arrival is held back 2 ms after its copy:
     a tile that read its chunk before the counter said so would produce NaN or a wrong value."""
     c = ctx()
+    set_engine(c, engine)
     c.set_option(B.RAG_OPT_ARRIVAL_DELAY_US, 2000)
     inp = W.make_ag(W.ag_shape(4, 1, 256, 256, 256, dist="int3", seed=17))
     _, ref = oracle_ag(inp)
     want = O.f32_to_bf16(ref)
     run = AGRun(inp)
     for it in range(3):
-        say(f"case gating it={it}")
+        say(f"case gating it={it} engine={engine}")
         run.G.fill_(float("nan"))
         run.D.fill_(float("nan"))
         run.run(c)
         assert np.array_equal(run.D_bits(), want)
 
 
-def test_ag_withheld_chunk_times_out_and_context_recovers():
+@pytest.mark.parametrize("engine", ENGINES)
+def test_ag_withheld_chunk_times_out_and_context_recovers(engine):
     c = ctx()
+    set_engine(c, engine)
     c.set_option(B.RAG_OPT_SPIN_LIMIT_US, 20000)
     c.set_option(B.RAG_OPT_WITHHOLD_MASK, 1 << 2)
     inp = W.make_ag(W.ag_shape(4, 0, 128, 128, 128, dist="int3", seed=23))
     run = AGRun(inp)
-    say("case withheld chunk")
+    say(f"case withheld chunk engine={engine}")
     run.run(c)
     with pytest.raises(B.RagError) as ei:
         c.check()
@@ -169,10 +188,12 @@ def test_ag_withheld_chunk_times_out_and_context_recovers():
     assert np.array_equal(run.D_bits(), O.f32_to_bf16(ref))
 
 
-def test_ag_epoch_stress_fresh_data_same_buffers():
+@pytest.mark.parametrize("engine", ENGINES)
+def test_ag_epoch_stress_fresh_data_same_buffers(engine):
     """Back-to-back calls in the same buffers with new data each time: stale cache lines or a
     counter left over from the previous call would show up as a mismatch."""
     c = ctx()
+    set_engine(c, engine)
     shape = W.ag_shape(4, 2, 256, 256, 256, dist="int3", seed=0)
     run = AGRun(W.make_ag(shape))
     for it in range(30):
@@ -184,11 +205,13 @@ def test_ag_epoch_stress_fresh_data_same_buffers():
         _, ref = oracle_ag(inp)
         if not np.array_equal(run.D_bits(), O.f32_to_bf16(ref)):
             pytest.fail(f"iteration {it} differs from its oracle")
-    say("case epoch stress done")
+    say(f"case epoch stress done engine={engine}")
 
 
-def test_ag_fp8_small_parity_and_exact():
+@pytest.mark.parametrize("engine", ENGINES)
+def test_ag_fp8_small_parity_and_exact(engine):
     c = ctx()
+    set_engine(c, engine)
     shape = W.ag_shape(4, 3, 160, 256, 224, dtype="fp8", dist="normal", seed=31)
     say(f"case {shape.name}")
     inp = W.make_ag(shape)
@@ -205,12 +228,14 @@ def test_ag_fp8_small_parity_and_exact():
         assert np.array_equal(run.D_bits(), O.f32_to_bf16(ref))
 
 
+@pytest.mark.parametrize("engine", ENGINES)
 @pytest.mark.parametrize("name", ["ag_4k", "ag_qkv", "ag_fc1_f8"])
-def test_ag_full_size_sampled_rows(name):
+def test_ag_full_size_sampled_rows(name, engine):
     """The measured workloads at full size: first, last and 62 seeded rows of every chunk are
     compared with the oracle's rows (the full product would take the host minutes)."""
     shape = W.WORKLOADS[name]
-    say(f"case {shape}")
+    set_engine(ctx(), engine)
+    say(f"case {shape} engine={engine}")
     inp = W.make_ag(shape)
     run = AGRun(inp).run(ctx())
     ctx().check()
