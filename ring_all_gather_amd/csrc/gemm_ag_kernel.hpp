@@ -58,22 +58,6 @@ __device__ inline unsigned hw_location() {
   return (xcc << 16) | (se << 8) | cu;
 }
 
-// The tile this workgroup runs in the round that covers ring-ordered tiles [r0, r0 + n) of a grid
-// of `grid` workgroups, or -1.  Workgroup w runs on XCD w % 8 (workgroups are dealt to the 8 XCDs
-// in turn), and XCD x takes the x-th eighth of the round as one contiguous block, so the tiles
-// that share an XCD's L2 come from one chunk (or two neighbours in ring order) and are released
-// together; tiles from chunks released at different times would share an L2 out of phase and
-// fetch the weight's slices separately.  Within a chunk u -> (u % tiles_i, u / tiles_i): an
-// XCD's block covers all of a chunk's row blocks and a band of the weight's rows.  Grids that
-// are not a multiple of 8 use plain round-robin.
-__device__ inline int round_tile(int r0, int n, int grid) {
-  const int w = (int)blockIdx.x;
-  if ((grid & 7) != 0) return w < n ? r0 + w : -1;
-  const int x = w & 7, q = w >> 3;
-  const int lo = (x * n) >> 3, hi = ((x + 1) * n) >> 3;
-  return q < hi - lo ? r0 + lo + q : -1;
-}
-
 template <class S, bool FP8>
 __device__ __forceinline__ void ag_gemm_body(const AgArgs& a) {
   __shared__ __attribute__((aligned(1024))) char lds[S::LDS];

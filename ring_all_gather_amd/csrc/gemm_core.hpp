@@ -70,6 +70,22 @@ using Tile256x256 = TileShape<256, 256, 2, 2, 64, 4>;       // 4 waves of 128x12
 using Tile256x256w8 = TileShape<256, 256, 2, 4, 128, 2>;    // 8 waves of 128x64, 2 stages
 using Tile256x256w8s4 = TileShape<256, 256, 2, 4, 64, 4>;   // 8 waves of 128x64, 4 stages
 
+// The tile this workgroup runs in the round that covers ring-ordered tiles [r0, r0 + n) of a grid
+// of `grid` workgroups, or -1.  Workgroup w runs on XCD w % 8 (workgroups are dealt to the 8 XCDs
+// in turn), and XCD x takes the x-th eighth of the round as one contiguous block, so the tiles
+// that share an XCD's L2 come from one chunk (or two neighbours in ring order) and are released
+// together; tiles from chunks released at different times would share an L2 out of phase and
+// fetch the weight's slices separately.  Callers map a chunk-local index u to (u % tiles_i,
+// u / tiles_i), so an XCD's block covers all of a chunk's row blocks and a band of the weight's
+// rows.  Grids that are not a multiple of 8 use plain round-robin.
+__device__ inline int round_tile(int r0, int n, int grid) {
+  const int w = (int)blockIdx.x;
+  if ((grid & 7) != 0) return w < n ? r0 + w : -1;
+  const int x = w & 7, q = w >> 3;
+  const int lo = (x * n) >> 3, hi = ((x + 1) * n) >> 3;
+  return q < hi - lo ? r0 + lo + q : -1;
+}
+
 // Swizzle key of a tile row.  128-byte rows: 2 rows per 256-byte bank line, key (row >> 1) & 7
 // gives the 8 rows of each parity in a 16-row group 8 distinct segments.  64-byte rows: 4 rows per
 // line, key (row >> 2) & 3 gives the 4 rows of each residue 4 distinct segments.

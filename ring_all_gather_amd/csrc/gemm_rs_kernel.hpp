@@ -7,8 +7,14 @@
 // The rank computes its whole partial P = X W^T, chunk by chunk in ring order (the rank's own
 // chunk last, as in a ring reduce-scatter where the own chunk's sum completes last).  Tiles of
 // another rank's chunk store their fp32 accumulators to `send` (the outgoing contribution).
-// Tiles of the own chunk add the peers' fp32 partials to the accumulators while they are still in
-// registers and store the bf16 result: the reduction costs no extra pass over D.
+// Tiles of the own chunk add the peers' fp32 partials to their accumulators and store the bf16
+// result, so the reduction costs no extra pass over D.
+//
+// Epilogue: the accumulators are staged through LDS one wave row (TM rows of the tile) at a time,
+// then every thread moves whole 16-byte vectors along tile rows: send is written, and the peers'
+// partials are read, in full contiguous rows rather than in the MFMA layout's 4-byte scatter.
+// For the own chunk each thread holds a batch of vectors and issues the loads of one peer for the
+// whole batch before adding them, so a batch's loads are in flight together.
 #pragma once
 
 #include "gemm_core.hpp"
@@ -16,26 +22,115 @@
 
 namespace ringag {
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+template <class S>
+struct RsEpilogue {
+  static constexpr int LD = S::BJ * 4 + 32;        // staging row stride: the two rows a wave
+                                                    // writes at once fall in different banks
+  static constexpr int VPR = S::BJ / 4;            // 16-byte vectors per tile row
+  static constexpr int VPT = S::TM * VPR / S::NT;  // vectors per thread per staged wave row
+  // 8-wave tiles have half the registers per lane, and the waves of the second wave row still
+  // hold their accumulators while the first is reduced: smaller batches there
+  static constexpr int MAXB = S::NW >= 8 ? 4 : 8;
+  static constexpr int BATCH = VPT < MAXB ? VPT : MAXB;
+  static_assert(S::TM * LD <= S::LDS, "a wave row of fp32 accumulators must fit in LDS");
+  static_assert((S::TM * VPR) % S::NT == 0 && VPT % BATCH == 0, "vectors must divide evenly");
+};
+
+template <class S>
+__device__ inline void rs_epilogue(const f32x16 (&acc)[S::FI][S::FJ], char* lds, const RsArgs& a,
+                                   int c, bool own, int rb, int cb, int wave, int lane) {
+  using E = RsEpilogue<S>;
+  const int wi = wave / S::WJ, wj = wave % S::WJ;
+  const int col0 = cb * S::BJ;
+  const size_t prow0 = (size_t)a.self_rank * a.nc;
+  for (int slab = 0; slab < S::WI; ++slab) {
+    if (wi == slab) {
+#pragma unroll
+      for (int i = 0; i < S::FI; ++i)
+#pragma unroll
+        for (int j = 0; j < S::FJ; ++j) {
+          const int col = wj * S::TN + acc_col(j, lane);
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            *(float*)(lds + acc_row(i, e, lane) * E::LD + col * 4) = acc[i][j][e];
+        }
+    }
+    __syncthreads();
+    const int row0 = rb * S::BI + slab * S::TM;   // chunk-local row of the staged row 0
+    if (!own) {
+      float* out = a.send + (size_t)c * a.nc * a.Mo;
+#pragma unroll
+      for (int k = 0; k < E::VPT; ++k) {
+        const int idx = (int)threadIdx.x + k * S::NT;
+        const int r = idx / E::VPR, v = idx % E::VPR;
+        const int row = row0 + r, col = col0 + v * 4;
+        if (row < a.nc && col < a.Mo)
+          *(f32x4*)(out + (size_t)row * a.Mo + col) = *(const f32x4*)(lds + r * E::LD + v * 16);
+      }
+    } else {
+      __bf16* out = (__bf16*)a.D;
+      for (int b = 0; b < E::VPT; b += E::BATCH) {
+        f32x4 x[E::BATCH];
+        int row[E::BATCH], col[E::BATCH];
+        bool ok[E::BATCH];
+#pragma unroll
+        for (int q = 0; q < E::BATCH; ++q) {
+          const int idx = (int)threadIdx.x + (b + q) * S::NT;
+          const int r = idx / E::VPR, v = idx % E::VPR;
+          row[q] = row0 + r;
+          col[q] = col0 + v * 4;
+          ok[q] = row[q] < a.nc && col[q] < a.Mo;
+          x[q] = *(const f32x4*)(lds + r * E::LD + v * 16);
+        }
+        for (int p = 0; p < a.tp; ++p) {
+          if (p == a.self_rank) continue;
+          const float* part = a.partial[p] + prow0 * (size_t)a.ldp;
+          f32x4 y[E::BATCH];
+#pragma unroll
+          for (int q = 0; q < E::BATCH; ++q) {
+            const float* src = part + (size_t)row[q] * a.ldp + col[q];
+            if (!ok[q]) y[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+            else if (a.partial_vec) y[q] = *(const f32x4*)src;
+            else y[q] = f32x4{src[0], src[1], src[2], src[3]};
+          }
+#pragma unroll
+          for (int q = 0; q < E::BATCH; ++q) x[q] += y[q];
+        }
+#pragma unroll
+        for (int q = 0; q < E::BATCH; ++q)
+          if (ok[q])
+            *(bf16x4*)(out + (size_t)row[q] * a.Mo + col[q]) =
+                bf16x4{(__bf16)x[q][0], (__bf16)x[q][1], (__bf16)x[q][2], (__bf16)x[q][3]};
+      }
+    }
+    __syncthreads();
+  }
+}
+
 template <class S>
 __device__ __forceinline__ void gemm_rs_body(const RsArgs& a) {
   __shared__ __attribute__((aligned(1024))) char lds[S::LDS];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wi = wave / S::WJ, wj = wave % S::WJ;
   const uint32_t ldb = (uint32_t)a.Kl * 2u;
   const int ksteps = (int)(ldb / S::BKB);
   const int U = a.tiles_i * a.tiles_j;
   const int total = U * a.tp;
   const i32x4 ry = make_rsrc(a.W, (uint32_t)a.Mo * ldb);
+  const int grid = (int)gridDim.x;
 
-  for (int t = blockIdx.x; t < total; t += gridDim.x) {
+  for (int r0 = 0; r0 < total; r0 += grid) {
+    const int t = round_tile(r0, min(grid, total - r0), grid);
+    if (t < 0) continue;
     const int j = t / U;
     const int u = t - j * U;
     const int c = a.chunk_of[j];
     const bool own = (c == a.self_rank);
     if (!own && a.send == nullptr) continue;
-    int rb, cb;
-    map_tile_xcd(u, U, a.tiles_i, a.tiles_j, a.xcd_rows, &rb, &cb);
+    const int rb = u % a.tiles_i, cb = u / a.tiles_i;
     const char* xbase = (const char*)a.X + (size_t)c * a.nc * ldb;
     const i32x4 rx = make_rsrc(xbase, (uint32_t)a.nc * ldb);
     uint32_t xo[S::XQ], yo[S::YQ];
@@ -43,51 +138,7 @@ __device__ __forceinline__ void gemm_rs_body(const RsArgs& a) {
     tile_offsets<S, S::YQ>(yo, cb * S::BJ, a.Mo, ldb, wave, lane);
     f32x16 acc[S::FI][S::FJ];
     tile_kloop<S, false>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);
-
-    const int row0 = rb * S::BI + wi * S::TM;
-    const int col0 = cb * S::BJ + wj * S::TN;
-    if (!own) {
-      float* out = a.send + (size_t)c * a.nc * a.Mo;
-#pragma unroll
-      for (int i = 0; i < S::FI; ++i)
-#pragma unroll
-        for (int jj = 0; jj < S::FJ; ++jj) {
-          const int col = col0 + acc_col(jj, lane);
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int row = row0 + acc_row(i, e, lane);
-            if (row < a.nc && col < a.Mo) out[(size_t)row * a.Mo + col] = acc[i][jj][e];
-          }
-        }
-    } else {
-      // Own chunk: add every peer's partial to the accumulators one block at a time (16 extra
-      // registers live), then round to bf16 and store.
-      __bf16* out = (__bf16*)a.D;
-      const size_t prow0 = (size_t)a.self_rank * a.nc;
-#pragma unroll
-      for (int i = 0; i < S::FI; ++i)
-#pragma unroll
-        for (int jj = 0; jj < S::FJ; ++jj) {
-          const int col = col0 + acc_col(jj, lane);
-          float v[16];
-#pragma unroll
-          for (int e = 0; e < 16; ++e) v[e] = acc[i][jj][e];
-          for (int p = 0; p < a.tp; ++p) {
-            if (p == a.self_rank) continue;
-            const float* part = a.partial[p] + prow0 * (size_t)a.ldp;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int row = row0 + acc_row(i, e, lane);
-              if (row < a.nc && col < a.Mo) v[e] += part[(size_t)row * a.ldp + col];
-            }
-          }
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int row = row0 + acc_row(i, e, lane);
-            if (row < a.nc && col < a.Mo) out[(size_t)row * a.Mo + col] = (__bf16)v[e];
-          }
-        }
-    }
+    rs_epilogue<S>(acc, lds, a, c, own, rb, cb, wave, lane);
   }
 }
 

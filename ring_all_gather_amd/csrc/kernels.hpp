@@ -65,7 +65,6 @@ struct AgArgs {
   const float* scale_A;          // fp8: dequantisation factors (device scalars)
   const float* scale_B;
   int tiles_i, tiles_j;          // tile grid of one chunk
-  int xcd_rows;                  // unused (the AG kernel's schedule is fixed, see round_tile)
   unsigned long long* trace;     // optional per-tile stamps (kTraceTileWords per tile), or null
   int copies;                    // 1 = this kernel also runs the copies of `cp`
   int copy_stride;               // workgroups w with (w / 8) % copy_stride == 0 copy
@@ -85,7 +84,7 @@ struct RsArgs {
   void* D;                       // [nc, Mo] bf16
   int T, Kl, Mo, nc, tp, self_rank;
   int tiles_i, tiles_j;
-  int xcd_rows;
+  int partial_vec;               // 1 = every partial and ldp allow 16-byte loads
 };
 
 // Arguments of the arrival (producer) kernel on the side stream: runs the whole piece queue.
@@ -140,42 +139,6 @@ constexpr int kArrivalThreads = 256;   // block size of the arrival kernel
 // Threads per workgroup of a tile configuration (4 waves, or 8 for the 8-wave tiles).
 inline int tile_threads(int tile) {
   return (tile == kTile256x256w8 || tile == kTile256x256w8s4) ? 512 : 256;
-}
-
-// Chunk-local tile u -> (row block rb, column block cb) of a chunk's R x C tile grid.
-// Workgroups are dealt round-robin to the 8 XCDs, each with its own L2; with the persistent grid
-// and the chunk's tile count both multiples of 8, tile u runs on XCD u % 8.  With xcd_rows = a
-// (a divides 8, R % a == 0, C % (8 / a) == 0) the grid is cut into an a x (8/a) array of equal
-// rectangles and XCD x gets rectangle (x % a, x / a) in every chunk: its L2 then serves R/a row
-// blocks of the chunk and C/(8/a) column blocks of the weight, the same columns in every chunk.
-// xcd_rows = 0 (or shapes that do not divide) keeps row-block-fastest linear order.
-RAG_HD inline void map_tile_xcd(int u, int U, int R, int C, int a, int* rb, int* cb) {
-  if (a > 0 && (U & 7) == 0 && R % a == 0 && C % (8 / a) == 0) {
-    const int x = u & 7, q = u >> 3;
-    const int rr = R / a, cc = C / (8 / a);
-    *rb = (x % a) * rr + q % rr;
-    *cb = (x / a) * cc + q / rr;
-    return;
-  }
-  *rb = u % R;
-  *cb = u / R;
-}
-
-// The split a in {1, 2, 4, 8} that minimises the rows an XCD's L2 must hold when `chunks`
-// chunks' tiles run at once: chunks * (R / a) * bi + (C / (8 / a)) * bj; 0 if none divides.
-inline int choose_xcd_rows(int R, int C, int chunks, int bi, int bj) {
-  if ((R * C) % 8 != 0) return 0;
-  int best = 0;
-  long long best_rows = -1;
-  for (int a = 1; a <= 8; a *= 2) {
-    if (R % a || C % (8 / a)) continue;
-    const long long rows = (long long)chunks * (R / a) * bi + (long long)(C / (8 / a)) * bj;
-    if (best_rows < 0 || rows < best_rows) {
-      best_rows = rows;
-      best = a;
-    }
-  }
-  return best;
 }
 
 // Tile sizes of a configuration.

@@ -170,10 +170,8 @@ int reserved_cus(int tile, bool arrivals) {
   return (arrivals && tile == kTile256x256) ? 8 : 0;
 }
 
-int choose_rs_tile(const rag_ctx* c, int nc, int Mo) {
-  if (c->tile != RAG_TILE_AUTO) return c->tile;
-  if (nc >= 256 && Mo >= 256) return kTile256x256;
-  return kTile128x128;
+int choose_rs_tile(const rag_ctx* c, int nc, int Mo, int tp) {
+  return choose_ag_tile(c, nc, Mo, tp);   // same GEMM core and the same trade-off
 }
 
 // Persistent grid: every workgroup resident at once (so none waits for a slot while others spin
@@ -544,7 +542,6 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
     if (c->wgs_per_cu > 0) bpc = std::min(bpc, c->wgs_per_cu);
     const bool beside = !no_copy && c->copy_engine == RAG_COPY_KERNEL;
     const int grid = persistent_grid(total, c->num_cus - reserved_cus(tile, beside), bpc);
-    a.xcd_rows = 0;   // the AG kernel deals each round's tiles to XCDs in contiguous blocks
     // in-kernel copies: workgroups w with (w / 8) % copy_stride == 0 take part (workgroup 0 always)
     a.copy_stride = 1;
     if (a.copies && c->gemm_copy_wgs > 0 && grid >= 8)
@@ -653,7 +650,7 @@ int gemm_rs(rag_ctx* c, const void* X, int T, int Kl, const void* W, int Mo,
   a.nc = nc;
   a.tp = tp;
   a.self_rank = self_rank;
-  const int tile = choose_rs_tile(c, nc, Mo);
+  const int tile = choose_rs_tile(c, nc, Mo, tp);
   int bi, bj;
   tile_dims(tile, &bi, &bj);
   a.tiles_i = (nc + bi - 1) / bi;
@@ -664,11 +661,9 @@ int gemm_rs(rag_ctx* c, const void* X, int T, int Kl, const void* W, int Mo,
   }
   const int total = a.tiles_i * a.tiles_j * tp;
   const int grid = persistent_grid(total, c->num_cus, c->rs_info[tile].max_blocks_per_cu);
-  {
-    const int U = a.tiles_i * a.tiles_j;
-    const int concurrent = std::min(tp, std::max(1, (grid + U - 1) / U));
-    a.xcd_rows = (grid % 8 == 0) ? choose_xcd_rows(a.tiles_i, a.tiles_j, concurrent, bi, bj) : 0;
-  }
+  a.partial_vec = (ldp % 4) == 0;
+  for (int p = 0; p < tp; ++p)
+    if (a.partial[p] && (reinterpret_cast<uintptr_t>(a.partial[p]) & 15u) != 0) a.partial_vec = 0;
   if (debug_enabled())
     fprintf(stderr, "[ringag] gemm_rs tp=%d s=%d T=%d Kl=%d Mo=%d tile=%dx%d tiles=%d grid=%d\n",
             tp, self_rank, T, Kl, Mo, bi, bj, total, grid);
