@@ -26,7 +26,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}   # 256 CU x 2.4 GHz x (4096 | 8192) flop/clk
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "ag_4k_gemm_hbm_traffic.json")
+
 PEAK_HBM_GBS = 8000.0
 METRICS = {
     "ag": "AG+GEMM TFLOP/s (+% MFMA peak) and overlap efficiency, M=K=N=4096 tp=4",
@@ -131,11 +131,12 @@ def cpu_baseline_rs(inp, target_s):
                       f"MACs, fp32 triple loop), {dt:.1f} s wall"}
 
 
-def measured_traffic(kernel: str, fingerprint: str):
-    """HBM bytes per launch from the committed counter record, if it was taken with this exact
-    build of the kernels and this kernel; otherwise None."""
+def measured_traffic(workload: str, kernel: str, fingerprint: str):
+    """HBM bytes per launch from the committed counter record of this workload, if it was taken
+    with this exact build of the kernels and this kernel; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_gemm_hbm_traffic.json")
     try:
-        with open(TRAFFIC_RECORD) as f:
+        with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
@@ -197,8 +198,7 @@ def main():
         kernel_ms = statistics.fmean(kt)
         achieved = flops / (kernel_ms * 1e-3) / 1e12
         kname = ctx.ag_kernel_name(shape.nc, shape.M, shape.tp, shape.dtype == "fp8")
-        traffic = measured_traffic(kname, B.kernels_fingerprint()) \
-            if args.workload == "ag_4k" else None
+        traffic = measured_traffic(args.workload, kname, B.kernels_fingerprint())
         peak = PEAK_TFLOPS[shape.dtype]
         value = flops / (ms * 1e-3) / 1e12
         out = {
@@ -247,6 +247,7 @@ def main():
         kernel_ms = statistics.fmean(kt)
         flops = shape.flops
         nc, Mo, tp = shape.nc, shape.Mo, shape.tp
+        kname = ctx.rs_kernel_name(nc, Mo, tp)
         alg_bytes = (shape.T * shape.Kl * 2 + Mo * shape.Kl * 2 + (tp - 1) * nc * Mo * 4 * 2
                      + nc * Mo * 2)
         value = flops / (ms * 1e-3) / 1e12
@@ -263,8 +264,10 @@ def main():
             "step_ms": {"p10": round(pctl(per, 0.1), 5), "p50": round(pctl(per, 0.5), 5),
                         "p90": round(pctl(per, 0.9), 5)},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                         "kernel": "rag_rs (tile %s)" % args.tile, "kernel_ms": round(kernel_ms, 5),
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic(args.workload, kname,
+                                                     B.kernels_fingerprint()),
+                         "kernel": kname, "kernel_ms": round(kernel_ms, 5),
                          "algorithmic_bytes": alg_bytes},
         }
         if not args.no_cpu:

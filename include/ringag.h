@@ -227,6 +227,11 @@ RAG_API int rag_kernel_times(rag_ctx* ctx, float* out, int max_n);
 RAG_API int rag_ag_kernel_name(rag_ctx* ctx, int nc, int M, int tp, rag_dtype dt, char* buf,
                                int len);
 
+/* Name of the GPU kernel entry point gemm_rs would launch for these sizes (nc rows per chunk, Mo
+ * output columns, tp chunks) with the context's current options (e.g. "rag_rs_t256x256w8").
+ * Diagnostics, like rag_ag_kernel_name. */
+RAG_API int rag_rs_kernel_name(rag_ctx* ctx, int nc, int Mo, int tp, char* buf, int len);
+
 /* Text for the last non-zero return on the calling thread ("" if none). */
 RAG_API const char* rag_last_error(void);
 

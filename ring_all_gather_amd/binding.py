@@ -76,10 +76,11 @@ def lib():
     L.rag_check.argtypes = [vp]
     L.rag_kernel_times.argtypes = [vp, ctypes.POINTER(ctypes.c_float), i]
     L.rag_ag_kernel_name.argtypes = [vp, i, i, i, i, ctypes.c_char_p, i]
+    L.rag_rs_kernel_name.argtypes = [vp, i, i, i, ctypes.c_char_p, i]
     L.rag_last_error.restype = ctypes.c_char_p
     L.rag_version.restype = i
     for f in ("rag_create", "rag_destroy", "rag_set_option", "ag_gemm", "gemm_rs", "rag_check",
-              "rag_kernel_times", "rag_ag_kernel_name"):
+              "rag_kernel_times", "rag_ag_kernel_name", "rag_rs_kernel_name"):
         getattr(L, f).restype = i
     _lib = L
     return L
@@ -164,6 +165,12 @@ class Context:
         buf = ctypes.create_string_buffer(128)
         _check(lib().rag_ag_kernel_name(self.h, nc, M, tp, RAG_FP8_E4M3 if fp8 else RAG_BF16,
                                         buf, 128))
+        return buf.value.decode()
+
+    def rs_kernel_name(self, nc: int, Mo: int, tp: int) -> str:
+        """Entry point gemm_rs would launch for these sizes (diagnostics)."""
+        buf = ctypes.create_string_buffer(128)
+        _check(lib().rag_rs_kernel_name(self.h, nc, Mo, tp, buf, 128))
         return buf.value.decode()
 
     def check(self):

@@ -682,6 +682,13 @@ int rag_ag_kernel_name(rag_ctx* c, int nc, int M, int tp, rag_dtype dt, char* bu
   return RAG_OK;
 }
 
+int rag_rs_kernel_name(rag_ctx* c, int nc, int Mo, int tp, char* buf, int len) {
+  if (!c || !buf || len < 1 || nc < 1 || Mo < 1 || tp < 1)
+    return fail(RAG_EINVAL, "rag_rs_kernel_name: bad arguments");
+  snprintf(buf, (size_t)len, "%s", rs_kernel_name(choose_rs_tile(c, nc, Mo, tp)));
+  return RAG_OK;
+}
+
 int rag_check(rag_ctx* c) {
   if (!c) return fail(RAG_EINVAL, "rag_check: ctx is NULL");
   HIPCHK(hipSetDevice(c->device));

@@ -10,7 +10,8 @@ from ring_all_gather_amd import binding as B
 def test_header_declares_the_boundary():
     names = B.declared_functions()
     for f in ("rag_create", "rag_destroy", "rag_set_option", "ag_gemm", "gemm_rs", "rag_check",
-              "rag_kernel_times", "rag_last_error", "rag_version", "rag_ag_kernel_name"):
+              "rag_kernel_times", "rag_last_error", "rag_version", "rag_ag_kernel_name",
+              "rag_rs_kernel_name"):
         assert f in names
 
 
