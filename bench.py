@@ -45,7 +45,9 @@ def parse():
     p.add_argument("--own-chunk", default="in-g", choices=["in-g", "separate"],
                    help="in-g: the own chunk lives in its slot of G, as the local shard does in a "
                         "ring all-gather; separate: it is its own buffer and is copied into G")
-    p.add_argument("--comm-wgs", type=int, default=int(os.environ.get("RAG_COMM_WGS", "32")))
+    p.add_argument("--comm-wgs", type=int, default=int(os.environ.get("RAG_COMM_WGS", "128")),
+                   help="workgroups of the side-stream copy kernel (side-stream engine and the "
+                        "split form)")
     p.add_argument("--tile", default=os.environ.get("RAG_TILE", "auto"))
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target wall time of the CPU oracle sample")
@@ -193,6 +195,9 @@ def main():
         ms_gemm, _ = time_steps(lambda: step(B.RAG_NO_COPY), args.steps, args.warmup, stream)
         ms_copy, _ = time_steps(lambda: step(B.RAG_COPY_ONLY), args.steps, args.warmup, stream)
         ms_staged, _ = time_steps(lambda: step(B.RAG_STAGED_OUT), args.steps, args.warmup, stream)
+        # the split form (one GEMM launch per chunk, gated by stream events): what the in-kernel
+        # counters buy
+        ms_split, _ = time_steps(lambda: step(B.RAG_PER_CHUNK), args.steps, args.warmup, stream)
         ctx.check()
         flops = shape.flops
         kernel_ms = statistics.fmean(kt)
@@ -221,7 +226,8 @@ def main():
                         "t_copy_only_ms": round(ms_copy, 5),
                         "overlap_ratio": round(ms / (ms_copy + ms_gemm), 4),
                         "hidden_fraction": round((ms_copy + ms_gemm - ms) / ms_copy, 4),
-                        "t_staged_out_ms": round(ms_staged, 5)},
+                        "t_staged_out_ms": round(ms_staged, 5),
+                        "t_split_per_chunk_ms": round(ms_split, 5)},
             "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                          "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                          "kernel": kname, "kernel_ms": round(kernel_ms, 5)},

@@ -82,7 +82,14 @@ enum {
                            staging); the default writes each chunk at its rank offset directly */
     RAG_NO_COPY = 2,    /* AG+GEMM: no arrivals; every chunk counts as ready and is read from its
                            slot of G as it is (GEMM-only timing; G must already hold the chunks) */
-    RAG_COPY_ONLY = 4   /* AG+GEMM: arrivals (copies + counter bumps) only, no GEMM */
+    RAG_COPY_ONLY = 4,  /* AG+GEMM: arrivals (copies + counter bumps) only, no GEMM */
+    RAG_PER_CHUNK = 8   /* AG+GEMM, split form: one GEMM launch per chunk in ring order on `stream`,
+                           each waiting for its chunk's copy through a stream event instead of an
+                           in-kernel counter (TransformerEngine PR #2443, sequence diagram: the
+                           split overlap path; nvFuser PR #3392, experiment: one GEMM per received
+                           chunk).  The copies always run on the side stream (the copy kernel, or
+                           SDMA with RAG_COPY_SDMA); the per-tile trace is not recorded and the
+                           withhold hook does not apply */
 };
 
 /* Copy engines of the simulated arrival (RAG_OPT_COPY_ENGINE). */

@@ -27,7 +27,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "ringag.h")
 # constants of include/ringag.h
 RAG_OK, RAG_EINVAL, RAG_EHIP, RAG_ETIMEOUT, RAG_ENOMEM = 0, -1, -2, -3, -4
 RAG_BF16, RAG_FP8_E4M3 = 0, 1
-RAG_STAGED_OUT, RAG_NO_COPY, RAG_COPY_ONLY = 1, 2, 4
+RAG_STAGED_OUT, RAG_NO_COPY, RAG_COPY_ONLY, RAG_PER_CHUNK = 1, 2, 4, 8
 RAG_OPT_COPY_ENGINE, RAG_OPT_COMM_WGS, RAG_OPT_SPIN_LIMIT_US = 1, 2, 3
 RAG_OPT_ARRIVAL_DELAY_US, RAG_OPT_WITHHOLD_MASK, RAG_OPT_TIMING, RAG_OPT_TILE = 4, 5, 6, 7
 RAG_OPT_TRACE_BUF, RAG_OPT_TRACE_BYTES, RAG_OPT_WGS_PER_CU, RAG_OPT_COPY_PRIORITY = 8, 9, 10, 11

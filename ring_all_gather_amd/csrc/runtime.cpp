@@ -64,6 +64,7 @@ struct rag_ctx {
   int max_tp = 0;
   hipStream_t side = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  std::vector<hipEvent_t> ev_chunk;   // split form: chunk j copied (created on first use)
   // device counters, kWordStride ints apart: ctr[max_tp] | copy-complete | arrival counts
   // [2 sets][grab, done][kArrSlots] | err
   int* words = nullptr;
@@ -263,6 +264,7 @@ int rag_destroy(rag_ctx* c) {
   if (c->side) (void)hipStreamSynchronize(c->side);
   for (auto ev : c->t_start) (void)hipEventDestroy(ev);
   for (auto ev : c->t_stop) (void)hipEventDestroy(ev);
+  for (auto ev : c->ev_chunk) (void)hipEventDestroy(ev);
   if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
   if (c->ev_join) (void)hipEventDestroy(c->ev_join);
   if (c->side) (void)hipStreamDestroy(c->side);
@@ -341,6 +343,132 @@ int rag_set_option(rag_ctx* c, int key, long long v) {
   }
 }
 
+// Staged output (RAG_STAGED_OUT): slot j of the staging buffer holds the chunk at ring position j;
+// move the slots to D's rank offsets.
+int finalize_staged(rag_ctx* c, void* D, int nc, int M, int tp, const int* order,
+                    hipStream_t stream) {
+  const size_t dchunk = (size_t)nc * M * 2;
+  char* st = (char*)c->stage;
+  bool rotation = true;   // slot j holds chunk j-1 and slot 0 chunk tp-1
+  for (int j = 0; j < tp; ++j)
+    if (order[j] != (j + tp - 1) % tp) rotation = false;
+  if (rotation) {
+    // the listing's two copies: first chunk to the spare slot, then slots 1..tp are D
+    HIPCHK(hipMemcpyAsync(st + (size_t)tp * dchunk, st, dchunk, hipMemcpyDeviceToDevice, stream));
+    HIPCHK(hipMemcpyAsync(D, st + dchunk, (size_t)tp * dchunk, hipMemcpyDeviceToDevice, stream));
+  } else {
+    for (int j = 0; j < tp; ++j)
+      HIPCHK(hipMemcpyAsync((char*)D + (size_t)order[j] * dchunk, st + (size_t)j * dchunk,
+                            dchunk, hipMemcpyDeviceToDevice, stream));
+  }
+  return RAG_OK;
+}
+
+// Split form of AG+GEMM (RAG_PER_CHUNK): the side stream copies the peers' chunks in ring order,
+// recording an event after each; the caller's stream launches one GEMM per chunk in ring order,
+// each after waiting for its chunk's event.  The GEMM of one chunk is the same kernel with tp = 1
+// and no counters.  The own chunk's copy into G (if any) goes last, and the caller's stream waits
+// for the side stream's end before the call's later work.
+int ag_gemm_split(rag_ctx* c, const void* A, int M, int K, const void* const* B, int nc, int tp,
+                  int self_rank, char* Gp, bool own_copy, void* D, bool fp8, const float* scale_A,
+                  const float* scale_B, bool staged, bool no_copy, bool copy_only,
+                  long long chunk_bytes, const int* order, int epoch, hipStream_t stream) {
+  if (c->ev_chunk.empty()) {
+    c->ev_chunk.resize(c->max_tp, nullptr);
+    for (auto& ev : c->ev_chunk) HIPCHK(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+  }
+  if (!no_copy) {
+    HIPCHK(hipEventRecord(c->ev_fork, stream));
+    HIPCHK(hipStreamWaitEvent(c->side, c->ev_fork, 0));
+    for (int j = 1; j <= tp; ++j) {   // j == tp: the own chunk into G
+      const void* src;
+      void* dst;
+      if (j < tp) {
+        src = B[order[j]];
+        dst = Gp + (size_t)order[j] * chunk_bytes;
+      } else if (own_copy) {
+        src = B[self_rank];
+        dst = Gp + (size_t)self_rank * chunk_bytes;
+      } else {
+        break;
+      }
+      if (c->copy_engine == RAG_COPY_SDMA) {
+        HIPCHK(hipMemcpyAsync(dst, src, (size_t)chunk_bytes, hipMemcpyDeviceToDeviceNoCU,
+                              c->side));
+      } else {
+        ArrivalArgs aa = {};
+        aa.cp.src[0] = src;
+        aa.cp.dst[0] = dst;
+        aa.cp.ctr_index[0] = -1;
+        aa.cp.pos[0] = j < tp ? j : 0;
+        aa.cp.n_peer = 1;
+        aa.cp.n = 1;
+        aa.cp.bytes = (unsigned long long)chunk_bytes;
+        aa.cp.piece_bytes = (unsigned)kArrivalThreads * 256u;
+        aa.cp.pieces = (unsigned)((aa.cp.bytes + aa.cp.piece_bytes - 1) / aa.cp.piece_bytes);
+        const unsigned set = c->arr_seq & 1u;
+        aa.cp.grab = c->arr + (size_t)set * 2 * kArrSlots * kWordStride;
+        aa.cp.done = aa.cp.grab + (size_t)kArrSlots * kWordStride;
+        aa.cp.clear_next = c->arr + (size_t)(set ^ 1u) * 2 * kArrSlots * kWordStride;
+        aa.cp.delay_ticks = c->delay_us * c->wall_khz / 1000;
+        aa.ctr = c->ctr;
+        aa.epoch = epoch;
+        aa.raise_priority = c->copy_priority;
+        HIPCHK(launch_arrival(c->device, aa, c->comm_wgs, c->side));
+        c->arr_seq++;
+      }
+      if (j < tp) HIPCHK(hipEventRecord(c->ev_chunk[j], c->side));
+    }
+    HIPCHK(hipEventRecord(c->ev_join, c->side));
+  }
+  if (!copy_only) {
+    const int tile = choose_ag_tile(c, nc, M, 1);
+    if (!c->ag_info_ok[tile][fp8]) {
+      HIPCHK(ag_kernel_info(c->device, tile, fp8, &c->ag_info[tile][fp8]));
+      c->ag_info_ok[tile][fp8] = true;
+    }
+    int bi, bj;
+    tile_dims(tile, &bi, &bj);
+    AgArgs a = {};
+    a.A = A;
+    a.M = M;
+    a.K = K;
+    a.nc = nc;
+    a.tp = 1;
+    a.ctr_index[0] = -1;
+    a.join_index = -1;
+    a.ctr = c->ctr;
+    a.epoch = epoch;
+    a.err = c->err;
+    a.spin_limit = c->spin_us * c->wall_khz / 1000;
+    a.scale_A = scale_A;
+    a.scale_B = scale_B;
+    a.tiles_i = (nc + bi - 1) / bi;
+    a.tiles_j = (M + bj - 1) / bj;
+    a.compute = 1;
+    a.copy_stride = 1;
+    int bpc = c->ag_info[tile][fp8].max_blocks_per_cu;
+    if (c->wgs_per_cu > 0) bpc = std::min(bpc, c->wgs_per_cu);
+    const int grid = persistent_grid(a.tiles_i * a.tiles_j, c->num_cus, bpc);
+    const size_t dchunk = (size_t)nc * M * 2;
+    bool rec = false;
+    int rc = record_timing_start(c, stream, &rec);
+    if (rc) return rc;
+    for (int j = 0; j < tp; ++j) {
+      const int r = order[j];
+      if (!no_copy && j > 0) HIPCHK(hipStreamWaitEvent(stream, c->ev_chunk[j], 0));
+      a.chunk[0] = (j == 0) ? B[self_rank] : (const void*)(Gp + (size_t)r * chunk_bytes);
+      a.out[0] = staged ? (void*)((char*)c->stage + (size_t)j * dchunk)
+                        : (void*)((char*)D + (size_t)r * dchunk);
+      HIPCHK(launch_ag_gemm(c->device, a, tile, fp8, grid, stream));
+    }
+    rc = record_timing_stop(c, stream, rec);
+    if (rc) return rc;
+  }
+  if (!no_copy) HIPCHK(hipStreamWaitEvent(stream, c->ev_join, 0));
+  return RAG_OK;
+}
+
 int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int nc, int tp,
             int self_rank, void* G, void* D, rag_dtype dt, const float* scale_A,
             const float* scale_B, int flags, void* stream_v) {
@@ -358,7 +486,7 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
   if (K % kmul)
     return fail(RAG_EINVAL, "ag_gemm: K=%d must be a multiple of %d for %s", K, kmul,
                 fp8 ? "fp8" : "bf16");
-  if (flags & ~(RAG_STAGED_OUT | RAG_NO_COPY | RAG_COPY_ONLY))
+  if (flags & ~(RAG_STAGED_OUT | RAG_NO_COPY | RAG_COPY_ONLY | RAG_PER_CHUNK))
     return fail(RAG_EINVAL, "ag_gemm: unknown flag bits 0x%x", flags);
   if ((flags & RAG_NO_COPY) && (flags & RAG_COPY_ONLY))
     return fail(RAG_EINVAL, "ag_gemm: RAG_NO_COPY and RAG_COPY_ONLY exclude each other");
@@ -438,6 +566,14 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
   }
   int order[kMaxTp];
   for (int j = 0; j < tp; ++j) order[j] = ((self_rank - j) % tp + tp) % tp;
+
+  if (flags & RAG_PER_CHUNK) {
+    const int rc = ag_gemm_split(c, A, M, K, B, nc, tp, self_rank, Gp, own_copy, D, fp8, scale_A,
+                                 scale_B, staged, no_copy, copy_only, chunk_bytes, order, epoch,
+                                 stream);
+    if (rc) return rc;
+    return staged && !copy_only ? finalize_staged(c, D, nc, M, tp, order, stream) : RAG_OK;
+  }
 
   // The copies of the simulated arrival: the peers' chunks in ring order, then the own chunk
   // into G.  Engines: a copy kernel on the side stream, SDMA on the side stream, or the GEMM's
@@ -564,23 +700,7 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
   }
   if (!no_copy && !in_kernel && copy_only) HIPCHK(hipStreamWaitEvent(stream, c->ev_join, 0));
 
-  if (staged && !copy_only) {
-    const size_t dchunk = (size_t)nc * M * 2;
-    char* st = (char*)c->stage;
-    bool rotation = true;   // slot j holds chunk j-1 and slot 0 chunk tp-1
-    for (int j = 0; j < tp; ++j)
-      if (order[j] != (j + tp - 1) % tp) rotation = false;
-    if (rotation) {
-      // the listing's two copies: first chunk to the spare slot, then slots 1..tp are D
-      HIPCHK(hipMemcpyAsync(st + (size_t)tp * dchunk, st, dchunk, hipMemcpyDeviceToDevice, stream));
-      HIPCHK(hipMemcpyAsync(D, st + dchunk, (size_t)tp * dchunk, hipMemcpyDeviceToDevice, stream));
-    } else {
-      for (int j = 0; j < tp; ++j)
-        HIPCHK(hipMemcpyAsync((char*)D + (size_t)order[j] * dchunk, st + (size_t)j * dchunk,
-                              dchunk, hipMemcpyDeviceToDevice, stream));
-    }
-  }
-  return RAG_OK;
+  return staged && !copy_only ? finalize_staged(c, D, nc, M, tp, order, stream) : RAG_OK;
 }
 
 int gemm_rs(rag_ctx* c, const void* X, int T, int Kl, const void* W, int Mo,

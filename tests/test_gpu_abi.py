@@ -33,7 +33,7 @@ def test_ag_gemm_rejects_bad_arguments():
         (dict(K=100), "multiple of 64"), (dict(M=0), ">= 1"), (dict(nc=0), ">= 1"),
         (dict(A=None), "NULL"), (dict(D=None), "NULL"), (dict(A=Ap + 2), "aligned"),
         (dict(D=Dp + 8), "aligned"), (dict(chunks=[bp[0], 0]), "B_chunks[1]"),
-        (dict(flags=8), "flag"), (dict(flags=B.RAG_NO_COPY | B.RAG_COPY_ONLY), "exclude"),
+        (dict(flags=16), "flag"), (dict(flags=B.RAG_NO_COPY | B.RAG_COPY_ONLY), "exclude"),
         (dict(D=Ap), "overlap"), (dict(dt=5), "dtype"),
     ]
     for change, needle in bad:

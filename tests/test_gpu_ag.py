@@ -251,3 +251,58 @@ def test_ag_full_size_sampled_rows(name, engine):
     for r in range(shape.tp):
         src = W.bits_u8(inp.chunks[r]) if shape.dtype == "fp8" else W.bits_u16(inp.chunks[r])
         assert np.array_equal(Gb[r * shape.nc:(r + 1) * shape.nc], src)
+
+
+SPLIT_CASES = [(1, 0, 48), (2, 1, 256), (3, 2, 300), (4, 1, 256), (8, 5, 48)]
+
+
+@pytest.mark.parametrize("engine", ["kernel", "sdma"])
+@pytest.mark.parametrize("tp,s,nc", SPLIT_CASES)
+def test_ag_split_form_exact(tp, s, nc, engine):
+    """RAG_PER_CHUNK: one GEMM launch per chunk, gated by stream events; same result, bit for
+    bit, as the oracle on integer data, and G complete."""
+    c = ctx()
+    set_engine(c, engine)
+    inp = _int_case(tp, s, nc, K=192, M=144, seed=500 + tp * 10 + s)
+    say(f"case split tp={tp} s={s} nc={nc} engine={engine}")
+    run = AGRun(inp).run(c, flags=B.RAG_PER_CHUNK)
+    c.check()
+    G_ref, ref = oracle_ag(inp)
+    assert np.array_equal(W.bits_u16(run.G.cpu()), G_ref)
+    assert np.array_equal(run.D_bits(), O.f32_to_bf16(ref))
+
+
+def test_ag_split_form_flags_and_gating():
+    """Split form with staged output, copies only, G = NULL, and arrivals held back 2 ms on
+    NaN-poisoned slots (a GEMM launched before its chunk's event would read NaN)."""
+    c = ctx()
+    set_engine(c, "kernel")
+    inp = _int_case(4, 2, 256, K=256, M=256, seed=77)
+    _, ref = oracle_ag(inp)
+    want = O.f32_to_bf16(ref)
+    G_ref = O.gather([W.bits_u16(x) for x in inp.chunks])
+    run = AGRun(inp)
+    say("case split staged")
+    run.run(c, flags=B.RAG_PER_CHUNK | B.RAG_STAGED_OUT)
+    assert np.array_equal(run.D_bits(), want)
+    say("case split copy-only")
+    run.D.fill_(7.0)
+    run.G.zero_()
+    run.run(c, flags=B.RAG_PER_CHUNK | B.RAG_COPY_ONLY)
+    assert np.array_equal(W.bits_u16(run.G.cpu()), G_ref)
+    assert bool((run.D.float() == 7.0).all())
+    say("case split no-copy")
+    run.D.zero_()
+    run.run(c, flags=B.RAG_PER_CHUNK | B.RAG_NO_COPY)
+    assert np.array_equal(run.D_bits(), want)
+    say("case split G=NULL")
+    run2 = AGRun(inp, with_G=False).run(c, flags=B.RAG_PER_CHUNK)
+    assert np.array_equal(run2.D_bits(), want)
+    c.set_option(B.RAG_OPT_ARRIVAL_DELAY_US, 2000)
+    for it in range(2):
+        say(f"case split gating it={it}")
+        run.G.fill_(float("nan"))
+        run.D.fill_(float("nan"))
+        run.run(c, flags=B.RAG_PER_CHUNK)
+        assert np.array_equal(run.D_bits(), want)
+    c.check()
