@@ -302,3 +302,49 @@ def gemm_rs_rows(X_bits, W_bits, peer_partials, tp, self_rank, local_rows):
             np.asarray(peer_partials[p], dtype=np.float32)[self_rank * nc + rows]
         acc = (acc + part).astype(np.float32)
     return acc
+
+
+def rs_ring_order(self_rank: int, tp: int) -> List[int]:
+    """Chunks in the order one rank works on them in a ring reduce-scatter whose running sums go
+    to rank s+1 (the same direction as the all-gather ring: send to next, receive from prev).
+    Chunk c's sum starts at rank c+1 and travels c+1 -> c+2 -> ... -> c, so rank s holds it at
+    step k = (s - c - 1) mod tp: at step k it works on c_k = (s - 1 - k) mod tp, its own chunk
+    last.  [TE-2443] sequence diagram (split GEMM, then reduce-scatter);
+    [TE-1583] listing (ring neighbours)."""
+    return [(self_rank - 1 - k) % tp for k in range(tp)]
+
+
+def gemm_rs_ring_step(X_bits: np.ndarray, W_bits: np.ndarray,
+                      incoming: Sequence[np.ndarray], tp: int, self_rank: int):
+    """One rank's share of a ring-accumulate reduce-scatter.  P = X W^T over all T rows; for
+    every chunk c, out[c] = incoming[c] + P[rows of c] (one fp32 add), where incoming[c] is the
+    running sum of chunk c that arrives from rank s-1, and incoming[(s-1) mod tp] is None (that
+    chain starts here: out = P's rows).  The own chunk's out[s] is the reduced result.
+    Returns (D fp32 [nc, Mo] = out[s], send [tp, nc, Mo] with send[c] = out[c] for c != s, P).
+    [TE-2443] sequence diagram (reduce-scatter of the split GEMM's output); [NVF-5742]
+    walkthrough (each output chunk is a sum over ranks)."""
+    T = X_bits.shape[0]
+    if T % tp:
+        raise ValueError("T must be a multiple of tp")
+    nc = T // tp
+    P = local_partial(X_bits, W_bits)
+    start = (self_rank - 1) % tp
+    out = []
+    for c in range(tp):
+        mine = P[c * nc:(c + 1) * nc]
+        if c == start:
+            out.append(mine.copy())
+        else:
+            out.append((np.asarray(incoming[c], dtype=np.float32) + mine).astype(np.float32))
+    return out[self_rank], np.stack(out), P
+
+
+def gemm_rs_ring_step_rows(X_bits, W_bits, incoming, tp, self_rank, chunk, local_rows):
+    """Rows `local_rows` of out[chunk] of gemm_rs_ring_step, fp32 (sampled checks)."""
+    T = X_bits.shape[0]
+    nc = T // tp
+    rows = np.asarray(local_rows, dtype=np.int64)
+    mine = gemm_tn_rows(bf16_to_f32(X_bits), bf16_to_f32(W_bits), chunk * nc + rows)
+    if chunk == (self_rank - 1) % tp:
+        return mine
+    return (np.asarray(incoming[chunk], dtype=np.float32)[rows] + mine).astype(np.float32)

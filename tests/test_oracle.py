@@ -330,6 +330,95 @@ def test_rs_rows_matches_full_and_ignores_poison():
     assert np.array_equal(O.gemm_rs_rows(X, W, peers, tp, s, rows), D[rows])
 
 
+def test_rs_ring_order_fixture():
+    for case in _golden("rs_ring_orders.json")["cases"]:
+        assert O.rs_ring_order(case["self_rank"], case["tp"]) == case["order"]
+
+
+def _ring_incoming(P, tp, r, nc):
+    """Running sums arriving at rank r in a ring reduce-scatter that sends to rank+1, from the
+    plain definition: chunk c's sum at rank r is the sum of the partials of ranks c+1 .. r-1 (its
+    chain so far), integers so that the order of the adds does not matter."""
+    inc = []
+    for c in range(tp):
+        k = (r - c - 1) % tp
+        if k == 0:
+            inc.append(None)
+            continue
+        acc = np.zeros_like(P[0][:nc])
+        for i in range(1, k + 1):
+            q = (c + i) % tp
+            acc = acc + P[q][c * nc:(c + 1) * nc]
+        inc.append(acc.astype(np.float32))
+    return inc
+
+
+def _ring_pins_pass(step):
+    rng = np.random.default_rng(91)
+    for tp in (1, 2, 3, 4):
+        nc, Kl, Mo = 2, 12, 5
+        T = tp * nc
+        Xs = [rng.integers(-3, 4, (T, Kl)) for _ in range(tp)]
+        Ws = [rng.integers(-3, 4, (Mo, Kl)) for _ in range(tp)]
+        P = [_exact_gemm(Xs[r], Ws[r]).astype(np.float32) for r in range(tp)]
+        outs = []
+        try:
+            for r in range(tp):
+                D, send, _ = step(_bf16_bits(Xs[r]), _bf16_bits(Ws[r]),
+                                  _ring_incoming(P, tp, r, nc), tp, r)
+                outs.append((D, send))
+        except Exception:
+            return False
+        for r in range(tp):
+            D, send = outs[r]
+            want = sum(P[q][r * nc:(r + 1) * nc].astype(np.int64) for q in range(tp))
+            if not np.array_equal(D.astype(np.int64), want):
+                return False
+            nxt = _ring_incoming(P, tp, (r + 1) % tp, nc)
+            for c in range(tp):
+                if c != r and not np.array_equal(send[c], nxt[c]):
+                    return False
+    return True
+
+
+def test_rs_ring_simulation_equals_reduce_scatter():
+    """Every rank runs one ring step on the running sums its predecessor would hand it: each
+    owner's result is the sum of all ranks' partials of its chunk, and what a rank sends on is
+    exactly what its successor receives."""
+    assert _ring_pins_pass(O.gemm_rs_ring_step)
+
+    def wrong_start(X, W, inc, tp, s):
+        inc = list(inc)
+        inc[(s - 1) % tp], inc[(s + 1) % tp] = inc[(s + 1) % tp], inc[(s - 1) % tp]
+        return O.gemm_rs_ring_step(X, W, inc, tp, s)
+
+    def dropped_incoming(X, W, inc, tp, s):
+        return O.gemm_rs_ring_step(X, W, [None if i is None else 0 * i for i in inc], tp, s)
+
+    def wrong_rows(X, W, inc, tp, s):
+        D, send, P = O.gemm_rs_ring_step(X, W, inc, tp, s)
+        return D, np.roll(send, 1, axis=0), P
+
+    assert not _ring_pins_pass(wrong_start)
+    assert not _ring_pins_pass(dropped_incoming)
+    assert not _ring_pins_pass(wrong_rows)
+
+
+def test_rs_ring_rows_matches_full():
+    rng = np.random.default_rng(93)
+    tp, s, nc, Kl, Mo = 4, 1, 5, 16, 7
+    T = tp * nc
+    X = _bf16_bits(rng.standard_normal((T, Kl)))
+    W = _bf16_bits(rng.standard_normal((Mo, Kl)))
+    inc = [None if c == (s - 1) % tp else rng.standard_normal((nc, Mo)).astype(np.float32)
+           for c in range(tp)]
+    D, send, _ = O.gemm_rs_ring_step(X, W, inc, tp, s)
+    rows = [0, 4, 2]
+    for c in range(tp):
+        assert np.array_equal(O.gemm_rs_ring_step_rows(X, W, inc, tp, s, c, rows), send[c][rows])
+    assert np.array_equal(send[s], D)
+
+
 # ------------------------------------------------------------------------------------ mutants
 
 def _pins_pass(gemm, gather, order_fn):
