@@ -276,6 +276,29 @@ def main():
                          "kernel": kname, "kernel_ms": round(kernel_ms, 5),
                          "algorithmic_bytes": alg_bytes},
         }
+        # the counter-gated forms: the peers' partials arrive during the call (side-stream copies in
+        # ring order, tiles wait before their epilogue), and one ring-accumulate step with its
+        # incoming running sums given or arriving
+        ms_arrive, _ = time_steps(lambda: B.gemm_rs(ctx, X, Wt, parts, shape.tp, shape.self_rank, D,
+                                                    send=send, flags=B.RAG_RS_ARRIVE),
+                                  args.steps, args.warmup, stream)
+        rin = W.make_rs_ring(shape)
+        inc = [t.to(dev) for t in rin.incoming]
+        Xr, Wr = rin.X.to(dev), rin.W.to(dev)
+        ms_ring, _ = time_steps(lambda: B.gemm_rs_ring(ctx, Xr, Wr, inc, shape.tp, shape.self_rank,
+                                                       D, send=send),
+                                args.steps, args.warmup, stream)
+        ms_ring_arrive, _ = time_steps(
+            lambda: B.gemm_rs_ring(ctx, Xr, Wr, inc, shape.tp, shape.self_rank, D, send=send,
+                                   flags=B.RAG_RS_ARRIVE), args.steps, args.warmup, stream)
+        ctx.check()
+        out["variants_ms_per_step"] = {
+            "one_shot_partials_given": round(ms, 5),
+            "one_shot_partials_arrive": round(ms_arrive, 5),
+            "ring_step_sums_given": round(ms_ring, 5),
+            "ring_step_sums_arrive": round(ms_ring_arrive, 5),
+            "arrival_engine": "kernel" if args.copy_engine != "sdma" else "sdma",
+            "comm_wgs": args.comm_wgs}
         if not args.no_cpu:
             out["cpu_baseline"] = cpu_baseline_rs(inp, args.cpu_seconds)
     ctx.close()

@@ -75,7 +75,7 @@ typedef enum {
     RAG_FP8_E4M3 = 1    /* OCP FP8 E4M3 (no infinities, max 448) with one fp32 scale per tensor */
 } rag_dtype;
 
-/* Flags for ag_gemm / gemm_rs (bitwise or). */
+/* Flags for ag_gemm, gemm_rs and gemm_rs_ring (bitwise or). */
 enum {
     RAG_STAGED_OUT = 1, /* AG+GEMM: write the output through a library-owned buffer of tp+1 chunks
                            in consumption order and copy it to D afterwards (the listing's output
@@ -83,13 +83,20 @@ enum {
     RAG_NO_COPY = 2,    /* AG+GEMM: no arrivals; every chunk counts as ready and is read from its
                            slot of G as it is (GEMM-only timing; G must already hold the chunks) */
     RAG_COPY_ONLY = 4,  /* AG+GEMM: arrivals (copies + counter bumps) only, no GEMM */
-    RAG_PER_CHUNK = 8   /* AG+GEMM, split form: one GEMM launch per chunk in ring order on `stream`,
+    RAG_PER_CHUNK = 8,  /* AG+GEMM, split form: one GEMM launch per chunk in ring order on `stream`,
                            each waiting for its chunk's copy through a stream event instead of an
                            in-kernel counter (TransformerEngine PR #2443, sequence diagram: the
                            split overlap path; nvFuser PR #3392, experiment: one GEMM per received
                            chunk).  The copies always run on the side stream (the copy kernel, or
                            SDMA with RAG_COPY_SDMA); the per-tile trace is not recorded and the
                            withhold hook does not apply */
+    RAG_RS_ARRIVE = 16  /* gemm_rs, gemm_rs_ring: the peers' data for this rank (gemm_rs: their
+                           partials of the own chunk; gemm_rs_ring: the incoming running sums)
+                           arrives during the call: the side stream copies it in ring order into a
+                           library receive buffer, each copy releasing a counter, and a tile waits
+                           for the counters of what its epilogue reads after its K loop (the
+                           "atomic" reduce-scatter).  Needs the row stride equal to Mo.  Copies run
+                           on the copy kernel, or on SDMA with RAG_COPY_SDMA */
 };
 
 /* Copy engines of the simulated arrival (RAG_OPT_COPY_ENGINE). */
@@ -203,12 +210,16 @@ RAG_API int ag_gemm(rag_ctx* ctx,
  *
  *   X         [T, Kl] bf16 activation shard; T = tp * nc
  *   W         [Mo, Kl] bf16 weight shard
- *   Kl        >= 1, multiple of 64;  Mo >= 1
+ *   Kl        >= 1, multiple of 64;  Mo >= 4, multiple of 4
  *   partials  HOST array of tp device pointers to fp32 [T, Mo] partials with row stride ldp
- *             (elements, >= Mo); only rows of chunk self_rank are read; entry self_rank ignored
+ *             (elements, >= Mo, 4-byte aligned); only rows of chunk self_rank are read; entry
+ *             self_rank ignored
  *   send      [tp, nc, Mo] fp32 outgoing chunks (slot self_rank untouched); NULL = not stored
  *   D         [nc, Mo] bf16, this rank's reduced chunk
- * Errors: RAG_EINVAL, RAG_EHIP.
+ *   flags     0 or RAG_RS_ARRIVE
+ * Row chunks are computed in the order c_j = (self_rank + 1 + j) mod tp, the own chunk last.
+ * Errors: RAG_EINVAL, RAG_EHIP; with RAG_RS_ARRIVE, rag_check reports RAG_ETIMEOUT for a copy
+ * that never completes.
  */
 RAG_API int gemm_rs(rag_ctx* ctx,
             const void* X, int T, int Kl,
@@ -233,6 +244,31 @@ RAG_API int rag_kernel_times(rag_ctx* ctx, float* out, int max_n);
  * kernel a measurement ran. */
 RAG_API int rag_ag_kernel_name(rag_ctx* ctx, int nc, int M, int tp, rag_dtype dt, char* buf,
                                int len);
+
+/*
+ * One rank's step of a ring-accumulate reduce-scatter (the running sums go to rank self_rank+1):
+ *     P       = X * W^T over all T rows
+ *     send[c] = incoming[c] + P[rows of chunk c]   for c != self_rank    (fp32, passed on)
+ *     D       = incoming[self_rank] + P[rows of chunk self_rank]        (bf16, the reduced chunk)
+ * where incoming[c] is the running sum of chunk c that arrives from rank self_rank-1, and the
+ * chain of chunk (self_rank-1) mod tp starts here (no incoming: send = P's rows).  Chunks are
+ * computed in the ring order c_k = (self_rank - 1 - k) mod tp, the own chunk last.
+ * TransformerEngine PR #2443 (sequence diagram: split GEMM then reduce-scatter);
+ * nvFuser PR #5742 (walkthrough: each output chunk is summed over ranks).
+ *
+ *   X, W, Kl, Mo, send, D as for gemm_rs (send NULL = the passed-on sums are not stored)
+ *   incoming  HOST array of tp device pointers to fp32 [nc, Mo] running sums with row stride ldi
+ *             (elements, >= Mo, 4-byte aligned); entry (self_rank - 1) mod tp ignored
+ *   flags     0 or RAG_RS_ARRIVE
+ * Errors: RAG_EINVAL, RAG_EHIP (RAG_ETIMEOUT through rag_check as for gemm_rs).
+ */
+RAG_API int gemm_rs_ring(rag_ctx* ctx,
+            const void* X, int T, int Kl,
+            const void* W, int Mo,
+            const float* const* incoming, long long ldi,
+            int tp, int self_rank,
+            float* send, void* D,
+            int flags, void* stream);
 
 /* Name of the GPU kernel entry point gemm_rs would launch for these sizes (nc rows per chunk, Mo
  * output columns, tp chunks) with the context's current options (e.g. "rag_rs_t256x256w8").

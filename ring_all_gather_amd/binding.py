@@ -27,7 +27,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "ringag.h")
 # constants of include/ringag.h
 RAG_OK, RAG_EINVAL, RAG_EHIP, RAG_ETIMEOUT, RAG_ENOMEM = 0, -1, -2, -3, -4
 RAG_BF16, RAG_FP8_E4M3 = 0, 1
-RAG_STAGED_OUT, RAG_NO_COPY, RAG_COPY_ONLY, RAG_PER_CHUNK = 1, 2, 4, 8
+RAG_STAGED_OUT, RAG_NO_COPY, RAG_COPY_ONLY, RAG_PER_CHUNK, RAG_RS_ARRIVE = 1, 2, 4, 8, 16
 RAG_OPT_COPY_ENGINE, RAG_OPT_COMM_WGS, RAG_OPT_SPIN_LIMIT_US = 1, 2, 3
 RAG_OPT_ARRIVAL_DELAY_US, RAG_OPT_WITHHOLD_MASK, RAG_OPT_TIMING, RAG_OPT_TILE = 4, 5, 6, 7
 RAG_OPT_TRACE_BUF, RAG_OPT_TRACE_BYTES, RAG_OPT_WGS_PER_CU, RAG_OPT_COPY_PRIORITY = 8, 9, 10, 11
@@ -73,13 +73,15 @@ def lib():
     L.rag_set_option.argtypes = [vp, i, ll]
     L.ag_gemm.argtypes = [vp, vp, i, i, ctypes.POINTER(vp), i, i, i, vp, vp, i, vp, vp, i, vp]
     L.gemm_rs.argtypes = [vp, vp, i, i, vp, i, ctypes.POINTER(vp), ll, i, i, vp, vp, i, vp]
+    L.gemm_rs_ring.argtypes = [vp, vp, i, i, vp, i, ctypes.POINTER(vp), ll, i, i, vp, vp, i, vp]
     L.rag_check.argtypes = [vp]
     L.rag_kernel_times.argtypes = [vp, ctypes.POINTER(ctypes.c_float), i]
     L.rag_ag_kernel_name.argtypes = [vp, i, i, i, i, ctypes.c_char_p, i]
     L.rag_rs_kernel_name.argtypes = [vp, i, i, i, ctypes.c_char_p, i]
     L.rag_last_error.restype = ctypes.c_char_p
     L.rag_version.restype = i
-    for f in ("rag_create", "rag_destroy", "rag_set_option", "ag_gemm", "gemm_rs", "rag_check",
+    for f in ("rag_create", "rag_destroy", "rag_set_option", "ag_gemm", "gemm_rs", "gemm_rs_ring",
+              "rag_check",
               "rag_kernel_times", "rag_ag_kernel_name", "rag_rs_kernel_name"):
         getattr(L, f).restype = i
     _lib = L
@@ -225,36 +227,55 @@ def ag_gemm(ctx: Context, A: torch.Tensor, B_chunks: Sequence[torch.Tensor], tp:
                                 flags, _stream(stream)))
 
 
-def gemm_rs(ctx: Context, X: torch.Tensor, W: torch.Tensor,
-            partials: Sequence[Optional[torch.Tensor]], tp: int, self_rank: int,
-            D: torch.Tensor, send: Optional[torch.Tensor] = None, stream=None) -> int:
-    """D = sum over ranks of the rows of chunk self_rank of X W^T (peers' partials given)."""
+def _rs(fn, ctx: Context, X: torch.Tensor, W: torch.Tensor, entries, rows: int, skip: int,
+        tp: int, self_rank: int, D: torch.Tensor, send, flags: int, stream) -> int:
     T, Kl = X.shape
     Mo = W.shape[0]
     if X.dtype != torch.bfloat16 or W.dtype != torch.bfloat16 or W.shape[1] != Kl:
         raise ValueError("X [T, Kl] and W [Mo, Kl] must be bfloat16")
-    if len(partials) != tp:
-        raise ValueError(f"need tp={tp} partial entries (entry self_rank may be None)")
+    if len(entries) != tp:
+        raise ValueError(f"need tp={tp} entries (the ignored one may be None)")
     nc = T // tp
     if D.dtype != torch.bfloat16 or tuple(D.shape) != (nc, Mo):
         raise ValueError(f"D must be bfloat16 [{nc}, {Mo}]")
     if send is not None and (send.dtype != torch.float32 or tuple(send.shape) != (tp, nc, Mo)):
         raise ValueError(f"send must be float32 [{tp}, {nc}, {Mo}]")
-    ldp = Mo
+    ld = None
     arr = []
-    for p, t in enumerate(partials):
-        if p == self_rank or t is None:
+    for i, t in enumerate(entries):
+        if i == skip or t is None:
             arr.append(None)
             continue
-        if t.dtype != torch.float32 or t.dim() != 2 or t.shape[0] != T or t.shape[1] < Mo \
+        if t.dtype != torch.float32 or t.dim() != 2 or t.shape[0] != rows or t.shape[1] < Mo \
                 or t.stride(1) != 1 or not t.is_cuda:
-            raise ValueError("each peer partial must be a float32 GPU tensor [T, >=Mo], unit "
+            raise ValueError(f"each entry must be a float32 GPU tensor [{rows}, >={Mo}], unit "
                              "column stride")
-        ldp = t.stride(0)
+        if ld is not None and t.stride(0) != ld:
+            raise ValueError("all entries must share one row stride")
+        ld = t.stride(0)
         arr.append(ctypes.c_void_p(t.data_ptr()))
-    for p, t in enumerate(partials):
-        if p != self_rank and t is not None and t.stride(0) != ldp:
-            raise ValueError("all peer partials must share one row stride")
     ptrs = (ctypes.c_void_p * tp)(*arr)
-    return _check(lib().gemm_rs(ctx.h, _ptr(X), T, Kl, _ptr(W), Mo, ptrs, ldp, tp, self_rank,
-                                _ptr(send), _ptr(D), 0, _stream(stream)))
+    return _check(fn(ctx.h, _ptr(X), T, Kl, _ptr(W), Mo, ptrs, Mo if ld is None else ld, tp,
+                     self_rank, _ptr(send), _ptr(D), flags, _stream(stream)))
+
+
+def gemm_rs(ctx: Context, X: torch.Tensor, W: torch.Tensor,
+            partials: Sequence[Optional[torch.Tensor]], tp: int, self_rank: int,
+            D: torch.Tensor, send: Optional[torch.Tensor] = None, flags: int = 0,
+            stream=None) -> int:
+    """D = sum over ranks of the rows of chunk self_rank of X W^T (peers' [T, Mo] partials given;
+    entry self_rank ignored); send[c] = this rank's rows of chunk c."""
+    return _rs(lib().gemm_rs, ctx, X, W, partials, X.shape[0], self_rank, tp, self_rank, D, send,
+               flags, stream)
+
+
+def gemm_rs_ring(ctx: Context, X: torch.Tensor, W: torch.Tensor,
+                 incoming: Sequence[Optional[torch.Tensor]], tp: int, self_rank: int,
+                 D: torch.Tensor, send: Optional[torch.Tensor] = None, flags: int = 0,
+                 stream=None) -> int:
+    """One ring-accumulate reduce-scatter step: send[c] = incoming[c] + this rank's rows of chunk
+    c, D = incoming[self_rank] + its own rows (incoming [nc, Mo] running sums by chunk; the entry
+    of the chain that starts here, (self_rank - 1) mod tp, is ignored)."""
+    nc = X.shape[0] // tp
+    return _rs(lib().gemm_rs_ring, ctx, X, W, incoming, nc, (self_rank - 1) % tp, tp, self_rank,
+               D, send, flags, stream)

@@ -19,6 +19,33 @@ namespace ringag {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
+// Wait until *ctr == epoch.  Returns false when the limit passed or another tile of this call
+// already gave up (then *err == epoch).  The loop polls with relaxed agent-scope loads, which
+// read the counter coherently without touching the caches; a single acquire fence after the
+// value is seen orders the tile's loads of the chunk after the producer's release.  (An acquire
+// load in the loop would invalidate this CU's cache lines on every poll, slowing the tiles and the
+// copies that share the XCD.)
+__device__ inline bool wait_ready(int* ctr, int epoch, int* err, long long limit) {
+  bool ok = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
+  if (!ok) {
+    const unsigned long long t0 = wall_clock64();
+    while (true) {
+      __builtin_amdgcn_s_sleep(8);
+      if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch) {
+        ok = true;
+        break;
+      }
+      if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch) break;
+      if ((long long)(wall_clock64() - t0) > limit) {
+        __hip_atomic_store(err, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+  }
+  if (ok) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return ok;
+}
+
 // Copy piece k of copy c with the NT threads of the workgroup (16-byte vectors, 8 in flight per
 // thread).
 template <int NT>

@@ -5,18 +5,21 @@
 // global k.  nvFuser PR #5742, walkthrough: each chunk of the output is summed over ranks.
 //
 // The rank computes its whole partial P = X W^T, chunk by chunk in ring order (the rank's own
-// chunk last, as in a ring reduce-scatter where the own chunk's sum completes last).  Tiles of
-// another rank's chunk store their fp32 accumulators to `send` (the outgoing contribution).
-// Tiles of the own chunk add the peers' fp32 partials to their accumulators and store the bf16
-// result, so the reduction costs no extra pass over D.
+// chunk last).  One-shot form: tiles of another rank's chunk store their fp32 accumulators to
+// `send` (the outgoing contribution); tiles of the own chunk add the peers' fp32 partials of it
+// and store the bf16 result.  Ring-accumulate form: the tiles of chunk c add the running sum of c
+// that arrives from the previous rank (none for the chunk whose chain starts here) and store the
+// result to send, or, for the own chunk, to D.  When that data arrives during the call (gated),
+// a tile runs its K loop first and waits for the counters only before its epilogue reads it.
 //
 // Epilogue: the accumulators are staged through LDS one wave row (TM rows of the tile) at a time,
-// then every thread moves whole 16-byte vectors along tile rows: send is written, and the peers'
-// partials are read, in full contiguous rows rather than in the MFMA layout's 4-byte scatter.
-// For the own chunk each thread holds a batch of vectors and issues the loads of one peer for the
-// whole batch before adding them, so a batch's loads are in flight together.
+// then every thread moves whole 16-byte vectors along tile rows: send is written, and partials
+// are read, in full contiguous rows rather than in the MFMA layout's 4-byte scatter.  A thread
+// holds a batch of vectors and issues one peer's loads for the whole batch before adding them,
+// so a batch's loads are in flight together.
 #pragma once
 
+#include "copy_queue.hpp"
 #include "gemm_core.hpp"
 #include "kernels.hpp"
 
@@ -45,7 +48,6 @@ __device__ inline void rs_epilogue(const f32x16 (&acc)[S::FI][S::FJ], char* lds,
   using E = RsEpilogue<S>;
   const int wi = wave / S::WJ, wj = wave % S::WJ;
   const int col0 = cb * S::BJ;
-  const size_t prow0 = (size_t)a.self_rank * a.nc;
   for (int slab = 0; slab < S::WI; ++slab) {
     if (wi == slab) {
 #pragma unroll
@@ -60,7 +62,11 @@ __device__ inline void rs_epilogue(const f32x16 (&acc)[S::FI][S::FJ], char* lds,
     }
     __syncthreads();
     const int row0 = rb * S::BI + slab * S::TM;   // chunk-local row of the staged row 0
-    if (!own) {
+    // what the staged rows get added to: every peer's partial (own chunk, one-shot), one
+    // incoming running sum (ring step), or nothing (another chunk, one-shot)
+    const int nadd = a.ring ? (a.partial[c] != nullptr ? 1 : 0) : (own ? a.tp - 1 : 0);
+    const bool to_d = own;
+    if (nadd == 0 && !to_d) {
       float* out = a.send + (size_t)c * a.nc * a.Mo;
 #pragma unroll
       for (int k = 0; k < E::VPT; ++k) {
@@ -71,7 +77,6 @@ __device__ inline void rs_epilogue(const f32x16 (&acc)[S::FI][S::FJ], char* lds,
           *(f32x4*)(out + (size_t)row * a.Mo + col) = *(const f32x4*)(lds + r * E::LD + v * 16);
       }
     } else {
-      __bf16* out = (__bf16*)a.D;
       for (int b = 0; b < E::VPT; b += E::BATCH) {
         f32x4 x[E::BATCH];
         int row[E::BATCH], col[E::BATCH];
@@ -85,9 +90,10 @@ __device__ inline void rs_epilogue(const f32x16 (&acc)[S::FI][S::FJ], char* lds,
           ok[q] = row[q] < a.nc && col[q] < a.Mo;
           x[q] = *(const f32x4*)(lds + r * E::LD + v * 16);
         }
-        for (int p = 0; p < a.tp; ++p) {
-          if (p == a.self_rank) continue;
-          const float* part = a.partial[p] + prow0 * (size_t)a.ldp;
+        for (int i = 0; i < nadd; ++i) {
+          // one-shot: the i-th peer in increasing rank, skipping this rank; ring: chunk c's sum
+          const int p = a.ring ? c : (i < a.self_rank ? i : i + 1);
+          const float* part = a.partial[p];
           f32x4 y[E::BATCH];
 #pragma unroll
           for (int q = 0; q < E::BATCH; ++q) {
@@ -99,11 +105,19 @@ __device__ inline void rs_epilogue(const f32x16 (&acc)[S::FI][S::FJ], char* lds,
 #pragma unroll
           for (int q = 0; q < E::BATCH; ++q) x[q] += y[q];
         }
+        if (to_d) {
+          __bf16* out = (__bf16*)a.D;
 #pragma unroll
-        for (int q = 0; q < E::BATCH; ++q)
-          if (ok[q])
-            *(bf16x4*)(out + (size_t)row[q] * a.Mo + col[q]) =
-                bf16x4{(__bf16)x[q][0], (__bf16)x[q][1], (__bf16)x[q][2], (__bf16)x[q][3]};
+          for (int q = 0; q < E::BATCH; ++q)
+            if (ok[q])
+              *(bf16x4*)(out + (size_t)row[q] * a.Mo + col[q]) =
+                  bf16x4{(__bf16)x[q][0], (__bf16)x[q][1], (__bf16)x[q][2], (__bf16)x[q][3]};
+        } else {
+          float* out = a.send + (size_t)c * a.nc * a.Mo;
+#pragma unroll
+          for (int q = 0; q < E::BATCH; ++q)
+            if (ok[q]) *(f32x4*)(out + (size_t)row[q] * a.Mo + col[q]) = x[q];
+        }
       }
     }
     __syncthreads();
@@ -121,6 +135,7 @@ __device__ __forceinline__ void gemm_rs_body(const RsArgs& a) {
   const int total = U * a.tp;
   const i32x4 ry = make_rsrc(a.W, (uint32_t)a.Mo * ldb);
   const int grid = (int)gridDim.x;
+  __shared__ int s_ok;
 
   for (int r0 = 0; r0 < total; r0 += grid) {
     const int t = round_tile(r0, min(grid, total - r0), grid);
@@ -138,6 +153,25 @@ __device__ __forceinline__ void gemm_rs_body(const RsArgs& a) {
     tile_offsets<S, S::YQ>(yo, cb * S::BJ, a.Mo, ldb, wave, lane);
     f32x16 acc[S::FI][S::FJ];
     tile_kloop<S, false>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);
+    // gated: wait for what the epilogue reads (the K loop did not need it)
+    const bool waits = a.gated && (a.ring ? a.partial[c] != nullptr : own);
+    if (waits) {
+      if (threadIdx.x == 0) {
+        bool ok = true;
+        if (a.ring) {
+          ok = wait_ready(a.ctr + c * kWordStride, a.epoch, a.err, a.spin_limit);
+        } else {
+          for (int p = 0; p < a.tp && ok; ++p)
+            if (p != a.self_rank)
+              ok = wait_ready(a.ctr + p * kWordStride, a.epoch, a.err, a.spin_limit);
+        }
+        s_ok = ok;
+      }
+      __syncthreads();
+      const int ok = __builtin_amdgcn_readfirstlane(s_ok);   // uniform: see run_copy_queue
+      __syncthreads();
+      if (!ok) continue;
+    }
     rs_epilogue<S>(acc, lds, a, c, own, rb, cb, wave, lane);
   }
 }

@@ -73,18 +73,31 @@ struct AgArgs {
 };
 
 // Arguments of the GEMM+RS kernel.  Row-chunk positions j = 0..tp-1 in visiting order; the last
-// one is this rank's own chunk, whose tiles are reduced with the peers' partials.
+// one is this rank's own chunk.  Two forms: the one-shot reduce-scatter (ring = 0: tiles of other
+// chunks store their fp32 accumulators to send, the own chunk's tiles add every peer's partial of
+// the own chunk) and one ring-accumulate step (ring = 1: the tiles of chunk c add the running sum
+// of chunk c that arrives from the previous rank, then store to send, or to D for the own chunk).
 struct RsArgs {
   const void* X;                 // [T, Kl] bf16
   const void* W;                 // [Mo, Kl] bf16
   int chunk_of[kMaxTp];          // by position: row chunk index c
-  const float* partial[kMaxTp];  // by rank: peers' fp32 partials (row stride ldp); self unused
+  const float* partial[kMaxTp];  // ring = 0: by rank p, p's partial rows of the own chunk;
+                                 // ring = 1: by chunk c, the incoming running sum (or null);
+                                 // [nc, Mo] fp32 with row stride ldp
   long long ldp;
+  int ring;
   float* send;                   // [tp, nc, Mo] fp32 or null
   void* D;                       // [nc, Mo] bf16
   int T, Kl, Mo, nc, tp, self_rank;
   int tiles_i, tiles_j;
   int partial_vec;               // 1 = every partial and ldp allow 16-byte loads
+  int gated;                     // 1 = the data of partial[] arrives during the call: a tile waits
+                                 // for the counters of what its epilogue reads (ctr, by rank for
+                                 // ring = 0, by chunk for ring = 1)
+  int* ctr;
+  int epoch;
+  int* err;
+  long long spin_limit;
 };
 
 // Arguments of the arrival (producer) kernel on the side stream: runs the whole piece queue.

@@ -77,6 +77,8 @@ struct rag_ctx {
   size_t gbuf_bytes = 0;
   void* stage = nullptr;
   size_t stage_bytes = 0;
+  void* rsbuf = nullptr;        // receive buffer of the reduce-scatter's arrivals
+  size_t rsbuf_bytes = 0;
   int num_cus = 0;
   long long wall_khz = 100000;
   // options
@@ -162,13 +164,18 @@ const char* engine_name(int e) {
   return e == RAG_COPY_SDMA ? "sdma" : e == RAG_COPY_IN_GEMM ? "in-gemm" : "kernel";
 }
 
-// Compute units kept free of GEMM workgroups while arrivals run.  The 4-wave 256x256 tile uses
-// every vector register of its SIMDs (512 per lane), so no wave of the copy kernel could share a
-// CU with it; with one such workgroup per CU (its LDS allows no second), leaving 8 CUs without one
-// guarantees the copy kernel a place to run while GEMM tiles wait for its chunks.  Every other
-// tile leaves at least 64 registers per SIMD lane free, enough for the copy kernel's waves.
-int reserved_cus(int tile, bool arrivals) {
-  return (arrivals && tile == kTile256x256) ? 8 : 0;
+// Compute units kept free of GEMM workgroups while a copy kernel runs beside it on the side
+// stream.  A GEMM workgroup whose tiles wait for the copies must never fill every compute unit so
+// completely that no copy wave can be placed: then, if the GEMM's persistent grid is dispatched
+// first, its waiting tiles spin until the limit while the copies cannot start.  The copy kernel
+// needs at most 64 VGPRs per lane and a few bytes of LDS; a GEMM that leaves less than that on a
+// SIMD (its resident waves times their registers, of the 512 per lane) gets 8 compute units, one
+// per XCD, left out of its grid.
+int reserved_cus(const KernelInfo& g, bool copies_beside) {
+  if (!copies_beside) return 0;
+  const int waves_per_simd = std::max(1, g.max_blocks_per_cu * (g.threads / 64) / 4);
+  const int regs = (g.vgprs_per_wave + 7) / 8 * 8;
+  return waves_per_simd * regs > 512 - 64 ? 8 : 0;
 }
 
 int choose_rs_tile(const rag_ctx* c, int nc, int Mo, int tp) {
@@ -201,147 +208,7 @@ int record_timing_stop(rag_ctx* c, hipStream_t s, bool recorded) {
 
 }  // namespace
 
-extern "C" {
-
-int rag_version(void) { return 100; }
-
-const char* rag_last_error(void) { return g_last_error; }
-
-int rag_create(rag_ctx** out, int device, int max_tp, int flags) {
-  if (!out) return fail(RAG_EINVAL, "rag_create: out is NULL");
-  *out = nullptr;
-  if (max_tp < 1 || max_tp > RAG_MAX_TP)
-    return fail(RAG_EINVAL, "rag_create: max_tp=%d outside [1, %d]", max_tp, RAG_MAX_TP);
-  if (flags != 0) return fail(RAG_EINVAL, "rag_create: flags must be 0 (got %d)", flags);
-  int ndev = 0;
-  HIPCHK(hipGetDeviceCount(&ndev));
-  if (device < 0 || device >= ndev)
-    return fail(RAG_EINVAL, "rag_create: device %d outside [0, %d)", device, ndev);
-  HIPCHK(hipSetDevice(device));
-  hipDeviceProp_t prop;
-  HIPCHK(hipGetDeviceProperties(&prop, device));
-  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
-    return fail(RAG_EINVAL, "rag_create: device %d is %s; this library is built for gfx950",
-                device, prop.gcnArchName);
-  rag_ctx* c = new rag_ctx();
-  c->device = device;
-  c->max_tp = max_tp;
-  c->num_cus = prop.multiProcessorCount;
-  int khz = 0;
-  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, device) == hipSuccess && khz > 0)
-    c->wall_khz = khz;
-  const size_t nwords = ((size_t)max_tp + 1 + 4 * (size_t)kArrSlots + 1) * kWordStride;
-  hipError_t e = load_kernels(device);
-  if (e != hipSuccess) {
-    delete c;
-    return fail(RAG_EHIP, "rag_create: loading the gfx950 kernels on device %d failed: %s", device,
-                hipGetErrorString(e));
-  }
-  e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming);
-  if (e == hipSuccess) e = hipMalloc((void**)&c->words, nwords * sizeof(int));
-  if (e == hipSuccess) e = hipMemset(c->words, 0, nwords * sizeof(int));
-  if (e == hipSuccess) e = hipDeviceSynchronize();
-  if (e != hipSuccess) {
-    std::string msg = std::string("rag_create: ") + hipGetErrorString(e);
-    rag_destroy(c);
-    return fail(RAG_EHIP, "%s", msg.c_str());
-  }
-  c->ctr = c->words;
-  c->arr = reinterpret_cast<unsigned*>(c->words + (size_t)(max_tp + 1) * kWordStride);
-  c->err = c->words + (size_t)(max_tp + 1 + 4 * kArrSlots) * kWordStride;
-  *out = c;
-  if (debug_enabled())
-    fprintf(stderr, "[ringag] context on device %d (%s, %d CUs, wall clock %lld kHz), max_tp %d\n",
-            device, prop.gcnArchName, c->num_cus, c->wall_khz, max_tp);
-  return RAG_OK;
-}
-
-int rag_destroy(rag_ctx* c) {
-  if (!c) return RAG_OK;
-  (void)hipSetDevice(c->device);
-  if (c->side) (void)hipStreamSynchronize(c->side);
-  for (auto ev : c->t_start) (void)hipEventDestroy(ev);
-  for (auto ev : c->t_stop) (void)hipEventDestroy(ev);
-  for (auto ev : c->ev_chunk) (void)hipEventDestroy(ev);
-  if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
-  if (c->ev_join) (void)hipEventDestroy(c->ev_join);
-  if (c->side) (void)hipStreamDestroy(c->side);
-  if (c->words) (void)hipFree(c->words);
-  if (c->gbuf) (void)hipFree(c->gbuf);
-  if (c->stage) (void)hipFree(c->stage);
-  delete c;
-  return RAG_OK;
-}
-
-int rag_set_option(rag_ctx* c, int key, long long v) {
-  if (!c) return fail(RAG_EINVAL, "rag_set_option: ctx is NULL");
-  switch (key) {
-    case RAG_OPT_COPY_ENGINE:
-      if (v != RAG_COPY_KERNEL && v != RAG_COPY_SDMA && v != RAG_COPY_IN_GEMM)
-        return fail(RAG_EINVAL, "copy engine must be 0 (kernel), 1 (sdma) or 2 (in the GEMM)");
-      c->copy_engine = (int)v;
-      return RAG_OK;
-    case RAG_OPT_COMM_WGS:
-      if (v < 1 || v > 1024) return fail(RAG_EINVAL, "comm workgroups must be in [1, 1024]");
-      c->comm_wgs = (int)v;
-      return RAG_OK;
-    case RAG_OPT_SPIN_LIMIT_US:
-      if (v < 1 || v > 60000000LL) return fail(RAG_EINVAL, "spin limit must be in [1, 6e7] us");
-      c->spin_us = v;
-      return RAG_OK;
-    case RAG_OPT_ARRIVAL_DELAY_US:
-      if (v < 0 || v > 1000000LL) return fail(RAG_EINVAL, "arrival delay must be in [0, 1e6] us");
-      c->delay_us = v;
-      return RAG_OK;
-    case RAG_OPT_WITHHOLD_MASK:
-      if (v < 0 || v > 0xffffLL) return fail(RAG_EINVAL, "withhold mask must fit in 16 bits");
-      c->withhold = (unsigned)v;
-      return RAG_OK;
-    case RAG_OPT_TIMING:
-      if (v != 0 && v != 1) return fail(RAG_EINVAL, "timing must be 0 or 1");
-      if (v && c->t_start.empty()) {
-        HIPCHK(hipSetDevice(c->device));
-        c->t_start.resize(kTimingSlots);
-        c->t_stop.resize(kTimingSlots);
-        for (int i = 0; i < kTimingSlots; ++i) {
-          HIPCHK(hipEventCreate(&c->t_start[i]));
-          HIPCHK(hipEventCreate(&c->t_stop[i]));
-        }
-      }
-      c->timing = v != 0;
-      return RAG_OK;
-    case RAG_OPT_WGS_PER_CU:
-      if (v < 0 || v > 16) return fail(RAG_EINVAL, "workgroups per CU must be in [0, 16]");
-      c->wgs_per_cu = (int)v;
-      return RAG_OK;
-    case RAG_OPT_GEMM_COPY_WGS:
-      if (v < 0 || v > 65536) return fail(RAG_EINVAL, "GEMM copy workgroups must be in [0, 65536]");
-      c->gemm_copy_wgs = (int)v;
-      return RAG_OK;
-    case RAG_OPT_COPY_PRIORITY:
-      if (v != 0 && v != 1) return fail(RAG_EINVAL, "copy priority must be 0 or 1");
-      c->copy_priority = (int)v;
-      return RAG_OK;
-    case RAG_OPT_TRACE_BUF:
-      if (v != 0 && (v & 7)) return fail(RAG_EINVAL, "trace buffer must be 8-byte aligned");
-      if (v != 0 && !on_device(reinterpret_cast<const void*>(v), c->device))
-        return fail(RAG_EINVAL, "trace buffer is not device memory of device %d", c->device);
-      c->trace_buf = (unsigned long long)v;
-      return RAG_OK;
-    case RAG_OPT_TRACE_BYTES:
-      if (v < 0) return fail(RAG_EINVAL, "trace size must be >= 0");
-      c->trace_bytes = v;
-      return RAG_OK;
-    case RAG_OPT_TILE:
-      if (v < RAG_TILE_AUTO || v > RAG_TILE_256x256_8W_S4) return fail(RAG_EINVAL, "unknown tile %lld", v);
-      c->tile = (int)v;
-      return RAG_OK;
-    default:
-      return fail(RAG_EINVAL, "rag_set_option: unknown key %d", key);
-  }
-}
+namespace {
 
 // Staged output (RAG_STAGED_OUT): slot j of the staging buffer holds the chunk at ring position j;
 // move the slots to D's rank offsets.
@@ -467,6 +334,345 @@ int ag_gemm_split(rag_ctx* c, const void* A, int M, int K, const void* const* B,
   }
   if (!no_copy) HIPCHK(hipStreamWaitEvent(stream, c->ev_join, 0));
   return RAG_OK;
+}
+
+// gemm_rs (ring = false) and gemm_rs_ring (ring = true).  ptrs: by rank, the peers' [T, Mo]
+// partials (one-shot), or by chunk, the incoming [nc, Mo] running sums (ring step); ld = their
+// row stride.
+int rs_call(rag_ctx* c, const char* fn, bool ring, const void* X, int T, int Kl, const void* W,
+            int Mo, const float* const* ptrs, long long ld, int tp, int self_rank, float* send,
+            void* D, int flags, void* stream_v) {
+  if (!c) return fail(RAG_EINVAL, "%s: ctx is NULL", fn);
+  if (tp < 1 || tp > c->max_tp)
+    return fail(RAG_EINVAL, "%s: tp=%d outside [1, %d] (max_tp of the context)", fn, tp,
+                c->max_tp);
+  if (self_rank < 0 || self_rank >= tp)
+    return fail(RAG_EINVAL, "%s: self_rank=%d outside [0, tp=%d)", fn, self_rank, tp);
+  if (T < 1 || Kl < 1 || Mo < 1)
+    return fail(RAG_EINVAL, "%s: T=%d, Kl=%d, Mo=%d must all be >= 1", fn, T, Kl, Mo);
+  if (T % tp) return fail(RAG_EINVAL, "%s: T=%d is not a multiple of tp=%d", fn, T, tp);
+  if (Kl % 64) return fail(RAG_EINVAL, "%s: Kl=%d must be a multiple of 64", fn, Kl);
+  if (Mo % 4) return fail(RAG_EINVAL, "%s: Mo=%d must be a multiple of 4", fn, Mo);
+  if (flags & ~RAG_RS_ARRIVE) return fail(RAG_EINVAL, "%s: unknown flags 0x%x", fn, flags);
+  const bool arrive = (flags & RAG_RS_ARRIVE) != 0;
+  if (!X || !W || !D) return fail(RAG_EINVAL, "%s: X, W and D must not be NULL", fn);
+  const int nc = T / tp;
+  // which entries of ptrs the call reads
+  const int start = ((self_rank - 1) % tp + tp) % tp;   // ring: the chain that starts here
+  auto used = [&](int i) { return ring ? i != start : i != self_rank; };
+  bool any = false;
+  for (int i = 0; i < tp; ++i) any = any || used(i);
+  if (any && !ptrs) return fail(RAG_EINVAL, "%s: the pointer array must not be NULL", fn);
+  const char* ldname = ring ? "ldi" : "ldp";
+  if (ld < Mo) return fail(RAG_EINVAL, "%s: %s=%lld must be >= Mo=%d", fn, ldname, ld, Mo);
+  if (arrive && ld != Mo)
+    return fail(RAG_EINVAL, "%s: RAG_RS_ARRIVE needs %s equal to Mo", fn, ldname);
+  if (misaligned(X) || misaligned(W) || misaligned(D) || (send && misaligned(send)))
+    return fail(RAG_EINVAL, "%s: X, W, send and D must be 16-byte aligned", fn);
+  {
+    HIPCHK(hipSetDevice(c->device));
+    const void* named[] = {X, W, D, send};
+    const char* names[] = {"X", "W", "D", "send"};
+    for (int i = 0; i < 4; ++i)
+      if (named[i] && !on_device(named[i], c->device))
+        return fail(RAG_EINVAL, "%s: %s is not device memory of device %d", fn, names[i],
+                    c->device);
+  }
+  const long long x_bytes = (long long)T * Kl * 2, w_bytes = (long long)Mo * Kl * 2;
+  if (x_bytes > kMaxOperandBytes || w_bytes > kMaxOperandBytes)
+    return fail(RAG_EINVAL, "%s: X (%lld B) and W (%lld B) must be < 2 GiB", fn, x_bytes,
+                w_bytes);
+  const long long d_bytes = (long long)nc * Mo * 2;
+  const long long send_bytes = (long long)tp * nc * Mo * 4;
+  const long long pb = ((long long)((ring ? nc : T) - 1) * ld + Mo) * 4;   // bytes spanned
+  for (int i = 0; i < tp; ++i) {
+    if (!used(i)) continue;
+    if (!ptrs[i]) return fail(RAG_EINVAL, "%s: entry %d of the pointer array is NULL", fn, i);
+    if ((reinterpret_cast<uintptr_t>(ptrs[i]) & 3u) != 0)
+      return fail(RAG_EINVAL, "%s: entry %d of the pointer array is not 4-byte aligned", fn, i);
+    if (!on_device(ptrs[i], c->device))
+      return fail(RAG_EINVAL, "%s: entry %d of the pointer array is not device memory of "
+                  "device %d", fn, i, c->device);
+    if (overlaps(D, d_bytes, ptrs[i], pb) || (send && overlaps(send, send_bytes, ptrs[i], pb)))
+      return fail(RAG_EINVAL, "%s: D and send must not overlap entry %d of the pointer array",
+                  fn, i);
+  }
+  if (overlaps(D, d_bytes, X, x_bytes) || overlaps(D, d_bytes, W, w_bytes) ||
+      (send && (overlaps(send, send_bytes, X, x_bytes) || overlaps(send, send_bytes, W, w_bytes) ||
+                overlaps(send, send_bytes, D, d_bytes))))
+    return fail(RAG_EINVAL, "%s: D and send must not overlap X, W or each other", fn);
+  if (arrive && c->copy_engine == RAG_COPY_SDMA && c->delay_us > 0)
+    return fail(RAG_EINVAL, "%s: the arrival delay hook needs the kernel copy engine", fn);
+
+  HIPCHK(hipSetDevice(c->device));
+  hipStream_t stream = (hipStream_t)stream_v;
+  const long long slot = (long long)nc * Mo;   // floats per receive slot
+  if (arrive && any) {
+    int rc = ensure_buffer(&c->rsbuf, &c->rsbuf_bytes, (size_t)tp * slot * 4, "receive buffer");
+    if (rc) return rc;
+  }
+  const int epoch = next_epoch(c);
+  RsArgs a = {};
+  a.X = X;
+  a.W = W;
+  a.ring = ring ? 1 : 0;
+  for (int j = 0; j < tp; ++j)
+    a.chunk_of[j] = ring ? ((self_rank - 1 - j) % tp + tp) % tp : (self_rank + 1 + j) % tp;
+  for (int i = 0; i < tp; ++i) {
+    if (!used(i)) continue;
+    if (arrive) a.partial[i] = (const float*)c->rsbuf + (size_t)i * slot;
+    else a.partial[i] = ring ? ptrs[i] : ptrs[i] + (size_t)self_rank * nc * ld;
+  }
+  a.ldp = arrive ? Mo : ld;
+  a.send = send;
+  a.D = D;
+  a.T = T;
+  a.Kl = Kl;
+  a.Mo = Mo;
+  a.nc = nc;
+  a.tp = tp;
+  a.self_rank = self_rank;
+  a.gated = arrive && any;
+  a.ctr = c->ctr;
+  a.epoch = epoch;
+  a.err = c->err;
+  a.spin_limit = c->spin_us * c->wall_khz / 1000;
+  a.partial_vec = (a.ldp % 4) == 0;
+  for (int i = 0; i < tp; ++i)
+    if (a.partial[i] && (reinterpret_cast<uintptr_t>(a.partial[i]) & 15u) != 0) a.partial_vec = 0;
+
+  // Arrivals: the side stream copies, in ring order, what each tile's epilogue reads, releasing
+  // one counter per copy; the tiles wait for them on the device.
+  bool join = false;
+  if (a.gated) {
+    CopyPlan cp = {};
+    int n = 0;
+    for (int k = 1; k < tp; ++k) {
+      // one-shot: peers in arrival order s-1, s-2, ...; ring: chunks in the ring order after the
+      // chain that starts here
+      const int i = ring ? ((self_rank - 1 - k) % tp + tp) % tp : ((self_rank - k) % tp + tp) % tp;
+      cp.src[n] = ring ? (const void*)ptrs[i] : (const void*)(ptrs[i] + (size_t)self_rank * nc * ld);
+      cp.dst[n] = (float*)c->rsbuf + (size_t)i * slot;
+      cp.ctr_index[n] = i;
+      cp.pos[n] = k;
+      ++n;
+    }
+    cp.n_peer = n;
+    cp.n = n;
+    cp.bytes = (unsigned long long)slot * 4;
+    cp.piece_bytes = (unsigned)kArrivalThreads * 256u;
+    cp.pieces = (unsigned)((cp.bytes + cp.piece_bytes - 1) / cp.piece_bytes);
+    const unsigned set = c->arr_seq & 1u;
+    cp.grab = c->arr + (size_t)set * 2 * kArrSlots * kWordStride;
+    cp.done = cp.grab + (size_t)kArrSlots * kWordStride;
+    cp.clear_next = c->arr + (size_t)(set ^ 1u) * 2 * kArrSlots * kWordStride;
+    cp.delay_ticks = c->delay_us * c->wall_khz / 1000;
+    cp.withhold_mask = c->withhold;
+    HIPCHK(hipEventRecord(c->ev_fork, stream));
+    HIPCHK(hipStreamWaitEvent(c->side, c->ev_fork, 0));
+    if (c->copy_engine == RAG_COPY_SDMA) {
+      for (int k = 0; k < cp.n; ++k) {
+        HIPCHK(hipMemcpyAsync(cp.dst[k], cp.src[k], (size_t)cp.bytes, hipMemcpyDeviceToDeviceNoCU,
+                              c->side));
+        if (!((c->withhold >> cp.pos[k]) & 1u))
+          HIPCHK(hipStreamWriteValue32(c->side, c->ctr + (size_t)cp.ctr_index[k] * kWordStride,
+                                       (uint32_t)epoch, 0));
+      }
+    } else {
+      ArrivalArgs aa = {};
+      aa.cp = cp;
+      aa.ctr = c->ctr;
+      aa.epoch = epoch;
+      aa.raise_priority = c->copy_priority;
+      HIPCHK(launch_arrival(c->device, aa, c->comm_wgs, c->side));
+      c->arr_seq++;
+    }
+    // every copy is waited for by some tile, except the ring step's passed-on sums when send is
+    // NULL (those tiles are skipped): then the caller's stream waits for the side stream
+    join = ring && !send;
+    if (join) HIPCHK(hipEventRecord(c->ev_join, c->side));
+  }
+
+  const bool beside = a.gated && c->copy_engine != RAG_COPY_SDMA;
+  int tile = choose_rs_tile(c, nc, Mo, tp);
+  for (int t : {tile, (int)kTile256x128, (int)kTile128x128}) {
+    if (!c->rs_info_ok[t]) {
+      HIPCHK(rs_kernel_info(c->device, t, &c->rs_info[t]));
+      c->rs_info_ok[t] = true;
+    }
+  }
+  // With copies beside it, the automatic choice prefers a tile that leaves every compute unit
+  // room for copy waves: the copies then spread over the whole GPU instead of 8 CUs.
+  if (beside && c->tile == RAG_TILE_AUTO && reserved_cus(c->rs_info[tile], true) > 0) {
+    for (int t : {(int)kTile256x128, (int)kTile128x128})
+      if (reserved_cus(c->rs_info[t], true) == 0) {
+        tile = t;
+        break;
+      }
+  }
+  int bi, bj;
+  tile_dims(tile, &bi, &bj);
+  a.tiles_i = (nc + bi - 1) / bi;
+  a.tiles_j = (Mo + bj - 1) / bj;
+  const int total = a.tiles_i * a.tiles_j * tp;
+  const int grid = persistent_grid(total, c->num_cus - reserved_cus(c->rs_info[tile], beside),
+                                   c->rs_info[tile].max_blocks_per_cu);
+  if (debug_enabled())
+    fprintf(stderr, "[ringag] %s tp=%d s=%d T=%d Kl=%d Mo=%d tile=%dx%d tiles=%d grid=%d "
+            "arrive=%d\n", fn, tp, self_rank, T, Kl, Mo, bi, bj, total, grid, (int)arrive);
+  bool rec = false;
+  int rc = record_timing_start(c, stream, &rec);
+  if (rc) return rc;
+  HIPCHK(launch_gemm_rs(c->device, a, tile, grid, stream));
+  rc = record_timing_stop(c, stream, rec);
+  if (rc) return rc;
+  if (join) HIPCHK(hipStreamWaitEvent(stream, c->ev_join, 0));
+  return RAG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rag_version(void) { return 100; }
+
+const char* rag_last_error(void) { return g_last_error; }
+
+int rag_create(rag_ctx** out, int device, int max_tp, int flags) {
+  if (!out) return fail(RAG_EINVAL, "rag_create: out is NULL");
+  *out = nullptr;
+  if (max_tp < 1 || max_tp > RAG_MAX_TP)
+    return fail(RAG_EINVAL, "rag_create: max_tp=%d outside [1, %d]", max_tp, RAG_MAX_TP);
+  if (flags != 0) return fail(RAG_EINVAL, "rag_create: flags must be 0 (got %d)", flags);
+  int ndev = 0;
+  HIPCHK(hipGetDeviceCount(&ndev));
+  if (device < 0 || device >= ndev)
+    return fail(RAG_EINVAL, "rag_create: device %d outside [0, %d)", device, ndev);
+  HIPCHK(hipSetDevice(device));
+  hipDeviceProp_t prop;
+  HIPCHK(hipGetDeviceProperties(&prop, device));
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(RAG_EINVAL, "rag_create: device %d is %s; this library is built for gfx950",
+                device, prop.gcnArchName);
+  rag_ctx* c = new rag_ctx();
+  c->device = device;
+  c->max_tp = max_tp;
+  c->num_cus = prop.multiProcessorCount;
+  int khz = 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, device) == hipSuccess && khz > 0)
+    c->wall_khz = khz;
+  const size_t nwords = ((size_t)max_tp + 1 + 4 * (size_t)kArrSlots + 1) * kWordStride;
+  hipError_t e = load_kernels(device);
+  if (e != hipSuccess) {
+    delete c;
+    return fail(RAG_EHIP, "rag_create: loading the gfx950 kernels on device %d failed: %s", device,
+                hipGetErrorString(e));
+  }
+  e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipMalloc((void**)&c->words, nwords * sizeof(int));
+  if (e == hipSuccess) e = hipMemset(c->words, 0, nwords * sizeof(int));
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    std::string msg = std::string("rag_create: ") + hipGetErrorString(e);
+    rag_destroy(c);
+    return fail(RAG_EHIP, "%s", msg.c_str());
+  }
+  c->ctr = c->words;
+  c->arr = reinterpret_cast<unsigned*>(c->words + (size_t)(max_tp + 1) * kWordStride);
+  c->err = c->words + (size_t)(max_tp + 1 + 4 * kArrSlots) * kWordStride;
+  *out = c;
+  if (debug_enabled())
+    fprintf(stderr, "[ringag] context on device %d (%s, %d CUs, wall clock %lld kHz), max_tp %d\n",
+            device, prop.gcnArchName, c->num_cus, c->wall_khz, max_tp);
+  return RAG_OK;
+}
+
+int rag_destroy(rag_ctx* c) {
+  if (!c) return RAG_OK;
+  (void)hipSetDevice(c->device);
+  if (c->side) (void)hipStreamSynchronize(c->side);
+  for (auto ev : c->t_start) (void)hipEventDestroy(ev);
+  for (auto ev : c->t_stop) (void)hipEventDestroy(ev);
+  for (auto ev : c->ev_chunk) (void)hipEventDestroy(ev);
+  if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
+  if (c->ev_join) (void)hipEventDestroy(c->ev_join);
+  if (c->side) (void)hipStreamDestroy(c->side);
+  if (c->words) (void)hipFree(c->words);
+  if (c->gbuf) (void)hipFree(c->gbuf);
+  if (c->stage) (void)hipFree(c->stage);
+  if (c->rsbuf) (void)hipFree(c->rsbuf);
+  delete c;
+  return RAG_OK;
+}
+
+int rag_set_option(rag_ctx* c, int key, long long v) {
+  if (!c) return fail(RAG_EINVAL, "rag_set_option: ctx is NULL");
+  switch (key) {
+    case RAG_OPT_COPY_ENGINE:
+      if (v != RAG_COPY_KERNEL && v != RAG_COPY_SDMA && v != RAG_COPY_IN_GEMM)
+        return fail(RAG_EINVAL, "copy engine must be 0 (kernel), 1 (sdma) or 2 (in the GEMM)");
+      c->copy_engine = (int)v;
+      return RAG_OK;
+    case RAG_OPT_COMM_WGS:
+      if (v < 1 || v > 1024) return fail(RAG_EINVAL, "comm workgroups must be in [1, 1024]");
+      c->comm_wgs = (int)v;
+      return RAG_OK;
+    case RAG_OPT_SPIN_LIMIT_US:
+      if (v < 1 || v > 60000000LL) return fail(RAG_EINVAL, "spin limit must be in [1, 6e7] us");
+      c->spin_us = v;
+      return RAG_OK;
+    case RAG_OPT_ARRIVAL_DELAY_US:
+      if (v < 0 || v > 1000000LL) return fail(RAG_EINVAL, "arrival delay must be in [0, 1e6] us");
+      c->delay_us = v;
+      return RAG_OK;
+    case RAG_OPT_WITHHOLD_MASK:
+      if (v < 0 || v > 0xffffLL) return fail(RAG_EINVAL, "withhold mask must fit in 16 bits");
+      c->withhold = (unsigned)v;
+      return RAG_OK;
+    case RAG_OPT_TIMING:
+      if (v != 0 && v != 1) return fail(RAG_EINVAL, "timing must be 0 or 1");
+      if (v && c->t_start.empty()) {
+        HIPCHK(hipSetDevice(c->device));
+        c->t_start.resize(kTimingSlots);
+        c->t_stop.resize(kTimingSlots);
+        for (int i = 0; i < kTimingSlots; ++i) {
+          HIPCHK(hipEventCreate(&c->t_start[i]));
+          HIPCHK(hipEventCreate(&c->t_stop[i]));
+        }
+      }
+      c->timing = v != 0;
+      return RAG_OK;
+    case RAG_OPT_WGS_PER_CU:
+      if (v < 0 || v > 16) return fail(RAG_EINVAL, "workgroups per CU must be in [0, 16]");
+      c->wgs_per_cu = (int)v;
+      return RAG_OK;
+    case RAG_OPT_GEMM_COPY_WGS:
+      if (v < 0 || v > 65536) return fail(RAG_EINVAL, "GEMM copy workgroups must be in [0, 65536]");
+      c->gemm_copy_wgs = (int)v;
+      return RAG_OK;
+    case RAG_OPT_COPY_PRIORITY:
+      if (v != 0 && v != 1) return fail(RAG_EINVAL, "copy priority must be 0 or 1");
+      c->copy_priority = (int)v;
+      return RAG_OK;
+    case RAG_OPT_TRACE_BUF:
+      if (v != 0 && (v & 7)) return fail(RAG_EINVAL, "trace buffer must be 8-byte aligned");
+      if (v != 0 && !on_device(reinterpret_cast<const void*>(v), c->device))
+        return fail(RAG_EINVAL, "trace buffer is not device memory of device %d", c->device);
+      c->trace_buf = (unsigned long long)v;
+      return RAG_OK;
+    case RAG_OPT_TRACE_BYTES:
+      if (v < 0) return fail(RAG_EINVAL, "trace size must be >= 0");
+      c->trace_bytes = v;
+      return RAG_OK;
+    case RAG_OPT_TILE:
+      if (v < RAG_TILE_AUTO || v > RAG_TILE_256x256_8W_S4) return fail(RAG_EINVAL, "unknown tile %lld", v);
+      c->tile = (int)v;
+      return RAG_OK;
+    default:
+      return fail(RAG_EINVAL, "rag_set_option: unknown key %d", key);
+  }
 }
 
 int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int nc, int tp,
@@ -677,7 +883,8 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
     int bpc = c->ag_info[tile][fp8].max_blocks_per_cu;
     if (c->wgs_per_cu > 0) bpc = std::min(bpc, c->wgs_per_cu);
     const bool beside = !no_copy && c->copy_engine == RAG_COPY_KERNEL;
-    const int grid = persistent_grid(total, c->num_cus - reserved_cus(tile, beside), bpc);
+    const int grid =
+        persistent_grid(total, c->num_cus - reserved_cus(c->ag_info[tile][fp8], beside), bpc);
     // in-kernel copies: workgroups w with (w / 8) % copy_stride == 0 take part (workgroup 0 always)
     a.copy_stride = 1;
     if (a.copies && c->gemm_copy_wgs > 0 && grid >= 8)
@@ -706,92 +913,15 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
 int gemm_rs(rag_ctx* c, const void* X, int T, int Kl, const void* W, int Mo,
             const float* const* partials, long long ldp, int tp, int self_rank, float* send,
             void* D, int flags, void* stream_v) {
-  if (!c) return fail(RAG_EINVAL, "gemm_rs: ctx is NULL");
-  if (tp < 1 || tp > c->max_tp)
-    return fail(RAG_EINVAL, "gemm_rs: tp=%d outside [1, %d] (max_tp of the context)", tp, c->max_tp);
-  if (self_rank < 0 || self_rank >= tp)
-    return fail(RAG_EINVAL, "gemm_rs: self_rank=%d outside [0, tp=%d)", self_rank, tp);
-  if (T < 1 || Kl < 1 || Mo < 1)
-    return fail(RAG_EINVAL, "gemm_rs: T=%d, Kl=%d, Mo=%d must all be >= 1", T, Kl, Mo);
-  if (T % tp) return fail(RAG_EINVAL, "gemm_rs: T=%d is not a multiple of tp=%d", T, tp);
-  if (Kl % 64) return fail(RAG_EINVAL, "gemm_rs: Kl=%d must be a multiple of 64", Kl);
-  if (flags != 0) return fail(RAG_EINVAL, "gemm_rs: flags must be 0 (got 0x%x)", flags);
-  if (!X || !W || !D) return fail(RAG_EINVAL, "gemm_rs: X, W and D must not be NULL");
-  if (tp > 1 && !partials) return fail(RAG_EINVAL, "gemm_rs: partials must not be NULL for tp > 1");
-  if (ldp < Mo) return fail(RAG_EINVAL, "gemm_rs: ldp=%lld must be >= Mo=%d", ldp, Mo);
-  if (misaligned(X) || misaligned(W) || misaligned(D) || (send && misaligned(send)))
-    return fail(RAG_EINVAL, "gemm_rs: X, W, send and D must be 16-byte aligned");
-  {
-    HIPCHK(hipSetDevice(c->device));
-    const void* named[] = {X, W, D, send};
-    const char* names[] = {"X", "W", "D", "send"};
-    for (int i = 0; i < 4; ++i)
-      if (named[i] && !on_device(named[i], c->device))
-        return fail(RAG_EINVAL, "gemm_rs: %s is not device memory of device %d", names[i],
-                    c->device);
-    for (int p = 0; p < tp; ++p)
-      if (p != self_rank && partials && partials[p] && !on_device(partials[p], c->device))
-        return fail(RAG_EINVAL, "gemm_rs: partials[%d] is not device memory of device %d", p,
-                    c->device);
-  }
-  const int nc = T / tp;
-  const long long x_bytes = (long long)T * Kl * 2, w_bytes = (long long)Mo * Kl * 2;
-  if (x_bytes > kMaxOperandBytes || w_bytes > kMaxOperandBytes)
-    return fail(RAG_EINVAL, "gemm_rs: X (%lld B) and W (%lld B) must be < 2 GiB", x_bytes, w_bytes);
-  const long long d_bytes = (long long)nc * Mo * 2;
-  const long long send_bytes = (long long)tp * nc * Mo * 4;
-  for (int p = 0; p < tp; ++p) {
-    if (p == self_rank) continue;
-    if (!partials[p]) return fail(RAG_EINVAL, "gemm_rs: partials[%d] is NULL", p);
-    if ((reinterpret_cast<uintptr_t>(partials[p]) & 3u) != 0)
-      return fail(RAG_EINVAL, "gemm_rs: partials[%d] is not 4-byte aligned", p);
-    const long long pb = ((long long)(T - 1) * ldp + Mo) * 4;
-    if (overlaps(D, d_bytes, partials[p], pb) || (send && overlaps(send, send_bytes, partials[p], pb)))
-      return fail(RAG_EINVAL, "gemm_rs: D and send must not overlap partials[%d]", p);
-  }
-  if (overlaps(D, d_bytes, X, x_bytes) || overlaps(D, d_bytes, W, w_bytes) ||
-      (send && (overlaps(send, send_bytes, X, x_bytes) || overlaps(send, send_bytes, W, w_bytes) ||
-                overlaps(send, send_bytes, D, d_bytes))))
-    return fail(RAG_EINVAL, "gemm_rs: D and send must not overlap X, W or each other");
+  return rs_call(c, "gemm_rs", false, X, T, Kl, W, Mo, partials, ldp, tp, self_rank, send, D,
+                 flags, stream_v);
+}
 
-  HIPCHK(hipSetDevice(c->device));
-  hipStream_t stream = (hipStream_t)stream_v;
-  RsArgs a = {};
-  a.X = X;
-  a.W = W;
-  for (int j = 0; j < tp; ++j) a.chunk_of[j] = (self_rank + 1 + j) % tp;
-  for (int p = 0; p < tp; ++p) a.partial[p] = (p == self_rank || !partials) ? nullptr : partials[p];
-  a.ldp = ldp;
-  a.send = send;
-  a.D = D;
-  a.T = T;
-  a.Kl = Kl;
-  a.Mo = Mo;
-  a.nc = nc;
-  a.tp = tp;
-  a.self_rank = self_rank;
-  const int tile = choose_rs_tile(c, nc, Mo, tp);
-  int bi, bj;
-  tile_dims(tile, &bi, &bj);
-  a.tiles_i = (nc + bi - 1) / bi;
-  a.tiles_j = (Mo + bj - 1) / bj;
-  if (!c->rs_info_ok[tile]) {
-    HIPCHK(rs_kernel_info(c->device, tile, &c->rs_info[tile]));
-    c->rs_info_ok[tile] = true;
-  }
-  const int total = a.tiles_i * a.tiles_j * tp;
-  const int grid = persistent_grid(total, c->num_cus, c->rs_info[tile].max_blocks_per_cu);
-  a.partial_vec = (ldp % 4) == 0;
-  for (int p = 0; p < tp; ++p)
-    if (a.partial[p] && (reinterpret_cast<uintptr_t>(a.partial[p]) & 15u) != 0) a.partial_vec = 0;
-  if (debug_enabled())
-    fprintf(stderr, "[ringag] gemm_rs tp=%d s=%d T=%d Kl=%d Mo=%d tile=%dx%d tiles=%d grid=%d\n",
-            tp, self_rank, T, Kl, Mo, bi, bj, total, grid);
-  bool rec = false;
-  int rc = record_timing_start(c, stream, &rec);
-  if (rc) return rc;
-  HIPCHK(launch_gemm_rs(c->device, a, tile, grid, stream));
-  return record_timing_stop(c, stream, rec);
+int gemm_rs_ring(rag_ctx* c, const void* X, int T, int Kl, const void* W, int Mo,
+                 const float* const* incoming, long long ldi, int tp, int self_rank, float* send,
+                 void* D, int flags, void* stream_v) {
+  return rs_call(c, "gemm_rs_ring", true, X, T, Kl, W, Mo, incoming, ldi, tp, self_rank, send, D,
+                 flags, stream_v);
 }
 
 int rag_ag_kernel_name(rag_ctx* c, int nc, int M, int tp, rag_dtype dt, char* buf, int len) {

@@ -176,6 +176,31 @@ def make_rs(shape: RSShape, poison_outside_chunk: bool = True) -> RSInputs:
     return RSInputs(shape, x.to(torch.bfloat16), w.to(torch.bfloat16), partials)
 
 
+@dataclass
+class RSRingInputs:
+    shape: RSShape
+    X: torch.Tensor                       # [T, Kl] bf16
+    W: torch.Tensor                       # [Mo, Kl] bf16
+    incoming: List[torch.Tensor] = field(default_factory=list)   # tp x [nc, Mo] fp32, by chunk
+
+
+def make_rs_ring(shape: RSShape) -> RSRingInputs:
+    """Inputs of one ring-accumulate reduce-scatter step: X and W drawn as in make_rs, then one
+    fp32 [nc, Mo] incoming running sum per chunk, in increasing chunk index (the step ignores the
+    entry of the chain that starts at this rank; it is drawn like the others)."""
+    g = torch.Generator("cpu").manual_seed(shape.seed)
+    if shape.dist == "normal_rs":
+        w = torch.randn((shape.Mo, shape.Kl), generator=g) / math.sqrt(shape.tp * shape.Kl)
+        x = torch.randn((shape.T, shape.Kl), generator=g) / math.sqrt(shape.tp * shape.Kl)
+        inc = [torch.randn((shape.nc, shape.Mo), generator=g) / 256.0 for _ in range(shape.tp)]
+    else:
+        w = _draw(g, (shape.Mo, shape.Kl), shape.dist, shape.Kl)
+        x = _draw(g, (shape.T, shape.Kl), shape.dist, shape.Kl)
+        inc = [_draw(g, (shape.nc, shape.Mo), shape.dist, shape.Kl) for _ in range(shape.tp)]
+    return RSRingInputs(shape, x.to(torch.bfloat16), w.to(torch.bfloat16),
+                        [t.to(torch.float32) for t in inc])
+
+
 def ag_shape(tp, self_rank, nc, K, M, dtype="bf16", dist="uniform1", seed=7) -> AGShape:
     return AGShape(f"ag_tp{tp}_s{self_rank}_nc{nc}_k{K}_m{M}_{dtype}_{dist}", tp, self_rank, nc, K,
                    M, dtype, dist, seed)

@@ -126,3 +126,219 @@ def test_rs_full_size_sampled_rows():
         ref = O.gemm_tn_rows(Xf, Wf, cix * shape.nc + rows[:8])
         got = send[cix][rows[:8]]
         assert np.abs(got - ref).max() <= TOL_SEND * np.abs(ref).max()
+
+
+# ------------------------------------------------- arrivals (counter-gated) and the ring step
+
+COPY_ENGINES = ["kernel", "sdma"]
+
+
+def _engine(c, e):
+    c.set_option(B.RAG_OPT_COPY_ENGINE, B.ENGINES[e])
+
+
+@pytest.mark.parametrize("engine", COPY_ENGINES)
+@pytest.mark.parametrize("tp,s", [(1, 0), (2, 1), (4, 3), (8, 5)])
+def test_rs_arrive_exact_integers(tp, s, engine):
+    """RAG_RS_ARRIVE: the peers' partials of the own chunk are copied in during the call and the
+    own chunk's tiles wait for their counters; same result, bit for bit."""
+    c = ctx()
+    _engine(c, engine)
+    shape = W.rs_shape(tp, s, tp * 72, 128, 136, dist="int3", seed=tp * 10 + s + 300)
+    say(f"case rs arrive {shape.name} engine={engine}")
+    inp = W.make_rs(shape)
+    run = RSRun(inp)
+    B.gemm_rs(c, run.X, run.W, run.partials, tp, s, run.D, send=run.send, flags=B.RAG_RS_ARRIVE)
+    c.check()
+    D_ref, send_ref, _ = oracle_rs(inp)
+    assert np.array_equal(W.bits_u16(run.D.cpu()), O.f32_to_bf16(D_ref))
+    _check_send(run, send_ref, exact=True)
+
+
+def test_rs_arrive_fresh_data_delayed():
+    """Back-to-back gated calls with new partials each time and every copy's counter held back
+    1 ms: an epilogue that read the receive buffer before its counter would add the previous
+    call's partials."""
+    c = ctx()
+    _engine(c, "kernel")
+    c.set_option(B.RAG_OPT_ARRIVAL_DELAY_US, 1000)
+    shape = W.rs_shape(4, 1, 4 * 64, 128, 128, dist="int3", seed=1)
+    run = RSRun(W.make_rs(shape))
+    for it in range(6):
+        inp = W.make_rs(W.rs_shape(4, 1, 4 * 64, 128, 128, dist="int3", seed=600 + it))
+        run.X.copy_(inp.X)
+        run.W.copy_(inp.W)
+        for d, h in zip(run.partials, inp.partials):
+            if d is not None:
+                d.copy_(h)
+        say(f"case rs arrive fresh it={it}")
+        B.gemm_rs(c, run.X, run.W, run.partials, 4, 1, run.D, send=run.send,
+                  flags=B.RAG_RS_ARRIVE)
+        torch.cuda.synchronize()
+        D_ref, _, _ = oracle_rs(inp)
+        assert np.array_equal(W.bits_u16(run.D.cpu()), O.f32_to_bf16(D_ref)), it
+    c.check()
+
+
+def test_rs_arrive_withheld_times_out_and_recovers():
+    c = ctx()
+    _engine(c, "kernel")
+    c.set_option(B.RAG_OPT_SPIN_LIMIT_US, 20000)
+    c.set_option(B.RAG_OPT_WITHHOLD_MASK, 1 << 2)
+    shape = W.rs_shape(4, 0, 4 * 64, 128, 128, dist="int3", seed=5)
+    inp = W.make_rs(shape)
+    run = RSRun(inp)
+    say("case rs arrive withheld")
+    B.gemm_rs(c, run.X, run.W, run.partials, 4, 0, run.D, send=run.send, flags=B.RAG_RS_ARRIVE)
+    with pytest.raises(B.RagError) as ei:
+        c.check()
+    assert ei.value.code == B.RAG_ETIMEOUT
+    c.set_option(B.RAG_OPT_WITHHOLD_MASK, 0)
+    c.set_option(B.RAG_OPT_SPIN_LIMIT_US, 2_000_000)
+    B.gemm_rs(c, run.X, run.W, run.partials, 4, 0, run.D, send=run.send, flags=B.RAG_RS_ARRIVE)
+    c.check()
+    D_ref, _, _ = oracle_rs(inp)
+    assert np.array_equal(W.bits_u16(run.D.cpu()), O.f32_to_bf16(D_ref))
+
+
+class RSRingRun:
+    def __init__(self, inp: W.RSRingInputs, with_send=True, poison_start=True):
+        s = inp.shape
+        self.inp = inp
+        self.X = inp.X.to(DEV)
+        self.W = inp.W.to(DEV)
+        self.incoming = [t.to(DEV) for t in inp.incoming]
+        self.start = O.rs_ring_order(s.self_rank, s.tp)[0]
+        if poison_start:
+            # the chain of this chunk starts here: its entry must not be read
+            self.incoming[self.start] = torch.full_like(self.incoming[self.start], float("nan"))
+        self.D = torch.empty((s.nc, s.Mo), dtype=torch.bfloat16, device=DEV)
+        self.send = torch.full((s.tp, s.nc, s.Mo), float("nan"), device=DEV) if with_send else None
+
+    def run(self, c, flags=0):
+        s = self.inp.shape
+        B.gemm_rs_ring(c, self.X, self.W, self.incoming, s.tp, s.self_rank, self.D,
+                       send=self.send, flags=flags)
+        torch.cuda.synchronize()
+        return self
+
+
+def oracle_ring(inp: W.RSRingInputs):
+    s = inp.shape
+    return O.gemm_rs_ring_step(W.bits_u16(inp.X), W.bits_u16(inp.W),
+                               [t.numpy() for t in inp.incoming], s.tp, s.self_rank)
+
+
+@pytest.mark.parametrize("mode", ["given", "kernel", "sdma"])
+@pytest.mark.parametrize("tp,s", [(1, 0), (2, 0), (3, 1), (4, 2), (8, 5)])
+def test_rs_ring_step_exact_integers(tp, s, mode):
+    """One ring step: send[c] = incoming[c] + P[c], D = incoming[s] + P[s], bit for bit on
+    integer data; the chain-start entry is NaN and must not be read; the own slot of send stays
+    untouched."""
+    c = ctx()
+    flags = 0
+    if mode != "given":
+        _engine(c, mode)
+        flags = B.RAG_RS_ARRIVE
+    shape = W.rs_shape(tp, s, tp * 72, 128, 136, dist="int3", seed=tp * 10 + s + 700)
+    say(f"case rs ring {shape.name} mode={mode}")
+    inp = W.make_rs_ring(shape)
+    run = RSRingRun(inp).run(c, flags)
+    c.check()
+    D_ref, send_ref, _ = oracle_ring(inp)
+    assert np.array_equal(W.bits_u16(run.D.cpu()), O.f32_to_bf16(D_ref))
+    _check_send(run, send_ref, exact=True)
+
+
+@pytest.mark.parametrize("tile", ["128x128", "256x128", "256x256w8"])
+def test_rs_ring_ragged_random(tile):
+    c = ctx()
+    c.set_option(B.RAG_OPT_TILE, B.TILES[tile])
+    _engine(c, "kernel")
+    shape = W.rs_shape(4, 1, 4 * 200, 192, 300, seed=13)
+    say(f"case rs ring ragged tile={tile}")
+    inp = W.make_rs_ring(shape)
+    run = RSRingRun(inp).run(c, B.RAG_RS_ARRIVE)
+    c.check()
+    D_ref, send_ref, _ = oracle_ring(inp)
+    assert rel_err(W.bits_u16(run.D.cpu()), D_ref) <= TOL_BF16
+    _check_send(run, send_ref)
+
+
+def test_rs_ring_no_send_and_delayed_arrivals():
+    """send = NULL (the passed-on sums are dropped, so only the own chunk waits on the device and
+    the call joins the side stream) with every copy held back 1 ms, then fresh data."""
+    c = ctx()
+    _engine(c, "kernel")
+    c.set_option(B.RAG_OPT_ARRIVAL_DELAY_US, 1000)
+    for it in range(3):
+        shape = W.rs_shape(4, 3, 4 * 64, 128, 128, dist="int3", seed=800 + it)
+        inp = W.make_rs_ring(shape)
+        say(f"case rs ring no-send it={it}")
+        run = RSRingRun(inp, with_send=False).run(c, B.RAG_RS_ARRIVE)
+        D_ref, _, _ = oracle_ring(inp)
+        assert np.array_equal(W.bits_u16(run.D.cpu()), O.f32_to_bf16(D_ref)), it
+    c.check()
+
+
+def test_rs_ring_full_size_sampled_rows():
+    """The ring step at the measured GEMM+RS size with arrivals: sampled rows of D and of every
+    passed-on sum against the oracle."""
+    shape = W.WORKLOADS["rs_8k"]
+    c = ctx()
+    _engine(c, "kernel")
+    say(f"case rs ring full {shape}")
+    inp = W.make_rs_ring(shape)
+    run = RSRingRun(inp).run(c, B.RAG_RS_ARRIVE)
+    c.check()
+    g = np.random.default_rng(shape.seed + 1)
+    rows = np.unique(np.concatenate([[0, shape.nc - 1], g.choice(shape.nc, 30, replace=False)]))
+    Xb, Wb = W.bits_u16(inp.X), W.bits_u16(inp.W)
+    inc = [t.numpy() for t in inp.incoming]
+    D_rows = O.gemm_rs_ring_step_rows(Xb, Wb, inc, shape.tp, shape.self_rank, shape.self_rank,
+                                      rows)
+    err = rel_err(W.bits_u16(run.D.cpu())[rows], D_rows)
+    say(f"rs ring D: {len(rows)} sampled rows, max rel err {err:.3e}")
+    assert err <= TOL_BF16
+    send = run.send.cpu().numpy()
+    for cix in range(shape.tp):
+        if cix == shape.self_rank:
+            continue
+        ref = O.gemm_rs_ring_step_rows(Xb, Wb, inc, shape.tp, shape.self_rank, cix, rows[:8])
+        got = send[cix][rows[:8]]
+        assert np.abs(got - ref).max() <= TOL_SEND * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("ring", [False, True])
+def test_rs_arrive_full_size_back_to_back(ring):
+    """Full-size gated calls back to back (no synchronisation between them) with the copy kernel
+    beside the GEMM: the GEMM's persistent grid must leave the copies room to run, or its waiting
+    tiles would spin to the limit (RAG_ETIMEOUT).  Then the last call is checked on sampled rows."""
+    shape = W.WORKLOADS["rs_8k"]
+    c = ctx()
+    _engine(c, "kernel")
+    c.set_option(B.RAG_OPT_COMM_WGS, 128)
+    say(f"case rs arrive back-to-back ring={ring} {shape}")
+    if ring:
+        inp = W.make_rs_ring(shape)
+        run = RSRingRun(inp, poison_start=False)
+        for _ in range(4):
+            B.gemm_rs_ring(c, run.X, run.W, run.incoming, shape.tp, shape.self_rank, run.D,
+                           send=run.send, flags=B.RAG_RS_ARRIVE)
+    else:
+        inp = W.make_rs(shape)
+        run = RSRun(inp)
+        for _ in range(4):
+            B.gemm_rs(c, run.X, run.W, run.partials, shape.tp, shape.self_rank, run.D,
+                      send=run.send, flags=B.RAG_RS_ARRIVE)
+    torch.cuda.synchronize()
+    c.check()
+    rows = np.array([0, 17, shape.nc // 2, shape.nc - 1])
+    Xb, Wb = W.bits_u16(inp.X), W.bits_u16(inp.W)
+    if ring:
+        ref = O.gemm_rs_ring_step_rows(Xb, Wb, [t.numpy() for t in inp.incoming], shape.tp,
+                                       shape.self_rank, shape.self_rank, rows)
+    else:
+        ref = O.gemm_rs_rows(Xb, Wb, [None if p is None else p.numpy() for p in inp.partials],
+                             shape.tp, shape.self_rank, rows)
+    assert rel_err(W.bits_u16(run.D.cpu())[rows], ref) <= TOL_BF16
