@@ -348,3 +348,24 @@ def gemm_rs_ring_step_rows(X_bits, W_bits, incoming, tp, self_rank, chunk, local
     if chunk == (self_rank - 1) % tp:
         return mine
     return (np.asarray(incoming[chunk], dtype=np.float32)[rows] + mine).astype(np.float32)
+
+
+def linear_allreduce_step(X_bits: np.ndarray, W_bits: np.ndarray,
+                          peer_partials: Sequence[np.ndarray], reduced_bits: Sequence[np.ndarray],
+                          tp: int, self_rank: int):
+    """One rank's share of a row-parallel linear whose output is all-reduced as a reduce-scatter
+    followed by an all-gather of the reduced chunks.  The reduce-scatter is gemm_rs (this rank
+    reduces its own chunk over all ranks' partials); the all-gather brings in every other chunk
+    c as its owner reduced it (reduced_bits[c], bf16 [nc, Mo]; entry self_rank ignored).
+    Returns (Y fp32 [T, Mo]: rows of chunk c = reduced chunk c widened, rows of the own chunk =
+    the fp32 sum before output rounding; send as gemm_rs).
+    [NVF-5742] walkthrough and sequence diagram (row-parallel linear: per-chunk matmul, then the
+    chunk's all-reduce); [TE-2443] sequence diagram (reduce-scatter of the split GEMM)."""
+    T = X_bits.shape[0]
+    nc = T // tp
+    D, send, _ = gemm_rs(X_bits, W_bits, peer_partials, tp, self_rank)
+    Mo = D.shape[1]
+    Y = np.empty((T, Mo), dtype=np.float32)
+    for c in range(tp):
+        Y[c * nc:(c + 1) * nc] = D if c == self_rank else bf16_to_f32(reduced_bits[c])
+    return Y, send

@@ -419,6 +419,32 @@ def test_rs_ring_rows_matches_full():
     assert np.array_equal(send[s], D)
 
 
+def test_linear_allreduce_equals_unsharded_linear():
+    """With every rank's partial and every owner's reduced chunk consistent (integers, so exact),
+    one rank's step gives the whole row-parallel linear: sum over ranks of X_r W_r^T, i.e. the
+    linear on the unsharded input and weight, for every self rank."""
+    rng = np.random.default_rng(97)
+    for tp in (1, 2, 4):
+        nc, Kl, Mo = 3, 8, 6
+        T = tp * nc
+        # entries in {-1, 0, 1}: every sum stays within +-32, exact in bf16 as well
+        Xs = [rng.integers(-1, 2, (T, Kl)) for _ in range(tp)]
+        Ws = [rng.integers(-1, 2, (Mo, Kl)) for _ in range(tp)]
+        P = [_exact_gemm(Xs[r], Ws[r]) for r in range(tp)]
+        # the unsharded linear: the input is [X_0 | X_1 | ...] along k, the weight likewise
+        full = _exact_gemm(np.concatenate(Xs, axis=1), np.concatenate(Ws, axis=1))
+        assert np.array_equal(full, sum(P))
+        reduced = [_bf16_bits(full[c * nc:(c + 1) * nc]) for c in range(tp)]
+        for s in range(tp):
+            peers = [None if p == s else P[p].astype(np.float32) for p in range(tp)]
+            Y, send = O.linear_allreduce_step(_bf16_bits(Xs[s]), _bf16_bits(Ws[s]), peers,
+                                              reduced, tp, s)
+            assert np.array_equal(Y.astype(np.int64), full)
+            for c in range(tp):
+                if c != s:
+                    assert np.array_equal(send[c].astype(np.int64), P[s][c * nc:(c + 1) * nc])
+
+
 # ------------------------------------------------------------------------------------ mutants
 
 def _pins_pass(gemm, gather, order_fn):
