@@ -291,12 +291,20 @@ def main():
         ms_ring_arrive, _ = time_steps(
             lambda: B.gemm_rs_ring(ctx, Xr, Wr, inc, shape.tp, shape.self_rank, D, send=send,
                                    flags=B.RAG_RS_ARRIVE), args.steps, args.warmup, stream)
+        # the row-parallel linear with its output all-reduced: the reduce-scatter above plus an
+        # all-gather of the owners' reduced chunks into Y, copied beside the GEMM
+        red = [t.to(dev) for t in W.make_reduced_chunks(shape)]
+        Y = torch.empty((shape.T, shape.Mo), dtype=torch.bfloat16, device=dev)
+        ms_lar, _ = time_steps(lambda: B.linear_allreduce(ctx, X, Wt, parts, red, shape.tp,
+                                                          shape.self_rank, Y, send=send),
+                               args.steps, args.warmup, stream)
         ctx.check()
         out["variants_ms_per_step"] = {
             "one_shot_partials_given": round(ms, 5),
             "one_shot_partials_arrive": round(ms_arrive, 5),
             "ring_step_sums_given": round(ms_ring, 5),
             "ring_step_sums_arrive": round(ms_ring_arrive, 5),
+            "linear_allreduce": round(ms_lar, 5),
             "arrival_engine": "kernel" if args.copy_engine != "sdma" else "sdma",
             "comm_wgs": args.comm_wgs}
         if not args.no_cpu:

@@ -270,6 +270,34 @@ RAG_API int gemm_rs_ring(rag_ctx* ctx,
             float* send, void* D,
             int flags, void* stream);
 
+/*
+ * One rank's share of a row-parallel linear whose output is all-reduced, as a reduce-scatter
+ * followed by an all-gather of the reduced chunks (nvFuser PR #5742, walkthrough and sequence
+ * diagram: per-chunk matmul, then that chunk's all-reduce; TransformerEngine PR #2443, sequence
+ * diagram: reduce-scatter of the split GEMM):
+ *     Y[rows of chunk self_rank] = sum over ranks of P_p[rows of chunk self_rank]  (gemm_rs)
+ *     Y[rows of chunk c]         = reduced[c]  for c != self_rank (the owners' reduced chunks,
+ *                                  all-gathered: copied in by the side stream in ring order,
+ *                                  self_rank-1 first, while the GEMM runs)
+ *     send                       as for gemm_rs
+ *
+ *   X, W, Kl, partials, ldp, send, flags as for gemm_rs
+ *   Mo        >= 8, multiple of 8
+ *   reduced   HOST array of tp device pointers to bf16 [nc, Mo] reduced chunks (contiguous);
+ *             entry self_rank ignored
+ *   Y         [T, Mo] bf16 output, T = tp * nc
+ * The all-gather's copies use the copy kernel, or SDMA with RAG_COPY_SDMA.
+ * Errors: RAG_EINVAL, RAG_EHIP.
+ */
+RAG_API int linear_allreduce(rag_ctx* ctx,
+            const void* X, int T, int Kl,
+            const void* W, int Mo,
+            const float* const* partials, long long ldp,
+            const void* const* reduced,
+            int tp, int self_rank,
+            float* send, void* Y,
+            int flags, void* stream);
+
 /* Name of the GPU kernel entry point gemm_rs would launch for these sizes (nc rows per chunk, Mo
  * output columns, tp chunks) with the context's current options (e.g. "rag_rs_t256x256w8").
  * Diagnostics, like rag_ag_kernel_name. */

@@ -74,6 +74,8 @@ def lib():
     L.ag_gemm.argtypes = [vp, vp, i, i, ctypes.POINTER(vp), i, i, i, vp, vp, i, vp, vp, i, vp]
     L.gemm_rs.argtypes = [vp, vp, i, i, vp, i, ctypes.POINTER(vp), ll, i, i, vp, vp, i, vp]
     L.gemm_rs_ring.argtypes = [vp, vp, i, i, vp, i, ctypes.POINTER(vp), ll, i, i, vp, vp, i, vp]
+    L.linear_allreduce.argtypes = [vp, vp, i, i, vp, i, ctypes.POINTER(vp), ll,
+                                   ctypes.POINTER(vp), i, i, vp, vp, i, vp]
     L.rag_check.argtypes = [vp]
     L.rag_kernel_times.argtypes = [vp, ctypes.POINTER(ctypes.c_float), i]
     L.rag_ag_kernel_name.argtypes = [vp, i, i, i, i, ctypes.c_char_p, i]
@@ -81,6 +83,7 @@ def lib():
     L.rag_last_error.restype = ctypes.c_char_p
     L.rag_version.restype = i
     for f in ("rag_create", "rag_destroy", "rag_set_option", "ag_gemm", "gemm_rs", "gemm_rs_ring",
+              "linear_allreduce",
               "rag_check",
               "rag_kernel_times", "rag_ag_kernel_name", "rag_rs_kernel_name"):
         getattr(L, f).restype = i
@@ -279,3 +282,43 @@ def gemm_rs_ring(ctx: Context, X: torch.Tensor, W: torch.Tensor,
     nc = X.shape[0] // tp
     return _rs(lib().gemm_rs_ring, ctx, X, W, incoming, nc, (self_rank - 1) % tp, tp, self_rank,
                D, send, flags, stream)
+
+
+def linear_allreduce(ctx: Context, X: torch.Tensor, W: torch.Tensor,
+                     partials: Sequence[Optional[torch.Tensor]],
+                     reduced: Sequence[Optional[torch.Tensor]], tp: int, self_rank: int,
+                     Y: torch.Tensor, send: Optional[torch.Tensor] = None, flags: int = 0,
+                     stream=None) -> int:
+    """Row-parallel linear with its output all-reduced (reduce-scatter + all-gather of the reduced
+    chunks): Y's own chunk = the sum over ranks of that chunk's partials, Y's chunk c = reduced[c]
+    (the owners' bf16 [nc, Mo] results, entry self_rank ignored)."""
+    T, Kl = X.shape
+    Mo = W.shape[0]
+    if Y.dtype != torch.bfloat16 or tuple(Y.shape) != (T, Mo) or not Y.is_contiguous():
+        raise ValueError(f"Y must be a contiguous bfloat16 [{T}, {Mo}] tensor")
+    if len(reduced) != tp:
+        raise ValueError(f"need tp={tp} reduced entries (entry self_rank may be None)")
+    nc = T // tp
+    rarr = []
+    for r, t in enumerate(reduced):
+        if r == self_rank or t is None:
+            rarr.append(None)
+            continue
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != (nc, Mo) or not t.is_contiguous() \
+                or not t.is_cuda:
+            raise ValueError(f"each reduced chunk must be a contiguous bfloat16 GPU [{nc}, {Mo}]")
+        rarr.append(ctypes.c_void_p(t.data_ptr()))
+    rptrs = (ctypes.c_void_p * tp)(*rarr)
+    arr = []
+    ldp = Mo
+    for p, t in enumerate(partials):
+        if p == self_rank or t is None:
+            arr.append(None)
+            continue
+        if t.dtype != torch.float32 or t.dim() != 2 or t.shape[0] != T or t.stride(1) != 1:
+            raise ValueError("each peer partial must be a float32 GPU tensor [T, >=Mo]")
+        ldp = t.stride(0)
+        arr.append(ctypes.c_void_p(t.data_ptr()))
+    ptrs = (ctypes.c_void_p * tp)(*arr)
+    return _check(lib().linear_allreduce(ctx.h, _ptr(X), T, Kl, _ptr(W), Mo, ptrs, ldp, rptrs, tp,
+                                         self_rank, _ptr(send), _ptr(Y), flags, _stream(stream)))

@@ -64,6 +64,7 @@ struct rag_ctx {
   int max_tp = 0;
   hipStream_t side = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  hipEvent_t ev_ag = nullptr;          // linear_allreduce: end of the all-gather's copies
   std::vector<hipEvent_t> ev_chunk;   // split form: chunk j copied (created on first use)
   // device counters, kWordStride ints apart: ctr[max_tp] | copy-complete | arrival counts
   // [2 sets][grab, done][kArrSlots] | err
@@ -341,7 +342,8 @@ int ag_gemm_split(rag_ctx* c, const void* A, int M, int K, const void* const* B,
 // row stride.
 int rs_call(rag_ctx* c, const char* fn, bool ring, const void* X, int T, int Kl, const void* W,
             int Mo, const float* const* ptrs, long long ld, int tp, int self_rank, float* send,
-            void* D, int flags, void* stream_v) {
+            void* D, int flags, void* stream_v, bool validate_only = false,
+            bool other_copies_beside = false) {
   if (!c) return fail(RAG_EINVAL, "%s: ctx is NULL", fn);
   if (tp < 1 || tp > c->max_tp)
     return fail(RAG_EINVAL, "%s: tp=%d outside [1, %d] (max_tp of the context)", fn, tp,
@@ -403,6 +405,7 @@ int rs_call(rag_ctx* c, const char* fn, bool ring, const void* X, int T, int Kl,
     return fail(RAG_EINVAL, "%s: D and send must not overlap X, W or each other", fn);
   if (arrive && c->copy_engine == RAG_COPY_SDMA && c->delay_us > 0)
     return fail(RAG_EINVAL, "%s: the arrival delay hook needs the kernel copy engine", fn);
+  if (validate_only) return RAG_OK;
 
   HIPCHK(hipSetDevice(c->device));
   hipStream_t stream = (hipStream_t)stream_v;
@@ -493,7 +496,7 @@ int rs_call(rag_ctx* c, const char* fn, bool ring, const void* X, int T, int Kl,
     if (join) HIPCHK(hipEventRecord(c->ev_join, c->side));
   }
 
-  const bool beside = a.gated && c->copy_engine != RAG_COPY_SDMA;
+  const bool beside = (a.gated || other_copies_beside) && c->copy_engine != RAG_COPY_SDMA;
   int tile = choose_rs_tile(c, nc, Mo, tp);
   for (int t : {tile, (int)kTile256x128, (int)kTile128x128}) {
     if (!c->rs_info_ok[t]) {
@@ -571,6 +574,7 @@ int rag_create(rag_ctx** out, int device, int max_tp, int flags) {
   e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_ag, hipEventDisableTiming);
   if (e == hipSuccess) e = hipMalloc((void**)&c->words, nwords * sizeof(int));
   if (e == hipSuccess) e = hipMemset(c->words, 0, nwords * sizeof(int));
   if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -598,6 +602,7 @@ int rag_destroy(rag_ctx* c) {
   for (auto ev : c->ev_chunk) (void)hipEventDestroy(ev);
   if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
   if (c->ev_join) (void)hipEventDestroy(c->ev_join);
+  if (c->ev_ag) (void)hipEventDestroy(c->ev_ag);
   if (c->side) (void)hipStreamDestroy(c->side);
   if (c->words) (void)hipFree(c->words);
   if (c->gbuf) (void)hipFree(c->gbuf);
@@ -922,6 +927,94 @@ int gemm_rs_ring(rag_ctx* c, const void* X, int T, int Kl, const void* W, int Mo
                  void* D, int flags, void* stream_v) {
   return rs_call(c, "gemm_rs_ring", true, X, T, Kl, W, Mo, incoming, ldi, tp, self_rank, send, D,
                  flags, stream_v);
+}
+
+int linear_allreduce(rag_ctx* c, const void* X, int T, int Kl, const void* W, int Mo,
+                     const float* const* partials, long long ldp, const void* const* reduced,
+                     int tp, int self_rank, float* send, void* Y, int flags, void* stream_v) {
+  if (!c) return fail(RAG_EINVAL, "linear_allreduce: ctx is NULL");
+  if (tp < 1 || tp > c->max_tp || self_rank < 0 || self_rank >= tp || T < 1 || T % tp)
+    return fail(RAG_EINVAL, "linear_allreduce: tp=%d, self_rank=%d, T=%d do not fit (1 <= tp <= "
+                "%d, 0 <= self_rank < tp, T a multiple of tp)", tp, self_rank, T, c->max_tp);
+  if (Mo < 8 || Mo % 8) return fail(RAG_EINVAL, "linear_allreduce: Mo=%d must be a multiple of 8", Mo);
+  if (!Y || misaligned(Y)) return fail(RAG_EINVAL, "linear_allreduce: Y must be 16-byte aligned");
+  const int nc = T / tp;
+  const long long cbytes = (long long)nc * Mo * 2;   // one bf16 chunk
+  if (tp > 1 && !reduced)
+    return fail(RAG_EINVAL, "linear_allreduce: reduced must not be NULL for tp > 1");
+  HIPCHK(hipSetDevice(c->device));
+  if (!on_device(Y, c->device))
+    return fail(RAG_EINVAL, "linear_allreduce: Y is not device memory of device %d", c->device);
+  for (int r = 0; r < tp; ++r) {
+    if (r == self_rank) continue;
+    if (!reduced[r] || misaligned(reduced[r]))
+      return fail(RAG_EINVAL, "linear_allreduce: reduced[%d] is NULL or not 16-byte aligned", r);
+    if (!on_device(reduced[r], c->device))
+      return fail(RAG_EINVAL, "linear_allreduce: reduced[%d] is not device memory of device %d",
+                  r, c->device);
+    if (overlaps(Y, (long long)T * Mo * 2, reduced[r], cbytes))
+      return fail(RAG_EINVAL, "linear_allreduce: Y must not overlap reduced[%d]", r);
+  }
+  {
+    // everything the reduce-scatter checks, before anything is enqueued
+    const int rc = rs_call(c, "linear_allreduce", false, X, T, Kl, W, Mo, partials, ldp, tp,
+                           self_rank, send, (char*)Y + (size_t)self_rank * cbytes, flags, stream_v,
+                           true);
+    if (rc) return rc;
+    const long long ybytes = (long long)T * Mo * 2;
+    if (overlaps(Y, ybytes, X, (long long)T * Kl * 2) || overlaps(Y, ybytes, W, (long long)Mo * Kl * 2) ||
+        (send && overlaps(Y, ybytes, send, (long long)T * Mo * 4)))
+      return fail(RAG_EINVAL, "linear_allreduce: Y must not overlap X, W or send");
+    for (int p = 0; p < tp; ++p)
+      if (p != self_rank && overlaps(Y, ybytes, partials[p], ((long long)(T - 1) * ldp + Mo) * 4))
+        return fail(RAG_EINVAL, "linear_allreduce: Y must not overlap partials[%d]", p);
+  }
+  hipStream_t stream = (hipStream_t)stream_v;
+  // the all-gather: fork before the GEMM so that its copies run beside it
+  if (tp > 1) {
+    HIPCHK(hipEventRecord(c->ev_fork, stream));
+    HIPCHK(hipStreamWaitEvent(c->side, c->ev_fork, 0));
+    if (c->copy_engine == RAG_COPY_SDMA) {
+      for (int k = 1; k < tp; ++k) {
+        const int r = ((self_rank - k) % tp + tp) % tp;
+        HIPCHK(hipMemcpyAsync((char*)Y + (size_t)r * cbytes, reduced[r], (size_t)cbytes,
+                              hipMemcpyDeviceToDeviceNoCU, c->side));
+      }
+    } else {
+      ArrivalArgs aa = {};
+      int n = 0;
+      for (int k = 1; k < tp; ++k, ++n) {
+        const int r = ((self_rank - k) % tp + tp) % tp;
+        aa.cp.src[n] = reduced[r];
+        aa.cp.dst[n] = (char*)Y + (size_t)r * cbytes;
+        aa.cp.ctr_index[n] = -1;
+        aa.cp.pos[n] = k;
+      }
+      aa.cp.n_peer = n;
+      aa.cp.n = n;
+      aa.cp.bytes = (unsigned long long)cbytes;
+      aa.cp.piece_bytes = (unsigned)kArrivalThreads * 256u;
+      aa.cp.pieces = (unsigned)((aa.cp.bytes + aa.cp.piece_bytes - 1) / aa.cp.piece_bytes);
+      const unsigned set = c->arr_seq & 1u;
+      aa.cp.grab = c->arr + (size_t)set * 2 * kArrSlots * kWordStride;
+      aa.cp.done = aa.cp.grab + (size_t)kArrSlots * kWordStride;
+      aa.cp.clear_next = c->arr + (size_t)(set ^ 1u) * 2 * kArrSlots * kWordStride;
+      aa.ctr = c->ctr;
+      aa.epoch = c->epoch;
+      aa.raise_priority = c->copy_priority;
+      HIPCHK(launch_arrival(c->device, aa, c->comm_wgs, c->side));
+      c->arr_seq++;
+    }
+    HIPCHK(hipEventRecord(c->ev_ag, c->side));
+  }
+  // the reduce-scatter of the own chunk, written straight into its slot of Y (with the
+  // all-gather's copy kernel running beside it)
+  const int rc = rs_call(c, "linear_allreduce", false, X, T, Kl, W, Mo, partials, ldp, tp,
+                         self_rank, send, (char*)Y + (size_t)self_rank * cbytes, flags, stream_v,
+                         false, tp > 1);
+  if (rc) return rc;
+  if (tp > 1) HIPCHK(hipStreamWaitEvent(stream, c->ev_ag, 0));
+  return RAG_OK;
 }
 
 int rag_ag_kernel_name(rag_ctx* c, int nc, int M, int tp, rag_dtype dt, char* buf, int len) {

@@ -201,6 +201,20 @@ def make_rs_ring(shape: RSShape) -> RSRingInputs:
                         [t.to(torch.float32) for t in inc])
 
 
+def make_reduced_chunks(shape: RSShape) -> List[torch.Tensor]:
+    """The owners' reduced output chunks that an all-gather brings to this rank: tp bf16
+    [nc, Mo] tensors in increasing chunk index (the own entry is drawn too and ignored), from a
+    generator of their own so that make_rs's draws stay as they are."""
+    g = torch.Generator("cpu").manual_seed(shape.seed + 7919)
+    out = []
+    for _ in range(shape.tp):
+        if shape.dist == "normal_rs":
+            out.append((torch.randn((shape.nc, shape.Mo), generator=g) / 16.0).to(torch.bfloat16))
+        else:
+            out.append(_draw(g, (shape.nc, shape.Mo), shape.dist, shape.Kl).to(torch.bfloat16))
+    return out
+
+
 def ag_shape(tp, self_rank, nc, K, M, dtype="bf16", dist="uniform1", seed=7) -> AGShape:
     return AGShape(f"ag_tp{tp}_s{self_rank}_nc{nc}_k{K}_m{M}_{dtype}_{dist}", tp, self_rank, nc, K,
                    M, dtype, dist, seed)

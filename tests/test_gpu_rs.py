@@ -342,3 +342,36 @@ def test_rs_arrive_full_size_back_to_back(ring):
         ref = O.gemm_rs_rows(Xb, Wb, [None if p is None else p.numpy() for p in inp.partials],
                              shape.tp, shape.self_rank, rows)
     assert rel_err(W.bits_u16(run.D.cpu())[rows], ref) <= TOL_BF16
+
+
+# ------------------------------------------------------- row-parallel linear with all-reduce
+
+@pytest.mark.parametrize("engine", COPY_ENGINES)
+@pytest.mark.parametrize("tp,s", [(1, 0), (2, 1), (4, 2), (8, 7)])
+def test_linear_allreduce_exact(tp, s, engine):
+    """Y's own chunk is the reduce-scatter's sum (bit for bit on integers), every other chunk is
+    the owner's reduced chunk as given, bit for bit; send as for gemm_rs."""
+    c = ctx()
+    _engine(c, engine)
+    shape = W.rs_shape(tp, s, tp * 64, 128, 136, dist="int3", seed=900 + tp * 10 + s)
+    say(f"case linear_allreduce {shape.name} engine={engine}")
+    inp = W.make_rs(shape)
+    red = W.make_reduced_chunks(shape)
+    run = RSRun(inp)
+    red_dev = [t.to(DEV) for t in red]
+    Y = torch.full((shape.T, shape.Mo), float("nan"), dtype=torch.bfloat16, device=DEV)
+    B.linear_allreduce(c, run.X, run.W, run.partials, red_dev, tp, s, Y, send=run.send)
+    torch.cuda.synchronize()
+    c.check()
+    peers = [None if p is None else p.numpy() for p in inp.partials]
+    Y_ref, send_ref = O.linear_allreduce_step(W.bits_u16(inp.X), W.bits_u16(inp.W), peers,
+                                              [W.bits_u16(t) for t in red], tp, s)
+    got = W.bits_u16(Y.cpu())
+    nc = shape.nc
+    for cix in range(tp):
+        rows = slice(cix * nc, (cix + 1) * nc)
+        if cix == s:
+            assert np.array_equal(got[rows], O.f32_to_bf16(Y_ref[rows]))
+        else:
+            assert np.array_equal(got[rows], W.bits_u16(red[cix]))
+    _check_send(run, send_ref, exact=True)
