@@ -88,6 +88,44 @@ void oracle_e4m3fn_to_f32(const uint8_t* src, float* dst, long n) {
     }
 }
 
+/* fp32 -> OCP E4M3 (no-infinity variant) codes: saturate to +-448 (the largest finite value,
+ * code 0x7e), then round to the nearest representable value with ties to even mantissa.  From
+ * the format: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits; normals (1 + m/8) 2^(e-7)
+ * for e = 1..15 (e = 15, m = 7 is NaN), subnormals (m/8) 2^-6.  NaN keeps its sign: 0x7f / 0xff.
+ * The arithmetic is in double, where every step below is exact; nearbyint rounds ties to even in
+ * the default rounding mode. */
+void oracle_f32_to_e4m3fn_sat(const float* src, uint8_t* dst, long n) {
+    for (long i = 0; i < n; ++i) {
+        const float v = src[i];
+        const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+        if (isnan(v)) {
+            dst[i] = sign | 0x7f;
+            continue;
+        }
+        const double a = fabs((double)v);
+        if (a >= 448.0) {
+            dst[i] = sign | 0x7e;
+            continue;
+        }
+        if (a < ldexp(1.0, -6)) {
+            /* subnormal range: multiples of 2^-9; a count of 8 is the smallest normal, code 8 */
+            dst[i] = sign | (uint8_t)nearbyint(a / ldexp(1.0, -9));
+            continue;
+        }
+        int e2;
+        (void)frexp(a, &e2);               /* a = f * 2^e2, f in [0.5, 1) */
+        int E = e2 - 1;                    /* a = (1 + r) * 2^E, r in [0, 1) */
+        double q = nearbyint((a / ldexp(1.0, E) - 1.0) * 8.0);
+        if (q == 8.0) {
+            q = 0.0;
+            E += 1;
+        }
+        int code = ((E + 7) << 3) | (int)q;
+        if (code > 0x7e) code = 0x7e;
+        dst[i] = sign | (uint8_t)code;
+    }
+}
+
 /* out[n][m] = sum_k G[n][k] * A[m][k] for n in [0, N), m in [0, M).
  * G is [N, K] with row stride ldg, A is [M, K] with row stride lda, out is [N, M] with row stride
  * ldo (all in elements, row-major).  Plain triple loop, k ascending, separate multiply and add. */

@@ -53,6 +53,7 @@ def _load():
         lib.oracle_bf16_to_f32.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_long]
         lib.oracle_f32_to_bf16_rne.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_long]
         lib.oracle_e4m3fn_to_f32.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_long]
+        lib.oracle_f32_to_e4m3fn_sat.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_long]
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -95,6 +96,16 @@ def e4m3fn_to_f32(codes: np.ndarray) -> np.ndarray:
     src = np.ascontiguousarray(codes, dtype=np.uint8)
     out = np.empty(src.shape, dtype=np.float32)
     _load().oracle_e4m3fn_to_f32(src.ctypes.data, out.ctypes.data, src.size)
+    return out
+
+
+def f32_to_e4m3fn_sat(x: np.ndarray) -> np.ndarray:
+    """fp32 -> OCP E4M3 (no-infinity variant) codes, saturating to +-448 and rounding to nearest
+    with ties to even: the fp8 output of the GEMM ([TE-1583] listing: the output tensor carries its
+    own scale and amax, so D can be fp8).  Written from the format's definition in oracle.c."""
+    src = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(src.shape, dtype=np.uint8)
+    _load().oracle_f32_to_e4m3fn_sat(src.ctypes.data, out.ctypes.data, src.size)
     return out
 
 
@@ -369,3 +380,14 @@ def linear_allreduce_step(X_bits: np.ndarray, W_bits: np.ndarray,
     for c in range(tp):
         Y[c * nc:(c + 1) * nc] = D if c == self_rank else bf16_to_f32(reduced_bits[c])
     return Y, send
+
+
+def quantize_output_e4m3(D: np.ndarray, scale_D: float) -> Tuple[np.ndarray, float]:
+    """fp8 output epilogue: codes = E4M3(D * scale_D) with one fp32 multiply per element, and
+    amax = max |D| over the output before the scale.  [TE-1583] listing: the GEMM's output
+    buffer is built with D's amax and scale, so the GEMM quantises its own output and records the
+    absolute maximum for the next scaling."""
+    D = np.asarray(D, dtype=np.float32)
+    codes = f32_to_e4m3fn_sat((D * np.float32(scale_D)).astype(np.float32))
+    amax = float(np.max(np.abs(D))) if D.size else 0.0
+    return codes, amax

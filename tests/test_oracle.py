@@ -445,6 +445,47 @@ def test_linear_allreduce_equals_unsharded_linear():
                     assert np.array_equal(send[c].astype(np.int64), P[s][c * nc:(c + 1) * nc])
 
 
+def _torch_e4m3_codes(x):
+    t = torch.tensor(np.clip(np.asarray(x, np.float32), -448.0, 448.0))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_encode_matches_torch():
+    """The encoder against torch's own fp32 -> float8_e4m3fn cast (after the same clamp), over
+    normal, subnormal and saturating values."""
+    rng = np.random.default_rng(101)
+    x = np.concatenate([rng.uniform(-500, 500, 20000), rng.standard_normal(20000) * 0.01,
+                        rng.uniform(-2 ** -6, 2 ** -6, 20000),
+                        np.array([0.0, -0.0, 448.0, -448.0, 460.0, 1e30, -1e30])]).astype(np.float32)
+    assert np.array_equal(O.f32_to_e4m3fn_sat(x), _torch_e4m3_codes(x))
+
+
+def test_e4m3_round_trip_and_ties_to_even():
+    codes = np.array([c for c in range(256) if c not in (0x7f, 0xff)], np.uint8)
+    vals = O.e4m3fn_to_f32(codes)
+    assert np.array_equal(O.f32_to_e4m3fn_sat(vals), codes)
+    # midpoints between neighbouring positive codes go to the even mantissa
+    pos = np.arange(0, 0x7e, dtype=np.uint8)
+    lo, hi = O.e4m3fn_to_f32(pos), O.e4m3fn_to_f32(pos + 1)
+    mid = ((lo.astype(np.float64) + hi) / 2).astype(np.float32)
+    assert np.array_equal(mid.astype(np.float64), (lo.astype(np.float64) + hi) / 2)  # exact
+    got = O.f32_to_e4m3fn_sat(mid)
+    want = np.where(pos % 2 == 0, pos, pos + 1).astype(np.uint8)
+    assert np.array_equal(got, want)
+    # saturation and NaN
+    sat = O.f32_to_e4m3fn_sat(np.array([449.0, 1e6, -1e6, np.nan, -np.nan], np.float32))
+    assert list(sat[:3]) == [0x7e, 0x7e, 0xfe] and sat[3] & 0x7f == 0x7f
+
+
+def test_quantize_output_exact_on_integers():
+    D = np.array([[3.0, -5.0], [0.0, 96.0], [100.0, -300.0]], np.float32)
+    codes, amax = O.quantize_output_e4m3(D, 2.0)
+    assert amax == 300.0
+    # 200 lies halfway between 192 and 208 (mantissas 4 and 5): ties go to 192; -600 saturates
+    want = np.array([[6.0, -10.0], [0.0, 192.0], [192.0, -448.0]], np.float32)
+    assert np.array_equal(O.e4m3fn_to_f32(codes), want)
+
+
 # ------------------------------------------------------------------------------------ mutants
 
 def _pins_pass(gemm, gather, order_fn):
