@@ -199,6 +199,29 @@ RAG_API int ag_gemm(rag_ctx* ctx,
             int flags, void* stream);
 
 /*
+ * ag_gemm with the output and save options of the listing's call (TransformerEngine issue #1583,
+ * C++ listing: the output buffer carries D's amax and scale, and B_copy stores the rank's input
+ * chunk for the backward pass).  Arguments as for ag_gemm, plus:
+ *   d_dt      RAG_BF16 (D as in ag_gemm) or RAG_FP8_E4M3: D is [tp*nc, M] E4M3 codes,
+ *             code = E4M3(v * scale_D[0]) with v the GEMM result (for fp8 inputs already
+ *             multiplied by scale_A * scale_B), saturated to +-448, round to nearest even
+ *   scale_D   device fp32 scalar; required for fp8 output, NULL otherwise
+ *   amax_D    device fp32 scalar or NULL (fp8 output only): max |v| over D is max-reduced into
+ *             it (the caller sets its starting value, e.g. 0)
+ *   B_copy    device buffer [nc, K] in the input dtype, or NULL: receives this rank's chunk,
+ *             copied by the same engine as the arrivals (RAG_NO_COPY skips it with them)
+ * Errors: as ag_gemm.
+ */
+RAG_API int ag_gemm_ex(rag_ctx* ctx,
+            const void* A, int M, int K,
+            const void* const* B_chunks, int nc,
+            int tp, int self_rank,
+            void* G, void* D,
+            rag_dtype dt, const float* scale_A, const float* scale_B,
+            rag_dtype d_dt, const float* scale_D, float* amax_D, void* B_copy,
+            int flags, void* stream);
+
+/*
  * GEMM + reduce-scatter (row-parallel linear) for rank self_rank of a tp-rank ring:
  *     P     = X * W^T over all T rows            (this rank's partial of the full output, fp32)
  *     D     = sum over ranks p of P_p[rows of chunk self_rank]   (bf16 out)

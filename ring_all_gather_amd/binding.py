@@ -73,6 +73,8 @@ def lib():
     L.rag_set_option.argtypes = [vp, i, ll]
     L.ag_gemm.argtypes = [vp, vp, i, i, ctypes.POINTER(vp), i, i, i, vp, vp, i, vp, vp, i, vp]
     L.gemm_rs.argtypes = [vp, vp, i, i, vp, i, ctypes.POINTER(vp), ll, i, i, vp, vp, i, vp]
+    L.ag_gemm_ex.argtypes = [vp, vp, i, i, ctypes.POINTER(vp), i, i, i, vp, vp, i, vp, vp, i,
+                             vp, vp, vp, i, vp]
     L.gemm_rs_ring.argtypes = [vp, vp, i, i, vp, i, ctypes.POINTER(vp), ll, i, i, vp, vp, i, vp]
     L.linear_allreduce.argtypes = [vp, vp, i, i, vp, i, ctypes.POINTER(vp), ll,
                                    ctypes.POINTER(vp), i, i, vp, vp, i, vp]
@@ -82,7 +84,8 @@ def lib():
     L.rag_rs_kernel_name.argtypes = [vp, i, i, i, ctypes.c_char_p, i]
     L.rag_last_error.restype = ctypes.c_char_p
     L.rag_version.restype = i
-    for f in ("rag_create", "rag_destroy", "rag_set_option", "ag_gemm", "gemm_rs", "gemm_rs_ring",
+    for f in ("rag_create", "rag_destroy", "rag_set_option", "ag_gemm", "ag_gemm_ex", "gemm_rs",
+              "gemm_rs_ring",
               "linear_allreduce",
               "rag_check",
               "rag_kernel_times", "rag_ag_kernel_name", "rag_rs_kernel_name"):
@@ -208,8 +211,11 @@ class Context:
 def ag_gemm(ctx: Context, A: torch.Tensor, B_chunks: Sequence[torch.Tensor], tp: int,
             self_rank: int, D: torch.Tensor, G: Optional[torch.Tensor] = None,
             scale_A: Optional[torch.Tensor] = None, scale_B: Optional[torch.Tensor] = None,
-            flags: int = 0, stream=None) -> int:
-    """D = [B_0; ...; B_{tp-1}] A^T for rank self_rank of a tp-rank ring (see ringag.h)."""
+            flags: int = 0, stream=None, scale_D: Optional[torch.Tensor] = None,
+            amax_D: Optional[torch.Tensor] = None, B_copy: Optional[torch.Tensor] = None) -> int:
+    """D = [B_0; ...; B_{tp-1}] A^T for rank self_rank of a tp-rank ring (see ringag.h).  D is
+    bfloat16, or float8_e4m3fn with scale_D (and optionally amax_D); B_copy, if given, receives
+    this rank's chunk (these go through ag_gemm_ex)."""
     if len(B_chunks) != tp:
         raise ValueError(f"need tp={tp} chunks, got {len(B_chunks)}")
     fp8 = A.dtype == torch.float8_e4m3fn
@@ -220,14 +226,23 @@ def ag_gemm(ctx: Context, A: torch.Tensor, B_chunks: Sequence[torch.Tensor], tp:
     for b in B_chunks:
         if b.dtype != A.dtype or tuple(b.shape) != (nc, K):
             raise ValueError("every chunk must be [nc, K] with A's dtype")
-    if D.dtype != torch.bfloat16 or tuple(D.shape) != (tp * nc, M):
-        raise ValueError(f"D must be bfloat16 [{tp * nc}, {M}]")
+    out8 = D.dtype == torch.float8_e4m3fn
+    if (D.dtype != torch.bfloat16 and not out8) or tuple(D.shape) != (tp * nc, M):
+        raise ValueError(f"D must be bfloat16 or float8_e4m3fn [{tp * nc}, {M}]")
     if G is not None and (G.dtype != A.dtype or tuple(G.shape) != (tp * nc, K)):
         raise ValueError(f"G must be [{tp * nc}, {K}] with A's dtype")
+    if B_copy is not None and (B_copy.dtype != A.dtype or tuple(B_copy.shape) != (nc, K)):
+        raise ValueError(f"B_copy must be [{nc}, {K}] with A's dtype")
     ptrs = (ctypes.c_void_p * tp)(*[_ptr(b) for b in B_chunks])
-    return _check(lib().ag_gemm(ctx.h, _ptr(A), M, K, ptrs, nc, tp, self_rank, _ptr(G), _ptr(D),
-                                RAG_FP8_E4M3 if fp8 else RAG_BF16, _ptr(scale_A), _ptr(scale_B),
-                                flags, _stream(stream)))
+    dt = RAG_FP8_E4M3 if fp8 else RAG_BF16
+    if not out8 and scale_D is None and amax_D is None and B_copy is None:
+        return _check(lib().ag_gemm(ctx.h, _ptr(A), M, K, ptrs, nc, tp, self_rank, _ptr(G),
+                                    _ptr(D), dt, _ptr(scale_A), _ptr(scale_B), flags,
+                                    _stream(stream)))
+    return _check(lib().ag_gemm_ex(ctx.h, _ptr(A), M, K, ptrs, nc, tp, self_rank, _ptr(G), _ptr(D),
+                                   dt, _ptr(scale_A), _ptr(scale_B),
+                                   RAG_FP8_E4M3 if out8 else RAG_BF16, _ptr(scale_D),
+                                   _ptr(amax_D), _ptr(B_copy), flags, _stream(stream)))
 
 
 def _rs(fn, ctx: Context, X: torch.Tensor, W: torch.Tensor, entries, rows: int, skip: int,

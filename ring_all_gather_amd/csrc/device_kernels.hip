@@ -2,7 +2,8 @@
 // object (hipcc --genco).  The host side embeds that object and loads it explicitly per device
 // (launch.cpp), so the shared library holds no compiler-generated registration code.
 //
-// Entry points: rag_ag_<bf16|fp8>_<tile>, rag_rs_<tile>, rag_arrival.  Tile names:
+// Entry points: rag_ag_<bf16|fp8>[_o8]_<tile> (input dtype; _o8 = E4M3 output), rag_rs_<tile>,
+// rag_arrival.  Tile names:
 //   t128x128, t256x128, t256x256 (4 waves), t256x256w8 (8 waves, 2 stages), t256x256w8s4 (8 waves,
 //   4 stages); see gemm_core.hpp.
 #include "arrival_kernel.hpp"
@@ -13,10 +14,16 @@ using namespace ringag;
 
 #define RAG_AG_ENTRY(TILE, SHAPE)                                                            \
   extern "C" __global__ void __launch_bounds__(SHAPE::NT) rag_ag_bf16_##TILE(AgArgs a) {    \
-    ag_gemm_body<SHAPE, false>(a);                                                           \
+    ag_gemm_body<SHAPE, false, false>(a);                                                    \
   }                                                                                          \
   extern "C" __global__ void __launch_bounds__(SHAPE::NT) rag_ag_fp8_##TILE(AgArgs a) {     \
-    ag_gemm_body<SHAPE, true>(a);                                                            \
+    ag_gemm_body<SHAPE, true, false>(a);                                                     \
+  }                                                                                          \
+  extern "C" __global__ void __launch_bounds__(SHAPE::NT) rag_ag_bf16_o8_##TILE(AgArgs a) { \
+    ag_gemm_body<SHAPE, false, true>(a);                                                     \
+  }                                                                                          \
+  extern "C" __global__ void __launch_bounds__(SHAPE::NT) rag_ag_fp8_o8_##TILE(AgArgs a) {  \
+    ag_gemm_body<SHAPE, true, true>(a);                                                      \
   }                                                                                          \
   extern "C" __global__ void __launch_bounds__(SHAPE::NT) rag_rs_##TILE(RsArgs a) {         \
     gemm_rs_body<SHAPE>(a);                                                                  \

@@ -31,11 +31,12 @@ __device__ inline unsigned hw_location() {
   return (xcc << 16) | (se << 8) | cu;
 }
 
-template <class S, bool FP8>
+template <class S, bool FP8, bool OUT8>
 __device__ __forceinline__ void ag_gemm_body(const AgArgs& a) {
   __shared__ __attribute__((aligned(1024))) char lds[S::LDS];
   __shared__ int s_ok;
   __shared__ unsigned s_piece;
+  __shared__ float s_red[OUT8 ? S::NW : 1];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t ldb = (uint32_t)a.K * (FP8 ? 1u : 2u);
@@ -77,8 +78,22 @@ __device__ __forceinline__ void ag_gemm_body(const AgArgs& a) {
     tile_offsets<S, S::YQ>(yo, cb * S::BJ, a.M, ldb, wave, lane);
     f32x16 acc[S::FI][S::FJ];
     tile_kloop<S, FP8>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);
-    __bf16* out = (__bf16*)a.out[j] + (size_t)rb * S::BI * a.M + (size_t)cb * S::BJ;
-    store_tile_bf16<S>(acc, scale, lds, out, a.M, a.nc - rb * S::BI, a.M - cb * S::BJ, wave, lane);
+    if constexpr (OUT8) {
+      uint8_t* out = (uint8_t*)a.out[j] + (size_t)rb * S::BI * a.M + (size_t)cb * S::BJ;
+      const float m = store_tile_fp8<S>(acc, scale, a.scale_D[0], lds, out, a.M,
+                                        a.nc - rb * S::BI, a.M - cb * S::BJ, wave, lane);
+      if (a.amax_D) {
+        const float bm = block_max<S>(m, s_red, wave, lane);
+        // amax >= 0, so its bits order like unsigned integers (a NaN sorts above everything)
+        if (threadIdx.x == 0)
+          __hip_atomic_fetch_max((unsigned*)a.amax_D, __float_as_uint(bm), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      }
+    } else {
+      __bf16* out = (__bf16*)a.out[j] + (size_t)rb * S::BI * a.M + (size_t)cb * S::BJ;
+      store_tile_bf16<S>(acc, scale, lds, out, a.M, a.nc - rb * S::BI, a.M - cb * S::BJ, wave,
+                         lane);
+    }
     if (tr && threadIdx.x == 0) {
       tr[2] = wall_clock64();
       tr[3] = ((unsigned long long)blockIdx.x << 32) | hw_location();

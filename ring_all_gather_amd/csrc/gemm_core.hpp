@@ -298,4 +298,64 @@ __device__ inline void store_tile_bf16(const f32x16 (&acc)[S::FI][S::FJ], float 
   __syncthreads();
 }
 
+// Epilogue for fp8 (OCP E4M3) output.  v = acc * scale is the GEMM's result; the code is
+// E4M3(v * scale_d), saturated to +-448 and rounded to nearest even by the hardware convert; the
+// codes are staged through LDS and written out 16 bytes at a time.  Returns this thread's
+// max |v| (its share of the output's amax).  Ends with a barrier (LDS free again).
+template <class S>
+__device__ inline float store_tile_fp8(const f32x16 (&acc)[S::FI][S::FJ], float scale,
+                                       float scale_d, char* lds, uint8_t* out, int ld,
+                                       int rows_valid, int cols_valid, int wave, int lane) {
+  constexpr int LD8 = S::BJ + 16;
+  const int wi = wave / S::WJ, wj = wave % S::WJ;
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < S::FI; ++i)
+#pragma unroll
+    for (int j = 0; j < S::FJ; ++j) {
+      const int col = wj * S::TN + acc_col(j, lane);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = wi * S::TM + acc_row(i, e, lane);
+        const float v = acc[i][j][e] * scale;
+        amax = fmaxf(amax, fabsf(v));
+        float q = v * scale_d;
+        if (!__builtin_isnan(q)) q = fminf(fmaxf(q, -448.0f), 448.0f);
+        lds[row * LD8 + col] = (char)(__builtin_amdgcn_cvt_pk_fp8_f32(q, 0.0f, 0, false) & 0xff);
+      }
+    }
+  __syncthreads();
+  constexpr int OSEGS = S::BJ / 16;   // 16-byte segments per tile row
+  const bool vec = (ld % 16) == 0 && (((uintptr_t)out) & 15u) == 0;
+  for (int idx = threadIdx.x; idx < S::BI * OSEGS; idx += S::NT) {
+    const int r = idx / OSEGS, sg = idx % OSEGS;
+    const int c = sg * 16;
+    if (r >= rows_valid || c >= cols_valid) continue;
+    const char* src = lds + r * LD8 + c;
+    uint8_t* dst = out + (size_t)r * ld + c;
+    if (vec && c + 16 <= cols_valid) {
+      *(i32x4*)dst = *(const i32x4*)src;
+    } else {
+      for (int e = 0; e < 16 && c + e < cols_valid; ++e) dst[e] = (uint8_t)src[e];
+    }
+  }
+  __syncthreads();
+  return amax;
+}
+
+// Max of v over the workgroup's threads; the result is valid in thread 0.  `red` is an LDS array
+// of one float per wave.
+template <class S>
+__device__ inline float block_max(float v, float* red, int wave, int lane) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float m = 0.0f;
+  if (threadIdx.x == 0)
+    for (int w = 0; w < S::NW; ++w) m = fmaxf(m, red[w]);
+  __syncthreads();
+  return m;
+}
+
 }  // namespace ringag

@@ -66,6 +66,9 @@ struct AgArgs {
   const float* scale_B;
   int tiles_i, tiles_j;          // tile grid of one chunk
   unsigned long long* trace;     // optional per-tile stamps (kTraceTileWords per tile), or null
+  int out_fp8;                   // 1 = D is E4M3: code = E4M3(acc * scale * scale_D[0])
+  const float* scale_D;          // fp8 output: quantisation factor (device scalar)
+  float* amax_D;                 // fp8 output, optional: max |acc * scale| is max-reduced into it
   int copies;                    // 1 = this kernel also runs the copies of `cp`
   int copy_stride;               // workgroups w with (w / 8) % copy_stride == 0 copy
   int compute;                   // 0 = copies only, no tiles
@@ -140,11 +143,11 @@ hipError_t launch_gemm_rs(int device, const RsArgs& a, int tile, int grid, hipSt
 hipError_t launch_arrival(int device, const ArrivalArgs& a, int grid, hipStream_t stream);
 
 // Entry-point names (launch.cpp).
-const char* ag_kernel_name(int tile, bool fp8);
+const char* ag_kernel_name(int tile, bool fp8, bool out8 = false);
 const char* rs_kernel_name(int tile);
 
 // Occupancy / resource facts for a kernel variant (cached by the caller).
-hipError_t ag_kernel_info(int device, int tile, bool fp8, KernelInfo* info);
+hipError_t ag_kernel_info(int device, int tile, bool fp8, bool out8, KernelInfo* info);
 hipError_t rs_kernel_info(int device, int tile, KernelInfo* info);
 
 constexpr int kArrivalThreads = 256;   // block size of the arrival kernel

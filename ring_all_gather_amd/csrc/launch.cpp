@@ -20,11 +20,15 @@ namespace {
 constexpr int kMaxDevices = 64;
 constexpr int kTiles = 6;   // tile ids 1..5
 
-const char* const kAgName[2][kTiles] = {
-    {nullptr, "rag_ag_bf16_t128x128", "rag_ag_bf16_t256x128", "rag_ag_bf16_t256x256",
-     "rag_ag_bf16_t256x256w8", "rag_ag_bf16_t256x256w8s4"},
-    {nullptr, "rag_ag_fp8_t128x128", "rag_ag_fp8_t256x128", "rag_ag_fp8_t256x256",
-     "rag_ag_fp8_t256x256w8", "rag_ag_fp8_t256x256w8s4"}};
+const char* const kAgName[2][2][kTiles] = {   // [fp8 input][fp8 output][tile]
+    {{nullptr, "rag_ag_bf16_t128x128", "rag_ag_bf16_t256x128", "rag_ag_bf16_t256x256",
+      "rag_ag_bf16_t256x256w8", "rag_ag_bf16_t256x256w8s4"},
+     {nullptr, "rag_ag_bf16_o8_t128x128", "rag_ag_bf16_o8_t256x128", "rag_ag_bf16_o8_t256x256",
+      "rag_ag_bf16_o8_t256x256w8", "rag_ag_bf16_o8_t256x256w8s4"}},
+    {{nullptr, "rag_ag_fp8_t128x128", "rag_ag_fp8_t256x128", "rag_ag_fp8_t256x256",
+      "rag_ag_fp8_t256x256w8", "rag_ag_fp8_t256x256w8s4"},
+     {nullptr, "rag_ag_fp8_o8_t128x128", "rag_ag_fp8_o8_t256x128", "rag_ag_fp8_o8_t256x256",
+      "rag_ag_fp8_o8_t256x256w8", "rag_ag_fp8_o8_t256x256w8s4"}}};
 const char* const kRsName[kTiles] = {nullptr, "rag_rs_t128x128", "rag_rs_t256x128",
                                      "rag_rs_t256x256", "rag_rs_t256x256w8",
                                      "rag_rs_t256x256w8s4"};
@@ -32,7 +36,7 @@ const char* const kRsName[kTiles] = {nullptr, "rag_rs_t128x128", "rag_rs_t256x12
 struct DeviceKernels {
   bool loaded = false;
   hipModule_t module = nullptr;
-  hipFunction_t ag[2][kTiles] = {};
+  hipFunction_t ag[2][2][kTiles] = {};
   hipFunction_t rs[kTiles] = {};
   hipFunction_t arrival = nullptr;
 };
@@ -64,8 +68,8 @@ hipError_t info(hipFunction_t f, int threads, KernelInfo* out) {
 
 }  // namespace
 
-const char* ag_kernel_name(int tile, bool fp8) {
-  return valid_tile(tile) ? kAgName[fp8 ? 1 : 0][tile] : "";
+const char* ag_kernel_name(int tile, bool fp8, bool out8) {
+  return valid_tile(tile) ? kAgName[fp8 ? 1 : 0][out8 ? 1 : 0][tile] : "";
 }
 
 const char* rs_kernel_name(int tile) { return valid_tile(tile) ? kRsName[tile] : ""; }
@@ -81,8 +85,10 @@ hipError_t load_kernels(int device) {
   e = hipModuleLoadData(&m, ringag_kernels_co);
   if (e != hipSuccess) return e;
   for (int fp8 = 0; fp8 < 2; ++fp8)
-    for (int t = 1; t < kTiles; ++t)
-      if ((e = hipModuleGetFunction(&d.ag[fp8][t], m, kAgName[fp8][t])) != hipSuccess) return e;
+    for (int o8 = 0; o8 < 2; ++o8)
+      for (int t = 1; t < kTiles; ++t)
+        if ((e = hipModuleGetFunction(&d.ag[fp8][o8][t], m, kAgName[fp8][o8][t])) != hipSuccess)
+          return e;
   for (int t = 1; t < kTiles; ++t)
     if ((e = hipModuleGetFunction(&d.rs[t], m, kRsName[t])) != hipSuccess) return e;
   if ((e = hipModuleGetFunction(&d.arrival, m, "rag_arrival")) != hipSuccess) return e;
@@ -93,10 +99,11 @@ hipError_t load_kernels(int device) {
 
 hipError_t launch_ag_gemm(int device, const AgArgs& a, int tile, bool fp8, int grid,
                           hipStream_t s) {
+  const int o8 = a.out_fp8 ? 1 : 0;
   if (device < 0 || device >= kMaxDevices || !g_dev[device].loaded || !valid_tile(tile))
     return hipErrorInvalidValue;
   AgArgs copy = a;
-  return launch(g_dev[device].ag[fp8 ? 1 : 0][tile], grid, tile_threads(tile), s, &copy);
+  return launch(g_dev[device].ag[fp8 ? 1 : 0][o8][tile], grid, tile_threads(tile), s, &copy);
 }
 
 hipError_t launch_gemm_rs(int device, const RsArgs& a, int tile, int grid, hipStream_t s) {
@@ -112,10 +119,10 @@ hipError_t launch_arrival(int device, const ArrivalArgs& a, int grid, hipStream_
   return launch(g_dev[device].arrival, grid, kArrivalThreads, s, &copy);
 }
 
-hipError_t ag_kernel_info(int device, int tile, bool fp8, KernelInfo* out) {
+hipError_t ag_kernel_info(int device, int tile, bool fp8, bool out8, KernelInfo* out) {
   if (device < 0 || device >= kMaxDevices || !g_dev[device].loaded || !valid_tile(tile))
     return hipErrorInvalidValue;
-  return info(g_dev[device].ag[fp8 ? 1 : 0][tile], tile_threads(tile), out);
+  return info(g_dev[device].ag[fp8 ? 1 : 0][out8 ? 1 : 0][tile], tile_threads(tile), out);
 }
 
 hipError_t rs_kernel_info(int device, int tile, KernelInfo* out) {

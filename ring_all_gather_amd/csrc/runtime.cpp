@@ -98,8 +98,8 @@ struct rag_ctx {
   std::vector<hipEvent_t> t_start, t_stop;
   int n_timed = 0;
   // occupancy cache: [tile][fp8]
-  KernelInfo ag_info[6][2] = {};
-  bool ag_info_ok[6][2] = {};
+  KernelInfo ag_info[6][2][2] = {};   // [tile][fp8 input][fp8 output]
+  bool ag_info_ok[6][2][2] = {};
   KernelInfo rs_info[6] = {};
   bool rs_info_ok[6] = {};
 };
@@ -213,9 +213,9 @@ namespace {
 
 // Staged output (RAG_STAGED_OUT): slot j of the staging buffer holds the chunk at ring position j;
 // move the slots to D's rank offsets.
-int finalize_staged(rag_ctx* c, void* D, int nc, int M, int tp, const int* order,
+int finalize_staged(rag_ctx* c, void* D, int nc, int M, int tp, const int* order, int oesz,
                     hipStream_t stream) {
-  const size_t dchunk = (size_t)nc * M * 2;
+  const size_t dchunk = (size_t)nc * M * oesz;
   char* st = (char*)c->stage;
   bool rotation = true;   // slot j holds chunk j-1 and slot 0 chunk tp-1
   for (int j = 0; j < tp; ++j)
@@ -239,8 +239,9 @@ int finalize_staged(rag_ctx* c, void* D, int nc, int M, int tp, const int* order
 // for the side stream's end before the call's later work.
 int ag_gemm_split(rag_ctx* c, const void* A, int M, int K, const void* const* B, int nc, int tp,
                   int self_rank, char* Gp, bool own_copy, void* D, bool fp8, const float* scale_A,
-                  const float* scale_B, bool staged, bool no_copy, bool copy_only,
-                  long long chunk_bytes, const int* order, int epoch, hipStream_t stream) {
+                  const float* scale_B, bool out8, const float* scale_D, float* amax_D,
+                  void* B_copy, bool staged, bool no_copy, bool copy_only, long long chunk_bytes,
+                  const int* order, int epoch, hipStream_t stream) {
   if (c->ev_chunk.empty()) {
     c->ev_chunk.resize(c->max_tp, nullptr);
     for (auto& ev : c->ev_chunk) HIPCHK(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
@@ -248,17 +249,20 @@ int ag_gemm_split(rag_ctx* c, const void* A, int M, int K, const void* const* B,
   if (!no_copy) {
     HIPCHK(hipEventRecord(c->ev_fork, stream));
     HIPCHK(hipStreamWaitEvent(c->side, c->ev_fork, 0));
-    for (int j = 1; j <= tp; ++j) {   // j == tp: the own chunk into G
+    for (int j = 1; j <= tp + 1; ++j) {   // j == tp: the own chunk into G, j == tp+1: B_copy
       const void* src;
       void* dst;
       if (j < tp) {
         src = B[order[j]];
         dst = Gp + (size_t)order[j] * chunk_bytes;
-      } else if (own_copy) {
+      } else if (j == tp && own_copy) {
         src = B[self_rank];
         dst = Gp + (size_t)self_rank * chunk_bytes;
+      } else if (j == tp + 1 && B_copy) {
+        src = B[self_rank];
+        dst = B_copy;
       } else {
-        break;
+        continue;
       }
       if (c->copy_engine == RAG_COPY_SDMA) {
         HIPCHK(hipMemcpyAsync(dst, src, (size_t)chunk_bytes, hipMemcpyDeviceToDeviceNoCU,
@@ -291,9 +295,9 @@ int ag_gemm_split(rag_ctx* c, const void* A, int M, int K, const void* const* B,
   }
   if (!copy_only) {
     const int tile = choose_ag_tile(c, nc, M, 1);
-    if (!c->ag_info_ok[tile][fp8]) {
-      HIPCHK(ag_kernel_info(c->device, tile, fp8, &c->ag_info[tile][fp8]));
-      c->ag_info_ok[tile][fp8] = true;
+    if (!c->ag_info_ok[tile][fp8][out8]) {
+      HIPCHK(ag_kernel_info(c->device, tile, fp8, out8, &c->ag_info[tile][fp8][out8]));
+      c->ag_info_ok[tile][fp8][out8] = true;
     }
     int bi, bj;
     tile_dims(tile, &bi, &bj);
@@ -315,10 +319,13 @@ int ag_gemm_split(rag_ctx* c, const void* A, int M, int K, const void* const* B,
     a.tiles_j = (M + bj - 1) / bj;
     a.compute = 1;
     a.copy_stride = 1;
-    int bpc = c->ag_info[tile][fp8].max_blocks_per_cu;
+    a.out_fp8 = out8 ? 1 : 0;
+    a.scale_D = scale_D;
+    a.amax_D = amax_D;
+    int bpc = c->ag_info[tile][fp8][out8].max_blocks_per_cu;
     if (c->wgs_per_cu > 0) bpc = std::min(bpc, c->wgs_per_cu);
     const int grid = persistent_grid(a.tiles_i * a.tiles_j, c->num_cus, bpc);
-    const size_t dchunk = (size_t)nc * M * 2;
+    const size_t dchunk = (size_t)nc * M * (out8 ? 1 : 2);
     bool rec = false;
     int rc = record_timing_start(c, stream, &rec);
     if (rc) return rc;
@@ -683,6 +690,14 @@ int rag_set_option(rag_ctx* c, int key, long long v) {
 int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int nc, int tp,
             int self_rank, void* G, void* D, rag_dtype dt, const float* scale_A,
             const float* scale_B, int flags, void* stream_v) {
+  return ag_gemm_ex(c, A, M, K, B, nc, tp, self_rank, G, D, dt, scale_A, scale_B, RAG_BF16,
+                    nullptr, nullptr, nullptr, flags, stream_v);
+}
+
+int ag_gemm_ex(rag_ctx* c, const void* A, int M, int K, const void* const* B, int nc, int tp,
+               int self_rank, void* G, void* D, rag_dtype dt, const float* scale_A,
+               const float* scale_B, rag_dtype d_dt, const float* scale_D, float* amax_D,
+               void* B_copy, int flags, void* stream_v) {
   if (!c) return fail(RAG_EINVAL, "ag_gemm: ctx is NULL");
   if (tp < 1 || tp > c->max_tp)
     return fail(RAG_EINVAL, "ag_gemm: tp=%d outside [1, %d] (max_tp of the context)", tp, c->max_tp);
@@ -712,11 +727,20 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
     return fail(RAG_EINVAL, "ag_gemm: fp8 needs scale_A and scale_B");
   if (!fp8 && (scale_A || scale_B))
     return fail(RAG_EINVAL, "ag_gemm: scales are only meaningful for fp8; pass NULL for bf16");
+  if (d_dt != RAG_BF16 && d_dt != RAG_FP8_E4M3)
+    return fail(RAG_EINVAL, "ag_gemm: unknown output dtype %d", d_dt);
+  const bool out8 = d_dt == RAG_FP8_E4M3;
+  const int oesz = out8 ? 1 : 2;
+  if (out8 && !scale_D) return fail(RAG_EINVAL, "ag_gemm: fp8 output needs scale_D");
+  if (!out8 && (scale_D || amax_D))
+    return fail(RAG_EINVAL, "ag_gemm: scale_D and amax_D are only meaningful for fp8 output");
+  if ((amax_D && (reinterpret_cast<uintptr_t>(amax_D) & 3u)) || (B_copy && misaligned(B_copy)))
+    return fail(RAG_EINVAL, "ag_gemm: amax_D must be 4-byte and B_copy 16-byte aligned");
   {
     HIPCHK(hipSetDevice(c->device));
-    const void* named[] = {A, D, G, scale_A, scale_B};
-    const char* names[] = {"A", "D", "G", "scale_A", "scale_B"};
-    for (int i = 0; i < 5; ++i)
+    const void* named[] = {A, D, G, scale_A, scale_B, scale_D, amax_D, B_copy};
+    const char* names[] = {"A", "D", "G", "scale_A", "scale_B", "scale_D", "amax_D", "B_copy"};
+    for (int i = 0; i < 8; ++i)
       if (named[i] && !on_device(named[i], c->device))
         return fail(RAG_EINVAL, "ag_gemm: %s is not device memory of device %d", names[i],
                     c->device);
@@ -728,7 +752,7 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
   const long long a_bytes = (long long)M * K * esz;
   const long long chunk_bytes = (long long)nc * K * esz;
   const long long g_bytes = chunk_bytes * tp;
-  const long long d_bytes = (long long)tp * nc * M * 2;
+  const long long d_bytes = (long long)tp * nc * M * oesz;
   if (a_bytes > kMaxOperandBytes || chunk_bytes > kMaxOperandBytes)
     return fail(RAG_EINVAL, "ag_gemm: the weight (%lld B) and each chunk (%lld B) must be < 2 GiB",
                 a_bytes, chunk_bytes);
@@ -739,6 +763,14 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
     if (overlaps(D, d_bytes, B[r], chunk_bytes) ||
         (G && r != self_rank && overlaps(G, g_bytes, B[r], chunk_bytes)))
       return fail(RAG_EINVAL, "ag_gemm: G and D must not overlap B_chunks[%d]", r);
+  if (B_copy) {
+    if (overlaps(B_copy, chunk_bytes, A, a_bytes) || overlaps(B_copy, chunk_bytes, D, d_bytes) ||
+        (G && overlaps(B_copy, chunk_bytes, G, g_bytes)))
+      return fail(RAG_EINVAL, "ag_gemm: B_copy must not overlap A, G or D");
+    for (int r = 0; r < tp; ++r)
+      if (overlaps(B_copy, chunk_bytes, B[r], chunk_bytes))
+        return fail(RAG_EINVAL, "ag_gemm: B_copy must not overlap B_chunks[%d]", r);
+  }
   if (G && overlaps(G, g_bytes, B[self_rank], chunk_bytes) &&
       (const char*)B[self_rank] != (const char*)G + (size_t)self_rank * chunk_bytes)
     return fail(RAG_EINVAL, "ag_gemm: the own chunk may only sit in G at its own slot");
@@ -762,7 +794,7 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
   // the own chunk also goes into G (after the peers' chunks) unless it is already there
   const bool own_copy = G && (const char*)B[self_rank] != Gp + (size_t)self_rank * chunk_bytes;
   if (staged && !copy_only) {
-    int rc = ensure_buffer(&c->stage, &c->stage_bytes, (size_t)(tp + 1) * nc * M * 2,
+    int rc = ensure_buffer(&c->stage, &c->stage_bytes, (size_t)(tp + 1) * nc * M * oesz,
                            "staging buffer");
     if (rc) return rc;
   }
@@ -780,10 +812,10 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
 
   if (flags & RAG_PER_CHUNK) {
     const int rc = ag_gemm_split(c, A, M, K, B, nc, tp, self_rank, Gp, own_copy, D, fp8, scale_A,
-                                 scale_B, staged, no_copy, copy_only, chunk_bytes, order, epoch,
-                                 stream);
+                                 scale_B, out8, scale_D, amax_D, B_copy, staged, no_copy,
+                                 copy_only, chunk_bytes, order, epoch, stream);
     if (rc) return rc;
-    return staged && !copy_only ? finalize_staged(c, D, nc, M, tp, order, stream) : RAG_OK;
+    return staged && !copy_only ? finalize_staged(c, D, nc, M, tp, order, oesz, stream) : RAG_OK;
   }
 
   // The copies of the simulated arrival: the peers' chunks in ring order, then the own chunk
@@ -805,8 +837,16 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
     if (own_copy) {
       cp.src[n] = B[self_rank];
       cp.dst[n] = Gp + (size_t)self_rank * chunk_bytes;
-      // the GEMM waits for it before exiting only when the copies run beside it
-      cp.ctr_index[n] = (copy_only || in_kernel) ? -1 : c->max_tp;
+      // the GEMM waits for it before exiting only when the copies run beside it (with B_copy
+      // too, the caller's stream waits for the side stream instead)
+      cp.ctr_index[n] = (copy_only || in_kernel || B_copy) ? -1 : c->max_tp;
+      cp.pos[n] = 0;
+      ++n;
+    }
+    if (B_copy) {   // this rank's chunk saved for the backward pass
+      cp.src[n] = B[self_rank];
+      cp.dst[n] = B_copy;
+      cp.ctr_index[n] = -1;
       cp.pos[n] = 0;
       ++n;
     }
@@ -847,8 +887,9 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
       }
     }
     // With a GEMM the join is on the device (its workgroups wait for the last copy before they
-    // exit); without one the caller's stream waits for the side stream's end.
-    if (copy_only) HIPCHK(hipEventRecord(c->ev_join, c->side));
+    // exit); without one, or with B_copy (two copies after the peers', completing in any order),
+    // the caller's stream waits for the side stream's end.
+    if (copy_only || B_copy) HIPCHK(hipEventRecord(c->ev_join, c->side));
   }
 
   if (!copy_only || in_kernel) {
@@ -857,8 +898,8 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
       const int r = order[j];
       a.chunk[j] = (j == 0) ? B[self_rank] : (const void*)(Gp + (size_t)r * chunk_bytes);
       a.ctr_index[j] = (j == 0 || no_copy) ? -1 : r;
-      a.out[j] = (staged && !copy_only) ? (void*)((char*)c->stage + (size_t)j * nc * M * 2)
-                                        : (void*)((char*)D + (size_t)r * nc * M * 2);
+      a.out[j] = (staged && !copy_only) ? (void*)((char*)c->stage + (size_t)j * nc * M * oesz)
+                                        : (void*)((char*)D + (size_t)r * nc * M * oesz);
     }
     a.A = A;
     a.M = M;
@@ -866,7 +907,7 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
     a.nc = nc;
     a.tp = tp;
     a.ctr = c->ctr;
-    a.join_index = (own_copy && !no_copy && !in_kernel) ? c->max_tp : -1;
+    a.join_index = (own_copy && !no_copy && !in_kernel && !B_copy) ? c->max_tp : -1;
     a.epoch = epoch;
     a.err = c->err;
     a.spin_limit = c->spin_us * c->wall_khz / 1000;
@@ -875,21 +916,24 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
     a.trace = trace ? trace + kTraceHeader : nullptr;
     a.copies = in_kernel && cp.n > 0;
     a.compute = copy_only ? 0 : 1;
+    a.out_fp8 = out8 ? 1 : 0;
+    a.scale_D = scale_D;
+    a.amax_D = amax_D;
     a.cp = cp;
     int bi, bj;
     tile_dims(tile, &bi, &bj);
     a.tiles_i = (nc + bi - 1) / bi;
     a.tiles_j = (M + bj - 1) / bj;
-    if (!c->ag_info_ok[tile][fp8]) {
-      HIPCHK(ag_kernel_info(c->device, tile, fp8, &c->ag_info[tile][fp8]));
-      c->ag_info_ok[tile][fp8] = true;
+    if (!c->ag_info_ok[tile][fp8][out8]) {
+      HIPCHK(ag_kernel_info(c->device, tile, fp8, out8, &c->ag_info[tile][fp8][out8]));
+      c->ag_info_ok[tile][fp8][out8] = true;
     }
     const int total = a.tiles_i * a.tiles_j * tp;
-    int bpc = c->ag_info[tile][fp8].max_blocks_per_cu;
+    int bpc = c->ag_info[tile][fp8][out8].max_blocks_per_cu;
     if (c->wgs_per_cu > 0) bpc = std::min(bpc, c->wgs_per_cu);
     const bool beside = !no_copy && c->copy_engine == RAG_COPY_KERNEL;
     const int grid =
-        persistent_grid(total, c->num_cus - reserved_cus(c->ag_info[tile][fp8], beside), bpc);
+        persistent_grid(total, c->num_cus - reserved_cus(c->ag_info[tile][fp8][out8], beside), bpc);
     // in-kernel copies: workgroups w with (w / 8) % copy_stride == 0 take part (workgroup 0 always)
     a.copy_stride = 1;
     if (a.copies && c->gemm_copy_wgs > 0 && grid >= 8)
@@ -899,8 +943,8 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
               "(blocks/CU %d, VGPRs %d, LDS %d) engine=%s comm_wgs=%d pieces=%ux%u B "
               "flags=0x%x epoch=%d\n",
               tp, self_rank, nc, K, M, fp8 ? "fp8" : "bf16", bi, bj, total, grid,
-              c->ag_info[tile][fp8].max_blocks_per_cu, c->ag_info[tile][fp8].vgprs_per_wave,
-              c->ag_info[tile][fp8].lds_bytes, engine_name(c->copy_engine),
+              c->ag_info[tile][fp8][out8].max_blocks_per_cu, c->ag_info[tile][fp8][out8].vgprs_per_wave,
+              c->ag_info[tile][fp8][out8].lds_bytes, engine_name(c->copy_engine),
               c->comm_wgs, cp.pieces, cp.piece_bytes, flags, epoch);
     bool rec = false;
     int rc = record_timing_start(c, stream, &rec);
@@ -910,9 +954,10 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
     rc = record_timing_stop(c, stream, rec);
     if (rc) return rc;
   }
-  if (!no_copy && !in_kernel && copy_only) HIPCHK(hipStreamWaitEvent(stream, c->ev_join, 0));
+  if (!no_copy && !in_kernel && (copy_only || B_copy))
+    HIPCHK(hipStreamWaitEvent(stream, c->ev_join, 0));
 
-  return staged && !copy_only ? finalize_staged(c, D, nc, M, tp, order, stream) : RAG_OK;
+  return staged && !copy_only ? finalize_staged(c, D, nc, M, tp, order, oesz, stream) : RAG_OK;
 }
 
 int gemm_rs(rag_ctx* c, const void* X, int T, int Kl, const void* W, int Mo,

@@ -11,7 +11,8 @@ def test_header_declares_the_boundary():
     names = B.declared_functions()
     for f in ("rag_create", "rag_destroy", "rag_set_option", "ag_gemm", "gemm_rs", "rag_check",
               "rag_kernel_times", "rag_last_error", "rag_version", "rag_ag_kernel_name",
-              "rag_rs_kernel_name", "gemm_rs_ring", "linear_allreduce"):
+              "rag_rs_kernel_name", "gemm_rs_ring", "linear_allreduce",
+              "ag_gemm_ex"):
         assert f in names
 
 

@@ -7,7 +7,7 @@ from oracle import ringag_oracle as O
 from ring_all_gather_amd import binding as B
 from ring_all_gather_amd import workloads as W
 
-from gpu_common import (AGRun, TOL_BF16, TOL_FP8, ctx, oracle_ag, oracle_ag_rows, rel_err,
+from gpu_common import (DEV, AGRun, TOL_BF16, TOL_FP8, ctx, oracle_ag, oracle_ag_rows, rel_err,
                         reset_options, sampled_rows, say)
 
 pytestmark = pytest.mark.gpu
@@ -306,3 +306,96 @@ def test_ag_split_form_flags_and_gating():
         run.run(c, flags=B.RAG_PER_CHUNK)
         assert np.array_equal(run.D_bits(), want)
     c.check()
+
+
+# --------------------------------------------------------- fp8 output (amax, scale) and B_copy
+
+def _fp8_out_run(inp, c, scale_d, flags=0, with_copy=True):
+    s = inp.shape
+    run = AGRun(inp)
+    D8 = torch.zeros((s.N, s.M), dtype=torch.float8_e4m3fn, device=DEV)
+    sD = torch.tensor([scale_d], dtype=torch.float32, device=DEV)
+    amax = torch.zeros(1, dtype=torch.float32, device=DEV)
+    bc = torch.zeros_like(run.chunks[s.self_rank]) if with_copy else None
+    B.ag_gemm(c, run.A, run.chunks, s.tp, s.self_rank, D8, G=run.G, scale_A=run.sA,
+              scale_B=run.sB, flags=flags, scale_D=sD, amax_D=amax, B_copy=bc)
+    torch.cuda.synchronize()
+    c.check()
+    return run, W.bits_u8(D8.cpu()), float(amax.cpu()[0]), bc
+
+
+@pytest.mark.parametrize("engine", ENGINES + ["sdma"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_ag_fp8_output_exact_integers(dtype, engine):
+    """fp8 output: codes = E4M3(result * scale_D) bit for bit on integer data (the result is exact,
+    so both sides round the same value), amax = max |result|, B_copy = this rank's chunk."""
+    c = ctx()
+    set_engine(c, engine)
+    for tp, s, nc in ((4, 1, 256), (3, 2, 300), (1, 0, 48)):
+        inp = W.make_ag(W.ag_shape(tp, s, nc, 256, 160, dtype=dtype, dist="int3",
+                                   seed=1100 + tp * 10 + s))
+        say(f"case fp8-out {dtype} tp={tp} s={s} nc={nc} engine={engine}")
+        run, codes, amax, bc = _fp8_out_run(inp, c, 0.75)
+        _, ref = oracle_ag(inp)
+        want, want_amax = O.quantize_output_e4m3(ref, 0.75)
+        assert np.array_equal(codes, want)
+        assert amax == want_amax
+        src = inp.chunks[s]
+        bits = W.bits_u8 if dtype == "fp8" else W.bits_u16
+        assert np.array_equal(bits(bc.cpu()), bits(src))
+
+
+@pytest.mark.parametrize("tile", TILE_NAMES)
+def test_ag_fp8_output_random_every_tile(tile):
+    """Random data, ragged shape: the codes may differ from the oracle's only where the fp32
+    result itself differs in its last bits (a different accumulation order), so each decoded value
+    is within one E4M3 step of the oracle's; amax within fp32 rounding."""
+    c = ctx()
+    set_engine(c, "in-gemm")
+    c.set_option(B.RAG_OPT_TILE, B.TILES[tile])
+    inp = W.make_ag(W.ag_shape(3, 1, 300, 320, 333, dist="normal_sqrtk", seed=61))
+    say(f"case fp8-out random tile={tile}")
+    run, codes, amax, _ = _fp8_out_run(inp, c, 64.0, with_copy=False)
+    _, ref = oracle_ag(inp)
+    want, want_amax = O.quantize_output_e4m3(ref, 64.0)
+    got_v, want_v = O.e4m3fn_to_f32(codes), O.e4m3fn_to_f32(want)
+    step = np.maximum(np.abs(want_v) / 8.0, 2.0 ** -9)   # one E4M3 step at that magnitude
+    assert np.all(np.abs(got_v - want_v) <= step + 1e-12)
+    assert np.mean(codes == want) > 0.99
+    assert abs(amax - want_amax) <= 1e-3 * want_amax
+
+
+def test_ag_fp8_output_staged_and_split():
+    c = ctx()
+    set_engine(c, "kernel")
+    inp = W.make_ag(W.ag_shape(4, 2, 128, 192, 96, dist="int3", seed=71))
+    _, ref = oracle_ag(inp)
+    want, want_amax = O.quantize_output_e4m3(ref, 2.0)
+    for flags in (B.RAG_STAGED_OUT, B.RAG_PER_CHUNK, B.RAG_PER_CHUNK | B.RAG_STAGED_OUT):
+        say(f"case fp8-out flags={flags}")
+        run, codes, amax, bc = _fp8_out_run(inp, c, 2.0, flags=flags)
+        assert np.array_equal(codes, want)
+        assert amax == want_amax
+        assert np.array_equal(W.bits_u16(bc.cpu()), W.bits_u16(inp.chunks[2]))
+
+
+def test_ag_b_copy_bf16_output_and_validation():
+    """B_copy alone (bf16 output), and the argument checks of the extended call."""
+    c = ctx()
+    set_engine(c, "in-gemm")
+    inp = W.make_ag(W.ag_shape(2, 1, 64, 128, 64, dist="int3", seed=81))
+    run = AGRun(inp)
+    bc = torch.zeros_like(run.chunks[1])
+    B.ag_gemm(c, run.A, run.chunks, 2, 1, run.D, G=run.G, B_copy=bc)
+    torch.cuda.synchronize()
+    _, ref = oracle_ag(inp)
+    assert np.array_equal(run.D_bits(), O.f32_to_bf16(ref))
+    assert np.array_equal(W.bits_u16(bc.cpu()), W.bits_u16(inp.chunks[1]))
+    D8 = torch.zeros(run.D.shape, dtype=torch.float8_e4m3fn, device=DEV)
+    with pytest.raises(B.RagError):   # fp8 output without scale_D
+        B.ag_gemm(c, run.A, run.chunks, 2, 1, D8, G=run.G, B_copy=bc)
+    assert "scale_D" in B.last_error()
+    sD = torch.ones(1, device=DEV)
+    with pytest.raises(B.RagError):   # B_copy overlapping G
+        B.ag_gemm(c, run.A, run.chunks, 2, 1, D8, G=run.G, scale_D=sD, B_copy=run.G[:64])
+    assert "overlap" in B.last_error()
