@@ -233,9 +233,10 @@ RAG_API int ag_gemm_ex(rag_ctx* ctx,
  *
  *   X         [T, Kl] bf16 activation shard; T = tp * nc
  *   W         [Mo, Kl] bf16 weight shard
- *   Kl        >= 1, multiple of 64;  Mo >= 4, multiple of 4
+ *   Kl        >= 1, multiple of 64;  Mo >= 4, multiple of 4, <= 2^20
  *   partials  HOST array of tp device pointers to fp32 [T, Mo] partials with row stride ldp
- *             (elements, >= Mo, 4-byte aligned); only rows of chunk self_rank are read; entry
+ *             (elements, Mo <= ldp <= 2^20, 4-byte aligned); only rows of chunk self_rank are
+ *             read (memory from the chunk's first element to its last must be readable); entry
  *             self_rank ignored
  *   send      [tp, nc, Mo] fp32 outgoing chunks (slot self_rank untouched); NULL = not stored
  *   D         [nc, Mo] bf16, this rank's reduced chunk
@@ -281,7 +282,7 @@ RAG_API int rag_ag_kernel_name(rag_ctx* ctx, int nc, int M, int tp, rag_dtype dt
  *
  *   X, W, Kl, Mo, send, D as for gemm_rs (send NULL = the passed-on sums are not stored)
  *   incoming  HOST array of tp device pointers to fp32 [nc, Mo] running sums with row stride ldi
- *             (elements, >= Mo, 4-byte aligned); entry (self_rank - 1) mod tp ignored
+ *             (elements, Mo <= ldi <= 2^20, 4-byte aligned); entry (self_rank - 1) mod tp ignored
  *   flags     0 or RAG_RS_ARRIVE
  * Errors: RAG_EINVAL, RAG_EHIP (RAG_ETIMEOUT through rag_check as for gemm_rs).
  */

@@ -12,6 +12,15 @@
 
 using namespace ringag;
 
+// Waves per SIMD the GEMM+RS kernels are compiled for (the register budget): two where two waves
+// fit beside each other anyway (8-wave tiles; 128x128, whose LDS allows two workgroups per CU).
+// Without the hint the compiler spreads the epilogue's loop-carried sums over fresh registers and
+// halves the 128x128 kernel's occupancy.
+template <class S>
+constexpr int rs_waves_per_simd() {
+  return (S::NW >= 8 || S::LDS <= 80 * 1024) ? 2 : 1;
+}
+
 #define RAG_AG_ENTRY(TILE, SHAPE)                                                            \
   extern "C" __global__ void __launch_bounds__(SHAPE::NT) rag_ag_bf16_##TILE(AgArgs a) {    \
     ag_gemm_body<SHAPE, false, false>(a);                                                    \
@@ -25,7 +34,8 @@ using namespace ringag;
   extern "C" __global__ void __launch_bounds__(SHAPE::NT) rag_ag_fp8_o8_##TILE(AgArgs a) {  \
     ag_gemm_body<SHAPE, true, true>(a);                                                      \
   }                                                                                          \
-  extern "C" __global__ void __launch_bounds__(SHAPE::NT) rag_rs_##TILE(RsArgs a) {         \
+  extern "C" __global__ void __launch_bounds__(SHAPE::NT, rs_waves_per_simd<SHAPE>())          \
+      rag_rs_##TILE(RsArgs a) {                                                              \
     gemm_rs_body<SHAPE>(a);                                                                  \
   }
 

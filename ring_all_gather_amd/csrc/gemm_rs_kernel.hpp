@@ -12,11 +12,15 @@
 // result to send, or, for the own chunk, to D.  When that data arrives during the call (gated),
 // a tile runs its K loop first and waits for the counters only before its epilogue reads it.
 //
-// Epilogue: the accumulators are staged through LDS one wave row (TM rows of the tile) at a time,
-// then every thread moves whole 16-byte vectors along tile rows: send is written, and partials
-// are read, in full contiguous rows rather than in the MFMA layout's 4-byte scatter.  A thread
-// holds a batch of vectors and issues one peer's loads for the whole batch before adding them,
-// so a batch's loads are in flight together.
+// Epilogue: the partials are added to the accumulators where they are, in the MFMA register
+// layout.  A lane's accumulator element (i, j, e) sits at row 32 i + 8 (e / 4) + 4 (lane / 32) +
+// e % 4 and column 32 j + lane % 32 of the wave's sub-tile, so one load instruction of the wave
+// reads two rows of 32 consecutive floats (two whole 128-byte lines), and the row offsets are
+// uniform across the wave.  The loads are raw buffer loads: the per-lane offset is fixed for the
+// tile, the row offset goes in a scalar register and the column block in the immediate field.  A
+// thread issues the loads of IB block rows (64 or more floats) before adding them, so a CU has
+// 8 waves x 64 lines x 128 bytes in flight rather than what fits in LDS.  fp32 results (send) are
+// stored the same way; the own chunk's bf16 result goes through LDS for 16-byte row stores.
 #pragma once
 
 #include "copy_queue.hpp"
@@ -25,103 +29,106 @@
 
 namespace ringag {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+// Bytes from the first element of `rows` rows of stride ld floats (the last one cols long) to the
+// end of that region, clamped to a buffer descriptor's 32-bit range; 0 when rows <= 0.
+__device__ inline uint32_t region_bytes(int rows, long long ld, int cols) {
+  if (rows <= 0) return 0u;
+  const long long b = ((long long)(rows - 1) * ld + cols) * 4;
+  return b > 0xffffffffll ? 0xffffffffu : (uint32_t)b;
+}
 
 template <class S>
-struct RsEpilogue {
-  static constexpr int LD = S::BJ * 4 + 32;        // staging row stride: the two rows a wave
-                                                    // writes at once fall in different banks
-  static constexpr int VPR = S::BJ / 4;            // 16-byte vectors per tile row
-  static constexpr int VPT = S::TM * VPR / S::NT;  // vectors per thread per staged wave row
-  // 8-wave tiles have half the registers per lane, and the waves of the second wave row still
-  // hold their accumulators while the first is reduced: smaller batches there
-  static constexpr int MAXB = S::NW >= 8 ? 4 : 8;
-  static constexpr int BATCH = VPT < MAXB ? VPT : MAXB;
-  static_assert(S::TM * LD <= S::LDS, "a wave row of fp32 accumulators must fit in LDS");
-  static_assert((S::TM * VPR) % S::NT == 0 && VPT % BATCH == 0, "vectors must divide evenly");
-};
-
-template <class S>
-__device__ inline void rs_epilogue(const f32x16 (&acc)[S::FI][S::FJ], char* lds, const RsArgs& a,
-                                   int c, bool own, int rb, int cb, int wave, int lane) {
-  using E = RsEpilogue<S>;
+__device__ inline void rs_epilogue(f32x16 (&acc)[S::FI][S::FJ], char* lds, const RsArgs& a, int c,
+                                   bool own, int rb, int cb, int wave, int lane) {
+  // loads in flight together: IB block rows x EB elements of each 32x32 block (64 floats per
+  // lane; 32 for the 4-wave 256x256 tile, whose accumulators take half the registers)
+  constexpr int IB = S::FJ * 16 >= 64 ? 1 : 64 / (S::FJ * 16);
+  constexpr int EB = S::FJ * 16 >= 64 ? 32 / S::FJ : 16;
+  static_assert(S::FI % IB == 0 && 16 % EB == 0, "blocks must divide into load batches");
   const int wi = wave / S::WJ, wj = wave % S::WJ;
-  const int col0 = cb * S::BJ;
-  for (int slab = 0; slab < S::WI; ++slab) {
-    if (wi == slab) {
+  const int r0 = rb * S::BI;                                   // chunk-local first row of the tile
+  const int lrow = wi * S::TM + 4 * (lane >> 5);               // lane's row in the tile (e = 0)
+  const int lcol = cb * S::BJ + wj * S::TN + (lane & 31);      // lane's column (j = 0)
+  // what the tile's result gets added to: every peer's partial (own chunk, one-shot), one
+  // incoming running sum (ring step), or nothing (another chunk, one-shot)
+  const int nadd = a.ring ? (a.partial[c] != nullptr ? 1 : 0) : (own ? a.tp - 1 : 0);
+  for (int n = 0; n < nadd; ++n) {
+    // one-shot: the n-th peer in increasing rank, skipping this rank; ring: chunk c's sum
+    const int p = a.ring ? c : (n < a.self_rank ? n : n + 1);
+    const float* part = a.partial[p] + (size_t)r0 * a.ldp;
+    // reads past the chunk's last valid element return zero (ragged rows); columns past Mo in
+    // earlier rows read the row's padding or the next row, which only feeds elements that are
+    // never stored
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)part, 0, (int)region_bytes(a.nc - r0, a.ldp, a.Mo), 0x00020000);
+    const int vo = (int)(((long long)lrow * a.ldp + lcol) * 4);
+    int rstride = (int)(a.ldp * 4);
+    // (opaque here, so the compiler does not hoist the 64 row offsets out of the tile loop and
+    // keep them live through the K loop)
+    asm volatile("" : "+s"(rstride));
 #pragma unroll
-      for (int i = 0; i < S::FI; ++i)
+    for (int i0 = 0; i0 < S::FI; i0 += IB)
 #pragma unroll
-        for (int j = 0; j < S::FJ; ++j) {
-          const int col = wj * S::TN + acc_col(j, lane);
+      for (int e0 = 0; e0 < 16; e0 += EB) {
+        float y[IB][S::FJ][EB];
 #pragma unroll
-          for (int e = 0; e < 16; ++e)
-            *(float*)(lds + acc_row(i, e, lane) * E::LD + col * 4) = acc[i][j][e];
-        }
-    }
-    __syncthreads();
-    const int row0 = rb * S::BI + slab * S::TM;   // chunk-local row of the staged row 0
-    // what the staged rows get added to: every peer's partial (own chunk, one-shot), one
-    // incoming running sum (ring step), or nothing (another chunk, one-shot)
-    const int nadd = a.ring ? (a.partial[c] != nullptr ? 1 : 0) : (own ? a.tp - 1 : 0);
-    const bool to_d = own;
-    if (nadd == 0 && !to_d) {
-      float* out = a.send + (size_t)c * a.nc * a.Mo;
+        for (int ii = 0; ii < IB; ++ii)
 #pragma unroll
-      for (int k = 0; k < E::VPT; ++k) {
-        const int idx = (int)threadIdx.x + k * S::NT;
-        const int r = idx / E::VPR, v = idx % E::VPR;
-        const int row = row0 + r, col = col0 + v * 4;
-        if (row < a.nc && col < a.Mo)
-          *(f32x4*)(out + (size_t)row * a.Mo + col) = *(const f32x4*)(lds + r * E::LD + v * 16);
-      }
-    } else {
-      for (int b = 0; b < E::VPT; b += E::BATCH) {
-        f32x4 x[E::BATCH];
-        int row[E::BATCH], col[E::BATCH];
-        bool ok[E::BATCH];
+          for (int e = 0; e < EB; ++e) {
+            const int r = 32 * (i0 + ii) + 8 * ((e0 + e) >> 2) + ((e0 + e) & 3);
 #pragma unroll
-        for (int q = 0; q < E::BATCH; ++q) {
-          const int idx = (int)threadIdx.x + (b + q) * S::NT;
-          const int r = idx / E::VPR, v = idx % E::VPR;
-          row[q] = row0 + r;
-          col[q] = col0 + v * 4;
-          ok[q] = row[q] < a.nc && col[q] < a.Mo;
-          x[q] = *(const f32x4*)(lds + r * E::LD + v * 16);
-        }
-        for (int i = 0; i < nadd; ++i) {
-          // one-shot: the i-th peer in increasing rank, skipping this rank; ring: chunk c's sum
-          const int p = a.ring ? c : (i < a.self_rank ? i : i + 1);
-          const float* part = a.partial[p];
-          f32x4 y[E::BATCH];
-#pragma unroll
-          for (int q = 0; q < E::BATCH; ++q) {
-            const float* src = part + (size_t)row[q] * a.ldp + col[q];
-            if (!ok[q]) y[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-            else if (a.partial_vec) y[q] = *(const f32x4*)src;
-            else y[q] = f32x4{src[0], src[1], src[2], src[3]};
+            for (int j = 0; j < S::FJ; ++j)
+              y[ii][j][e] = __uint_as_float(
+                  __builtin_amdgcn_raw_buffer_load_b32(rs, vo + 128 * j, r * rstride, 0));
           }
 #pragma unroll
-          for (int q = 0; q < E::BATCH; ++q) x[q] += y[q];
-        }
-        if (to_d) {
-          __bf16* out = (__bf16*)a.D;
+        for (int ii = 0; ii < IB; ++ii)
 #pragma unroll
-          for (int q = 0; q < E::BATCH; ++q)
-            if (ok[q])
-              *(bf16x4*)(out + (size_t)row[q] * a.Mo + col[q]) =
-                  bf16x4{(__bf16)x[q][0], (__bf16)x[q][1], (__bf16)x[q][2], (__bf16)x[q][3]};
-        } else {
-          float* out = a.send + (size_t)c * a.nc * a.Mo;
+          for (int j = 0; j < S::FJ; ++j)
 #pragma unroll
-          for (int q = 0; q < E::BATCH; ++q)
-            if (ok[q]) *(f32x4*)(out + (size_t)row[q] * a.Mo + col[q]) = x[q];
-        }
+            for (int e = 0; e < EB; ++e) acc[i0 + ii][j][e0 + e] += y[ii][j][e];
       }
-    }
-    __syncthreads();
   }
+  if (own) {
+    store_tile_bf16<S>(acc, 1.0f, lds, (__bf16*)a.D + (size_t)r0 * a.Mo + cb * S::BJ, a.Mo,
+                       a.nc - r0, a.Mo - cb * S::BJ, wave, lane);
+    return;
+  }
+  // fp32 to send: rows past the chunk fall outside the descriptor and are dropped; columns past
+  // Mo are masked per lane
+  float* out = a.send + ((size_t)c * a.nc + r0) * a.Mo;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(out, 0, (int)region_bytes(a.nc - r0, a.Mo, a.Mo),
+                                        0x00020000);
+  const int vo = (lrow * a.Mo + lcol) * 4;
+  int rstride = a.Mo * 4;
+  asm volatile("" : "+s"(rstride));
+#pragma unroll
+  for (int j = 0; j < S::FJ; ++j) {
+    if (lcol + 32 * j >= a.Mo) continue;
+#pragma unroll
+    for (int i = 0; i < S::FI; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float v = acc[i][j][e];
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, vo + 128 * j,
+                                              (32 * i + 8 * (e >> 2) + (e & 3)) * rstride, 0);
+      }
+  }
+}
+
+// The tile this workgroup runs in the round [r0, r0 + n) of a grid of `grid` workgroups, for a
+// kernel whose chunks have U tiles each.  When every round holds whole chunks, XCD x (workgroups
+// w with w % 8 == x) takes the x-th eighth of every chunk in the round, as chunk-local indices in
+// a row: a chunk's epilogue traffic (the own chunk's partial reads, another chunk's fp32 stores)
+// then goes through all eight XCDs' paths to memory instead of the one or few XCDs that
+// round_tile would give it.  Other shapes use round_tile.
+__device__ inline int spread_tile(int r0, int n, int grid, int U) {
+  if ((grid & 7) != 0 || (U & 7) != 0 || r0 % U != 0 || n % U != 0) return round_tile(r0, n, grid);
+  const int w = (int)blockIdx.x, x = w & 7, q = w >> 3;
+  const int e = U >> 3;   // tiles of one chunk per XCD
+  if (q >= (n / U) * e) return -1;
+  return r0 + (q / e) * U + x * e + q % e;
 }
 
 template <class S>
@@ -138,7 +145,7 @@ __device__ __forceinline__ void gemm_rs_body(const RsArgs& a) {
   __shared__ int s_ok;
 
   for (int r0 = 0; r0 < total; r0 += grid) {
-    const int t = round_tile(r0, min(grid, total - r0), grid);
+    const int t = spread_tile(r0, min(grid, total - r0), grid, U);
     if (t < 0) continue;
     const int j = t / U;
     const int u = t - j * U;

@@ -93,7 +93,6 @@ struct RsArgs {
   void* D;                       // [nc, Mo] bf16
   int T, Kl, Mo, nc, tp, self_rank;
   int tiles_i, tiles_j;
-  int partial_vec;               // 1 = every partial and ldp allow 16-byte loads
   int gated;                     // 1 = the data of partial[] arrives during the call: a tile waits
                                  // for the counters of what its epilogue reads (ctr, by rank for
                                  // ring = 0, by chunk for ring = 1)

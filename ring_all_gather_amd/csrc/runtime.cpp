@@ -50,6 +50,7 @@ int fail(int code, const char* fmt, ...) {
   } while (0)
 
 constexpr long long kMaxOperandBytes = 0x7fffffffLL;   // buffer descriptors address < 2 GiB
+constexpr int kMaxRsRow = 1 << 20;   // GEMM+RS: floats per row of send and the partials, at most
 constexpr int kTimingSlots = 4096;
 
 bool debug_enabled() {
@@ -374,6 +375,10 @@ int rs_call(rag_ctx* c, const char* fn, bool ring, const void* X, int T, int Kl,
   if (any && !ptrs) return fail(RAG_EINVAL, "%s: the pointer array must not be NULL", fn);
   const char* ldname = ring ? "ldi" : "ldp";
   if (ld < Mo) return fail(RAG_EINVAL, "%s: %s=%lld must be >= Mo=%d", fn, ldname, ld, Mo);
+  // the epilogue addresses a tile's rows with 32-bit offsets
+  if (Mo > kMaxRsRow || ld > kMaxRsRow)
+    return fail(RAG_EINVAL, "%s: Mo=%d and %s=%lld must be at most %d", fn, Mo, ldname, ld,
+                kMaxRsRow);
   if (arrive && ld != Mo)
     return fail(RAG_EINVAL, "%s: RAG_RS_ARRIVE needs %s equal to Mo", fn, ldname);
   if (misaligned(X) || misaligned(W) || misaligned(D) || (send && misaligned(send)))
@@ -447,9 +452,6 @@ int rs_call(rag_ctx* c, const char* fn, bool ring, const void* X, int T, int Kl,
   a.epoch = epoch;
   a.err = c->err;
   a.spin_limit = c->spin_us * c->wall_khz / 1000;
-  a.partial_vec = (a.ldp % 4) == 0;
-  for (int i = 0; i < tp; ++i)
-    if (a.partial[i] && (reinterpret_cast<uintptr_t>(a.partial[i]) & 15u) != 0) a.partial_vec = 0;
 
   // Arrivals: the side stream copies, in ring order, what each tile's epilogue reads, releasing
   // one counter per copy; the tiles wait for them on the device.

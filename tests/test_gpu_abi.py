@@ -76,6 +76,8 @@ def test_gemm_rs_rejects_bad_arguments():
     for kw, needle in [(dict(T=63), "multiple of tp"), (dict(Kl=100), "multiple of 64"),
                        (dict(ldp=40), "ldp"), (dict(s=2), "self_rank"), (dict(flags=1), "flags"),
                        (dict(Dp=0), "NULL"), (dict(Dp=P.data_ptr()), "overlap"),
-                       (dict(Xp=X.data_ptr() + 4), "aligned")]:
+                       (dict(Xp=X.data_ptr() + 4), "aligned"),
+                       (dict(ldp=(1 << 20) + 4), "at most"),
+                       (dict(Mo=(1 << 20) + 4, ldp=(1 << 20) + 4), "at most")]:
         assert rs(**kw) == B.RAG_EINVAL, kw
         assert needle in B.last_error(), (kw, B.last_error())

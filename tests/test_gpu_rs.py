@@ -81,6 +81,46 @@ def test_rs_exact_integers(tp, s):
     _check_send(run, send_ref, exact=True)
 
 
+@pytest.mark.parametrize("tile", ["128x128", "256x128", "256x256", "256x256w8", "256x256w8s4"])
+def test_rs_padded_row_stride(tile):
+    """Partials and incoming sums with a row stride past Mo (views of NaN-padded buffers): the
+    padding must never reach D or send, in both the one-shot and the ring step forms, on ragged
+    sizes (nc and Mo not multiples of the tile, Mo not a multiple of 32)."""
+    c = ctx()
+    c.set_option(B.RAG_OPT_TILE, B.TILES[tile])
+    shape = W.rs_shape(4, 2, 4 * 136, 128, 212, dist="int3", seed=77)
+    pad = 44
+    say(f"case rs padded stride {shape.name} tile={tile}")
+
+    def padded(t):
+        buf = torch.full((t.shape[0], t.shape[1] + pad), float("nan"), device=DEV)
+        buf[:, :t.shape[1]] = t.to(DEV)
+        return buf[:, :t.shape[1]]
+
+    inp = W.make_rs(shape)
+    run = RSRun(inp)
+    run.partials = [None if p is None else padded(p) for p in inp.partials]
+    run.run(c)
+    D_ref, send_ref, _ = oracle_rs(inp)
+    assert np.array_equal(W.bits_u16(run.D.cpu()), O.f32_to_bf16(D_ref))
+    _check_send(run, send_ref, exact=True)
+
+    rin = W.make_rs_ring(shape)
+    D = torch.empty((shape.nc, shape.Mo), dtype=torch.bfloat16, device=DEV)
+    send = torch.full((shape.tp, shape.nc, shape.Mo), float("nan"), device=DEV)
+    inc = [padded(t) for t in rin.incoming]
+    B.gemm_rs_ring(c, rin.X.to(DEV), rin.W.to(DEV), inc, shape.tp, shape.self_rank, D, send=send)
+    torch.cuda.synchronize()
+    D_ref, send_ref, _ = oracle_ring(rin)
+    assert np.array_equal(W.bits_u16(D.cpu()), O.f32_to_bf16(D_ref))
+    got = send.cpu().numpy()
+    for cix in range(shape.tp):
+        if cix == shape.self_rank:
+            assert np.isnan(got[cix]).all()
+        else:
+            assert np.array_equal(got[cix], send_ref[cix])
+
+
 def test_rs_special_cases_and_no_send():
     c = ctx()
     shape = W.rs_shape(4, 2, 4 * 64, 128, 192, dist="int3", seed=41)
