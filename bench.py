@@ -3,14 +3,18 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ag_4k|ag_qkv|ag_fc1_f8|rs_8k]
 
 A step is one ag_gemm call (or one gemm_rs call for rs_8k) through the C ABI on inputs already
-resident in HBM: the arrival copies on the side stream, the counter-gated GEMM on the caller's
-stream and the join.  The default workload is AG+GEMM at M=K=N=4096, tp=4, self_rank=1, bf16.
+resident in HBM: with the default engine, one GEMM launch whose waiting workgroups copy the peers'
+chunks into G and release their counters.  The default workload is AG+GEMM at M=K=N=4096, tp=4,
+self_rank=1, bf16.  The default warm-up (1000 steps) lets the chip's clock settle before the
+timed steps; the timed steps are bracketed by one event pair, and the per-step and per-kernel
+figures come from a separate instrumented pass right after them.
 
 Prints one JSON line: throughput (TFLOP/s) of the whole step, the overlap figures (GEMM-only and
-copy-only times of the same kernels, overlap ratio T_chunked / (T_copy_only + T_gemm_only) and the
-hidden fraction of the copy time), the roofline of the GEMM kernel (algorithmic flops per launch
-over its average launch duration, from HIP events around each launch on the stream it runs on) and
-the CPU oracle's throughput on a bounded sample of the same workload.
+copy-only times of the same kernels, overlap ratio T_chunked / (T_copy_only + T_gemm_only), the
+hidden fraction of the copy time, and the same work without overlap in one step: the copies-only
+launch followed by the GEMM-only launch), the roofline of the GEMM kernel (algorithmic flops per
+launch over its average launch duration, from HIP events around each launch on the stream it runs
+on) and the CPU oracle's throughput on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -37,8 +41,10 @@ METRICS = {
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    # The chip's clock settles only after some 25 ms of sustained calls (from idle, the first 50
+    # ag_4k calls run 16% slower than the steady state); the default warm-up covers that.
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=1000)
     p.add_argument("--workload", default="ag_4k")
     p.add_argument("--copy-engine", default=os.environ.get("RAG_COPY_ENGINE", "in-gemm"),
                    choices=["kernel", "sdma", "in-gemm"])
@@ -52,28 +58,49 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target wall time of the CPU oracle sample")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    p.add_argument("--headline-only", action="store_true",
+                   help="measure the headline call (and, for AG, its GEMM-only and copies-only "
+                        "forms) but none of the other variants; for counter-collection runs, "
+                        "where the profiler serialises dispatches and a GEMM whose arrivals come "
+                        "from a kernel on another stream would wait for it in vain")
     return p.parse_args()
 
 
 def time_steps(fn, steps, warmup, stream):
+    """Average ms per step over `steps` back-to-back steps after `warmup` untimed ones, bracketed
+    by one event pair (and a synchronisation on both sides): nothing else is enqueued between the
+    steps."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    stops = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0.record(stream)
+    for _ in range(steps):
+        fn()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def per_step_times(fn, steps, stream):
+    """ms of each of `steps` steps, from an event pair around each (a separate, instrumented pass:
+    each event record costs a few microseconds of queue time)."""
+    import torch
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    stops = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
     for i in range(steps):
         starts[i].record(stream)
         fn()
         stops[i].record(stream)
-    t1.record(stream)
     torch.cuda.synchronize()
-    per = [a.elapsed_time(b) for a, b in zip(starts, stops)]
-    return t0.elapsed_time(t1) / steps, per
+    return [a.elapsed_time(b) for a, b in zip(starts, stops)]
+
+
+def rnd(x, nd=5):
+    return None if x is None else round(x, nd)
 
 
 def pctl(xs, q):
@@ -185,19 +212,27 @@ def main():
             B.ag_gemm(ctx, A, chunks, shape.tp, shape.self_rank, D, G=G, scale_A=sA, scale_B=sB,
                       flags=flags)
 
-        torch.cuda.synchronize()
+        ms = time_steps(step, args.steps, args.warmup, stream)
+        # instrumented pass right after it: per-step events, and the library's events around each
+        # GEMM launch on the stream it runs on (the roofline's kernel duration)
         ctx.kernel_times()
         ctx.set_option(B.RAG_OPT_TIMING, 1)
-        ms, per = time_steps(step, args.steps, args.warmup, stream)
-        kt = ctx.kernel_times()[args.warmup:]
+        per = per_step_times(step, args.steps, stream)
+        kt = ctx.kernel_times()
         ctx.set_option(B.RAG_OPT_TIMING, 0)
         ctx.check()
-        ms_gemm, _ = time_steps(lambda: step(B.RAG_NO_COPY), args.steps, args.warmup, stream)
-        ms_copy, _ = time_steps(lambda: step(B.RAG_COPY_ONLY), args.steps, args.warmup, stream)
-        ms_staged, _ = time_steps(lambda: step(B.RAG_STAGED_OUT), args.steps, args.warmup, stream)
-        # the split form (one GEMM launch per chunk, gated by stream events): what the in-kernel
-        # counters buy
-        ms_split, _ = time_steps(lambda: step(B.RAG_PER_CHUNK), args.steps, args.warmup, stream)
+        ms_gemm = time_steps(lambda: step(B.RAG_NO_COPY), args.steps, args.warmup, stream)
+        ms_copy = time_steps(lambda: step(B.RAG_COPY_ONLY), args.steps, args.warmup, stream)
+        ms_staged = ms_split = ms_seq = None
+        if not args.headline_only:
+            ms_staged = time_steps(lambda: step(B.RAG_STAGED_OUT), args.steps, args.warmup,
+                                   stream)
+            # the split form (one GEMM launch per chunk, gated by stream events): what the
+            # in-kernel counters buy
+            ms_split = time_steps(lambda: step(B.RAG_PER_CHUNK), args.steps, args.warmup, stream)
+            # the same work without overlap: the copies-only launch, then the GEMM-only launch
+            ms_seq = time_steps(lambda: (step(B.RAG_COPY_ONLY), step(B.RAG_NO_COPY)), args.steps,
+                                args.warmup, stream)
         ctx.check()
         flops = shape.flops
         kernel_ms = statistics.fmean(kt)
@@ -226,8 +261,10 @@ def main():
                         "t_copy_only_ms": round(ms_copy, 5),
                         "overlap_ratio": round(ms / (ms_copy + ms_gemm), 4),
                         "hidden_fraction": round((ms_copy + ms_gemm - ms) / ms_copy, 4),
-                        "t_staged_out_ms": round(ms_staged, 5),
-                        "t_split_per_chunk_ms": round(ms_split, 5)},
+                        "t_copy_then_gemm_ms": rnd(ms_seq),
+                        "chunked_vs_copy_then_gemm": rnd(ms_seq and ms / ms_seq, 4),
+                        "t_staged_out_ms": rnd(ms_staged),
+                        "t_split_per_chunk_ms": rnd(ms_split)},
             "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                          "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                          "kernel": kname, "kernel_ms": round(kernel_ms, 5)},
@@ -244,11 +281,11 @@ def main():
         def step():
             B.gemm_rs(ctx, X, Wt, parts, shape.tp, shape.self_rank, D, send=send)
 
-        torch.cuda.synchronize()
+        ms = time_steps(step, args.steps, args.warmup, stream)
         ctx.kernel_times()
         ctx.set_option(B.RAG_OPT_TIMING, 1)
-        ms, per = time_steps(step, args.steps, args.warmup, stream)
-        kt = ctx.kernel_times()[args.warmup:]
+        per = per_step_times(step, args.steps, stream)
+        kt = ctx.kernel_times()
         ctx.set_option(B.RAG_OPT_TIMING, 0)
         kernel_ms = statistics.fmean(kt)
         flops = shape.flops
@@ -276,37 +313,38 @@ def main():
                          "kernel": kname, "kernel_ms": round(kernel_ms, 5),
                          "algorithmic_bytes": alg_bytes},
         }
-        # the counter-gated forms: the peers' partials arrive during the call (side-stream copies in
-        # ring order, tiles wait before their epilogue), and one ring-accumulate step with its
-        # incoming running sums given or arriving
-        ms_arrive, _ = time_steps(lambda: B.gemm_rs(ctx, X, Wt, parts, shape.tp, shape.self_rank, D,
-                                                    send=send, flags=B.RAG_RS_ARRIVE),
-                                  args.steps, args.warmup, stream)
-        rin = W.make_rs_ring(shape)
-        inc = [t.to(dev) for t in rin.incoming]
-        Xr, Wr = rin.X.to(dev), rin.W.to(dev)
-        ms_ring, _ = time_steps(lambda: B.gemm_rs_ring(ctx, Xr, Wr, inc, shape.tp, shape.self_rank,
-                                                       D, send=send),
-                                args.steps, args.warmup, stream)
-        ms_ring_arrive, _ = time_steps(
-            lambda: B.gemm_rs_ring(ctx, Xr, Wr, inc, shape.tp, shape.self_rank, D, send=send,
-                                   flags=B.RAG_RS_ARRIVE), args.steps, args.warmup, stream)
-        # the row-parallel linear with its output all-reduced: the reduce-scatter above plus an
-        # all-gather of the owners' reduced chunks into Y, copied beside the GEMM
-        red = [t.to(dev) for t in W.make_reduced_chunks(shape)]
-        Y = torch.empty((shape.T, shape.Mo), dtype=torch.bfloat16, device=dev)
-        ms_lar, _ = time_steps(lambda: B.linear_allreduce(ctx, X, Wt, parts, red, shape.tp,
-                                                          shape.self_rank, Y, send=send),
-                               args.steps, args.warmup, stream)
-        ctx.check()
-        out["variants_ms_per_step"] = {
-            "one_shot_partials_given": round(ms, 5),
-            "one_shot_partials_arrive": round(ms_arrive, 5),
-            "ring_step_sums_given": round(ms_ring, 5),
-            "ring_step_sums_arrive": round(ms_ring_arrive, 5),
-            "linear_allreduce": round(ms_lar, 5),
-            "arrival_engine": "kernel" if args.copy_engine != "sdma" else "sdma",
-            "comm_wgs": args.comm_wgs}
+        if not args.headline_only:
+            # the counter-gated forms: the peers' partials arrive during the call (side-stream
+            # copies in ring order, tiles wait before their epilogue), and one ring-accumulate step
+            # with its incoming running sums given or arriving
+            ms_arrive = time_steps(
+                lambda: B.gemm_rs(ctx, X, Wt, parts, shape.tp, shape.self_rank, D, send=send,
+                                  flags=B.RAG_RS_ARRIVE), args.steps, args.warmup, stream)
+            rin = W.make_rs_ring(shape)
+            inc = [t.to(dev) for t in rin.incoming]
+            Xr, Wr = rin.X.to(dev), rin.W.to(dev)
+            ms_ring = time_steps(
+                lambda: B.gemm_rs_ring(ctx, Xr, Wr, inc, shape.tp, shape.self_rank, D, send=send),
+                args.steps, args.warmup, stream)
+            ms_ring_arrive = time_steps(
+                lambda: B.gemm_rs_ring(ctx, Xr, Wr, inc, shape.tp, shape.self_rank, D, send=send,
+                                       flags=B.RAG_RS_ARRIVE), args.steps, args.warmup, stream)
+            # the row-parallel linear with its output all-reduced: the reduce-scatter above plus
+            # an all-gather of the owners' reduced chunks into Y, copied beside the GEMM
+            red = [t.to(dev) for t in W.make_reduced_chunks(shape)]
+            Y = torch.empty((shape.T, shape.Mo), dtype=torch.bfloat16, device=dev)
+            ms_lar = time_steps(
+                lambda: B.linear_allreduce(ctx, X, Wt, parts, red, shape.tp, shape.self_rank, Y,
+                                           send=send), args.steps, args.warmup, stream)
+            ctx.check()
+            out["variants_ms_per_step"] = {
+                "one_shot_partials_given": round(ms, 5),
+                "one_shot_partials_arrive": round(ms_arrive, 5),
+                "ring_step_sums_given": round(ms_ring, 5),
+                "ring_step_sums_arrive": round(ms_ring_arrive, 5),
+                "linear_allreduce": round(ms_lar, 5),
+                "arrival_engine": "kernel" if args.copy_engine != "sdma" else "sdma",
+                "comm_wgs": args.comm_wgs}
         if not args.no_cpu:
             out["cpu_baseline"] = cpu_baseline_rs(inp, args.cpu_seconds)
     ctx.close()

@@ -121,7 +121,9 @@ enum {
                                    max 10^6) */
     RAG_OPT_WITHHOLD_MASK = 5,  /* test hook: bit j set = never bump the counter of the chunk at
                                    ring position j (1..tp-1); the waiting tiles then time out */
-    RAG_OPT_TIMING = 6,         /* 1 = record HIP events around every GEMM launch (rag_kernel_times) */
+    RAG_OPT_TIMING = 6,         /* 1 = time every GEMM call (rag_kernel_times): a call that is one
+                                   GEMM launch has the launch record its events itself (the
+                                   kernel's duration); the split form, its launches together */
     RAG_OPT_TILE = 7,           /* GEMM tile configuration: 0 = automatic, else a RAG_TILE_* value */
     RAG_OPT_TRACE_BUF = 8,      /* diagnostics: device address of a buffer of 64-bit words that the
                                    next ag_gemm calls fill with wall-clock stamps (100 MHz): words

@@ -134,11 +134,14 @@ struct KernelInfo {
 // Kernel loading and launching (launch.cpp).  load_kernels loads the embedded code object on
 // `device` once per process (kept until the process ends, so nothing of the library runs at exit);
 // the launchers enqueue on `stream` (the current device must be `device`) and return the
-// hipError_t of the launch.
+// hipError_t of the launch; given ev_start / ev_stop, the launch itself records them around the
+// kernel.
 hipError_t load_kernels(int device);
 hipError_t launch_ag_gemm(int device, const AgArgs& a, int tile, bool fp8, int grid,
-                          hipStream_t stream);
-hipError_t launch_gemm_rs(int device, const RsArgs& a, int tile, int grid, hipStream_t stream);
+                          hipStream_t stream, hipEvent_t ev_start = nullptr,
+                          hipEvent_t ev_stop = nullptr);
+hipError_t launch_gemm_rs(int device, const RsArgs& a, int tile, int grid, hipStream_t stream,
+                          hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 hipError_t launch_arrival(int device, const ArrivalArgs& a, int grid, hipStream_t stream);
 
 // Entry-point names (launch.cpp).

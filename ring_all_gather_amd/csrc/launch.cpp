@@ -12,6 +12,16 @@
 
 #include "kernels.hpp"
 
+// The HIP runtime's extended module launch (declared in hip_ext.h, whose templates need the HIP
+// compiler; this file is plain C++).
+extern "C" hipError_t hipExtModuleLaunchKernel(hipFunction_t f, uint32_t globalWorkSizeX,
+                                               uint32_t globalWorkSizeY, uint32_t globalWorkSizeZ,
+                                               uint32_t localWorkSizeX, uint32_t localWorkSizeY,
+                                               uint32_t localWorkSizeZ, size_t sharedMemBytes,
+                                               hipStream_t hStream, void** kernelParams,
+                                               void** extra, hipEvent_t startEvent,
+                                               hipEvent_t stopEvent, uint32_t flags);
+
 extern "C" const unsigned char ringag_kernels_co[];
 
 namespace ringag {
@@ -46,9 +56,16 @@ std::mutex g_mu;
 
 bool valid_tile(int tile) { return tile >= 1 && tile < kTiles; }
 
-hipError_t launch(hipFunction_t f, int grid, int threads, hipStream_t s, void* args) {
+// With ev_start / ev_stop, the events are recorded by the kernel's own dispatch (the extended
+// launch takes the global work size, grid x threads), so their interval is the kernel's duration
+// without the queue time of separate event markers.
+hipError_t launch(hipFunction_t f, int grid, int threads, hipStream_t s, void* args,
+                  hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr) {
   if (!f) return hipErrorInvalidDeviceFunction;
   void* params[] = {args};
+  if (ev_start || ev_stop)
+    return hipExtModuleLaunchKernel(f, (uint32_t)grid * (uint32_t)threads, 1, 1, threads, 1, 1,
+                                    0, s, params, nullptr, ev_start, ev_stop, 0);
   return hipModuleLaunchKernel(f, grid, 1, 1, threads, 1, 1, 0, s, params, nullptr);
 }
 
@@ -98,19 +115,21 @@ hipError_t load_kernels(int device) {
 }
 
 hipError_t launch_ag_gemm(int device, const AgArgs& a, int tile, bool fp8, int grid,
-                          hipStream_t s) {
+                          hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   const int o8 = a.out_fp8 ? 1 : 0;
   if (device < 0 || device >= kMaxDevices || !g_dev[device].loaded || !valid_tile(tile))
     return hipErrorInvalidValue;
   AgArgs copy = a;
-  return launch(g_dev[device].ag[fp8 ? 1 : 0][o8][tile], grid, tile_threads(tile), s, &copy);
+  return launch(g_dev[device].ag[fp8 ? 1 : 0][o8][tile], grid, tile_threads(tile), s, &copy,
+                ev_start, ev_stop);
 }
 
-hipError_t launch_gemm_rs(int device, const RsArgs& a, int tile, int grid, hipStream_t s) {
+hipError_t launch_gemm_rs(int device, const RsArgs& a, int tile, int grid, hipStream_t s,
+                          hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (device < 0 || device >= kMaxDevices || !g_dev[device].loaded || !valid_tile(tile))
     return hipErrorInvalidValue;
   RsArgs copy = a;
-  return launch(g_dev[device].rs[tile], grid, tile_threads(tile), s, &copy);
+  return launch(g_dev[device].rs[tile], grid, tile_threads(tile), s, &copy, ev_start, ev_stop);
 }
 
 hipError_t launch_arrival(int device, const ArrivalArgs& a, int grid, hipStream_t s) {

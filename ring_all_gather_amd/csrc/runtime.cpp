@@ -208,6 +208,16 @@ int record_timing_stop(rag_ctx* c, hipStream_t s, bool recorded) {
   return RAG_OK;
 }
 
+// For a call that is one GEMM launch: the next timing slot's events, which the launch itself
+// records around the kernel (both null when timing is off or the slots are used up).
+void launch_timing_events(rag_ctx* c, hipEvent_t* start, hipEvent_t* stop) {
+  *start = *stop = nullptr;
+  if (!c->timing || c->n_timed >= (int)c->t_start.size()) return;
+  *start = c->t_start[c->n_timed];
+  *stop = c->t_stop[c->n_timed];
+  c->n_timed++;
+}
+
 }  // namespace
 
 namespace {
@@ -532,12 +542,9 @@ int rs_call(rag_ctx* c, const char* fn, bool ring, const void* X, int T, int Kl,
   if (debug_enabled())
     fprintf(stderr, "[ringag] %s tp=%d s=%d T=%d Kl=%d Mo=%d tile=%dx%d tiles=%d grid=%d "
             "arrive=%d\n", fn, tp, self_rank, T, Kl, Mo, bi, bj, total, grid, (int)arrive);
-  bool rec = false;
-  int rc = record_timing_start(c, stream, &rec);
-  if (rc) return rc;
-  HIPCHK(launch_gemm_rs(c->device, a, tile, grid, stream));
-  rc = record_timing_stop(c, stream, rec);
-  if (rc) return rc;
+  hipEvent_t ev0, ev1;
+  launch_timing_events(c, &ev0, &ev1);
+  HIPCHK(launch_gemm_rs(c->device, a, tile, grid, stream, ev0, ev1));
   if (join) HIPCHK(hipStreamWaitEvent(stream, c->ev_join, 0));
   return RAG_OK;
 }
@@ -948,13 +955,10 @@ int ag_gemm_ex(rag_ctx* c, const void* A, int M, int K, const void* const* B, in
               c->ag_info[tile][fp8][out8].max_blocks_per_cu, c->ag_info[tile][fp8][out8].vgprs_per_wave,
               c->ag_info[tile][fp8][out8].lds_bytes, engine_name(c->copy_engine),
               c->comm_wgs, cp.pieces, cp.piece_bytes, flags, epoch);
-    bool rec = false;
-    int rc = record_timing_start(c, stream, &rec);
-    if (rc) return rc;
-    HIPCHK(launch_ag_gemm(c->device, a, tile, fp8, grid, stream));
+    hipEvent_t ev0, ev1;
+    launch_timing_events(c, &ev0, &ev1);
+    HIPCHK(launch_ag_gemm(c->device, a, tile, fp8, grid, stream, ev0, ev1));
     if (a.copies) c->arr_seq++;
-    rc = record_timing_stop(c, stream, rec);
-    if (rc) return rc;
   }
   if (!no_copy && !in_kernel && (copy_only || B_copy))
     HIPCHK(hipStreamWaitEvent(stream, c->ev_join, 0));
