@@ -209,13 +209,17 @@ int record_timing_stop(rag_ctx* c, hipStream_t s, bool recorded) {
 }
 
 // For a call that is one GEMM launch: the next timing slot's events, which the launch itself
-// records around the kernel (both null when timing is off or the slots are used up).
+// records around the kernel (both null when timing is off or the slots are used up).  The slot
+// counts as used once the launch has succeeded (launch_timed).
 void launch_timing_events(rag_ctx* c, hipEvent_t* start, hipEvent_t* stop) {
   *start = *stop = nullptr;
   if (!c->timing || c->n_timed >= (int)c->t_start.size()) return;
   *start = c->t_start[c->n_timed];
   *stop = c->t_stop[c->n_timed];
-  c->n_timed++;
+}
+
+void launch_timed(rag_ctx* c, hipEvent_t start) {
+  if (start) c->n_timed++;
 }
 
 }  // namespace
@@ -545,6 +549,7 @@ int rs_call(rag_ctx* c, const char* fn, bool ring, const void* X, int T, int Kl,
   hipEvent_t ev0, ev1;
   launch_timing_events(c, &ev0, &ev1);
   HIPCHK(launch_gemm_rs(c->device, a, tile, grid, stream, ev0, ev1));
+  launch_timed(c, ev0);
   if (join) HIPCHK(hipStreamWaitEvent(stream, c->ev_join, 0));
   return RAG_OK;
 }
@@ -958,6 +963,7 @@ int ag_gemm_ex(rag_ctx* c, const void* A, int M, int K, const void* const* B, in
     hipEvent_t ev0, ev1;
     launch_timing_events(c, &ev0, &ev1);
     HIPCHK(launch_ag_gemm(c->device, a, tile, fp8, grid, stream, ev0, ev1));
+    launch_timed(c, ev0);
     if (a.copies) c->arr_seq++;
   }
   if (!no_copy && !in_kernel && (copy_only || B_copy))
