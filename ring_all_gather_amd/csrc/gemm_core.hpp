@@ -290,7 +290,8 @@ __device__ inline void store_tile_bf16(const f32x16 (&acc)[S::FI][S::FJ], float 
     const char* src = lds + r * S::OUT_LD + c * 2;
     __bf16* dst = out + (size_t)r * ld + c;
     if (vec && c + 8 <= cols_valid) {
-      *(i32x4*)dst = *(const i32x4*)src;
+      // non-temporal: written once, never read back here; keeps the operands in L2
+      __builtin_nontemporal_store(*(const i32x4*)src, (i32x4*)dst);
     } else {
       for (int e = 0; e < 8 && c + e < cols_valid; ++e) dst[e] = ((const __bf16*)src)[e];
     }
@@ -334,7 +335,7 @@ __device__ inline float store_tile_fp8(const f32x16 (&acc)[S::FI][S::FJ], float 
     const char* src = lds + r * LD8 + c;
     uint8_t* dst = out + (size_t)r * ld + c;
     if (vec && c + 16 <= cols_valid) {
-      *(i32x4*)dst = *(const i32x4*)src;
+      __builtin_nontemporal_store(*(const i32x4*)src, (i32x4*)dst);
     } else {
       for (int e = 0; e < 16 && c + e < cols_valid; ++e) dst[e] = (uint8_t)src[e];
     }

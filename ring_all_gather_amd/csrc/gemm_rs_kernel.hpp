@@ -20,7 +20,8 @@
 // tile, the row offset goes in a scalar register and the column block in the immediate field.  A
 // thread issues the loads of IB block rows (64 or more floats) before adding them, so a CU has
 // 8 waves x 64 lines x 128 bytes in flight rather than what fits in LDS.  fp32 results (send) are
-// stored the same way; the own chunk's bf16 result goes through LDS for 16-byte row stores.
+// stored the same way, non-temporal (they stream past L2 instead of displacing the operands); the
+// own chunk's bf16 result goes through LDS for 16-byte row stores.
 #pragma once
 
 #include "copy_queue.hpp"
@@ -28,6 +29,10 @@
 #include "kernels.hpp"
 
 namespace ringag {
+
+// Cache policy of a raw buffer access with the non-temporal bit set ("nt" on gfx950): for data
+// written once and not read back by the kernel, so it does not displace the GEMM's operands in L2.
+constexpr int kNonTemporal = 2;
 
 // Bytes from the first element of `rows` rows of stride ld floats (the last one cols long) to the
 // end of that region, clamped to a buffer descriptor's 32-bit range; 0 when rows <= 0.
@@ -112,7 +117,8 @@ __device__ inline void rs_epilogue(f32x16 (&acc)[S::FI][S::FJ], char* lds, const
       for (int e = 0; e < 16; ++e) {
         const float v = acc[i][j][e];
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, vo + 128 * j,
-                                              (32 * i + 8 * (e >> 2) + (e & 3)) * rstride, 0);
+                                              (32 * i + 8 * (e >> 2) + (e & 3)) * rstride,
+                                              kNonTemporal);
       }
   }
 }
