@@ -13,8 +13,10 @@ Prints one JSON line: throughput (TFLOP/s) of the whole step, the overlap figure
 copy-only times of the same kernels, overlap ratio T_chunked / (T_copy_only + T_gemm_only), the
 hidden fraction of the copy time, and the same work without overlap in one step: the copies-only
 launch followed by the GEMM-only launch), the roofline of the GEMM kernel (algorithmic flops per
-launch over its average launch duration, from HIP events around each launch on the stream it runs
-on) and the CPU oracle's throughput on a bounded sample of the same workload.
+launch over its average launch duration, from HIP events that each launch records on the stream
+it runs on), for AG a timeline of one traced call (chunk releases against tile starts; the stamps
+slow a traced call by some 15%, so its times are relative) and the CPU oracle's throughput on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -58,6 +60,10 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target wall time of the CPU oracle sample")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    p.add_argument("--no-timeline", action="store_true",
+                   help="AG: skip the timeline (after the timed steps, 20 more calls traced with "
+                        "the library's per-tile wall-clock stamps: for the last, when each chunk "
+                        "was released and when its tiles ran)")
     p.add_argument("--headline-only", action="store_true",
                    help="measure the headline call (and, for AG, its GEMM-only and copies-only "
                         "forms) but none of the other variants; for counter-collection runs, "
@@ -158,6 +164,39 @@ def cpu_baseline_rs(inp, target_s):
             "cores": O.num_threads(), "kind": "oracle",
             "sample": f"{nrows} of the {s.T} rows of the local partial X W^T (each {s.Mo}x{s.Kl} "
                       f"MACs, fp32 triple loop), {dt:.1f} s wall"}
+
+
+def timeline_ag(ctx, B, step, shape, kname):
+    """The last of 20 back-to-back traced calls (RAG_OPT_TRACE_BUF: every traced call overwrites
+    the stamps; 100 MHz wall clock): per ring position, when the chunk was released and when the
+    first of its tiles started computing and the last ended, in microseconds from the first
+    tile's start.  The stamps themselves slow a traced call (by some 15% at ag_4k)."""
+    import math
+    import re
+    import torch
+    m = re.search(r"_t(\d+)x(\d+)", kname)
+    bi, bj = int(m.group(1)), int(m.group(2))
+    per_chunk = math.ceil(shape.nc / bi) * math.ceil(shape.M / bj)
+    total = per_chunk * shape.tp
+    buf = torch.zeros(64 + 5 * total, dtype=torch.int64, device="cuda:0")
+    ctx.set_trace(buf)
+    for _ in range(20):
+        step()
+    ctx.set_trace(None)
+    torch.cuda.synchronize()
+    w = buf.cpu().tolist()
+    tiles = [w[64 + 5 * t: 64 + 5 * t + 5] for t in range(total)]
+    t0 = min(x[0] for x in tiles)
+    us = lambda v: round((v - t0) / 100.0, 2)
+    chunks = []
+    for j in range(shape.tp):
+        tj = tiles[j * per_chunk:(j + 1) * per_chunk]
+        chunks.append({"ring_pos": j, "rank": (shape.self_rank - j) % shape.tp,
+                       "released_us": 0.0 if j == 0 else us(w[j - 1]),
+                       "first_tile_go_us": us(min(x[1] for x in tj)),
+                       "last_tile_end_us": us(max(x[2] for x in tj))})
+    return {"tiles_per_chunk": per_chunk, "copies_start_us": us(w[32]),
+            "gemm_end_us": us(max(x[2] for x in tiles)), "chunks": chunks}
 
 
 def measured_traffic(workload: str, kernel: str, fingerprint: str):
@@ -269,6 +308,8 @@ def main():
                          "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                          "kernel": kname, "kernel_ms": round(kernel_ms, 5)},
         }
+        if not (args.no_timeline or args.headline_only):
+            out["timeline"] = timeline_ag(ctx, B, step, shape, kname)
         if not args.no_cpu:
             out["cpu_baseline"] = cpu_baseline_ag(inp, args.cpu_seconds)
     else:
