@@ -170,25 +170,42 @@ __device__ inline i32x8 frag_fp8(const char* tile_rows, int seg, int lane) {
 // k-steps of 64 (v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales).  Lane l of a 32x32 operand
 // fragment holds row (l & 31) and the (l >> 5)-th half of the k-step; X (MFMA A operand, output
 // rows) and Y (B operand, output columns) use the same k assignment.
+//
+// bf16 fragments are double-buffered in registers: the reads of k-step kk + 1 are issued before
+// the MFMAs of k-step kk (scheduling barriers keep that order), so each read has a k-step of
+// MFMAs to land in instead of stalling the wave right before its first use; the LDS latency
+// grows while the next stage's DMA writes share the LDS.  (fp8 fragments are twice as large and
+// the second set does not fit beside the 8-wave tile's accumulators.)
 template <class S, bool FP8>
 __device__ inline void stage_mma(const char* xs, const char* ys, int lane,
                                  f32x16 (&acc)[S::FI][S::FJ]) {
   const int h = lane >> 5;
   if constexpr (!FP8) {
+    constexpr int NK = S::SEGS / 2;
+    bf16x8 a[2][S::FI], b[2][S::FJ];
 #pragma unroll
-    for (int kk = 0; kk < S::SEGS / 2; ++kk) {
-      bf16x8 a[S::FI], b[S::FJ];
+    for (int f = 0; f < S::FI; ++f) a[0][f] = frag_bf16<S::BKB>(xs + f * 32 * S::BKB, h, lane);
 #pragma unroll
-      for (int f = 0; f < S::FI; ++f)
-        a[f] = frag_bf16<S::BKB>(xs + f * 32 * S::BKB, kk * 2 + h, lane);
+    for (int f = 0; f < S::FJ; ++f) b[0][f] = frag_bf16<S::BKB>(ys + f * 32 * S::BKB, h, lane);
 #pragma unroll
-      for (int f = 0; f < S::FJ; ++f)
-        b[f] = frag_bf16<S::BKB>(ys + f * 32 * S::BKB, kk * 2 + h, lane);
+    for (int kk = 0; kk < NK; ++kk) {
+      const int c = kk & 1;
+      if (kk + 1 < NK) {
+#pragma unroll
+        for (int f = 0; f < S::FI; ++f)
+          a[c ^ 1][f] = frag_bf16<S::BKB>(xs + f * 32 * S::BKB, (kk + 1) * 2 + h, lane);
+#pragma unroll
+        for (int f = 0; f < S::FJ; ++f)
+          b[c ^ 1][f] = frag_bf16<S::BKB>(ys + f * 32 * S::BKB, (kk + 1) * 2 + h, lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < S::FI; ++i)
 #pragma unroll
         for (int j = 0; j < S::FJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+          acc[i][j] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   } else {
 #pragma unroll
