@@ -146,7 +146,8 @@ enum {
 };
 
 /* Tile configurations (rows of D x columns of D per workgroup; 4 waves unless stated). */
-enum { RAG_TILE_AUTO = 0, RAG_TILE_128x128 = 1, RAG_TILE_256x128 = 2, RAG_TILE_256x256 = 3,
+enum { RAG_TILE_AUTO = 0, RAG_TILE_128x128 = 1, RAG_TILE_256x128 = 2,
+       RAG_TILE_256x256 = 3 /* 4 waves of 128x128, 2 LDS stages of 128-byte rows */,
        RAG_TILE_256x256_8W = 4 /* 8 waves of 128x64, 2 LDS stages of 128-byte rows */,
        RAG_TILE_256x256_8W_S4 = 5 /* 8 waves of 128x64, 4 LDS stages of 64-byte rows */ };
 

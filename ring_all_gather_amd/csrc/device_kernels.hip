@@ -4,8 +4,8 @@
 //
 // Entry points: rag_ag_<bf16|fp8>[_o8]_<tile> (input dtype; _o8 = E4M3 output), rag_rs_<tile>,
 // rag_arrival.  Tile names:
-//   t128x128, t256x128, t256x256 (4 waves), t256x256w8 (8 waves, 2 stages), t256x256w8s4 (8 waves,
-//   4 stages); see gemm_core.hpp.
+//   t128x128, t256x128, t256x256 (4 waves, 2 stages), t256x256w8 (8 waves, 2 stages), t256x256w8s4
+//   (8 waves, 4 stages); see gemm_core.hpp.
 #include "arrival_kernel.hpp"
 #include "gemm_ag_kernel.hpp"
 #include "gemm_rs_kernel.hpp"

@@ -66,7 +66,7 @@ struct TileShape {
 // The configurations the kernels are built for.
 using Tile128x128 = TileShape<128, 128, 2, 2, 128, 2>;
 using Tile256x128 = TileShape<256, 128, 2, 2, 128, 2>;
-using Tile256x256 = TileShape<256, 256, 2, 2, 64, 4>;       // 4 waves of 128x128, 4 stages
+using Tile256x256 = TileShape<256, 256, 2, 2, 128, 2>;      // 4 waves of 128x128, 2 stages
 using Tile256x256w8 = TileShape<256, 256, 2, 4, 128, 2>;    // 8 waves of 128x64, 2 stages
 using Tile256x256w8s4 = TileShape<256, 256, 2, 4, 64, 4>;   // 8 waves of 128x64, 4 stages
 
@@ -228,6 +228,102 @@ __device__ inline void stage_mma(const char* xs, const char* ys, int lane,
   }
 }
 
+template <class S>
+__device__ inline void load_frags_bf16(bf16x8 (&a)[S::FI], bf16x8 (&b)[S::FJ], const char* xs,
+                                       const char* ys, int seg, int lane) {
+#pragma unroll
+  for (int f = 0; f < S::FI; ++f) a[f] = frag_bf16<S::BKB>(xs + f * 32 * S::BKB, seg, lane);
+#pragma unroll
+  for (int f = 0; f < S::FJ; ++f) b[f] = frag_bf16<S::BKB>(ys + f * 32 * S::BKB, seg, lane);
+}
+
+// bf16 K loop over two LDS stages with the stage handover inside a stage's last MFMA k-step.
+// Fragments are double-buffered as in stage_mma.  Once the fragments of the last k-step are in
+// registers, the wave waits for its DMA of the next stage and for its reads, meets the others at
+// the barrier, reads the next stage's first fragments, and starts the DMA of the stage after next
+// into the buffer just read, its DMA instructions spread over the MFMAs of that last k-step; so
+// no fragment read waits right behind a barrier, and the DMA issue hides under MFMAs.  The loop
+// body has no branch: past the last stage the DMA reads at kOOB (zeros, into a buffer nobody
+// reads) and the prefetch reads the idle buffer; the DMA is drained before the final barrier.
+// (fp8 fragments are twice as large; a second set spills beside the 8-wave tile's accumulators,
+// so fp8 keeps the loop below.)
+template <class S>
+__device__ inline void tile_kloop_2s(i32x4 rx, const uint32_t* xo, i32x4 ry, const uint32_t* yo,
+                                     int ksteps, char* lds, int wave, int lane,
+                                     f32x16 (&acc)[S::FI][S::FJ]) {
+  constexpr int NK = S::SEGS / 2;
+  constexpr int NM = S::FI * S::FJ;
+  static_assert(S::NS == 2 && NK % 2 == 0, "two stages of an even number of k-steps");
+  const int wi = wave / S::WJ, wj = wave % S::WJ;
+  const int h = lane >> 5;
+  const uint32_t base = lds_addr(lds);
+#pragma unroll
+  for (int i = 0; i < S::FI; ++i)
+#pragma unroll
+    for (int j = 0; j < S::FJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  if (ksteps <= 0) {
+    __syncthreads();
+    return;
+  }
+  issue_loads<S, S::XQ>(rx, xo, 0, base, wave);
+  issue_loads<S, S::YQ>(ry, yo, 0, base + S::BI * S::BKB, wave);
+  wait_vmem<0>();
+  __syncthreads();
+  {
+    const uint32_t kb = ksteps > 1 ? (uint32_t)S::BKB : kOOB;
+    issue_loads<S, S::XQ>(rx, xo, kb, base + S::STAGE, wave);
+    issue_loads<S, S::YQ>(ry, yo, kb, base + S::STAGE + S::BI * S::BKB, wave);
+  }
+  const int xrow = wi * S::TM * S::BKB, yrow = (S::BI + wj * S::TN) * S::BKB;
+  bf16x8 a[2][S::FI], b[2][S::FJ];
+  load_frags_bf16<S>(a[0], b[0], lds + xrow, lds + yrow, h, lane);
+  for (int kt = 0; kt < ksteps; ++kt) {
+    const int cur = (kt & 1) * S::STAGE, nxt = S::STAGE - cur;
+#pragma unroll
+    for (int kk = 0; kk < NK - 1; ++kk) {
+      const int c = kk & 1;
+      load_frags_bf16<S>(a[c ^ 1], b[c ^ 1], lds + cur + xrow, lds + cur + yrow,
+                         (kk + 1) * 2 + h, lane);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < S::FI; ++i)
+#pragma unroll
+        for (int j = 0; j < S::FJ; ++j)
+          acc[i][j] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // last k-step of the stage (its fragments are in set 1: NK is even)
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    load_frags_bf16<S>(a[0], b[0], lds + nxt + xrow, lds + nxt + yrow, h, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint32_t kb = kt + 2 < ksteps ? (uint32_t)(kt + 2) * S::BKB : kOOB;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const int i = m / S::FJ, j = m % S::FJ;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][i], b[1][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      // DMA instructions [m LOADS / NM, (m + 1) LOADS / NM) after MFMA m
+#pragma unroll
+      for (int q = m * S::LOADS / NM; q < (m + 1) * S::LOADS / NM; ++q) {
+        if (q < S::XQ)
+          dma16(rx, base + cur + (uint32_t)((q * S::NW + wave) * S::RPI * S::BKB), xo[q] + kb);
+        else
+          dma16(ry,
+                base + cur + S::BI * S::BKB +
+                    (uint32_t)(((q - S::XQ) * S::NW + wave) * S::RPI * S::BKB),
+                yo[q - S::XQ] + kb);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  wait_vmem<0>();
+  __syncthreads();
+}
+
 // Full K loop of one tile.  rx/ry: descriptors of X and Y; xo/yo from tile_offsets; ksteps = K
 // bytes / BKB.  Returns with acc = the wave's fp32 sub-tile and all waves past a final barrier
 // (LDS free for the epilogue).  The caller must have passed a barrier since the last LDS reads.
@@ -235,6 +331,10 @@ template <class S, bool FP8>
 __device__ inline void tile_kloop(i32x4 rx, const uint32_t* xo, i32x4 ry, const uint32_t* yo,
                                   int ksteps, char* lds, int wave, int lane,
                                   f32x16 (&acc)[S::FI][S::FJ]) {
+  if constexpr (!FP8 && S::NS == 2) {
+    tile_kloop_2s<S>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);
+    return;
+  }
   const int wi = wave / S::WJ, wj = wave % S::WJ;
   const uint32_t base = lds_addr(lds);
 #pragma unroll
