@@ -245,8 +245,6 @@ __device__ inline void load_frags_bf16(bf16x8 (&a)[S::FI], bf16x8 (&b)[S::FJ], c
 // no fragment read waits right behind a barrier, and the DMA issue hides under MFMAs.  The loop
 // body has no branch: past the last stage the DMA reads at kOOB (zeros, into a buffer nobody
 // reads) and the prefetch reads the idle buffer; the DMA is drained before the final barrier.
-// (fp8 fragments are twice as large; a second set spills beside the 8-wave tile's accumulators,
-// so fp8 keeps the loop below.)
 template <class S>
 __device__ inline void tile_kloop_2s(i32x4 rx, const uint32_t* xo, i32x4 ry, const uint32_t* yo,
                                      int ksteps, char* lds, int wave, int lane,
@@ -324,6 +322,109 @@ __device__ inline void tile_kloop_2s(i32x4 rx, const uint32_t* xo, i32x4 ry, con
   __syncthreads();
 }
 
+// The same two-stage loop for fp8 (64-k MFMA steps, 32-byte fragments).  A second full fragment
+// set does not fit beside the 8-wave tile's accumulators, so only the Y (B operand) fragments are
+// double-buffered and the X fragments rotate in place: X fragment i of the next k-step is read as
+// soon as the MFMAs of row i are issued, with the rest of the k-step's MFMAs to land in.  In a
+// stage's last k-step the MFMAs of row 0 go out before the barrier, covering the wait for the
+// stage's last reads.
+template <class S>
+__device__ inline void tile_kloop_2s_fp8(i32x4 rx, const uint32_t* xo, i32x4 ry,
+                                         const uint32_t* yo, int ksteps, char* lds, int wave,
+                                         int lane, f32x16 (&acc)[S::FI][S::FJ]) {
+  constexpr int NK = S::SEGS / 4;
+  static_assert(S::NS == 2 && NK % 2 == 0, "two stages of an even number of k-steps");
+  const int wi = wave / S::WJ, wj = wave % S::WJ;
+  const int h2 = (lane >> 5) * 2;
+  const uint32_t base = lds_addr(lds);
+#pragma unroll
+  for (int i = 0; i < S::FI; ++i)
+#pragma unroll
+    for (int j = 0; j < S::FJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  if (ksteps <= 0) {
+    __syncthreads();
+    return;
+  }
+  issue_loads<S, S::XQ>(rx, xo, 0, base, wave);
+  issue_loads<S, S::YQ>(ry, yo, 0, base + S::BI * S::BKB, wave);
+  wait_vmem<0>();
+  __syncthreads();
+  {
+    const uint32_t kb = ksteps > 1 ? (uint32_t)S::BKB : kOOB;
+    issue_loads<S, S::XQ>(rx, xo, kb, base + S::STAGE, wave);
+    issue_loads<S, S::YQ>(ry, yo, kb, base + S::STAGE + S::BI * S::BKB, wave);
+  }
+  const int xrow = wi * S::TM * S::BKB, yrow = (S::BI + wj * S::TN) * S::BKB;
+  // k-step kk's fragments of the stage at offset st
+  auto xfrag = [&](int st, int f, int kk) {
+    return frag_fp8<S::BKB>(lds + st + xrow + f * 32 * S::BKB, kk * 4 + h2, lane);
+  };
+  auto yfrag = [&](int st, int f, int kk) {
+    return frag_fp8<S::BKB>(lds + st + yrow + f * 32 * S::BKB, kk * 4 + h2, lane);
+  };
+  // format 0 = FP8 E4M3 for both operands; E8M0 scale 127 = 2^0 on both
+  auto mma = [](const i32x8& x, const i32x8& y, const f32x16& c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, 0, 0, 0, 127, 0, 127);
+  };
+  i32x8 a[S::FI], b[2][S::FJ];
+#pragma unroll
+  for (int f = 0; f < S::FI; ++f) a[f] = xfrag(0, f, 0);
+#pragma unroll
+  for (int f = 0; f < S::FJ; ++f) b[0][f] = yfrag(0, f, 0);
+  for (int kt = 0; kt < ksteps; ++kt) {
+    const int cur = (kt & 1) * S::STAGE, nxt = S::STAGE - cur;
+#pragma unroll
+    for (int kk = 0; kk < NK - 1; ++kk) {
+      const int c = kk & 1;
+#pragma unroll
+      for (int f = 0; f < S::FJ; ++f) b[c ^ 1][f] = yfrag(cur, f, kk + 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < S::FI; ++i) {
+#pragma unroll
+        for (int j = 0; j < S::FJ; ++j) acc[i][j] = mma(a[i], b[c][j], acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);
+        a[i] = xfrag(cur, i, kk + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // last k-step of the stage (Y fragments in set 1: NK is even)
+#pragma unroll
+    for (int j = 0; j < S::FJ; ++j) acc[0][j] = mma(a[0], b[1][j], acc[0][j]);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int f = 0; f < S::FJ; ++f) b[0][f] = yfrag(nxt, f, 0);
+    const uint32_t kb = kt + 2 < ksteps ? (uint32_t)(kt + 2) * S::BKB : kOOB;
+#pragma unroll
+    for (int i = 0; i < S::FI; ++i) {
+      if (i > 0) {
+#pragma unroll
+        for (int j = 0; j < S::FJ; ++j) acc[i][j] = mma(a[i], b[1][j], acc[i][j]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      a[i] = xfrag(nxt, i, 0);
+      // DMA instructions [i LOADS / FI, (i + 1) LOADS / FI) after row i
+#pragma unroll
+      for (int q = i * S::LOADS / S::FI; q < (i + 1) * S::LOADS / S::FI; ++q) {
+        if (q < S::XQ)
+          dma16(rx, base + cur + (uint32_t)((q * S::NW + wave) * S::RPI * S::BKB), xo[q] + kb);
+        else
+          dma16(ry,
+                base + cur + S::BI * S::BKB +
+                    (uint32_t)(((q - S::XQ) * S::NW + wave) * S::RPI * S::BKB),
+                yo[q - S::XQ] + kb);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  wait_vmem<0>();
+  __syncthreads();
+}
+
 // Full K loop of one tile.  rx/ry: descriptors of X and Y; xo/yo from tile_offsets; ksteps = K
 // bytes / BKB.  Returns with acc = the wave's fp32 sub-tile and all waves past a final barrier
 // (LDS free for the epilogue).  The caller must have passed a barrier since the last LDS reads.
@@ -331,8 +432,9 @@ template <class S, bool FP8>
 __device__ inline void tile_kloop(i32x4 rx, const uint32_t* xo, i32x4 ry, const uint32_t* yo,
                                   int ksteps, char* lds, int wave, int lane,
                                   f32x16 (&acc)[S::FI][S::FJ]) {
-  if constexpr (!FP8 && S::NS == 2) {
-    tile_kloop_2s<S>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);
+  if constexpr (S::NS == 2) {
+    if constexpr (FP8) tile_kloop_2s_fp8<S>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);
+    else tile_kloop_2s<S>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);
     return;
   }
   const int wi = wave / S::WJ, wj = wave % S::WJ;
