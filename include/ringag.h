@@ -101,7 +101,10 @@ enum {
 
 /* Copy engines of the simulated arrival (RAG_OPT_COPY_ENGINE). */
 enum {
-    RAG_COPY_KERNEL = 0,   /* a copy kernel on the side stream, beside the GEMM */
+    RAG_COPY_KERNEL = 0,   /* a copy kernel on the side stream, beside the GEMM.  Its waves need
+                              room on every compute unit: with the automatic tile, a GEMM kernel
+                              that leaves none gives way to one of the same tile size that does,
+                              else 8 compute units are left out of the GEMM's grid */
     RAG_COPY_SDMA = 1,     /* SDMA engines on the side stream (hipMemcpyDeviceToDeviceNoCU, then
                               hipStreamWriteValue32 of the counter) */
     RAG_COPY_IN_GEMM = 2   /* the GEMM launch itself: workgroups whose chunk is not there yet copy
@@ -265,10 +268,10 @@ RAG_API int rag_check(rag_ctx* ctx);
  * how many were recorded (>= 0), or a negative RAG_E* code. */
 RAG_API int rag_kernel_times(rag_ctx* ctx, float* out, int max_n);
 
-/* Name of the GPU kernel entry point ag_gemm would launch for these sizes (nc rows per chunk, M
- * output columns, tp chunks) with the context's current options (e.g. "rag_ag_bf16_t256x256w8"),
- * written NUL-terminated into buf (len bytes).  Diagnostics: lets a profile be matched to the
- * kernel a measurement ran. */
+/* Name of the GPU kernel entry point a chunked ag_gemm call (bf16 output) would launch for these
+ * sizes (nc rows per chunk, M output columns, tp chunks) with the context's current options (e.g.
+ * "rag_ag_bf16_t256x256w8"), written NUL-terminated into buf (len bytes).  Diagnostics: lets a
+ * profile be matched to the kernel a measurement ran. */
 RAG_API int rag_ag_kernel_name(rag_ctx* ctx, int nc, int M, int tp, rag_dtype dt, char* buf,
                                int len);
 

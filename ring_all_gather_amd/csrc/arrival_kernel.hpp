@@ -14,14 +14,18 @@
 
 namespace ringag {
 
+// 16-byte vectors in flight per copying thread: 6 keeps the kernel at 48 VGPRs, which fit beside
+// two GEMM waves of up to 232 VGPRs on a SIMD (of its 512).
+constexpr int kArrivalInFlight = 6;
+
 __device__ __forceinline__ void arrival_body(const ArrivalArgs& a) {
   __shared__ unsigned s_piece;
   // The copy shares SIMDs with GEMM waves: issue its (few) instructions first so the chunks the
   // GEMM waits for are not starved by the waves that will consume them.
   if (a.raise_priority) __builtin_amdgcn_s_setprio(3);
   copy_queue_begin(a.cp);
-  run_copy_queue<kArrivalThreads>(a.cp, a.ctr, a.epoch, 0, -1, &s_piece);
-  run_copy_queue<kArrivalThreads>(a.cp, a.ctr, a.epoch, 1, -1, &s_piece);
+  run_copy_queue<kArrivalThreads, kArrivalInFlight>(a.cp, a.ctr, a.epoch, 0, -1, &s_piece);
+  run_copy_queue<kArrivalThreads, kArrivalInFlight>(a.cp, a.ctr, a.epoch, 1, -1, &s_piece);
 }
 
 }  // namespace ringag

@@ -46,11 +46,10 @@ __device__ inline bool wait_ready(int* ctr, int epoch, int* err, long long limit
   return ok;
 }
 
-// Copy piece k of copy c with the NT threads of the workgroup (16-byte vectors, 8 in flight per
+// Copy piece k of copy c with the NT threads of the workgroup (16-byte vectors, U in flight per
 // thread).
-template <int NT>
+template <int NT, int U>
 __device__ __forceinline__ void copy_piece(const CopyPlan& p, unsigned c, unsigned k) {
-  constexpr int U = 8;
   const unsigned long long beg = (unsigned long long)k * p.piece_bytes;
   const unsigned long long len = min((unsigned long long)p.piece_bytes, p.bytes - beg);
   const v4i* s = (const v4i*)((const char*)p.src[c] + beg);
@@ -107,7 +106,7 @@ __device__ inline void copy_queue_begin(const CopyPlan& p) {
 // and lower the loop so that thread 0's lane is held back while the wave's other lanes start the
 // next iteration with the stale piece number, a loop that never ends.)  The taken number is read
 // into a scalar register, so the loop's exit is uniform.
-template <int NT>
+template <int NT, int U = 8>
 __device__ inline void run_copy_queue(const CopyPlan& p, int* ctr, int epoch, int q, int stop,
                                       unsigned* s_word) {
   const unsigned first = q == 0 ? 0u : (unsigned)p.n_peer;
@@ -129,7 +128,7 @@ __device__ inline void run_copy_queue(const CopyPlan& p, int* ctr, int epoch, in
     __syncthreads();
     if (g >= total) return;
     const unsigned c = first + g / p.pieces;
-    copy_piece<NT>(p, c, g % p.pieces);
+    copy_piece<NT, U>(p, c, g % p.pieces);
     // every wave waits for its own stores; after the barrier thread 0 completes the piece
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();

@@ -151,6 +151,7 @@ const char* rs_kernel_name(int tile);
 // Occupancy / resource facts for a kernel variant (cached by the caller).
 hipError_t ag_kernel_info(int device, int tile, bool fp8, bool out8, KernelInfo* info);
 hipError_t rs_kernel_info(int device, int tile, KernelInfo* info);
+hipError_t arrival_kernel_info(int device, KernelInfo* info);
 
 constexpr int kArrivalThreads = 256;   // block size of the arrival kernel
 

@@ -144,6 +144,11 @@ hipError_t ag_kernel_info(int device, int tile, bool fp8, bool out8, KernelInfo*
   return info(g_dev[device].ag[fp8 ? 1 : 0][out8 ? 1 : 0][tile], tile_threads(tile), out);
 }
 
+hipError_t arrival_kernel_info(int device, KernelInfo* out) {
+  if (device < 0 || device >= kMaxDevices || !g_dev[device].loaded) return hipErrorInvalidValue;
+  return info(g_dev[device].arrival, kArrivalThreads, out);
+}
+
 hipError_t rs_kernel_info(int device, int tile, KernelInfo* out) {
   if (device < 0 || device >= kMaxDevices || !g_dev[device].loaded || !valid_tile(tile))
     return hipErrorInvalidValue;

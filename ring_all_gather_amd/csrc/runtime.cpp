@@ -103,6 +103,8 @@ struct rag_ctx {
   bool ag_info_ok[6][2][2] = {};
   KernelInfo rs_info[6] = {};
   bool rs_info_ok[6] = {};
+  KernelInfo arr_info = {};
+  bool arr_info_ok = false;
 };
 
 namespace {
@@ -170,14 +172,52 @@ const char* engine_name(int e) {
 // stream.  A GEMM workgroup whose tiles wait for the copies must never fill every compute unit so
 // completely that no copy wave can be placed: then, if the GEMM's persistent grid is dispatched
 // first, its waiting tiles spin until the limit while the copies cannot start.  The copy kernel
-// needs at most 64 VGPRs per lane and a few bytes of LDS; a GEMM that leaves less than that on a
+// needs few bytes of LDS and copy_vgprs registers per lane; a GEMM that leaves less than that on a
 // SIMD (its resident waves times their registers, of the 512 per lane) gets 8 compute units, one
 // per XCD, left out of its grid.
-int reserved_cus(const KernelInfo& g, bool copies_beside) {
+int reserved_cus(const KernelInfo& g, bool copies_beside, int copy_vgprs) {
   if (!copies_beside) return 0;
   const int waves_per_simd = std::max(1, g.max_blocks_per_cu * (g.threads / 64) / 4);
   const int regs = (g.vgprs_per_wave + 7) / 8 * 8;
-  return waves_per_simd * regs > 512 - 64 ? 8 : 0;
+  return waves_per_simd * regs > 512 - copy_vgprs ? 8 : 0;
+}
+
+// Registers per lane of one copy-kernel wave, rounded up to the allocation granule of 8.
+int copy_wave_vgprs(rag_ctx* c, int* out) {
+  if (!c->arr_info_ok) {
+    HIPCHK(arrival_kernel_info(c->device, &c->arr_info));
+    c->arr_info_ok = true;
+  }
+  *out = (c->arr_info.vgprs_per_wave + 7) / 8 * 8;
+  return RAG_OK;
+}
+
+int ag_info(rag_ctx* c, int tile, bool fp8, bool out8, const KernelInfo** out) {
+  if (!c->ag_info_ok[tile][fp8][out8]) {
+    HIPCHK(ag_kernel_info(c->device, tile, fp8, out8, &c->ag_info[tile][fp8][out8]));
+    c->ag_info_ok[tile][fp8][out8] = true;
+  }
+  *out = &c->ag_info[tile][fp8][out8];
+  return RAG_OK;
+}
+
+// The tile an AG+GEMM launch uses: choose_ag_tile's, except that with the automatic choice and a
+// copy kernel beside the GEMM, an 8-wave 256x256 kernel that would need compute units kept free
+// (above) gives way to the 4-stage 8-wave kernel of the same tile size if that one leaves room
+// for the copy waves: the copies then run on every compute unit instead of 8.
+int ag_launch_tile(rag_ctx* c, int nc, int M, int tp, bool fp8, bool out8, bool beside,
+                   int* tile) {
+  *tile = choose_ag_tile(c, nc, M, tp);
+  if (!beside || c->tile != RAG_TILE_AUTO || *tile != kTile256x256w8) return RAG_OK;
+  int cv = 0;
+  const KernelInfo *w8 = nullptr, *s4 = nullptr;
+  int rc = copy_wave_vgprs(c, &cv);
+  if (!rc) rc = ag_info(c, kTile256x256w8, fp8, out8, &w8);
+  if (!rc) rc = ag_info(c, kTile256x256w8s4, fp8, out8, &s4);
+  if (rc) return rc;
+  if (reserved_cus(*w8, true, cv) > 0 && reserved_cus(*s4, true, cv) == 0)
+    *tile = kTile256x256w8s4;
+  return RAG_OK;
 }
 
 int choose_rs_tile(const rag_ctx* c, int nc, int Mo, int tp) {
@@ -529,9 +569,14 @@ int rs_call(rag_ctx* c, const char* fn, bool ring, const void* X, int T, int Kl,
   }
   // With copies beside it, the automatic choice prefers a tile that leaves every compute unit
   // room for copy waves: the copies then spread over the whole GPU instead of 8 CUs.
-  if (beside && c->tile == RAG_TILE_AUTO && reserved_cus(c->rs_info[tile], true) > 0) {
+  int copy_vgprs = 0;
+  if (beside) {
+    const int rc = copy_wave_vgprs(c, &copy_vgprs);
+    if (rc) return rc;
+  }
+  if (beside && c->tile == RAG_TILE_AUTO && reserved_cus(c->rs_info[tile], true, copy_vgprs) > 0) {
     for (int t : {(int)kTile256x128, (int)kTile128x128})
-      if (reserved_cus(c->rs_info[t], true) == 0) {
+      if (reserved_cus(c->rs_info[t], true, copy_vgprs) == 0) {
         tile = t;
         break;
       }
@@ -541,7 +586,8 @@ int rs_call(rag_ctx* c, const char* fn, bool ring, const void* X, int T, int Kl,
   a.tiles_i = (nc + bi - 1) / bi;
   a.tiles_j = (Mo + bj - 1) / bj;
   const int total = a.tiles_i * a.tiles_j * tp;
-  const int grid = persistent_grid(total, c->num_cus - reserved_cus(c->rs_info[tile], beside),
+  const int grid = persistent_grid(total,
+                                   c->num_cus - reserved_cus(c->rs_info[tile], beside, copy_vgprs),
                                    c->rs_info[tile].max_blocks_per_cu);
   if (debug_enabled())
     fprintf(stderr, "[ringag] %s tp=%d s=%d T=%d Kl=%d Mo=%d tile=%dx%d tiles=%d grid=%d "
@@ -812,11 +858,18 @@ int ag_gemm_ex(rag_ctx* c, const void* A, int M, int K, const void* const* B, in
                            "staging buffer");
     if (rc) return rc;
   }
+  // copies beside the GEMM: a copy kernel on the side stream (the engine of the single launch)
+  const bool beside = !no_copy && c->copy_engine == RAG_COPY_KERNEL;
+  int tile = 0;
+  {
+    const int rc = ag_launch_tile(c, nc, M, tp, fp8, out8, beside && !(flags & RAG_PER_CHUNK), &tile);
+    if (rc) return rc;
+  }
   const int epoch = next_epoch(c);
   unsigned long long* trace = nullptr;
   if (c->trace_buf) {
     int bi, bj;
-    tile_dims(choose_ag_tile(c, nc, M, tp), &bi, &bj);
+    tile_dims(tile, &bi, &bj);
     const long long tiles = (long long)((nc + bi - 1) / bi) * ((M + bj - 1) / bj) * tp;
     if ((kTraceHeader + kTraceTileWords * tiles) * 8 <= c->trace_bytes)
       trace = reinterpret_cast<unsigned long long*>(c->trace_buf);
@@ -836,7 +889,6 @@ int ag_gemm_ex(rag_ctx* c, const void* A, int M, int K, const void* const* B, in
   // into G.  Engines: a copy kernel on the side stream, SDMA on the side stream, or the GEMM's
   // own workgroups (in-kernel: no side stream, no fork or join).
   const bool in_kernel = !no_copy && c->copy_engine == RAG_COPY_IN_GEMM;
-  const int tile = choose_ag_tile(c, nc, M, tp);
   CopyPlan cp = {};
   if (!no_copy) {
     int n = 0;
@@ -945,9 +997,13 @@ int ag_gemm_ex(rag_ctx* c, const void* A, int M, int K, const void* const* B, in
     const int total = a.tiles_i * a.tiles_j * tp;
     int bpc = c->ag_info[tile][fp8][out8].max_blocks_per_cu;
     if (c->wgs_per_cu > 0) bpc = std::min(bpc, c->wgs_per_cu);
-    const bool beside = !no_copy && c->copy_engine == RAG_COPY_KERNEL;
-    const int grid =
-        persistent_grid(total, c->num_cus - reserved_cus(c->ag_info[tile][fp8][out8], beside), bpc);
+    int copy_vgprs = 0;
+    if (beside) {
+      const int rc = copy_wave_vgprs(c, &copy_vgprs);
+      if (rc) return rc;
+    }
+    const int grid = persistent_grid(
+        total, c->num_cus - reserved_cus(c->ag_info[tile][fp8][out8], beside, copy_vgprs), bpc);
     // in-kernel copies: workgroups w with (w / 8) % copy_stride == 0 take part (workgroup 0 always)
     a.copy_stride = 1;
     if (a.copies && c->gemm_copy_wgs > 0 && grid >= 8)
@@ -1078,7 +1134,12 @@ int rag_ag_kernel_name(rag_ctx* c, int nc, int M, int tp, rag_dtype dt, char* bu
   if (!c || !buf || len < 1 || nc < 1 || M < 1 || tp < 1)
     return fail(RAG_EINVAL, "rag_ag_kernel_name: bad arguments");
   if (dt != RAG_BF16 && dt != RAG_FP8_E4M3) return fail(RAG_EINVAL, "unknown dtype %d", dt);
-  snprintf(buf, (size_t)len, "%s", ag_kernel_name(choose_ag_tile(c, nc, M, tp), dt == RAG_FP8_E4M3));
+  const bool fp8 = dt == RAG_FP8_E4M3;
+  int tile = 0;
+  const int rc =
+      ag_launch_tile(c, nc, M, tp, fp8, false, c->copy_engine == RAG_COPY_KERNEL, &tile);
+  if (rc) return rc;
+  snprintf(buf, (size_t)len, "%s", ag_kernel_name(tile, fp8));
   return RAG_OK;
 }
 

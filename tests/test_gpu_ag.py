@@ -80,6 +80,25 @@ def test_ag_ragged_tiles_random(tile, engine):
     assert rel_err(run.D_bits(), ref) <= TOL_BF16
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("nsteps", [1, 2, 3])
+@pytest.mark.parametrize("tile", TILE_NAMES)
+def test_ag_short_k_every_tile(tile, nsteps, dtype):
+    """K of one, two and three 128-byte k-steps: the K loop's first stage alone, one stage
+    handover, and the DMA past the last stage that the loop drains; exact integers on a ragged
+    shape, every tile."""
+    c = ctx()
+    c.set_option(B.RAG_OPT_TILE, B.TILES[tile])
+    K = nsteps * (128 if dtype == "fp8" else 64)
+    inp = _int_case(2, 1, 100, K=K, M=90, seed=900 + nsteps, dtype=dtype)
+    say(f"case short K={K} dtype={dtype} tile={tile}")
+    run = AGRun(inp).run(c)
+    G_ref, ref = oracle_ag(inp)
+    bits = W.bits_u8 if dtype == "fp8" else W.bits_u16
+    assert np.array_equal(bits(run.G.cpu()), G_ref)
+    assert np.array_equal(run.D_bits(), O.f32_to_bf16(ref))
+
+
 def test_ag_bitwise_invariant_across_ranks_and_modes():
     """Chunking splits the gathered rows, not K: the result must not depend on the self rank,
     on whether chunks arrive (counters) or are already there, or on the split at all (tp=1)."""

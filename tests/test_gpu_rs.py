@@ -81,6 +81,22 @@ def test_rs_exact_integers(tp, s):
     _check_send(run, send_ref, exact=True)
 
 
+@pytest.mark.parametrize("kl", [64, 128, 192])
+@pytest.mark.parametrize("tile", ["128x128", "256x128", "256x256", "256x256w8", "256x256w8s4"])
+def test_rs_short_k_every_tile(tile, kl):
+    """Local K of one, two and three 128-byte k-steps (the K loop's first stage alone, one
+    handover, the drained DMA past the last stage), exact integers, every tile."""
+    c = ctx()
+    c.set_option(B.RAG_OPT_TILE, B.TILES[tile])
+    shape = W.rs_shape(4, 2, 4 * 72, kl, 136, dist="int3", seed=kl + 5)
+    say(f"case {shape.name} tile={tile}")
+    inp = W.make_rs(shape)
+    run = RSRun(inp).run(c)
+    D_ref, send_ref, _ = oracle_rs(inp)
+    assert np.array_equal(W.bits_u16(run.D.cpu()), O.f32_to_bf16(D_ref))
+    _check_send(run, send_ref, exact=True)
+
+
 @pytest.mark.parametrize("tile", ["128x128", "256x128", "256x256", "256x256w8", "256x256w8s4"])
 def test_rs_padded_row_stride(tile):
     """Partials and incoming sums with a row stride past Mo (views of NaN-padded buffers): the
