@@ -228,6 +228,15 @@ __device__ inline void stage_mma(const char* xs, const char* ys, int lane,
   }
 }
 
+// Stage handover inside the K loops: wait until at most N DMA instructions and no LDS reads of
+// this wave are outstanding (one instruction; the asm is also a compiler memory barrier), then
+// meet the workgroup at the barrier, which the backend keeps ordered with every memory access.
+template <int N>
+__device__ inline void stage_handover() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+  __builtin_amdgcn_s_barrier();
+}
+
 template <class S>
 __device__ inline void load_frags_bf16(bf16x8 (&a)[S::FI], bf16x8 (&b)[S::FJ], const char* xs,
                                        const char* ys, int seg, int lane) {
@@ -237,21 +246,21 @@ __device__ inline void load_frags_bf16(bf16x8 (&a)[S::FI], bf16x8 (&b)[S::FJ], c
   for (int f = 0; f < S::FJ; ++f) b[f] = frag_bf16<S::BKB>(ys + f * 32 * S::BKB, seg, lane);
 }
 
-// bf16 K loop over two LDS stages with the stage handover inside a stage's last MFMA k-step.
+// bf16 K loop over NS LDS stages with the stage handover inside a stage's last MFMA k-step.
 // Fragments are double-buffered as in stage_mma.  Once the fragments of the last k-step are in
 // registers, the wave waits for its DMA of the next stage and for its reads, meets the others at
-// the barrier, reads the next stage's first fragments, and starts the DMA of the stage after next
-// into the buffer just read, its DMA instructions spread over the MFMAs of that last k-step; so
-// no fragment read waits right behind a barrier, and the DMA issue hides under MFMAs.  The loop
-// body has no branch: past the last stage the DMA reads at kOOB (zeros, into a buffer nobody
-// reads) and the prefetch reads the idle buffer; the DMA is drained before the final barrier.
+// the barrier, reads the next stage's first fragments, and starts the DMA of stage kt + NS into
+// the buffer just read, its DMA instructions spread over the MFMAs of that last k-step; so no
+// fragment read waits right behind a barrier, and the DMA issue hides under MFMAs.  The loop body
+// has no branch: past the last stage the DMA reads at kOOB (zeros, into a buffer nobody reads) and
+// the prefetch reads an idle buffer; the DMA is drained before the final barrier.
 template <class S>
-__device__ inline void tile_kloop_2s(i32x4 rx, const uint32_t* xo, i32x4 ry, const uint32_t* yo,
-                                     int ksteps, char* lds, int wave, int lane,
-                                     f32x16 (&acc)[S::FI][S::FJ]) {
+__device__ inline void tile_kloop_bf16(i32x4 rx, const uint32_t* xo, i32x4 ry, const uint32_t* yo,
+                                       int ksteps, char* lds, int wave, int lane,
+                                       f32x16 (&acc)[S::FI][S::FJ]) {
   constexpr int NK = S::SEGS / 2;
   constexpr int NM = S::FI * S::FJ;
-  static_assert(S::NS == 2 && NK % 2 == 0, "two stages of an even number of k-steps");
+  static_assert(NK % 2 == 0, "an even number of MFMA k-steps per stage");
   const int wi = wave / S::WJ, wj = wave % S::WJ;
   const int h = lane >> 5;
   const uint32_t base = lds_addr(lds);
@@ -265,20 +274,26 @@ __device__ inline void tile_kloop_2s(i32x4 rx, const uint32_t* xo, i32x4 ry, con
     __syncthreads();
     return;
   }
-  issue_loads<S, S::XQ>(rx, xo, 0, base, wave);
-  issue_loads<S, S::YQ>(ry, yo, 0, base + S::BI * S::BKB, wave);
-  wait_vmem<0>();
+  // stages 0 .. NS-2, then (stage 0 complete everywhere) stage NS-1
+#pragma unroll
+  for (int st = 0; st < S::NS - 1; ++st) {
+    const uint32_t kb = st < ksteps ? (uint32_t)st * S::BKB : kOOB;
+    issue_loads<S, S::XQ>(rx, xo, kb, base + st * S::STAGE, wave);
+    issue_loads<S, S::YQ>(ry, yo, kb, base + st * S::STAGE + S::BI * S::BKB, wave);
+  }
+  wait_vmem<(S::NS - 2) * S::LOADS>();
   __syncthreads();
   {
-    const uint32_t kb = ksteps > 1 ? (uint32_t)S::BKB : kOOB;
-    issue_loads<S, S::XQ>(rx, xo, kb, base + S::STAGE, wave);
-    issue_loads<S, S::YQ>(ry, yo, kb, base + S::STAGE + S::BI * S::BKB, wave);
+    const uint32_t kb = S::NS - 1 < ksteps ? (uint32_t)(S::NS - 1) * S::BKB : kOOB;
+    issue_loads<S, S::XQ>(rx, xo, kb, base + (S::NS - 1) * S::STAGE, wave);
+    issue_loads<S, S::YQ>(ry, yo, kb, base + (S::NS - 1) * S::STAGE + S::BI * S::BKB, wave);
   }
   const int xrow = wi * S::TM * S::BKB, yrow = (S::BI + wj * S::TN) * S::BKB;
   bf16x8 a[2][S::FI], b[2][S::FJ];
   load_frags_bf16<S>(a[0], b[0], lds + xrow, lds + yrow, h, lane);
   for (int kt = 0; kt < ksteps; ++kt) {
-    const int cur = (kt & 1) * S::STAGE, nxt = S::STAGE - cur;
+    const int cur = (S::NS == 2 ? (kt & 1) : kt % S::NS) * S::STAGE;
+    const int nxt = S::NS == 2 ? S::STAGE - cur : ((kt + 1) % S::NS) * S::STAGE;
 #pragma unroll
     for (int kk = 0; kk < NK - 1; ++kk) {
       const int c = kk & 1;
@@ -293,12 +308,12 @@ __device__ inline void tile_kloop_2s(i32x4 rx, const uint32_t* xo, i32x4 ry, con
               __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // last k-step of the stage (its fragments are in set 1: NK is even)
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
+    // last k-step of the stage (its fragments are in set 1: NK is even).  Outstanding DMA: stages
+    // kt+1 .. kt+NS-1; stage kt+1 is complete once at most NS-2 of them are.
+    stage_handover<(S::NS - 2) * S::LOADS>();
     load_frags_bf16<S>(a[0], b[0], lds + nxt + xrow, lds + nxt + yrow, h, lane);
     __builtin_amdgcn_sched_barrier(0);
-    const uint32_t kb = kt + 2 < ksteps ? (uint32_t)(kt + 2) * S::BKB : kOOB;
+    const uint32_t kb = kt + S::NS < ksteps ? (uint32_t)(kt + S::NS) * S::BKB : kOOB;
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       const int i = m / S::FJ, j = m % S::FJ;
@@ -322,7 +337,7 @@ __device__ inline void tile_kloop_2s(i32x4 rx, const uint32_t* xo, i32x4 ry, con
   __syncthreads();
 }
 
-// The same two-stage loop for fp8 (64-k MFMA steps, 32-byte fragments).  A second full fragment
+// The two-stage form of that loop for fp8 (64-k MFMA steps, 32-byte fragments).  A second full fragment
 // set does not fit beside the 8-wave tile's accumulators, so only the Y (B operand) fragments are
 // double-buffered and the X fragments rotate in place: X fragment i of the next k-step is read as
 // soon as the MFMAs of row i are issued, with the rest of the k-step's MFMAs to land in.  In a
@@ -394,8 +409,7 @@ __device__ inline void tile_kloop_2s_fp8(i32x4 rx, const uint32_t* xo, i32x4 ry,
 #pragma unroll
     for (int j = 0; j < S::FJ; ++j) acc[0][j] = mma(a[0], b[1][j], acc[0][j]);
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
+    stage_handover<0>();
 #pragma unroll
     for (int f = 0; f < S::FJ; ++f) b[0][f] = yfrag(nxt, f, 0);
     const uint32_t kb = kt + 2 < ksteps ? (uint32_t)(kt + 2) * S::BKB : kOOB;
@@ -432,9 +446,11 @@ template <class S, bool FP8>
 __device__ inline void tile_kloop(i32x4 rx, const uint32_t* xo, i32x4 ry, const uint32_t* yo,
                                   int ksteps, char* lds, int wave, int lane,
                                   f32x16 (&acc)[S::FI][S::FJ]) {
-  if constexpr (S::NS == 2) {
-    if constexpr (FP8) tile_kloop_2s_fp8<S>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);
-    else tile_kloop_2s<S>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);
+  if constexpr (!FP8) {
+    tile_kloop_bf16<S>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);
+    return;
+  } else if constexpr (S::NS == 2) {
+    tile_kloop_2s_fp8<S>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);
     return;
   }
   const int wi = wave / S::WJ, wj = wave % S::WJ;
