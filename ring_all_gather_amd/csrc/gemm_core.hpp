@@ -246,11 +246,31 @@ __device__ inline void load_frags_bf16(bf16x8 (&a)[S::FI], bf16x8 (&b)[S::FJ], c
   for (int f = 0; f < S::FJ; ++f) b[f] = frag_bf16<S::BKB>(ys + f * 32 * S::BKB, seg, lane);
 }
 
+// DMA instructions [q0, q1) of a stage (X rows first, then Y rows) into the stage buffer at byte
+// offset buf of the LDS, at K offset kb.
+template <class S>
+__device__ inline void dma_range(i32x4 rx, const uint32_t* xo, i32x4 ry, const uint32_t* yo,
+                                 uint32_t base, int buf, uint32_t kb, int wave, int q0, int q1) {
+#pragma unroll
+  for (int q = q0; q < q1; ++q) {
+    if (q < S::XQ)
+      dma16(rx, base + buf + (uint32_t)((q * S::NW + wave) * S::RPI * S::BKB), xo[q] + kb);
+    else
+      dma16(ry,
+            base + buf + S::BI * S::BKB +
+                (uint32_t)(((q - S::XQ) * S::NW + wave) * S::RPI * S::BKB),
+            yo[q - S::XQ] + kb);
+  }
+}
+
 // bf16 K loop over NS LDS stages with the stage handover inside a stage's last MFMA k-step.
 // Fragments are double-buffered as in stage_mma.  Once the fragments of the last k-step are in
 // registers, the wave waits for its DMA of the next stage and for its reads, meets the others at
 // the barrier, reads the next stage's first fragments, and starts the DMA of stage kt + NS into
-// the buffer just read, its DMA instructions spread over the MFMAs of that last k-step; so no
+// the buffer just read.  That DMA is issued in two halves, one DMA instruction after each of a few
+// MFMAs: the first half over the last k-step of stage kt, the second over the first k-step of
+// stage kt + 1 (all of a stage's DMA in one k-step queues up in the memory pipeline and stalls the
+// wave's MFMA issue; spread further, the last pieces have too little time to land).  So no
 // fragment read waits right behind a barrier, and the DMA issue hides under MFMAs.  The loop body
 // has no branch: past the last stage the DMA reads at kOOB (zeros, into a buffer nobody reads) and
 // the prefetch reads an idle buffer; the DMA is drained before the final barrier.
@@ -260,6 +280,7 @@ __device__ inline void tile_kloop_bf16(i32x4 rx, const uint32_t* xo, i32x4 ry, c
                                        f32x16 (&acc)[S::FI][S::FJ]) {
   constexpr int NK = S::SEGS / 2;
   constexpr int NM = S::FI * S::FJ;
+  constexpr int H = S::LOADS / 2;   // the first half of a stage's DMA
   static_assert(NK % 2 == 0, "an even number of MFMA k-steps per stage");
   const int wi = wave / S::WJ, wj = wave % S::WJ;
   const int h = lane >> 5;
@@ -274,20 +295,18 @@ __device__ inline void tile_kloop_bf16(i32x4 rx, const uint32_t* xo, i32x4 ry, c
     __syncthreads();
     return;
   }
-  // stages 0 .. NS-2, then (stage 0 complete everywhere) stage NS-1
+  // stages 0 .. NS-2, then (stage 0 complete everywhere) the first half of stage NS-1
 #pragma unroll
   for (int st = 0; st < S::NS - 1; ++st) {
     const uint32_t kb = st < ksteps ? (uint32_t)st * S::BKB : kOOB;
-    issue_loads<S, S::XQ>(rx, xo, kb, base + st * S::STAGE, wave);
-    issue_loads<S, S::YQ>(ry, yo, kb, base + st * S::STAGE + S::BI * S::BKB, wave);
+    dma_range<S>(rx, xo, ry, yo, base, st * S::STAGE, kb, wave, 0, S::LOADS);
   }
   wait_vmem<(S::NS - 2) * S::LOADS>();
   __syncthreads();
-  {
-    const uint32_t kb = S::NS - 1 < ksteps ? (uint32_t)(S::NS - 1) * S::BKB : kOOB;
-    issue_loads<S, S::XQ>(rx, xo, kb, base + (S::NS - 1) * S::STAGE, wave);
-    issue_loads<S, S::YQ>(ry, yo, kb, base + (S::NS - 1) * S::STAGE + S::BI * S::BKB, wave);
-  }
+  // the stage whose DMA is under way: its K offset and buffer
+  uint32_t pend_kb = S::NS - 1 < ksteps ? (uint32_t)(S::NS - 1) * S::BKB : kOOB;
+  int pend_buf = (S::NS - 1) * S::STAGE;
+  dma_range<S>(rx, xo, ry, yo, base, pend_buf, pend_kb, wave, 0, H);
   const int xrow = wi * S::TM * S::BKB, yrow = (S::BI + wj * S::TN) * S::BKB;
   bf16x8 a[2][S::FI], b[2][S::FJ];
   load_frags_bf16<S>(a[0], b[0], lds + xrow, lds + yrow, h, lane);
@@ -301,35 +320,33 @@ __device__ inline void tile_kloop_bf16(i32x4 rx, const uint32_t* xo, i32x4 ry, c
                          (kk + 1) * 2 + h, lane);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < S::FI; ++i)
-#pragma unroll
-        for (int j = 0; j < S::FJ; ++j)
-          acc[i][j] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
+      for (int m = 0; m < NM; ++m) {
+        const int i = m / S::FJ, j = m % S::FJ;
+        acc[i][j] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
+        if (kk == 0) {
+          // the second half of the pending stage's DMA, spread over this k-step's MFMAs
+          __builtin_amdgcn_sched_barrier(0);
+          dma_range<S>(rx, xo, ry, yo, base, pend_buf, pend_kb, wave,
+                       H + m * (S::LOADS - H) / NM, H + (m + 1) * (S::LOADS - H) / NM);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     // last k-step of the stage (its fragments are in set 1: NK is even).  Outstanding DMA: stages
-    // kt+1 .. kt+NS-1; stage kt+1 is complete once at most NS-2 of them are.
+    // kt+1 .. kt+NS-1, all issued in full; stage kt+1 is complete once at most NS-2 of them are.
     stage_handover<(S::NS - 2) * S::LOADS>();
     load_frags_bf16<S>(a[0], b[0], lds + nxt + xrow, lds + nxt + yrow, h, lane);
     __builtin_amdgcn_sched_barrier(0);
-    const uint32_t kb = kt + S::NS < ksteps ? (uint32_t)(kt + S::NS) * S::BKB : kOOB;
+    pend_kb = kt + S::NS < ksteps ? (uint32_t)(kt + S::NS) * S::BKB : kOOB;
+    pend_buf = cur;
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       const int i = m / S::FJ, j = m % S::FJ;
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][i], b[1][j], acc[i][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      // DMA instructions [m LOADS / NM, (m + 1) LOADS / NM) after MFMA m
-#pragma unroll
-      for (int q = m * S::LOADS / NM; q < (m + 1) * S::LOADS / NM; ++q) {
-        if (q < S::XQ)
-          dma16(rx, base + cur + (uint32_t)((q * S::NW + wave) * S::RPI * S::BKB), xo[q] + kb);
-        else
-          dma16(ry,
-                base + cur + S::BI * S::BKB +
-                    (uint32_t)(((q - S::XQ) * S::NW + wave) * S::RPI * S::BKB),
-                yo[q - S::XQ] + kb);
-      }
+      dma_range<S>(rx, xo, ry, yo, base, pend_buf, pend_kb, wave, m * H / NM, (m + 1) * H / NM);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -337,7 +354,10 @@ __device__ inline void tile_kloop_bf16(i32x4 rx, const uint32_t* xo, i32x4 ry, c
   __syncthreads();
 }
 
-// The two-stage form of that loop for fp8 (64-k MFMA steps, 32-byte fragments).  A second full fragment
+// The two-stage form of that loop for fp8 (64-k MFMA steps, 32-byte fragments).  A stage holds
+// only two MFMA k-steps here, so the DMA of a stage stays in the last k-step before the handover:
+// issued half of it one k-step later, the second half had one k-step to land and the launch lost
+// 10%.  A second full fragment
 // set does not fit beside the 8-wave tile's accumulators, so only the Y (B operand) fragments are
 // double-buffered and the X fragments rotate in place: X fragment i of the next k-step is read as
 // soon as the MFMAs of row i are issued, with the rest of the k-step's MFMAs to land in.  In a
@@ -368,8 +388,7 @@ __device__ inline void tile_kloop_2s_fp8(i32x4 rx, const uint32_t* xo, i32x4 ry,
   __syncthreads();
   {
     const uint32_t kb = ksteps > 1 ? (uint32_t)S::BKB : kOOB;
-    issue_loads<S, S::XQ>(rx, xo, kb, base + S::STAGE, wave);
-    issue_loads<S, S::YQ>(ry, yo, kb, base + S::STAGE + S::BI * S::BKB, wave);
+    dma_range<S>(rx, xo, ry, yo, base, S::STAGE, kb, wave, 0, S::LOADS);
   }
   const int xrow = wi * S::TM * S::BKB, yrow = (S::BI + wj * S::TN) * S::BKB;
   // k-step kk's fragments of the stage at offset st
@@ -421,17 +440,9 @@ __device__ inline void tile_kloop_2s_fp8(i32x4 rx, const uint32_t* xo, i32x4 ry,
       }
       __builtin_amdgcn_sched_barrier(0);
       a[i] = xfrag(nxt, i, 0);
-      // DMA instructions [i LOADS / FI, (i + 1) LOADS / FI) after row i
-#pragma unroll
-      for (int q = i * S::LOADS / S::FI; q < (i + 1) * S::LOADS / S::FI; ++q) {
-        if (q < S::XQ)
-          dma16(rx, base + cur + (uint32_t)((q * S::NW + wave) * S::RPI * S::BKB), xo[q] + kb);
-        else
-          dma16(ry,
-                base + cur + S::BI * S::BKB +
-                    (uint32_t)(((q - S::XQ) * S::NW + wave) * S::RPI * S::BKB),
-                yo[q - S::XQ] + kb);
-      }
+      // the DMA of stage kt + 2 into the buffer just read, spread over the rows
+      dma_range<S>(rx, xo, ry, yo, base, cur, kb, wave, i * S::LOADS / S::FI,
+                   (i + 1) * S::LOADS / S::FI);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
