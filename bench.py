@@ -64,6 +64,8 @@ def parse():
                    help="AG: skip the timeline (after the timed steps, 20 more calls traced with "
                         "the library's per-tile wall-clock stamps: for the last, when each chunk "
                         "was released and when its tiles ran)")
+    p.add_argument("--flush-calls", type=int, default=50,
+                   help="RS: calls timed with the MALL scrubbed before each (a 512 MiB write)")
     p.add_argument("--headline-only", action="store_true",
                    help="measure the headline call (and, for AG, its GEMM-only and copies-only "
                         "forms) but none of the other variants; for counter-collection runs, "
@@ -195,8 +197,13 @@ def timeline_ag(ctx, B, step, shape, kname):
                        "released_us": 0.0 if j == 0 else us(w[j - 1]),
                        "first_tile_go_us": us(min(x[1] for x in tj)),
                        "last_tile_end_us": us(max(x[2] for x in tj))})
+    # the core clock the tiles ran at: s_memtime cycles over the 100 MHz wall time of each tile's
+    # computation (from after its wait to its end), in GHz
+    clk = sorted(x[4] / ((x[2] - x[1]) * 10.0) for x in tiles if x[2] > x[1])
+    q = lambda f: round(clk[min(len(clk) - 1, int(f * len(clk)))], 3) if clk else None
     return {"tiles_per_chunk": per_chunk, "copies_start_us": us(w[32]),
-            "gemm_end_us": us(max(x[2] for x in tiles)), "chunks": chunks}
+            "gemm_end_us": us(max(x[2] for x in tiles)),
+            "tile_clock_ghz": {"p10": q(0.1), "p50": q(0.5), "p90": q(0.9)}, "chunks": chunks}
 
 
 def measured_traffic(workload: str, kernel: str, fingerprint: str):
@@ -355,6 +362,25 @@ def main():
                          "algorithmic_bytes": alg_bytes},
         }
         if not args.headline_only:
+            # the same launch with the 256 MB MALL scrubbed before each call (a 512 MiB buffer
+            # written in between), timed by the launches' own events: the partials and operands
+            # then come from HBM, not from the memory-side cache that holds them in steady state
+            scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+            ctx.kernel_times()
+            ctx.set_option(B.RAG_OPT_TIMING, 1)
+            for i in range(args.flush_calls):
+                scrub.fill_(i & 0xFF)
+                step()
+            torch.cuda.synchronize()
+            kt_flushed = ctx.kernel_times()
+            ctx.set_option(B.RAG_OPT_TIMING, 0)
+            del scrub
+            kms_f = statistics.fmean(kt_flushed)
+            gbs_f = alg_bytes / (kms_f * 1e-3) / 1e9
+            out["mall_scrubbed"] = {"calls": len(kt_flushed), "kernel_ms": round(kms_f, 5),
+                                    "achieved_GBps": round(gbs_f, 1),
+                                    "frac": round(gbs_f / PEAK_HBM_GBS, 4),
+                                    "tflops": round(flops / (kms_f * 1e-3) / 1e12, 2)}
             # the counter-gated forms: the peers' partials arrive during the call (side-stream
             # copies in ring order, tiles wait before their epilogue), and one ring-accumulate step
             # with its incoming running sums given or arriving
