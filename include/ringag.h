@@ -152,7 +152,8 @@ enum {
 enum { RAG_TILE_AUTO = 0, RAG_TILE_128x128 = 1, RAG_TILE_256x128 = 2,
        RAG_TILE_256x256 = 3 /* 4 waves of 128x128, 2 LDS stages of 128-byte rows */,
        RAG_TILE_256x256_8W = 4 /* 8 waves of 128x64, 2 LDS stages of 128-byte rows */,
-       RAG_TILE_256x256_8W_S4 = 5 /* 8 waves of 128x64, 4 LDS stages of 64-byte rows */ };
+       RAG_TILE_256x256_8W_S4 = 5 /* 8 waves of 128x64, 4 LDS stages of 64-byte rows */,
+       RAG_TILE_256x192_8W = 6 /* 8 waves of 64x96, 2 LDS stages of 128-byte rows */ };
 
 typedef struct rag_ctx rag_ctx;     /* opaque; owned by the library */
 

@@ -35,7 +35,8 @@ RAG_OPT_GEMM_COPY_WGS = 12
 RAG_COPY_KERNEL, RAG_COPY_SDMA, RAG_COPY_IN_GEMM = 0, 1, 2
 ENGINES = {"kernel": RAG_COPY_KERNEL, "sdma": RAG_COPY_SDMA, "in-gemm": RAG_COPY_IN_GEMM}
 TRACE_HEADER, TRACE_START, TRACE_TILE_WORDS = 64, 32, 5
-TILES = {"auto": 0, "128x128": 1, "256x128": 2, "256x256": 3, "256x256w8": 4, "256x256w8s4": 5}
+TILES = {"auto": 0, "128x128": 1, "256x128": 2, "256x256": 3, "256x256w8": 4, "256x256w8s4": 5,
+         "256x192w8": 6}
 RAG_MAX_TP = 16
 
 _lib = None

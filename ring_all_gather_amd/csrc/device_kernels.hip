@@ -5,7 +5,7 @@
 // Entry points: rag_ag_<bf16|fp8>[_o8]_<tile> (input dtype; _o8 = E4M3 output), rag_rs_<tile>,
 // rag_arrival.  Tile names:
 //   t128x128, t256x128, t256x256 (4 waves, 2 stages), t256x256w8 (8 waves, 2 stages), t256x256w8s4
-//   (8 waves, 4 stages); see gemm_core.hpp.
+//   (8 waves, 4 stages), t256x192w8 (8 waves, 2 stages); see gemm_core.hpp.
 #include "arrival_kernel.hpp"
 #include "gemm_ag_kernel.hpp"
 #include "gemm_rs_kernel.hpp"
@@ -44,6 +44,7 @@ RAG_AG_ENTRY(t256x128, Tile256x128)
 RAG_AG_ENTRY(t256x256, Tile256x256)
 RAG_AG_ENTRY(t256x256w8, Tile256x256w8)
 RAG_AG_ENTRY(t256x256w8s4, Tile256x256w8s4)
+RAG_AG_ENTRY(t256x192w8, Tile256x192w8)
 
 extern "C" __global__ void __launch_bounds__(kArrivalThreads) rag_arrival(ArrivalArgs a) {
   arrival_body(a);

@@ -69,6 +69,7 @@ using Tile256x128 = TileShape<256, 128, 2, 2, 128, 2>;
 using Tile256x256 = TileShape<256, 256, 2, 2, 128, 2>;      // 4 waves of 128x128, 2 stages
 using Tile256x256w8 = TileShape<256, 256, 2, 4, 128, 2>;    // 8 waves of 128x64, 2 stages
 using Tile256x256w8s4 = TileShape<256, 256, 2, 4, 64, 4>;   // 8 waves of 128x64, 4 stages
+using Tile256x192w8 = TileShape<256, 192, 4, 2, 128, 2>;    // 8 waves of 64x96, 2 stages
 
 // The tile this workgroup runs in the round that covers ring-ordered tiles [r0, r0 + n) of a grid
 // of `grid` workgroups, or -1.  Workgroup w runs on XCD w % 8 (workgroups are dealt to the 8 XCDs

@@ -121,8 +121,10 @@ constexpr int kTraceStart = 32;
 constexpr int kTraceTileWords = 5;
 
 enum TileCfg {
-  kTile128x128 = 1, kTile256x128 = 2, kTile256x256 = 3, kTile256x256w8 = 4, kTile256x256w8s4 = 5
+  kTile128x128 = 1, kTile256x128 = 2, kTile256x256 = 3, kTile256x256w8 = 4, kTile256x256w8s4 = 5,
+  kTile256x192w8 = 6
 };
+constexpr int kNumTiles = 7;   // tile ids 1 .. kNumTiles - 1
 
 struct KernelInfo {
   int threads;
@@ -157,7 +159,8 @@ constexpr int kArrivalThreads = 256;   // block size of the arrival kernel
 
 // Threads per workgroup of a tile configuration (4 waves, or 8 for the 8-wave tiles).
 inline int tile_threads(int tile) {
-  return (tile == kTile256x256w8 || tile == kTile256x256w8s4) ? 512 : 256;
+  return (tile == kTile256x256w8 || tile == kTile256x256w8s4 || tile == kTile256x192w8) ? 512
+                                                                                      : 256;
 }
 
 // Tile sizes of a configuration.
@@ -166,6 +169,7 @@ inline void tile_dims(int tile, int* bi, int* bj) {
     case kTile256x256:
     case kTile256x256w8:
     case kTile256x256w8s4: *bi = 256; *bj = 256; break;
+    case kTile256x192w8: *bi = 256; *bj = 192; break;
     case kTile256x128: *bi = 256; *bj = 128; break;
     default: *bi = 128; *bj = 128; break;
   }

@@ -28,20 +28,20 @@ namespace ringag {
 namespace {
 
 constexpr int kMaxDevices = 64;
-constexpr int kTiles = 6;   // tile ids 1..5
+constexpr int kTiles = kNumTiles;
 
 const char* const kAgName[2][2][kTiles] = {   // [fp8 input][fp8 output][tile]
     {{nullptr, "rag_ag_bf16_t128x128", "rag_ag_bf16_t256x128", "rag_ag_bf16_t256x256",
-      "rag_ag_bf16_t256x256w8", "rag_ag_bf16_t256x256w8s4"},
+      "rag_ag_bf16_t256x256w8", "rag_ag_bf16_t256x256w8s4", "rag_ag_bf16_t256x192w8"},
      {nullptr, "rag_ag_bf16_o8_t128x128", "rag_ag_bf16_o8_t256x128", "rag_ag_bf16_o8_t256x256",
-      "rag_ag_bf16_o8_t256x256w8", "rag_ag_bf16_o8_t256x256w8s4"}},
+      "rag_ag_bf16_o8_t256x256w8", "rag_ag_bf16_o8_t256x256w8s4", "rag_ag_bf16_o8_t256x192w8"}},
     {{nullptr, "rag_ag_fp8_t128x128", "rag_ag_fp8_t256x128", "rag_ag_fp8_t256x256",
-      "rag_ag_fp8_t256x256w8", "rag_ag_fp8_t256x256w8s4"},
+      "rag_ag_fp8_t256x256w8", "rag_ag_fp8_t256x256w8s4", "rag_ag_fp8_t256x192w8"},
      {nullptr, "rag_ag_fp8_o8_t128x128", "rag_ag_fp8_o8_t256x128", "rag_ag_fp8_o8_t256x256",
-      "rag_ag_fp8_o8_t256x256w8", "rag_ag_fp8_o8_t256x256w8s4"}}};
+      "rag_ag_fp8_o8_t256x256w8", "rag_ag_fp8_o8_t256x256w8s4", "rag_ag_fp8_o8_t256x192w8"}}};
 const char* const kRsName[kTiles] = {nullptr, "rag_rs_t128x128", "rag_rs_t256x128",
                                      "rag_rs_t256x256", "rag_rs_t256x256w8",
-                                     "rag_rs_t256x256w8s4"};
+                                     "rag_rs_t256x256w8s4", "rag_rs_t256x192w8"};
 
 struct DeviceKernels {
   bool loaded = false;

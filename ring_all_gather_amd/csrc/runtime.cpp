@@ -99,10 +99,10 @@ struct rag_ctx {
   std::vector<hipEvent_t> t_start, t_stop;
   int n_timed = 0;
   // occupancy cache: [tile][fp8]
-  KernelInfo ag_info[6][2][2] = {};   // [tile][fp8 input][fp8 output]
-  bool ag_info_ok[6][2][2] = {};
-  KernelInfo rs_info[6] = {};
-  bool rs_info_ok[6] = {};
+  KernelInfo ag_info[kNumTiles][2][2] = {};   // [tile][fp8 input][fp8 output]
+  bool ag_info_ok[kNumTiles][2][2] = {};
+  KernelInfo rs_info[kNumTiles] = {};
+  bool rs_info_ok[kNumTiles] = {};
   KernelInfo arr_info = {};
   bool arr_info_ok = false;
 };
@@ -153,13 +153,22 @@ int next_epoch(rag_ctx* c) {
 }
 
 // The largest tile that still gives every compute unit a tile: bigger tiles re-read less from
-// L2 per flop, but a grid with idle compute units loses more than that.
+// L2 per flop, but a grid with idle compute units loses more than that.  Between the two 8-wave
+// sizes, 256x256 and 256x192, the one whose persistent rounds leave the compute units less to do
+// in all (rounds x tile area, the 256x192 tile's area weighted 1.1 for its higher LDS and operand
+// traffic per flop): 256x192 where it fills whole rounds and 256x256 would leave a partial one
+// (8 chunks of 1024 rows by 3072 columns: 512 tiles in 2 rounds against 384 in 1.5).
 int choose_ag_tile(const rag_ctx* c, int nc, int M, int tp) {
   if (c->tile != RAG_TILE_AUTO) return c->tile;
   auto tiles = [&](int bi, int bj) {
     return (long long)((nc + bi - 1) / bi) * ((M + bj - 1) / bj) * tp;
   };
-  if (tiles(256, 256) >= c->num_cus) return kTile256x256w8;
+  if (tiles(256, 256) >= c->num_cus) {
+    auto rounds = [&](long long t) { return (t + c->num_cus - 1) / c->num_cus; };
+    const double cost256 = (double)rounds(tiles(256, 256)) * 256 * 256;
+    const double cost192 = (double)rounds(tiles(256, 192)) * 256 * 192 * 1.1;
+    return cost192 < cost256 ? kTile256x192w8 : kTile256x256w8;
+  }
   if (tiles(256, 128) >= c->num_cus) return kTile256x128;
   return kTile128x128;
 }
@@ -739,7 +748,7 @@ int rag_set_option(rag_ctx* c, int key, long long v) {
       c->trace_bytes = v;
       return RAG_OK;
     case RAG_OPT_TILE:
-      if (v < RAG_TILE_AUTO || v > RAG_TILE_256x256_8W_S4) return fail(RAG_EINVAL, "unknown tile %lld", v);
+      if (v < RAG_TILE_AUTO || v > RAG_TILE_256x192_8W) return fail(RAG_EINVAL, "unknown tile %lld", v);
       c->tile = (int)v;
       return RAG_OK;
     default:

@@ -12,7 +12,7 @@ from gpu_common import (DEV, AGRun, TOL_BF16, TOL_FP8, ctx, oracle_ag, oracle_ag
 
 pytestmark = pytest.mark.gpu
 
-TILE_NAMES = ["128x128", "256x128", "256x256", "256x256w8", "256x256w8s4"]
+TILE_NAMES = ["128x128", "256x128", "256x256", "256x256w8", "256x256w8s4", "256x192w8"]
 # copy engines of the simulated arrival that run on compute units: the side-stream copy kernel and
 # the GEMM's own waiting workgroups (SDMA is covered in the flags test)
 ENGINES = ["kernel", "in-gemm"]

@@ -56,7 +56,8 @@ def _check_send(run, send_ref, exact=False):
             assert np.abs(got[c] - send_ref[c]).max() <= TOL_SEND * scale
 
 
-@pytest.mark.parametrize("tile", ["128x128", "256x128", "256x256", "256x256w8", "256x256w8s4"])
+@pytest.mark.parametrize("tile", ["128x128", "256x128", "256x256", "256x256w8", "256x256w8s4",
+                                  "256x192w8"])
 def test_rs_ragged_random(tile):
     c = ctx()
     c.set_option(B.RAG_OPT_TILE, B.TILES[tile])
@@ -82,7 +83,8 @@ def test_rs_exact_integers(tp, s):
 
 
 @pytest.mark.parametrize("kl", [64, 128, 192])
-@pytest.mark.parametrize("tile", ["128x128", "256x128", "256x256", "256x256w8", "256x256w8s4"])
+@pytest.mark.parametrize("tile", ["128x128", "256x128", "256x256", "256x256w8", "256x256w8s4",
+                                  "256x192w8"])
 def test_rs_short_k_every_tile(tile, kl):
     """Local K of one, two and three 128-byte k-steps (the K loop's first stage alone, one
     handover, the drained DMA past the last stage), exact integers, every tile."""
@@ -97,7 +99,8 @@ def test_rs_short_k_every_tile(tile, kl):
     _check_send(run, send_ref, exact=True)
 
 
-@pytest.mark.parametrize("tile", ["128x128", "256x128", "256x256", "256x256w8", "256x256w8s4"])
+@pytest.mark.parametrize("tile", ["128x128", "256x128", "256x256", "256x256w8", "256x256w8s4",
+                                  "256x192w8"])
 def test_rs_padded_row_stride(tile):
     """Partials and incoming sums with a row stride past Mo (views of NaN-padded buffers): the
     padding must never reach D or send, in both the one-shot and the ring step forms, on ragged
