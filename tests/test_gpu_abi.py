@@ -7,7 +7,7 @@ import torch
 
 from ring_all_gather_amd import binding as B
 
-from gpu_common import DEV, ctx, say
+from gpu_common import DEV, ctx, reset_options, say
 
 pytestmark = pytest.mark.gpu
 
@@ -81,3 +81,25 @@ def test_gemm_rs_rejects_bad_arguments():
                        (dict(Mo=(1 << 20) + 4, ldp=(1 << 20) + 4), "at most")]:
         assert rs(**kw) == B.RAG_EINVAL, kw
         assert needle in B.last_error(), (kw, B.last_error())
+
+
+def test_automatic_tile_choice_by_shape():
+    """The automatic tile: the largest that gives every compute unit a tile, and between the two
+    8-wave sizes the one whose persistent rounds leave the least to do (whole rounds of 256x192
+    where 256x256 would leave a partial one).  Checked on the measured workloads' shapes, on a
+    GPU with 256 compute units."""
+    c = ctx()
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    say(f"case automatic tiles, {n_cu} compute units")
+    if n_cu != 256:
+        pytest.skip("the expected choices assume 256 compute units")
+    reset_options(c)   # automatic tile
+    c.set_option(B.RAG_OPT_COPY_ENGINE, B.ENGINES["in-gemm"])   # (no copy kernel beside the GEMM)
+    try:
+        assert c.ag_kernel_name(1024, 4096, 4) == "rag_ag_bf16_t256x256w8"   # 256 tiles: 1 round
+        assert c.ag_kernel_name(1024, 3072, 8) == "rag_ag_bf16_t256x192w8"   # 512 vs 384 tiles
+        assert c.ag_kernel_name(2048, 3584, 8, fp8=True) == "rag_ag_fp8_t256x256w8"
+        assert c.rs_kernel_name(1024, 8192, 8) == "rag_rs_t256x256w8"        # 1024 tiles: 4 rounds
+        assert c.ag_kernel_name(256, 1024, 2) == "rag_ag_bf16_t128x128"      # too few big tiles
+    finally:
+        reset_options(c)
