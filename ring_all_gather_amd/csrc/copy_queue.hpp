@@ -46,6 +46,12 @@ __device__ inline bool wait_ready(int* ctr, int epoch, int* err, long long limit
   return ok;
 }
 
+// Cache policy of the copies' stores: sc1, agent scope.  The data is written through the copying
+// XCD's L2 to the point where every XCD sees it, instead of staying dirty in that L2 until the
+// piece's agent-scope release writes the L2 back; the release then has little left to flush.
+// (ag_4k: copies-only launch 21.1 -> 18.0 us, chunked call 125.0 -> 120.6 us.)
+constexpr int kCopyStorePolicy = 16;
+
 // Copy piece k of copy c with the NT threads of the workgroup (16-byte vectors, U in flight per
 // thread).
 template <int NT, int U>
@@ -53,17 +59,21 @@ __device__ __forceinline__ void copy_piece(const CopyPlan& p, unsigned c, unsign
   const unsigned long long beg = (unsigned long long)k * p.piece_bytes;
   const unsigned long long len = min((unsigned long long)p.piece_bytes, p.bytes - beg);
   const v4i* s = (const v4i*)((const char*)p.src[c] + beg);
-  v4i* d = (v4i*)((char*)p.dst[c] + beg);
   const unsigned nvec = (unsigned)(len / 16);
+  const __amdgpu_buffer_rsrc_t d = __builtin_amdgcn_make_buffer_rsrc(
+      (char*)p.dst[c] + beg, 0, (int)(nvec * 16), 0x00020000);
   unsigned i = threadIdx.x;
   for (; i + (U - 1) * NT < nvec; i += U * NT) {
     v4i v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) v[u] = s[i + u * NT];
 #pragma unroll
-    for (int u = 0; u < U; ++u) d[i + u * NT] = v[u];
+    for (int u = 0; u < U; ++u)
+      __builtin_amdgcn_raw_buffer_store_b128(v[u], d, (int)((i + u * NT) * 16), 0,
+                                             kCopyStorePolicy);
   }
-  for (; i < nvec; i += NT) d[i] = s[i];
+  for (; i < nvec; i += NT)
+    __builtin_amdgcn_raw_buffer_store_b128(s[i], d, (int)(i * 16), 0, kCopyStorePolicy);
 }
 
 // Thread 0, after the workgroup's stores of `count` pieces of copy c are complete: add them to the
