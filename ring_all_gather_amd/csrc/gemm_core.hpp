@@ -7,12 +7,15 @@
 // Data path per K step (BKB bytes of K per row: 64 or 128 bytes, i.e. 32/64 bf16 or 64/128 fp8):
 //   HBM/L2 --buffer_load_dwordx4 ... lds (16 B per lane, range-checked by the descriptor)--> LDS
 //   LDS --ds_read_b128--> VGPR fragments --v_mfma--> accumulators
-// LDS holds NS stages in a ring: while the waves multiply stage s, the loads of the next NS-1
-// stages are in flight, so a load has NS-1 steps of MFMA work to arrive.  The loads are issued with
-// inline assembly: the compiler cannot tell which stage they write, and would otherwise wait for
-// all of them before every LDS read.  Their completion is awaited explicitly with s_waitcnt
-// vmcnt(N), N = the loads issued after the stage about to be read, followed by the one barrier of
-// the step, which also tells the loads of the step that the stage they overwrite has been read.
+// LDS holds NS stages in a ring: while the waves multiply stage s, the loads of later stages are
+// in flight.  The loads are issued with inline assembly: the compiler cannot tell which stage they
+// write, and would otherwise wait for all of them before every LDS read.  Their completion is
+// awaited explicitly with s_waitcnt vmcnt(N), N = the loads issued after the stage about to be
+// read, followed by the one barrier per stage, which also tells the loads issued after it that the
+// stage they overwrite has been read.  Where that wait and barrier sit inside the stage, and how
+// the loads and fragment reads are spread over the MFMAs, is the K loop's business: see
+// tile_kloop_bf16 and tile_kloop_2s_fp8 (the pipelined loops) and tile_kloop (the plain one, for
+// the 4-stage fp8 tile).
 //
 // LDS layout: rows of BKB bytes, split into 16-byte segments whose order is permuted by an XOR
 // key of the row (swz).  gfx950's LDS serves 256 bytes (64 banks) per cycle, i.e. 16 lanes of a
@@ -454,6 +457,8 @@ __device__ inline void tile_kloop_2s_fp8(i32x4 rx, const uint32_t* xo, i32x4 ry,
 // Full K loop of one tile.  rx/ry: descriptors of X and Y; xo/yo from tile_offsets; ksteps = K
 // bytes / BKB.  Returns with acc = the wave's fp32 sub-tile and all waves past a final barrier
 // (LDS free for the epilogue).  The caller must have passed a barrier since the last LDS reads.
+// bf16 takes the pipelined loop on every tile, fp8 on the two-stage tiles; the plain loop below
+// (barrier at the start of each stage, stage_mma per stage) is left for the 4-stage fp8 tile.
 template <class S, bool FP8>
 __device__ inline void tile_kloop(i32x4 rx, const uint32_t* xo, i32x4 ry, const uint32_t* yo,
                                   int ksteps, char* lds, int wave, int lane,
