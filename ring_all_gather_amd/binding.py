@@ -40,7 +40,6 @@ TILES = {"auto": 0, "128x128": 1, "256x128": 2, "256x256": 3, "256x256w8": 4, "2
 RAG_MAX_TP = 16
 
 _lib = None
-_is_finalizing = sys.is_finalizing
 _live = weakref.WeakSet()     # open contexts, closed at exit before the runtime shuts down
 
 
@@ -198,12 +197,13 @@ class Context:
             lib().rag_destroy(self.h)
             self.h = None
 
-    def __del__(self):
+    def __del__(self, _finalizing=sys.is_finalizing):
         # During interpreter shutdown the HIP runtime may already be going away: leave the
-        # context to the process exit (atexit above closes it earlier in a normal exit).
-        if _is_finalizing():
-            return
+        # context to the process exit (atexit above closes it earlier in a normal exit).  The
+        # check is bound as a default argument: module globals may already be gone by then.
         try:
+            if _finalizing() or not getattr(self, "h", None):
+                return
             self.close()
         except Exception:
             pass
