@@ -140,7 +140,7 @@ def cpu_baseline_ag(inp, target_s):
     O.gemm_tn_rows(G, A, rows)
     dt = time.perf_counter() - t
     return {"value": round(flops_row * nrows / dt / 1e12, 6), "unit": "TFLOP/s",
-            "cores": O.num_threads(), "kind": "oracle",
+            "cores": O.num_threads(), "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{nrows} of the {s.N} output rows (each {s.M}x{s.K} MACs, fp32 triple loop "
                       f"over the gathered input), {dt:.1f} s wall"}
 
@@ -163,9 +163,21 @@ def cpu_baseline_rs(inp, target_s):
     O.gemm_tn_rows(Xf, Wf, rows)
     dt = time.perf_counter() - t
     return {"value": round(flops_row * nrows / dt / 1e12, 6), "unit": "TFLOP/s",
-            "cores": O.num_threads(), "kind": "oracle",
+            "cores": O.num_threads(), "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{nrows} of the {s.T} rows of the local partial X W^T (each {s.Mo}x{s.Kl} "
                       f"MACs, fp32 triple loop), {dt:.1f} s wall"}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), for the CPU baseline."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def timeline_ag(ctx, B, step, shape, kname):
