@@ -137,6 +137,33 @@ __device__ inline int spread_tile(int r0, int n, int grid, int U) {
   return r0 + (q / e) * U + x * e + q % e;
 }
 
+// The tile this workgroup runs in round [r0, r0 + n) of the one-shot form when every partial is
+// in memory from the start.  A tile of the own chunk reads tp - 1 partials of its block; with the
+// own chunk last in ring order those reads all fall in the final round, where they kept half the
+// workgroups busy long after the others ran out of tiles (rs_8k: 7 x 32 MiB read by the 128 own
+// tiles of the fourth round).  Here each round takes a share of the own chunk in proportion to
+// its size, on slots that rotate from round to round (so the own tiles go to different
+// workgroups: rs_8k gives each of 128 workgroups one), and fills its other slots with the other
+// chunks' tiles in ring order.
+// With grid, round and share multiples of 8, XCD x (workgroups w with w % 8 == x) takes its eighth
+// of both as contiguous runs, as spread_tile does.  Returns a ring-ordered tile index or -1.
+__device__ inline int oneshot_tile(int r0, int n, int grid, int U, int tp) {
+  const long long total = (long long)U * tp;
+  const int ob = (int)((long long)U * r0 / total);              // own tiles of earlier rounds
+  const int oc = (int)((long long)U * (r0 + n) / total) - ob;   // own tiles of this round
+  const int nb = r0 - ob;                                       // other tiles of earlier rounds
+  const int w = (int)blockIdx.x;
+  const bool by_xcd = (grid & 7) == 0 && (n & 7) == 0 && (oc & 7) == 0;
+  const int g = by_xcd ? (w & 7) : 0;                           // slot group (XCD)
+  const int s = by_xcd ? (w >> 3) : w;                          // slot in the group
+  const int S = by_xcd ? n >> 3 : n, O = by_xcd ? oc >> 3 : oc;
+  if (s >= S) return -1;
+  const int rot = (int)((long long)(r0 / grid) * O % S);
+  const int q = (s - rot + S) % S;
+  if (q < O) return (tp - 1) * U + ob + g * O + q;
+  return nb + g * (S - O) + (q - O);
+}
+
 template <class S>
 __device__ __forceinline__ void gemm_rs_body(const RsArgs& a) {
   __shared__ __attribute__((aligned(1024))) char lds[S::LDS];
@@ -151,7 +178,9 @@ __device__ __forceinline__ void gemm_rs_body(const RsArgs& a) {
   __shared__ int s_ok;
 
   for (int r0 = 0; r0 < total; r0 += grid) {
-    const int t = spread_tile(r0, min(grid, total - r0), grid, U);
+    const int n = min(grid, total - r0);
+    const int t = (a.ring || a.gated) ? spread_tile(r0, n, grid, U)
+                                      : oneshot_tile(r0, n, grid, U, a.tp);
     if (t < 0) continue;
     const int j = t / U;
     const int u = t - j * U;
