@@ -140,6 +140,37 @@ def test_rs_padded_row_stride(tile):
             assert np.array_equal(got[cix], send_ref[cix])
 
 
+# Shapes with several persistent rounds: the one-shot form deals the own chunk's tiles over all
+# rounds, in groups of eight workgroups (one per XCD) when the grid, the round and the round's
+# share of the own chunk allow it, else over the whole grid.  (4, 2, 1100 rows, 3600 columns):
+# 75 tiles per chunk at 256x256 (rounds of 256 and 44 tiles: grouped, then whole-grid), 261 at
+# 128x128 (512, 512, 20).  (8, 3, 512 rows, 8192 columns): 64 tiles per chunk, two full rounds.
+_MANY_ROUNDS = {}
+
+
+def _many_rounds_case(tp, s, nc, mo):
+    """Inputs and oracle results of one shape, computed once for all its tile / send cases."""
+    key = (tp, s, nc, mo)
+    if key not in _MANY_ROUNDS:
+        inp = W.make_rs(W.rs_shape(tp, s, tp * nc, 128, mo, dist="int3", seed=tp * 100 + nc))
+        _MANY_ROUNDS[key] = (inp, oracle_rs(inp))
+    return _MANY_ROUNDS[key]
+
+
+@pytest.mark.parametrize("with_send", [True, False])
+@pytest.mark.parametrize("tile", ["256x256w8", "128x128"])
+@pytest.mark.parametrize("tp,s,nc,mo", [(4, 2, 1100, 3600), (8, 3, 512, 8192)])
+def test_rs_many_rounds_exact(tp, s, nc, mo, tile, with_send):
+    c = ctx()
+    c.set_option(B.RAG_OPT_TILE, B.TILES[tile])
+    inp, (D_ref, send_ref, _) = _many_rounds_case(tp, s, nc, mo)
+    say(f"case {inp.shape.name} tile {tile} send {with_send}")
+    run = RSRun(inp, with_send=with_send).run(c)
+    assert np.array_equal(W.bits_u16(run.D.cpu()), O.f32_to_bf16(D_ref))
+    if with_send:
+        _check_send(run, send_ref, exact=True)
+
+
 def test_rs_special_cases_and_no_send():
     c = ctx()
     shape = W.rs_shape(4, 2, 4 * 64, 128, 192, dist="int3", seed=41)
