@@ -95,8 +95,13 @@ enum {
                            arrives during the call: the side stream copies it in ring order into a
                            library receive buffer, each copy releasing a counter, and a tile waits
                            for the counters of what its epilogue reads after its K loop (the
-                           "atomic" reduce-scatter).  Needs the row stride equal to Mo.  Copies run
-                           on the copy kernel, or on SDMA with RAG_COPY_SDMA */
+                           "atomic" reduce-scatter).  Needs the row stride equal to Mo.  With
+                           RAG_COPY_IN_GEMM the GEMM+RS launch runs the copies itself (a waiting
+                           tile copies until its counter is released, every workgroup copies a
+                           share after each tile and the rest before it exits), except inside
+                           rag_linear_allreduce, whose gather copies already run beside it: there,
+                           and with RAG_COPY_KERNEL, the copy kernel on the side stream runs them;
+                           with RAG_COPY_SDMA, SDMA */
 };
 
 /* Copy engines of the simulated arrival (RAG_OPT_COPY_ENGINE). */
@@ -109,7 +114,8 @@ enum {
                               hipStreamWriteValue32 of the counter) */
     RAG_COPY_IN_GEMM = 2   /* the GEMM launch itself: workgroups whose chunk is not there yet copy
                               pieces of the peers' chunks (ring order) until it is released, and
-                              help with the rest once out of tiles; no side stream is used */
+                              help with the rest once out of tiles; no side stream is used (see
+                              RAG_RS_ARRIVE for the GEMM+RS form) */
 };
 
 /* Option keys for rag_set_option. */
@@ -143,8 +149,9 @@ enum {
                                    ring's chunks in more rounds) */
     RAG_OPT_COPY_PRIORITY = 11, /* 1 (default) = copy-kernel waves issue at the highest wave
                                    priority, 0 = normal */
-    RAG_OPT_GEMM_COPY_WGS = 12  /* RAG_COPY_IN_GEMM: how many of the GEMM's workgroups take part in
-                                   the copies, spread evenly over the XCDs (0 = all, the default);
+    RAG_OPT_GEMM_COPY_WGS = 12  /* RAG_COPY_IN_GEMM, AG+GEMM calls: how many of the GEMM's
+                                   workgroups take part in the copies, spread evenly over the XCDs
+                                   (0 = all, the default; GEMM+RS always uses all);
                                    fewer copy more slowly but draw less power at once */
 };
 

@@ -107,8 +107,8 @@ __device__ inline void copy_queue_begin(const CopyPlan& p) {
 }
 
 // Take pieces of queue q (0 = the peers' chunks, 1 = the own chunk) and copy them until the queue
-// is empty or, with stop >= 0, until ctr[stop] == epoch (checked before each take).  Called by
-// every thread of the workgroup; s_word is a workgroup-shared word.
+// is empty, until max_pieces are copied or, with stop >= 0, until ctr[stop] == epoch (checked
+// before each take).  Called by every thread of the workgroup; s_word is a workgroup-shared word.
 //
 // Each iteration has exactly one thread-0 step, between barriers: complete the piece copied in
 // the previous iteration, then take the next one.  (With a thread-0 step at the end of the body
@@ -118,17 +118,19 @@ __device__ inline void copy_queue_begin(const CopyPlan& p) {
 // into a scalar register, so the loop's exit is uniform.
 template <int NT, int U = 8>
 __device__ inline void run_copy_queue(const CopyPlan& p, int* ctr, int epoch, int q, int stop,
-                                      unsigned* s_word) {
+                                      unsigned* s_word, unsigned max_pieces = ~0u) {
   const unsigned first = q == 0 ? 0u : (unsigned)p.n_peer;
   const unsigned total = (q == 0 ? (unsigned)p.n_peer : (unsigned)(p.n - p.n_peer)) * p.pieces;
   if (total == 0) return;
   unsigned prev = ~0u;   // copy of the piece finished in the previous iteration, if any
+  unsigned taken = 0;    // pieces copied (uniform)
   while (true) {
     if (threadIdx.x == 0) {
       if (prev != ~0u) pieces_done(p, ctr, epoch, prev, 1);
       unsigned g = ~0u;
-      if (stop < 0 || __hip_atomic_load(ctr + stop * kWordStride, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT) != epoch)
+      if (taken < max_pieces &&
+          (stop < 0 || __hip_atomic_load(ctr + stop * kWordStride, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT) != epoch))
         g = __hip_atomic_fetch_add(p.grab + q * kWordStride, 1u, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
       *s_word = g;
@@ -143,6 +145,7 @@ __device__ inline void run_copy_queue(const CopyPlan& p, int* ctr, int epoch, in
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     prev = c;
+    ++taken;
   }
 }
 

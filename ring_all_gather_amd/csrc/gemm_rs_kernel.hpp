@@ -176,6 +176,8 @@ __device__ __forceinline__ void gemm_rs_body(const RsArgs& a) {
   const i32x4 ry = make_rsrc(a.W, (uint32_t)a.Mo * ldb);
   const int grid = (int)gridDim.x;
   __shared__ int s_ok;
+  __shared__ unsigned s_piece;
+  if (a.copies) copy_queue_begin(a.cp);
 
   for (int r0 = 0; r0 < total; r0 += grid) {
     const int n = min(grid, total - r0);
@@ -195,27 +197,32 @@ __device__ __forceinline__ void gemm_rs_body(const RsArgs& a) {
     tile_offsets<S, S::YQ>(yo, cb * S::BJ, a.Mo, ldb, wave, lane);
     f32x16 acc[S::FI][S::FJ];
     tile_kloop<S, false>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);
-    // gated: wait for what the epilogue reads (the K loop did not need it)
+    // gated: wait for what the epilogue reads (the K loop did not need it): chunk c's running sum
+    // (ring), or every peer's partial of the own chunk (one-shot).  With in-kernel copies the
+    // workgroup copies pieces, in ring order, until each counter it needs is released.
     const bool waits = a.gated && (a.ring ? a.partial[c] != nullptr : own);
     if (waits) {
-      if (threadIdx.x == 0) {
-        bool ok = true;
-        if (a.ring) {
-          ok = wait_ready(a.ctr + c * kWordStride, a.epoch, a.err, a.spin_limit);
-        } else {
-          for (int p = 0; p < a.tp && ok; ++p)
-            if (p != a.self_rank)
-              ok = wait_ready(a.ctr + p * kWordStride, a.epoch, a.err, a.spin_limit);
-        }
-        s_ok = ok;
+      int ok = 1;
+      for (int k = 0; k < (a.ring ? 1 : a.tp) && ok; ++k) {
+        const int idx = a.ring ? c : k;
+        if (!a.ring && k == a.self_rank) continue;
+        if (a.copies) run_copy_queue<S::NT>(a.cp, a.ctr, a.epoch, 0, idx, &s_piece);
+        if (threadIdx.x == 0)
+          s_ok = wait_ready(a.ctr + idx * kWordStride, a.epoch, a.err, a.spin_limit);
+        __syncthreads();
+        ok = __builtin_amdgcn_readfirstlane(s_ok);   // uniform: see run_copy_queue
+        __syncthreads();
       }
-      __syncthreads();
-      const int ok = __builtin_amdgcn_readfirstlane(s_ok);   // uniform: see run_copy_queue
-      __syncthreads();
       if (!ok) continue;
     }
     rs_epilogue<S>(acc, lds, a, c, own, rb, cb, wave, lane);
+    if (a.copies) {
+      run_copy_queue<S::NT>(a.cp, a.ctr, a.epoch, 0, -1, &s_piece, (unsigned)a.copy_quota);
+      __syncthreads();   // keeps this thread-0 step and the next tile's apart
+    }
   }
+  // whatever is left (every piece is taken by a running workgroup, so every count completes)
+  if (a.copies) run_copy_queue<S::NT>(a.cp, a.ctr, a.epoch, 0, -1, &s_piece);
 }
 
 }  // namespace ringag

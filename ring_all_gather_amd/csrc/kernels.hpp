@@ -100,6 +100,11 @@ struct RsArgs {
   int epoch;
   int* err;
   long long spin_limit;
+  int copies;                    // 1 = this kernel also runs the copies of `cp` (gated only): a
+                                 // tile copies until the counter it waits for is released, and
+                                 // every workgroup copies up to copy_quota pieces after each tile
+  int copy_quota;
+  CopyPlan cp;
 };
 
 // Arguments of the arrival (producer) kernel on the side stream: runs the whole piece queue.

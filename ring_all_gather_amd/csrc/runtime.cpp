@@ -516,8 +516,12 @@ int rs_call(rag_ctx* c, const char* fn, bool ring, const void* X, int T, int Kl,
   a.err = c->err;
   a.spin_limit = c->spin_us * c->wall_khz / 1000;
 
-  // Arrivals: the side stream copies, in ring order, what each tile's epilogue reads, releasing
-  // one counter per copy; the tiles wait for them on the device.
+  // Arrivals: copies, in ring order, of what each tile's epilogue reads, releasing one counter per
+  // copy; the tiles wait for them on the device.  With the in-GEMM engine the GEMM's own
+  // workgroups run them, unless other copies run beside this call (linear_allreduce's gather,
+  // whose copy kernel uses the other set of piece counts that a copying launch clears); else the
+  // side stream does.
+  const bool in_gemm = a.gated && c->copy_engine == RAG_COPY_IN_GEMM && !other_copies_beside;
   bool join = false;
   if (a.gated) {
     CopyPlan cp = {};
@@ -543,32 +547,39 @@ int rs_call(rag_ctx* c, const char* fn, bool ring, const void* X, int T, int Kl,
     cp.clear_next = c->arr + (size_t)(set ^ 1u) * 2 * kArrSlots * kWordStride;
     cp.delay_ticks = c->delay_us * c->wall_khz / 1000;
     cp.withhold_mask = c->withhold;
-    HIPCHK(hipEventRecord(c->ev_fork, stream));
-    HIPCHK(hipStreamWaitEvent(c->side, c->ev_fork, 0));
-    if (c->copy_engine == RAG_COPY_SDMA) {
-      for (int k = 0; k < cp.n; ++k) {
-        HIPCHK(hipMemcpyAsync(cp.dst[k], cp.src[k], (size_t)cp.bytes, hipMemcpyDeviceToDeviceNoCU,
-                              c->side));
-        if (!((c->withhold >> cp.pos[k]) & 1u))
-          HIPCHK(hipStreamWriteValue32(c->side, c->ctr + (size_t)cp.ctr_index[k] * kWordStride,
-                                       (uint32_t)epoch, 0));
-      }
-    } else {
-      ArrivalArgs aa = {};
-      aa.cp = cp;
-      aa.ctr = c->ctr;
-      aa.epoch = epoch;
-      aa.raise_priority = c->copy_priority;
-      HIPCHK(launch_arrival(c->device, aa, c->comm_wgs, c->side));
+    if (in_gemm) {
+      a.copies = 1;
+      a.cp = cp;
       c->arr_seq++;
+    } else {
+      HIPCHK(hipEventRecord(c->ev_fork, stream));
+      HIPCHK(hipStreamWaitEvent(c->side, c->ev_fork, 0));
+      if (c->copy_engine == RAG_COPY_SDMA) {
+        for (int k = 0; k < cp.n; ++k) {
+          HIPCHK(hipMemcpyAsync(cp.dst[k], cp.src[k], (size_t)cp.bytes, hipMemcpyDeviceToDeviceNoCU,
+                                c->side));
+          if (!((c->withhold >> cp.pos[k]) & 1u))
+            HIPCHK(hipStreamWriteValue32(c->side, c->ctr + (size_t)cp.ctr_index[k] * kWordStride,
+                                         (uint32_t)epoch, 0));
+        }
+      } else {
+        ArrivalArgs aa = {};
+        aa.cp = cp;
+        aa.ctr = c->ctr;
+        aa.epoch = epoch;
+        aa.raise_priority = c->copy_priority;
+        HIPCHK(launch_arrival(c->device, aa, c->comm_wgs, c->side));
+        c->arr_seq++;
+      }
+      // every copy is waited for by some tile, except the ring step's passed-on sums when send is
+      // NULL (those tiles are skipped): then the caller's stream waits for the side stream
+      join = ring && !send;
+      if (join) HIPCHK(hipEventRecord(c->ev_join, c->side));
     }
-    // every copy is waited for by some tile, except the ring step's passed-on sums when send is
-    // NULL (those tiles are skipped): then the caller's stream waits for the side stream
-    join = ring && !send;
-    if (join) HIPCHK(hipEventRecord(c->ev_join, c->side));
   }
 
-  const bool beside = (a.gated || other_copies_beside) && c->copy_engine != RAG_COPY_SDMA;
+  const bool beside =
+      ((a.gated && !in_gemm) || other_copies_beside) && c->copy_engine != RAG_COPY_SDMA;
   int tile = choose_rs_tile(c, nc, Mo, tp);
   for (int t : {tile, (int)kTile256x128, (int)kTile128x128}) {
     if (!c->rs_info_ok[t]) {
@@ -598,6 +609,23 @@ int rs_call(rag_ctx* c, const char* fn, bool ring, const void* X, int T, int Kl,
   const int grid = persistent_grid(total,
                                    c->num_cus - reserved_cus(c->rs_info[tile], beside, copy_vgprs),
                                    c->rs_info[tile].max_blocks_per_cu);
+  if (in_gemm) {
+    // Pieces of (all bytes) / grid rounded up to a power of two from 64 KiB to 1 MiB: a piece
+    // costs a take, two barriers, a full wait and an agent-scope release, so at rs_8k (224 MiB)
+    // 64 KiB pieces copied at 1.9 TB/s and 1 MiB pieces at well over twice that (896 KiB pieces
+    // were 5% slower than 1 MiB, 2 MiB 10%).  After each tile a workgroup copies its share, so
+    // that the copies are done by the last round (the one-shot form's own chunk) and overlap the
+    // other workgroups' tiles.
+    const unsigned long long all = a.cp.bytes * (unsigned long long)a.cp.n;
+    unsigned piece = 64u << 10;
+    while (piece < (1u << 20) && (unsigned long long)piece * (unsigned long long)grid < all)
+      piece *= 2;
+    a.cp.piece_bytes = piece;
+    a.cp.pieces = (unsigned)((a.cp.bytes + a.cp.piece_bytes - 1) / a.cp.piece_bytes);
+    const long long rounds = std::max(1, (total + grid - 1) / grid - 1);
+    const long long pieces = (long long)a.cp.pieces * a.cp.n;
+    a.copy_quota = (int)((pieces + grid * rounds - 1) / (grid * rounds));
+  }
   if (debug_enabled())
     fprintf(stderr, "[ringag] %s tp=%d s=%d T=%d Kl=%d Mo=%d tile=%dx%d tiles=%d grid=%d "
             "arrive=%d\n", fn, tp, self_rank, T, Kl, Mo, bi, bj, total, grid, (int)arrive);

@@ -220,7 +220,7 @@ def test_rs_full_size_sampled_rows():
 
 # ------------------------------------------------- arrivals (counter-gated) and the ring step
 
-COPY_ENGINES = ["kernel", "sdma"]
+COPY_ENGINES = ["kernel", "sdma", "in-gemm"]
 
 
 def _engine(c, e):
@@ -245,12 +245,13 @@ def test_rs_arrive_exact_integers(tp, s, engine):
     _check_send(run, send_ref, exact=True)
 
 
-def test_rs_arrive_fresh_data_delayed():
+@pytest.mark.parametrize("engine", ["kernel", "in-gemm"])
+def test_rs_arrive_fresh_data_delayed(engine):
     """Back-to-back gated calls with new partials each time and every copy's counter held back
     1 ms: an epilogue that read the receive buffer before its counter would add the previous
     call's partials."""
     c = ctx()
-    _engine(c, "kernel")
+    _engine(c, engine)
     c.set_option(B.RAG_OPT_ARRIVAL_DELAY_US, 1000)
     shape = W.rs_shape(4, 1, 4 * 64, 128, 128, dist="int3", seed=1)
     run = RSRun(W.make_rs(shape))
@@ -261,7 +262,7 @@ def test_rs_arrive_fresh_data_delayed():
         for d, h in zip(run.partials, inp.partials):
             if d is not None:
                 d.copy_(h)
-        say(f"case rs arrive fresh it={it}")
+        say(f"case rs arrive fresh engine={engine} it={it}")
         B.gemm_rs(c, run.X, run.W, run.partials, 4, 1, run.D, send=run.send,
                   flags=B.RAG_RS_ARRIVE)
         torch.cuda.synchronize()
@@ -270,9 +271,10 @@ def test_rs_arrive_fresh_data_delayed():
     c.check()
 
 
-def test_rs_arrive_withheld_times_out_and_recovers():
+@pytest.mark.parametrize("engine", ["kernel", "in-gemm"])
+def test_rs_arrive_withheld_times_out_and_recovers(engine):
     c = ctx()
-    _engine(c, "kernel")
+    _engine(c, engine)
     c.set_option(B.RAG_OPT_SPIN_LIMIT_US, 20000)
     c.set_option(B.RAG_OPT_WITHHOLD_MASK, 1 << 2)
     shape = W.rs_shape(4, 0, 4 * 64, 128, 128, dist="int3", seed=5)
@@ -319,7 +321,7 @@ def oracle_ring(inp: W.RSRingInputs):
                                [t.numpy() for t in inp.incoming], s.tp, s.self_rank)
 
 
-@pytest.mark.parametrize("mode", ["given", "kernel", "sdma"])
+@pytest.mark.parametrize("mode", ["given", "kernel", "sdma", "in-gemm"])
 @pytest.mark.parametrize("tp,s", [(1, 0), (2, 0), (3, 1), (4, 2), (8, 5)])
 def test_rs_ring_step_exact_integers(tp, s, mode):
     """One ring step: send[c] = incoming[c] + P[c], D = incoming[s] + P[s], bit for bit on
@@ -355,11 +357,13 @@ def test_rs_ring_ragged_random(tile):
     _check_send(run, send_ref)
 
 
-def test_rs_ring_no_send_and_delayed_arrivals():
+@pytest.mark.parametrize("engine", ["kernel", "in-gemm"])
+def test_rs_ring_no_send_and_delayed_arrivals(engine):
     """send = NULL (the passed-on sums are dropped, so only the own chunk waits on the device and
-    the call joins the side stream) with every copy held back 1 ms, then fresh data."""
+    the call joins the side stream, or the GEMM's workgroups copy what is left before they exit)
+    with every copy held back 1 ms, then fresh data."""
     c = ctx()
-    _engine(c, "kernel")
+    _engine(c, engine)
     c.set_option(B.RAG_OPT_ARRIVAL_DELAY_US, 1000)
     for it in range(3):
         shape = W.rs_shape(4, 3, 4 * 64, 128, 128, dist="int3", seed=800 + it)
@@ -399,16 +403,18 @@ def test_rs_ring_full_size_sampled_rows():
         assert np.abs(got - ref).max() <= TOL_SEND * np.abs(ref).max()
 
 
+@pytest.mark.parametrize("engine", ["kernel", "in-gemm"])
 @pytest.mark.parametrize("ring", [False, True])
-def test_rs_arrive_full_size_back_to_back(ring):
-    """Full-size gated calls back to back (no synchronisation between them) with the copy kernel
-    beside the GEMM: the GEMM's persistent grid must leave the copies room to run, or its waiting
-    tiles would spin to the limit (RAG_ETIMEOUT).  Then the last call is checked on sampled rows."""
+def test_rs_arrive_full_size_back_to_back(ring, engine):
+    """Full-size gated calls back to back (no synchronisation between them).  With the copy kernel
+    beside the GEMM, the GEMM's persistent grid must leave the copies room to run, or its waiting
+    tiles would spin to the limit (RAG_ETIMEOUT); with the GEMM's own workgroups copying, every
+    piece must be taken by some workgroup.  Then the last call is checked on sampled rows."""
     shape = W.WORKLOADS["rs_8k"]
     c = ctx()
-    _engine(c, "kernel")
+    _engine(c, engine)
     c.set_option(B.RAG_OPT_COMM_WGS, 128)
-    say(f"case rs arrive back-to-back ring={ring} {shape}")
+    say(f"case rs arrive back-to-back ring={ring} engine={engine} {shape}")
     if ring:
         inp = W.make_rs_ring(shape)
         run = RSRingRun(inp, poison_start=False)
