@@ -393,9 +393,10 @@ def main():
                                     "achieved_GBps": round(gbs_f, 1),
                                     "frac": round(gbs_f / PEAK_HBM_GBS, 4),
                                     "tflops": round(flops / (kms_f * 1e-3) / 1e12, 2)}
-            # the counter-gated forms: the peers' partials arrive during the call (side-stream
-            # copies in ring order, tiles wait before their epilogue), and one ring-accumulate step
-            # with its incoming running sums given or arriving
+            # the counter-gated forms: the peers' partials arrive during the call (copies in ring
+            # order, run by the GEMM's own workgroups with the in-GEMM engine, else beside it;
+            # tiles wait before their epilogue), and one ring-accumulate step with its incoming
+            # running sums given or arriving
             ms_arrive = time_steps(
                 lambda: B.gemm_rs(ctx, X, Wt, parts, shape.tp, shape.self_rank, D, send=send,
                                   flags=B.RAG_RS_ARRIVE), args.steps, args.warmup, stream)
@@ -422,7 +423,7 @@ def main():
                 "ring_step_sums_given": round(ms_ring, 5),
                 "ring_step_sums_arrive": round(ms_ring_arrive, 5),
                 "linear_allreduce": round(ms_lar, 5),
-                "arrival_engine": "kernel" if args.copy_engine != "sdma" else "sdma",
+                "arrival_engine": args.copy_engine,
                 "comm_wgs": args.comm_wgs}
         if not args.no_cpu:
             out["cpu_baseline"] = cpu_baseline_rs(inp, args.cpu_seconds)
