@@ -99,7 +99,7 @@ enum {
                            RAG_COPY_IN_GEMM the GEMM+RS launch runs the copies itself (a waiting
                            tile copies until its counter is released, every workgroup copies a
                            share after each tile and the rest before it exits), except inside
-                           rag_linear_allreduce, whose gather copies already run beside it: there,
+                           rag_linear_allreduce, whose gather copies then run beside it: there,
                            and with RAG_COPY_KERNEL, the copy kernel on the side stream runs them;
                            with RAG_COPY_SDMA, SDMA */
 };
@@ -315,8 +315,10 @@ RAG_API int gemm_rs_ring(rag_ctx* ctx,
  * diagram: reduce-scatter of the split GEMM):
  *     Y[rows of chunk self_rank] = sum over ranks of P_p[rows of chunk self_rank]  (gemm_rs)
  *     Y[rows of chunk c]         = reduced[c]  for c != self_rank (the owners' reduced chunks,
- *                                  all-gathered: copied in by the side stream in ring order,
- *                                  self_rank-1 first, while the GEMM runs)
+ *                                  all-gathered: copied in ring order, self_rank-1 first,
+ *                                  by the GEMM+RS launch's own workgroups after their tiles
+ *                                  with RAG_COPY_IN_GEMM and no RAG_RS_ARRIVE, else by the
+ *                                  side stream while the GEMM runs)
  *     send                       as for gemm_rs
  *
  *   X, W, Kl, partials, ldp, send, flags as for gemm_rs

@@ -414,7 +414,7 @@ int ag_gemm_split(rag_ctx* c, const void* A, int M, int K, const void* const* B,
 int rs_call(rag_ctx* c, const char* fn, bool ring, const void* X, int T, int Kl, const void* W,
             int Mo, const float* const* ptrs, long long ld, int tp, int self_rank, float* send,
             void* D, int flags, void* stream_v, bool validate_only = false,
-            bool other_copies_beside = false) {
+            bool other_copies_beside = false, const CopyPlan* extra_copies = nullptr) {
   if (!c) return fail(RAG_EINVAL, "%s: ctx is NULL", fn);
   if (tp < 1 || tp > c->max_tp)
     return fail(RAG_EINVAL, "%s: tp=%d outside [1, %d] (max_tp of the context)", fn, tp,
@@ -521,7 +521,10 @@ int rs_call(rag_ctx* c, const char* fn, bool ring, const void* X, int T, int Kl,
   // workgroups run them, unless other copies run beside this call (linear_allreduce's gather,
   // whose copy kernel uses the other set of piece counts that a copying launch clears); else the
   // side stream does.
-  const bool in_gemm = a.gated && c->copy_engine == RAG_COPY_IN_GEMM && !other_copies_beside;
+  // extra_copies (linear_allreduce's gather, not gated): copies with nothing waiting for them on
+  // the device, run by the same launch
+  const bool in_gemm = (a.gated && c->copy_engine == RAG_COPY_IN_GEMM && !other_copies_beside) ||
+                       extra_copies != nullptr;
   bool join = false;
   if (a.gated) {
     CopyPlan cp = {};
@@ -578,6 +581,15 @@ int rs_call(rag_ctx* c, const char* fn, bool ring, const void* X, int T, int Kl,
     }
   }
 
+  if (extra_copies) {
+    a.copies = 1;
+    a.cp = *extra_copies;
+    const unsigned set = c->arr_seq & 1u;
+    a.cp.grab = c->arr + (size_t)set * 2 * kArrSlots * kWordStride;
+    a.cp.done = a.cp.grab + (size_t)kArrSlots * kWordStride;
+    a.cp.clear_next = c->arr + (size_t)(set ^ 1u) * 2 * kArrSlots * kWordStride;
+    c->arr_seq++;
+  }
   const bool beside =
       ((a.gated && !in_gemm) || other_copies_beside) && c->copy_engine != RAG_COPY_SDMA;
   int tile = choose_rs_tile(c, nc, Mo, tp);
@@ -1120,7 +1132,28 @@ int linear_allreduce(rag_ctx* c, const void* X, int T, int Kl, const void* W, in
         return fail(RAG_EINVAL, "linear_allreduce: Y must not overlap partials[%d]", p);
   }
   hipStream_t stream = (hipStream_t)stream_v;
-  // the all-gather: fork before the GEMM so that its copies run beside it
+  // the all-gather.  With the in-GEMM engine and nothing gated, the GEMM+RS launch copies the
+  // owners' reduced chunks itself (after its tiles' epilogues, in ring order); else a copy kernel
+  // or SDMA on the side stream, forked before the GEMM so that the copies run beside it.
+  if (tp > 1 && c->copy_engine == RAG_COPY_IN_GEMM && !(flags & RAG_RS_ARRIVE)) {
+    CopyPlan gp = {};
+    int n = 0;
+    for (int k = 1; k < tp; ++k, ++n) {
+      const int r = ((self_rank - k) % tp + tp) % tp;
+      gp.src[n] = reduced[r];
+      gp.dst[n] = (char*)Y + (size_t)r * cbytes;
+      gp.ctr_index[n] = -1;
+      gp.pos[n] = k;
+    }
+    gp.n_peer = n;
+    gp.n = n;
+    gp.bytes = (unsigned long long)cbytes;
+    gp.piece_bytes = (unsigned)kArrivalThreads * 256u;
+    gp.pieces = (unsigned)((gp.bytes + gp.piece_bytes - 1) / gp.piece_bytes);
+    return rs_call(c, "linear_allreduce", false, X, T, Kl, W, Mo, partials, ldp, tp, self_rank,
+                   send, (char*)Y + (size_t)self_rank * cbytes, flags, stream_v, false, false,
+                   &gp);
+  }
   if (tp > 1) {
     HIPCHK(hipEventRecord(c->ev_fork, stream));
     HIPCHK(hipStreamWaitEvent(c->side, c->ev_fork, 0));
