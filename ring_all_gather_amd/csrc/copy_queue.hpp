@@ -54,7 +54,7 @@ constexpr int kCopyStorePolicy = 16;
 
 // Copy piece k of copy c with the NT threads of the workgroup (16-byte vectors, U in flight per
 // thread).
-template <int NT, int U>
+template <int NT, int U, bool PIPE>
 __device__ __forceinline__ void copy_piece(const CopyPlan& p, unsigned c, unsigned k) {
   const unsigned long long beg = (unsigned long long)k * p.piece_bytes;
   const unsigned long long len = min((unsigned long long)p.piece_bytes, p.bytes - beg);
@@ -62,15 +62,59 @@ __device__ __forceinline__ void copy_piece(const CopyPlan& p, unsigned c, unsign
   const unsigned nvec = (unsigned)(len / 16);
   const __amdgpu_buffer_rsrc_t d = __builtin_amdgcn_make_buffer_rsrc(
       (char*)p.dst[c] + beg, 0, (int)(nvec * 16), 0x00020000);
-  unsigned i = threadIdx.x;
-  for (; i + (U - 1) * NT < nvec; i += U * NT) {
-    v4i v[U];
+  // PIPE: batches of U vectors per thread that every thread copies in full, software-pipelined:
+  // the next batch's loads go out before this batch's stores, so the wait for a batch's loads
+  // (vmcnt counts loads and stores in order) leaves the previous batch's stores and the next
+  // batch's loads in flight (ag_4k copies-only launch 18.0 -> 17.4 us, ag_qkv 61.8 -> 57.1 us).
+  // The trip count is uniform, so the compiler can count them.  It holds two batches in
+  // registers, so the GEMM+RS kernel (which copies while its accumulators are live) and the
+  // arrival kernel (whose waves must fit beside a GEMM's) use the plain loop: load a batch,
+  // store it.
+  unsigned i;
+  if constexpr (PIPE) {
+    const unsigned nb = nvec / (U * NT);
+    const unsigned t0 = threadIdx.x;
+    auto ld = [&](v4i(&r)[U], unsigned q) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = s[i + u * NT];
+      for (int u = 0; u < U; ++u) r[u] = s[t0 + (q * U + u) * NT];
+    };
+    auto st = [&](const v4i(&r)[U], unsigned q) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      __builtin_amdgcn_raw_buffer_store_b128(v[u], d, (int)((i + u * NT) * 16), 0,
-                                             kCopyStorePolicy);
+      for (int u = 0; u < U; ++u)
+        __builtin_amdgcn_raw_buffer_store_b128(r[u], d, (int)((t0 + (q * U + u) * NT) * 16), 0,
+                                               kCopyStorePolicy);
+    };
+    if (nb > 0) {
+      // two register sets used in turn (no moves between them, which would wait for every load)
+      v4i v[U], w[U];
+      ld(v, 0);
+      unsigned b = 1;
+      for (; b + 1 < nb; b += 2) {
+        ld(w, b);
+        st(v, b - 1);
+        ld(v, b + 1);
+        st(w, b);
+      }
+      if (b < nb) {
+        ld(w, b);
+        st(v, b - 1);
+        st(w, b);
+      } else {
+        st(v, b - 1);
+      }
+    }
+    i = t0 + nb * U * NT;
+  } else {
+    i = threadIdx.x;
+    for (; i + (U - 1) * NT < nvec; i += U * NT) {
+      v4i v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = s[i + u * NT];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        __builtin_amdgcn_raw_buffer_store_b128(v[u], d, (int)((i + u * NT) * 16), 0,
+                                               kCopyStorePolicy);
+    }
   }
   for (; i < nvec; i += NT)
     __builtin_amdgcn_raw_buffer_store_b128(s[i], d, (int)(i * 16), 0, kCopyStorePolicy);
@@ -116,7 +160,7 @@ __device__ inline void copy_queue_begin(const CopyPlan& p) {
 // and lower the loop so that thread 0's lane is held back while the wave's other lanes start the
 // next iteration with the stale piece number, a loop that never ends.)  The taken number is read
 // into a scalar register, so the loop's exit is uniform.
-template <int NT, int U = 8>
+template <int NT, int U = 8, bool PIPE = true>
 __device__ inline void run_copy_queue(const CopyPlan& p, int* ctr, int epoch, int q, int stop,
                                       unsigned* s_word, unsigned max_pieces = ~0u) {
   const unsigned first = q == 0 ? 0u : (unsigned)p.n_peer;
@@ -140,7 +184,7 @@ __device__ inline void run_copy_queue(const CopyPlan& p, int* ctr, int epoch, in
     __syncthreads();
     if (g >= total) return;
     const unsigned c = first + g / p.pieces;
-    copy_piece<NT, U>(p, c, g % p.pieces);
+    copy_piece<NT, U, PIPE>(p, c, g % p.pieces);
     // every wave waits for its own stores; after the barrier thread 0 completes the piece
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();

@@ -206,7 +206,7 @@ __device__ __forceinline__ void gemm_rs_body(const RsArgs& a) {
       for (int k = 0; k < (a.ring ? 1 : a.tp) && ok; ++k) {
         const int idx = a.ring ? c : k;
         if (!a.ring && k == a.self_rank) continue;
-        if (a.copies) run_copy_queue<S::NT>(a.cp, a.ctr, a.epoch, 0, idx, &s_piece);
+        if (a.copies) run_copy_queue<S::NT, 8, false>(a.cp, a.ctr, a.epoch, 0, idx, &s_piece);
         if (threadIdx.x == 0)
           s_ok = wait_ready(a.ctr + idx * kWordStride, a.epoch, a.err, a.spin_limit);
         __syncthreads();
@@ -217,12 +217,13 @@ __device__ __forceinline__ void gemm_rs_body(const RsArgs& a) {
     }
     rs_epilogue<S>(acc, lds, a, c, own, rb, cb, wave, lane);
     if (a.copies) {
-      run_copy_queue<S::NT>(a.cp, a.ctr, a.epoch, 0, -1, &s_piece, (unsigned)a.copy_quota);
+      run_copy_queue<S::NT, 8, false>(a.cp, a.ctr, a.epoch, 0, -1, &s_piece,
+                                      (unsigned)a.copy_quota);
       __syncthreads();   // keeps this thread-0 step and the next tile's apart
     }
   }
   // whatever is left (every piece is taken by a running workgroup, so every count completes)
-  if (a.copies) run_copy_queue<S::NT>(a.cp, a.ctr, a.epoch, 0, -1, &s_piece);
+  if (a.copies) run_copy_queue<S::NT, 8, false>(a.cp, a.ctr, a.epoch, 0, -1, &s_piece);
 }
 
 }  // namespace ringag
