@@ -21,8 +21,9 @@
  *
  * Simulated ring: the library runs one rank (self_rank) of a tp-rank ring on a single GPU.  The
  * other ranks' chunks are caller-provided device buffers; their "arrival" is a device-to-device
- * copy into the gathered buffer on a library-owned side stream, in ring order, each followed by a
- * bump of that chunk's ready counter.  A rank sends to rank+1 and receives from rank-1, so chunks
+ * copy into the gathered buffer, in ring order, each followed by a bump of that chunk's ready
+ * counter.  The copies run inside the GEMM launch itself (RAG_COPY_IN_GEMM, the default) or on a
+ * library-owned side stream (RAG_COPY_KERNEL, RAG_COPY_SDMA).  A rank sends to rank+1 and receives from rank-1, so chunks
  * reach self_rank in the order s, s-1, s-2, ... (mod tp).
  *
  * Conventions for every entry point:
@@ -31,10 +32,11 @@
  *     passed the operation.  Host arrays of pointers (B_chunks, partials) are read during the call
  *     only.
  *   - Every call is stream-ordered on `stream` (0 = the null stream): it enqueues work and returns.
- *     Outputs are valid in `stream` order.  The side stream that carries the copies starts after
- *     the work already in `stream` (event fork), and the call's last kernel on `stream` completes
- *     only after every copy of the call has completed (its workgroups wait for the copy counters;
- *     with RAG_COPY_ONLY, `stream` waits for an event of the side stream instead).  So in `stream`
+ *     Outputs are valid in `stream` order.  A side stream that carries copies starts after the
+ *     work already in `stream` (event fork), and the call's last kernel on `stream` completes
+ *     only after every copy of the call has completed (its workgroups wait for the copy counters
+ *     or run the copies themselves; with RAG_COPY_ONLY on the side stream, `stream` waits for an
+ *     event of the side stream instead).  So in `stream`
  *     order the inputs may be reused and the outputs are complete.
  *   - One operation in flight per context; a context is not thread-safe.  Calls on different
  *     contexts are independent.
