@@ -123,8 +123,9 @@ enum {
 /* Option keys for rag_set_option. */
 enum {
     RAG_OPT_COPY_ENGINE = 1,    /* a RAG_COPY_* value (default RAG_COPY_IN_GEMM) */
-    RAG_OPT_COMM_WGS = 2,       /* workgroups of the side-stream copy kernel (default 32, 1..1024):
-                                   the share of compute units that communication takes */
+    RAG_OPT_COMM_WGS = 2,       /* workgroups of the side-stream copy kernel (default 128,
+                                   1..1024): the share of compute units that communication takes
+                                   (gated rs_8k: 0.75 ms per call with 32, 0.45 with 128) */
     RAG_OPT_SPIN_LIMIT_US = 3,  /* how long a tile waits for its chunk before giving up
                                    (microseconds, default 2,000,000) */
     RAG_OPT_ARRIVAL_DELAY_US = 4, /* test hook: the kernel copy engines hold each counter bump back

@@ -85,7 +85,7 @@ struct rag_ctx {
   long long wall_khz = 100000;
   // options
   int copy_engine = RAG_COPY_IN_GEMM;
-  int comm_wgs = 32;
+  int comm_wgs = 128;
   long long spin_us = 2000000;
   long long delay_us = 0;
   unsigned withhold = 0;
