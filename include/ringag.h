@@ -71,7 +71,8 @@ enum {
     RAG_ENOMEM = -4     /* a library-owned buffer could not be allocated */
 };
 
-/* Element types of the GEMM inputs.  The output D is always bf16. */
+/* Element types of the GEMM inputs, and of ag_gemm_ex's output D (bf16 unless ag_gemm_ex asks for
+ * E4M3; every other entry point writes bf16). */
 typedef enum {
     RAG_BF16 = 0,       /* bfloat16 */
     RAG_FP8_E4M3 = 1    /* OCP FP8 E4M3 (no infinities, max 448) with one fp32 scale per tensor */
@@ -175,10 +176,16 @@ typedef struct rag_ctx rag_ctx;     /* opaque; owned by the library */
  * context.  TransformerEngine PR #2443, sequence diagram: context creation at initialisation. */
 RAG_API int rag_create(rag_ctx** out, int device, int max_tp, int flags);
 
-/* Destroy a context (waits for its side stream first).  Safe on NULL. */
+/* Destroy a context: waits for its side stream, then destroys its streams and events and frees
+ * its counters and cached buffers.  Safe on NULL; always returns RAG_OK.  TransformerEngine PR
+ * #2443, sequence diagram, cleanup phase: the overlap object's destructor destroys the context
+ * (nvte_comm_gemm_ctx_destroy) or, on the other backend, its streams and events. */
 RAG_API int rag_destroy(rag_ctx* ctx);
 
-/* Set an option (RAG_OPT_*).  Takes effect from the next call. */
+/* Set an option (RAG_OPT_*).  Takes effect from the next call.  The library's own addition (the
+ * pages configure their overlap objects through constructor arguments): engine, tile and test-hook
+ * settings that the tests and the benchmark change between calls.  RAG_EINVAL for an unknown key
+ * or a value out of range (nothing changes then). */
 RAG_API int rag_set_option(rag_ctx* ctx, int key, long long value);
 
 /*
@@ -270,19 +277,25 @@ RAG_API int gemm_rs(rag_ctx* ctx,
             float* send, void* D,
             int flags, void* stream);
 
-/* Synchronise the context's device work and report whether any wait timed out since the last
- * check (RAG_ETIMEOUT; the error word is then cleared), or RAG_OK. */
+/* Synchronise the context's device (hipDeviceSynchronize) and report whether any wait of a
+ * counter-gated tile timed out since the last check: RAG_ETIMEOUT (the error word is then cleared
+ * and the message names the call's epoch), or RAG_OK.  The library's own addition: the pages'
+ * counter waits have no time limit; here a wait is bounded (RAG_OPT_SPIN_LIMIT_US) so that a
+ * chunk that never arrives ends as an error instead of a hang.  Errors: RAG_EINVAL (NULL ctx),
+ * RAG_EHIP. */
 RAG_API int rag_check(rag_ctx* ctx);
 
 /* GEMM kernel durations (milliseconds) recorded since the last call to this function while
  * RAG_OPT_TIMING was on; synchronises those events.  Writes up to max_n values to out and returns
- * how many were recorded (>= 0), or a negative RAG_E* code. */
+ * how many were recorded (>= 0), or a negative RAG_E* code.  The library's own addition, for
+ * measurement: the pages time their kernels with a profiler (nvFuser PR #5742, nsys trace), which
+ * this gives without one. */
 RAG_API int rag_kernel_times(rag_ctx* ctx, float* out, int max_n);
 
 /* Name of the GPU kernel entry point a chunked ag_gemm call (bf16 output) would launch for these
  * sizes (nc rows per chunk, M output columns, tp chunks) with the context's current options (e.g.
- * "rag_ag_bf16_t256x256w8"), written NUL-terminated into buf (len bytes).  Diagnostics: lets a
- * profile be matched to the kernel a measurement ran. */
+ * "rag_ag_bf16_t256x256w8"), written NUL-terminated into buf (len bytes).  Diagnostics, the
+ * library's own addition: lets a profile be matched to the kernel a measurement ran. */
 RAG_API int rag_ag_kernel_name(rag_ctx* ctx, int nc, int M, int tp, rag_dtype dt, char* buf,
                                int len);
 
@@ -329,7 +342,10 @@ RAG_API int gemm_rs_ring(rag_ctx* ctx,
  *   reduced   HOST array of tp device pointers to bf16 [nc, Mo] reduced chunks (contiguous);
  *             entry self_rank ignored
  *   Y         [T, Mo] bf16 output, T = tp * nc
- * The all-gather's copies use the copy kernel, or SDMA with RAG_COPY_SDMA.
+ * Engines of the all-gather's copies: with RAG_COPY_IN_GEMM and no RAG_RS_ARRIVE, the GEMM+RS
+ * launch's own workgroups (after their tiles); with RAG_COPY_IN_GEMM and RAG_RS_ARRIVE, and with
+ * RAG_COPY_KERNEL, the copy kernel on the side stream; with RAG_COPY_SDMA, SDMA on the side
+ * stream.  Side-stream copies are joined back into `stream` before the call's later work.
  * Errors: RAG_EINVAL, RAG_EHIP.
  */
 RAG_API int linear_allreduce(rag_ctx* ctx,
@@ -343,13 +359,16 @@ RAG_API int linear_allreduce(rag_ctx* ctx,
 
 /* Name of the GPU kernel entry point gemm_rs would launch for these sizes (nc rows per chunk, Mo
  * output columns, tp chunks) with the context's current options (e.g. "rag_rs_t256x256w8").
- * Diagnostics, like rag_ag_kernel_name. */
+ * Diagnostics, the library's own addition, like rag_ag_kernel_name. */
 RAG_API int rag_rs_kernel_name(rag_ctx* ctx, int nc, int Mo, int tp, char* buf, int len);
 
-/* Text for the last non-zero return on the calling thread ("" if none). */
+/* Text for the last non-zero return on the calling thread ("" if none): names the entry point,
+ * the offending argument and its value, or the HIP call and its error string.  TransformerEngine
+ * PR #2443, review comments: an error message should say what was chosen and what it requires
+ * instead of only that something failed. */
 RAG_API const char* rag_last_error(void);
 
-/* Library version, major * 10000 + minor * 100 + patch. */
+/* Library version, major * 10000 + minor * 100 + patch.  The library's own addition. */
 RAG_API int rag_version(void);
 
 #ifdef __cplusplus

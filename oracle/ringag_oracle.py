@@ -22,8 +22,11 @@ Products and sums are fp32 with k ascending and no fused multiply-add (the workl
 accumulation); the C library under this directory does the loops.
 
 Pins: every function here is checked by the CPU tests against exact integer products, float64
-brute force within the fp32 error bound, hand-worked fixtures and library conversions.  No function
-is "parity unpinned".
+brute force within the fp32 error bound, hand-worked fixtures and library conversions; the
+sampled-row forms (ag_gemm_rows, ag_gemm_fp8_rows, gemm_rs_rows, gemm_rs_ring_step_rows) are also
+checked against exact integer products at rows that span every chunk and bit for bit against rows
+of their full forms, and planted row-index mistakes are shown to fail those pins.  No function is
+"parity unpinned".
 """
 from __future__ import annotations
 
@@ -220,6 +223,8 @@ def ag_gemm_fp8(A_q: np.ndarray, scale_A: float, chunk_q: Sequence[np.ndarray],
 
 
 def ag_gemm_fp8_rows(A_q, scale_A, chunk_q, scale_B, rows) -> np.ndarray:
+    """Rows `rows` (indices into the gathered N) of the fp8 AG+GEMM result on dequantised values,
+    fp32 (same loop and order as ag_gemm_fp8)."""
     G = gather(chunk_q)
     return gemm_tn_rows(dequantize_e4m3(G, scale_B), dequantize_e4m3(A_q, scale_A), rows)
 

@@ -255,6 +255,84 @@ def test_fp8_gemm_random_within_bound():
     assert np.all(np.abs(D - exact) <= _fp32_bound(Ga.astype(np.float32), Aa.astype(np.float32)))
 
 
+def _int_ag_inputs(rng, tp, nc, K, M):
+    chunks = [rng.integers(-3, 4, (nc, K)) for _ in range(tp)]
+    A = rng.integers(-3, 4, (M, K))
+    return chunks, A
+
+
+def _rows_pin_pass(rows_fn):
+    """rows_fn(A_bits, chunk_bits, rows) against the exact int64 product of the explicitly
+    concatenated chunks, on integer inputs (exact in bf16 and in fp32), at rows that span every
+    chunk, repeat, and come out of order."""
+    rng = np.random.default_rng(31)
+    tp, nc, K, M = 3, 5, 48, 7
+    chunks, A = _int_ag_inputs(rng, tp, nc, K, M)
+    exact = _exact_gemm(np.concatenate(chunks), A)
+    rows = [14, 0, 5, 4, 9, 10, 5, 13]
+    try:
+        got = rows_fn(_bf16_bits(A), [_bf16_bits(c) for c in chunks], rows)
+        return got.shape == (len(rows), M) and np.array_equal(got.astype(np.int64), exact[rows])
+    except Exception:
+        return False
+
+
+def test_ag_rows_exact_integers():
+    assert _rows_pin_pass(O.ag_gemm_rows)
+
+
+def test_ag_rows_match_full_random():
+    """The sampled-row form used at full size is bit-identical to rows of the full AG+GEMM (same
+    loop, same order), for random bf16 data and every chunk."""
+    rng = np.random.default_rng(32)
+    tp, nc, K, M = 4, 6, 96, 9
+    chunks = [_bf16_bits(rng.standard_normal((nc, K))) for _ in range(tp)]
+    A = _bf16_bits(rng.standard_normal((M, K)))
+    rows = [23, 0, 6, 5, 11, 12, 17, 18, 1]
+    _, full = O.ag_gemm(A, chunks)
+    assert np.array_equal(O.ag_gemm_rows(A, chunks, rows), full[rows])
+    with pytest.raises(IndexError):
+        O.ag_gemm_rows(A, chunks, [tp * nc])
+
+
+def test_ag_fp8_rows_exact_integers_and_match_full():
+    rng = np.random.default_rng(33)
+    tp, nc, K, M = 3, 4, 128, 6
+    chunks, A = _int_ag_inputs(rng, tp, nc, K, M)
+    q = lambda x: torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).view(
+        torch.uint8).numpy()
+    sa, sb = 0.5, 0.125
+    rows = [11, 0, 4, 3, 8, 4]
+    got = O.ag_gemm_fp8_rows(q(A), sa, [q(c) for c in chunks], sb, rows)
+    exact = _exact_gemm(np.concatenate(chunks), A)[rows] * (sa * sb)
+    assert np.array_equal(got.astype(np.float64), exact)
+    # random codes: bit-identical to rows of the full fp8 AG+GEMM
+    x = torch.from_numpy(rng.standard_normal((M + tp * nc, K)).astype(np.float32))
+    codes = x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    a_codes, b = codes[:M], [codes[M + r * nc:M + (r + 1) * nc] for r in range(tp)]
+    _, full = O.ag_gemm_fp8(a_codes, 0.03125, b, 0.0078125)
+    assert np.array_equal(O.ag_gemm_fp8_rows(a_codes, 0.03125, b, 0.0078125, rows), full[rows])
+
+
+def test_rows_pin_catches_planted_row_mistakes():
+    """Plausible mistakes in a sampled-row helper, planted in copies on the CPU: a row index taken
+    within its chunk instead of within the gathered N, off by one, or read from the chunks in
+    arrival order instead of rank order."""
+    nc = 5
+
+    def within_chunk(A, ch, rows):
+        return O.ag_gemm_rows(A, ch, [r % nc for r in rows])
+
+    def off_by_one(A, ch, rows):
+        return O.ag_gemm_rows(A, ch, [min(r + 1, 3 * nc - 1) for r in rows])
+
+    def arrival_order(A, ch, rows):
+        return O.ag_gemm_rows(A, [ch[r] for r in O.ring_order(len(ch), 1)], rows)
+
+    for bad in (within_chunk, off_by_one, arrival_order):
+        assert not _rows_pin_pass(bad), bad.__name__
+
+
 # ------------------------------------------------------------------------------------ GEMM+RS
 
 def test_rs_hand_fixture():
