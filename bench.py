@@ -116,9 +116,11 @@ def pctl(xs, q):
     return xs[min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))]
 
 
-def cpu_baseline_ag(inp, target_s):
+def cpu_baseline_ag(inp, target_s, D_timed):
     """The oracle (as it stands) on whole output rows of the same workload; sample sized so the
-    timed part takes about target_s seconds of wall time."""
+    timed part takes about target_s seconds of wall time (all rows when they fit).  The rows it
+    computes are also the reference for the output of the last timed GPU step: returns
+    (baseline, parity)."""
     import numpy as np
     from oracle import ringag_oracle as O
     from ring_all_gather_amd import workloads as W
@@ -137,15 +139,26 @@ def cpu_baseline_ag(inp, target_s):
     nrows = int(min(s.N, max(16, len(probe) * target_s / dt)))
     rows = np.linspace(0, s.N - 1, nrows).astype(np.int64)
     t = time.perf_counter()
-    O.gemm_tn_rows(G, A, rows)
+    ref = O.gemm_tn_rows(G, A, rows)
     dt = time.perf_counter() - t
-    return {"value": round(flops_row * nrows / dt / 1e12, 6), "unit": "TFLOP/s",
+    base = {"value": round(flops_row * nrows / dt / 1e12, 6), "unit": "TFLOP/s",
             "cores": O.num_threads(), "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{nrows} of the {s.N} output rows (each {s.M}x{s.K} MACs, fp32 triple loop "
                       f"over the gathered input), {dt:.1f} s wall"}
+    got = O.bf16_to_f32(W.bits_u16(D_timed.cpu()))[rows].astype(np.float64)
+    err = float(np.abs(got - ref).max() / max(float(np.abs(ref).max()), 1e-30))
+    tol = 5e-2 if fp8 else 2e-2
+    par = {"rows_checked": int(nrows), "of_rows": int(s.N), "max_rel_err": round(err, 6),
+           "tolerance": tol, "ok": bool(np.isfinite(err) and err <= tol)}
+    return base, par
 
 
-def cpu_baseline_rs(inp, target_s):
+def cpu_baseline_rs(inp, target_s, D_timed, send_timed):
+    """The oracle on whole rows of the local partial X W^T (sample sized for about target_s
+    seconds, all rows when they fit).  Those rows are also the reference for the outgoing chunks
+    of the last timed GPU step (send[c] = rows of chunk c of the partial), and the oracle's
+    reduce-scatter on the own chunk's sampled rows is the reference for its D: returns (baseline,
+    parity)."""
     import numpy as np
     from oracle import ringag_oracle as O
     from ring_all_gather_amd import workloads as W
@@ -160,12 +173,28 @@ def cpu_baseline_rs(inp, target_s):
     nrows = int(min(s.T, max(16, len(probe) * target_s / dt)))
     rows = np.linspace(0, s.T - 1, nrows).astype(np.int64)
     t = time.perf_counter()
-    O.gemm_tn_rows(Xf, Wf, rows)
+    P_rows = O.gemm_tn_rows(Xf, Wf, rows)
     dt = time.perf_counter() - t
-    return {"value": round(flops_row * nrows / dt / 1e12, 6), "unit": "TFLOP/s",
+    base = {"value": round(flops_row * nrows / dt / 1e12, 6), "unit": "TFLOP/s",
             "cores": O.num_threads(), "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{nrows} of the {s.T} rows of the local partial X W^T (each {s.Mo}x{s.Kl} "
                       f"MACs, fp32 triple loop), {dt:.1f} s wall"}
+    send = send_timed.cpu().numpy()
+    chunk = rows // s.nc
+    out_rows = chunk != s.self_rank
+    got_send = send[chunk[out_rows], rows[out_rows] % s.nc]
+    ref_send = P_rows[out_rows]
+    e_send = float(np.abs(got_send - ref_send).max() / max(float(np.abs(ref_send).max()), 1e-30))
+    own = rows[~out_rows] - s.self_rank * s.nc
+    peers = [None if p is None else p.numpy() for p in inp.partials]
+    D_ref = O.gemm_rs_rows(Xb, Wb, peers, s.tp, s.self_rank, own)
+    got_D = O.bf16_to_f32(W.bits_u16(D_timed.cpu()))[own].astype(np.float64)
+    e_D = float(np.abs(got_D - D_ref).max() / max(float(np.abs(D_ref).max()), 1e-30))
+    par = {"rows_checked": int(nrows), "of_rows": int(s.T), "D_rows_checked": int(len(own)),
+           "max_rel_err_D": round(e_D, 6), "max_rel_err_send": round(e_send, 8),
+           "tolerance_D": 2e-2, "tolerance_send": 1e-3,
+           "ok": bool(e_D <= 2e-2 and e_send <= 1e-3)}
+    return base, par
 
 
 def cpu_model() -> str:
@@ -216,6 +245,34 @@ def timeline_ag(ctx, B, step, shape, kname):
     return {"tiles_per_chunk": per_chunk, "copies_start_us": us(w[32]),
             "gemm_end_us": us(max(x[2] for x in tiles)),
             "tile_clock_ghz": {"p10": q(0.1), "p50": q(0.5), "p90": q(0.9)}, "chunks": chunks}
+
+
+def overlap_per_engine(ctx, B, step, args, stream, shape, ms_head):
+    """T_gemm_only, T_copy_only, T_chunked, the overlap ratio and the hidden fraction for the
+    headline copy engine (whose chunked time was just measured) and, unless --headline-only, for
+    the other engines.  Each engine's GEMM-only launch uses the tile its chunked call uses (the
+    side-stream kernel engine may pick another kernel of the same tile size, see the library's
+    tile choice), so the three times are of the same kernel."""
+    names = [args.copy_engine] + ([] if args.headline_only else
+                                  [e for e in ("in-gemm", "kernel", "sdma") if e != args.copy_engine])
+    res = {}
+    for eng in names:
+        ctx.set_option(B.RAG_OPT_COPY_ENGINE, B.ENGINES[eng])
+        kname = ctx.ag_kernel_name(shape.nc, shape.M, shape.tp, shape.dtype == "fp8")
+        t_chunked = ms_head if eng == args.copy_engine else \
+            time_steps(step, args.steps, args.warmup, stream)
+        t_copy = time_steps(lambda: step(B.RAG_COPY_ONLY), args.steps, args.warmup, stream)
+        tile = kname.split("_t", 1)[1]
+        if args.tile == "auto":
+            ctx.set_option(B.RAG_OPT_TILE, B.TILES[tile])
+        t_gemm = time_steps(lambda: step(B.RAG_NO_COPY), args.steps, args.warmup, stream)
+        ctx.set_option(B.RAG_OPT_TILE, B.TILES[args.tile])
+        ctx.check()
+        res[eng] = {"kernel": kname, "t_chunked_ms": round(t_chunked, 5),
+                    "t_gemm_only_ms": round(t_gemm, 5), "t_copy_only_ms": round(t_copy, 5),
+                    "overlap_ratio": round(t_chunked / (t_copy + t_gemm), 4),
+                    "hidden_fraction": round((t_copy + t_gemm - t_chunked) / t_copy, 4)}
+    return res
 
 
 def measured_traffic(workload: str, kernel: str, fingerprint: str):
@@ -271,6 +328,7 @@ def main():
                       flags=flags)
 
         ms = time_steps(step, args.steps, args.warmup, stream)
+        D_timed = D.clone()   # the output of the last timed step, checked against the oracle
         # instrumented pass right after it: per-step events, and the library's events around each
         # GEMM launch on the stream it runs on (the roofline's kernel duration)
         ctx.kernel_times()
@@ -279,10 +337,13 @@ def main():
         kt = ctx.kernel_times()
         ctx.set_option(B.RAG_OPT_TIMING, 0)
         ctx.check()
-        ms_gemm = time_steps(lambda: step(B.RAG_NO_COPY), args.steps, args.warmup, stream)
-        ms_copy = time_steps(lambda: step(B.RAG_COPY_ONLY), args.steps, args.warmup, stream)
+        kname = ctx.ag_kernel_name(shape.nc, shape.M, shape.tp, shape.dtype == "fp8")
+        engines = overlap_per_engine(ctx, B, step, args, stream, shape, ms)
+        head = engines[args.copy_engine]
+        ms_gemm, ms_copy = head["t_gemm_only_ms"], head["t_copy_only_ms"]
         ms_staged = ms_split = ms_seq = None
         if not args.headline_only:
+            ctx.set_option(B.RAG_OPT_COPY_ENGINE, B.ENGINES[args.copy_engine])
             ms_staged = time_steps(lambda: step(B.RAG_STAGED_OUT), args.steps, args.warmup,
                                    stream)
             # the split form (one GEMM launch per chunk, gated by stream events): what the
@@ -292,10 +353,10 @@ def main():
             ms_seq = time_steps(lambda: (step(B.RAG_COPY_ONLY), step(B.RAG_NO_COPY)), args.steps,
                                 args.warmup, stream)
         ctx.check()
+        ctx.set_option(B.RAG_OPT_COPY_ENGINE, B.ENGINES[args.copy_engine])
         flops = shape.flops
         kernel_ms = statistics.fmean(kt)
         achieved = flops / (kernel_ms * 1e-3) / 1e12
-        kname = ctx.ag_kernel_name(shape.nc, shape.M, shape.tp, shape.dtype == "fp8")
         traffic = measured_traffic(args.workload, kname, B.kernels_fingerprint())
         peak = PEAK_TFLOPS[shape.dtype]
         value = flops / (ms * 1e-3) / 1e12
@@ -322,15 +383,22 @@ def main():
                         "t_copy_then_gemm_ms": rnd(ms_seq),
                         "chunked_vs_copy_then_gemm": rnd(ms_seq and ms / ms_seq, 4),
                         "t_staged_out_ms": rnd(ms_staged),
-                        "t_split_per_chunk_ms": rnd(ms_split)},
+                        "t_split_per_chunk_ms": rnd(ms_split),
+                        "per_engine": engines},
             "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                          "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                          "kernel": kname, "kernel_ms": round(kernel_ms, 5)},
         }
         if not (args.no_timeline or args.headline_only):
             out["timeline"] = timeline_ag(ctx, B, step, shape, kname)
+        # the gathered buffer must hold every chunk at its rank offset, bit for bit
+        G_ok = all(torch.equal(G[r * shape.nc:(r + 1) * shape.nc].view(torch.uint8),
+                               chunks[r].view(torch.uint8)) for r in range(shape.tp))
+        out["parity"] = {"G_equals_chunks": bool(G_ok)}
         if not args.no_cpu:
-            out["cpu_baseline"] = cpu_baseline_ag(inp, args.cpu_seconds)
+            base, par = cpu_baseline_ag(inp, args.cpu_seconds, D_timed)
+            out["cpu_baseline"] = base
+            out["parity"].update(par)
     else:
         inp = W.make_rs(shape)
         X, Wt = inp.X.to(dev), inp.W.to(dev)
@@ -342,6 +410,7 @@ def main():
             B.gemm_rs(ctx, X, Wt, parts, shape.tp, shape.self_rank, D, send=send)
 
         ms = time_steps(step, args.steps, args.warmup, stream)
+        D_timed, send_timed = D.clone(), send.clone()   # checked against the oracle below
         ctx.kernel_times()
         ctx.set_option(B.RAG_OPT_TIMING, 1)
         per = per_step_times(step, args.steps, stream)
@@ -417,16 +486,23 @@ def main():
                 lambda: B.linear_allreduce(ctx, X, Wt, parts, red, shape.tp, shape.self_rank, Y,
                                            send=send), args.steps, args.warmup, stream)
             ctx.check()
+            # the gathered chunks of Y after the timed steps: bit for bit the owners' reduced chunks
+            nc_ = shape.nc
+            y_gather_ok = all(
+                torch.equal(Y[c * nc_:(c + 1) * nc_].view(torch.int16), red[c].view(torch.int16))
+                for c in range(shape.tp) if c != shape.self_rank)
             out["variants_ms_per_step"] = {
                 "one_shot_partials_given": round(ms, 5),
                 "one_shot_partials_arrive": round(ms_arrive, 5),
                 "ring_step_sums_given": round(ms_ring, 5),
                 "ring_step_sums_arrive": round(ms_ring_arrive, 5),
                 "linear_allreduce": round(ms_lar, 5),
+                "linear_allreduce_gather_bitwise_ok": bool(y_gather_ok),
                 "arrival_engine": args.copy_engine,
                 "comm_wgs": args.comm_wgs}
         if not args.no_cpu:
-            out["cpu_baseline"] = cpu_baseline_rs(inp, args.cpu_seconds)
+            out["cpu_baseline"], out["parity"] = cpu_baseline_rs(inp, args.cpu_seconds, D_timed,
+                                                                 send_timed)
     ctx.close()
     print(json.dumps(out), flush=True)
     return 0

@@ -38,8 +38,10 @@
  *     or run the copies themselves; with RAG_COPY_ONLY on the side stream, `stream` waits for an
  *     event of the side stream instead).  So in `stream`
  *     order the inputs may be reused and the outputs are complete.
- *   - One operation in flight per context; a context is not thread-safe.  Calls on different
- *     contexts are independent.
+ *   - One operation in flight per context; a context is not thread-safe.  Consecutive calls on
+ *     one context must be ordered: issue them on one stream, or make a later call's stream wait
+ *     for the earlier call's (they share the context's counters).  Calls on different contexts
+ *     are independent.
  *   - Every entry point returns RAG_OK (0) or a negative RAG_E* code and never throws.  Arguments
  *     are validated before any device work is enqueued; on failure nothing is enqueued and
  *     rag_last_error() describes the problem.

@@ -60,21 +60,31 @@ bool debug_enabled() {
 
 }  // namespace
 
+// One set of the device words a call uses, with the host-side state that goes with them: a
+// context's own allocation (other sets can be added without touching the calls).
+// Layout, kWordStride ints apart: ctr[kMaxTp] (ready counters; a context allocates max_tp) |
+// copy-complete counter | piece counts [2 sets][grab, done][kArrSlots] | error word.
+struct Words {
+  int* ctr = nullptr;
+  unsigned* arr = nullptr;
+  int* err = nullptr;
+  int epoch = 0;
+  unsigned arr_seq = 0;   // copying launches so far (selects the set of grab/done counts)
+};
+
 struct rag_ctx {
   int device = 0;
   int max_tp = 0;
   hipStream_t side = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
-  hipEvent_t ev_ag = nullptr;          // linear_allreduce: end of the all-gather's copies
+  hipEvent_t ev_ag = nullptr;          // linear_allreduce: end of the side stream's copies
+  // After a copy kernel on the side stream: ev_side marks its end, and the next launch that runs
+  // copies on a caller's stream waits for it first (see join_side_copies)
+  hipEvent_t ev_side = nullptr;
+  bool side_pending = false;
   std::vector<hipEvent_t> ev_chunk;   // split form: chunk j copied (created on first use)
-  // device counters, kWordStride ints apart: ctr[max_tp] | copy-complete | arrival counts
-  // [2 sets][grab, done][kArrSlots] | err
-  int* words = nullptr;
-  int* ctr = nullptr;
-  unsigned* arr = nullptr;
-  int* err = nullptr;
-  int epoch = 0;
-  unsigned arr_seq = 0;   // arrival launches so far (selects the set of grab/done counts)
+  int* words = nullptr;   // the context's device words (hipMalloc at creation), see Words
+  Words w;
   void* gbuf = nullptr;
   size_t gbuf_bytes = 0;
   void* stage = nullptr;
@@ -147,9 +157,38 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-int next_epoch(rag_ctx* c) {
-  c->epoch = (c->epoch == 0x7fffffff) ? 1 : c->epoch + 1;
-  return c->epoch;
+// A copy kernel was just enqueued on the side stream.  A launch that runs copies clears the other
+// set of piece counts for the next call (copy_queue_begin), and the side stream's kernel may still
+// be running, or not yet have started, when the caller's stream moves on: its GEMM waits for the
+// copies' counters only, and workgroups that found the queue empty still add to the grab count on
+// their way out.  So the next launch that runs copies on a caller's stream waits for the side
+// stream's kernel to end first (join_side_copies); launches on the side stream itself are ordered
+// by the stream.
+int note_side_copies(rag_ctx* c) {
+  HIPCHK(hipEventRecord(c->ev_side, c->side));
+  c->side_pending = true;
+  return RAG_OK;
+}
+
+int join_side_copies(rag_ctx* c, hipStream_t stream) {
+  if (!c->side_pending) return RAG_OK;
+  HIPCHK(hipStreamWaitEvent(stream, c->ev_side, 0));
+  c->side_pending = false;
+  return RAG_OK;
+}
+
+int next_epoch(Words& W) {
+  W.epoch = (W.epoch == 0x7fffffff) ? 1 : W.epoch + 1;
+  return W.epoch;
+}
+
+// The set of piece counts the next copying launch on W uses, and the other set, which that
+// launch clears for the call after it.
+void use_count_set(const Words& W, CopyPlan& cp) {
+  const unsigned set = W.arr_seq & 1u;
+  cp.grab = W.arr + (size_t)set * 2 * kArrSlots * kWordStride;
+  cp.done = cp.grab + (size_t)kArrSlots * kWordStride;
+  cp.clear_next = W.arr + (size_t)(set ^ 1u) * 2 * kArrSlots * kWordStride;
 }
 
 // The largest tile that still gives every compute unit a tile: bigger tiles re-read less from
@@ -301,9 +340,9 @@ int finalize_staged(rag_ctx* c, void* D, int nc, int M, int tp, const int* order
 // each after waiting for its chunk's event.  The GEMM of one chunk is the same kernel with tp = 1
 // and no counters.  The own chunk's copy into G (if any) goes last, and the caller's stream waits
 // for the side stream's end before the call's later work.
-int ag_gemm_split(rag_ctx* c, const void* A, int M, int K, const void* const* B, int nc, int tp,
-                  int self_rank, char* Gp, bool own_copy, void* D, bool fp8, const float* scale_A,
-                  const float* scale_B, bool out8, const float* scale_D, float* amax_D,
+int ag_gemm_split(rag_ctx* c, Words& W, const void* A, int M, int K, const void* const* B,
+                  int nc, int tp, int self_rank, char* Gp, bool own_copy, void* D, bool fp8,
+                  const float* scale_A, const float* scale_B, bool out8, const float* scale_D, float* amax_D,
                   void* B_copy, bool staged, bool no_copy, bool copy_only, long long chunk_bytes,
                   const int* order, int epoch, hipStream_t stream) {
   if (c->ev_chunk.empty()) {
@@ -342,16 +381,15 @@ int ag_gemm_split(rag_ctx* c, const void* A, int M, int K, const void* const* B,
         aa.cp.bytes = (unsigned long long)chunk_bytes;
         aa.cp.piece_bytes = (unsigned)kArrivalThreads * 256u;
         aa.cp.pieces = (unsigned)((aa.cp.bytes + aa.cp.piece_bytes - 1) / aa.cp.piece_bytes);
-        const unsigned set = c->arr_seq & 1u;
-        aa.cp.grab = c->arr + (size_t)set * 2 * kArrSlots * kWordStride;
-        aa.cp.done = aa.cp.grab + (size_t)kArrSlots * kWordStride;
-        aa.cp.clear_next = c->arr + (size_t)(set ^ 1u) * 2 * kArrSlots * kWordStride;
+        use_count_set(W, aa.cp);
         aa.cp.delay_ticks = c->delay_us * c->wall_khz / 1000;
-        aa.ctr = c->ctr;
+        aa.ctr = W.ctr;
         aa.epoch = epoch;
         aa.raise_priority = c->copy_priority;
         HIPCHK(launch_arrival(c->device, aa, c->comm_wgs, c->side));
-        c->arr_seq++;
+        W.arr_seq++;
+        const int rc = note_side_copies(c);
+        if (rc) return rc;
       }
       if (j < tp) HIPCHK(hipEventRecord(c->ev_chunk[j], c->side));
     }
@@ -373,9 +411,9 @@ int ag_gemm_split(rag_ctx* c, const void* A, int M, int K, const void* const* B,
     a.tp = 1;
     a.ctr_index[0] = -1;
     a.join_index = -1;
-    a.ctr = c->ctr;
+    a.ctr = W.ctr;
     a.epoch = epoch;
-    a.err = c->err;
+    a.err = W.err;
     a.spin_limit = c->spin_us * c->wall_khz / 1000;
     a.scale_A = scale_A;
     a.scale_B = scale_B;
@@ -489,7 +527,7 @@ int rs_call(rag_ctx* c, const char* fn, bool ring, const void* X, int T, int Kl,
     int rc = ensure_buffer(&c->rsbuf, &c->rsbuf_bytes, (size_t)tp * slot * 4, "receive buffer");
     if (rc) return rc;
   }
-  const int epoch = next_epoch(c);
+  const int epoch = next_epoch(c->w);
   RsArgs a = {};
   a.X = X;
   a.W = W;
@@ -511,9 +549,9 @@ int rs_call(rag_ctx* c, const char* fn, bool ring, const void* X, int T, int Kl,
   a.tp = tp;
   a.self_rank = self_rank;
   a.gated = arrive && any;
-  a.ctr = c->ctr;
+  a.ctr = c->w.ctr;
   a.epoch = epoch;
-  a.err = c->err;
+  a.err = c->w.err;
   a.spin_limit = c->spin_us * c->wall_khz / 1000;
 
   // Arrivals: copies, in ring order, of what each tile's epilogue reads, releasing one counter per
@@ -544,16 +582,13 @@ int rs_call(rag_ctx* c, const char* fn, bool ring, const void* X, int T, int Kl,
     cp.bytes = (unsigned long long)slot * 4;
     cp.piece_bytes = (unsigned)kArrivalThreads * 256u;
     cp.pieces = (unsigned)((cp.bytes + cp.piece_bytes - 1) / cp.piece_bytes);
-    const unsigned set = c->arr_seq & 1u;
-    cp.grab = c->arr + (size_t)set * 2 * kArrSlots * kWordStride;
-    cp.done = cp.grab + (size_t)kArrSlots * kWordStride;
-    cp.clear_next = c->arr + (size_t)(set ^ 1u) * 2 * kArrSlots * kWordStride;
+    use_count_set(c->w, cp);
     cp.delay_ticks = c->delay_us * c->wall_khz / 1000;
     cp.withhold_mask = c->withhold;
     if (in_gemm) {
       a.copies = 1;
       a.cp = cp;
-      c->arr_seq++;
+      c->w.arr_seq++;
     } else {
       HIPCHK(hipEventRecord(c->ev_fork, stream));
       HIPCHK(hipStreamWaitEvent(c->side, c->ev_fork, 0));
@@ -562,17 +597,19 @@ int rs_call(rag_ctx* c, const char* fn, bool ring, const void* X, int T, int Kl,
           HIPCHK(hipMemcpyAsync(cp.dst[k], cp.src[k], (size_t)cp.bytes, hipMemcpyDeviceToDeviceNoCU,
                                 c->side));
           if (!((c->withhold >> cp.pos[k]) & 1u))
-            HIPCHK(hipStreamWriteValue32(c->side, c->ctr + (size_t)cp.ctr_index[k] * kWordStride,
+            HIPCHK(hipStreamWriteValue32(c->side, c->w.ctr + (size_t)cp.ctr_index[k] * kWordStride,
                                          (uint32_t)epoch, 0));
         }
       } else {
         ArrivalArgs aa = {};
         aa.cp = cp;
-        aa.ctr = c->ctr;
+        aa.ctr = c->w.ctr;
         aa.epoch = epoch;
         aa.raise_priority = c->copy_priority;
         HIPCHK(launch_arrival(c->device, aa, c->comm_wgs, c->side));
-        c->arr_seq++;
+        c->w.arr_seq++;
+        const int rc = note_side_copies(c);
+        if (rc) return rc;
       }
       // every copy is waited for by some tile, except the ring step's passed-on sums when send is
       // NULL (those tiles are skipped): then the caller's stream waits for the side stream
@@ -584,11 +621,8 @@ int rs_call(rag_ctx* c, const char* fn, bool ring, const void* X, int T, int Kl,
   if (extra_copies) {
     a.copies = 1;
     a.cp = *extra_copies;
-    const unsigned set = c->arr_seq & 1u;
-    a.cp.grab = c->arr + (size_t)set * 2 * kArrSlots * kWordStride;
-    a.cp.done = a.cp.grab + (size_t)kArrSlots * kWordStride;
-    a.cp.clear_next = c->arr + (size_t)(set ^ 1u) * 2 * kArrSlots * kWordStride;
-    c->arr_seq++;
+    use_count_set(c->w, a.cp);
+    c->w.arr_seq++;
   }
   const bool beside =
       ((a.gated && !in_gemm) || other_copies_beside) && c->copy_engine != RAG_COPY_SDMA;
@@ -641,6 +675,10 @@ int rs_call(rag_ctx* c, const char* fn, bool ring, const void* X, int T, int Kl,
   if (debug_enabled())
     fprintf(stderr, "[ringag] %s tp=%d s=%d T=%d Kl=%d Mo=%d tile=%dx%d tiles=%d grid=%d "
             "arrive=%d\n", fn, tp, self_rank, T, Kl, Mo, bi, bj, total, grid, (int)arrive);
+  if (a.copies) {
+    const int rc = join_side_copies(c, stream);
+    if (rc) return rc;
+  }
   hipEvent_t ev0, ev1;
   launch_timing_events(c, &ev0, &ev1);
   HIPCHK(launch_gemm_rs(c->device, a, tile, grid, stream, ev0, ev1));
@@ -691,6 +729,7 @@ int rag_create(rag_ctx** out, int device, int max_tp, int flags) {
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_ag, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_side, hipEventDisableTiming);
   if (e == hipSuccess) e = hipMalloc((void**)&c->words, nwords * sizeof(int));
   if (e == hipSuccess) e = hipMemset(c->words, 0, nwords * sizeof(int));
   if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -699,9 +738,9 @@ int rag_create(rag_ctx** out, int device, int max_tp, int flags) {
     rag_destroy(c);
     return fail(RAG_EHIP, "%s", msg.c_str());
   }
-  c->ctr = c->words;
-  c->arr = reinterpret_cast<unsigned*>(c->words + (size_t)(max_tp + 1) * kWordStride);
-  c->err = c->words + (size_t)(max_tp + 1 + 4 * kArrSlots) * kWordStride;
+  c->w.ctr = c->words;
+  c->w.arr = reinterpret_cast<unsigned*>(c->words + (size_t)(max_tp + 1) * kWordStride);
+  c->w.err = c->words + (size_t)(max_tp + 1 + 4 * kArrSlots) * kWordStride;
   *out = c;
   if (debug_enabled())
     fprintf(stderr, "[ringag] context on device %d (%s, %d CUs, wall clock %lld kHz), max_tp %d\n",
@@ -719,6 +758,7 @@ int rag_destroy(rag_ctx* c) {
   if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
   if (c->ev_join) (void)hipEventDestroy(c->ev_join);
   if (c->ev_ag) (void)hipEventDestroy(c->ev_ag);
+  if (c->ev_side) (void)hipEventDestroy(c->ev_side);
   if (c->side) (void)hipStreamDestroy(c->side);
   if (c->words) (void)hipFree(c->words);
   if (c->gbuf) (void)hipFree(c->gbuf);
@@ -803,59 +843,65 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
                     nullptr, nullptr, nullptr, flags, stream_v);
 }
 
-int ag_gemm_ex(rag_ctx* c, const void* A, int M, int K, const void* const* B, int nc, int tp,
-               int self_rank, void* G, void* D, rag_dtype dt, const float* scale_A,
-               const float* scale_B, rag_dtype d_dt, const float* scale_D, float* amax_D,
-               void* B_copy, int flags, void* stream_v) {
-  if (!c) return fail(RAG_EINVAL, "ag_gemm: ctx is NULL");
+}  // extern "C"
+
+namespace {
+
+// ag_gemm_ex on the device words W.
+int ag_call(rag_ctx* c, Words& W, const char* fn, const void* A, int M, int K,
+            const void* const* B, int nc, int tp, int self_rank, void* G, void* D, rag_dtype dt, const float* scale_A,
+            const float* scale_B, rag_dtype d_dt, const float* scale_D, float* amax_D,
+            void* B_copy, int flags, void* stream_v) {
   if (tp < 1 || tp > c->max_tp)
-    return fail(RAG_EINVAL, "ag_gemm: tp=%d outside [1, %d] (max_tp of the context)", tp, c->max_tp);
+    return fail(RAG_EINVAL, "%s: tp=%d outside [1, %d] (max_tp of the context)", fn, tp,
+                c->max_tp);
   if (self_rank < 0 || self_rank >= tp)
-    return fail(RAG_EINVAL, "ag_gemm: self_rank=%d outside [0, tp=%d)", self_rank, tp);
-  if (dt != RAG_BF16 && dt != RAG_FP8_E4M3) return fail(RAG_EINVAL, "ag_gemm: unknown dtype %d", dt);
+    return fail(RAG_EINVAL, "%s: self_rank=%d outside [0, tp=%d)", fn, self_rank, tp);
+  if (dt != RAG_BF16 && dt != RAG_FP8_E4M3)
+    return fail(RAG_EINVAL, "%s: unknown dtype %d", fn, dt);
   const bool fp8 = dt == RAG_FP8_E4M3;
   const int esz = fp8 ? 1 : 2;
   const int kmul = fp8 ? 128 : 64;
   if (M < 1 || nc < 1 || K < 1)
-    return fail(RAG_EINVAL, "ag_gemm: M=%d, K=%d, nc=%d must all be >= 1", M, K, nc);
+    return fail(RAG_EINVAL, "%s: M=%d, K=%d, nc=%d must all be >= 1", fn, M, K, nc);
   if (K % kmul)
-    return fail(RAG_EINVAL, "ag_gemm: K=%d must be a multiple of %d for %s", K, kmul,
+    return fail(RAG_EINVAL, "%s: K=%d must be a multiple of %d for %s", fn, K, kmul,
                 fp8 ? "fp8" : "bf16");
   if (flags & ~(RAG_STAGED_OUT | RAG_NO_COPY | RAG_COPY_ONLY | RAG_PER_CHUNK))
-    return fail(RAG_EINVAL, "ag_gemm: unknown flag bits 0x%x", flags);
+    return fail(RAG_EINVAL, "%s: unknown flag bits 0x%x", fn, flags);
   if ((flags & RAG_NO_COPY) && (flags & RAG_COPY_ONLY))
-    return fail(RAG_EINVAL, "ag_gemm: RAG_NO_COPY and RAG_COPY_ONLY exclude each other");
-  if (!A || !B || !D) return fail(RAG_EINVAL, "ag_gemm: A, B_chunks and D must not be NULL");
+    return fail(RAG_EINVAL, "%s: RAG_NO_COPY and RAG_COPY_ONLY exclude each other", fn);
+  if (!A || !B || !D) return fail(RAG_EINVAL, "%s: A, B_chunks and D must not be NULL", fn);
   for (int r = 0; r < tp; ++r) {
-    if (!B[r]) return fail(RAG_EINVAL, "ag_gemm: B_chunks[%d] is NULL", r);
-    if (misaligned(B[r])) return fail(RAG_EINVAL, "ag_gemm: B_chunks[%d] is not 16-byte aligned", r);
+    if (!B[r]) return fail(RAG_EINVAL, "%s: B_chunks[%d] is NULL", fn, r);
+    if (misaligned(B[r])) return fail(RAG_EINVAL, "%s: B_chunks[%d] is not 16-byte aligned", fn, r);
   }
   if (misaligned(A) || misaligned(D) || (G && misaligned(G)))
-    return fail(RAG_EINVAL, "ag_gemm: A, G and D must be 16-byte aligned");
+    return fail(RAG_EINVAL, "%s: A, G and D must be 16-byte aligned", fn);
   if (fp8 && (!scale_A || !scale_B))
-    return fail(RAG_EINVAL, "ag_gemm: fp8 needs scale_A and scale_B");
+    return fail(RAG_EINVAL, "%s: fp8 needs scale_A and scale_B", fn);
   if (!fp8 && (scale_A || scale_B))
-    return fail(RAG_EINVAL, "ag_gemm: scales are only meaningful for fp8; pass NULL for bf16");
+    return fail(RAG_EINVAL, "%s: scales are only meaningful for fp8; pass NULL for bf16", fn);
   if (d_dt != RAG_BF16 && d_dt != RAG_FP8_E4M3)
-    return fail(RAG_EINVAL, "ag_gemm: unknown output dtype %d", d_dt);
+    return fail(RAG_EINVAL, "%s: unknown output dtype %d", fn, d_dt);
   const bool out8 = d_dt == RAG_FP8_E4M3;
   const int oesz = out8 ? 1 : 2;
-  if (out8 && !scale_D) return fail(RAG_EINVAL, "ag_gemm: fp8 output needs scale_D");
+  if (out8 && !scale_D) return fail(RAG_EINVAL, "%s: fp8 output needs scale_D", fn);
   if (!out8 && (scale_D || amax_D))
-    return fail(RAG_EINVAL, "ag_gemm: scale_D and amax_D are only meaningful for fp8 output");
+    return fail(RAG_EINVAL, "%s: scale_D and amax_D are only meaningful for fp8 output", fn);
   if ((amax_D && (reinterpret_cast<uintptr_t>(amax_D) & 3u)) || (B_copy && misaligned(B_copy)))
-    return fail(RAG_EINVAL, "ag_gemm: amax_D must be 4-byte and B_copy 16-byte aligned");
+    return fail(RAG_EINVAL, "%s: amax_D must be 4-byte and B_copy 16-byte aligned", fn);
   {
     HIPCHK(hipSetDevice(c->device));
     const void* named[] = {A, D, G, scale_A, scale_B, scale_D, amax_D, B_copy};
     const char* names[] = {"A", "D", "G", "scale_A", "scale_B", "scale_D", "amax_D", "B_copy"};
     for (int i = 0; i < 8; ++i)
       if (named[i] && !on_device(named[i], c->device))
-        return fail(RAG_EINVAL, "ag_gemm: %s is not device memory of device %d", names[i],
+        return fail(RAG_EINVAL, "%s: %s is not device memory of device %d", fn, names[i],
                     c->device);
     for (int r = 0; r < tp; ++r)
       if (!on_device(B[r], c->device))
-        return fail(RAG_EINVAL, "ag_gemm: B_chunks[%d] is not device memory of device %d", r,
+        return fail(RAG_EINVAL, "%s: B_chunks[%d] is not device memory of device %d", fn, r,
                     c->device);
   }
   const long long a_bytes = (long long)M * K * esz;
@@ -863,30 +909,30 @@ int ag_gemm_ex(rag_ctx* c, const void* A, int M, int K, const void* const* B, in
   const long long g_bytes = chunk_bytes * tp;
   const long long d_bytes = (long long)tp * nc * M * oesz;
   if (a_bytes > kMaxOperandBytes || chunk_bytes > kMaxOperandBytes)
-    return fail(RAG_EINVAL, "ag_gemm: the weight (%lld B) and each chunk (%lld B) must be < 2 GiB",
+    return fail(RAG_EINVAL, "%s: the weight (%lld B) and each chunk (%lld B) must be < 2 GiB", fn,
                 a_bytes, chunk_bytes);
   if (overlaps(D, d_bytes, A, a_bytes) || (G && overlaps(G, g_bytes, A, a_bytes)) ||
       (G && overlaps(G, g_bytes, D, d_bytes)))
-    return fail(RAG_EINVAL, "ag_gemm: G and D must not overlap A or each other");
+    return fail(RAG_EINVAL, "%s: G and D must not overlap A or each other", fn);
   for (int r = 0; r < tp; ++r)
     if (overlaps(D, d_bytes, B[r], chunk_bytes) ||
         (G && r != self_rank && overlaps(G, g_bytes, B[r], chunk_bytes)))
-      return fail(RAG_EINVAL, "ag_gemm: G and D must not overlap B_chunks[%d]", r);
+      return fail(RAG_EINVAL, "%s: G and D must not overlap B_chunks[%d]", fn, r);
   if (B_copy) {
     if (overlaps(B_copy, chunk_bytes, A, a_bytes) || overlaps(B_copy, chunk_bytes, D, d_bytes) ||
         (G && overlaps(B_copy, chunk_bytes, G, g_bytes)))
-      return fail(RAG_EINVAL, "ag_gemm: B_copy must not overlap A, G or D");
+      return fail(RAG_EINVAL, "%s: B_copy must not overlap A, G or D", fn);
     for (int r = 0; r < tp; ++r)
       if (overlaps(B_copy, chunk_bytes, B[r], chunk_bytes))
-        return fail(RAG_EINVAL, "ag_gemm: B_copy must not overlap B_chunks[%d]", r);
+        return fail(RAG_EINVAL, "%s: B_copy must not overlap B_chunks[%d]", fn, r);
   }
   if (G && overlaps(G, g_bytes, B[self_rank], chunk_bytes) &&
       (const char*)B[self_rank] != (const char*)G + (size_t)self_rank * chunk_bytes)
-    return fail(RAG_EINVAL, "ag_gemm: the own chunk may only sit in G at its own slot");
+    return fail(RAG_EINVAL, "%s: the own chunk may only sit in G at its own slot", fn);
   if ((flags & RAG_NO_COPY) && !G && !c->gbuf)
-    return fail(RAG_EINVAL, "ag_gemm: RAG_NO_COPY reads the chunks from G; pass G");
+    return fail(RAG_EINVAL, "%s: RAG_NO_COPY reads the chunks from G; pass G", fn);
   if (c->copy_engine == RAG_COPY_SDMA && c->delay_us > 0 && !(flags & RAG_NO_COPY))
-    return fail(RAG_EINVAL, "ag_gemm: the arrival delay hook needs the kernel copy engine");
+    return fail(RAG_EINVAL, "%s: the arrival delay hook needs the kernel copy engine", fn);
 
   HIPCHK(hipSetDevice(c->device));
   hipStream_t stream = (hipStream_t)stream_v;
@@ -914,7 +960,7 @@ int ag_gemm_ex(rag_ctx* c, const void* A, int M, int K, const void* const* B, in
     const int rc = ag_launch_tile(c, nc, M, tp, fp8, out8, beside && !(flags & RAG_PER_CHUNK), &tile);
     if (rc) return rc;
   }
-  const int epoch = next_epoch(c);
+  const int epoch = next_epoch(W);
   unsigned long long* trace = nullptr;
   if (c->trace_buf) {
     int bi, bj;
@@ -927,7 +973,7 @@ int ag_gemm_ex(rag_ctx* c, const void* A, int M, int K, const void* const* B, in
   for (int j = 0; j < tp; ++j) order[j] = ((self_rank - j) % tp + tp) % tp;
 
   if (flags & RAG_PER_CHUNK) {
-    const int rc = ag_gemm_split(c, A, M, K, B, nc, tp, self_rank, Gp, own_copy, D, fp8, scale_A,
+    const int rc = ag_gemm_split(c, W, A, M, K, B, nc, tp, self_rank, Gp, own_copy, D, fp8, scale_A,
                                  scale_B, out8, scale_D, amax_D, B_copy, staged, no_copy,
                                  copy_only, chunk_bytes, order, epoch, stream);
     if (rc) return rc;
@@ -970,10 +1016,7 @@ int ag_gemm_ex(rag_ctx* c, const void* A, int M, int K, const void* const* B, in
     // a piece is two rounds of 8 16-byte vectors per thread of the copying workgroup
     cp.piece_bytes = (unsigned)(in_kernel ? tile_threads(tile) : kArrivalThreads) * 256u;
     cp.pieces = (unsigned)((cp.bytes + cp.piece_bytes - 1) / cp.piece_bytes);
-    const unsigned set = c->arr_seq & 1u;
-    cp.grab = c->arr + (size_t)set * 2 * kArrSlots * kWordStride;
-    cp.done = cp.grab + (size_t)kArrSlots * kWordStride;
-    cp.clear_next = c->arr + (size_t)(set ^ 1u) * 2 * kArrSlots * kWordStride;
+    use_count_set(W, cp);
     cp.delay_ticks = c->delay_us * c->wall_khz / 1000;
     cp.withhold_mask = c->withhold;
     cp.trace = trace;
@@ -985,19 +1028,21 @@ int ag_gemm_ex(rag_ctx* c, const void* A, int M, int K, const void* const* B, in
     if (c->copy_engine == RAG_COPY_KERNEL) {
       ArrivalArgs aa = {};
       aa.cp = cp;
-      aa.ctr = c->ctr;
+      aa.ctr = W.ctr;
       aa.epoch = epoch;
       aa.raise_priority = c->copy_priority;
       if (cp.n > 0) {
         HIPCHK(launch_arrival(c->device, aa, c->comm_wgs, c->side));
-        c->arr_seq++;
+        W.arr_seq++;
+        const int rc = note_side_copies(c);
+        if (rc) return rc;
       }
     } else {
       for (int k = 0; k < cp.n; ++k) {
         HIPCHK(hipMemcpyAsync(cp.dst[k], cp.src[k], (size_t)chunk_bytes,
                               hipMemcpyDeviceToDeviceNoCU, c->side));
         if (cp.ctr_index[k] >= 0 && (cp.pos[k] == 0 || !((c->withhold >> cp.pos[k]) & 1u)))
-          HIPCHK(hipStreamWriteValue32(c->side, c->ctr + (size_t)cp.ctr_index[k] * kWordStride,
+          HIPCHK(hipStreamWriteValue32(c->side, W.ctr + (size_t)cp.ctr_index[k] * kWordStride,
                                        (uint32_t)epoch, 0));
       }
     }
@@ -1021,10 +1066,10 @@ int ag_gemm_ex(rag_ctx* c, const void* A, int M, int K, const void* const* B, in
     a.K = K;
     a.nc = nc;
     a.tp = tp;
-    a.ctr = c->ctr;
+    a.ctr = W.ctr;
     a.join_index = (own_copy && !no_copy && !in_kernel && !B_copy) ? c->max_tp : -1;
     a.epoch = epoch;
-    a.err = c->err;
+    a.err = W.err;
     a.spin_limit = c->spin_us * c->wall_khz / 1000;
     a.scale_A = scale_A;
     a.scale_B = scale_B;
@@ -1065,16 +1110,33 @@ int ag_gemm_ex(rag_ctx* c, const void* A, int M, int K, const void* const* B, in
               c->ag_info[tile][fp8][out8].max_blocks_per_cu, c->ag_info[tile][fp8][out8].vgprs_per_wave,
               c->ag_info[tile][fp8][out8].lds_bytes, engine_name(c->copy_engine),
               c->comm_wgs, cp.pieces, cp.piece_bytes, flags, epoch);
+    if (a.copies) {
+      const int rc = join_side_copies(c, stream);
+      if (rc) return rc;
+    }
     hipEvent_t ev0, ev1;
     launch_timing_events(c, &ev0, &ev1);
     HIPCHK(launch_ag_gemm(c->device, a, tile, fp8, grid, stream, ev0, ev1));
     launch_timed(c, ev0);
-    if (a.copies) c->arr_seq++;
+    if (a.copies) W.arr_seq++;
   }
   if (!no_copy && !in_kernel && (copy_only || B_copy))
     HIPCHK(hipStreamWaitEvent(stream, c->ev_join, 0));
 
   return staged && !copy_only ? finalize_staged(c, D, nc, M, tp, order, oesz, stream) : RAG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ag_gemm_ex(rag_ctx* c, const void* A, int M, int K, const void* const* B, int nc, int tp,
+               int self_rank, void* G, void* D, rag_dtype dt, const float* scale_A,
+               const float* scale_B, rag_dtype d_dt, const float* scale_D, float* amax_D,
+               void* B_copy, int flags, void* stream_v) {
+  if (!c) return fail(RAG_EINVAL, "ag_gemm: ctx is NULL");
+  return ag_call(c, c->w, "ag_gemm", A, M, K, B, nc, tp, self_rank, G, D, dt, scale_A, scale_B,
+                 d_dt, scale_D, amax_D, B_copy, flags, stream_v);
 }
 
 int gemm_rs(rag_ctx* c, const void* X, int T, int Kl, const void* W, int Mo,
@@ -1178,17 +1240,15 @@ int linear_allreduce(rag_ctx* c, const void* X, int T, int Kl, const void* W, in
       aa.cp.bytes = (unsigned long long)cbytes;
       aa.cp.piece_bytes = (unsigned)kArrivalThreads * 256u;
       aa.cp.pieces = (unsigned)((aa.cp.bytes + aa.cp.piece_bytes - 1) / aa.cp.piece_bytes);
-      const unsigned set = c->arr_seq & 1u;
-      aa.cp.grab = c->arr + (size_t)set * 2 * kArrSlots * kWordStride;
-      aa.cp.done = aa.cp.grab + (size_t)kArrSlots * kWordStride;
-      aa.cp.clear_next = c->arr + (size_t)(set ^ 1u) * 2 * kArrSlots * kWordStride;
-      aa.ctr = c->ctr;
-      aa.epoch = c->epoch;
+      use_count_set(c->w, aa.cp);
+      aa.ctr = c->w.ctr;
+      aa.epoch = c->w.epoch;
       aa.raise_priority = c->copy_priority;
       HIPCHK(launch_arrival(c->device, aa, c->comm_wgs, c->side));
-      c->arr_seq++;
+      c->w.arr_seq++;
+      const int rc = note_side_copies(c);
+      if (rc) return rc;
     }
-    HIPCHK(hipEventRecord(c->ev_ag, c->side));
   }
   // the reduce-scatter of the own chunk, written straight into its slot of Y (with the
   // all-gather's copy kernel running beside it)
@@ -1196,7 +1256,13 @@ int linear_allreduce(rag_ctx* c, const void* X, int T, int Kl, const void* W, in
                          self_rank, send, (char*)Y + (size_t)self_rank * cbytes, flags, stream_v,
                          false, tp > 1);
   if (rc) return rc;
-  if (tp > 1) HIPCHK(hipStreamWaitEvent(stream, c->ev_ag, 0));
+  if (tp > 1) {
+    // the caller's stream joins everything the side stream ran for this call: the gather's
+    // copies, and with RAG_RS_ARRIVE the reduce-scatter's arrivals that rs_call put after them
+    HIPCHK(hipEventRecord(c->ev_ag, c->side));
+    HIPCHK(hipStreamWaitEvent(stream, c->ev_ag, 0));
+    c->side_pending = false;
+  }
   return RAG_OK;
 }
 
@@ -1225,9 +1291,9 @@ int rag_check(rag_ctx* c) {
   HIPCHK(hipSetDevice(c->device));
   HIPCHK(hipDeviceSynchronize());
   int err = 0;
-  HIPCHK(hipMemcpy(&err, c->err, sizeof(int), hipMemcpyDeviceToHost));
+  HIPCHK(hipMemcpy(&err, c->w.err, sizeof(int), hipMemcpyDeviceToHost));
   if (err != 0) {
-    HIPCHK(hipMemset(c->err, 0, sizeof(int)));
+    HIPCHK(hipMemset(c->w.err, 0, sizeof(int)));
     HIPCHK(hipDeviceSynchronize());
     return fail(RAG_ETIMEOUT, "a chunk did not arrive within the spin limit (%lld us) in the call "
                 "with epoch %d; its tiles were skipped", c->spin_us, err);

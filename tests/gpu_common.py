@@ -52,15 +52,22 @@ def bits(t: torch.Tensor) -> np.ndarray:
 
 
 class AGRun:
-    """Device copies of one AG+GEMM input set plus output buffers."""
+    """Device copies of one AG+GEMM input set plus output buffers.  own_in_g: the own chunk lives
+    in its slot of G (as the local shard does in a ring all-gather's output buffer, and as the
+    benchmark places it), so the call copies only the peers' chunks."""
 
-    def __init__(self, inp: W.AGInputs, with_G: bool = True):
+    def __init__(self, inp: W.AGInputs, with_G: bool = True, own_in_g: bool = False):
         self.inp = inp
         s = inp.shape
         self.A = inp.A.to(DEV)
         self.chunks = [c.to(DEV) for c in inp.chunks]
         self.D = torch.empty((s.N, s.M), dtype=torch.bfloat16, device=DEV)
         self.G = torch.empty((s.N, s.K), dtype=inp.A.dtype, device=DEV) if with_G else None
+        if own_in_g:
+            assert with_G
+            r0 = s.self_rank * s.nc
+            self.G[r0:r0 + s.nc].copy_(self.chunks[s.self_rank])
+            self.chunks[s.self_rank] = self.G[r0:r0 + s.nc]
         self.sA = scale_tensor(inp.scale_A) if s.dtype == "fp8" else None
         self.sB = scale_tensor(inp.scale_B) if s.dtype == "fp8" else None
 
@@ -81,6 +88,17 @@ def oracle_ag(inp: W.AGInputs):
     if inp.shape.dtype == "fp8":
         return O.ag_gemm_fp8(bits(inp.A), inp.scale_A, [bits(c) for c in inp.chunks], inp.scale_B)
     return O.ag_gemm(bits(inp.A), [bits(c) for c in inp.chunks])
+
+
+_full_cache = {}
+
+
+def cached(key, fn):
+    """fn() computed once per test session under `key` (the full oracle of a full-size workload
+    takes seconds on the host; several GPU variants are compared with the same result)."""
+    if key not in _full_cache:
+        _full_cache[key] = fn()
+    return _full_cache[key]
 
 
 def oracle_ag_rows(inp: W.AGInputs, rows):

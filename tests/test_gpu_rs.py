@@ -7,7 +7,7 @@ from oracle import ringag_oracle as O
 from ring_all_gather_amd import binding as B
 from ring_all_gather_amd import workloads as W
 
-from gpu_common import DEV, TOL_BF16, TOL_SEND, ctx, rel_err, reset_options, say
+from gpu_common import DEV, TOL_BF16, TOL_SEND, cached, ctx, rel_err, reset_options, say
 
 pytestmark = pytest.mark.gpu
 
@@ -193,29 +193,38 @@ def test_rs_special_cases_and_no_send():
     _check_send(run, send_ref, exact=True)
 
 
-def test_rs_full_size_sampled_rows():
+def _rs_8k_reference(inp):
+    """Full oracle of the one-shot GEMM+RS at rs_8k, (D fp32, send [tp, nc, Mo]), computed once
+    per session."""
+    return cached(("rs_8k", "one-shot"), lambda: oracle_rs(inp)[:2])
+
+
+def _check_full(D_dev, send_dev, D_ref, send_ref, self_rank, what):
+    err = rel_err(W.bits_u16(D_dev.cpu()), D_ref)
+    say(f"{what} D: all {D_ref.shape[0]} x {D_ref.shape[1]} outputs, max rel err {err:.3e}")
+    assert err <= TOL_BF16
+    if send_dev is None:
+        return
+    got = send_dev.cpu().numpy()
+    for c in range(got.shape[0]):
+        if c == self_rank:
+            continue
+        e = np.abs(got[c] - send_ref[c]).max() / np.abs(send_ref[c]).max()
+        assert e <= TOL_SEND, (what, c, e)
+
+
+def test_rs_full_size_full_output():
     """The measured GEMM+RS workload at full size (peer partial rows outside this rank's chunk are
-    NaN, so reading them fails); sampled rows of D and of every outgoing chunk vs the oracle."""
+    NaN, so reading them fails): every element of D and of every outgoing chunk against the full
+    oracle."""
     shape = W.WORKLOADS["rs_8k"]
     say(f"case {shape}")
     inp = W.make_rs(shape)
     run = RSRun(inp).run(ctx())
-    g = np.random.default_rng(shape.seed)
-    rows = np.unique(np.concatenate([[0, shape.nc - 1], g.choice(shape.nc, 62, replace=False)]))
-    peers = [None if p is None else p.numpy() for p in inp.partials]
-    Xb, Wb = W.bits_u16(inp.X), W.bits_u16(inp.W)
-    D_rows = O.gemm_rs_rows(Xb, Wb, peers, shape.tp, shape.self_rank, rows)
-    err = rel_err(W.bits_u16(run.D.cpu())[rows], D_rows)
-    say(f"rs_8k D: {len(rows)} sampled rows, max rel err {err:.3e}")
-    assert err <= TOL_BF16
-    send = run.send.cpu().numpy()
-    Xf, Wf = O.bf16_to_f32(Xb), O.bf16_to_f32(Wb)
-    for cix in range(shape.tp):
-        if cix == shape.self_rank:
-            continue
-        ref = O.gemm_tn_rows(Xf, Wf, cix * shape.nc + rows[:8])
-        got = send[cix][rows[:8]]
-        assert np.abs(got - ref).max() <= TOL_SEND * np.abs(ref).max()
+    ctx().check()
+    assert np.isnan(run.send[shape.self_rank].cpu().numpy()).all()
+    D_ref, send_ref = _rs_8k_reference(inp)
+    _check_full(run.D, run.send, D_ref, send_ref, shape.self_rank, "rs_8k")
 
 
 # ------------------------------------------------- arrivals (counter-gated) and the ring step
@@ -375,32 +384,25 @@ def test_rs_ring_no_send_and_delayed_arrivals(engine):
     c.check()
 
 
-def test_rs_ring_full_size_sampled_rows():
-    """The ring step at the measured GEMM+RS size with arrivals: sampled rows of D and of every
-    passed-on sum against the oracle."""
+def _rs_8k_ring_reference(inp):
+    """Full oracle of one ring-accumulate step at rs_8k, (D fp32, out [tp, nc, Mo]), computed
+    once per session."""
+    return cached(("rs_8k", "ring"), lambda: oracle_ring(inp)[:2])
+
+
+@pytest.mark.parametrize("engine", ["kernel", "in-gemm"])
+def test_rs_ring_full_size_full_output(engine):
+    """The ring step at the measured GEMM+RS size with arrivals: every element of D and of every
+    passed-on sum against the full oracle."""
     shape = W.WORKLOADS["rs_8k"]
     c = ctx()
-    _engine(c, "kernel")
-    say(f"case rs ring full {shape}")
+    _engine(c, engine)
+    say(f"case rs ring full {shape} engine={engine}")
     inp = W.make_rs_ring(shape)
     run = RSRingRun(inp).run(c, B.RAG_RS_ARRIVE)
     c.check()
-    g = np.random.default_rng(shape.seed + 1)
-    rows = np.unique(np.concatenate([[0, shape.nc - 1], g.choice(shape.nc, 30, replace=False)]))
-    Xb, Wb = W.bits_u16(inp.X), W.bits_u16(inp.W)
-    inc = [t.numpy() for t in inp.incoming]
-    D_rows = O.gemm_rs_ring_step_rows(Xb, Wb, inc, shape.tp, shape.self_rank, shape.self_rank,
-                                      rows)
-    err = rel_err(W.bits_u16(run.D.cpu())[rows], D_rows)
-    say(f"rs ring D: {len(rows)} sampled rows, max rel err {err:.3e}")
-    assert err <= TOL_BF16
-    send = run.send.cpu().numpy()
-    for cix in range(shape.tp):
-        if cix == shape.self_rank:
-            continue
-        ref = O.gemm_rs_ring_step_rows(Xb, Wb, inc, shape.tp, shape.self_rank, cix, rows[:8])
-        got = send[cix][rows[:8]]
-        assert np.abs(got - ref).max() <= TOL_SEND * np.abs(ref).max()
+    D_ref, out_ref = _rs_8k_ring_reference(inp)
+    _check_full(run.D, run.send, D_ref, out_ref, shape.self_rank, "rs ring")
 
 
 @pytest.mark.parametrize("engine", ["kernel", "in-gemm"])
@@ -409,7 +411,7 @@ def test_rs_arrive_full_size_back_to_back(ring, engine):
     """Full-size gated calls back to back (no synchronisation between them).  With the copy kernel
     beside the GEMM, the GEMM's persistent grid must leave the copies room to run, or its waiting
     tiles would spin to the limit (RAG_ETIMEOUT); with the GEMM's own workgroups copying, every
-    piece must be taken by some workgroup.  Then the last call is checked on sampled rows."""
+    piece must be taken by some workgroup.  Then the last call's D and send are checked in full."""
     shape = W.WORKLOADS["rs_8k"]
     c = ctx()
     _engine(c, engine)
@@ -429,15 +431,11 @@ def test_rs_arrive_full_size_back_to_back(ring, engine):
                       send=run.send, flags=B.RAG_RS_ARRIVE)
     torch.cuda.synchronize()
     c.check()
-    rows = np.array([0, 17, shape.nc // 2, shape.nc - 1])
-    Xb, Wb = W.bits_u16(inp.X), W.bits_u16(inp.W)
     if ring:
-        ref = O.gemm_rs_ring_step_rows(Xb, Wb, [t.numpy() for t in inp.incoming], shape.tp,
-                                       shape.self_rank, shape.self_rank, rows)
+        D_ref, send_ref = _rs_8k_ring_reference(inp)
     else:
-        ref = O.gemm_rs_rows(Xb, Wb, [None if p is None else p.numpy() for p in inp.partials],
-                             shape.tp, shape.self_rank, rows)
-    assert rel_err(W.bits_u16(run.D.cpu())[rows], ref) <= TOL_BF16
+        D_ref, send_ref = _rs_8k_reference(inp)
+    _check_full(run.D, run.send, D_ref, send_ref, shape.self_rank, f"back-to-back ring={ring}")
 
 
 # ------------------------------------------------------- row-parallel linear with all-reduce
@@ -471,3 +469,96 @@ def test_linear_allreduce_exact(tp, s, engine):
         else:
             assert np.array_equal(got[rows], W.bits_u16(red[cix]))
     _check_send(run, send_ref, exact=True)
+
+
+def _check_y(Y, D_ref, red, shape, what):
+    """Y's own chunk against the reduce-scatter's oracle, every other chunk bit for bit against
+    the owner's reduced chunk."""
+    got = W.bits_u16(Y.cpu())
+    nc, s = shape.nc, shape.self_rank
+    for cix in range(shape.tp):
+        rows = slice(cix * nc, (cix + 1) * nc)
+        if cix == s:
+            err = rel_err(got[rows], D_ref)
+            say(f"{what}: own chunk max rel err {err:.3e}")
+            assert err <= TOL_BF16
+        else:
+            assert np.array_equal(got[rows], W.bits_u16(red[cix])), (what, cix)
+
+
+@pytest.mark.parametrize("engine", ["in-gemm", "kernel"])
+def test_linear_allreduce_full_size(engine):
+    """rs_8k shape: with the GEMM's own workgroups gathering the reduced chunks, each chunk is 16
+    pieces and the launch runs several rounds, so the piece sizing, the per-tile quota and the
+    final drain all run; every non-own chunk of Y is compared bit for bit, the own chunk and send
+    with the full oracle."""
+    shape = W.WORKLOADS["rs_8k"]
+    c = ctx()
+    _engine(c, engine)
+    say(f"case linear_allreduce full {shape} engine={engine}")
+    inp = W.make_rs(shape)
+    red = W.make_reduced_chunks(shape)
+    run = RSRun(inp)
+    red_dev = [t.to(DEV) for t in red]
+    Y = torch.full((shape.T, shape.Mo), float("nan"), dtype=torch.bfloat16, device=DEV)
+    B.linear_allreduce(c, run.X, run.W, run.partials, red_dev, shape.tp, shape.self_rank, Y,
+                       send=run.send)
+    torch.cuda.synchronize()
+    c.check()
+    D_ref, send_ref = _rs_8k_reference(inp)
+    _check_y(Y, D_ref, red, shape, f"linear_allreduce {engine}")
+    _check_full(Y[shape.self_rank * shape.nc:(shape.self_rank + 1) * shape.nc], run.send, D_ref,
+                send_ref, shape.self_rank, "linear_allreduce send")
+
+
+def test_side_stream_arrivals_then_in_gemm_copies_back_to_back():
+    """linear_allreduce with RAG_RS_ARRIVE runs its copies in a kernel on the side stream; the
+    in-GEMM calls enqueued right after it on the caller's stream (no synchronisation) clear and
+    reuse the piece counts that kernel used.  Two rounds of: gated linear_allreduce at rs_8k, an
+    in-GEMM ag_gemm, an in-GEMM linear_allreduce; every output is then checked."""
+    shape = W.WORKLOADS["rs_8k"]
+    c = ctx()
+    _engine(c, "in-gemm")
+    c.set_option(B.RAG_OPT_COMM_WGS, 128)
+    inp = W.make_rs(shape)
+    red = W.make_reduced_chunks(shape)
+    run = RSRun(inp)
+    red_dev = [t.to(DEV) for t in red]
+    ag_shape = W.ag_shape(4, 2, 512, 1024, 768, dist="int3", seed=4242)
+    ag_inp = W.make_ag(ag_shape)
+    outs = []
+    say("case side-stream arrivals then in-GEMM copies, back to back")
+    for _ in range(2):
+        Y1 = torch.full((shape.T, shape.Mo), float("nan"), dtype=torch.bfloat16, device=DEV)
+        B.linear_allreduce(c, run.X, run.W, run.partials, red_dev, shape.tp, shape.self_rank, Y1,
+                           send=run.send, flags=B.RAG_RS_ARRIVE)
+        ag = AGRunNoSync(ag_inp)
+        ag.enqueue(c)
+        Y2 = torch.full((shape.T, shape.Mo), float("nan"), dtype=torch.bfloat16, device=DEV)
+        B.linear_allreduce(c, run.X, run.W, run.partials, red_dev, shape.tp, shape.self_rank, Y2,
+                           send=run.send)
+        outs.append((Y1, ag, Y2))
+    torch.cuda.synchronize()
+    c.check()
+    D_ref, _ = _rs_8k_reference(inp)
+    _, ag_ref = O.ag_gemm(W.bits_u16(ag_inp.A), [W.bits_u16(t) for t in ag_inp.chunks])
+    for i, (Y1, ag, Y2) in enumerate(outs):
+        _check_y(Y1, D_ref, red, shape, f"gated linear_allreduce #{i}")
+        assert np.array_equal(W.bits_u16(ag.D.cpu()), O.f32_to_bf16(ag_ref)), i
+        _check_y(Y2, D_ref, red, shape, f"in-GEMM linear_allreduce #{i}")
+
+
+class AGRunNoSync:
+    """An AG+GEMM call enqueued without a synchronisation after it."""
+
+    def __init__(self, inp):
+        s = inp.shape
+        self.inp = inp
+        self.A = inp.A.to(DEV)
+        self.chunks = [t.to(DEV) for t in inp.chunks]
+        self.G = torch.empty((s.N, s.K), dtype=torch.bfloat16, device=DEV)
+        self.D = torch.full((s.N, s.M), float("nan"), dtype=torch.bfloat16, device=DEV)
+
+    def enqueue(self, c):
+        s = self.inp.shape
+        B.ag_gemm(c, self.A, self.chunks, s.tp, s.self_rank, self.D, G=self.G)
