@@ -248,6 +248,32 @@ RAG_API int ag_gemm_ex(rag_ctx* ctx,
             int flags, void* stream);
 
 /*
+ * ag_gemm for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the call's ready counters, piece counts and
+ * error word live in a fixed array of the library's code object, RAG_SCRATCH_BYTES per device
+ * (set up and cleared when the first context on the device is created, kept until the process
+ * ends), instead of the context's own allocation.  The call allocates nothing.
+ *   Arguments as for ag_gemm, except: G is required (not NULL); flags may hold only RAG_NO_COPY or
+ *   RAG_COPY_ONLY (RAG_STAGED_OUT and RAG_PER_CHUNK use a buffer and events that the library
+ *   allocates on first use); tp <= RAG_MAX_TP, the most the array holds words for.
+ *   Every call on a device shares that device's array, with every context there: calls that
+ *   overlap on one device race (their counters and piece counts collide), so they must be ordered
+ *   like calls on one context.  The array keeps the last call's contents; the counters are compared
+ *   with a per-device epoch that rises with every call, and each launch clears the piece counts
+ *   the next call uses, so nothing needs clearing between calls.  A wait that times out is
+ *   reported by rag_check on any context of the device.
+ * Errors: RAG_EINVAL (as ag_gemm, plus a NULL G, a forbidden flag, tp > RAG_MAX_TP), RAG_EHIP.
+ */
+#define RAG_SCRATCH_BYTES 22016
+RAG_API int ag_gemm_noalloc(rag_ctx* ctx,
+            const void* A, int M, int K,
+            const void* const* B_chunks, int nc,
+            int tp, int self_rank,
+            void* G, void* D,
+            rag_dtype dt, const float* scale_A, const float* scale_B,
+            int flags, void* stream);
+
+/*
  * GEMM + reduce-scatter (row-parallel linear) for rank self_rank of a tp-rank ring:
  *     P     = X * W^T over all T rows            (this rank's partial of the full output, fp32)
  *     D     = sum over ranks p of P_p[rows of chunk self_rank]   (bf16 out)

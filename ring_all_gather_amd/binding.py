@@ -73,6 +73,8 @@ def lib():
     L.rag_set_option.argtypes = [vp, i, ll]
     L.ag_gemm.argtypes = [vp, vp, i, i, ctypes.POINTER(vp), i, i, i, vp, vp, i, vp, vp, i, vp]
     L.gemm_rs.argtypes = [vp, vp, i, i, vp, i, ctypes.POINTER(vp), ll, i, i, vp, vp, i, vp]
+    L.ag_gemm_noalloc.argtypes = [vp, vp, i, i, ctypes.POINTER(vp), i, i, i, vp, vp, i, vp, vp,
+                                  i, vp]
     L.ag_gemm_ex.argtypes = [vp, vp, i, i, ctypes.POINTER(vp), i, i, i, vp, vp, i, vp, vp, i,
                              vp, vp, vp, i, vp]
     L.gemm_rs_ring.argtypes = [vp, vp, i, i, vp, i, ctypes.POINTER(vp), ll, i, i, vp, vp, i, vp]
@@ -244,6 +246,23 @@ def ag_gemm(ctx: Context, A: torch.Tensor, B_chunks: Sequence[torch.Tensor], tp:
                                    dt, _ptr(scale_A), _ptr(scale_B),
                                    RAG_FP8_E4M3 if out8 else RAG_BF16, _ptr(scale_D),
                                    _ptr(amax_D), _ptr(B_copy), flags, _stream(stream)))
+
+
+def ag_gemm_noalloc(ctx: Context, A: torch.Tensor, B_chunks: Sequence[torch.Tensor], tp: int,
+                    self_rank: int, D: torch.Tensor, G: torch.Tensor,
+                    scale_A: Optional[torch.Tensor] = None,
+                    scale_B: Optional[torch.Tensor] = None, flags: int = 0, stream=None) -> int:
+    """ag_gemm with the call's device words in the library's fixed scratch array (ringag.h):
+    G is required; D is bfloat16."""
+    if len(B_chunks) != tp:
+        raise ValueError(f"need tp={tp} chunks, got {len(B_chunks)}")
+    fp8 = A.dtype == torch.float8_e4m3fn
+    M, K = A.shape
+    nc = B_chunks[0].shape[0]
+    ptrs = (ctypes.c_void_p * tp)(*[_ptr(b) for b in B_chunks])
+    return _check(lib().ag_gemm_noalloc(ctx.h, _ptr(A), M, K, ptrs, nc, tp, self_rank, _ptr(G),
+                                        _ptr(D), RAG_FP8_E4M3 if fp8 else RAG_BF16,
+                                        _ptr(scale_A), _ptr(scale_B), flags, _stream(stream)))
 
 
 def _rs(fn, ctx: Context, X: torch.Tensor, W: torch.Tensor, entries, rows: int, skip: int,

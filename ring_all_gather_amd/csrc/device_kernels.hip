@@ -12,6 +12,14 @@
 
 using namespace ringag;
 
+// Fixed device scratch of ag_gemm_noalloc, for callers that cannot allocate device memory: the
+// ready counters, piece counts and error word that a context otherwise allocates.  Every kernel
+// takes its words through a pointer argument; the host looks up this array's device address in
+// the module it loaded on each device (hipModuleGetGlobal, once per device) and passes that.
+// It is defined with external linkage, at global scope (so its symbol is the plain name), for
+// the lookup to find it by name: a file-local array would be a local symbol of the code object.
+__device__ __align__(256) int scratch[kScratchWords];
+
 // Waves per SIMD the GEMM+RS kernels are compiled for (the register budget): two where two waves
 // fit beside each other anyway (8-wave tiles; 128x128, whose LDS allows two workgroups per CU).
 // Without the hint the compiler spreads the epilogue's loop-carried sums over fresh registers and

@@ -31,6 +31,12 @@ constexpr int kWordStride = 64;
 // launch zeroes the other set (clear_next, 2 * kArrSlots counts) for the next call.
 constexpr int kArrSlots = kMaxTp + 1;   // copies per call at most (tp - 1 peers + the own chunk)
 
+// Ints in one set of a call's device words for rings of up to kMaxTp ranks, kWordStride ints
+// apart: ready counters [kMaxTp] | copy-complete counter | piece counts [2 sets][grab, done]
+// [kArrSlots] | error word.  A context allocates this layout for its max_tp; the library's fixed
+// scratch array (device_kernels.hip) holds it for kMaxTp (22 KiB).
+constexpr int kScratchWords = (kMaxTp + 1 + 4 * kArrSlots + 1) * kWordStride;
+
 struct CopyPlan {
   const void* src[kArrSlots];
   void* dst[kArrSlots];
@@ -144,6 +150,9 @@ struct KernelInfo {
 // hipError_t of the launch; given ev_start / ev_stop, the launch itself records them around the
 // kernel.
 hipError_t load_kernels(int device);
+// The device address of the fixed scratch array in the code object loaded on `device` (looked up
+// once, when load_kernels loads the module there, and cleared then); null before that.
+int* device_scratch(int device);
 hipError_t launch_ag_gemm(int device, const AgArgs& a, int tile, bool fp8, int grid,
                           hipStream_t stream, hipEvent_t ev_start = nullptr,
                           hipEvent_t ev_stop = nullptr);

@@ -49,6 +49,7 @@ struct DeviceKernels {
   hipFunction_t ag[2][2][kTiles] = {};
   hipFunction_t rs[kTiles] = {};
   hipFunction_t arrival = nullptr;
+  int* scratch = nullptr;   // device address of the module's scratch array
 };
 
 DeviceKernels g_dev[kMaxDevices];
@@ -109,9 +110,24 @@ hipError_t load_kernels(int device) {
   for (int t = 1; t < kTiles; ++t)
     if ((e = hipModuleGetFunction(&d.rs[t], m, kRsName[t])) != hipSuccess) return e;
   if ((e = hipModuleGetFunction(&d.arrival, m, "rag_arrival")) != hipSuccess) return e;
+  // the fixed scratch array: its address on this device (each device's copy of the module has
+  // its own), checked for the size the host expects, and cleared once
+  hipDeviceptr_t sp = nullptr;
+  size_t sbytes = 0;
+  if ((e = hipModuleGetGlobal(&sp, &sbytes, m, "scratch")) != hipSuccess) return e;
+  if (sp == nullptr || sbytes != sizeof(int) * (size_t)kScratchWords) return hipErrorInvalidSymbol;
+  if ((e = hipMemset(sp, 0, sbytes)) != hipSuccess) return e;
+  if ((e = hipDeviceSynchronize()) != hipSuccess) return e;
+  d.scratch = reinterpret_cast<int*>(sp);
   d.module = m;
   d.loaded = true;
   return hipSuccess;
+}
+
+int* device_scratch(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_mu);
+  return g_dev[device].loaded ? g_dev[device].scratch : nullptr;
 }
 
 hipError_t launch_ag_gemm(int device, const AgArgs& a, int tile, bool fp8, int grid,

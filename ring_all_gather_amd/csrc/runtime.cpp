@@ -17,6 +17,7 @@
 
 #include <algorithm>
 #include <cstdarg>
+#include <mutex>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -61,7 +62,7 @@ bool debug_enabled() {
 }  // namespace
 
 // One set of the device words a call uses, with the host-side state that goes with them: a
-// context's own allocation (other sets can be added without touching the calls).
+// context's own allocation, or (ag_gemm_noalloc) the library's fixed scratch array of a device.
 // Layout, kWordStride ints apart: ctr[kMaxTp] (ready counters; a context allocates max_tp) |
 // copy-complete counter | piece counts [2 sets][grab, done][kArrSlots] | error word.
 struct Words {
@@ -174,6 +175,30 @@ int join_side_copies(rag_ctx* c, hipStream_t stream) {
   if (!c->side_pending) return RAG_OK;
   HIPCHK(hipStreamWaitEvent(stream, c->ev_side, 0));
   c->side_pending = false;
+  return RAG_OK;
+}
+
+// The fixed scratch array's words of each device (ag_gemm_noalloc), set up by the first
+// rag_create on that device.  Shared by every context on the device.
+constexpr int kMaxScratchDevices = 64;
+static_assert(sizeof(int) * kScratchWords == RAG_SCRATCH_BYTES, "the header states the size");
+Words g_scratch_words[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+int setup_scratch_words(int device) {
+  if (device >= kMaxScratchDevices)
+    return fail(RAG_EINVAL, "rag_create: device %d is beyond the %d devices the fixed scratch "
+                "covers", device, kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  Words& W = g_scratch_words[device];
+  if (W.ctr) return RAG_OK;
+  int* base = device_scratch(device);
+  if (!base)
+    return fail(RAG_EHIP, "rag_create: the fixed scratch array of device %d was not found in "
+                "the loaded kernels", device);
+  W.ctr = base;
+  W.arr = reinterpret_cast<unsigned*>(base + (size_t)(kMaxTp + 1) * kWordStride);
+  W.err = base + (size_t)(kMaxTp + 1 + 4 * kArrSlots) * kWordStride;
   return RAG_OK;
 }
 
@@ -741,6 +766,13 @@ int rag_create(rag_ctx** out, int device, int max_tp, int flags) {
   c->w.ctr = c->words;
   c->w.arr = reinterpret_cast<unsigned*>(c->words + (size_t)(max_tp + 1) * kWordStride);
   c->w.err = c->words + (size_t)(max_tp + 1 + 4 * kArrSlots) * kWordStride;
+  {
+    const int rc = setup_scratch_words(device);
+    if (rc) {
+      rag_destroy(c);
+      return rc;
+    }
+  }
   *out = c;
   if (debug_enabled())
     fprintf(stderr, "[ringag] context on device %d (%s, %d CUs, wall clock %lld kHz), max_tp %d\n",
@@ -847,7 +879,7 @@ int ag_gemm(rag_ctx* c, const void* A, int M, int K, const void* const* B, int n
 
 namespace {
 
-// ag_gemm_ex on the device words W.
+// ag_gemm_ex on the device words W (the context's own, or a device's fixed scratch).
 int ag_call(rag_ctx* c, Words& W, const char* fn, const void* A, int M, int K,
             const void* const* B, int nc, int tp, int self_rank, void* G, void* D, rag_dtype dt, const float* scale_A,
             const float* scale_B, rag_dtype d_dt, const float* scale_D, float* amax_D,
@@ -1139,6 +1171,28 @@ int ag_gemm_ex(rag_ctx* c, const void* A, int M, int K, const void* const* B, in
                  d_dt, scale_D, amax_D, B_copy, flags, stream_v);
 }
 
+int ag_gemm_noalloc(rag_ctx* c, const void* A, int M, int K, const void* const* B, int nc,
+                    int tp, int self_rank, void* G, void* D, rag_dtype dt, const float* scale_A,
+                    const float* scale_B, int flags, void* stream_v) {
+  if (!c) return fail(RAG_EINVAL, "ag_gemm_noalloc: ctx is NULL");
+  if (tp > kMaxTp)
+    return fail(RAG_EINVAL, "ag_gemm_noalloc: tp=%d exceeds the %d ranks the fixed scratch array "
+                "holds words for (%d bytes per device)", tp, kMaxTp,
+                (int)(sizeof(int) * kScratchWords));
+  if (!G)
+    return fail(RAG_EINVAL, "ag_gemm_noalloc: G must be given (without it the library would "
+                "allocate its own gather buffer)");
+  if (flags & (RAG_STAGED_OUT | RAG_PER_CHUNK))
+    return fail(RAG_EINVAL, "ag_gemm_noalloc: RAG_STAGED_OUT and RAG_PER_CHUNK are not available "
+                "(they use a staging buffer and events the library allocates on first use)");
+  Words& W = g_scratch_words[c->device];
+  if (!W.ctr)
+    return fail(RAG_EINVAL, "ag_gemm_noalloc: the fixed scratch of device %d is not set up",
+                c->device);
+  return ag_call(c, W, "ag_gemm_noalloc", A, M, K, B, nc, tp, self_rank, G, D, dt, scale_A,
+                 scale_B, RAG_BF16, nullptr, nullptr, nullptr, flags, stream_v);
+}
+
 int gemm_rs(rag_ctx* c, const void* X, int T, int Kl, const void* W, int Mo,
             const float* const* partials, long long ldp, int tp, int self_rank, float* send,
             void* D, int flags, void* stream_v) {
@@ -1290,10 +1344,15 @@ int rag_check(rag_ctx* c) {
   if (!c) return fail(RAG_EINVAL, "rag_check: ctx is NULL");
   HIPCHK(hipSetDevice(c->device));
   HIPCHK(hipDeviceSynchronize());
-  int err = 0;
+  // the context's error word, and that of the device's fixed scratch (ag_gemm_noalloc)
+  int err = 0, err_s = 0;
   HIPCHK(hipMemcpy(&err, c->w.err, sizeof(int), hipMemcpyDeviceToHost));
+  int* serr = g_scratch_words[c->device].err;
+  if (serr) HIPCHK(hipMemcpy(&err_s, serr, sizeof(int), hipMemcpyDeviceToHost));
+  if (err == 0) err = err_s;
   if (err != 0) {
     HIPCHK(hipMemset(c->w.err, 0, sizeof(int)));
+    if (serr) HIPCHK(hipMemset(serr, 0, sizeof(int)));
     HIPCHK(hipDeviceSynchronize());
     return fail(RAG_ETIMEOUT, "a chunk did not arrive within the spin limit (%lld us) in the call "
                 "with epoch %d; its tiles were skipped", c->spin_us, err);
