@@ -49,7 +49,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=1000)
     p.add_argument("--workload", default="ag_4k")
     p.add_argument("--copy-engine", default=os.environ.get("RAG_COPY_ENGINE", "in-gemm"),
-                   choices=["kernel", "sdma", "in-gemm"])
+                   choices=["kernel", "sdma", "in-gemm", "assist"])
+    p.add_argument("--comm-cus", type=int, default=0,
+                   help="compute units the side stream's copy kernels are limited to (0 = all)")
+    p.add_argument("--sdma-streams", type=int, default=1,
+                   help="side streams the SDMA engine spreads its copies over (1-3)")
     p.add_argument("--own-chunk", default="in-g", choices=["in-g", "separate"],
                    help="in-g: the own chunk lives in its slot of G, as the local shard does in a "
                         "ring all-gather; separate: it is its own buffer and is copied into G")
@@ -74,12 +78,26 @@ def parse():
     return p.parse_args()
 
 
-def time_steps(fn, steps, warmup, stream):
+_CHECK = None   # the context's check (raises if a counter wait timed out), set in main()
+
+
+def progress(msg: str):
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
+def time_steps(fn, steps, warmup, stream, label="step"):
     """Average ms per step over `steps` back-to-back steps after `warmup` untimed ones, bracketed
     by one event pair (and a synchronisation on both sides): nothing else is enqueued between the
-    steps."""
+    steps.  The first warm-up step is checked on its own, so that a call whose waits time out
+    fails the benchmark at once instead of after every step has waited out its limit."""
     import torch
-    for _ in range(warmup):
+    w0 = time.perf_counter()
+    if warmup > 0:
+        fn()
+        torch.cuda.synchronize()
+        if _CHECK is not None:
+            _CHECK()
+    for _ in range(warmup - 1):
         fn()
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
@@ -89,7 +107,9 @@ def time_steps(fn, steps, warmup, stream):
         fn()
     t1.record(stream)
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps
+    ms = t0.elapsed_time(t1) / steps
+    progress(f"{label}: {ms:.5f} ms per step ({time.perf_counter() - w0:.1f} s)")
+    return ms
 
 
 def per_step_times(fn, steps, stream):
@@ -254,18 +274,21 @@ def overlap_per_engine(ctx, B, step, args, stream, shape, ms_head):
     side-stream kernel engine may pick another kernel of the same tile size, see the library's
     tile choice), so the three times are of the same kernel."""
     names = [args.copy_engine] + ([] if args.headline_only else
-                                  [e for e in ("in-gemm", "kernel", "sdma") if e != args.copy_engine])
+                                  [e for e in ("in-gemm", "assist", "kernel", "sdma")
+                                   if e != args.copy_engine])
     res = {}
     for eng in names:
         ctx.set_option(B.RAG_OPT_COPY_ENGINE, B.ENGINES[eng])
         kname = ctx.ag_kernel_name(shape.nc, shape.M, shape.tp, shape.dtype == "fp8")
         t_chunked = ms_head if eng == args.copy_engine else \
-            time_steps(step, args.steps, args.warmup, stream)
-        t_copy = time_steps(lambda: step(B.RAG_COPY_ONLY), args.steps, args.warmup, stream)
+            time_steps(step, args.steps, args.warmup, stream, f"{eng} chunked")
+        t_copy = time_steps(lambda: step(B.RAG_COPY_ONLY), args.steps, args.warmup, stream,
+                            f"{eng} copies only")
         tile = kname.split("_t", 1)[1]
         if args.tile == "auto":
             ctx.set_option(B.RAG_OPT_TILE, B.TILES[tile])
-        t_gemm = time_steps(lambda: step(B.RAG_NO_COPY), args.steps, args.warmup, stream)
+        t_gemm = time_steps(lambda: step(B.RAG_NO_COPY), args.steps, args.warmup, stream,
+                            f"{eng} GEMM only")
         ctx.set_option(B.RAG_OPT_TILE, B.TILES[args.tile])
         ctx.check()
         res[eng] = {"kernel": kname, "t_chunked_ms": round(t_chunked, 5),
@@ -300,10 +323,17 @@ def main():
     from ring_all_gather_amd import workloads as W
 
     dev = "cuda:0"
+    # every call goes on a stream of the bench's own: a side stream limited to some compute units
+    # is blocking with respect to the null stream, which would serialise its copies with the GEMM
+    torch.cuda.set_stream(torch.cuda.Stream())
     ctx = B.Context(0, max_tp=16)
+    global _CHECK
+    _CHECK = ctx.check
     ctx.set_option(B.RAG_OPT_COPY_ENGINE, B.ENGINES[args.copy_engine])
     ctx.set_option(B.RAG_OPT_COMM_WGS, args.comm_wgs)
     ctx.set_option(B.RAG_OPT_TILE, B.TILES[args.tile])
+    ctx.set_option(B.RAG_OPT_COMM_CUS, args.comm_cus)
+    ctx.set_option(B.RAG_OPT_SDMA_STREAMS, args.sdma_streams)
     shape = W.WORKLOADS[args.workload]
     stream = torch.cuda.current_stream()
     out = {}
@@ -327,7 +357,7 @@ def main():
             B.ag_gemm(ctx, A, chunks, shape.tp, shape.self_rank, D, G=G, scale_A=sA, scale_B=sB,
                       flags=flags)
 
-        ms = time_steps(step, args.steps, args.warmup, stream)
+        ms = time_steps(step, args.steps, args.warmup, stream, "chunked (headline)")
         D_timed = D.clone()   # the output of the last timed step, checked against the oracle
         # instrumented pass right after it: per-step events, and the library's events around each
         # GEMM launch on the stream it runs on (the roofline's kernel duration)
@@ -345,13 +375,14 @@ def main():
         if not args.headline_only:
             ctx.set_option(B.RAG_OPT_COPY_ENGINE, B.ENGINES[args.copy_engine])
             ms_staged = time_steps(lambda: step(B.RAG_STAGED_OUT), args.steps, args.warmup,
-                                   stream)
+                                   stream, "staged output")
             # the split form (one GEMM launch per chunk, gated by stream events): what the
             # in-kernel counters buy
-            ms_split = time_steps(lambda: step(B.RAG_PER_CHUNK), args.steps, args.warmup, stream)
+            ms_split = time_steps(lambda: step(B.RAG_PER_CHUNK), args.steps, args.warmup, stream,
+                                  "split form")
             # the same work without overlap: the copies-only launch, then the GEMM-only launch
             ms_seq = time_steps(lambda: (step(B.RAG_COPY_ONLY), step(B.RAG_NO_COPY)), args.steps,
-                                args.warmup, stream)
+                                args.warmup, stream, "copies then GEMM")
         ctx.check()
         ctx.set_option(B.RAG_OPT_COPY_ENGINE, B.ENGINES[args.copy_engine])
         flops = shape.flops
@@ -371,8 +402,8 @@ def main():
                                    f"{shape.dtype}",
                        "tp": shape.tp, "self_rank": shape.self_rank, "N": shape.N, "M": shape.M,
                        "K": shape.K, "copy_engine": args.copy_engine, "own_chunk": args.own_chunk,
-                       "comm_wgs": args.comm_wgs,
-                       "tile": args.tile},
+                       "comm_wgs": args.comm_wgs, "comm_cus": args.comm_cus,
+                       "sdma_streams": args.sdma_streams, "tile": args.tile},
             "pct_mfma_peak": round(100.0 * value / peak, 2),
             "step_ms": {"p10": round(pctl(per, 0.1), 5), "p50": round(pctl(per, 0.5), 5),
                         "p90": round(pctl(per, 0.9), 5)},
@@ -409,7 +440,7 @@ def main():
         def step():
             B.gemm_rs(ctx, X, Wt, parts, shape.tp, shape.self_rank, D, send=send)
 
-        ms = time_steps(step, args.steps, args.warmup, stream)
+        ms = time_steps(step, args.steps, args.warmup, stream, "gemm_rs (headline)")
         D_timed, send_timed = D.clone(), send.clone()   # checked against the oracle below
         ctx.kernel_times()
         ctx.set_option(B.RAG_OPT_TIMING, 1)
@@ -468,23 +499,26 @@ def main():
             # running sums given or arriving
             ms_arrive = time_steps(
                 lambda: B.gemm_rs(ctx, X, Wt, parts, shape.tp, shape.self_rank, D, send=send,
-                                  flags=B.RAG_RS_ARRIVE), args.steps, args.warmup, stream)
+                                  flags=B.RAG_RS_ARRIVE), args.steps, args.warmup, stream,
+                "gemm_rs, partials arrive")
             rin = W.make_rs_ring(shape)
             inc = [t.to(dev) for t in rin.incoming]
             Xr, Wr = rin.X.to(dev), rin.W.to(dev)
             ms_ring = time_steps(
                 lambda: B.gemm_rs_ring(ctx, Xr, Wr, inc, shape.tp, shape.self_rank, D, send=send),
-                args.steps, args.warmup, stream)
+                args.steps, args.warmup, stream, "ring step, sums given")
             ms_ring_arrive = time_steps(
                 lambda: B.gemm_rs_ring(ctx, Xr, Wr, inc, shape.tp, shape.self_rank, D, send=send,
-                                       flags=B.RAG_RS_ARRIVE), args.steps, args.warmup, stream)
+                                       flags=B.RAG_RS_ARRIVE), args.steps, args.warmup, stream,
+                "ring step, sums arrive")
             # the row-parallel linear with its output all-reduced: the reduce-scatter above plus
             # an all-gather of the owners' reduced chunks into Y, copied beside the GEMM
             red = [t.to(dev) for t in W.make_reduced_chunks(shape)]
             Y = torch.empty((shape.T, shape.Mo), dtype=torch.bfloat16, device=dev)
             ms_lar = time_steps(
                 lambda: B.linear_allreduce(ctx, X, Wt, parts, red, shape.tp, shape.self_rank, Y,
-                                           send=send), args.steps, args.warmup, stream)
+                                           send=send), args.steps, args.warmup, stream,
+                "linear_allreduce")
             ctx.check()
             # the gathered chunks of Y after the timed steps: bit for bit the owners' reduced chunks
             nc_ = shape.nc

@@ -116,11 +116,19 @@ enum {
                               that leaves none gives way to one of the same tile size that does,
                               else 8 compute units are left out of the GEMM's grid */
     RAG_COPY_SDMA = 1,     /* SDMA engines on the side stream (hipMemcpyDeviceToDeviceNoCU, then
-                              hipStreamWriteValue32 of the counter) */
-    RAG_COPY_IN_GEMM = 2   /* the GEMM launch itself: workgroups whose chunk is not there yet copy
+                              hipStreamWriteValue32 of the counter; RAG_OPT_SDMA_STREAMS spreads
+                              the copies over up to three streams).  The runtime runs the
+                              write-value as a small kernel on the compute units, so a GEMM whose
+                              tiles wait for it leaves it room as for the copy kernel */
+    RAG_COPY_IN_GEMM = 2,  /* the GEMM launch itself: workgroups whose chunk is not there yet copy
                               pieces of the peers' chunks (ring order) until it is released, and
                               help with the rest once out of tiles; no side stream is used (see
                               RAG_RS_ARRIVE for the GEMM+RS form) */
+    RAG_COPY_IN_GEMM_ASSIST = 3 /* AG+GEMM: as RAG_COPY_IN_GEMM, and a copy kernel on the side
+                              stream takes pieces from the same queue beside the GEMM
+                              (RAG_OPT_COMM_WGS workgroups): the chunks that only later rounds of
+                              the GEMM need are copied while the first round computes, instead of
+                              at the round boundary.  GEMM+RS calls treat it as RAG_COPY_IN_GEMM */
 };
 
 /* Option keys for rag_set_option. */
@@ -155,10 +163,21 @@ enum {
                                    ring's chunks in more rounds) */
     RAG_OPT_COPY_PRIORITY = 11, /* 1 (default) = copy-kernel waves issue at the highest wave
                                    priority, 0 = normal */
-    RAG_OPT_GEMM_COPY_WGS = 12  /* RAG_COPY_IN_GEMM, AG+GEMM calls: how many of the GEMM's
+    RAG_OPT_GEMM_COPY_WGS = 12, /* RAG_COPY_IN_GEMM, AG+GEMM calls: how many of the GEMM's
                                    workgroups take part in the copies, spread evenly over the XCDs
                                    (0 = all, the default; GEMM+RS always uses all);
                                    fewer copy more slowly but draw less power at once */
+    RAG_OPT_COMM_CUS = 13,      /* compute units given to communication: 0 (default) = the side
+                                   stream's copy kernels may run anywhere; n (a multiple of 8,
+                                   8 <= n <= CUs - 8) = the side stream is recreated with a
+                                   compute-unit mask of n/8 units on every XCD, so copy kernels run
+                                   only there (TransformerEngine issue #1583, C++ listing: the
+                                   communication kernel gets its own number of SMs).  The GEMM's
+                                   workgroups may share those units.  Such a stream is blocking with
+                                   respect to the null stream: call from another stream, or the
+                                   null stream serialises the copies with the GEMM */
+    RAG_OPT_SDMA_STREAMS = 14   /* RAG_COPY_SDMA: side streams the chunk copies are spread over
+                                   (1..3, default 1), so that more than one copy engine works */
 };
 
 /* Tile configurations (rows of D x columns of D per workgroup; 4 waves unless stated). */

@@ -31,9 +31,10 @@ RAG_STAGED_OUT, RAG_NO_COPY, RAG_COPY_ONLY, RAG_PER_CHUNK, RAG_RS_ARRIVE = 1, 2,
 RAG_OPT_COPY_ENGINE, RAG_OPT_COMM_WGS, RAG_OPT_SPIN_LIMIT_US = 1, 2, 3
 RAG_OPT_ARRIVAL_DELAY_US, RAG_OPT_WITHHOLD_MASK, RAG_OPT_TIMING, RAG_OPT_TILE = 4, 5, 6, 7
 RAG_OPT_TRACE_BUF, RAG_OPT_TRACE_BYTES, RAG_OPT_WGS_PER_CU, RAG_OPT_COPY_PRIORITY = 8, 9, 10, 11
-RAG_OPT_GEMM_COPY_WGS = 12
-RAG_COPY_KERNEL, RAG_COPY_SDMA, RAG_COPY_IN_GEMM = 0, 1, 2
-ENGINES = {"kernel": RAG_COPY_KERNEL, "sdma": RAG_COPY_SDMA, "in-gemm": RAG_COPY_IN_GEMM}
+RAG_OPT_GEMM_COPY_WGS, RAG_OPT_COMM_CUS, RAG_OPT_SDMA_STREAMS = 12, 13, 14
+RAG_COPY_KERNEL, RAG_COPY_SDMA, RAG_COPY_IN_GEMM, RAG_COPY_IN_GEMM_ASSIST = 0, 1, 2, 3
+ENGINES = {"kernel": RAG_COPY_KERNEL, "sdma": RAG_COPY_SDMA, "in-gemm": RAG_COPY_IN_GEMM,
+           "assist": RAG_COPY_IN_GEMM_ASSIST}
 TRACE_HEADER, TRACE_START, TRACE_TILE_WORDS = 64, 32, 5
 TILES = {"auto": 0, "128x128": 1, "256x128": 2, "256x256": 3, "256x256w8": 4, "256x256w8s4": 5,
          "256x192w8": 6}
@@ -87,7 +88,7 @@ def lib():
     L.rag_last_error.restype = ctypes.c_char_p
     L.rag_version.restype = i
     for f in ("rag_create", "rag_destroy", "rag_set_option", "ag_gemm", "ag_gemm_ex", "gemm_rs",
-              "gemm_rs_ring",
+              "gemm_rs_ring", "ag_gemm_noalloc",
               "linear_allreduce",
               "rag_check",
               "rag_kernel_times", "rag_ag_kernel_name", "rag_rs_kernel_name"):

@@ -24,7 +24,10 @@ __device__ __forceinline__ void arrival_body(const ArrivalArgs& a) {
   // GEMM waits for are not starved by the waves that will consume them.
   if (a.raise_priority) __builtin_amdgcn_s_setprio(3);
   copy_queue_begin(a.cp);
-  run_copy_queue<kArrivalThreads, kArrivalInFlight, false>(a.cp, a.ctr, a.epoch, 0, -1,
+  if (!a.late_only)
+    run_copy_queue<kArrivalThreads, kArrivalInFlight, false>(a.cp, a.ctr, a.epoch, 0, -1,
+                                                             &s_piece);
+  run_copy_queue<kArrivalThreads, kArrivalInFlight, false>(a.cp, a.ctr, a.epoch, 2, -1,
                                                            &s_piece);
   run_copy_queue<kArrivalThreads, kArrivalInFlight, false>(a.cp, a.ctr, a.epoch, 1, -1,
                                                            &s_piece);

@@ -150,7 +150,8 @@ __device__ inline void copy_queue_begin(const CopyPlan& p) {
   if (p.trace && threadIdx.x == 0) p.trace[kTraceStart] = wall_clock64();
 }
 
-// Take pieces of queue q (0 = the peers' chunks, 1 = the own chunk) and copy them until the queue
+// Take pieces of queue q (0 = the early peers' chunks, 2 = the late ones, 1 = the own chunk's
+// copies) and copy them until the queue
 // is empty, until max_pieces are copied or, with stop >= 0, until ctr[stop] == epoch (checked
 // before each take).  Called by every thread of the workgroup; s_word is a workgroup-shared word.
 //
@@ -163,8 +164,10 @@ __device__ inline void copy_queue_begin(const CopyPlan& p) {
 template <int NT, int U = 8, bool PIPE = true>
 __device__ inline void run_copy_queue(const CopyPlan& p, int* ctr, int epoch, int q, int stop,
                                       unsigned* s_word, unsigned max_pieces = ~0u) {
-  const unsigned first = q == 0 ? 0u : (unsigned)p.n_peer;
-  const unsigned total = (q == 0 ? (unsigned)p.n_peer : (unsigned)(p.n - p.n_peer)) * p.pieces;
+  const unsigned early = (unsigned)(p.n_peer - p.late);
+  const unsigned first = q == 0 ? 0u : q == 1 ? (unsigned)p.n_peer : early;
+  const unsigned total =
+      (q == 0 ? early : q == 1 ? (unsigned)(p.n - p.n_peer) : (unsigned)p.late) * p.pieces;
   if (total == 0) return;
   unsigned prev = ~0u;   // copy of the piece finished in the previous iteration, if any
   unsigned taken = 0;    // pieces copied (uniform)

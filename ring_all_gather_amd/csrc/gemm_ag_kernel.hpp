@@ -59,7 +59,10 @@ __device__ __forceinline__ void ag_gemm_body(const AgArgs& a) {
     unsigned long long* tr = a.trace ? a.trace + kTraceTileWords * (size_t)t : nullptr;
     if (tr && threadIdx.x == 0) tr[0] = wall_clock64();
     if (a.ctr_index[j] >= 0) {
-      if (copier) run_copy_queue<S::NT>(a.cp, a.ctr, a.epoch, 0, a.ctr_index[j], &s_piece);
+      if (copier) {
+        run_copy_queue<S::NT>(a.cp, a.ctr, a.epoch, 0, a.ctr_index[j], &s_piece);
+        run_copy_queue<S::NT>(a.cp, a.ctr, a.epoch, 2, a.ctr_index[j], &s_piece);
+      }
       if (threadIdx.x == 0)
         s_ok = wait_ready(a.ctr + a.ctr_index[j] * kWordStride, a.epoch, a.err, a.spin_limit);
       __syncthreads();
@@ -104,6 +107,7 @@ __device__ __forceinline__ void ag_gemm_body(const AgArgs& a) {
   }
   if (copier) {
     run_copy_queue<S::NT>(a.cp, a.ctr, a.epoch, 0, -1, &s_piece);
+    run_copy_queue<S::NT>(a.cp, a.ctr, a.epoch, 2, -1, &s_piece);
     run_copy_queue<S::NT>(a.cp, a.ctr, a.epoch, 1, -1, &s_piece);
   }
   // With the copies on another stream, which the caller's stream does not wait for, the kernel

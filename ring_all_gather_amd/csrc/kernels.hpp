@@ -25,9 +25,11 @@ constexpr int kWordStride = 64;
 // stream, or the GEMM's own workgroups while their chunk is not there yet).  Copies
 // 0..n_peer-1 are the peers' chunks in ring order; each releases ctr[ctr_index[c]] = epoch once
 // all its pieces are copied.  Copy n_peer, when n > n_peer, is the own chunk into its slot of G
-// (ctr_index -1 unless something waits for it).  Two grab counts hand out the pieces in order:
-// grab[0] over the peers' pieces, grab[kWordStride] over the own chunk's; done[c * kWordStride]
-// counts the copied pieces of copy c.  The counts come in two sets used by alternate calls; a
+// (ctr_index -1 unless something waits for it).  Grab counts hand out the pieces of three queues
+// in order: queue 0 (grab[0]) = the first n_peer - late peers, queue 2 (grab[2 kWordStride]) = the
+// last `late` peers (chunks that only later rounds of the GEMM need, which a copy kernel beside it
+// takes in the background), queue 1 (grab[kWordStride]) = the own chunk's copies;
+// done[c * kWordStride] counts the copied pieces of copy c.  The counts come in two sets used by alternate calls; a
 // launch zeroes the other set (clear_next, 2 * kArrSlots counts) for the next call.
 constexpr int kArrSlots = kMaxTp + 1;   // copies per call at most (tp - 1 peers + the own chunk)
 
@@ -43,6 +45,7 @@ struct CopyPlan {
   int ctr_index[kArrSlots];      // counter released when copy c is complete, or -1
   int pos[kArrSlots];            // ring position of copy c (withhold hook); 0 = the own chunk
   int n_peer, n;
+  int late;                      // the last `late` of the n_peer peer copies form queue 2
   unsigned long long bytes;      // bytes per copy, multiple of 16
   unsigned pieces;               // pieces per copy: ceil(bytes / piece_bytes)
   unsigned piece_bytes;          // multiple of 16
@@ -119,6 +122,8 @@ struct ArrivalArgs {
   int* ctr;
   int epoch;
   int raise_priority;            // 1 = run the copy waves at the highest issue priority
+  int late_only;                 // 1 = only queues 2 and 1 (beside a GEMM whose own workgroups
+                                 // copy queue 0)
 };
 
 // Trace layout (64-bit words, wall clock at 100 MHz): words [0, kTraceHeader) belong to the

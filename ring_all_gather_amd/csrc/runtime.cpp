@@ -83,6 +83,11 @@ struct rag_ctx {
   // copies on a caller's stream waits for it first (see join_side_copies)
   hipEvent_t ev_side = nullptr;
   bool side_pending = false;
+  // SDMA copies may spread over the side stream and up to two more (RAG_OPT_SDMA_STREAMS)
+  hipStream_t sdma[2] = {nullptr, nullptr};
+  hipEvent_t ev_sdma[2] = {nullptr, nullptr};
+  int sdma_streams = 1;
+  int comm_cus = 0;      // > 0: the side stream runs only on these compute units (RAG_OPT_COMM_CUS)
   std::vector<hipEvent_t> ev_chunk;   // split form: chunk j copied (created on first use)
   int* words = nullptr;   // the context's device words (hipMalloc at creation), see Words
   Words w;
@@ -238,21 +243,41 @@ int choose_ag_tile(const rag_ctx* c, int nc, int M, int tp) {
 }
 
 const char* engine_name(int e) {
-  return e == RAG_COPY_SDMA ? "sdma" : e == RAG_COPY_IN_GEMM ? "in-gemm" : "kernel";
+  return e == RAG_COPY_SDMA ? "sdma" : e == RAG_COPY_IN_GEMM ? "in-gemm"
+         : e == RAG_COPY_IN_GEMM_ASSIST ? "in-gemm+assist" : "kernel";
 }
 
-// Compute units kept free of GEMM workgroups while a copy kernel runs beside it on the side
-// stream.  A GEMM workgroup whose tiles wait for the copies must never fill every compute unit so
-// completely that no copy wave can be placed: then, if the GEMM's persistent grid is dispatched
-// first, its waiting tiles spin until the limit while the copies cannot start.  The copy kernel
-// needs few bytes of LDS and copy_vgprs registers per lane; a GEMM that leaves less than that on a
-// SIMD (its resident waves times their registers, of the 512 per lane) gets 8 compute units, one
-// per XCD, left out of its grid.
-int reserved_cus(const KernelInfo& g, bool copies_beside, int copy_vgprs) {
-  if (!copies_beside) return 0;
+// Persistent grid: every workgroup resident at once (so none waits for a slot while others spin
+// on counters), a multiple of 8 so that tile t always runs on XCD t % 8.
+int persistent_grid(int total_tiles, int num_cus, int blocks_per_cu) {
+  int cap = num_cus * std::max(1, blocks_per_cu);
+  int g = std::min(total_tiles, cap);
+  if (g >= 8) g -= g % 8;
+  return std::max(1, g);
+}
+
+// Registers per lane to leave for the HIP runtime's stream write-value kernel: hipStreamWriteValue32
+// runs as a small kernel on the compute units (it shows in kernel traces), and the SDMA engine
+// releases the counters with it.  Measured bounds: a GEMM+RS grid that left 16 registers per lane
+// on every SIMD kept it from running (every gated wait ran out its limit), one that left 32 (the
+// bf16 256x256 8-wave AG kernel, 240 registers at two waves per SIMD) did not.
+constexpr int kStreamOpVgprs = 32;
+
+// Compute units kept free of GEMM workgroups while a kernel that the GEMM waits for runs beside
+// it: the copy kernel on the side stream, or the runtime's write-value kernel that releases the
+// counters of SDMA copies.  A GEMM workgroup whose tiles wait for them must never fill every
+// compute unit so completely that none of their waves can be placed: then, if the GEMM's
+// persistent grid is dispatched first, its waiting tiles spin until the limit while the copies or
+// the counter writes cannot start (seen with SDMA and the fp8 256x256 8-wave kernel, 254 registers
+// at two waves per SIMD: every wait ran out its limit).  Those kernels need few bytes of LDS and
+// `room_vgprs` registers per lane; a GEMM that leaves less than that on a SIMD (its resident waves
+// times their registers, of the 512 per lane) gets 8 compute units, one per XCD, left out of its
+// grid.  room_vgprs = 0: nothing runs beside it.
+int reserved_cus(const KernelInfo& g, int room_vgprs) {
+  if (room_vgprs <= 0) return 0;
   const int waves_per_simd = std::max(1, g.max_blocks_per_cu * (g.threads / 64) / 4);
   const int regs = (g.vgprs_per_wave + 7) / 8 * 8;
-  return waves_per_simd * regs > 512 - copy_vgprs ? 8 : 0;
+  return waves_per_simd * regs > 512 - room_vgprs ? 8 : 0;
 }
 
 // Registers per lane of one copy-kernel wave, rounded up to the allocation granule of 8.
@@ -275,35 +300,78 @@ int ag_info(rag_ctx* c, int tile, bool fp8, bool out8, const KernelInfo** out) {
 }
 
 // The tile an AG+GEMM launch uses: choose_ag_tile's, except that with the automatic choice and a
-// copy kernel beside the GEMM, an 8-wave 256x256 kernel that would need compute units kept free
-// (above) gives way to the 4-stage 8-wave kernel of the same tile size if that one leaves room
-// for the copy waves: the copies then run on every compute unit instead of 8.
-int ag_launch_tile(rag_ctx* c, int nc, int M, int tp, bool fp8, bool out8, bool beside,
+// kernel the GEMM waits for running beside it (room_vgprs > 0), an 8-wave 256x256 kernel that
+// would need compute units kept free (above) gives way to the 4-stage 8-wave kernel of the same
+// tile size if that one leaves room: the kernel beside then runs on every compute unit.
+int ag_launch_tile(rag_ctx* c, int nc, int M, int tp, bool fp8, bool out8, int room_vgprs,
                    int* tile) {
   *tile = choose_ag_tile(c, nc, M, tp);
-  if (!beside || c->tile != RAG_TILE_AUTO || *tile != kTile256x256w8) return RAG_OK;
-  int cv = 0;
+  if (room_vgprs <= 0 || c->tile != RAG_TILE_AUTO || *tile != kTile256x256w8) return RAG_OK;
   const KernelInfo *w8 = nullptr, *s4 = nullptr;
-  int rc = copy_wave_vgprs(c, &cv);
-  if (!rc) rc = ag_info(c, kTile256x256w8, fp8, out8, &w8);
+  int rc = ag_info(c, kTile256x256w8, fp8, out8, &w8);
   if (!rc) rc = ag_info(c, kTile256x256w8s4, fp8, out8, &s4);
   if (rc) return rc;
-  if (reserved_cus(*w8, true, cv) > 0 && reserved_cus(*s4, true, cv) == 0)
+  if (reserved_cus(*w8, room_vgprs) > 0 && reserved_cus(*s4, room_vgprs) == 0)
     *tile = kTile256x256w8s4;
+  return RAG_OK;
+}
+
+// How one AG+GEMM call runs (everything but the split form): the copy engine's parts, the tile,
+// the persistent grid, and the late queue of the assisting copy kernel.
+struct AgPlan {
+  bool gemm_copies = false;   // the GEMM launch's workgroups copy
+  bool side_kernel = false;   // a copy kernel runs on the side stream
+  bool sdma = false;          // SDMA copies on the side streams
+  bool assist = false;
+  int room_vgprs = 0;         // registers per lane the GEMM leaves for what it waits for
+  int tile = 0, tiles_i = 0, tiles_j = 0, grid = 0;
+  int late = 0;               // peers in the assisting kernel's late queue
+};
+
+int plan_ag(rag_ctx* c, int nc, int M, int tp, bool fp8, bool out8, bool no_copy, AgPlan* p) {
+  const int engine = c->copy_engine;
+  p->assist = !no_copy && engine == RAG_COPY_IN_GEMM_ASSIST;
+  p->gemm_copies = !no_copy && (engine == RAG_COPY_IN_GEMM || p->assist);
+  p->side_kernel = !no_copy && (engine == RAG_COPY_KERNEL || p->assist);
+  p->sdma = !no_copy && engine == RAG_COPY_SDMA;
+  int copy_vgprs = 0;
+  if (p->side_kernel) {
+    const int rc = copy_wave_vgprs(c, &copy_vgprs);
+    if (rc) return rc;
+  }
+  // With the assisting copy kernel: the chunks at ring positions the first round of the grid does
+  // not reach (P = ceil(grid / U) and on) are the late queue, which the copy kernel takes beside
+  // the first round; the GEMM's waiting workgroups copy the early ones.  Without late chunks (one
+  // round holds every chunk) no copy kernel is launched and the call is the in-GEMM one.
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool beside = p->side_kernel && !(p->assist && pass == 0);
+    p->room_vgprs = beside ? copy_vgprs : p->sdma ? kStreamOpVgprs : 0;
+    int rc = ag_launch_tile(c, nc, M, tp, fp8, out8, p->room_vgprs, &p->tile);
+    if (rc) return rc;
+    const KernelInfo* info = nullptr;
+    rc = ag_info(c, p->tile, fp8, out8, &info);
+    if (rc) return rc;
+    int bi, bj;
+    tile_dims(p->tile, &bi, &bj);
+    p->tiles_i = (nc + bi - 1) / bi;
+    p->tiles_j = (M + bj - 1) / bj;
+    int bpc = info->max_blocks_per_cu;
+    if (c->wgs_per_cu > 0) bpc = std::min(bpc, c->wgs_per_cu);
+    p->grid = persistent_grid(p->tiles_i * p->tiles_j * tp,
+                              c->num_cus - reserved_cus(*info, p->room_vgprs), bpc);
+    if (!p->assist) break;
+    const int U = p->tiles_i * p->tiles_j;
+    p->late = std::max(0, tp - std::max(1, (p->grid + U - 1) / U));
+    if (p->late == 0) {
+      p->side_kernel = false;
+      break;
+    }
+  }
   return RAG_OK;
 }
 
 int choose_rs_tile(const rag_ctx* c, int nc, int Mo, int tp) {
   return choose_ag_tile(c, nc, Mo, tp);   // same GEMM core and the same trade-off
-}
-
-// Persistent grid: every workgroup resident at once (so none waits for a slot while others spin
-// on counters), a multiple of 8 so that tile t always runs on XCD t % 8.
-int persistent_grid(int total_tiles, int num_cus, int blocks_per_cu) {
-  int cap = num_cus * std::max(1, blocks_per_cu);
-  int g = std::min(total_tiles, cap);
-  if (g >= 8) g -= g % 8;
-  return std::max(1, g);
 }
 
 int record_timing_start(rag_ctx* c, hipStream_t s, bool* recorded) {
@@ -586,8 +654,9 @@ int rs_call(rag_ctx* c, const char* fn, bool ring, const void* X, int T, int Kl,
   // side stream does.
   // extra_copies (linear_allreduce's gather, not gated): copies with nothing waiting for them on
   // the device, run by the same launch
-  const bool in_gemm = (a.gated && c->copy_engine == RAG_COPY_IN_GEMM && !other_copies_beside) ||
-                       extra_copies != nullptr;
+  const bool ig_engine =
+      c->copy_engine == RAG_COPY_IN_GEMM || c->copy_engine == RAG_COPY_IN_GEMM_ASSIST;
+  const bool in_gemm = (a.gated && ig_engine && !other_copies_beside) || extra_copies != nullptr;
   bool join = false;
   if (a.gated) {
     CopyPlan cp = {};
@@ -658,16 +727,21 @@ int rs_call(rag_ctx* c, const char* fn, bool ring, const void* X, int T, int Kl,
       c->rs_info_ok[t] = true;
     }
   }
-  // With copies beside it, the automatic choice prefers a tile that leaves every compute unit
-  // room for copy waves: the copies then spread over the whole GPU instead of 8 CUs.
-  int copy_vgprs = 0;
-  if (beside) {
-    const int rc = copy_wave_vgprs(c, &copy_vgprs);
+  // Room the GEMM leaves for what runs beside it: the copy kernel's waves, or, with gated SDMA
+  // arrivals, the runtime's write-value kernel that releases their counters (see reserved_cus).
+  // The automatic choice prefers a tile that leaves every compute unit that room: the copies
+  // then spread over the whole GPU instead of 8 CUs.
+  int room_vgprs = 0;
+  if (a.gated && !in_gemm && c->copy_engine == RAG_COPY_SDMA) {
+    room_vgprs = kStreamOpVgprs;
+  } else if (beside) {
+    const int rc = copy_wave_vgprs(c, &room_vgprs);
     if (rc) return rc;
   }
-  if (beside && c->tile == RAG_TILE_AUTO && reserved_cus(c->rs_info[tile], true, copy_vgprs) > 0) {
+  if (room_vgprs > 0 && c->tile == RAG_TILE_AUTO &&
+      reserved_cus(c->rs_info[tile], room_vgprs) > 0) {
     for (int t : {(int)kTile256x128, (int)kTile128x128})
-      if (reserved_cus(c->rs_info[t], true, copy_vgprs) == 0) {
+      if (reserved_cus(c->rs_info[t], room_vgprs) == 0) {
         tile = t;
         break;
       }
@@ -677,8 +751,7 @@ int rs_call(rag_ctx* c, const char* fn, bool ring, const void* X, int T, int Kl,
   a.tiles_i = (nc + bi - 1) / bi;
   a.tiles_j = (Mo + bj - 1) / bj;
   const int total = a.tiles_i * a.tiles_j * tp;
-  const int grid = persistent_grid(total,
-                                   c->num_cus - reserved_cus(c->rs_info[tile], beside, copy_vgprs),
+  const int grid = persistent_grid(total, c->num_cus - reserved_cus(c->rs_info[tile], room_vgprs),
                                    c->rs_info[tile].max_blocks_per_cu);
   if (in_gemm) {
     // Pieces of (all bytes) / grid rounded up to a power of two from 64 KiB to 1 MiB: a piece
@@ -784,6 +857,11 @@ int rag_destroy(rag_ctx* c) {
   if (!c) return RAG_OK;
   (void)hipSetDevice(c->device);
   if (c->side) (void)hipStreamSynchronize(c->side);
+  for (int q = 0; q < 2; ++q) {
+    if (c->sdma[q]) (void)hipStreamSynchronize(c->sdma[q]);
+    if (c->sdma[q]) (void)hipStreamDestroy(c->sdma[q]);
+    if (c->ev_sdma[q]) (void)hipEventDestroy(c->ev_sdma[q]);
+  }
   for (auto ev : c->t_start) (void)hipEventDestroy(ev);
   for (auto ev : c->t_stop) (void)hipEventDestroy(ev);
   for (auto ev : c->ev_chunk) (void)hipEventDestroy(ev);
@@ -804,9 +882,44 @@ int rag_set_option(rag_ctx* c, int key, long long v) {
   if (!c) return fail(RAG_EINVAL, "rag_set_option: ctx is NULL");
   switch (key) {
     case RAG_OPT_COPY_ENGINE:
-      if (v != RAG_COPY_KERNEL && v != RAG_COPY_SDMA && v != RAG_COPY_IN_GEMM)
-        return fail(RAG_EINVAL, "copy engine must be 0 (kernel), 1 (sdma) or 2 (in the GEMM)");
+      if (v != RAG_COPY_KERNEL && v != RAG_COPY_SDMA && v != RAG_COPY_IN_GEMM &&
+          v != RAG_COPY_IN_GEMM_ASSIST)
+        return fail(RAG_EINVAL, "copy engine must be 0 (kernel), 1 (sdma), 2 (in the GEMM) or 3 "
+                    "(in the GEMM with a copy kernel assisting), got %lld", v);
       c->copy_engine = (int)v;
+      return RAG_OK;
+    case RAG_OPT_COMM_CUS: {
+      if (v != 0 && (v < 8 || v > c->num_cus - 8 || v % 8))
+        return fail(RAG_EINVAL, "comm CUs must be 0 (off) or a multiple of 8 in [8, %d], got %lld",
+                    c->num_cus - 8, v);
+      if (v == c->comm_cus) return RAG_OK;
+      // replace the side stream: after its work is done, by one limited to the lowest v
+      // compute-unit mask bits (bit b is compute unit b / 8 of XCD b % 8 on gfx950, so every XCD
+      // gets v / 8), or by an unrestricted one
+      HIPCHK(hipSetDevice(c->device));
+      HIPCHK(hipStreamSynchronize(c->side));
+      hipStream_t ns = nullptr;
+      if (v == 0) {
+        HIPCHK(hipStreamCreateWithFlags(&ns, hipStreamNonBlocking));
+      } else {
+        std::vector<uint32_t> mask((size_t)(c->num_cus + 31) / 32, 0u);
+        for (long long b = 0; b < v; ++b) mask[(size_t)b / 32] |= 1u << (b % 32);
+        HIPCHK(hipExtStreamCreateWithCUMask(&ns, (uint32_t)mask.size(), mask.data()));
+      }
+      HIPCHK(hipStreamDestroy(c->side));
+      c->side = ns;
+      c->side_pending = false;
+      c->comm_cus = (int)v;
+      return RAG_OK;
+    }
+    case RAG_OPT_SDMA_STREAMS:
+      if (v < 1 || v > 3) return fail(RAG_EINVAL, "SDMA streams must be in [1, 3], got %lld", v);
+      HIPCHK(hipSetDevice(c->device));
+      for (int q = 0; q + 1 < v; ++q) {
+        if (!c->sdma[q]) HIPCHK(hipStreamCreateWithFlags(&c->sdma[q], hipStreamNonBlocking));
+        if (!c->ev_sdma[q]) HIPCHK(hipEventCreateWithFlags(&c->ev_sdma[q], hipEventDisableTiming));
+      }
+      c->sdma_streams = (int)v;
       return RAG_OK;
     case RAG_OPT_COMM_WGS:
       if (v < 1 || v > 1024) return fail(RAG_EINVAL, "comm workgroups must be in [1, 1024]");
@@ -985,13 +1098,20 @@ int ag_call(rag_ctx* c, Words& W, const char* fn, const void* A, int M, int K,
                            "staging buffer");
     if (rc) return rc;
   }
-  // copies beside the GEMM: a copy kernel on the side stream (the engine of the single launch)
-  const bool beside = !no_copy && c->copy_engine == RAG_COPY_KERNEL;
-  int tile = 0;
+  // Who runs the copies of the simulated arrival: the GEMM launch's own workgroups (in-GEMM,
+  // in-GEMM with assist), a copy kernel on the side stream beside the GEMM (kernel, in-GEMM with
+  // assist: both take pieces from the same queue), or SDMA on up to three side streams.
+  const int engine = c->copy_engine;
+  AgPlan plan;
   {
-    const int rc = ag_launch_tile(c, nc, M, tp, fp8, out8, beside && !(flags & RAG_PER_CHUNK), &tile);
+    const int rc = plan_ag(c, nc, M, tp, fp8, out8, no_copy, &plan);
     if (rc) return rc;
   }
+  const bool assist = plan.assist, gemm_copies = plan.gemm_copies, sdma = plan.sdma;
+  const bool side_kernel = plan.side_kernel;
+  const int tile = plan.tile, tiles_i = plan.tiles_i, tiles_j = plan.tiles_j, grid = plan.grid;
+  const int late = plan.late;
+  const bool side = side_kernel || sdma;
   const int epoch = next_epoch(W);
   unsigned long long* trace = nullptr;
   if (c->trace_buf) {
@@ -1005,17 +1125,15 @@ int ag_call(rag_ctx* c, Words& W, const char* fn, const void* A, int M, int K,
   for (int j = 0; j < tp; ++j) order[j] = ((self_rank - j) % tp + tp) % tp;
 
   if (flags & RAG_PER_CHUNK) {
-    const int rc = ag_gemm_split(c, W, A, M, K, B, nc, tp, self_rank, Gp, own_copy, D, fp8, scale_A,
-                                 scale_B, out8, scale_D, amax_D, B_copy, staged, no_copy,
+    const int rc = ag_gemm_split(c, W, A, M, K, B, nc, tp, self_rank, Gp, own_copy, D, fp8,
+                                 scale_A, scale_B, out8, scale_D, amax_D, B_copy, staged, no_copy,
                                  copy_only, chunk_bytes, order, epoch, stream);
     if (rc) return rc;
     return staged && !copy_only ? finalize_staged(c, D, nc, M, tp, order, oesz, stream) : RAG_OK;
   }
 
-  // The copies of the simulated arrival: the peers' chunks in ring order, then the own chunk
-  // into G.  Engines: a copy kernel on the side stream, SDMA on the side stream, or the GEMM's
-  // own workgroups (in-kernel: no side stream, no fork or join).
-  const bool in_kernel = !no_copy && c->copy_engine == RAG_COPY_IN_GEMM;
+  // The copies: the peers' chunks in ring order (the last `late` of them the assisting kernel's
+  // queue), then the own chunk into G, then B_copy.
   CopyPlan cp = {};
   if (!no_copy) {
     int n = 0;
@@ -1030,9 +1148,10 @@ int ag_call(rag_ctx* c, Words& W, const char* fn, const void* A, int M, int K,
     if (own_copy) {
       cp.src[n] = B[self_rank];
       cp.dst[n] = Gp + (size_t)self_rank * chunk_bytes;
-      // the GEMM waits for it before exiting only when the copies run beside it (with B_copy
-      // too, the caller's stream waits for the side stream instead)
-      cp.ctr_index[n] = (copy_only || in_kernel || B_copy) ? -1 : c->max_tp;
+      // when something on a side stream may copy it, the GEMM waits for it before exiting (with
+      // B_copy too, or with no GEMM, the caller's stream waits for the side streams instead);
+      // when only the GEMM's own workgroups copy, they finish it before the launch ends
+      cp.ctr_index[n] = (copy_only || !side || B_copy) ? -1 : c->max_tp;
       cp.pos[n] = 0;
       ++n;
     }
@@ -1044,47 +1163,63 @@ int ag_call(rag_ctx* c, Words& W, const char* fn, const void* A, int M, int K,
       ++n;
     }
     cp.n = n;
+    cp.late = late;
     cp.bytes = (unsigned long long)chunk_bytes;
-    // a piece is two rounds of 8 16-byte vectors per thread of the copying workgroup
-    cp.piece_bytes = (unsigned)(in_kernel ? tile_threads(tile) : kArrivalThreads) * 256u;
+    // a piece is two rounds of 8 16-byte vectors per thread of the GEMM's copying workgroups
+    // (or of the copy kernel's, when only it copies)
+    cp.piece_bytes = (unsigned)(gemm_copies ? tile_threads(tile) : kArrivalThreads) * 256u;
     cp.pieces = (unsigned)((cp.bytes + cp.piece_bytes - 1) / cp.piece_bytes);
     use_count_set(W, cp);
     cp.delay_ticks = c->delay_us * c->wall_khz / 1000;
     cp.withhold_mask = c->withhold;
     cp.trace = trace;
   }
-
-  if (!no_copy && !in_kernel) {
+  // A launch that copies on the caller's stream clears the piece counts a previous call's copy
+  // kernel may still use: join it first (before this call's own side-stream kernel is forked)
+  if (gemm_copies && cp.n > 0) {
+    const int rc = join_side_copies(c, stream);
+    if (rc) return rc;
+  }
+  bool copied = false;   // a launch used this call's set of piece counts
+  const int nsdma = sdma ? std::min(c->sdma_streams, std::max(1, cp.n)) : 0;
+  if (side) {
     HIPCHK(hipEventRecord(c->ev_fork, stream));
     HIPCHK(hipStreamWaitEvent(c->side, c->ev_fork, 0));
-    if (c->copy_engine == RAG_COPY_KERNEL) {
+    if (side_kernel) {
       ArrivalArgs aa = {};
       aa.cp = cp;
       aa.ctr = W.ctr;
       aa.epoch = epoch;
       aa.raise_priority = c->copy_priority;
+      aa.late_only = assist ? 1 : 0;
       if (cp.n > 0) {
         HIPCHK(launch_arrival(c->device, aa, c->comm_wgs, c->side));
-        W.arr_seq++;
+        copied = true;
         const int rc = note_side_copies(c);
         if (rc) return rc;
       }
     } else {
+      // SDMA: copy k on side stream k mod nsdma, each followed by its counter's release
+      for (int q = 1; q < nsdma; ++q) HIPCHK(hipStreamWaitEvent(c->sdma[q - 1], c->ev_fork, 0));
       for (int k = 0; k < cp.n; ++k) {
+        hipStream_t sk = (k % nsdma == 0) ? c->side : c->sdma[k % nsdma - 1];
         HIPCHK(hipMemcpyAsync(cp.dst[k], cp.src[k], (size_t)chunk_bytes,
-                              hipMemcpyDeviceToDeviceNoCU, c->side));
+                              hipMemcpyDeviceToDeviceNoCU, sk));
         if (cp.ctr_index[k] >= 0 && (cp.pos[k] == 0 || !((c->withhold >> cp.pos[k]) & 1u)))
-          HIPCHK(hipStreamWriteValue32(c->side, W.ctr + (size_t)cp.ctr_index[k] * kWordStride,
+          HIPCHK(hipStreamWriteValue32(sk, W.ctr + (size_t)cp.ctr_index[k] * kWordStride,
                                        (uint32_t)epoch, 0));
       }
     }
     // With a GEMM the join is on the device (its workgroups wait for the last copy before they
     // exit); without one, or with B_copy (two copies after the peers', completing in any order),
-    // the caller's stream waits for the side stream's end.
-    if (copy_only || B_copy) HIPCHK(hipEventRecord(c->ev_join, c->side));
+    // the caller's stream waits for the side streams' ends.
+    if (copy_only || B_copy) {
+      HIPCHK(hipEventRecord(c->ev_join, c->side));
+      for (int q = 1; q < nsdma; ++q) HIPCHK(hipEventRecord(c->ev_sdma[q - 1], c->sdma[q - 1]));
+    }
   }
 
-  if (!copy_only || in_kernel) {
+  if (!copy_only || gemm_copies) {
     AgArgs a = {};
     for (int j = 0; j < tp; ++j) {
       const int r = order[j];
@@ -1099,61 +1234,47 @@ int ag_call(rag_ctx* c, Words& W, const char* fn, const void* A, int M, int K,
     a.nc = nc;
     a.tp = tp;
     a.ctr = W.ctr;
-    a.join_index = (own_copy && !no_copy && !in_kernel && !B_copy) ? c->max_tp : -1;
+    a.join_index = (own_copy && side && !B_copy && !copy_only) ? c->max_tp : -1;
     a.epoch = epoch;
     a.err = W.err;
     a.spin_limit = c->spin_us * c->wall_khz / 1000;
     a.scale_A = scale_A;
     a.scale_B = scale_B;
     a.trace = trace ? trace + kTraceHeader : nullptr;
-    a.copies = in_kernel && cp.n > 0;
+    a.copies = gemm_copies && cp.n > 0;
     a.compute = copy_only ? 0 : 1;
     a.out_fp8 = out8 ? 1 : 0;
     a.scale_D = scale_D;
     a.amax_D = amax_D;
     a.cp = cp;
-    int bi, bj;
-    tile_dims(tile, &bi, &bj);
-    a.tiles_i = (nc + bi - 1) / bi;
-    a.tiles_j = (M + bj - 1) / bj;
-    if (!c->ag_info_ok[tile][fp8][out8]) {
-      HIPCHK(ag_kernel_info(c->device, tile, fp8, out8, &c->ag_info[tile][fp8][out8]));
-      c->ag_info_ok[tile][fp8][out8] = true;
-    }
-    const int total = a.tiles_i * a.tiles_j * tp;
-    int bpc = c->ag_info[tile][fp8][out8].max_blocks_per_cu;
-    if (c->wgs_per_cu > 0) bpc = std::min(bpc, c->wgs_per_cu);
-    int copy_vgprs = 0;
-    if (beside) {
-      const int rc = copy_wave_vgprs(c, &copy_vgprs);
-      if (rc) return rc;
-    }
-    const int grid = persistent_grid(
-        total, c->num_cus - reserved_cus(c->ag_info[tile][fp8][out8], beside, copy_vgprs), bpc);
+    a.tiles_i = tiles_i;
+    a.tiles_j = tiles_j;
+    const int total = tiles_i * tiles_j * tp;
     // in-kernel copies: workgroups w with (w / 8) % copy_stride == 0 take part (workgroup 0 always)
     a.copy_stride = 1;
     if (a.copies && c->gemm_copy_wgs > 0 && grid >= 8)
       a.copy_stride = std::max(1, (grid / 8) / std::max(1, c->gemm_copy_wgs / 8));
     if (debug_enabled())
-      fprintf(stderr, "[ringag] ag_gemm tp=%d s=%d nc=%d K=%d M=%d %s tile=%dx%d tiles=%d grid=%d "
-              "(blocks/CU %d, VGPRs %d, LDS %d) engine=%s comm_wgs=%d pieces=%ux%u B "
+      fprintf(stderr, "[ringag] ag_gemm tp=%d s=%d nc=%d K=%d M=%d %s %s tiles=%d grid=%d "
+              "(blocks/CU %d, VGPRs %d, LDS %d) engine=%s late=%d comm_wgs=%d pieces=%ux%u B "
               "flags=0x%x epoch=%d\n",
-              tp, self_rank, nc, K, M, fp8 ? "fp8" : "bf16", bi, bj, total, grid,
-              c->ag_info[tile][fp8][out8].max_blocks_per_cu, c->ag_info[tile][fp8][out8].vgprs_per_wave,
-              c->ag_info[tile][fp8][out8].lds_bytes, engine_name(c->copy_engine),
-              c->comm_wgs, cp.pieces, cp.piece_bytes, flags, epoch);
-    if (a.copies) {
-      const int rc = join_side_copies(c, stream);
-      if (rc) return rc;
-    }
+              tp, self_rank, nc, K, M, fp8 ? "fp8" : "bf16", ag_kernel_name(tile, fp8, out8),
+              total, grid,
+              c->ag_info[tile][fp8][out8].max_blocks_per_cu,
+              c->ag_info[tile][fp8][out8].vgprs_per_wave, c->ag_info[tile][fp8][out8].lds_bytes,
+              engine_name(engine), late, c->comm_wgs, cp.pieces, cp.piece_bytes, flags, epoch);
     hipEvent_t ev0, ev1;
     launch_timing_events(c, &ev0, &ev1);
     HIPCHK(launch_ag_gemm(c->device, a, tile, fp8, grid, stream, ev0, ev1));
     launch_timed(c, ev0);
-    if (a.copies) W.arr_seq++;
+    copied = copied || a.copies;
   }
-  if (!no_copy && !in_kernel && (copy_only || B_copy))
+  if (copied) W.arr_seq++;
+  if (side && (copy_only || B_copy)) {
     HIPCHK(hipStreamWaitEvent(stream, c->ev_join, 0));
+    for (int q = 1; q < nsdma; ++q) HIPCHK(hipStreamWaitEvent(stream, c->ev_sdma[q - 1], 0));
+    if (side_kernel) c->side_pending = false;
+  }
 
   return staged && !copy_only ? finalize_staged(c, D, nc, M, tp, order, oesz, stream) : RAG_OK;
 }
@@ -1251,7 +1372,8 @@ int linear_allreduce(rag_ctx* c, const void* X, int T, int Kl, const void* W, in
   // the all-gather.  With the in-GEMM engine and nothing gated, the GEMM+RS launch copies the
   // owners' reduced chunks itself (after its tiles' epilogues, in ring order); else a copy kernel
   // or SDMA on the side stream, forked before the GEMM so that the copies run beside it.
-  if (tp > 1 && c->copy_engine == RAG_COPY_IN_GEMM && !(flags & RAG_RS_ARRIVE)) {
+  if (tp > 1 && (c->copy_engine == RAG_COPY_IN_GEMM || c->copy_engine == RAG_COPY_IN_GEMM_ASSIST) &&
+      !(flags & RAG_RS_ARRIVE)) {
     CopyPlan gp = {};
     int n = 0;
     for (int k = 1; k < tp; ++k, ++n) {
@@ -1325,11 +1447,10 @@ int rag_ag_kernel_name(rag_ctx* c, int nc, int M, int tp, rag_dtype dt, char* bu
     return fail(RAG_EINVAL, "rag_ag_kernel_name: bad arguments");
   if (dt != RAG_BF16 && dt != RAG_FP8_E4M3) return fail(RAG_EINVAL, "unknown dtype %d", dt);
   const bool fp8 = dt == RAG_FP8_E4M3;
-  int tile = 0;
-  const int rc =
-      ag_launch_tile(c, nc, M, tp, fp8, false, c->copy_engine == RAG_COPY_KERNEL, &tile);
+  AgPlan plan;
+  const int rc = plan_ag(c, nc, M, tp, fp8, false, false, &plan);
   if (rc) return rc;
-  snprintf(buf, (size_t)len, "%s", ag_kernel_name(tile, fp8));
+  snprintf(buf, (size_t)len, "%s", ag_kernel_name(plan.tile, fp8));
   return RAG_OK;
 }
 

@@ -37,6 +37,8 @@ def reset_options(c: B.Context):
     c.set_option(B.RAG_OPT_ARRIVAL_DELAY_US, 0)
     c.set_option(B.RAG_OPT_WITHHOLD_MASK, 0)
     c.set_option(B.RAG_OPT_TILE, 0)
+    c.set_option(B.RAG_OPT_COMM_CUS, 0)
+    c.set_option(B.RAG_OPT_SDMA_STREAMS, 1)
 
 
 def scale_tensor(s):

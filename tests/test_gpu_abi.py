@@ -101,5 +101,34 @@ def test_automatic_tile_choice_by_shape():
         assert c.ag_kernel_name(2048, 3584, 8, fp8=True) == "rag_ag_fp8_t256x256w8"
         assert c.rs_kernel_name(1024, 8192, 8) == "rag_rs_t256x256w8"        # 1024 tiles: 4 rounds
         assert c.ag_kernel_name(256, 1024, 2) == "rag_ag_bf16_t128x128"      # too few big tiles
+        # engines whose copies or counter writes run beside the GEMM get a kernel that leaves them
+        # room on every SIMD: the fp8 256x256 8-wave kernel (254 registers at two waves per SIMD)
+        # gives way to the 4-stage one for the copy kernel and for SDMA, whose counters the
+        # runtime's write-value kernel releases
+        for engine in ("kernel", "sdma"):
+            c.set_option(B.RAG_OPT_COPY_ENGINE, B.ENGINES[engine])
+            assert c.ag_kernel_name(2048, 3584, 8, fp8=True) == "rag_ag_fp8_t256x256w8s4", engine
+        # the assisting copy kernel runs only when a later round needs chunks: one round (ag_4k)
+        # keeps the in-GEMM kernel
+        c.set_option(B.RAG_OPT_COPY_ENGINE, B.ENGINES["assist"])
+        assert c.ag_kernel_name(1024, 4096, 4) == "rag_ag_bf16_t256x256w8"
     finally:
         reset_options(c)
+
+
+def test_set_option_rejects_bad_values():
+    """Every option refuses out-of-range values with RAG_EINVAL and leaves the context usable."""
+    c = ctx()
+    say("case option validation")
+    bad = [(B.RAG_OPT_COPY_ENGINE, 4), (B.RAG_OPT_COPY_ENGINE, -1), (B.RAG_OPT_COMM_CUS, 4),
+           (B.RAG_OPT_COMM_CUS, 12), (B.RAG_OPT_COMM_CUS, 256), (B.RAG_OPT_SDMA_STREAMS, 0),
+           (B.RAG_OPT_SDMA_STREAMS, 4), (B.RAG_OPT_TILE, 99), (B.RAG_OPT_COMM_WGS, 0), (999, 1)]
+    for key, value in bad:
+        rc = B.lib().rag_set_option(c.h, key, value)
+        assert rc == B.RAG_EINVAL, (key, value, rc)
+        assert B.last_error(), (key, value)
+    for key, value in [(B.RAG_OPT_COMM_CUS, 8), (B.RAG_OPT_COMM_CUS, 0),
+                       (B.RAG_OPT_SDMA_STREAMS, 3), (B.RAG_OPT_SDMA_STREAMS, 1),
+                       (B.RAG_OPT_COPY_ENGINE, B.RAG_COPY_IN_GEMM_ASSIST)]:
+        assert B.lib().rag_set_option(c.h, key, value) == B.RAG_OK, (key, value)
+    reset_options(c)

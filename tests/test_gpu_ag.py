@@ -13,9 +13,9 @@ from gpu_common import (DEV, AGRun, TOL_BF16, TOL_FP8, cached, ctx, oracle_ag, r
 pytestmark = pytest.mark.gpu
 
 TILE_NAMES = ["128x128", "256x128", "256x256", "256x256w8", "256x256w8s4", "256x192w8"]
-# copy engines of the simulated arrival that run on compute units: the side-stream copy kernel and
-# the GEMM's own waiting workgroups (SDMA is covered in the flags test)
-ENGINES = ["kernel", "in-gemm"]
+# copy engines of the simulated arrival that run on compute units: the side-stream copy kernel, the
+# GEMM's own waiting workgroups, and both on one queue (SDMA is covered in the flags test)
+ENGINES = ["kernel", "in-gemm", "assist"]
 
 
 def set_engine(c, engine):
@@ -155,6 +155,97 @@ def test_ag_flags_staged_copy_only_sdma(engine):
         set_engine(c, engine)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("tp,s,wgs_per_cu", [(8, 3, 0), (8, 0, 1), (4, 2, 1), (16, 9, 0)])
+def test_ag_assist_late_queue_exact(tp, s, wgs_per_cu, dtype):
+    """Shapes whose GEMM needs several persistent rounds, so that the assisting copy kernel takes
+    the late chunks beside the first round while the GEMM's waiting workgroups copy the early
+    ones: exact integer parity, three calls back to back with fresh data, then an in-GEMM call."""
+    c = ctx()
+    set_engine(c, "assist")
+    c.set_option(B.RAG_OPT_TILE, B.TILES["128x128"])
+    c.set_option(B.RAG_OPT_WGS_PER_CU, wgs_per_cu)
+    runs = []
+    for it in range(3):
+        # 128x128 tiles: chunks of 4 x 32 tiles, so the persistent grid (512, or 256 with one
+        # workgroup per CU) covers the first 4 (or 2) ring positions in its first round
+        inp = W.make_ag(W.ag_shape(tp, s, 512, 256, 4096, dtype=dtype, dist="int3",
+                                   seed=80 + it + tp))
+        runs.append((AGRun(inp), inp))
+    say(f"case assist late queue tp={tp} s={s} wgs/cu={wgs_per_cu} {dtype}")
+    for run, inp in runs:
+        sh = inp.shape
+        B.ag_gemm(c, run.A, run.chunks, sh.tp, sh.self_rank, run.D, G=run.G, scale_A=run.sA,
+                  scale_B=run.sB)
+    set_engine(c, "in-gemm")
+    run0, inp0 = runs[0]
+    D2 = torch.empty_like(run0.D)
+    B.ag_gemm(c, run0.A, run0.chunks, tp, s, D2, G=run0.G, scale_A=run0.sA, scale_B=run0.sB)
+    torch.cuda.synchronize()
+    c.check()
+    for run, inp in runs:
+        G_ref, ref = oracle_ag(inp)
+        assert np.array_equal(run.D_bits(), O.f32_to_bf16(ref))
+        Gb = W.bits_u8(run.G.cpu()) if dtype == "fp8" else W.bits_u16(run.G.cpu())
+        assert np.array_equal(Gb, G_ref)
+    assert torch.equal(D2.view(torch.int16), run0.D.view(torch.int16))
+
+
+@pytest.mark.parametrize("streams", [1, 2, 3])
+def test_ag_sdma_spread_over_streams(streams):
+    """SDMA copies spread over 1-3 side streams: every chunk lands, D and G exact, with the own
+    chunk copied into G, with B_copy (joined by events) and copy-only."""
+    c = ctx()
+    set_engine(c, "sdma")
+    c.set_option(B.RAG_OPT_SDMA_STREAMS, streams)
+    for tp, s in ((8, 5), (4, 1), (3, 2)):
+        inp = W.make_ag(W.ag_shape(tp, s, 64, 128, 192, dist="int3", seed=40 + tp + s))
+        _, ref = oracle_ag(inp)
+        G_ref = O.gather([W.bits_u16(x) for x in inp.chunks])
+        say(f"case sdma streams={streams} tp={tp} s={s}")
+        run = AGRun(inp).run(c)
+        assert np.array_equal(run.D_bits(), O.f32_to_bf16(ref))
+        assert np.array_equal(W.bits_u16(run.G.cpu()), G_ref)
+        Bc = torch.zeros_like(run.chunks[s])
+        run.G.zero_()
+        B.ag_gemm(c, run.A, run.chunks, tp, s, run.D, G=run.G, B_copy=Bc)
+        torch.cuda.synchronize()
+        assert np.array_equal(W.bits_u16(run.G.cpu()), G_ref)
+        assert torch.equal(Bc.view(torch.int16), run.chunks[s].view(torch.int16))
+        run.G.zero_()
+        run.run(c, flags=B.RAG_COPY_ONLY)
+        assert np.array_equal(W.bits_u16(run.G.cpu()), G_ref)
+    c.check()
+
+
+@pytest.mark.parametrize("engine", ["kernel", "assist"])
+def test_ag_comm_cus_masked_side_stream(engine):
+    """The side stream limited to 32 compute units (4 per XCD): exact results from a caller on a
+    stream of its own (where the copies overlap the GEMM) and on the null stream (which the masked
+    stream serialises with), back to back with fresh data, then the option switched off again."""
+    c = ctx()
+    set_engine(c, engine)
+    c.set_option(B.RAG_OPT_COMM_CUS, 32)
+    try:
+        st = torch.cuda.Stream()
+        for it, (tp, s) in enumerate(((4, 1), (8, 6), (4, 1))):
+            inp = W.make_ag(W.ag_shape(tp, s, 256, 512, 512, dist="int3", seed=60 + it))
+            _, ref = oracle_ag(inp)
+            run = AGRun(inp)
+            say(f"case comm_cus=32 engine={engine} tp={tp} s={s} (own stream)")
+            with torch.cuda.stream(st):
+                B.ag_gemm(c, run.A, run.chunks, tp, s, run.D, G=run.G)
+            torch.cuda.synchronize()
+            assert np.array_equal(run.D_bits(), O.f32_to_bf16(ref))
+            say(f"case comm_cus=32 engine={engine} tp={tp} s={s} (null stream)")
+            run.D.zero_()
+            run.run(c)
+            assert np.array_equal(run.D_bits(), O.f32_to_bf16(ref))
+        c.check()
+    finally:
+        c.set_option(B.RAG_OPT_COMM_CUS, 0)
+
+
 @pytest.mark.parametrize("engine", ENGINES)
 def test_ag_internal_gather_buffer(engine):
     c = ctx()
@@ -248,7 +339,11 @@ def test_ag_fp8_small_parity_and_exact(engine):
 
 
 FULL_CASES = [(name, engine, placement) for name in ("ag_4k", "ag_qkv", "ag_fc1_f8")
-              for engine in ENGINES for placement in ("separate", "in-g")]
+              for engine in ENGINES for placement in ("separate", "in-g")] + [
+    # SDMA at full size: its counters are released by the runtime's write-value kernel, which the
+    # GEMM must leave room for (with the fp8 256x256 8-wave kernel filling every SIMD, every wait
+    # ran out its limit)
+    ("ag_fc1_f8", "sdma", "in-g"), ("ag_qkv", "sdma", "separate")]
 
 
 @pytest.mark.parametrize("name,engine,placement", FULL_CASES)
@@ -260,7 +355,11 @@ def test_ag_full_size_full_output(name, engine, placement):
     set_engine(ctx(), engine)
     say(f"case {shape} engine={engine} placement={placement}")
     inp = W.make_ag(shape)
-    run = AGRun(inp, own_in_g=(placement == "in-g")).run(ctx())
+    run = AGRun(inp, own_in_g=(placement == "in-g"))
+    for _ in range(3):   # back to back
+        B.ag_gemm(ctx(), run.A, run.chunks, shape.tp, shape.self_rank, run.D, G=run.G,
+                  scale_A=run.sA, scale_B=run.sB)
+    torch.cuda.synchronize()
     ctx().check()
     G_ref, ref = cached(("ag", name), lambda: oracle_ag(inp))
     tol = TOL_FP8 if shape.dtype == "fp8" else TOL_BF16

@@ -405,7 +405,7 @@ def test_rs_ring_full_size_full_output(engine):
     _check_full(run.D, run.send, D_ref, out_ref, shape.self_rank, "rs ring")
 
 
-@pytest.mark.parametrize("engine", ["kernel", "in-gemm"])
+@pytest.mark.parametrize("engine", ["kernel", "in-gemm", "sdma"])
 @pytest.mark.parametrize("ring", [False, True])
 def test_rs_arrive_full_size_back_to_back(ring, engine):
     """Full-size gated calls back to back (no synchronisation between them).  With the copy kernel
