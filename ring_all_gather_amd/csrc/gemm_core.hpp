@@ -37,14 +37,11 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kOOB = 0x80000000u;         // voffset that is always past num_records
 
-template <int BI_, int BJ_, int WI_, int WJ_, int BKB_, int NS_, bool IL_ = false>
+template <int BI_, int BJ_, int WI_, int WJ_, int BKB_, int NS_>
 struct TileShape {
   static constexpr int BI = BI_, BJ = BJ_, WI = WI_, WJ = WJ_;
   static constexpr int BKB = BKB_;               // bytes of K per row per stage
   static constexpr int NS = NS_;                 // LDS stages
-  // bf16 K loop: interleave a k-step's fragment reads with its MFMAs (one read after every
-  // FI FJ / (FI + FJ) MFMAs) instead of issuing them as one burst before the MFMAs
-  static constexpr bool IL = IL_;
   static constexpr int NW = WI * WJ;             // waves
   static constexpr int NT = NW * 64;             // threads
   static constexpr int TM = BI / WI, TN = BJ / WJ;   // wave sub-tile
@@ -72,16 +69,8 @@ struct TileShape {
 // The configurations the kernels are built for.
 using Tile128x128 = TileShape<128, 128, 2, 2, 128, 2>;
 using Tile256x128 = TileShape<256, 128, 2, 2, 128, 2>;
-#ifndef RAG_W4_BKB
-#define RAG_W4_BKB 128
-#define RAG_W4_NS 2
-#define RAG_W4_IL false
-#endif
-using Tile256x256 = TileShape<256, 256, 2, 2, RAG_W4_BKB, RAG_W4_NS, RAG_W4_IL>;  // 4 waves of 128x128
-#ifndef RAG_W8_IL
-#define RAG_W8_IL false
-#endif
-using Tile256x256w8 = TileShape<256, 256, 2, 4, 128, 2, RAG_W8_IL>;    // 8 waves of 128x64, 2 stages
+using Tile256x256 = TileShape<256, 256, 2, 2, 128, 2>;      // 4 waves of 128x128, 2 stages
+using Tile256x256w8 = TileShape<256, 256, 2, 4, 128, 2>;    // 8 waves of 128x64, 2 stages
 using Tile256x256w8s4 = TileShape<256, 256, 2, 4, 64, 4>;   // 8 waves of 128x64, 4 stages
 using Tile256x192w8 = TileShape<256, 192, 4, 2, 128, 2>;    // 8 waves of 64x96, 2 stages
 
@@ -261,24 +250,6 @@ __device__ inline void load_frags_bf16(bf16x8 (&a)[S::FI], bf16x8 (&b)[S::FJ], c
   for (int f = 0; f < S::FJ; ++f) b[f] = frag_bf16<S::BKB>(ys + f * 32 * S::BKB, seg, lane);
 }
 
-// Interleaved fragment reads (S::IL): after MFMA m of a k-step, read the next k-step's fragments
-// with positions [m R / span, (m + 1) R / span) of the order in which that k-step's MFMAs (row i
-// by row, j = 0..FJ-1 in each) first use them: X fragment 0, the FJ Y fragments, then X fragments
-// 1..FI-1.  R = FI + FJ; span = NM spreads them over the whole k-step, span = NM / 2 over its
-// first half (the k-step before a stage handover, whose wait for the reads then finds them done).
-template <class S, int SPAN>
-__device__ inline void read_frag_il(bf16x8 (&a)[S::FI], bf16x8 (&b)[S::FJ], const char* xs,
-                                    const char* ys, int seg, int lane, int m) {
-  constexpr int R = S::FI + S::FJ;
-#pragma unroll
-  for (int u = 0; u < R; ++u) {
-    if (u < m * R / SPAN || u >= (m + 1) * R / SPAN) continue;
-    if (u == 0) a[0] = frag_bf16<S::BKB>(xs, seg, lane);
-    else if (u <= S::FJ) b[u - 1] = frag_bf16<S::BKB>(ys + (u - 1) * 32 * S::BKB, seg, lane);
-    else a[u - S::FJ] = frag_bf16<S::BKB>(xs + (u - S::FJ) * 32 * S::BKB, seg, lane);
-  }
-}
-
 // DMA instructions [q0, q1) of a stage (X rows first, then Y rows) into the stage buffer at byte
 // offset buf of the LDS, at K offset kb.
 template <class S>
@@ -349,25 +320,14 @@ __device__ inline void tile_kloop_bf16(i32x4 rx, const uint32_t* xo, i32x4 ry, c
 #pragma unroll
     for (int kk = 0; kk < NK - 1; ++kk) {
       const int c = kk & 1;
-      if constexpr (!S::IL)
-        load_frags_bf16<S>(a[c ^ 1], b[c ^ 1], lds + cur + xrow, lds + cur + yrow,
-                           (kk + 1) * 2 + h, lane);
+      load_frags_bf16<S>(a[c ^ 1], b[c ^ 1], lds + cur + xrow, lds + cur + yrow,
+                         (kk + 1) * 2 + h, lane);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         const int i = m / S::FJ, j = m % S::FJ;
         acc[i][j] =
             __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
-        if constexpr (S::IL) {
-          __builtin_amdgcn_sched_barrier(0);
-          // the k-step before the handover reads in its first half
-          if (kk == NK - 2)
-            read_frag_il<S, NM / 2>(a[c ^ 1], b[c ^ 1], lds + cur + xrow, lds + cur + yrow,
-                                    (kk + 1) * 2 + h, lane, m);
-          else
-            read_frag_il<S, NM>(a[c ^ 1], b[c ^ 1], lds + cur + xrow, lds + cur + yrow,
-                                (kk + 1) * 2 + h, lane, m);
-        }
         if (kk == 0) {
           // the second half of the pending stage's DMA, spread over this k-step's MFMAs
           __builtin_amdgcn_sched_barrier(0);
@@ -380,37 +340,17 @@ __device__ inline void tile_kloop_bf16(i32x4 rx, const uint32_t* xo, i32x4 ry, c
     }
     // last k-step of the stage (its fragments are in set 1: NK is even).  Outstanding DMA: stages
     // kt+1 .. kt+NS-1, all issued in full; stage kt+1 is complete once at most NS-2 of them are.
-#ifndef RAG_HO
-#define RAG_HO 0
-#endif
-    constexpr int HO = (S::IL && S::NW == 4) ? RAG_HO : 0;   // last k-step MFMAs before the handover
-#pragma unroll
-    for (int m = 0; m < HO; ++m) {
-      const int i = m / S::FJ, j = m % S::FJ;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][i], b[1][j], acc[i][j], 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
     stage_handover<(S::NS - 2) * S::LOADS>();
-    if constexpr (!S::IL)
-      load_frags_bf16<S>(a[0], b[0], lds + nxt + xrow, lds + nxt + yrow, h, lane);
+    load_frags_bf16<S>(a[0], b[0], lds + nxt + xrow, lds + nxt + yrow, h, lane);
     __builtin_amdgcn_sched_barrier(0);
-#ifdef RAG_PROBE_SAMEK
-    pend_kb = (uint32_t)((kt + S::NS) % 2) * S::BKB;
-#else
     pend_kb = kt + S::NS < ksteps ? (uint32_t)(kt + S::NS) * S::BKB : kOOB;
-#endif
     pend_buf = cur;
 #pragma unroll
-    for (int m = HO; m < NM; ++m) {
+    for (int m = 0; m < NM; ++m) {
       const int i = m / S::FJ, j = m % S::FJ;
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][i], b[1][j], acc[i][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (S::IL) {
-        read_frag_il<S, NM - HO>(a[0], b[0], lds + nxt + xrow, lds + nxt + yrow, h, lane, m - HO);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      dma_range<S>(rx, xo, ry, yo, base, pend_buf, pend_kb, wave, (m - HO) * H / (NM - HO),
-                   (m - HO + 1) * H / (NM - HO));
+      dma_range<S>(rx, xo, ry, yo, base, pend_buf, pend_kb, wave, m * H / NM, (m + 1) * H / NM);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
