@@ -40,6 +40,14 @@ METRICS = {
 }
 
 
+def set_engine(ctx, B, name):
+    """Copy engine by name; "in-gemm-slab" is the in-GEMM engine with K-slab gating (AG+GEMM; a
+    GEMM+RS call treats it as the in-GEMM engine)."""
+    ctx.set_option(B.RAG_OPT_COPY_ENGINE, B.ENGINES[name.replace("-slab", "")])
+    ctx.set_option(B.RAG_OPT_AG_GATE,
+                   B.RAG_GATE_SLAB if name.endswith("-slab") else B.RAG_GATE_CHUNK)
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -49,7 +57,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=1000)
     p.add_argument("--workload", default="ag_4k")
     p.add_argument("--copy-engine", default=os.environ.get("RAG_COPY_ENGINE", "in-gemm"),
-                   choices=["kernel", "sdma", "in-gemm", "assist"])
+                   choices=["kernel", "sdma", "in-gemm", "in-gemm-slab", "assist"])
     p.add_argument("--comm-cus", type=int, default=0,
                    help="compute units the side stream's copy kernels are limited to (0 = all)")
     p.add_argument("--sdma-streams", type=int, default=1,
@@ -255,7 +263,8 @@ def timeline_ag(ctx, B, step, shape, kname):
     for j in range(shape.tp):
         tj = tiles[j * per_chunk:(j + 1) * per_chunk]
         chunks.append({"ring_pos": j, "rank": (shape.self_rank - j) % shape.tp,
-                       "released_us": 0.0 if j == 0 else us(w[j - 1]),
+                       # (K-slab gating releases slabs, not chunks: no chunk stamp)
+                       "released_us": 0.0 if j == 0 else (us(w[j - 1]) if w[j - 1] else None),
                        "first_tile_go_us": us(min(x[1] for x in tj)),
                        "last_tile_end_us": us(max(x[2] for x in tj))})
     # the core clock the tiles ran at: s_memtime cycles over the 100 MHz wall time of each tile's
@@ -274,11 +283,11 @@ def overlap_per_engine(ctx, B, step, args, stream, shape, ms_head):
     side-stream kernel engine may pick another kernel of the same tile size, see the library's
     tile choice), so the three times are of the same kernel."""
     names = [args.copy_engine] + ([] if args.headline_only else
-                                  [e for e in ("in-gemm", "assist", "kernel", "sdma")
-                                   if e != args.copy_engine])
+                                  [e for e in ("in-gemm", "in-gemm-slab", "assist", "kernel",
+                                               "sdma") if e != args.copy_engine])
     res = {}
     for eng in names:
-        ctx.set_option(B.RAG_OPT_COPY_ENGINE, B.ENGINES[eng])
+        set_engine(ctx, B, eng)
         kname = ctx.ag_kernel_name(shape.nc, shape.M, shape.tp, shape.dtype == "fp8")
         t_chunked = ms_head if eng == args.copy_engine else \
             time_steps(step, args.steps, args.warmup, stream, f"{eng} chunked")
@@ -329,7 +338,7 @@ def main():
     ctx = B.Context(0, max_tp=16)
     global _CHECK
     _CHECK = ctx.check
-    ctx.set_option(B.RAG_OPT_COPY_ENGINE, B.ENGINES[args.copy_engine])
+    set_engine(ctx, B, args.copy_engine)
     ctx.set_option(B.RAG_OPT_COMM_WGS, args.comm_wgs)
     ctx.set_option(B.RAG_OPT_TILE, B.TILES[args.tile])
     ctx.set_option(B.RAG_OPT_COMM_CUS, args.comm_cus)
@@ -373,7 +382,7 @@ def main():
         ms_gemm, ms_copy = head["t_gemm_only_ms"], head["t_copy_only_ms"]
         ms_staged = ms_split = ms_seq = None
         if not args.headline_only:
-            ctx.set_option(B.RAG_OPT_COPY_ENGINE, B.ENGINES[args.copy_engine])
+            set_engine(ctx, B, args.copy_engine)
             ms_staged = time_steps(lambda: step(B.RAG_STAGED_OUT), args.steps, args.warmup,
                                    stream, "staged output")
             # the split form (one GEMM launch per chunk, gated by stream events): what the
@@ -384,7 +393,7 @@ def main():
             ms_seq = time_steps(lambda: (step(B.RAG_COPY_ONLY), step(B.RAG_NO_COPY)), args.steps,
                                 args.warmup, stream, "copies then GEMM")
         ctx.check()
-        ctx.set_option(B.RAG_OPT_COPY_ENGINE, B.ENGINES[args.copy_engine])
+        set_engine(ctx, B, args.copy_engine)
         flops = shape.flops
         kernel_ms = statistics.fmean(kt)
         achieved = flops / (kernel_ms * 1e-3) / 1e12

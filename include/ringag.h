@@ -123,7 +123,9 @@ enum {
     RAG_COPY_IN_GEMM = 2,  /* the GEMM launch itself: workgroups whose chunk is not there yet copy
                               pieces of the peers' chunks (ring order) until it is released, and
                               help with the rest once out of tiles; no side stream is used (see
-                              RAG_RS_ARRIVE for the GEMM+RS form) */
+                              RAG_RS_ARRIVE for the GEMM+RS form).  With K-slab gating
+                              (RAG_OPT_AG_GATE), every workgroup copies its share of slab pieces
+                              instead, and a tile waits only for the slab it loads next */
     RAG_COPY_IN_GEMM_ASSIST = 3 /* AG+GEMM: as RAG_COPY_IN_GEMM, and a copy kernel on the side
                               stream takes pieces from the same queue beside the GEMM
                               (RAG_OPT_COMM_WGS workgroups): the chunks that only later rounds of
@@ -176,9 +178,25 @@ enum {
                                    workgroups may share those units.  Such a stream is blocking with
                                    respect to the null stream: call from another stream, or the
                                    null stream serialises the copies with the GEMM */
-    RAG_OPT_SDMA_STREAMS = 14   /* RAG_COPY_SDMA: side streams the chunk copies are spread over
+    RAG_OPT_SDMA_STREAMS = 14,  /* RAG_COPY_SDMA: side streams the chunk copies are spread over
                                    (1..3, default 1), so that more than one copy engine works */
+    RAG_OPT_AG_GATE = 15,       /* AG+GEMM with RAG_COPY_IN_GEMM: what a tile of a peer's chunk
+                                   waits for.  RAG_GATE_CHUNK (default): the whole chunk (the
+                                   listing's per-chunk counters).  RAG_GATE_SLAB: one K slab, where
+                                   that applies (bf16 input, the 8-wave 2-stage tiles, G 128-byte
+                                   aligned, no test hook set, not ag_gemm_noalloc; else by chunk):
+                                   the peers' chunks are copied in pieces of 16 rows x 512 bytes of
+                                   K, spread over every workgroup's K loop, and a tile waits for the
+                                   pieces of the 4 K stages it loads next, so every tile starts at
+                                   once.  The library's own addition: finer-grained gating of the
+                                   same arrival */
+    RAG_OPT_SLAB_HELP_US = 16   /* K-slab gating: how long a tile waits for a slab before its
+                                   workgroup copies the slab's missing pieces itself (0..1e7 us,
+                                   default 20; 0 = at once, a test hook for that path) */
 };
+
+/* Values of RAG_OPT_AG_GATE. */
+enum { RAG_GATE_CHUNK = 0, RAG_GATE_SLAB = 1 };
 
 /* Tile configurations (rows of D x columns of D per workgroup; 4 waves unless stated). */
 enum { RAG_TILE_AUTO = 0, RAG_TILE_128x128 = 1, RAG_TILE_256x128 = 2,

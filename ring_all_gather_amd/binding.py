@@ -31,7 +31,9 @@ RAG_STAGED_OUT, RAG_NO_COPY, RAG_COPY_ONLY, RAG_PER_CHUNK, RAG_RS_ARRIVE = 1, 2,
 RAG_OPT_COPY_ENGINE, RAG_OPT_COMM_WGS, RAG_OPT_SPIN_LIMIT_US = 1, 2, 3
 RAG_OPT_ARRIVAL_DELAY_US, RAG_OPT_WITHHOLD_MASK, RAG_OPT_TIMING, RAG_OPT_TILE = 4, 5, 6, 7
 RAG_OPT_TRACE_BUF, RAG_OPT_TRACE_BYTES, RAG_OPT_WGS_PER_CU, RAG_OPT_COPY_PRIORITY = 8, 9, 10, 11
-RAG_OPT_GEMM_COPY_WGS, RAG_OPT_COMM_CUS, RAG_OPT_SDMA_STREAMS = 12, 13, 14
+RAG_OPT_GEMM_COPY_WGS, RAG_OPT_COMM_CUS, RAG_OPT_SDMA_STREAMS, RAG_OPT_AG_GATE = 12, 13, 14, 15
+RAG_OPT_SLAB_HELP_US = 16
+RAG_GATE_CHUNK, RAG_GATE_SLAB = 0, 1
 RAG_COPY_KERNEL, RAG_COPY_SDMA, RAG_COPY_IN_GEMM, RAG_COPY_IN_GEMM_ASSIST = 0, 1, 2, 3
 ENGINES = {"kernel": RAG_COPY_KERNEL, "sdma": RAG_COPY_SDMA, "in-gemm": RAG_COPY_IN_GEMM,
            "assist": RAG_COPY_IN_GEMM_ASSIST}

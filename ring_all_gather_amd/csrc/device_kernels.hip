@@ -2,8 +2,8 @@
 // object (hipcc --genco).  The host side embeds that object and loads it explicitly per device
 // (launch.cpp), so the shared library holds no compiler-generated registration code.
 //
-// Entry points: rag_ag_<bf16|fp8>[_o8]_<tile> (input dtype; _o8 = E4M3 output), rag_rs_<tile>,
-// rag_arrival.  Tile names:
+// Entry points: rag_ag_<bf16|fp8>[_o8]_<tile> (input dtype; _o8 = E4M3 output),
+// rag_ag_bf16[_o8]_slab_<tile> (K-slab gating, 8-wave 2-stage tiles), rag_rs_<tile>, rag_arrival.  Tile names:
 //   t128x128, t256x128, t256x256 (4 waves, 2 stages), t256x256w8 (8 waves, 2 stages), t256x256w8s4
 //   (8 waves, 4 stages), t256x192w8 (8 waves, 2 stages); see gemm_core.hpp.
 #include "arrival_kernel.hpp"
@@ -53,6 +53,19 @@ RAG_AG_ENTRY(t256x256, Tile256x256)
 RAG_AG_ENTRY(t256x256w8, Tile256x256w8)
 RAG_AG_ENTRY(t256x256w8s4, Tile256x256w8s4)
 RAG_AG_ENTRY(t256x192w8, Tile256x192w8)
+
+// The K-slab-gated AG+GEMM kernels (bf16 input; bf16 or E4M3 output).
+#define RAG_AG_SLAB_ENTRY(TILE, SHAPE)                                                         \
+  extern "C" __global__ void __launch_bounds__(SHAPE::NT) rag_ag_bf16_slab_##TILE(AgArgs a) {  \
+    ag_gemm_body<SHAPE, false, false, true>(a);                                                \
+  }                                                                                            \
+  extern "C" __global__ void __launch_bounds__(SHAPE::NT)                                      \
+      rag_ag_bf16_o8_slab_##TILE(AgArgs a) {                                                   \
+    ag_gemm_body<SHAPE, false, true, true>(a);                                                 \
+  }
+
+RAG_AG_SLAB_ENTRY(t256x256w8, Tile256x256w8)
+RAG_AG_SLAB_ENTRY(t256x192w8, Tile256x192w8)
 
 extern "C" __global__ void __launch_bounds__(kArrivalThreads) rag_arrival(ArrivalArgs a) {
   arrival_body(a);

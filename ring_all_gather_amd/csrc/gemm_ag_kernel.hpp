@@ -15,11 +15,17 @@
 // whatever is left, the own chunk's copy into G last.  The waiting workgroups are exactly the ones
 // with nothing to compute, so the copies use compute units that would otherwise idle, and no side
 // stream or stream fork/join is involved.
+//
+// With K-slab gating (AgArgs::slab, bf16 8-wave 2-stage tiles) the peers' chunks are not queued
+// whole: every workgroup copies its own slots of slab pieces (before its first tile, inside its K
+// loops, after its last tile), and a tile waits only for the slab its next loads read; see
+// slab_copy.hpp.
 #pragma once
 
 #include "copy_queue.hpp"
 #include "gemm_core.hpp"
 #include "kernels.hpp"
+#include "slab_copy.hpp"
 
 namespace ringag {
 
@@ -31,11 +37,17 @@ __device__ inline unsigned hw_location() {
   return (xcc << 16) | (se << 8) | cu;
 }
 
-template <class S, bool FP8, bool OUT8>
+// SLAB: the K-slab-gated form (its own entry points, so that the registers and LDS of the slab
+// copies are not charged to the chunk-gated kernels).
+template <class S, bool FP8, bool OUT8, bool SLAB = false>
 __device__ __forceinline__ void ag_gemm_body(const AgArgs& a) {
+  static_assert(!SLAB || (!FP8 && S::NT == kSlabThreads && S::NS == 2 && S::BKB == 128),
+                "K-slab gating is built for bf16 8-wave tiles with 2 stages of 128 bytes");
   __shared__ __attribute__((aligned(1024))) char lds[S::LDS];
   __shared__ int s_ok;
   __shared__ unsigned s_piece;
+  __shared__ int s_gate;
+  __shared__ __attribute__((aligned(1024))) char s_slab[SLAB ? kSlabMaxQ * 8192 : 16];
   __shared__ float s_red[OUT8 ? S::NW : 1];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -48,6 +60,12 @@ __device__ __forceinline__ void ag_gemm_body(const AgArgs& a) {
   const i32x4 ry = make_rsrc(a.A, (uint32_t)a.M * ldb);
   if (a.copies) copy_queue_begin(a.cp);
   const bool copier = a.copies && ((blockIdx.x >> 3) % a.copy_stride) == 0;
+  constexpr bool slab = SLAB;
+  int slot = 0;   // slab gating: this workgroup's next slot of pieces
+  if (slab) {
+    slab_copy_slots(a, 0, a.slab.pre, ldb);
+    slot = a.slab.pre;
+  }
 
   const int grid = (int)gridDim.x;
   for (int r0 = 0; a.compute && r0 < total; r0 += grid) {
@@ -58,7 +76,9 @@ __device__ __forceinline__ void ag_gemm_body(const AgArgs& a) {
     const int rb = u % a.tiles_i, cb = u / a.tiles_i;
     unsigned long long* tr = a.trace ? a.trace + kTraceTileWords * (size_t)t : nullptr;
     if (tr && threadIdx.x == 0) tr[0] = wall_clock64();
-    if (a.ctr_index[j] >= 0) {
+    if (slab && a.ctr_index[j] >= 0) {
+      slab_gate_tile(a, j - 1, ldb, &s_gate);
+    } else if (a.ctr_index[j] >= 0) {
       if (copier) {
         run_copy_queue<S::NT>(a.cp, a.ctr, a.epoch, 0, a.ctr_index[j], &s_piece);
         run_copy_queue<S::NT>(a.cp, a.ctr, a.epoch, 2, a.ctr_index[j], &s_piece);
@@ -80,7 +100,12 @@ __device__ __forceinline__ void ag_gemm_body(const AgArgs& a) {
     tile_offsets<S, S::XQ>(xo, rb * S::BI, a.nc, ldb, wave, lane);
     tile_offsets<S, S::YQ>(yo, cb * S::BJ, a.M, ldb, wave, lane);
     f32x16 acc[S::FI][S::FJ];
-    tile_kloop<S, FP8>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);
+    if constexpr (SLAB) {
+      SlabHook hook{a, a.ctr_index[j] >= 0 ? j - 1 : -1, ksteps, ldb, &s_gate, s_slab, slot};
+      tile_kloop_bf16<S>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc, hook);
+    } else {
+      tile_kloop<S, FP8>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);
+    }
     if constexpr (OUT8) {
       uint8_t* out = (uint8_t*)a.out[j] + (size_t)rb * S::BI * a.M + (size_t)cb * S::BJ;
       const float m = store_tile_fp8<S>(acc, scale, a.scale_D[0], lds, out, a.M,
@@ -105,9 +130,12 @@ __device__ __forceinline__ void ag_gemm_body(const AgArgs& a) {
     // keeps this thread-0 step and the next tile's apart (see run_copy_queue)
     __syncthreads();
   }
+  if (slab) slab_copy_slots(a, slot, max(slot, slab_slots_end(a)), ldb);
   if (copier) {
-    run_copy_queue<S::NT>(a.cp, a.ctr, a.epoch, 0, -1, &s_piece);
-    run_copy_queue<S::NT>(a.cp, a.ctr, a.epoch, 2, -1, &s_piece);
+    if (!slab) {
+      run_copy_queue<S::NT>(a.cp, a.ctr, a.epoch, 0, -1, &s_piece);
+      run_copy_queue<S::NT>(a.cp, a.ctr, a.epoch, 2, -1, &s_piece);
+    }
     run_copy_queue<S::NT>(a.cp, a.ctr, a.epoch, 1, -1, &s_piece);
   }
   // With the copies on another stream, which the caller's stream does not wait for, the kernel

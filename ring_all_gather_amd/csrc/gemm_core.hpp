@@ -267,6 +267,12 @@ __device__ inline void dma_range(i32x4 rx, const uint32_t* xo, i32x4 ry, const u
   }
 }
 
+// A K loop stage hook that does nothing.
+struct NoStageHook {
+  __device__ void pre(int) {}
+  __device__ void post(int) {}
+};
+
 // bf16 K loop over NS LDS stages with the stage handover inside a stage's last MFMA k-step.
 // Fragments are double-buffered as in stage_mma.  Once the fragments of the last k-step are in
 // registers, the wave waits for its DMA of the next stage and for its reads, meets the others at
@@ -278,10 +284,14 @@ __device__ inline void dma_range(i32x4 rx, const uint32_t* xo, i32x4 ry, const u
 // fragment read waits right behind a barrier, and the DMA issue hides under MFMAs.  The loop body
 // has no branch: past the last stage the DMA reads at kOOB (zeros, into a buffer nobody reads) and
 // the prefetch reads an idle buffer; the DMA is drained before the final barrier.
-template <class S>
+//
+// `hook` (see NoStageHook) runs code of the caller's at every stage handover: pre(kt) just before
+// the wait and barrier that complete stage kt + 1, post(kt) right after them, before the loads of
+// stage kt + 2 are issued.
+template <class S, class Hook>
 __device__ inline void tile_kloop_bf16(i32x4 rx, const uint32_t* xo, i32x4 ry, const uint32_t* yo,
                                        int ksteps, char* lds, int wave, int lane,
-                                       f32x16 (&acc)[S::FI][S::FJ]) {
+                                       f32x16 (&acc)[S::FI][S::FJ], Hook& hook) {
   constexpr int NK = S::SEGS / 2;
   constexpr int NM = S::FI * S::FJ;
   constexpr int H = S::LOADS / 2;   // the first half of a stage's DMA
@@ -340,7 +350,9 @@ __device__ inline void tile_kloop_bf16(i32x4 rx, const uint32_t* xo, i32x4 ry, c
     }
     // last k-step of the stage (its fragments are in set 1: NK is even).  Outstanding DMA: stages
     // kt+1 .. kt+NS-1, all issued in full; stage kt+1 is complete once at most NS-2 of them are.
+    hook.pre(kt);
     stage_handover<(S::NS - 2) * S::LOADS>();
+    hook.post(kt);
     load_frags_bf16<S>(a[0], b[0], lds + nxt + xrow, lds + nxt + yrow, h, lane);
     __builtin_amdgcn_sched_barrier(0);
     pend_kb = kt + S::NS < ksteps ? (uint32_t)(kt + S::NS) * S::BKB : kOOB;
@@ -464,7 +476,8 @@ __device__ inline void tile_kloop(i32x4 rx, const uint32_t* xo, i32x4 ry, const 
                                   int ksteps, char* lds, int wave, int lane,
                                   f32x16 (&acc)[S::FI][S::FJ]) {
   if constexpr (!FP8) {
-    tile_kloop_bf16<S>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);
+    NoStageHook none;
+    tile_kloop_bf16<S>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc, none);
     return;
   } else if constexpr (S::NS == 2) {
     tile_kloop_2s_fp8<S>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);

@@ -57,6 +57,32 @@ struct CopyPlan {
   unsigned long long* trace;     // optional: [c] = completion time of copy c, [kTraceStart] = start
 };
 
+// K-slab gating of the in-GEMM copies (AG+GEMM, bf16, 8-wave tiles with 2 stages of 128 bytes).
+// The peers' chunks are cut into pieces of kSlabRows rows by kSlabRowBytes bytes of K (one group
+// of kSlabStages K stages), numbered group by group: piece (g, c, rb) = rows [rb * kSlabRows, +
+// kSlabRows) of group g of copy c, index (g * n_peer + c) * ppc + rb.  Piece i belongs to
+// workgroup (i / q) % grid, which copies it in its slot i / (q * grid): slots 0 .. pre-1 before
+// its first tile, later ones one per group of K stages inside its K loops, and whatever is left
+// after its last tile.  flags[(c * groups + g) * ppc + rb] holds the epoch of the last call that
+// copied that piece; a tile of chunk c waits for all ppc flags of group g before loading it, and
+// copies the missing pieces itself once it has waited help_ticks.
+constexpr int kSlabRowBytes = 512;
+constexpr int kSlabRows = 16;       // 16 rows x 512 bytes = 8 KiB: one 16-byte vector per thread
+constexpr int kSlabThreads = 512;
+constexpr int kSlabStages = 4;      // K stages of 128 bytes per group
+constexpr int kSlabMaxQ = 2;        // pieces per slot at most
+
+struct SlabPlan {
+  int on;                        // 1 = the peers' chunks are copied and waited for by K slab
+  int groups;                    // groups of K per row: ceil(K bytes / kSlabRowBytes)
+  int ppc;                       // pieces per chunk and group: ceil(nc / kSlabRows)
+  int q;                         // pieces per slot (1 .. kSlabMaxQ)
+  int pre;                       // slots copied before the first tile
+  int total;                     // pieces of the call: groups * n_peer * ppc
+  long long help_ticks;          // wall-clock ticks a tile waits before copying missing pieces
+  int* flags;                    // [n_peer][groups][ppc] epochs
+};
+
 // Arguments of the counter-gated AG+GEMM kernel.  Chunk positions j = 0..tp-1 are the ring order
 // at this rank (position 0 = own chunk).
 struct AgArgs {
@@ -82,6 +108,7 @@ struct AgArgs {
   int copy_stride;               // workgroups w with (w / 8) % copy_stride == 0 copy
   int compute;                   // 0 = copies only, no tiles
   CopyPlan cp;
+  SlabPlan slab;                 // slab.on: the peers' copies (cp 0 .. n_peer-1) go by K slab
 };
 
 // Arguments of the GEMM+RS kernel.  Row-chunk positions j = 0..tp-1 in visiting order; the last
@@ -165,8 +192,10 @@ hipError_t launch_gemm_rs(int device, const RsArgs& a, int tile, int grid, hipSt
                           hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 hipError_t launch_arrival(int device, const ArrivalArgs& a, int grid, hipStream_t stream);
 
-// Entry-point names (launch.cpp).
-const char* ag_kernel_name(int tile, bool fp8, bool out8 = false);
+// Entry-point names (launch.cpp); "" when there is none (slab: the K-slab-gated form).
+const char* ag_kernel_name(int tile, bool fp8, bool out8 = false, bool slab = false);
+// Whether a tile configuration has K-slab-gated kernels.
+bool ag_slab_tile(int tile);
 const char* rs_kernel_name(int tile);
 
 // Occupancy / resource facts for a kernel variant (cached by the caller).

@@ -39,6 +39,11 @@ const char* const kAgName[2][2][kTiles] = {   // [fp8 input][fp8 output][tile]
       "rag_ag_fp8_t256x256w8", "rag_ag_fp8_t256x256w8s4", "rag_ag_fp8_t256x192w8"},
      {nullptr, "rag_ag_fp8_o8_t128x128", "rag_ag_fp8_o8_t256x128", "rag_ag_fp8_o8_t256x256",
       "rag_ag_fp8_o8_t256x256w8", "rag_ag_fp8_o8_t256x256w8s4", "rag_ag_fp8_o8_t256x192w8"}}};
+const char* const kAgSlabName[2][kTiles] = {   // [fp8 output][tile], bf16 input
+    {nullptr, nullptr, nullptr, nullptr, "rag_ag_bf16_slab_t256x256w8", nullptr,
+     "rag_ag_bf16_slab_t256x192w8"},
+    {nullptr, nullptr, nullptr, nullptr, "rag_ag_bf16_o8_slab_t256x256w8", nullptr,
+     "rag_ag_bf16_o8_slab_t256x192w8"}};
 const char* const kRsName[kTiles] = {nullptr, "rag_rs_t128x128", "rag_rs_t256x128",
                                      "rag_rs_t256x256", "rag_rs_t256x256w8",
                                      "rag_rs_t256x256w8s4", "rag_rs_t256x192w8"};
@@ -47,6 +52,7 @@ struct DeviceKernels {
   bool loaded = false;
   hipModule_t module = nullptr;
   hipFunction_t ag[2][2][kTiles] = {};
+  hipFunction_t ag_slab[2][kTiles] = {};
   hipFunction_t rs[kTiles] = {};
   hipFunction_t arrival = nullptr;
   int* scratch = nullptr;   // device address of the module's scratch array
@@ -86,9 +92,13 @@ hipError_t info(hipFunction_t f, int threads, KernelInfo* out) {
 
 }  // namespace
 
-const char* ag_kernel_name(int tile, bool fp8, bool out8) {
-  return valid_tile(tile) ? kAgName[fp8 ? 1 : 0][out8 ? 1 : 0][tile] : "";
+const char* ag_kernel_name(int tile, bool fp8, bool out8, bool slab) {
+  if (!valid_tile(tile)) return "";
+  if (slab) return (!fp8 && kAgSlabName[out8 ? 1 : 0][tile]) ? kAgSlabName[out8 ? 1 : 0][tile] : "";
+  return kAgName[fp8 ? 1 : 0][out8 ? 1 : 0][tile];
 }
+
+bool ag_slab_tile(int tile) { return valid_tile(tile) && kAgSlabName[0][tile] != nullptr; }
 
 const char* rs_kernel_name(int tile) { return valid_tile(tile) ? kRsName[tile] : ""; }
 
@@ -107,6 +117,11 @@ hipError_t load_kernels(int device) {
       for (int t = 1; t < kTiles; ++t)
         if ((e = hipModuleGetFunction(&d.ag[fp8][o8][t], m, kAgName[fp8][o8][t])) != hipSuccess)
           return e;
+  for (int o8 = 0; o8 < 2; ++o8)
+    for (int t = 1; t < kTiles; ++t)
+      if (kAgSlabName[o8][t] &&
+          (e = hipModuleGetFunction(&d.ag_slab[o8][t], m, kAgSlabName[o8][t])) != hipSuccess)
+        return e;
   for (int t = 1; t < kTiles; ++t)
     if ((e = hipModuleGetFunction(&d.rs[t], m, kRsName[t])) != hipSuccess) return e;
   if ((e = hipModuleGetFunction(&d.arrival, m, "rag_arrival")) != hipSuccess) return e;
@@ -136,8 +151,9 @@ hipError_t launch_ag_gemm(int device, const AgArgs& a, int tile, bool fp8, int g
   if (device < 0 || device >= kMaxDevices || !g_dev[device].loaded || !valid_tile(tile))
     return hipErrorInvalidValue;
   AgArgs copy = a;
-  return launch(g_dev[device].ag[fp8 ? 1 : 0][o8][tile], grid, tile_threads(tile), s, &copy,
-                ev_start, ev_stop);
+  hipFunction_t f = g_dev[device].ag[fp8 ? 1 : 0][o8][tile];
+  if (a.slab.on) f = fp8 ? nullptr : g_dev[device].ag_slab[o8][tile];
+  return launch(f, grid, tile_threads(tile), s, &copy, ev_start, ev_stop);
 }
 
 hipError_t launch_gemm_rs(int device, const RsArgs& a, int tile, int grid, hipStream_t s,

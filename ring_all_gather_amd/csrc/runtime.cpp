@@ -97,6 +97,8 @@ struct rag_ctx {
   size_t stage_bytes = 0;
   void* rsbuf = nullptr;        // receive buffer of the reduce-scatter's arrivals
   size_t rsbuf_bytes = 0;
+  int* slab_flags = nullptr;    // K-slab gating: per-piece epochs (zeroed when allocated)
+  size_t slab_flags_bytes = 0;
   int num_cus = 0;
   long long wall_khz = 100000;
   // options
@@ -110,6 +112,10 @@ struct rag_ctx {
   int wgs_per_cu = 0;
   int copy_priority = 1;
   int gemm_copy_wgs = 0;
+  int ag_gate = RAG_GATE_CHUNK;
+  // K-slab gating: how long a tile waits for a slab before it copies the slab's missing pieces
+  // itself (normally every slab is there long before a tile needs it)
+  long long slab_help_us = 20;
   unsigned long long trace_buf = 0;
   long long trace_bytes = 0;
   std::vector<hipEvent_t> t_start, t_stop;
@@ -326,7 +332,45 @@ struct AgPlan {
   int room_vgprs = 0;         // registers per lane the GEMM leaves for what it waits for
   int tile = 0, tiles_i = 0, tiles_j = 0, grid = 0;
   int late = 0;               // peers in the assisting kernel's late queue
+  SlabPlan slab = {};         // slab.on: K-slab gating (the in-GEMM copies of the peers' chunks)
 };
+
+// K-slab gating of a call (SlabPlan), when asked for and where it applies: the in-GEMM engine
+// copying the peers' chunks for a bf16 GEMM on an 8-wave 2-stage tile, no test hook that holds copies back, the
+// context's own device words, G 128-byte aligned (so that no 128-byte line holds two slabs), and
+// at most kSlabMaxQ pieces of each group per workgroup.  Slots hold q pieces: one piece per
+// workgroup and group of K when a group has at most `grid` pieces, else two.  `pre`: slots
+// copied before the first tile, enough that group 0 is complete and that every later group g is
+// flagged two stages before a tile reaches its gate (slot S(g) holds g's last piece; the K loop
+// flags slot pre + i at stage 4 i + 4 and gates group g at stage 4 g - 2).
+void plan_slab(const rag_ctx* c, int nc, int K, int tp, bool fp8, bool copy_only, bool ctx_words,
+               const void* G, AgPlan* p) {
+  SlabPlan& s = p->slab;
+  s = SlabPlan{};
+  if (c->ag_gate != RAG_GATE_SLAB || !p->gemm_copies || p->assist || fp8 || copy_only ||
+      !ctx_words || tp < 2 || !ag_slab_tile(p->tile) || c->delay_us > 0 || c->withhold != 0 ||
+      (reinterpret_cast<uintptr_t>(G) & 127u) != 0)
+    return;
+  const long long ldb = 2LL * K;
+  const int groups = (int)((ldb + kSlabRowBytes - 1) / kSlabRowBytes);
+  const int ppc = (nc + kSlabRows - 1) / kSlabRows;
+  const long long per_group = (long long)(tp - 1) * ppc;
+  const int q = per_group <= p->grid ? 1 : 2;
+  if (per_group > (long long)kSlabMaxQ * p->grid) return;
+  const long long per_slot = (long long)p->grid * q;
+  auto last_slot = [&](long long g) { return ((g + 1) * per_group + per_slot - 1) / per_slot - 1; };
+  long long pre = last_slot(0) + 1;
+  for (long long g = 1; g < groups; ++g) pre = std::max(pre, last_slot(g) - g + 2);
+  const long long total = per_group * groups;
+  if (pre > 4 || total > (1LL << 30)) return;
+  s.on = 1;
+  s.groups = groups;
+  s.ppc = ppc;
+  s.q = q;
+  s.pre = (int)pre;
+  s.total = (int)total;
+  s.help_ticks = c->slab_help_us * c->wall_khz / 1000;
+}
 
 int plan_ag(rag_ctx* c, int nc, int M, int tp, bool fp8, bool out8, bool no_copy, AgPlan* p) {
   const int engine = c->copy_engine;
@@ -874,6 +918,7 @@ int rag_destroy(rag_ctx* c) {
   if (c->gbuf) (void)hipFree(c->gbuf);
   if (c->stage) (void)hipFree(c->stage);
   if (c->rsbuf) (void)hipFree(c->rsbuf);
+  if (c->slab_flags) (void)hipFree(c->slab_flags);
   delete c;
   return RAG_OK;
 }
@@ -957,6 +1002,15 @@ int rag_set_option(rag_ctx* c, int key, long long v) {
     case RAG_OPT_GEMM_COPY_WGS:
       if (v < 0 || v > 65536) return fail(RAG_EINVAL, "GEMM copy workgroups must be in [0, 65536]");
       c->gemm_copy_wgs = (int)v;
+      return RAG_OK;
+    case RAG_OPT_AG_GATE:
+      if (v != RAG_GATE_CHUNK && v != RAG_GATE_SLAB)
+        return fail(RAG_EINVAL, "AG gate must be 0 (whole chunks) or 1 (K slabs), got %lld", v);
+      c->ag_gate = (int)v;
+      return RAG_OK;
+    case RAG_OPT_SLAB_HELP_US:
+      if (v < 0 || v > 10000000LL) return fail(RAG_EINVAL, "slab help time must be in [0, 1e7] us");
+      c->slab_help_us = v;
       return RAG_OK;
     case RAG_OPT_COPY_PRIORITY:
       if (v != 0 && v != 1) return fail(RAG_EINVAL, "copy priority must be 0 or 1");
@@ -1107,6 +1161,18 @@ int ag_call(rag_ctx* c, Words& W, const char* fn, const void* A, int M, int K,
     const int rc = plan_ag(c, nc, M, tp, fp8, out8, no_copy, &plan);
     if (rc) return rc;
   }
+  plan_slab(c, nc, K, tp, fp8, copy_only, &W == &c->w, Gp, &plan);
+  if (plan.slab.on) {
+    // the pieces' flags, zeroed when (re)allocated: they hold past epochs only
+    const size_t need = sizeof(int) * (size_t)(tp - 1) * plan.slab.groups * plan.slab.ppc;
+    if (c->slab_flags_bytes < need) {
+      int rc = ensure_buffer((void**)&c->slab_flags, &c->slab_flags_bytes, need,
+                             "slab flags");
+      if (rc) return rc;
+      HIPCHK(hipMemset(c->slab_flags, 0, need));
+    }
+    plan.slab.flags = c->slab_flags;
+  }
   const bool assist = plan.assist, gemm_copies = plan.gemm_copies, sdma = plan.sdma;
   const bool side_kernel = plan.side_kernel;
   const int tile = plan.tile, tiles_i = plan.tiles_i, tiles_j = plan.tiles_j, grid = plan.grid;
@@ -1247,6 +1313,7 @@ int ag_call(rag_ctx* c, Words& W, const char* fn, const void* A, int M, int K,
     a.scale_D = scale_D;
     a.amax_D = amax_D;
     a.cp = cp;
+    a.slab = plan.slab;
     a.tiles_i = tiles_i;
     a.tiles_j = tiles_j;
     const int total = tiles_i * tiles_j * tp;
@@ -1257,12 +1324,13 @@ int ag_call(rag_ctx* c, Words& W, const char* fn, const void* A, int M, int K,
     if (debug_enabled())
       fprintf(stderr, "[ringag] ag_gemm tp=%d s=%d nc=%d K=%d M=%d %s %s tiles=%d grid=%d "
               "(blocks/CU %d, VGPRs %d, LDS %d) engine=%s late=%d comm_wgs=%d pieces=%ux%u B "
-              "flags=0x%x epoch=%d\n",
-              tp, self_rank, nc, K, M, fp8 ? "fp8" : "bf16", ag_kernel_name(tile, fp8, out8),
-              total, grid,
+              "slab=%d (groups %d, pieces %d, q %d, pre %d) flags=0x%x epoch=%d\n",
+              tp, self_rank, nc, K, M, fp8 ? "fp8" : "bf16",
+              ag_kernel_name(tile, fp8, out8, a.slab.on != 0), total, grid,
               c->ag_info[tile][fp8][out8].max_blocks_per_cu,
               c->ag_info[tile][fp8][out8].vgprs_per_wave, c->ag_info[tile][fp8][out8].lds_bytes,
-              engine_name(engine), late, c->comm_wgs, cp.pieces, cp.piece_bytes, flags, epoch);
+              engine_name(engine), late, c->comm_wgs, cp.pieces, cp.piece_bytes, a.slab.on,
+              a.slab.groups, a.slab.total, a.slab.q, a.slab.pre, flags, epoch);
     hipEvent_t ev0, ev1;
     launch_timing_events(c, &ev0, &ev1);
     HIPCHK(launch_ag_gemm(c->device, a, tile, fp8, grid, stream, ev0, ev1));
@@ -1450,7 +1518,10 @@ int rag_ag_kernel_name(rag_ctx* c, int nc, int M, int tp, rag_dtype dt, char* bu
   AgPlan plan;
   const int rc = plan_ag(c, nc, M, tp, fp8, false, false, &plan);
   if (rc) return rc;
-  snprintf(buf, (size_t)len, "%s", ag_kernel_name(plan.tile, fp8));
+  // (a call with K = 64, G from the library's own buffer; slab gating does not depend on K
+  // otherwise)
+  plan_slab(c, nc, 64, tp, fp8, false, true, nullptr, &plan);
+  snprintf(buf, (size_t)len, "%s", ag_kernel_name(plan.tile, fp8, false, plan.slab.on != 0));
   return RAG_OK;
 }
 

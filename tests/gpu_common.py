@@ -39,6 +39,8 @@ def reset_options(c: B.Context):
     c.set_option(B.RAG_OPT_TILE, 0)
     c.set_option(B.RAG_OPT_COMM_CUS, 0)
     c.set_option(B.RAG_OPT_SDMA_STREAMS, 1)
+    c.set_option(B.RAG_OPT_AG_GATE, B.RAG_GATE_CHUNK)
+    c.set_option(B.RAG_OPT_SLAB_HELP_US, 20)
 
 
 def scale_tensor(s):

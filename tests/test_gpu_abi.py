@@ -98,6 +98,11 @@ def test_automatic_tile_choice_by_shape():
     try:
         assert c.ag_kernel_name(1024, 4096, 4) == "rag_ag_bf16_t256x256w8"   # 256 tiles: 1 round
         assert c.ag_kernel_name(1024, 3072, 8) == "rag_ag_bf16_t256x192w8"   # 512 vs 384 tiles
+        # (K-slab gating: the slab kernels of the same tiles)
+        c.set_option(B.RAG_OPT_AG_GATE, B.RAG_GATE_SLAB)
+        assert c.ag_kernel_name(1024, 4096, 4) == "rag_ag_bf16_slab_t256x256w8"
+        assert c.ag_kernel_name(1024, 3072, 8) == "rag_ag_bf16_slab_t256x192w8"
+        c.set_option(B.RAG_OPT_AG_GATE, B.RAG_GATE_CHUNK)
         assert c.ag_kernel_name(2048, 3584, 8, fp8=True) == "rag_ag_fp8_t256x256w8"
         assert c.rs_kernel_name(1024, 8192, 8) == "rag_rs_t256x256w8"        # 1024 tiles: 4 rounds
         assert c.ag_kernel_name(256, 1024, 2) == "rag_ag_bf16_t128x128"      # too few big tiles
@@ -122,7 +127,9 @@ def test_set_option_rejects_bad_values():
     say("case option validation")
     bad = [(B.RAG_OPT_COPY_ENGINE, 4), (B.RAG_OPT_COPY_ENGINE, -1), (B.RAG_OPT_COMM_CUS, 4),
            (B.RAG_OPT_COMM_CUS, 12), (B.RAG_OPT_COMM_CUS, 256), (B.RAG_OPT_SDMA_STREAMS, 0),
-           (B.RAG_OPT_SDMA_STREAMS, 4), (B.RAG_OPT_TILE, 99), (B.RAG_OPT_COMM_WGS, 0), (999, 1)]
+           (B.RAG_OPT_SDMA_STREAMS, 4), (B.RAG_OPT_TILE, 99), (B.RAG_OPT_COMM_WGS, 0),
+           (B.RAG_OPT_AG_GATE, 2), (B.RAG_OPT_AG_GATE, -1), (B.RAG_OPT_SLAB_HELP_US, -1),
+           (B.RAG_OPT_SLAB_HELP_US, 10_000_001), (999, 1)]
     for key, value in bad:
         rc = B.lib().rag_set_option(c.h, key, value)
         assert rc == B.RAG_EINVAL, (key, value, rc)

@@ -14,12 +14,15 @@ pytestmark = pytest.mark.gpu
 
 TILE_NAMES = ["128x128", "256x128", "256x256", "256x256w8", "256x256w8s4", "256x192w8"]
 # copy engines of the simulated arrival that run on compute units: the side-stream copy kernel, the
-# GEMM's own waiting workgroups, and both on one queue (SDMA is covered in the flags test)
-ENGINES = ["kernel", "in-gemm", "assist"]
+# GEMM's own workgroups (gating by chunk, or by K slab where that applies), and both on one queue
+# (SDMA is covered in the flags test)
+ENGINES = ["kernel", "in-gemm", "in-gemm-slab", "assist"]
 
 
 def set_engine(c, engine):
-    c.set_option(B.RAG_OPT_COPY_ENGINE, B.ENGINES[engine])
+    c.set_option(B.RAG_OPT_COPY_ENGINE, B.ENGINES[engine.replace("-slab", "")])
+    c.set_option(B.RAG_OPT_AG_GATE,
+                 B.RAG_GATE_SLAB if engine.endswith("-slab") else B.RAG_GATE_CHUNK)
 
 
 @pytest.fixture(autouse=True)
@@ -369,6 +372,74 @@ def test_ag_full_size_full_output(name, engine, placement):
     G = run.G.cpu()
     Gb = W.bits_u8(G) if shape.dtype == "fp8" else W.bits_u16(G)
     assert np.array_equal(Gb, G_ref)
+
+
+SLAB_TILES = ["256x256w8", "256x192w8"]
+# (K-slab gating needs a grid of at least half as many workgroups as a group has pieces, so the
+# narrow shapes have enough output columns to give it one)
+SLAB_CASES = [   # tp, s, nc, K, M
+    (2, 1, 16, 64, 80),       # one K stage: only group 0, one piece per chunk
+    (2, 0, 300, 320, 1100),   # rows not a multiple of 16; 640-byte rows: a 128-byte last group
+    (3, 2, 48, 576, 200),     # 9 stages: gates at stages 2 and 6, copy cycles in the K loop
+    (4, 1, 256, 1024, 2048),  # 16 stages
+    (8, 5, 100, 2048, 1100),  # ragged rows and columns, 7 peers
+    (16, 9, 64, 512, 300),    # 15 peers
+    (8, 3, 600, 320, 4000),   # more tiles than compute units: later rounds, copy slots carried over
+]
+
+
+@pytest.mark.parametrize("help_us", [20, 0])
+@pytest.mark.parametrize("tile", SLAB_TILES)
+@pytest.mark.parametrize("tp,s,nc,K,M", SLAB_CASES)
+def test_ag_slab_gating_exact(tp, s, nc, K, M, tile, help_us):
+    """K-slab gating (in-GEMM engine, bf16, 8-wave 2-stage tiles): exact integers, G and D bit for
+    bit, on shapes that exercise ragged rows and groups, one and many rounds and up to 15 peers.
+    help_us = 0: a tile copies a slab's missing pieces itself as soon as it finds one (the path
+    that keeps the launch going when the owners of pieces are late)."""
+    c = ctx()
+    set_engine(c, "in-gemm-slab")
+    c.set_option(B.RAG_OPT_TILE, B.TILES[tile])
+    c.set_option(B.RAG_OPT_SLAB_HELP_US, help_us)
+    assert "_slab_" in c.ag_kernel_name(nc, M, tp)
+    inp = _int_case(tp, s, nc, K=K, M=M, seed=5000 + tp * 37 + nc + K)
+    say(f"case slab tp={tp} s={s} nc={nc} K={K} M={M} tile={tile} help_us={help_us}")
+    for own_in_g in (False, True):
+        run = AGRun(inp, own_in_g=own_in_g)
+        run.run(c)
+        c.check()
+        G_ref, ref = oracle_ag(inp)
+        assert np.array_equal(W.bits_u16(run.G.cpu()), G_ref)
+        assert np.array_equal(run.D_bits(), O.f32_to_bf16(ref))
+
+
+def test_ag_slab_fresh_data_poisoned_g():
+    """The full-size ag_4k shape under K-slab gating, 24 calls back to back on one G that is
+    refilled with NaN before each call, alternating two input sets: a tile that read a slab before
+    its pieces landed, or a stale line of the previous call, would put NaN or the other set's
+    product into D."""
+    c = ctx()
+    set_engine(c, "in-gemm-slab")
+    base = W.WORKLOADS["ag_4k"]
+    assert "_slab_" in c.ag_kernel_name(base.nc, base.M, base.tp)
+    sets = []
+    for seed in (base.seed, base.seed + 1):
+        shape = W.ag_shape(base.tp, base.self_rank, base.nc, base.K, base.M,
+                           dist="normal_sqrtk", seed=seed)
+        inp = W.make_ag(shape)
+        _, ref = cached(("ag_4k_seed", seed), lambda: oracle_ag(inp))
+        sets.append((AGRun(inp), ref))
+    G = torch.empty_like(sets[0][0].G)
+    for i in range(24):
+        run, ref = sets[i % 2]
+        say(f"case slab fresh data call {i}")
+        G.fill_(float("nan"))
+        run.D.fill_(float("nan"))
+        s = run.inp.shape
+        B.ag_gemm(c, run.A, run.chunks, s.tp, s.self_rank, run.D, G=G)
+        torch.cuda.synchronize()
+        err = rel_err(run.D_bits(), ref)
+        assert err <= TOL_BF16, (i, err)
+    c.check()
 
 
 SPLIT_CASES = [(1, 0, 48), (2, 1, 256), (3, 2, 300), (4, 1, 256), (8, 5, 48)]
