@@ -60,6 +60,9 @@ __device__ __forceinline__ void ag_gemm_body(const AgArgs& a) {
   const i32x4 ry = make_rsrc(a.A, (uint32_t)a.M * ldb);
   if (a.copies) copy_queue_begin(a.cp);
   const bool copier = a.copies && ((blockIdx.x >> 3) % a.copy_stride) == 0;
+  // the software-pipelined copy holds two register sets; the 4-wave 256x256 tile (128x128 per
+  // wave, 256 accumulator registers) spills without them already, so it copies with the plain loop
+  constexpr bool kPipe = !(S::NW == 4 && S::FI * S::FJ >= 16);
   constexpr bool slab = SLAB;
   int slot = 0;   // slab gating: this workgroup's next slot of pieces
   if (slab) {
@@ -80,8 +83,8 @@ __device__ __forceinline__ void ag_gemm_body(const AgArgs& a) {
       slab_gate_tile(a, j - 1, ldb, &s_gate);
     } else if (a.ctr_index[j] >= 0) {
       if (copier) {
-        run_copy_queue<S::NT>(a.cp, a.ctr, a.epoch, 0, a.ctr_index[j], &s_piece);
-        run_copy_queue<S::NT>(a.cp, a.ctr, a.epoch, 2, a.ctr_index[j], &s_piece);
+        run_copy_queue<S::NT, 8, kPipe>(a.cp, a.ctr, a.epoch, 0, a.ctr_index[j], &s_piece);
+        run_copy_queue<S::NT, 8, kPipe>(a.cp, a.ctr, a.epoch, 2, a.ctr_index[j], &s_piece);
       }
       if (threadIdx.x == 0)
         s_ok = wait_ready(a.ctr + a.ctr_index[j] * kWordStride, a.epoch, a.err, a.spin_limit);
@@ -133,10 +136,10 @@ __device__ __forceinline__ void ag_gemm_body(const AgArgs& a) {
   if (slab) slab_copy_slots(a, slot, max(slot, slab_slots_end(a)), ldb);
   if (copier) {
     if (!slab) {
-      run_copy_queue<S::NT>(a.cp, a.ctr, a.epoch, 0, -1, &s_piece);
-      run_copy_queue<S::NT>(a.cp, a.ctr, a.epoch, 2, -1, &s_piece);
+      run_copy_queue<S::NT, 8, kPipe>(a.cp, a.ctr, a.epoch, 0, -1, &s_piece);
+      run_copy_queue<S::NT, 8, kPipe>(a.cp, a.ctr, a.epoch, 2, -1, &s_piece);
     }
-    run_copy_queue<S::NT>(a.cp, a.ctr, a.epoch, 1, -1, &s_piece);
+    run_copy_queue<S::NT, 8, kPipe>(a.cp, a.ctr, a.epoch, 1, -1, &s_piece);
   }
   // With the copies on another stream, which the caller's stream does not wait for, the kernel
   // ends only once the last copy (the own chunk into G) is complete, so that everything enqueued
