@@ -429,7 +429,7 @@ def main():
                          "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                          "kernel": kname, "kernel_ms": round(kernel_ms, 5)},
         }
-        if not (args.no_timeline or args.headline_only):
+        if not args.no_timeline:
             out["timeline"] = timeline_ag(ctx, B, step, shape, kname)
         # the gathered buffer must hold every chunk at its rank offset, bit for bit
         G_ok = all(torch.equal(G[r * shape.nc:(r + 1) * shape.nc].view(torch.uint8),
