@@ -57,7 +57,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=1000)
     p.add_argument("--workload", default="ag_4k")
     p.add_argument("--copy-engine", default=os.environ.get("RAG_COPY_ENGINE", "in-gemm"),
-                   choices=["kernel", "sdma", "in-gemm", "in-gemm-slab", "assist"])
+                   choices=["kernel", "sdma", "in-gemm", "in-gemm-slab", "assist", "in-gemm-sdma"])
     p.add_argument("--comm-cus", type=int, default=0,
                    help="compute units the side stream's copy kernels are limited to (0 = all)")
     p.add_argument("--sdma-streams", type=int, default=1,
@@ -283,8 +283,8 @@ def overlap_per_engine(ctx, B, step, args, stream, shape, ms_head):
     side-stream kernel engine may pick another kernel of the same tile size, see the library's
     tile choice), so the three times are of the same kernel."""
     names = [args.copy_engine] + ([] if args.headline_only else
-                                  [e for e in ("in-gemm", "in-gemm-slab", "assist", "kernel",
-                                               "sdma") if e != args.copy_engine])
+                                  [e for e in ("in-gemm", "in-gemm-slab", "assist", "in-gemm-sdma",
+                                               "kernel", "sdma") if e != args.copy_engine])
     res = {}
     for eng in names:
         set_engine(ctx, B, eng)

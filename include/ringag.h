@@ -126,11 +126,18 @@ enum {
                               RAG_RS_ARRIVE for the GEMM+RS form).  With K-slab gating
                               (RAG_OPT_AG_GATE), every workgroup copies its share of slab pieces
                               instead, and a tile waits only for the slab it loads next */
-    RAG_COPY_IN_GEMM_ASSIST = 3 /* AG+GEMM: as RAG_COPY_IN_GEMM, and a copy kernel on the side
+    RAG_COPY_IN_GEMM_ASSIST = 3, /* AG+GEMM: as RAG_COPY_IN_GEMM, and a copy kernel on the side
                               stream takes pieces from the same queue beside the GEMM
                               (RAG_OPT_COMM_WGS workgroups): the chunks that only later rounds of
                               the GEMM need are copied while the first round computes, instead of
                               at the round boundary.  GEMM+RS calls treat it as RAG_COPY_IN_GEMM */
+    RAG_COPY_IN_GEMM_SDMA = 4  /* AG+GEMM: as RAG_COPY_IN_GEMM for the chunks the first round of the
+                              GEMM reads, and SDMA (as RAG_COPY_SDMA, over RAG_OPT_SDMA_STREAMS
+                              streams) for the chunks only later rounds read: those are copied in
+                              the background while the first round computes, on no compute unit.
+                              The GEMM leaves room for the runtime's write-value kernel as with
+                              RAG_COPY_SDMA.  One round: the same as RAG_COPY_IN_GEMM.  GEMM+RS
+                              calls treat it as RAG_COPY_IN_GEMM */
 };
 
 /* Option keys for rag_set_option. */

@@ -35,8 +35,9 @@ RAG_OPT_GEMM_COPY_WGS, RAG_OPT_COMM_CUS, RAG_OPT_SDMA_STREAMS, RAG_OPT_AG_GATE =
 RAG_OPT_SLAB_HELP_US = 16
 RAG_GATE_CHUNK, RAG_GATE_SLAB = 0, 1
 RAG_COPY_KERNEL, RAG_COPY_SDMA, RAG_COPY_IN_GEMM, RAG_COPY_IN_GEMM_ASSIST = 0, 1, 2, 3
+RAG_COPY_IN_GEMM_SDMA = 4
 ENGINES = {"kernel": RAG_COPY_KERNEL, "sdma": RAG_COPY_SDMA, "in-gemm": RAG_COPY_IN_GEMM,
-           "assist": RAG_COPY_IN_GEMM_ASSIST}
+           "assist": RAG_COPY_IN_GEMM_ASSIST, "in-gemm-sdma": RAG_COPY_IN_GEMM_SDMA}
 TRACE_HEADER, TRACE_START, TRACE_TILE_WORDS = 64, 32, 5
 TILES = {"auto": 0, "128x128": 1, "256x128": 2, "256x256": 3, "256x256w8": 4, "256x256w8s4": 5,
          "256x192w8": 6}

@@ -4,11 +4,21 @@
 //
 // TransformerEngine issue #1583, C++ listing: each ring step copies one chunk into the gathered
 // buffer and then bumps that chunk's counter.  Here a chunk is cut into pieces; workgroups take
-// pieces in ring order with an atomic, copy them, and add them to the chunk's done count with one
-// agent-scope release each (which writes the copying XCD's L2 back).  The add that completes the
-// count releases the chunk's counter, after an acquire fence that orders every other workgroup's
-// pieces before it.  Whoever takes a piece copies it without waiting on anything, so every
-// chunk's count completes even when not all workgroups are resident.
+// pieces in ring order with an atomic, copy them, and add them to the chunk's done count.  The
+// add that completes the count stores the chunk's counter.  Whoever takes a piece copies it
+// without waiting on anything, so every chunk's count completes even when not all workgroups are
+// resident.
+//
+// Visibility of the copied bytes: the pieces are stored with the agent-scope write-through policy
+// (kCopyStorePolicy), every wave waits until its stores are complete before the workgroup's
+// barrier, and only then does thread 0 add to the done count, an agent-scope atomic.  A store of
+// that policy is visible device-wide once it is complete (it is how the memory model's own
+// agent-scope atomic stores are built), so the count and the counter need no release: a release
+// would add an L2 write-back of the copying XCD, which covers only lines that were not written
+// through, and these copies leave none.  That write-back took about 2.3 us per piece whether or
+// not there was anything to write, against ~4 us to copy a 128 KiB piece (copies-only ag_qkv 49
+// -> 38 us, chunked 391 -> 359 us without it).  The consumer still takes an acquire fence after
+// it sees the counter (wait_ready), which drops any stale line of the slot from its XCD's L2.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -22,9 +32,9 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // Wait until *ctr == epoch.  Returns false when the limit passed or another tile of this call
 // already gave up (then *err == epoch).  The loop polls with relaxed agent-scope loads, which
 // read the counter coherently without touching the caches; a single acquire fence after the
-// value is seen orders the tile's loads of the chunk after the producer's release.  (An acquire
-// load in the loop would invalidate this CU's cache lines on every poll, slowing the tiles and the
-// copies that share the XCD.)
+// value is seen orders the tile's loads of the chunk after the producer's counter store.  (An
+// acquire load in the loop would invalidate this CU's cache lines on every poll, slowing the
+// tiles and the copies that share the XCD.)
 __device__ inline bool wait_ready(int* ctr, int epoch, int* err, long long limit) {
   bool ok = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
   if (!ok) {
@@ -47,9 +57,9 @@ __device__ inline bool wait_ready(int* ctr, int epoch, int* err, long long limit
 }
 
 // Cache policy of the copies' stores: sc1, agent scope.  The data is written through the copying
-// XCD's L2 to the point where every XCD sees it, instead of staying dirty in that L2 until the
-// piece's agent-scope release writes the L2 back; the release then has little left to flush.
-// (ag_4k: copies-only launch 21.1 -> 18.0 us, chunked call 125.0 -> 120.6 us.)
+// XCD's L2 to the point where every XCD sees it, instead of staying dirty in that L2 (ag_4k:
+// copies-only launch 21.1 -> 18.0 us, chunked call 125.0 -> 120.6 us, when each piece still ended
+// with a release that wrote the L2 back).
 constexpr int kCopyStorePolicy = 16;
 
 // Copy piece k of copy c with the NT threads of the workgroup (16-byte vectors, U in flight per
@@ -120,14 +130,14 @@ __device__ __forceinline__ void copy_piece(const CopyPlan& p, unsigned c, unsign
     __builtin_amdgcn_raw_buffer_store_b128(s[i], d, (int)(i * 16), 0, kCopyStorePolicy);
 }
 
-// Thread 0, after the workgroup's stores of `count` pieces of copy c are complete: add them to the
-// copy's done count; the add that completes it releases the copy's counter.
+// Thread 0, after the stores of `count` pieces of copy c by every wave of the workgroup are
+// complete: add them to the copy's done count; the add that completes it stores the copy's
+// counter (see the head of this file for why both are relaxed).
 __device__ inline void pieces_done(const CopyPlan& p, int* ctr, int epoch, unsigned c,
                                    unsigned count) {
-  const unsigned old = __hip_atomic_fetch_add(p.done + c * kWordStride, count, __ATOMIC_RELEASE,
+  const unsigned old = __hip_atomic_fetch_add(p.done + c * kWordStride, count, __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_AGENT);
   if (old + count != p.pieces) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if (p.delay_ticks > 0) {
     const unsigned long long t0 = wall_clock64();
     while ((long long)(wall_clock64() - t0) < p.delay_ticks) __builtin_amdgcn_s_sleep(8);
@@ -136,7 +146,7 @@ __device__ inline void pieces_done(const CopyPlan& p, int* ctr, int epoch, unsig
   // may read the trace)
   if (p.trace) p.trace[c] = wall_clock64();
   if (p.ctr_index[c] >= 0 && (p.pos[c] == 0 || !((p.withhold_mask >> p.pos[c]) & 1u)))
-    __hip_atomic_store(ctr + p.ctr_index[c] * kWordStride, epoch, __ATOMIC_RELEASE,
+    __hip_atomic_store(ctr + p.ctr_index[c] * kWordStride, epoch, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
 }
 

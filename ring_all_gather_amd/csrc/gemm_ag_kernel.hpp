@@ -84,7 +84,8 @@ __device__ __forceinline__ void ag_gemm_body(const AgArgs& a) {
     } else if (a.ctr_index[j] >= 0) {
       if (copier) {
         run_copy_queue<S::NT, 8, kPipe>(a.cp, a.ctr, a.epoch, 0, a.ctr_index[j], &s_piece);
-        run_copy_queue<S::NT, 8, kPipe>(a.cp, a.ctr, a.epoch, 2, a.ctr_index[j], &s_piece);
+        if (!a.cp.late_external)
+          run_copy_queue<S::NT, 8, kPipe>(a.cp, a.ctr, a.epoch, 2, a.ctr_index[j], &s_piece);
       }
       if (threadIdx.x == 0)
         s_ok = wait_ready(a.ctr + a.ctr_index[j] * kWordStride, a.epoch, a.err, a.spin_limit);
@@ -137,7 +138,8 @@ __device__ __forceinline__ void ag_gemm_body(const AgArgs& a) {
   if (copier) {
     if (!slab) {
       run_copy_queue<S::NT, 8, kPipe>(a.cp, a.ctr, a.epoch, 0, -1, &s_piece);
-      run_copy_queue<S::NT, 8, kPipe>(a.cp, a.ctr, a.epoch, 2, -1, &s_piece);
+      if (!a.cp.late_external)
+        run_copy_queue<S::NT, 8, kPipe>(a.cp, a.ctr, a.epoch, 2, -1, &s_piece);
     }
     run_copy_queue<S::NT, 8, kPipe>(a.cp, a.ctr, a.epoch, 1, -1, &s_piece);
   }

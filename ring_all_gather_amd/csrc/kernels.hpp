@@ -46,6 +46,8 @@ struct CopyPlan {
   int pos[kArrSlots];            // ring position of copy c (withhold hook); 0 = the own chunk
   int n_peer, n;
   int late;                      // the last `late` of the n_peer peer copies form queue 2
+  int late_external;             // 1 = SDMA copies queue 2 (and releases its counters): no
+                                 // kernel takes its pieces
   unsigned long long bytes;      // bytes per copy, multiple of 16
   unsigned pieces;               // pieces per copy: ceil(bytes / piece_bytes)
   unsigned piece_bytes;          // multiple of 16

@@ -248,9 +248,15 @@ int choose_ag_tile(const rag_ctx* c, int nc, int M, int tp) {
   return kTile128x128;
 }
 
+// The engines whose copies run inside the GEMM launch (GEMM+RS calls treat all three alike).
+bool in_gemm_engine(int e) {
+  return e == RAG_COPY_IN_GEMM || e == RAG_COPY_IN_GEMM_ASSIST || e == RAG_COPY_IN_GEMM_SDMA;
+}
+
 const char* engine_name(int e) {
   return e == RAG_COPY_SDMA ? "sdma" : e == RAG_COPY_IN_GEMM ? "in-gemm"
-         : e == RAG_COPY_IN_GEMM_ASSIST ? "in-gemm+assist" : "kernel";
+         : e == RAG_COPY_IN_GEMM_ASSIST ? "in-gemm+assist"
+         : e == RAG_COPY_IN_GEMM_SDMA ? "in-gemm+sdma" : "kernel";
 }
 
 // Persistent grid: every workgroup resident at once (so none waits for a slot while others spin
@@ -329,9 +335,10 @@ struct AgPlan {
   bool side_kernel = false;   // a copy kernel runs on the side stream
   bool sdma = false;          // SDMA copies on the side streams
   bool assist = false;
+  bool hybrid = false;        // in-GEMM copies of the early chunks, SDMA for the late ones
   int room_vgprs = 0;         // registers per lane the GEMM leaves for what it waits for
   int tile = 0, tiles_i = 0, tiles_j = 0, grid = 0;
-  int late = 0;               // peers in the assisting kernel's late queue
+  int late = 0;               // peers in the late queue (assisting kernel or SDMA)
   SlabPlan slab = {};         // slab.on: K-slab gating (the in-GEMM copies of the peers' chunks)
 };
 
@@ -375,21 +382,26 @@ void plan_slab(const rag_ctx* c, int nc, int K, int tp, bool fp8, bool copy_only
 int plan_ag(rag_ctx* c, int nc, int M, int tp, bool fp8, bool out8, bool no_copy, AgPlan* p) {
   const int engine = c->copy_engine;
   p->assist = !no_copy && engine == RAG_COPY_IN_GEMM_ASSIST;
-  p->gemm_copies = !no_copy && (engine == RAG_COPY_IN_GEMM || p->assist);
+  p->hybrid = !no_copy && engine == RAG_COPY_IN_GEMM_SDMA;
+  p->gemm_copies = !no_copy && (engine == RAG_COPY_IN_GEMM || p->assist || p->hybrid);
   p->side_kernel = !no_copy && (engine == RAG_COPY_KERNEL || p->assist);
-  p->sdma = !no_copy && engine == RAG_COPY_SDMA;
+  p->sdma = !no_copy && (engine == RAG_COPY_SDMA || p->hybrid);
   int copy_vgprs = 0;
   if (p->side_kernel) {
     const int rc = copy_wave_vgprs(c, &copy_vgprs);
     if (rc) return rc;
   }
-  // With the assisting copy kernel: the chunks at ring positions the first round of the grid does
-  // not reach (P = ceil(grid / U) and on) are the late queue, which the copy kernel takes beside
-  // the first round; the GEMM's waiting workgroups copy the early ones.  Without late chunks (one
-  // round holds every chunk) no copy kernel is launched and the call is the in-GEMM one.
+  // With the assisting copy kernel, or SDMA for the late chunks: the chunks at ring positions the
+  // first round of the grid does not reach (P = ceil(grid / U) and on) are the late queue, which
+  // the copy kernel or SDMA takes beside the first round; the GEMM's waiting workgroups copy the
+  // early ones.  Without late chunks (one round holds every chunk) nothing runs beside the GEMM
+  // and the call is the in-GEMM one.  The first pass plans the GEMM with nothing beside it; when
+  // there are late chunks the second plans it with the room the side kernel needs (which may
+  // change the tile, and so the late queue).
   for (int pass = 0; pass < 2; ++pass) {
     const bool beside = p->side_kernel && !(p->assist && pass == 0);
-    p->room_vgprs = beside ? copy_vgprs : p->sdma ? kStreamOpVgprs : 0;
+    const bool sdma_beside = p->sdma && !(p->hybrid && pass == 0);
+    p->room_vgprs = beside ? copy_vgprs : sdma_beside ? kStreamOpVgprs : 0;
     int rc = ag_launch_tile(c, nc, M, tp, fp8, out8, p->room_vgprs, &p->tile);
     if (rc) return rc;
     const KernelInfo* info = nullptr;
@@ -403,11 +415,12 @@ int plan_ag(rag_ctx* c, int nc, int M, int tp, bool fp8, bool out8, bool no_copy
     if (c->wgs_per_cu > 0) bpc = std::min(bpc, c->wgs_per_cu);
     p->grid = persistent_grid(p->tiles_i * p->tiles_j * tp,
                               c->num_cus - reserved_cus(*info, p->room_vgprs), bpc);
-    if (!p->assist) break;
+    if (!p->assist && !p->hybrid) break;
     const int U = p->tiles_i * p->tiles_j;
     p->late = std::max(0, tp - std::max(1, (p->grid + U - 1) / U));
     if (p->late == 0) {
       p->side_kernel = false;
+      p->sdma = false;
       break;
     }
   }
@@ -699,7 +712,7 @@ int rs_call(rag_ctx* c, const char* fn, bool ring, const void* X, int T, int Kl,
   // extra_copies (linear_allreduce's gather, not gated): copies with nothing waiting for them on
   // the device, run by the same launch
   const bool ig_engine =
-      c->copy_engine == RAG_COPY_IN_GEMM || c->copy_engine == RAG_COPY_IN_GEMM_ASSIST;
+      in_gemm_engine(c->copy_engine);
   const bool in_gemm = (a.gated && ig_engine && !other_copies_beside) || extra_copies != nullptr;
   bool join = false;
   if (a.gated) {
@@ -928,9 +941,10 @@ int rag_set_option(rag_ctx* c, int key, long long v) {
   switch (key) {
     case RAG_OPT_COPY_ENGINE:
       if (v != RAG_COPY_KERNEL && v != RAG_COPY_SDMA && v != RAG_COPY_IN_GEMM &&
-          v != RAG_COPY_IN_GEMM_ASSIST)
-        return fail(RAG_EINVAL, "copy engine must be 0 (kernel), 1 (sdma), 2 (in the GEMM) or 3 "
-                    "(in the GEMM with a copy kernel assisting), got %lld", v);
+          v != RAG_COPY_IN_GEMM_ASSIST && v != RAG_COPY_IN_GEMM_SDMA)
+        return fail(RAG_EINVAL, "copy engine must be 0 (kernel), 1 (sdma), 2 (in the GEMM), 3 "
+                    "(in the GEMM with a copy kernel assisting) or 4 (in the GEMM with SDMA for "
+                    "the late chunks), got %lld", v);
       c->copy_engine = (int)v;
       return RAG_OK;
     case RAG_OPT_COMM_CUS: {
@@ -1130,8 +1144,9 @@ int ag_call(rag_ctx* c, Words& W, const char* fn, const void* A, int M, int K,
     return fail(RAG_EINVAL, "%s: the own chunk may only sit in G at its own slot", fn);
   if ((flags & RAG_NO_COPY) && !G && !c->gbuf)
     return fail(RAG_EINVAL, "%s: RAG_NO_COPY reads the chunks from G; pass G", fn);
-  if (c->copy_engine == RAG_COPY_SDMA && c->delay_us > 0 && !(flags & RAG_NO_COPY))
-    return fail(RAG_EINVAL, "%s: the arrival delay hook needs the kernel copy engine", fn);
+  if ((c->copy_engine == RAG_COPY_SDMA || c->copy_engine == RAG_COPY_IN_GEMM_SDMA) &&
+      c->delay_us > 0 && !(flags & RAG_NO_COPY))
+    return fail(RAG_EINVAL, "%s: the arrival delay hook needs a compute-unit copy engine", fn);
 
   HIPCHK(hipSetDevice(c->device));
   hipStream_t stream = (hipStream_t)stream_v;
@@ -1175,6 +1190,9 @@ int ag_call(rag_ctx* c, Words& W, const char* fn, const void* A, int M, int K,
   }
   const bool assist = plan.assist, gemm_copies = plan.gemm_copies, sdma = plan.sdma;
   const bool side_kernel = plan.side_kernel;
+  // SDMA beside in-GEMM copies takes only the late peers; the GEMM's workgroups copy the rest
+  // (the early peers, the own chunk, B_copy)
+  const bool hybrid = plan.hybrid && sdma;
   const int tile = plan.tile, tiles_i = plan.tiles_i, tiles_j = plan.tiles_j, grid = plan.grid;
   const int late = plan.late;
   const bool side = side_kernel || sdma;
@@ -1216,8 +1234,8 @@ int ag_call(rag_ctx* c, Words& W, const char* fn, const void* A, int M, int K,
       cp.dst[n] = Gp + (size_t)self_rank * chunk_bytes;
       // when something on a side stream may copy it, the GEMM waits for it before exiting (with
       // B_copy too, or with no GEMM, the caller's stream waits for the side streams instead);
-      // when only the GEMM's own workgroups copy, they finish it before the launch ends
-      cp.ctr_index[n] = (copy_only || !side || B_copy) ? -1 : c->max_tp;
+      // when only the GEMM's own workgroups copy it, they finish it before the launch ends
+      cp.ctr_index[n] = (copy_only || !side || hybrid || B_copy) ? -1 : c->max_tp;
       cp.pos[n] = 0;
       ++n;
     }
@@ -1230,6 +1248,7 @@ int ag_call(rag_ctx* c, Words& W, const char* fn, const void* A, int M, int K,
     }
     cp.n = n;
     cp.late = late;
+    cp.late_external = hybrid ? 1 : 0;
     cp.bytes = (unsigned long long)chunk_bytes;
     // a piece is two rounds of 8 16-byte vectors per thread of the GEMM's copying workgroups
     // (or of the copy kernel's, when only it copies)
@@ -1247,7 +1266,10 @@ int ag_call(rag_ctx* c, Words& W, const char* fn, const void* A, int M, int K,
     if (rc) return rc;
   }
   bool copied = false;   // a launch used this call's set of piece counts
-  const int nsdma = sdma ? std::min(c->sdma_streams, std::max(1, cp.n)) : 0;
+  // the copies SDMA makes: all of them, or with in-GEMM copies beside only the late peers
+  const int sdma_first = hybrid ? cp.n_peer - late : 0;
+  const int sdma_end = hybrid ? cp.n_peer : cp.n;
+  const int nsdma = sdma ? std::min(c->sdma_streams, std::max(1, sdma_end - sdma_first)) : 0;
   if (side) {
     HIPCHK(hipEventRecord(c->ev_fork, stream));
     HIPCHK(hipStreamWaitEvent(c->side, c->ev_fork, 0));
@@ -1267,8 +1289,9 @@ int ag_call(rag_ctx* c, Words& W, const char* fn, const void* A, int M, int K,
     } else {
       // SDMA: copy k on side stream k mod nsdma, each followed by its counter's release
       for (int q = 1; q < nsdma; ++q) HIPCHK(hipStreamWaitEvent(c->sdma[q - 1], c->ev_fork, 0));
-      for (int k = 0; k < cp.n; ++k) {
-        hipStream_t sk = (k % nsdma == 0) ? c->side : c->sdma[k % nsdma - 1];
+      for (int k = sdma_first; k < sdma_end; ++k) {
+        const int q = (k - sdma_first) % nsdma;
+        hipStream_t sk = q == 0 ? c->side : c->sdma[q - 1];
         HIPCHK(hipMemcpyAsync(cp.dst[k], cp.src[k], (size_t)chunk_bytes,
                               hipMemcpyDeviceToDeviceNoCU, sk));
         if (cp.ctr_index[k] >= 0 && (cp.pos[k] == 0 || !((c->withhold >> cp.pos[k]) & 1u)))
@@ -1300,7 +1323,7 @@ int ag_call(rag_ctx* c, Words& W, const char* fn, const void* A, int M, int K,
     a.nc = nc;
     a.tp = tp;
     a.ctr = W.ctr;
-    a.join_index = (own_copy && side && !B_copy && !copy_only) ? c->max_tp : -1;
+    a.join_index = (own_copy && side && !hybrid && !B_copy && !copy_only) ? c->max_tp : -1;
     a.epoch = epoch;
     a.err = W.err;
     a.spin_limit = c->spin_us * c->wall_khz / 1000;
@@ -1440,7 +1463,7 @@ int linear_allreduce(rag_ctx* c, const void* X, int T, int Kl, const void* W, in
   // the all-gather.  With the in-GEMM engine and nothing gated, the GEMM+RS launch copies the
   // owners' reduced chunks itself (after its tiles' epilogues, in ring order); else a copy kernel
   // or SDMA on the side stream, forked before the GEMM so that the copies run beside it.
-  if (tp > 1 && (c->copy_engine == RAG_COPY_IN_GEMM || c->copy_engine == RAG_COPY_IN_GEMM_ASSIST) &&
+  if (tp > 1 && in_gemm_engine(c->copy_engine) &&
       !(flags & RAG_RS_ARRIVE)) {
     CopyPlan gp = {};
     int n = 0;

@@ -13,13 +13,13 @@
 //
 // Coherence.  A piece's stores go through the copying XCD's L2 to the device-wide point (the
 // agent-scope write-through policy of the chunk copies), and its flag is stored once every wave's
-// stores are complete.  The flags are read with agent-scope loads.  The tile then reads the slab
-// with ordinary loads: they cannot hit a stale line, because the tile took an agent-scope acquire
-// (which invalidates the XCD's L2) before its first load, and since then no workgroup of this call
-// has read a line of a slab before all of that slab's flags were set (lines are 128 bytes and a
-// slab is 512-byte aligned in G, so no line holds two slabs).  Per slab, this trades the release
-// and acquire fences of the chunk protocol (an L2 write-back and an L2 invalidate, each costing
-// microseconds when taken every few stages) for these two properties of the hardware.
+// stores are complete, as the chunk copies' counts are (copy_queue.hpp).  The flags are read with
+// agent-scope loads.  The tile then reads the slab with ordinary loads: they cannot hit a stale
+// line, because the tile took an agent-scope acquire (which invalidates the XCD's L2) before its
+// first load, and since then no workgroup of this call has read a line of a slab before all of
+// that slab's flags were set (lines are 128 bytes and a slab is 512-byte aligned in G, so no line
+// holds two slabs).  So the acquire the chunk protocol takes once per tile is not repeated per
+// slab, where an L2 invalidate every few stages would cost microseconds each time.
 //
 // Progress does not depend on which workgroups are resident: a tile that has waited help_ticks
 // for a slab copies the slab's missing pieces itself (a piece copied twice is written twice with

@@ -117,6 +117,13 @@ def test_automatic_tile_choice_by_shape():
         # keeps the in-GEMM kernel
         c.set_option(B.RAG_OPT_COPY_ENGINE, B.ENGINES["assist"])
         assert c.ag_kernel_name(1024, 4096, 4) == "rag_ag_bf16_t256x256w8"
+        # SDMA for the late chunks: the GEMM leaves the write-value kernel room where there are
+        # late chunks (fp8 ag_fc1_f8: the 4-stage tile; bf16 ag_qkv: the 256x192 kernel has room),
+        # and one round (ag_4k) is the in-GEMM call
+        c.set_option(B.RAG_OPT_COPY_ENGINE, B.ENGINES["in-gemm-sdma"])
+        assert c.ag_kernel_name(1024, 4096, 4) == "rag_ag_bf16_t256x256w8"
+        assert c.ag_kernel_name(1024, 3072, 8) == "rag_ag_bf16_t256x192w8"
+        assert c.ag_kernel_name(2048, 3584, 8, fp8=True) == "rag_ag_fp8_t256x256w8s4"
     finally:
         reset_options(c)
 
@@ -125,7 +132,7 @@ def test_set_option_rejects_bad_values():
     """Every option refuses out-of-range values with RAG_EINVAL and leaves the context usable."""
     c = ctx()
     say("case option validation")
-    bad = [(B.RAG_OPT_COPY_ENGINE, 4), (B.RAG_OPT_COPY_ENGINE, -1), (B.RAG_OPT_COMM_CUS, 4),
+    bad = [(B.RAG_OPT_COPY_ENGINE, 5), (B.RAG_OPT_COPY_ENGINE, -1), (B.RAG_OPT_COMM_CUS, 4),
            (B.RAG_OPT_COMM_CUS, 12), (B.RAG_OPT_COMM_CUS, 256), (B.RAG_OPT_SDMA_STREAMS, 0),
            (B.RAG_OPT_SDMA_STREAMS, 4), (B.RAG_OPT_TILE, 99), (B.RAG_OPT_COMM_WGS, 0),
            (B.RAG_OPT_AG_GATE, 2), (B.RAG_OPT_AG_GATE, -1), (B.RAG_OPT_SLAB_HELP_US, -1),

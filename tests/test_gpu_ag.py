@@ -158,14 +158,16 @@ def test_ag_flags_staged_copy_only_sdma(engine):
         set_engine(c, engine)
 
 
+@pytest.mark.parametrize("engine", ["assist", "in-gemm-sdma"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 @pytest.mark.parametrize("tp,s,wgs_per_cu", [(8, 3, 0), (8, 0, 1), (4, 2, 1), (16, 9, 0)])
-def test_ag_assist_late_queue_exact(tp, s, wgs_per_cu, dtype):
-    """Shapes whose GEMM needs several persistent rounds, so that the assisting copy kernel takes
-    the late chunks beside the first round while the GEMM's waiting workgroups copy the early
-    ones: exact integer parity, three calls back to back with fresh data, then an in-GEMM call."""
+def test_ag_late_queue_exact(tp, s, wgs_per_cu, dtype, engine):
+    """Shapes whose GEMM needs several persistent rounds, so that the late chunks are copied
+    beside the first round (by the assisting copy kernel, or by SDMA) while the GEMM's waiting
+    workgroups copy the early ones: exact integer parity, three calls back to back with fresh
+    data, then an in-GEMM call."""
     c = ctx()
-    set_engine(c, "assist")
+    set_engine(c, engine)
     c.set_option(B.RAG_OPT_TILE, B.TILES["128x128"])
     c.set_option(B.RAG_OPT_WGS_PER_CU, wgs_per_cu)
     runs = []
@@ -175,7 +177,7 @@ def test_ag_assist_late_queue_exact(tp, s, wgs_per_cu, dtype):
         inp = W.make_ag(W.ag_shape(tp, s, 512, 256, 4096, dtype=dtype, dist="int3",
                                    seed=80 + it + tp))
         runs.append((AGRun(inp), inp))
-    say(f"case assist late queue tp={tp} s={s} wgs/cu={wgs_per_cu} {dtype}")
+    say(f"case late queue {engine} tp={tp} s={s} wgs/cu={wgs_per_cu} {dtype}")
     for run, inp in runs:
         sh = inp.shape
         B.ag_gemm(c, run.A, run.chunks, sh.tp, sh.self_rank, run.D, G=run.G, scale_A=run.sA,
@@ -346,7 +348,9 @@ FULL_CASES = [(name, engine, placement) for name in ("ag_4k", "ag_qkv", "ag_fc1_
     # SDMA at full size: its counters are released by the runtime's write-value kernel, which the
     # GEMM must leave room for (with the fp8 256x256 8-wave kernel filling every SIMD, every wait
     # ran out its limit)
-    ("ag_fc1_f8", "sdma", "in-g"), ("ag_qkv", "sdma", "separate")]
+    ("ag_fc1_f8", "sdma", "in-g"), ("ag_qkv", "sdma", "separate"),
+    # the late chunks by SDMA beside in-GEMM copies of the early ones
+    ("ag_qkv", "in-gemm-sdma", "in-g"), ("ag_fc1_f8", "in-gemm-sdma", "separate")]
 
 
 @pytest.mark.parametrize("name,engine,placement", FULL_CASES)
@@ -566,6 +570,26 @@ def test_ag_fp8_output_staged_and_split():
         assert np.array_equal(codes, want)
         assert amax == want_amax
         assert np.array_equal(W.bits_u16(bc.cpu()), W.bits_u16(inp.chunks[2]))
+
+
+@pytest.mark.parametrize("tile", SLAB_TILES)
+def test_ag_slab_fp8_output_and_b_copy(tile):
+    """The E4M3-output K-slab kernels (rag_ag_bf16_o8_slab_*): codes and amax bit for bit on
+    integer data, B_copy and the own chunk's copy into G after the slab copies."""
+    c = ctx()
+    set_engine(c, "in-gemm-slab")
+    c.set_option(B.RAG_OPT_TILE, B.TILES[tile])
+    tp, s, nc, K, M = 4, 1, 256, 576, 2048
+    assert "_slab_" in c.ag_kernel_name(nc, M, tp)
+    inp = W.make_ag(W.ag_shape(tp, s, nc, K, M, dist="int3", seed=1201))
+    say(f"case slab fp8-out tile={tile}")
+    run, codes, amax, bc = _fp8_out_run(inp, c, 0.5)
+    G_ref, ref = oracle_ag(inp)
+    want, want_amax = O.quantize_output_e4m3(ref, 0.5)
+    assert np.array_equal(codes, want)
+    assert amax == want_amax
+    assert np.array_equal(W.bits_u16(bc.cpu()), W.bits_u16(inp.chunks[s]))
+    assert np.array_equal(W.bits_u16(run.G.cpu()), G_ref)
 
 
 def test_ag_b_copy_bf16_output_and_validation():
