@@ -112,8 +112,8 @@ __device__ __forceinline__ void ag_gemm_body(const AgArgs& a) {
     }
     if constexpr (OUT8) {
       uint8_t* out = (uint8_t*)a.out[j] + (size_t)rb * S::BI * a.M + (size_t)cb * S::BJ;
-      const float m = store_tile_fp8<S>(acc, scale, a.scale_D[0], lds, out, a.M,
-                                        a.nc - rb * S::BI, a.M - cb * S::BJ, wave, lane);
+      const float m = store_tile_fp8<S, acc_block<S, FP8>()>(
+          acc, scale, a.scale_D[0], lds, out, a.M, a.nc - rb * S::BI, a.M - cb * S::BJ, wave, lane);
       if (a.amax_D) {
         const float bm = block_max<S>(m, s_red, wave, lane);
         // amax >= 0, so its bits order like unsigned integers (a NaN sorts above everything)
@@ -123,8 +123,8 @@ __device__ __forceinline__ void ag_gemm_body(const AgArgs& a) {
       }
     } else {
       __bf16* out = (__bf16*)a.out[j] + (size_t)rb * S::BI * a.M + (size_t)cb * S::BJ;
-      store_tile_bf16<S>(acc, scale, lds, out, a.M, a.nc - rb * S::BI, a.M - cb * S::BJ, wave,
-                         lane);
+      store_tile_bf16<S, acc_block<S, FP8>()>(acc, scale, lds, out, a.M, a.nc - rb * S::BI,
+                                             a.M - cb * S::BJ, wave, lane);
     }
     if (tr && threadIdx.x == 0) {
       tr[2] = wall_clock64();

@@ -1,8 +1,9 @@
 // Device-side building blocks of the "TN" GEMM tile used by both operations:
 //     out[i][j] = sum_k X[i][k] * Y[j][k]       X [rows, K], Y [cols, K], both K-contiguous
 // on gfx950 matrix cores.  A workgroup of WI x WJ waves computes a BI x BJ output tile; wave
-// (wi, wj) owns the (BI/WI) x (BJ/WJ) sub-tile at (wi * BI/WI, wj * BJ/WJ), made of 32 x 32 MFMA
-// blocks with fp32 accumulators.
+// (wi, wj) owns the (BI/WI) x (BJ/WJ) sub-tile at (wi * BI/WI, wj * BJ/WJ), held as 32 x 32
+// blocks of fp32 accumulators, which the K loop fills with 32x32 MFMAs or, four 16x16 blocks
+// each, with 16x16 MFMAs (acc_row / acc_col give the layout).
 //
 // Data path per K step (BKB bytes of K per row: 64 or 128 bytes, i.e. 32/64 bf16 or 64/128 fp8):
 //   HBM/L2 --buffer_load_dwordx4 ... lds (16 B per lane, range-checked by the descriptor)--> LDS
@@ -14,8 +15,8 @@
 // read, followed by the one barrier per stage, which also tells the loads issued after it that the
 // stage they overwrite has been read.  Where that wait and barrier sit inside the stage, and how
 // the loads and fragment reads are spread over the MFMAs, is the K loop's business: see
-// tile_kloop_bf16 and tile_kloop_2s_fp8 (the pipelined loops) and tile_kloop (the plain one, for
-// the 4-stage fp8 tile).
+// tile_kloop_bf16, tile_kloop_bf16_32 and tile_kloop_2s_fp8 (the pipelined loops) and tile_kloop
+// (the plain one, for the 4-stage fp8 tile).
 //
 // LDS layout: rows of BKB bytes, split into 16-byte segments whose order is permuted by an XOR
 // key of the row (swz).  gfx950's LDS serves 256 bytes (64 banks) per cycle, i.e. 16 lanes of a
@@ -32,6 +33,7 @@ namespace ringag {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -273,7 +275,9 @@ struct NoStageHook {
   __device__ void post(int) {}
 };
 
-// bf16 K loop over NS LDS stages with the stage handover inside a stage's last MFMA k-step.
+// bf16 K loop with 32x32x16 MFMAs over NS LDS stages (the 64-byte-row tile, and the GEMM+RS
+// kernels, whose epilogue wants the 32x32 layout; the AG kernels' 128-byte-row tiles take the
+// 16x16 loop, tile_kloop_bf16 below), with the stage handover inside a stage's last MFMA k-step.
 // Fragments are double-buffered as in stage_mma.  Once the fragments of the last k-step are in
 // registers, the wave waits for its DMA of the next stage and for its reads, meets the others at
 // the barrier, reads the next stage's first fragments, and starts the DMA of stage kt + NS into
@@ -289,9 +293,9 @@ struct NoStageHook {
 // the wait and barrier that complete stage kt + 1, post(kt) right after them, before the loads of
 // stage kt + 2 are issued.
 template <class S, class Hook>
-__device__ inline void tile_kloop_bf16(i32x4 rx, const uint32_t* xo, i32x4 ry, const uint32_t* yo,
-                                       int ksteps, char* lds, int wave, int lane,
-                                       f32x16 (&acc)[S::FI][S::FJ], Hook& hook) {
+__device__ inline void tile_kloop_bf16_32(i32x4 rx, const uint32_t* xo, i32x4 ry,
+                                          const uint32_t* yo, int ksteps, char* lds, int wave,
+                                          int lane, f32x16 (&acc)[S::FI][S::FJ], Hook& hook) {
   constexpr int NK = S::SEGS / 2;
   constexpr int NM = S::FI * S::FJ;
   constexpr int H = S::LOADS / 2;   // the first half of a stage's DMA
@@ -363,6 +367,136 @@ __device__ inline void tile_kloop_bf16(i32x4 rx, const uint32_t* xo, i32x4 ry, c
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][i], b[1][j], acc[i][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       dma_range<S>(rx, xo, ry, yo, base, pend_buf, pend_kb, wave, m * H / NM, (m + 1) * H / NM);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  wait_vmem<0>();
+  __syncthreads();
+}
+
+// 16x16x32 MFMA fragment: row (lane & 15) of a 16-row block starting at tile_rows, 16 bytes at
+// logical segment `seg` (the lane's quarter of a 32-deep k-step is segment 4 kk + lane / 16).
+template <int BKB>
+__device__ inline bf16x8 frag16_bf16(const char* tile_rows, int seg, int lane) {
+  const int r = lane & 15;
+  return *(const bf16x8*)(tile_rows + r * BKB + ((seg ^ swz<BKB>(r)) << 4));
+}
+
+// One 16x16x32 MFMA on 16x16 block (gi, gj) of the wave's sub-tile.  The accumulators keep the
+// 32x32-block arrays of the other loops: 16x16 block (gi, gj) is elements 4 s .. 4 s + 3 of
+// block (gi / 2, gj / 2), s = 2 (gi % 2) + gj % 2 (acc_row / acc_col with MB = 16).
+template <int FI, int FJ>
+__device__ inline void mma16_bf16(f32x16 (&acc)[FI][FJ], int gi, int gj, const bf16x8& x,
+                                  const bf16x8& y) {
+  const int i = gi >> 1, j = gj >> 1, s = 2 * (gi & 1) + (gj & 1);
+  f32x4 c = {acc[i][j][4 * s], acc[i][j][4 * s + 1], acc[i][j][4 * s + 2], acc[i][j][4 * s + 3]};
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, c, 0, 0, 0);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) acc[i][j][4 * s + k] = c[k];
+}
+
+// bf16 K loop for the tiles with two stages of 128-byte rows: 16x16x32 MFMAs, two 32-deep k-steps
+// per stage.  The 16x16 shape costs the same MFMA time and LDS traffic as 32x32x16 but runs the
+// chip at a higher clock under its power limit (4096^3 GEMM-only, same DMA schedule: 1.81 against
+// 1.62 GHz at the same share of busy MFMA cycles).
+//
+// Per stage kt (fragments of k-step 0 already in set 0):
+//   k-step 0: its MFMAs, with the reads of k-step 1 (set 1) placed one after every other MFMA in
+//             order of first use;
+//   k-step 1: HB MFMAs, then the stage handover (this wave's DMA of stage kt + 1 complete, reads
+//             of stage kt done, workgroup barrier), then the rest of its MFMAs with the reads of
+//             stage kt + 1's k-step 0 (set 0) and, after each MFMA, a share of the DMA of stage
+//             kt + 2 into the buffer of stage kt, which the barrier has freed.
+// So the whole DMA of a stage goes out right after a handover and has one full stage to land
+// (issued half there and half a k-step later it left the second half short of time: the handover
+// then waited on it); no fragment read waits right behind the barrier.  Past the last stage the
+// DMA reads at kOOB (zeros, into a buffer nobody reads) and the reads take an idle buffer; the DMA
+// is drained before the final barrier.  `hook` (see NoStageHook) runs at every handover:
+// pre(kt) right before the wait and barrier that complete stage kt + 1, post(kt) right after
+// them, before the loads of stage kt + 2 are issued.
+template <class S, class Hook>
+__device__ inline void tile_kloop_bf16(i32x4 rx, const uint32_t* xo, i32x4 ry, const uint32_t* yo,
+                                       int ksteps, char* lds, int wave, int lane,
+                                       f32x16 (&acc)[S::FI][S::FJ], Hook& hook) {
+  static_assert(S::BKB == 128 && S::NS == 2, "two stages of 128-byte rows");
+  constexpr int GI = 2 * S::FI, GJ = 2 * S::FJ;   // 16x16 blocks of the wave sub-tile
+  constexpr int NM = GI * GJ;                     // MFMAs per k-step
+  constexpr int NR = GI + GJ;                     // fragment reads per k-step
+  constexpr int HB = NM / 4;                      // MFMAs of k-step 1 before the handover
+  constexpr int NA = NM - HB;                     // ... and after it
+  constexpr int R0 = 2 * NR < NM ? 2 * NR : NM;   // MFMA slots the reads of k-step 1 spread over
+  constexpr int R1 = 2 * NR < NA ? 2 * NR : NA;   // ... those of the next stage's k-step 0
+  constexpr int L = S::LOADS;
+  const int wi = wave / S::WJ, wj = wave % S::WJ;
+  const int q4 = lane >> 4;
+  const uint32_t base = lds_addr(lds);
+#pragma unroll
+  for (int i = 0; i < S::FI; ++i)
+#pragma unroll
+    for (int j = 0; j < S::FJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  if (ksteps <= 0) {
+    __syncthreads();
+    return;
+  }
+  // stage 0, then (stage 0 complete everywhere) stage 1 in full
+  dma_range<S>(rx, xo, ry, yo, base, 0, 0, wave, 0, L);
+  wait_vmem<0>();
+  __syncthreads();
+  uint32_t pend_kb = 1 < ksteps ? (uint32_t)S::BKB : kOOB;
+  int pend_buf = S::STAGE;
+  dma_range<S>(rx, xo, ry, yo, base, pend_buf, pend_kb, wave, 0, L);
+  const int xrow = wi * S::TM * S::BKB, yrow = (S::BI + wj * S::TN) * S::BKB;
+  bf16x8 a[2][GI], b[2][GJ];
+  // read n (in order of first use: x0, y0 .. y(GJ-1), x1 .. x(GI-1)) of the k-step at segment
+  // base sg0 of the stage at byte offset st, into fragment set `set`
+  auto rd = [&](int set, int st, int n, int sg0) {
+    if (n == 0)
+      a[set][0] = frag16_bf16<S::BKB>(lds + st + xrow, sg0 + q4, lane);
+    else if (n <= GJ)
+      b[set][n - 1] = frag16_bf16<S::BKB>(lds + st + yrow + (n - 1) * 16 * S::BKB, sg0 + q4, lane);
+    else
+      a[set][n - GJ] =
+          frag16_bf16<S::BKB>(lds + st + xrow + (n - GJ) * 16 * S::BKB, sg0 + q4, lane);
+  };
+#pragma unroll
+  for (int n = 0; n < NR; ++n) rd(0, 0, n, 0);
+  for (int kt = 0; kt < ksteps; ++kt) {
+    const int cur = (kt & 1) * S::STAGE;
+    const int nxt = S::STAGE - cur;
+    // k-step 0 (set 0); reads of k-step 1 (segments 4..7) into set 1
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      mma16_bf16(acc, m / GJ, m % GJ, a[0][m / GJ], b[0][m % GJ]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (m < R0) {
+#pragma unroll
+        for (int n = m * NR / R0; n < (m + 1) * NR / R0; ++n) rd(1, cur, n, 4);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // k-step 1 (set 1): HB MFMAs, the handover, the rest with the next stage's first reads and
+    // the DMA of stage kt + 2
+#pragma unroll
+    for (int m = 0; m < HB; ++m) mma16_bf16(acc, m / GJ, m % GJ, a[1][m / GJ], b[1][m % GJ]);
+    __builtin_amdgcn_sched_barrier(0);
+    hook.pre(kt);
+    stage_handover<0>();
+    hook.post(kt);
+    __builtin_amdgcn_sched_barrier(0);
+    pend_kb = kt + 2 < ksteps ? (uint32_t)(kt + 2) * S::BKB : kOOB;
+    pend_buf = cur;
+#pragma unroll
+    for (int m = HB; m < NM; ++m) {
+      mma16_bf16(acc, m / GJ, m % GJ, a[1][m / GJ], b[1][m % GJ]);
+      __builtin_amdgcn_sched_barrier(0);
+      const int r = m - HB;
+      if (r < R1) {
+#pragma unroll
+        for (int n = r * NR / R1; n < (r + 1) * NR / R1; ++n) rd(0, nxt, n, 0);
+      }
+      dma_range<S>(rx, xo, ry, yo, base, pend_buf, pend_kb, wave, r * L / NA, (r + 1) * L / NA);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -466,18 +600,29 @@ __device__ inline void tile_kloop_2s_fp8(i32x4 rx, const uint32_t* xo, i32x4 ry,
   __syncthreads();
 }
 
-// Full K loop of one tile.  rx/ry: descriptors of X and Y; xo/yo from tile_offsets; ksteps = K
-// bytes / BKB.  Returns with acc = the wave's fp32 sub-tile and all waves past a final barrier
-// (LDS free for the epilogue).  The caller must have passed a barrier since the last LDS reads.
-// bf16 takes the pipelined loop on every tile, fp8 on the two-stage tiles; the plain loop below
-// (barrier at the start of each stage, stage_mma per stage) is left for the 4-stage fp8 tile.
+// The accumulator layout (MB of acc_row / acc_col) of a tile's K loop by default: 16x16 MFMAs for
+// bf16 on the tiles with 128-byte rows, 32x32 otherwise.
 template <class S, bool FP8>
+constexpr int acc_block() {
+  return (!FP8 && S::BKB == 128) ? 16 : 32;
+}
+
+// Full K loop of one tile.  rx/ry: descriptors of X and Y; xo/yo from tile_offsets; ksteps = K
+// bytes / BKB.  Returns with acc = the wave's fp32 sub-tile, in layout MB, and all waves past a
+// final barrier (LDS free for the epilogue).  The caller must have passed a barrier since the
+// last LDS reads.  bf16 takes a pipelined loop on every tile (16x16 MFMAs for MB = 16, 32x32
+// otherwise), fp8 on the two-stage tiles; the plain loop below (barrier at the start of each
+// stage, stage_mma per stage) is left for the 4-stage fp8 tile.
+template <class S, bool FP8, int MB = acc_block<S, FP8>()>
 __device__ inline void tile_kloop(i32x4 rx, const uint32_t* xo, i32x4 ry, const uint32_t* yo,
                                   int ksteps, char* lds, int wave, int lane,
                                   f32x16 (&acc)[S::FI][S::FJ]) {
+  static_assert(MB == 32 || (MB == 16 && !FP8 && S::BKB == 128),
+                "16x16 MFMAs: the bf16 loop of the 128-byte-row tiles");
   if constexpr (!FP8) {
     NoStageHook none;
-    tile_kloop_bf16<S>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc, none);
+    if constexpr (MB == 16) tile_kloop_bf16<S>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc, none);
+    else tile_kloop_bf16_32<S>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc, none);
     return;
   } else if constexpr (S::NS == 2) {
     tile_kloop_2s_fp8<S>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);
@@ -518,18 +663,28 @@ __device__ inline void tile_kloop(i32x4 rx, const uint32_t* xo, i32x4 ry, const 
   __syncthreads();
 }
 
-// Output coordinates of accumulator element e of block (i, j) for this lane, relative to the
-// wave's sub-tile origin: row = 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4, col = 32 j + lane % 32.
+// Output coordinates of accumulator element e of 32x32 block (i, j) for this lane, relative to
+// the wave's sub-tile origin.  MB = 32 (32x32 MFMAs): row = 32 i + 8 (e / 4) + 4 (lane / 32) +
+// e % 4, col = 32 j + lane % 32.  MB = 16 (16x16 MFMAs; the block holds four 16x16 blocks, block
+// s = e / 4 = 2 bi + bj): row = 32 i + 16 bi + 4 (lane / 16) + e % 4, col = 32 j + 16 bj +
+// lane % 16.
+template <int MB>
 __device__ inline int acc_row(int i, int e, int lane) {
-  return i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+  if constexpr (MB == 16) return i * 32 + (e >> 3) * 16 + (lane >> 4) * 4 + (e & 3);
+  else return i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
 }
-__device__ inline int acc_col(int j, int lane) { return j * 32 + (lane & 31); }
+template <int MB>
+__device__ inline int acc_col(int j, int e, int lane) {
+  if constexpr (MB == 16) return j * 32 + ((e >> 2) & 1) * 16 + (lane & 15);
+  else return j * 32 + (lane & 31);
+}
+
 
 // Epilogue for bf16 output: the accumulators (times `scale`) are rounded to bf16 into an LDS
 // tile, then written out row by row with 16-byte stores.  out points at row 0 / column 0 of the
 // tile; ld = row stride in elements; rows/cols valid = how much of the tile lies inside the
 // output.  Ends with a barrier (LDS free again).
-template <class S>
+template <class S, int MB>
 __device__ inline void store_tile_bf16(const f32x16 (&acc)[S::FI][S::FJ], float scale, char* lds,
                                        __bf16* out, int ld, int rows_valid, int cols_valid,
                                        int wave, int lane) {
@@ -538,10 +693,10 @@ __device__ inline void store_tile_bf16(const f32x16 (&acc)[S::FI][S::FJ], float 
   for (int i = 0; i < S::FI; ++i)
 #pragma unroll
     for (int j = 0; j < S::FJ; ++j) {
-      const int col = wj * S::TN + acc_col(j, lane);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int row = wi * S::TM + acc_row(i, e, lane);
+        const int col = wj * S::TN + acc_col<MB>(j, e, lane);
+        const int row = wi * S::TM + acc_row<MB>(i, e, lane);
         *(__bf16*)(lds + row * S::OUT_LD + col * 2) = (__bf16)(acc[i][j][e] * scale);
       }
     }
@@ -568,7 +723,7 @@ __device__ inline void store_tile_bf16(const f32x16 (&acc)[S::FI][S::FJ], float 
 // E4M3(v * scale_d), saturated to +-448 and rounded to nearest even by the hardware convert; the
 // codes are staged through LDS and written out 16 bytes at a time.  Returns this thread's
 // max |v| (its share of the output's amax).  Ends with a barrier (LDS free again).
-template <class S>
+template <class S, int MB>
 __device__ inline float store_tile_fp8(const f32x16 (&acc)[S::FI][S::FJ], float scale,
                                        float scale_d, char* lds, uint8_t* out, int ld,
                                        int rows_valid, int cols_valid, int wave, int lane) {
@@ -579,10 +734,10 @@ __device__ inline float store_tile_fp8(const f32x16 (&acc)[S::FI][S::FJ], float 
   for (int i = 0; i < S::FI; ++i)
 #pragma unroll
     for (int j = 0; j < S::FJ; ++j) {
-      const int col = wj * S::TN + acc_col(j, lane);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int row = wi * S::TM + acc_row(i, e, lane);
+        const int col = wj * S::TN + acc_col<MB>(j, e, lane);
+        const int row = wi * S::TM + acc_row<MB>(i, e, lane);
         const float v = acc[i][j][e] * scale;
         amax = fmaxf(amax, fabsf(v));
         float q = v * scale_d;

@@ -42,6 +42,15 @@ __device__ inline uint32_t region_bytes(int rows, long long ld, int cols) {
   return b > 0xffffffffll ? 0xffffffffu : (uint32_t)b;
 }
 
+// Accumulator layout of the GEMM+RS kernels' K loop (acc_row / acc_col): 32x32 MFMAs.  The 16x16
+// loop the AG kernels take would leave each load and store of this epilogue four 64-byte row
+// pieces instead of two whole 128-byte lines; at rs_8k that cost more than the loop gains (kernel
+// 173 against 167 us, 244 against 222 us with the memory-side cache scrubbed).
+template <class S>
+constexpr int rs_acc_block() {
+  return 32;
+}
+
 template <class S>
 __device__ inline void rs_epilogue(f32x16 (&acc)[S::FI][S::FJ], char* lds, const RsArgs& a, int c,
                                    bool own, int rb, int cb, int wave, int lane) {
@@ -50,10 +59,15 @@ __device__ inline void rs_epilogue(f32x16 (&acc)[S::FI][S::FJ], char* lds, const
   constexpr int IB = S::FJ * 16 >= 64 ? 1 : 64 / (S::FJ * 16);
   constexpr int EB = S::FJ * 16 >= 64 ? 32 / S::FJ : 16;
   static_assert(S::FI % IB == 0 && 16 % EB == 0, "blocks must divide into load batches");
+  constexpr int MB = rs_acc_block<S>();
   const int wi = wave / S::WJ, wj = wave % S::WJ;
   const int r0 = rb * S::BI;                                   // chunk-local first row of the tile
-  const int lrow = wi * S::TM + 4 * (lane >> 5);               // lane's row in the tile (e = 0)
-  const int lcol = cb * S::BJ + wj * S::TN + (lane & 31);      // lane's column (j = 0)
+  // the lane's own row and column offsets; element (i, j, e) adds urow(i, e) rows and
+  // ucol(j, e) columns, the same for every lane (acc_row / acc_col)
+  const int lrow = wi * S::TM + (MB == 16 ? 4 * (lane >> 4) : 4 * (lane >> 5));
+  const int lcol = cb * S::BJ + wj * S::TN + (MB == 16 ? (lane & 15) : (lane & 31));
+  auto urow = [](int i, int e) { return acc_row<MB>(i, e, 0); };
+  auto ucol = [](int j, int e) { return acc_col<MB>(j, e, 0); };
   // what the tile's result gets added to: every peer's partial (own chunk, one-shot), one
   // incoming running sum (ring step), or nothing (another chunk, one-shot)
   const int nadd = a.ring ? (a.partial[c] != nullptr ? 1 : 0) : (own ? a.tp - 1 : 0);
@@ -80,11 +94,11 @@ __device__ inline void rs_epilogue(f32x16 (&acc)[S::FI][S::FJ], char* lds, const
         for (int ii = 0; ii < IB; ++ii)
 #pragma unroll
           for (int e = 0; e < EB; ++e) {
-            const int r = 32 * (i0 + ii) + 8 * ((e0 + e) >> 2) + ((e0 + e) & 3);
+            const int r = urow(i0 + ii, e0 + e);
 #pragma unroll
             for (int j = 0; j < S::FJ; ++j)
-              y[ii][j][e] = __uint_as_float(
-                  __builtin_amdgcn_raw_buffer_load_b32(rs, vo + 128 * j, r * rstride, 0));
+              y[ii][j][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                  rs, vo + 4 * ucol(j, e0 + e), r * rstride, 0));
           }
 #pragma unroll
         for (int ii = 0; ii < IB; ++ii)
@@ -95,8 +109,8 @@ __device__ inline void rs_epilogue(f32x16 (&acc)[S::FI][S::FJ], char* lds, const
       }
   }
   if (own) {
-    store_tile_bf16<S>(acc, 1.0f, lds, (__bf16*)a.D + (size_t)r0 * a.Mo + cb * S::BJ, a.Mo,
-                       a.nc - r0, a.Mo - cb * S::BJ, wave, lane);
+    store_tile_bf16<S, MB>(acc, 1.0f, lds, (__bf16*)a.D + (size_t)r0 * a.Mo + cb * S::BJ, a.Mo,
+                           a.nc - r0, a.Mo - cb * S::BJ, wave, lane);
     return;
   }
   // fp32 to send: rows past the chunk fall outside the descriptor and are dropped; columns past
@@ -109,18 +123,16 @@ __device__ inline void rs_epilogue(f32x16 (&acc)[S::FI][S::FJ], char* lds, const
   int rstride = a.Mo * 4;
   asm volatile("" : "+s"(rstride));
 #pragma unroll
-  for (int j = 0; j < S::FJ; ++j) {
-    if (lcol + 32 * j >= a.Mo) continue;
+  for (int j = 0; j < S::FJ; ++j)
 #pragma unroll
     for (int i = 0; i < S::FI; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
+        if (lcol + ucol(j, e) >= a.Mo) continue;
         const float v = acc[i][j][e];
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, vo + 128 * j,
-                                              (32 * i + 8 * (e >> 2) + (e & 3)) * rstride,
-                                              kNonTemporal);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, vo + 4 * ucol(j, e),
+                                              urow(i, e) * rstride, kNonTemporal);
       }
-  }
 }
 
 // The tile this workgroup runs in the round [r0, r0 + n) of a grid of `grid` workgroups, for a
@@ -196,7 +208,7 @@ __device__ __forceinline__ void gemm_rs_body(const RsArgs& a) {
     tile_offsets<S, S::XQ>(xo, rb * S::BI, a.nc, ldb, wave, lane);
     tile_offsets<S, S::YQ>(yo, cb * S::BJ, a.Mo, ldb, wave, lane);
     f32x16 acc[S::FI][S::FJ];
-    tile_kloop<S, false>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);
+    tile_kloop<S, false, rs_acc_block<S>()>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);
     // gated: wait for what the epilogue reads (the K loop did not need it): chunk c's running sum
     // (ring), or every peer's partial of the own chunk (one-shot).  With in-kernel copies the
     // workgroup copies pieces, in ring order, until each counter it needs is released.
