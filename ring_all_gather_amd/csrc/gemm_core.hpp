@@ -39,6 +39,11 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kOOB = 0x80000000u;         // voffset that is always past num_records
 
+// Accumulator layouts (the MB parameter of acc_row / acc_col and the epilogues): kAcc32 after
+// 32x32 MFMAs; kAcc16 after 16x16 MFMAs, four 16x16 blocks per 32x32 block of the array;
+// kAcc16S = kAcc16 after acc_swap_rows16.
+constexpr int kAcc32 = 32, kAcc16 = 16, kAcc16S = 17;
+
 template <int BI_, int BJ_, int WI_, int WJ_, int BKB_, int NS_>
 struct TileShape {
   static constexpr int BI = BI_, BJ = BJ_, WI = WI_, WJ = WJ_;
@@ -275,9 +280,9 @@ struct NoStageHook {
   __device__ void post(int) {}
 };
 
-// bf16 K loop with 32x32x16 MFMAs over NS LDS stages (the 64-byte-row tile, and the GEMM+RS
-// kernels, whose epilogue wants the 32x32 layout; the AG kernels' 128-byte-row tiles take the
-// 16x16 loop, tile_kloop_bf16 below), with the stage handover inside a stage's last MFMA k-step.
+// bf16 K loop with 32x32x16 MFMAs over NS LDS stages (the 64-byte-row tile; the 128-byte-row
+// tiles take the 16x16 loop, tile_kloop_bf16 below), with the stage handover inside a stage's
+// last MFMA k-step.
 // Fragments are double-buffered as in stage_mma.  Once the fragments of the last k-step are in
 // registers, the wave waits for its DMA of the next stage and for its reads, meets the others at
 // the barrier, reads the next stage's first fragments, and starts the DMA of stage kt + NS into
@@ -604,7 +609,7 @@ __device__ inline void tile_kloop_2s_fp8(i32x4 rx, const uint32_t* xo, i32x4 ry,
 // bf16 on the tiles with 128-byte rows, 32x32 otherwise.
 template <class S, bool FP8>
 constexpr int acc_block() {
-  return (!FP8 && S::BKB == 128) ? 16 : 32;
+  return (!FP8 && S::BKB == 128) ? kAcc16 : kAcc32;
 }
 
 // Full K loop of one tile.  rx/ry: descriptors of X and Y; xo/yo from tile_offsets; ksteps = K
@@ -617,11 +622,11 @@ template <class S, bool FP8, int MB = acc_block<S, FP8>()>
 __device__ inline void tile_kloop(i32x4 rx, const uint32_t* xo, i32x4 ry, const uint32_t* yo,
                                   int ksteps, char* lds, int wave, int lane,
                                   f32x16 (&acc)[S::FI][S::FJ]) {
-  static_assert(MB == 32 || (MB == 16 && !FP8 && S::BKB == 128),
+  static_assert(MB == kAcc32 || (MB == kAcc16 && !FP8 && S::BKB == 128),
                 "16x16 MFMAs: the bf16 loop of the 128-byte-row tiles");
   if constexpr (!FP8) {
     NoStageHook none;
-    if constexpr (MB == 16) tile_kloop_bf16<S>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc, none);
+    if constexpr (MB == kAcc16) tile_kloop_bf16<S>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc, none);
     else tile_kloop_bf16_32<S>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc, none);
     return;
   } else if constexpr (S::NS == 2) {
@@ -664,19 +669,46 @@ __device__ inline void tile_kloop(i32x4 rx, const uint32_t* xo, i32x4 ry, const 
 }
 
 // Output coordinates of accumulator element e of 32x32 block (i, j) for this lane, relative to
-// the wave's sub-tile origin.  MB = 32 (32x32 MFMAs): row = 32 i + 8 (e / 4) + 4 (lane / 32) +
-// e % 4, col = 32 j + lane % 32.  MB = 16 (16x16 MFMAs; the block holds four 16x16 blocks, block
-// s = e / 4 = 2 bi + bj): row = 32 i + 16 bi + 4 (lane / 16) + e % 4, col = 32 j + 16 bj +
-// lane % 16.
+// the wave's sub-tile origin; each is a lane part plus a part the same for every lane.
+//   kAcc32:  row = 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4,  col = 32 j + lane % 32;
+//   kAcc16:  block s = e / 4 = 2 bi + bj:  row = 32 i + 16 bi + 4 (lane / 16) + e % 4,
+//            col = 32 j + 16 bj + lane % 16;
+//   kAcc16S: row = 32 i + 16 bi + 4 bj + 8 (lane / 32) + e % 4,  col = 32 j + lane % 32.
 template <int MB>
 __device__ inline int acc_row(int i, int e, int lane) {
-  if constexpr (MB == 16) return i * 32 + (e >> 3) * 16 + (lane >> 4) * 4 + (e & 3);
+  if constexpr (MB == kAcc16) return i * 32 + (e >> 3) * 16 + (lane >> 4) * 4 + (e & 3);
+  else if constexpr (MB == kAcc16S)
+    return i * 32 + (e >> 3) * 16 + ((e >> 2) & 1) * 4 + (lane >> 5) * 8 + (e & 3);
   else return i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
 }
 template <int MB>
 __device__ inline int acc_col(int j, int e, int lane) {
-  if constexpr (MB == 16) return j * 32 + ((e >> 2) & 1) * 16 + (lane & 15);
+  if constexpr (MB == kAcc16) return j * 32 + ((e >> 2) & 1) * 16 + (lane & 15);
   else return j * 32 + (lane & 31);
+}
+
+// kAcc16 -> kAcc16S in registers: in each pair of 16x16 blocks side by side (bj = 0, 1) the
+// second and fourth 16-lane rows of the left block trade places with the first and third of the
+// right one (v_permlane16_swap), so that a lane's element e then sits at 32 consecutive columns
+// across lanes 0-31 (and 32-63) instead of 16: one wave instruction on it covers two whole rows of
+// 32 floats (two 128-byte lines) instead of four rows of 16.
+template <int FI, int FJ>
+__device__ inline void acc_swap_rows16(f32x16 (&acc)[FI][FJ]) {
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < FJ; ++j)
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int l = 8 * bi + e4, r = 8 * bi + 4 + e4;   // blocks (bi, 0) and (bi, 1)
+          const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[i][j][l]),
+                                                          __float_as_uint(acc[i][j][r]), false,
+                                                          false);
+          acc[i][j][l] = __uint_as_float(p[0]);
+          acc[i][j][r] = __uint_as_float(p[1]);
+        }
 }
 
 

@@ -12,12 +12,14 @@
 // result to send, or, for the own chunk, to D.  When that data arrives during the call (gated),
 // a tile runs its K loop first and waits for the counters only before its epilogue reads it.
 //
-// Epilogue: the partials are added to the accumulators where they are, in the MFMA register
-// layout.  A lane's accumulator element (i, j, e) sits at row 32 i + 8 (e / 4) + 4 (lane / 32) +
-// e % 4 and column 32 j + lane % 32 of the wave's sub-tile, so one load instruction of the wave
-// reads two rows of 32 consecutive floats (two whole 128-byte lines), and the row offsets are
-// uniform across the wave.  The loads are raw buffer loads: the per-lane offset is fixed for the
-// tile, the row offset goes in a scalar register and the column block in the immediate field.  A
+// Epilogue: the partials are added to the accumulators where they are, in the register layout
+// the K loop leaves them in, after one lane swap (kAcc16S, acc_swap_rows16 in gemm_core.hpp).  A
+// lane's accumulator element (i, j, e) then sits at row 32 i + 16 (e / 8) + 4 ((e / 4) % 2) +
+// 8 (lane / 32) + e % 4 and column 32 j + lane % 32 of the wave's sub-tile, so one load
+// instruction of the wave reads two rows of 32 consecutive floats (two whole 128-byte lines), and
+// the row offsets are uniform across the wave.  The loads are raw buffer loads: the per-lane
+// offset is fixed for the tile, the row offset goes in a scalar register and the column block in
+// the immediate field.  A
 // thread issues the loads of IB block rows (64 or more floats) before adding them, so a CU has
 // 8 waves x 64 lines x 128 bytes in flight rather than what fits in LDS.  fp32 results (send) are
 // stored the same way, non-temporal (they stream past L2 instead of displacing the operands); the
@@ -42,13 +44,19 @@ __device__ inline uint32_t region_bytes(int rows, long long ld, int cols) {
   return b > 0xffffffffll ? 0xffffffffu : (uint32_t)b;
 }
 
-// Accumulator layout of the GEMM+RS kernels' K loop (acc_row / acc_col): 32x32 MFMAs.  The 16x16
-// loop the AG kernels take would leave each load and store of this epilogue four 64-byte row
-// pieces instead of two whole 128-byte lines; at rs_8k that cost more than the loop gains (kernel
-// 173 against 167 us, 244 against 222 us with the memory-side cache scrubbed).
+// K loop of the GEMM+RS kernels: 16x16 MFMAs where the AG kernels take them (tile_kloop_bf16),
+// 32x32 otherwise.
+template <class S>
+constexpr int rs_loop_block() {
+  return S::BKB == 128 ? kAcc16 : kAcc32;
+}
+// Layout of the accumulators in the epilogue: kAcc16 is swapped to kAcc16S first
+// (acc_swap_rows16), since in kAcc16 every load and store of this epilogue would cover four
+// 64-byte row pieces instead of two whole 128-byte lines (rs_8k: 173 against 167 us unswapped;
+// swapped, 156-157 against 159-160 us for the 32x32 loop, one box).
 template <class S>
 constexpr int rs_acc_block() {
-  return 32;
+  return rs_loop_block<S>() == kAcc16 ? kAcc16S : kAcc32;
 }
 
 template <class S>
@@ -64,8 +72,8 @@ __device__ inline void rs_epilogue(f32x16 (&acc)[S::FI][S::FJ], char* lds, const
   const int r0 = rb * S::BI;                                   // chunk-local first row of the tile
   // the lane's own row and column offsets; element (i, j, e) adds urow(i, e) rows and
   // ucol(j, e) columns, the same for every lane (acc_row / acc_col)
-  const int lrow = wi * S::TM + (MB == 16 ? 4 * (lane >> 4) : 4 * (lane >> 5));
-  const int lcol = cb * S::BJ + wj * S::TN + (MB == 16 ? (lane & 15) : (lane & 31));
+  const int lrow = wi * S::TM + acc_row<MB>(0, 0, lane);
+  const int lcol = cb * S::BJ + wj * S::TN + acc_col<MB>(0, 0, lane);
   auto urow = [](int i, int e) { return acc_row<MB>(i, e, 0); };
   auto ucol = [](int j, int e) { return acc_col<MB>(j, e, 0); };
   // what the tile's result gets added to: every peer's partial (own chunk, one-shot), one
@@ -208,7 +216,8 @@ __device__ __forceinline__ void gemm_rs_body(const RsArgs& a) {
     tile_offsets<S, S::XQ>(xo, rb * S::BI, a.nc, ldb, wave, lane);
     tile_offsets<S, S::YQ>(yo, cb * S::BJ, a.Mo, ldb, wave, lane);
     f32x16 acc[S::FI][S::FJ];
-    tile_kloop<S, false, rs_acc_block<S>()>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);
+    tile_kloop<S, false, rs_loop_block<S>()>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);
+    if constexpr (rs_loop_block<S>() == kAcc16) acc_swap_rows16(acc);
     // gated: wait for what the epilogue reads (the K loop did not need it): chunk c's running sum
     // (ring), or every peer's partial of the own chunk (one-shot).  With in-kernel copies the
     // workgroup copies pieces, in ring order, until each counter it needs is released.
