@@ -37,6 +37,24 @@ __device__ inline unsigned hw_location() {
   return (xcc << 16) | (se << 8) | cu;
 }
 
+template <class T>
+struct TileTag {
+  using type = T;
+};
+
+// The half tile of an 8-wave 256-column tile: the same rows and waves, half the columns, each
+// wave 64x64.  A round of the persistent grid that is at most half full (the last one of a
+// problem whose tile count is not a multiple of the grid) runs its tiles as two halves on two
+// workgroups, so that every compute unit works through it instead of half of them for a whole
+// tile time.  ag_fc1_f8 (896 tiles, 3.5 rounds): chunked call 401 -> 391 us, GEMM-only 365 ->
+// 359 us (one box); less than the half round's share, since half-idle rounds ran at a higher
+// clock.
+template <class S>
+struct HalfTile {
+  static constexpr bool on = S::NW == 8 && S::BJ == 256 && S::BKB == 128 && S::NS == 2;
+  using type = TileShape<S::BI, 128, 4, 2, S::BKB, S::NS>;
+};
+
 // SLAB: the K-slab-gated form (its own entry points, so that the registers and LDS of the slab
 // copies are not charged to the chunk-gated kernels).
 template <class S, bool FP8, bool OUT8, bool SLAB = false>
@@ -72,12 +90,25 @@ __device__ __forceinline__ void ag_gemm_body(const AgArgs& a) {
 
   const int grid = (int)gridDim.x;
   for (int r0 = 0; a.compute && r0 < total; r0 += grid) {
-    const int t = round_tile(r0, min(grid, total - r0), grid);
-    if (t < 0) continue;
+    const int n = min(grid, total - r0);
+    // a round at most half full runs as 2n half tiles (HalfTile), dealt like whole ones
+    const bool split = HalfTile<S>::on && !SLAB && 2 * n <= grid;
+    int t, half = 0;
+    if (split) {
+      const int v = round_tile(0, 2 * n, grid);
+      if (v < 0) continue;
+      t = r0 + (v >> 1);
+      half = v & 1;
+    } else {
+      t = round_tile(r0, n, grid);
+      if (t < 0) continue;
+    }
     const int j = t / U;
     const int u = t - j * U;
     const int rb = u % a.tiles_i, cb = u / a.tiles_i;
-    unsigned long long* tr = a.trace ? a.trace + kTraceTileWords * (size_t)t : nullptr;
+    // (one stamp record per tile: a split tile's first half writes it)
+    unsigned long long* tr =
+        a.trace && half == 0 ? a.trace + kTraceTileWords * (size_t)t : nullptr;
     if (tr && threadIdx.x == 0) tr[0] = wall_clock64();
     if (slab && a.ctr_index[j] >= 0) {
       slab_gate_tile(a, j - 1, ldb, &s_gate);
@@ -100,31 +131,46 @@ __device__ __forceinline__ void ag_gemm_body(const AgArgs& a) {
       cyc0 = __builtin_amdgcn_s_memtime();
     }
     const i32x4 rx = make_rsrc(a.chunk[j], (uint32_t)a.nc * ldb);
-    uint32_t xo[S::XQ], yo[S::YQ];
-    tile_offsets<S, S::XQ>(xo, rb * S::BI, a.nc, ldb, wave, lane);
-    tile_offsets<S, S::YQ>(yo, cb * S::BJ, a.M, ldb, wave, lane);
-    f32x16 acc[S::FI][S::FJ];
-    if constexpr (SLAB) {
-      SlabHook hook{a, a.ctr_index[j] >= 0 ? j - 1 : -1, ksteps, ldb, &s_gate, s_slab, slot};
-      tile_kloop_bf16<S>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc, hook);
-    } else {
-      tile_kloop<S, FP8>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);
-    }
-    if constexpr (OUT8) {
-      uint8_t* out = (uint8_t*)a.out[j] + (size_t)rb * S::BI * a.M + (size_t)cb * S::BJ;
-      const float m = store_tile_fp8<S, acc_block<S, FP8>()>(
-          acc, scale, a.scale_D[0], lds, out, a.M, a.nc - rb * S::BI, a.M - cb * S::BJ, wave, lane);
-      if (a.amax_D) {
-        const float bm = block_max<S>(m, s_red, wave, lane);
-        // amax >= 0, so its bits order like unsigned integers (a NaN sorts above everything)
-        if (threadIdx.x == 0)
-          __hip_atomic_fetch_max((unsigned*)a.amax_D, __float_as_uint(bm), __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
+    // the tile (or half tile) of shape T whose first output column is col0
+    auto run_tile = [&](auto tag, int col0) {
+      using T = typename decltype(tag)::type;
+      uint32_t xo[T::XQ], yo[T::YQ];
+      tile_offsets<T, T::XQ>(xo, rb * T::BI, a.nc, ldb, wave, lane);
+      tile_offsets<T, T::YQ>(yo, col0, a.M, ldb, wave, lane);
+      f32x16 acc[T::FI][T::FJ];
+      if constexpr (SLAB) {
+        SlabHook hook{a, a.ctr_index[j] >= 0 ? j - 1 : -1, ksteps, ldb, &s_gate, s_slab, slot};
+        tile_kloop_bf16<T>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc, hook);
+      } else {
+        tile_kloop<T, FP8>(rx, xo, ry, yo, ksteps, lds, wave, lane, acc);
+      }
+      if constexpr (OUT8) {
+        uint8_t* out = (uint8_t*)a.out[j] + (size_t)rb * T::BI * a.M + (size_t)col0;
+        const float m = store_tile_fp8<T, acc_block<T, FP8>()>(
+            acc, scale, a.scale_D[0], lds, out, a.M, a.nc - rb * T::BI, a.M - col0, wave, lane);
+        if (a.amax_D) {
+          const float bm = block_max<T>(m, s_red, wave, lane);
+          // amax >= 0, so its bits order like unsigned integers (a NaN sorts above everything)
+          if (threadIdx.x == 0)
+            __hip_atomic_fetch_max((unsigned*)a.amax_D, __float_as_uint(bm), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+      } else {
+        __bf16* out = (__bf16*)a.out[j] + (size_t)rb * T::BI * a.M + (size_t)col0;
+        store_tile_bf16<T, acc_block<T, FP8>()>(acc, scale, lds, out, a.M, a.nc - rb * T::BI,
+                                               a.M - col0, wave, lane);
+      }
+    };
+    if constexpr (HalfTile<S>::on && !SLAB) {
+      using Th = typename HalfTile<S>::type;
+      if (split) {
+        // (a right half wholly past the last column has nothing to do)
+        if (cb * S::BJ + half * Th::BJ < a.M) run_tile(TileTag<Th>{}, cb * S::BJ + half * Th::BJ);
+      } else {
+        run_tile(TileTag<S>{}, cb * S::BJ);
       }
     } else {
-      __bf16* out = (__bf16*)a.out[j] + (size_t)rb * S::BI * a.M + (size_t)cb * S::BJ;
-      store_tile_bf16<S, acc_block<S, FP8>()>(acc, scale, lds, out, a.M, a.nc - rb * S::BI,
-                                             a.M - cb * S::BJ, wave, lane);
+      run_tile(TileTag<S>{}, cb * S::BJ);
     }
     if (tr && threadIdx.x == 0) {
       tr[2] = wall_clock64();
