@@ -102,6 +102,26 @@ def test_ag_short_k_every_tile(tile, nsteps, dtype):
     assert np.array_equal(run.D_bits(), O.f32_to_bf16(ref))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("M", [1280, 3072, 2916], ids=["whole", "half", "half-ragged"])
+def test_ag_rounds_whole_and_half_tiles(M, dtype):
+    """The 8-wave 256x256 tile runs a round that is at most half full as twice as many 256x128
+    half tiles.  tp=4 with 2048-row chunks gives 8 row blocks per chunk: M = 1280 gives 160 tiles
+    on a grid of 256 workgroups (whole tiles), 3072 gives 384 (256 whole, then 128 split), and
+    2916 gives 384 too, with a last column block 100 columns wide, so that its right halves have
+    nothing to do; exact integers, D bit for bit."""
+    c = ctx()
+    c.set_option(B.RAG_OPT_TILE, B.TILES["256x256w8"])
+    K = 256 if dtype == "fp8" else 128
+    inp = _int_case(4, 1, 2048, K=K, M=M, seed=1300 + M, dtype=dtype)
+    say(f"case rounds M={M} dtype={dtype}")
+    run = AGRun(inp).run(c)
+    G_ref, ref = oracle_ag(inp)
+    bits = W.bits_u8 if dtype == "fp8" else W.bits_u16
+    assert np.array_equal(bits(run.G.cpu()), G_ref)
+    assert np.array_equal(run.D_bits(), O.f32_to_bf16(ref))
+
+
 def test_ag_bitwise_invariant_across_ranks_and_modes():
     """Chunking splits the gathered rows, not K: the result must not depend on the self rank,
     on whether chunks arrive (counters) or are already there, or on the split at all (tp=1)."""
