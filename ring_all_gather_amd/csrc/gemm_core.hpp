@@ -389,7 +389,7 @@ __device__ inline bf16x8 frag16_bf16(const char* tile_rows, int seg, int lane) {
 
 // One 16x16x32 MFMA on 16x16 block (gi, gj) of the wave's sub-tile.  The accumulators keep the
 // 32x32-block arrays of the other loops: 16x16 block (gi, gj) is elements 4 s .. 4 s + 3 of
-// block (gi / 2, gj / 2), s = 2 (gi % 2) + gj % 2 (acc_row / acc_col with MB = 16).
+// block (gi / 2, gj / 2), s = 2 (gi % 2) + gj % 2 (layout kAcc16 of acc_row / acc_col).
 template <int FI, int FJ>
 __device__ inline void mma16_bf16(f32x16 (&acc)[FI][FJ], int gi, int gj, const bf16x8& x,
                                   const bf16x8& y) {
@@ -615,7 +615,7 @@ constexpr int acc_block() {
 // Full K loop of one tile.  rx/ry: descriptors of X and Y; xo/yo from tile_offsets; ksteps = K
 // bytes / BKB.  Returns with acc = the wave's fp32 sub-tile, in layout MB, and all waves past a
 // final barrier (LDS free for the epilogue).  The caller must have passed a barrier since the
-// last LDS reads.  bf16 takes a pipelined loop on every tile (16x16 MFMAs for MB = 16, 32x32
+// last LDS reads.  bf16 takes a pipelined loop on every tile (16x16 MFMAs for MB = kAcc16, 32x32
 // otherwise), fp8 on the two-stage tiles; the plain loop below (barrier at the start of each
 // stage, stage_mma per stage) is left for the 4-stage fp8 tile.
 template <class S, bool FP8, int MB = acc_block<S, FP8>()>
