@@ -9,9 +9,10 @@ self_rank=1, bf16.  The default warm-up (1000 steps) lets the chip's clock settl
 timed steps; the timed steps are bracketed by one event pair, and the per-step and per-kernel
 figures come from a separate instrumented pass right after them.
 
-Prints one JSON line: throughput (TFLOP/s) of the whole step, the overlap figures (GEMM-only and
-copy-only times of the same kernels, overlap ratio T_chunked / (T_copy_only + T_gemm_only), the
-hidden fraction of the copy time, and the same work without overlap in one step: the copies-only
+Prints one JSON line: throughput (TFLOP/s) of the whole step, the overlap figures (chunked,
+GEMM-only and copy-only times of the same kernels measured back to back after the headline, overlap
+ratio T_chunked / (T_copy_only + T_gemm_only), the hidden fraction of the copy time, the headline's
+time over that chunked time, and the same work without overlap in one step: the copies-only
 launch followed by the GEMM-only launch), the roofline of the GEMM kernel (algorithmic flops per
 launch over its average launch duration, from HIP events that each launch records on the stream
 it runs on), for AG a timeline of one traced call (chunk releases against tile starts; the stamps
@@ -276,12 +277,15 @@ def timeline_ag(ctx, B, step, shape, kname):
             "tile_clock_ghz": {"p10": q(0.1), "p50": q(0.5), "p90": q(0.9)}, "chunks": chunks}
 
 
-def overlap_per_engine(ctx, B, step, args, stream, shape, ms_head):
+def overlap_per_engine(ctx, B, step, args, stream, shape):
     """T_gemm_only, T_copy_only, T_chunked, the overlap ratio and the hidden fraction for the
-    headline copy engine (whose chunked time was just measured) and, unless --headline-only, for
-    the other engines.  Each engine's GEMM-only launch uses the tile its chunked call uses (the
-    side-stream kernel engine may pick another kernel of the same tile size, see the library's
-    tile choice), so the three times are of the same kernel."""
+    headline copy engine and, unless --headline-only, for the other engines.  An engine's three
+    times are measured back to back (its chunked call again for the headline engine), so that
+    they come from one regime of the clock: with a short warm-up the headline's own steps still
+    run while the clock ramps up from idle, and setting them against legs timed later would
+    charge the ramp to the overlap.  Each engine's GEMM-only launch uses the tile its chunked
+    call uses (the side-stream kernel engine may pick another kernel of the same tile size, see
+    the library's tile choice), so the three times are of the same kernel."""
     names = [args.copy_engine] + ([] if args.headline_only else
                                   [e for e in ("in-gemm", "in-gemm-slab", "assist", "in-gemm-sdma",
                                                "kernel", "sdma") if e != args.copy_engine])
@@ -289,8 +293,7 @@ def overlap_per_engine(ctx, B, step, args, stream, shape, ms_head):
     for eng in names:
         set_engine(ctx, B, eng)
         kname = ctx.ag_kernel_name(shape.nc, shape.M, shape.tp, shape.dtype == "fp8")
-        t_chunked = ms_head if eng == args.copy_engine else \
-            time_steps(step, args.steps, args.warmup, stream, f"{eng} chunked")
+        t_chunked = time_steps(step, args.steps, args.warmup, stream, f"{eng} chunked")
         t_copy = time_steps(lambda: step(B.RAG_COPY_ONLY), args.steps, args.warmup, stream,
                             f"{eng} copies only")
         tile = kname.split("_t", 1)[1]
@@ -377,8 +380,9 @@ def main():
         ctx.set_option(B.RAG_OPT_TIMING, 0)
         ctx.check()
         kname = ctx.ag_kernel_name(shape.nc, shape.M, shape.tp, shape.dtype == "fp8")
-        engines = overlap_per_engine(ctx, B, step, args, stream, shape, ms)
+        engines = overlap_per_engine(ctx, B, step, args, stream, shape)
         head = engines[args.copy_engine]
+        ms_pair = head["t_chunked_ms"]
         ms_gemm, ms_copy = head["t_gemm_only_ms"], head["t_copy_only_ms"]
         ms_staged = ms_split = ms_seq = None
         if not args.headline_only:
@@ -416,12 +420,13 @@ def main():
             "pct_mfma_peak": round(100.0 * value / peak, 2),
             "step_ms": {"p10": round(pctl(per, 0.1), 5), "p50": round(pctl(per, 0.5), 5),
                         "p90": round(pctl(per, 0.9), 5)},
-            "overlap": {"t_chunked_ms": round(ms, 5), "t_gemm_only_ms": round(ms_gemm, 5),
+            "overlap": {"t_chunked_ms": round(ms_pair, 5), "t_gemm_only_ms": round(ms_gemm, 5),
                         "t_copy_only_ms": round(ms_copy, 5),
-                        "overlap_ratio": round(ms / (ms_copy + ms_gemm), 4),
-                        "hidden_fraction": round((ms_copy + ms_gemm - ms) / ms_copy, 4),
+                        "overlap_ratio": round(ms_pair / (ms_copy + ms_gemm), 4),
+                        "hidden_fraction": round((ms_copy + ms_gemm - ms_pair) / ms_copy, 4),
+                        "headline_vs_chunked_pair": round(ms / ms_pair, 4),
                         "t_copy_then_gemm_ms": rnd(ms_seq),
-                        "chunked_vs_copy_then_gemm": rnd(ms_seq and ms / ms_seq, 4),
+                        "chunked_vs_copy_then_gemm": rnd(ms_seq and ms_pair / ms_seq, 4),
                         "t_staged_out_ms": rnd(ms_staged),
                         "t_split_per_chunk_ms": rnd(ms_split),
                         "per_engine": engines},
