@@ -14,8 +14,8 @@
 
 namespace ringag {
 
-// 16-byte vectors in flight per copying thread: 6 keeps the kernel at 48 VGPRs, which fit beside
-// two GEMM waves of up to 232 VGPRs on a SIMD (of its 512).
+// 16-byte vectors in flight per copying thread: 6 keeps the kernel at 38 VGPRs (40 as allocated),
+// which fit beside two GEMM waves of up to 232 VGPRs on a SIMD (of its 512).
 constexpr int kArrivalInFlight = 6;
 
 __device__ __forceinline__ void arrival_body(const ArrivalArgs& a) {
