@@ -110,6 +110,16 @@ __device__ __forceinline__ void ag_gemm_body(const AgArgs& a) {
     unsigned long long* tr =
         a.trace && half == 0 ? a.trace + kTraceTileWords * (size_t)t : nullptr;
     if (tr && threadIdx.x == 0) tr[0] = wall_clock64();
+    // In a one-round launch the own chunk's tiles start at once and end well before the peers'
+    // tiles, which start only after the copies; so each of the own chunk's workgroups first
+    // copies one piece of the peers' chunks.  The copies then run on every XCD, not only on those
+    // holding the peers' tiles, and each XCD's path to memory carries less of them (ag_4k chunked
+    // call 112.5-113.0 -> 111.5-112.0 us, one box).  With more rounds the delay reaches the own
+    // workgroups' later tiles (ag_fc1_f8 394.0-394.5 -> 395.5-396.6 us), so they do not.
+    if (copier && !slab && total <= grid && a.ctr_index[j] < 0) {
+      run_copy_queue<S::NT, 8, kPipe>(a.cp, a.ctr, a.epoch, 0, -1, &s_piece, 1u);
+      __syncthreads();   // keeps the queue's thread-0 step and this tile's apart
+    }
     if (slab && a.ctr_index[j] >= 0) {
       slab_gate_tile(a, j - 1, ldb, &s_gate);
     } else if (a.ctr_index[j] >= 0) {
