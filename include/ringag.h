@@ -122,7 +122,9 @@ enum {
                               tiles wait for it leaves it room as for the copy kernel */
     RAG_COPY_IN_GEMM = 2,  /* the GEMM launch itself: workgroups whose chunk is not there yet copy
                               pieces of the peers' chunks (ring order) until it is released, and
-                              help with the rest once out of tiles; no side stream is used (see
+                              help with the rest once out of tiles (in a launch of one persistent
+                              round the own chunk's workgroups also copy one piece each before
+                              their tile); no side stream is used (see
                               RAG_RS_ARRIVE for the GEMM+RS form).  With K-slab gating
                               (RAG_OPT_AG_GATE), every workgroup copies its share of slab pieces
                               instead, and a tile waits only for the slab it loads next */

@@ -12,9 +12,10 @@
 // With in-kernel copies (AgArgs::copies) the launch also carries the call's arrival: a workgroup
 // whose next tile belongs to a chunk that is not there yet takes pieces of the peers' chunks from
 // the copy queue (ring order) until that chunk is released, and once out of tiles it helps with
-// whatever is left, the own chunk's copy into G last.  The waiting workgroups are exactly the ones
-// with nothing to compute, so the copies use compute units that would otherwise idle, and no side
-// stream or stream fork/join is involved.
+// whatever is left, the own chunk's copy into G last.  The waiting workgroups are the ones with
+// nothing to compute yet (in a one-round launch the own chunk's workgroups, which have time to
+// spare, also copy one piece each first), so the copies use compute units that would otherwise
+// idle, and no side stream or stream fork/join is involved.
 //
 // With K-slab gating (AgArgs::slab, bf16 8-wave 2-stage tiles) the peers' chunks are not queued
 // whole: every workgroup copies its own slots of slab pieces (before its first tile, inside its K
