@@ -292,7 +292,10 @@ struct NoStageHook {
 // wave's MFMA issue; spread further, the last pieces have too little time to land).  So no
 // fragment read waits right behind a barrier, and the DMA issue hides under MFMAs.  The loop body
 // has no branch: past the last stage the DMA reads at kOOB (zeros, into a buffer nobody reads) and
-// the prefetch reads an idle buffer; the DMA is drained before the final barrier.
+// the prefetch reads an idle buffer; the DMA is drained before the final barrier.  From the
+// handover to the start of the next stage a wave issues at raised priority (s_setprio 1), as in
+// tile_kloop_bf16 (ag_4k on this tile: GEMM-only 115.8-116.2 -> 113.1-113.5 us, in-GEMM copies
+// 128.7-129.7 -> 125.7-126.2 us, one box; all waves at priority 1 gain nothing).
 //
 // `hook` (see NoStageHook) runs code of the caller's at every stage handover: pre(kt) just before
 // the wait and barrier that complete stage kt + 1, post(kt) right after them, before the loads of
@@ -336,6 +339,7 @@ __device__ inline void tile_kloop_bf16_32(i32x4 rx, const uint32_t* xo, i32x4 ry
   for (int kt = 0; kt < ksteps; ++kt) {
     const int cur = (S::NS == 2 ? (kt & 1) : kt % S::NS) * S::STAGE;
     const int nxt = S::NS == 2 ? S::STAGE - cur : ((kt + 1) % S::NS) * S::STAGE;
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int kk = 0; kk < NK - 1; ++kk) {
       const int c = kk & 1;
@@ -362,6 +366,7 @@ __device__ inline void tile_kloop_bf16_32(i32x4 rx, const uint32_t* xo, i32x4 ry
     hook.pre(kt);
     stage_handover<(S::NS - 2) * S::LOADS>();
     hook.post(kt);
+    __builtin_amdgcn_s_setprio(1);   // until the next stage starts (see above)
     load_frags_bf16<S>(a[0], b[0], lds + nxt + xrow, lds + nxt + yrow, h, lane);
     __builtin_amdgcn_sched_barrier(0);
     pend_kb = kt + S::NS < ksteps ? (uint32_t)(kt + S::NS) * S::BKB : kOOB;
@@ -375,6 +380,7 @@ __device__ inline void tile_kloop_bf16_32(i32x4 rx, const uint32_t* xo, i32x4 ry
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  __builtin_amdgcn_s_setprio(0);
   wait_vmem<0>();
   __syncthreads();
 }
