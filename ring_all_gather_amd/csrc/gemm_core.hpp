@@ -36,6 +36,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr uint32_t kOOB = 0x80000000u;         // voffset that is always past num_records
 
@@ -694,14 +696,14 @@ __device__ inline void tile_kloop(i32x4 rx, const uint32_t* xo, i32x4 ry, const 
 //            col = 32 j + 16 bj + lane % 16;
 //   kAcc16S: row = 32 i + 16 bi + 4 bj + 8 (lane / 32) + e % 4,  col = 32 j + lane % 32.
 template <int MB>
-__device__ inline int acc_row(int i, int e, int lane) {
+__host__ __device__ constexpr int acc_row(int i, int e, int lane) {
   if constexpr (MB == kAcc16) return i * 32 + (e >> 3) * 16 + (lane >> 4) * 4 + (e & 3);
   else if constexpr (MB == kAcc16S)
     return i * 32 + (e >> 3) * 16 + ((e >> 2) & 1) * 4 + (lane >> 5) * 8 + (e & 3);
   else return i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
 }
 template <int MB>
-__device__ inline int acc_col(int j, int e, int lane) {
+__host__ __device__ constexpr int acc_col(int j, int e, int lane) {
   if constexpr (MB == kAcc16) return j * 32 + ((e >> 2) & 1) * 16 + (lane & 15);
   else return j * 32 + (lane & 31);
 }
@@ -740,16 +742,35 @@ __device__ inline void store_tile_bf16(const f32x16 (&acc)[S::FI][S::FJ], float 
                                        __bf16* out, int ld, int rows_valid, int cols_valid,
                                        int wave, int lane) {
   const int wi = wave / S::WJ, wj = wave % S::WJ;
+  // Two adjacent columns per LDS write: lanes 2m and 2m + 1 hold adjacent columns of the same
+  // rows, so each packs two of its elements (rows r and r + DR of its column) into one bf16 pair,
+  // trades that word with its neighbour (DPP quad_perm [1,0,3,2]) and keeps a pair of one row:
+  // the even lane row r, the odd lane row r + DR.  With DR = 2 (kAcc16), 4 (kAcc16S) or 8 (kAcc32)
+  // the 64 lanes of one write fall in distinct banks at every OUT_LD here.  Half as many LDS
+  // writes as one element per write (ag_4k GEMM-only 97.6 -> 97.0 us, chunked 109.5-110.0 ->
+  // 108.4-109.2 us, one box; the same bits).
+  constexpr int P = MB == kAcc16 ? 2 : 4;   // the partner element
+  constexpr int DR = acc_row<MB>(0, P, 0) - acc_row<MB>(0, 0, 0);
+  const bool odd = lane & 1;
+  // v_perm byte selector: odd lane {nb.hi, own.hi}, even lane {own.lo, nb.lo}
+  const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
+  char* const wb = lds + (wi * S::TM + acc_row<MB>(0, 0, lane) + (odd ? DR : 0)) * S::OUT_LD +
+                   ((wj * S::TN + acc_col<MB>(0, 0, lane)) & ~1) * 2;
 #pragma unroll
   for (int i = 0; i < S::FI; ++i)
 #pragma unroll
     for (int j = 0; j < S::FJ; ++j) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int col = wj * S::TN + acc_col<MB>(j, e, lane);
-        const int row = wi * S::TM + acc_row<MB>(i, e, lane);
-        *(__bf16*)(lds + row * S::OUT_LD + col * 2) = (__bf16)(acc[i][j][e] * scale);
+        if (e & P) continue;
+        const f32x2 v = {acc[i][j][e] * scale, acc[i][j][e + P] * scale};
+        const uint32_t own = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+        const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)own, 0xB1, 0xF, 0xF, false);
+        const int off = (acc_row<MB>(i, e, 0) - acc_row<MB>(0, 0, 0)) * S::OUT_LD +
+                        (acc_col<MB>(j, e, 0) - acc_col<MB>(0, 0, 0)) * 2;
+        *(uint32_t*)(wb + off) = __builtin_amdgcn_perm(nb, own, sel);
       }
+      __builtin_amdgcn_sched_barrier(0);   // one block at a time: bounds the live temporaries
     }
   __syncthreads();
   constexpr int OSEGS = S::BJ / 8;   // 16-byte segments per tile row
