@@ -61,11 +61,13 @@ struct TileShape {
   static constexpr int XQ = BI / (RPI * NW);     // DMA instructions per wave per stage (X)
   static constexpr int YQ = BJ / (RPI * NW);
   static constexpr int LOADS = XQ + YQ;          // vmcnt increments per wave per stage
-  // bf16 output staging: rows padded by 16 bytes so the two row halves a wave writes do not
-  // share banks
+  // bf16 output staging row stride, by accumulator layout (store_tile_bf16): rows padded by 16
+  // bytes after 16x16 MFMAs, by 32 after 32x32 ones, so that the lanes of one packed LDS write
+  // fall in distinct banks
   static constexpr int OUT_LD = BJ * 2 + 16;
+  static constexpr int OUT_LD32 = BJ * 2 + 32;
   static constexpr int LDS_MAIN = NS * STAGE;
-  static constexpr int LDS_OUT = BI * OUT_LD;
+  static constexpr int LDS_OUT = BI * OUT_LD32;
   static constexpr int LDS = LDS_MAIN > LDS_OUT ? LDS_MAIN : LDS_OUT;
   static_assert(BKB == 64 || BKB == 128, "rows of 64 or 128 bytes");
   static_assert(NS >= 2 && NS <= 4, "2 to 4 stages");
@@ -745,16 +747,18 @@ __device__ inline void store_tile_bf16(const f32x16 (&acc)[S::FI][S::FJ], float 
   // Two adjacent columns per LDS write: lanes 2m and 2m + 1 hold adjacent columns of the same
   // rows, so each packs two of its elements (rows r and r + DR of its column) into one bf16 pair,
   // trades that word with its neighbour (DPP quad_perm [1,0,3,2]) and keeps a pair of one row:
-  // the even lane row r, the odd lane row r + DR.  With DR = 2 (kAcc16), 4 (kAcc16S) or 8 (kAcc32)
-  // the 64 lanes of one write fall in distinct banks at every OUT_LD here.  Half as many LDS
-  // writes as one element per write (ag_4k GEMM-only 97.6 -> 97.0 us, chunked 109.5-110.0 ->
-  // 108.4-109.2 us, one box; the same bits).
-  constexpr int P = MB == kAcc16 ? 2 : 4;   // the partner element
+  // the even lane row r, the odd lane row r + DR.  DR = 2 (kAcc16, kAcc32) or 4 (kAcc16S) with
+  // the layout's row stride LD puts the odd lanes' words 16 banks (mod 32) past the even lanes'
+  // and the lane groups of one write in distinct banks.  Half as many LDS writes as one element
+  // per write (ag_4k GEMM-only 97.6 -> 97.0 us, chunked 109.5-110.0 -> 108.4-109.2 us, one box;
+  // the same bits).
+  constexpr int LD = MB == kAcc32 ? S::OUT_LD32 : S::OUT_LD;
+  constexpr int P = MB == kAcc16S ? 4 : 2;   // the partner element
   constexpr int DR = acc_row<MB>(0, P, 0) - acc_row<MB>(0, 0, 0);
   const bool odd = lane & 1;
   // v_perm byte selector: odd lane {nb.hi, own.hi}, even lane {own.lo, nb.lo}
   const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
-  char* const wb = lds + (wi * S::TM + acc_row<MB>(0, 0, lane) + (odd ? DR : 0)) * S::OUT_LD +
+  char* const wb = lds + (wi * S::TM + acc_row<MB>(0, 0, lane) + (odd ? DR : 0)) * LD +
                    ((wj * S::TN + acc_col<MB>(0, 0, lane)) & ~1) * 2;
 #pragma unroll
   for (int i = 0; i < S::FI; ++i)
@@ -766,7 +770,7 @@ __device__ inline void store_tile_bf16(const f32x16 (&acc)[S::FI][S::FJ], float 
         const f32x2 v = {acc[i][j][e] * scale, acc[i][j][e + P] * scale};
         const uint32_t own = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
         const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)own, 0xB1, 0xF, 0xF, false);
-        const int off = (acc_row<MB>(i, e, 0) - acc_row<MB>(0, 0, 0)) * S::OUT_LD +
+        const int off = (acc_row<MB>(i, e, 0) - acc_row<MB>(0, 0, 0)) * LD +
                         (acc_col<MB>(j, e, 0) - acc_col<MB>(0, 0, 0)) * 2;
         *(uint32_t*)(wb + off) = __builtin_amdgcn_perm(nb, own, sel);
       }
@@ -779,7 +783,7 @@ __device__ inline void store_tile_bf16(const f32x16 (&acc)[S::FI][S::FJ], float 
     const int r = idx / OSEGS, sg = idx % OSEGS;
     const int c = sg * 8;
     if (r >= rows_valid || c >= cols_valid) continue;
-    const char* src = lds + r * S::OUT_LD + c * 2;
+    const char* src = lds + r * LD + c * 2;
     __bf16* dst = out + (size_t)r * ld + c;
     if (vec && c + 8 <= cols_valid) {
       // non-temporal: written once, never read back here; keeps the operands in L2
